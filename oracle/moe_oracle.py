@@ -1,0 +1,300 @@
+"""Plain, slow fp64 CPU oracle of the sparse-MoE block forward.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The HIP library never
+links, calls or falls back to it, and it shares no code with the HIP path.
+
+What it computes (Qwen3-MoE sparse block, decode or prefill, one layer):
+
+  1. router logits   l[t,e] = sum_h X[t,h] * Wr[e,h], rounded to fp32, then
+                     plus an optional fp32 per-expert bias (added in fp32).
+                     The workload fixes "softmax over fp32 logits"; the fp32
+                     value is the correctly rounded fp32 of the dot product of
+                     the bf16 operands (their products are exact).
+  2. top-k           the k experts with the largest fp32 logit; equal logits
+                     go to the lower expert index; ids stored best first.
+  3. weights         softmax over all E logits (fp64), then renormalised over
+                     the k chosen: w_j = p[id_j] / sum_j' p[id_j'].
+  4. bucketing       per-expert counts (histogram), exclusive-scan offsets
+                     (E+1 entries), and the stable permutation of the flat
+                     token-expert slots s = t*k + j grouped by expert: the
+                     bincount/scatter_add + cumsum + argsort steps of the
+                     grouped_mm MoE path [unsloth commit 80aaf1121b page
+                     (Qwen3-MoE decode CUDA-graph capture), third and last
+                     paragraphs].
+  5. experts         SwiGLU MLP per chosen expert: g = Wg x, u = Wu x,
+                     h = silu(g) * u with silu(z) = z / (1 + exp(-z)),
+                     y = Wd h  (the grouped GEMMs of the same path).
+  6. combine         out[t] = sum_j w[t,j] * y[t,j], j ascending (the
+                     index_add_ step of the same path), returned as a plain
+                     tensor [unsloth commit 4f2bfe7f69 page (first MoE decode
+                     bench), second paragraph].
+
+4-bit expert weights: W[n, k] = fp32(codebook[code] * absmax[n, k // 64]) with
+codes packed two per byte (even element in the low nibble).
+
+Everything is numpy fp64 (bf16 and fp32 inputs convert exactly).  The
+per-token loop `forward_per_token` is the definition; `forward_batched` is the
+same arithmetic grouped by expert (one matmul per expert) for large T, and is
+checked against the per-token loop by the tests.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+NF4_BLOCK = 64
+
+
+# --------------------------------------------------------------------------
+# storage formats -> fp64
+# --------------------------------------------------------------------------
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp64 values."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def nf4_unpack(packed: np.ndarray) -> np.ndarray:
+    """uint8 [..., K/2] -> codes uint8 [..., K]; element 2i is the low nibble."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    lo = packed & np.uint8(0x0F)
+    hi = packed >> np.uint8(4)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def nf4_dequant(packed: np.ndarray, absmax: np.ndarray, codebook: np.ndarray) -> np.ndarray:
+    """4-bit blockwise weights -> fp32 values W = fp32(codebook[code] * absmax),
+    one absmax per 64 consecutive weights along the last axis."""
+    codes = nf4_unpack(packed)
+    cb = np.asarray(codebook, dtype=np.float32)
+    vals = cb[codes]                                             # fp32
+    sc = np.repeat(np.asarray(absmax, dtype=np.float32), NF4_BLOCK, axis=-1)
+    return (vals * sc).astype(np.float32)                        # fp32 product
+
+
+# --------------------------------------------------------------------------
+# router
+# --------------------------------------------------------------------------
+def router_logits(x_bits: np.ndarray, wr_bits: np.ndarray,
+                  bias: Optional[np.ndarray] = None, exact: bool = False) -> np.ndarray:
+    """fp32 router logits [T][E].
+
+    The dot product of bf16 operands is formed in fp64 (numpy matmul; with
+    exact=True each entry is math.fsum over the exact products, the correctly
+    rounded fp64 sum) and then rounded to fp32.  The bias, if any, is added in
+    fp32 arithmetic.
+    """
+    x = bf16_bits_to_f64(x_bits)
+    wr = bf16_bits_to_f64(wr_bits)
+    if exact:
+        T, E = x.shape[0], wr.shape[0]
+        l64 = np.empty((T, E), dtype=np.float64)
+        for t in range(T):
+            for e in range(E):
+                l64[t, e] = math.fsum((x[t] * wr[e]).tolist())
+    else:
+        l64 = x @ wr.T
+    l32 = l64.astype(np.float32)
+    if bias is not None:
+        l32 = (l32 + np.asarray(bias, dtype=np.float32)).astype(np.float32)
+    return l32
+
+
+def topk_lowest_index(logits32: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest logits per row, best first; equal logits are
+    ordered by ascending expert index.  int32 [T][k]."""
+    logits32 = np.asarray(logits32)
+    T, E = logits32.shape
+    idx = np.broadcast_to(np.arange(E), (T, E))
+    # lexsort: last key is primary -> sort by (-logit, index)
+    order = np.lexsort((idx, -logits32.astype(np.float64)), axis=-1)
+    return order[:, :k].astype(np.int32)
+
+
+def renormalised_weights(logits32: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Softmax over all E logits (fp64, max-subtracted), then renormalised over
+    the chosen k: w_j = p[id_j] / sum_j' p[id_j'].  fp64 [T][k]."""
+    l = np.asarray(logits32, dtype=np.float64)
+    m = l.max(axis=1, keepdims=True)
+    p = np.exp(l - m)
+    p = p / p.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def route(x_bits, wr_bits, k: int, bias=None, exact: bool = False):
+    """(ids int32 [T][k], weights fp64 [T][k], logits fp32 [T][E])."""
+    l32 = router_logits(x_bits, wr_bits, bias, exact=exact)
+    ids = topk_lowest_index(l32, k)
+    w = renormalised_weights(l32, ids)
+    return ids, w, l32
+
+
+# --------------------------------------------------------------------------
+# bucketing: histogram, exclusive scan, stable permutation
+# --------------------------------------------------------------------------
+def histogram(ids_flat: np.ndarray, E: int) -> np.ndarray:
+    counts = np.zeros(E, dtype=np.int64)
+    for e in np.asarray(ids_flat).tolist():
+        counts[e] += 1
+    return counts.astype(np.int32)
+
+
+def exclusive_scan(counts: np.ndarray) -> np.ndarray:
+    """offsets[0] = 0, offsets[e+1] = offsets[e] + counts[e]  (E+1 entries)."""
+    out = np.zeros(len(counts) + 1, dtype=np.int64)
+    run = 0
+    for e, c in enumerate(np.asarray(counts).tolist()):
+        out[e] = run
+        run += c
+    out[len(counts)] = run
+    return out.astype(np.int32)
+
+
+def stable_permute(ids_flat: np.ndarray, offsets: np.ndarray):
+    """Counting sort of flat slots by expert, keeping slot order inside each
+    expert.  perm[p] = slot s placed at position p; pos[s] = p (inverse)."""
+    ids_flat = np.asarray(ids_flat).tolist()
+    cursor = np.asarray(offsets[:-1], dtype=np.int64).copy()
+    n = len(ids_flat)
+    perm = np.empty(n, dtype=np.int32)
+    pos = np.empty(n, dtype=np.int32)
+    for s, e in enumerate(ids_flat):
+        p = int(cursor[e])
+        cursor[e] += 1
+        perm[p] = s
+        pos[s] = p
+    return perm, pos
+
+
+def permute(ids: np.ndarray, E: int):
+    """(counts [E], offsets [E+1], perm [T*k], pos [T*k]) from ids [T][k]."""
+    flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    counts = histogram(flat, E)
+    offsets = exclusive_scan(counts)
+    perm, pos = stable_permute(flat, offsets)
+    return counts, offsets, perm, pos
+
+
+# --------------------------------------------------------------------------
+# experts
+# --------------------------------------------------------------------------
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+class ExpertWeights:
+    """fp64 views of the expert weights, converted per expert on first use."""
+
+    def __init__(self, inp):
+        self.inp = inp
+        self.I = inp.I
+        self._cache = {}
+        self._pending = {}
+
+    def get(self, e: int):
+        if e not in self._cache:
+            if self.inp.wfmt not in ("bf16", "nf4"):
+                raise ValueError(self.inp.wfmt)
+            self._convert(e)
+            self._cache[e] = self._pending.pop(e)
+        return self._cache[e]
+
+    def preload(self, experts):
+        """Convert several experts at once on a thread pool (numpy casts drop
+        the GIL); the values are the same as converting one by one."""
+        todo = [int(e) for e in experts if int(e) not in self._cache]
+        n = min(len(todo), max(1, len(os.sched_getaffinity(0))))
+        if n <= 1:
+            for e in todo:
+                self.get(e)
+            return
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(self._convert, todo))
+        # dict writes happen here, on one thread
+        for e, val in self._pending.items():
+            self._cache[e] = val
+        self._pending.clear()
+
+    def _convert(self, e: int):
+        inp = self.inp
+        if inp.wfmt == "bf16":
+            gu = bf16_bits_to_f64(inp.w_gate_up[e])
+            wd = bf16_bits_to_f64(inp.w_down[e])
+        else:
+            gu = nf4_dequant(inp.q_gate_up[e], inp.s_gate_up[e], inp.codebook).astype(np.float64)
+            wd = nf4_dequant(inp.q_down[e], inp.s_down[e], inp.codebook).astype(np.float64)
+        self._pending[e] = (gu[: self.I], gu[self.I:], wd)
+
+
+def expert_mlp(x64: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """SwiGLU expert on one token (vector) or a batch (rows): y = Wd (silu(Wg x) * Wu x)."""
+    g = x64 @ wg.T
+    u = x64 @ wu.T
+    h = silu(g) * u
+    return h @ wd.T
+
+
+# --------------------------------------------------------------------------
+# full block
+# --------------------------------------------------------------------------
+def forward_per_token(inp, weights: Optional[ExpertWeights] = None, exact_router: bool = False,
+                      routing=None):
+    """The definition: loop over tokens, then over the k chosen experts.
+
+    Returns (out fp64 [T][H], routing dict)."""
+    if routing is None:
+        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias, exact=exact_router)
+    else:
+        ids, w, l32 = routing["ids"], routing["w"], routing["logits"]
+    W = weights or ExpertWeights(inp)
+    x64 = bf16_bits_to_f64(inp.x)
+    out = np.zeros((inp.T, inp.H), dtype=np.float64)
+    for t in range(inp.T):
+        acc = np.zeros(inp.H, dtype=np.float64)
+        for j in range(inp.k):
+            wg, wu, wd = W.get(int(ids[t, j]))
+            acc = acc + w[t, j] * expert_mlp(x64[t], wg, wu, wd)
+        out[t] = acc
+    return out, dict(ids=ids, w=w, logits=l32)
+
+
+def forward_batched(inp, weights: Optional[ExpertWeights] = None, routing=None):
+    """Same arithmetic grouped by expert: for each expert, one matmul over the
+    tokens routed to it, then the per-token weighted sum in ascending j.
+
+    Returns (out fp64 [T][H], routing dict incl. counts/offsets/perm/pos)."""
+    if routing is None:
+        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias)
+    else:
+        ids, w, l32 = routing["ids"], routing["w"], routing["logits"]
+    counts, offsets, perm, pos = permute(ids, inp.E)
+    W = weights or ExpertWeights(inp)
+    W.preload(np.nonzero(counts)[0])
+    x64 = bf16_bits_to_f64(inp.x)
+    T, k = ids.shape
+    y_slot = np.zeros((T * k, inp.H), dtype=np.float64)
+    for e in range(inp.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        slots = perm[a:b].astype(np.int64)
+        wg, wu, wd = W.get(e)
+        y_slot[slots] = expert_mlp(x64[slots // k], wg, wu, wd)
+    out = np.zeros((T, inp.H), dtype=np.float64)
+    for j in range(k):
+        out += w[:, j:j + 1] * y_slot[np.arange(T) * k + j]
+    return out, dict(ids=ids, w=w, logits=l32, counts=counts, offsets=offsets, perm=perm, pos=pos)
+
+
+def rms(a: np.ndarray) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    return float(np.sqrt(np.mean(a * a)))

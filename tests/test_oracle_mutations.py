@@ -1,0 +1,114 @@
+"""Plant plausible mistakes in the oracle (on the CPU, via monkeypatch) and
+check that at least one pin fails for each.  This is what makes the pins worth
+trusting: a dropped term, a flipped tie rule, a swapped operand or an
+off-by-one scan would not slip through."""
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.moe_oracle as M
+from tests import test_formats_pins as F
+from tests import test_oracle_pins as P
+
+
+def patch(monkeypatch, name, fn):
+    monkeypatch.setattr(M, name, fn)
+    monkeypatch.setattr(O, name, fn)
+
+
+def ties_to_higher_index(logits32, k):
+    T, E = logits32.shape
+    idx = np.broadcast_to(-np.arange(E), (T, E))
+    return np.lexsort((idx, -logits32.astype(np.float64)), axis=-1)[:, :k].astype(np.int32)
+
+
+def no_renormalisation(logits32, ids):
+    l = np.asarray(logits32, dtype=np.float64)
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    return np.take_along_axis(p, ids.astype(np.int64), axis=1)
+
+
+def sigmoid_not_silu(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def inclusive_scan(counts):
+    c = np.cumsum(counts)
+    return np.concatenate([c, [c[-1]]]).astype(np.int32)
+
+
+def unstable_permute(ids_flat, offsets):
+    perm, pos = ORIG_STABLE(ids_flat, offsets)
+    for e in range(len(offsets) - 1):
+        a, b = offsets[e], offsets[e + 1]
+        perm[a:b] = perm[a:b][::-1].copy()
+    pos[perm] = np.arange(len(perm))
+    return perm, pos
+
+
+def bias_ignored(x_bits, wr_bits, bias=None, exact=False):
+    return ORIG_LOGITS(x_bits, wr_bits, None, exact)
+
+
+def swapped_nibbles(packed):
+    out = ORIG_UNPACK(packed)
+    out[..., 0::2], out[..., 1::2] = out[..., 1::2].copy(), out[..., 0::2].copy()
+    return out
+
+
+ORIG_STABLE = M.stable_permute
+ORIG_LOGITS = M.router_logits
+ORIG_UNPACK = M.nf4_unpack
+
+
+def swap_gate_up(monkeypatch):
+    orig = M.ExpertWeights._convert
+
+    def conv(self, e):
+        orig(self, e)
+        g, u, d = self._pending[e]
+        self._pending[e] = (u, g, d)
+
+    monkeypatch.setattr(M.ExpertWeights, "_convert", conv)
+
+
+def uniform_combine(monkeypatch):
+    orig = M.route
+
+    def route(*a, **kw):
+        ids, w, l = orig(*a, **kw)
+        return ids, np.full_like(w, 1.0 / w.shape[1]), l
+
+    patch(monkeypatch, "route", route)
+
+
+MUTATIONS = {
+    "ties_to_higher_index": (lambda mp: patch(mp, "topk_lowest_index", ties_to_higher_index),
+                             [P.test_hand_worked_block_closed_form, P.test_identical_router_rows_lower_index_wins]),
+    "no_renormalisation": (lambda mp: patch(mp, "renormalised_weights", no_renormalisation),
+                           [P.test_hand_worked_block_closed_form, P.test_weights_sum_to_one_and_are_positive]),
+    "sigmoid_not_silu": (lambda mp: patch(mp, "silu", sigmoid_not_silu),
+                         [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
+    "gate_up_swapped": (swap_gate_up,
+                        [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
+    "routing_weights_ignored": (uniform_combine, [P.test_hand_worked_block_closed_form]),
+    "inclusive_scan": (lambda mp: patch(mp, "exclusive_scan", inclusive_scan),
+                       [P.test_bucketing_random_and_adversarial]),
+    "unstable_permute": (lambda mp: patch(mp, "stable_permute", unstable_permute),
+                         [P.test_bucketing_random_and_adversarial, P.test_bucketing_zero_input_closed_form]),
+    "bias_ignored": (lambda mp: patch(mp, "router_logits", bias_ignored),
+                     [P.test_router_bias_added_in_fp32]),
+    "nibbles_swapped": (lambda mp: patch(mp, "nf4_unpack", swapped_nibbles),
+                        [F.test_nf4_pack_unpack_round_trip_and_nibble_order,
+                         F.test_nf4_dequant_is_codebook_times_absmax_in_fp32]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    apply, pins = MUTATIONS[name]
+    apply(monkeypatch)
+    for pin in pins:
+        with pytest.raises((AssertionError, IndexError, ValueError)):
+            pin()
