@@ -1,0 +1,209 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse-MoE block library.
+ *
+ * The block is the Qwen3-MoE sparse feed-forward layer as run on the
+ * grouped_mm path described on the unsloth commit 80aaf1121b page
+ * (Qwen3-MoE decode CUDA-graph capture), third paragraph: router ->
+ * per-expert token counts -> cumulative offsets -> argsort permutation ->
+ * one grouped GEMM over all active experts -> per-token weighted add.  The
+ * router turns fp32 logits into the top-k experts (ties go to the lower
+ * expert index) and renormalises their softmax weights; each expert is a
+ * SwiGLU MLP; the result is a plain tensor (unsloth commit 4f2bfe7f69 page,
+ * second paragraph).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers unless marked "host".  Tensors are
+ *     dense, row-major, and 16-byte aligned.  bf16 data is passed as void*.
+ *   - The caller owns every buffer.  Entry points never allocate device
+ *     memory, never synchronise the stream and never copy to the host
+ *     (except moe_read_counts, which says so).  Work is enqueued on `stream`
+ *     (NULL = the default stream) in call order.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-MOE_OK status means nothing was launched.  moe_last_error() gives
+ *     a message for the calling thread's last failure.  A fault on the GPU
+ *     surfaces at the caller's next synchronising HIP call.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     on every run, eager or graph-replayed (no floating-point atomics).
+ *   - Supported shapes: hidden % 64 == 0 and 64 <= hidden <= 4096;
+ *     inter % 64 == 0 and 64 <= inter <= 4096; n_experts % 16 == 0 and
+ *     16 <= n_experts <= 256; 1 <= top_k <= min(n_experts, 16);
+ *     1 <= t_max and t_max * top_k <= 65536.  Other shapes return
+ *     MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,       /* null/misaligned pointer, T out of range, bad bucket list */
+  MOE_ERR_UNSUPPORTED = 2,       /* shape or format outside the built kernels */
+  MOE_ERR_WORKSPACE = 3,         /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_NOT_CAPTURABLE = 4,    /* graph capture refused; stream left uncaptured, run eagerly */
+  MOE_ERR_CAPTURE_VIOLATION = 5, /* a synchronising call was made on a capturing stream */
+  MOE_ERR_HIP = 6                /* a HIP runtime call failed (message in moe_last_error) */
+} moe_status;
+
+typedef enum {
+  MOE_W_BF16 = 0,     /* bf16 expert weights */
+  MOE_W_NF4_B64 = 1   /* 4-bit codes + one fp32 absmax per 64 consecutive weights */
+} moe_wformat;
+
+/* Shape of one MoE layer.  t_max bounds T for every call made with this
+ * config and sizes the workspace. */
+typedef struct {
+  int32_t hidden;     /* H: model width */
+  int32_t inter;      /* I: expert intermediate width */
+  int32_t n_experts;  /* E */
+  int32_t top_k;      /* k */
+  int32_t t_max;      /* largest token count T passed with this config */
+  int32_t wfmt;       /* moe_wformat */
+} moe_config;
+
+/* Layer weights (device, read-only).  Expert tensors are stacked on E.
+ *   w_router   bf16 [E][H]
+ *   router_bias fp32 [E] or NULL: added to the fp32 router logits before
+ *              selection and softmax.
+ * MOE_W_BF16:
+ *   w_gate_up  bf16 [E][2I][H]   rows [0,I) = gate, rows [I,2I) = up
+ *   w_down     bf16 [E][H][I]
+ * MOE_W_NF4_B64 (weight = codebook[code] * absmax, 64 weights per absmax
+ * along the last axis; element 2i in the low nibble of byte i):
+ *   q_gate_up  uint8 [E][2I][H/2]    s_gate_up fp32 [E][2I][H/64]
+ *   q_down     uint8 [E][H][I/2]     s_down    fp32 [E][H][I/64]
+ *   codebook   fp32 [16]
+ * Unused fields may be NULL. */
+typedef struct {
+  const void* w_router;
+  const float* router_bias;
+  const void* w_gate_up;
+  const void* w_down;
+  const uint8_t* q_gate_up;
+  const float* s_gate_up;
+  const uint8_t* q_down;
+  const float* s_down;
+  const float* codebook;
+} moe_weights;
+
+/* Routing arrays inside a forward workspace (device pointers), valid after a
+ * moe_forward or a graph replay has completed on the stream. */
+typedef struct {
+  int32_t* topk_ids;   /* [T][k] */
+  float* topk_w;       /* [T][k] */
+  int32_t* counts;     /* [E] */
+  int32_t* offsets;    /* [E+1] */
+  int32_t* perm;       /* [T*k] */
+  int32_t* pos;        /* [T*k] */
+} moe_views;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(int32_t status);
+
+/* Message describing the calling thread's most recent non-OK status. */
+const char* moe_last_error(void);
+
+/* MOE_OK if the config is within the supported shapes. */
+moe_status moe_config_check(const moe_config* cfg);
+
+/* Bytes of workspace moe_forward / moe_graph_capture need for cfg (sized
+ * for cfg->t_max); 0 if cfg is invalid. */
+size_t moe_workspace_size(const moe_config* cfg);
+
+/* Router: fp32 logits l[t][e] = sum_h x[t][h]*w_router[e][h] (+ bias[e]),
+ * the top-k experts per token (largest logit first, equal logits -> lower
+ * expert index) and their renormalised softmax weights
+ * w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0).
+ * The k chosen experts and their order are decided on the correctly rounded
+ * fp32 logits (each candidate's dot product is re-formed in fp64).
+ *   x         bf16 [T][H]
+ *   topk_ids  int32 [T][k]   (out)
+ *   topk_w    fp32  [T][k]   (out)
+ *   logits    fp32  [T][E]   (out, nullable): exact for the candidates of
+ *             each token, within a stated error bound for the others.
+ * Defined by the router step of the grouped_mm path (unsloth commit
+ * 80aaf1121b page, third paragraph; router fusion on the unsloth commit
+ * a1bc5cbd page, first paragraph). */
+moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
+                     int32_t* topk_ids, float* topk_w, float* logits, hipStream_t stream);
+
+/* Bucketing of the T*k token-expert slots s = t*k + j by expert, with no
+ * host synchronisation (the capture-safe replacement for bincount described
+ * on the unsloth commit 80aaf1121b page, last paragraph):
+ *   counts[e]   = number of slots routed to e                  int32 [E]
+ *   offsets     = exclusive scan of counts, offsets[E] = T*k   int32 [E+1]
+ *   perm[p]     = slot placed at position p, slots grouped by expert in
+ *                 ascending expert order, ascending s inside a group
+ *                 (a stable argsort of the flat ids)           int32 [T*k]
+ *   pos[s]      = p with perm[p] = s (nullable)                int32 [T*k]
+ * topk_ids values must lie in [0, E); out-of-range ids are not counted and
+ * leave perm/pos entries unspecified (memory-safe). */
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T,
+                       int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                       hipStream_t stream);
+
+/* Whole block: route -> permute -> grouped gate/up with SiLU*up ->
+ * grouped down -> per-token weighted combine.
+ *   x     bf16 [T][H]
+ *   out   fp32 [T][H]: out[t] = sum_{j ascending} topk_w[t][j] * y[t][j]
+ *   workspace  >= moe_workspace_size(cfg) bytes, 256-byte aligned; its
+ *              contents need no initialisation and are overwritten.
+ * Calls sharing one workspace must be ordered on one stream. */
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
+                       float* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* moe_forward that also records `events[0..5]` (host array of hipEvent_t
+ * created by the caller) on `stream` before route, permute, gate/up, down,
+ * combine and after combine, for per-stage timing.  Same results. */
+moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x,
+                             int32_t T, float* out, void* workspace, size_t ws_bytes,
+                             hipStream_t stream, hipEvent_t* events /* host, 6 */);
+
+/* Device pointers of the routing arrays inside `workspace` (pure host
+ * arithmetic; nothing is read from the device). */
+moe_status moe_workspace_views(const moe_config* cfg, void* workspace, size_t ws_bytes,
+                               moe_views* views /* host out */);
+
+/* Copies counts[E] from a forward workspace to host memory and synchronises
+ * the stream.  Refused with MOE_ERR_CAPTURE_VIOLATION on a capturing stream. */
+moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t ws_bytes,
+                           int32_t* host_counts /* host, E */, hipStream_t stream);
+
+/* Per-batch-size hipGraphs of moe_forward (the bucketed decode-step capture
+ * of the unsloth commit 80aaf1121b page, second paragraph): one graph per
+ * bucket size, all reading `x_static` (bf16 [t_max][H]) and writing
+ * `out_static` (fp32 [t_max][H]) through one shared workspace.  Those
+ * buffers and the weights must outlive the graph; their addresses are baked
+ * in.  `buckets` (host) must be strictly ascending within [1, t_max].
+ * `stream` must be a created stream (not NULL) that is not capturing.  On
+ * any capture failure everything made so far is released, the stream is
+ * left uncaptured and MOE_ERR_NOT_CAPTURABLE is returned, so the caller can
+ * run moe_forward eagerly instead. */
+typedef struct moe_graph moe_graph;
+moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const int32_t* buckets,
+                             int32_t n_buckets, const void* x_static, float* out_static,
+                             void* workspace, size_t ws_bytes, hipStream_t stream,
+                             moe_graph** graph /* host out */);
+
+/* Launches the graph of the smallest bucket >= T on `stream`.  Rows
+ * [T, bucket) of x_static are processed as well (their outputs land in rows
+ * [T, bucket) of out_static; rows < T do not depend on them).  T larger than
+ * the largest bucket -> MOE_ERR_INVALID_ARG. */
+moe_status moe_graph_replay(moe_graph* graph, int32_t T, hipStream_t stream);
+
+/* Bucket size moe_graph_replay(graph, T) would use, or -1. */
+int32_t moe_graph_bucket_for(const moe_graph* graph, int32_t T);
+
+/* Releases the graphs (NULL is a no-op).  Do not replay afterwards. */
+void moe_graph_destroy(moe_graph* graph);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

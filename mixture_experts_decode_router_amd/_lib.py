@@ -1,0 +1,259 @@
+"""ctypes binding of libmoe_mi355x.so (include/moe.h), argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of the block: it turns torch device tensors (or raw integer device
+pointers) and streams into the C arguments, calls the library, and raises
+MoEError on a non-OK status.  If the library is not built, `lib()` raises: the
+block has no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, Structure, c_char_p, c_int32, c_size_t, c_void_p
+
+import numpy as np
+
+LIB_NAME = "libmoe_mi355x.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_NOT_CAPTURABLE = 4
+MOE_ERR_CAPTURE_VIOLATION = 5
+MOE_ERR_HIP = 6
+
+MOE_W_BF16 = 0
+MOE_W_NF4_B64 = 1
+
+# every entry point include/moe.h declares
+EXPORTS = (
+    "moe_status_str", "moe_last_error", "moe_config_check", "moe_workspace_size",
+    "moe_route", "moe_permute", "moe_forward", "moe_forward_timed", "moe_workspace_views",
+    "moe_read_counts", "moe_graph_capture", "moe_graph_replay", "moe_graph_bucket_for",
+    "moe_graph_destroy",
+)
+
+
+class moe_config(Structure):
+    _fields_ = [("hidden", c_int32), ("inter", c_int32), ("n_experts", c_int32),
+                ("top_k", c_int32), ("t_max", c_int32), ("wfmt", c_int32)]
+
+
+class moe_weights(Structure):
+    _fields_ = [("w_router", c_void_p), ("router_bias", c_void_p), ("w_gate_up", c_void_p),
+                ("w_down", c_void_p), ("q_gate_up", c_void_p), ("s_gate_up", c_void_p),
+                ("q_down", c_void_p), ("s_down", c_void_p), ("codebook", c_void_p)]
+
+
+class moe_views(Structure):
+    _fields_ = [("topk_ids", c_void_p), ("topk_w", c_void_p), ("counts", c_void_p),
+                ("offsets", c_void_p), ("perm", c_void_p), ("pos", c_void_p)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; build it with "
+            "`python -m mixture_experts_decode_router_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    S = c_int32  # moe_status
+    sig = {
+        "moe_status_str": (c_char_p, [c_int32]),
+        "moe_last_error": (c_char_p, []),
+        "moe_config_check": (S, [POINTER(moe_config)]),
+        "moe_workspace_size": (c_size_t, [POINTER(moe_config)]),
+        "moe_route": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
+                          c_void_p, c_void_p, c_void_p, c_void_p]),
+        "moe_permute": (S, [POINTER(moe_config), c_void_p, c_int32, c_void_p, c_void_p,
+                            c_void_p, c_void_p, c_void_p]),
+        "moe_forward": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
+                            c_void_p, c_void_p, c_size_t, c_void_p]),
+        "moe_forward_timed": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
+                                  c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+        "moe_workspace_views": (S, [POINTER(moe_config), c_void_p, c_size_t, POINTER(moe_views)]),
+        "moe_read_counts": (S, [POINTER(moe_config), c_void_p, c_size_t, c_void_p, c_void_p]),
+        "moe_graph_capture": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
+                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
+                                  POINTER(c_void_p)]),
+        "moe_graph_replay": (S, [c_void_p, c_int32, c_void_p]),
+        "moe_graph_bucket_for": (c_int32, [c_void_p, c_int32]),
+        "moe_graph_destroy": (None, [c_void_p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        L = lib()
+        raise MoEError(status, f"{L.moe_status_str(status).decode()}: {L.moe_last_error().decode()}")
+
+
+def ptr(t) -> int | None:
+    """Device pointer of a torch tensor (or pass an int / None through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    return t.data_ptr()
+
+
+def stream_handle(stream) -> int | None:
+    """hipStream_t of a torch stream (None -> torch's current stream)."""
+    if isinstance(stream, int):
+        return stream
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def moe_status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_config_check(cfg: moe_config) -> int:
+    return lib().moe_config_check(ctypes.byref(cfg))
+
+
+def moe_workspace_size(cfg: moe_config) -> int:
+    return lib().moe_workspace_size(ctypes.byref(cfg))
+
+
+def moe_route(cfg, w, x, T, topk_ids, topk_w, logits=None, stream=None):
+    _check(lib().moe_route(ctypes.byref(cfg), ctypes.byref(w), ptr(x), T, ptr(topk_ids),
+                           ptr(topk_w), ptr(logits), stream_handle(stream)))
+
+
+def moe_permute(cfg, topk_ids, T, counts, offsets, perm, pos=None, stream=None):
+    _check(lib().moe_permute(ctypes.byref(cfg), ptr(topk_ids), T, ptr(counts), ptr(offsets),
+                             ptr(perm), ptr(pos), stream_handle(stream)))
+
+
+def moe_forward(cfg, w, x, T, out, workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_forward(ctypes.byref(cfg), ctypes.byref(w), ptr(x), T, ptr(out),
+                             ptr(workspace), ws_bytes, stream_handle(stream)))
+
+
+def moe_forward_timed(cfg, w, x, T, out, workspace, ws_bytes, stream, events):
+    """`events`: six raw hipEvent_t handles (ints), see hip_events()."""
+    arr = (c_void_p * 6)(*events)
+    _check(lib().moe_forward_timed(ctypes.byref(cfg), ctypes.byref(w), ptr(x), T, ptr(out),
+                                   ptr(workspace), ws_bytes, stream_handle(stream), arr))
+
+
+def moe_workspace_views(cfg, workspace, ws_bytes=None) -> moe_views:
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    v = moe_views()
+    _check(lib().moe_workspace_views(ctypes.byref(cfg), ptr(workspace), ws_bytes, ctypes.byref(v)))
+    return v
+
+
+def moe_read_counts(cfg, workspace, ws_bytes=None, stream=None) -> np.ndarray:
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    out = np.zeros(cfg.n_experts, dtype=np.int32)
+    _check(lib().moe_read_counts(ctypes.byref(cfg), ptr(workspace), ws_bytes,
+                                 out.ctypes.data_as(c_void_p), stream_handle(stream)))
+    return out
+
+
+def moe_graph_capture(cfg, w, buckets, x_static, out_static, workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    b = (c_int32 * len(buckets))(*buckets)
+    g = c_void_p()
+    _check(lib().moe_graph_capture(ctypes.byref(cfg), ctypes.byref(w), b, len(buckets), ptr(x_static),
+                                   ptr(out_static), ptr(workspace), ws_bytes, stream_handle(stream),
+                                   ctypes.byref(g)))
+    return g.value
+
+
+def moe_graph_replay(graph, T, stream=None):
+    _check(lib().moe_graph_replay(graph, T, stream_handle(stream)))
+
+
+def moe_graph_bucket_for(graph, T) -> int:
+    return lib().moe_graph_bucket_for(graph, T)
+
+
+def moe_graph_destroy(graph) -> None:
+    lib().moe_graph_destroy(graph)
+
+
+# ---------------------------------------------------------------- HIP events
+_hip = None
+
+
+def _hiprt():
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [POINTER(c_void_p)]
+        h.hipEventDestroy.argtypes = [c_void_p]
+        h.hipEventSynchronize.argtypes = [c_void_p]
+        h.hipEventElapsedTime.argtypes = [POINTER(ctypes.c_float), c_void_p, c_void_p]
+        h.hipEventRecord.argtypes = [c_void_p, c_void_p]
+        _hip = h
+    return _hip
+
+
+def hip_events(n: int) -> list[int]:
+    """n raw hipEvent_t handles (caller destroys them with hip_events_destroy)."""
+    h = _hiprt()
+    out = []
+    for _ in range(n):
+        e = c_void_p()
+        if h.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        out.append(e.value)
+    return out
+
+
+def hip_event_record(ev: int, stream=None) -> None:
+    if _hiprt().hipEventRecord(ev, stream_handle(stream)) != 0:
+        raise RuntimeError("hipEventRecord failed")
+
+
+def hip_event_elapsed_ms(a: int, b: int) -> float:
+    h = _hiprt()
+    if h.hipEventSynchronize(b) != 0:
+        raise RuntimeError("hipEventSynchronize failed")
+    ms = ctypes.c_float()
+    if h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return ms.value
+
+
+def hip_events_destroy(evs) -> None:
+    h = _hiprt()
+    for e in evs:
+        h.hipEventDestroy(e)

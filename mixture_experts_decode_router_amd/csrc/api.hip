@@ -1,0 +1,439 @@
+// Host implementation of the C ABI in include/moe.h: argument validation,
+// workspace carve-up, stream-ordered launches and per-bucket hipGraphs.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "moe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// K dimension staged through LDS in at most 2048-wide chunks; each chunk must
+// be a whole number of 128-wide 4-bit blocks.
+bool k_chunks_ok(int K) {
+  const int n = (K + 2047) / 2048;
+  return K % n == 0 && (K / n) % 128 == 0;
+}
+
+struct Layout {
+  size_t ids, wts, counts, offsets, perm, pos, items, n_items, h, y, total;
+  int max_items;
+};
+
+int max_items_for(int N, int E) { return std::min(E, N) + (N + moe::kSkinnyTile - 1) / moe::kSkinnyTile; }
+
+Layout layout(const moe_config& c) {
+  Layout L{};
+  const size_t N = (size_t)c.t_max * c.top_k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = al256(off + bytes);
+    return o;
+  };
+  L.max_items = max_items_for((int)N, c.n_experts);
+  L.ids = take(N * 4);
+  L.wts = take(N * 4);
+  L.counts = take((size_t)c.n_experts * 4);
+  L.offsets = take((size_t)(c.n_experts + 1) * 4);
+  L.perm = take(N * 4);
+  L.pos = take(N * 4);
+  L.items = take((size_t)L.max_items * 8);
+  L.n_items = take(4);
+  L.h = take(N * c.inter * 2);
+  L.y = take(N * c.hidden * 4);
+  L.total = off;
+  return L;
+}
+
+moe_status check_cfg(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
+  char buf[256];
+  if (c->hidden < 128 || c->hidden > 4096 || c->hidden % 128 || !k_chunks_ok(c->hidden) ||
+      c->inter < 128 || c->inter > 4096 || c->inter % 128 || !k_chunks_ok(c->inter) ||
+      c->n_experts < 16 || c->n_experts > 256 || c->n_experts % 16 || c->top_k < 1 ||
+      c->top_k > 16 || c->top_k > c->n_experts || (c->wfmt != MOE_W_BF16 && c->wfmt != MOE_W_NF4_B64)) {
+    snprintf(buf, sizeof buf, "unsupported shape: hidden=%d inter=%d n_experts=%d top_k=%d wfmt=%d",
+             c->hidden, c->inter, c->n_experts, c->top_k, c->wfmt);
+    return fail(MOE_ERR_UNSUPPORTED, buf);
+  }
+  if (c->t_max < 1 || (long long)c->t_max * c->top_k > 65536) {
+    snprintf(buf, sizeof buf, "t_max=%d out of range (need 1 <= t_max and t_max*top_k <= 65536)", c->t_max);
+    return fail(MOE_ERR_UNSUPPORTED, buf);
+  }
+  return MOE_OK;
+}
+
+moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
+  if (!p) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned(p, align)) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned");
+  return MOE_OK;
+}
+
+#define MOE_TRY(x)                   \
+  do {                               \
+    moe_status _s = (x);             \
+    if (_s != MOE_OK) return _s;     \
+  } while (0)
+
+moe_status check_weights(const moe_config& c, const moe_weights* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  MOE_TRY(check_ptr(w->w_router, "w_router"));
+  if (w->router_bias && !aligned(w->router_bias, 4))
+    return fail(MOE_ERR_INVALID_ARG, "router_bias is not 4-byte aligned");
+  if (c.wfmt == MOE_W_BF16) {
+    MOE_TRY(check_ptr(w->w_gate_up, "w_gate_up"));
+    MOE_TRY(check_ptr(w->w_down, "w_down"));
+  } else {
+    MOE_TRY(check_ptr(w->q_gate_up, "q_gate_up"));
+    MOE_TRY(check_ptr(w->s_gate_up, "s_gate_up"));
+    MOE_TRY(check_ptr(w->q_down, "q_down"));
+    MOE_TRY(check_ptr(w->s_down, "s_down"));
+    MOE_TRY(check_ptr(w->codebook, "codebook"));
+  }
+  return MOE_OK;
+}
+
+moe_status check_T(const moe_config& c, int32_t T) {
+  if (T < 1 || T > c.t_max) {
+    char buf[128];
+    snprintf(buf, sizeof buf, "T=%d outside [1, t_max=%d]", T, c.t_max);
+    return fail(MOE_ERR_INVALID_ARG, buf);
+  }
+  return MOE_OK;
+}
+
+moe_status check_ws(const moe_config& c, const void* ws, size_t ws_bytes) {
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MOE_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const size_t need = layout(c).total;
+  if (ws_bytes < need) {
+    char buf[128];
+    snprintf(buf, sizeof buf, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    return fail(MOE_ERR_WORKSPACE, buf);
+  }
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+// Enqueues the whole block; arguments already validated.
+moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void* x, int32_t T, float* out,
+                           void* ws, hipStream_t s, hipEvent_t* ev) {
+  const Layout L = layout(c);
+  const int N = T * c.top_k;
+  hipError_t e;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  moe::RouteArgs ra{};
+  ra.x = static_cast<const uint16_t*>(x);
+  ra.wr = static_cast<const uint16_t*>(w.w_router);
+  ra.bias = w.router_bias;
+  ra.T = T;
+  ra.H = c.hidden;
+  ra.E = c.n_experts;
+  ra.k = c.top_k;
+  ra.ids = at<int32_t>(ws, L.ids);
+  ra.wts = at<float>(ws, L.wts);
+  ra.logits = nullptr;
+  if ((e = moe::launch_route(ra, s)) != hipSuccess) return hip_fail(e, "route launch");
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  moe::PermuteArgs pa{};
+  pa.ids = ra.ids;
+  pa.N = N;
+  pa.E = c.n_experts;
+  pa.tile = moe::kSkinnyTile;
+  pa.counts = at<int32_t>(ws, L.counts);
+  pa.offsets = at<int32_t>(ws, L.offsets);
+  pa.perm = at<int32_t>(ws, L.perm);
+  pa.pos = at<int32_t>(ws, L.pos);
+  pa.items = at<int32_t>(ws, L.items);
+  pa.n_items = at<int32_t>(ws, L.n_items);
+  if ((e = moe::launch_permute(pa, s)) != hipSuccess) return hip_fail(e, "permute launch");
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  moe::ExpertArgs ea{};
+  ea.counts = pa.counts;
+  ea.offsets = pa.offsets;
+  ea.perm = pa.perm;
+  ea.items = pa.items;
+  ea.n_items = pa.n_items;
+  ea.max_items = max_items_for(N, c.n_experts);
+  ea.H = c.hidden;
+  ea.I = c.inter;
+  ea.E = c.n_experts;
+  ea.k = c.top_k;
+  ea.x = ra.x;
+  ea.h = at<uint16_t>(ws, L.h);
+  ea.y = at<float>(ws, L.y);
+  ea.w_gate_up = static_cast<const uint16_t*>(w.w_gate_up);
+  ea.w_down = static_cast<const uint16_t*>(w.w_down);
+  ea.q_gate_up = w.q_gate_up;
+  ea.s_gate_up = w.s_gate_up;
+  ea.q_down = w.q_down;
+  ea.s_down = w.s_down;
+  ea.codebook = w.codebook;
+  const bool nf4 = c.wfmt == MOE_W_NF4_B64;
+  if ((e = moe::launch_gate_up(ea, nf4, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if ((e = moe::launch_down(ea, nf4, s)) != hipSuccess) return hip_fail(e, "down launch");
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+
+  moe::CombineArgs ca{};
+  ca.y = ea.y;
+  ca.wts = ra.wts;
+  ca.out = out;
+  ca.T = T;
+  ca.H = c.hidden;
+  ca.k = c.top_k;
+  if ((e = moe::launch_combine(ca, s)) != hipSuccess) return hip_fail(e, "combine launch");
+  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return MOE_OK;
+}
+
+moe_status check_forward_args(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
+                              const float* out, const void* ws, size_t ws_bytes) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_weights(*cfg, w));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(out, "out"));
+  MOE_TRY(check_ws(*cfg, ws, ws_bytes));
+  return MOE_OK;
+}
+
+}  // namespace
+
+struct moe_graph {
+  moe_config cfg;
+  std::vector<int32_t> buckets;
+  std::vector<hipGraph_t> graphs;
+  std::vector<hipGraphExec_t> execs;
+};
+
+static void graph_release(moe_graph* g) {
+  for (auto ge : g->execs)
+    if (ge) (void)hipGraphExecDestroy(ge);
+  for (auto gr : g->graphs)
+    if (gr) (void)hipGraphDestroy(gr);
+  delete g;
+}
+
+extern "C" {
+
+const char* moe_status_str(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_NOT_CAPTURABLE: return "MOE_ERR_NOT_CAPTURABLE";
+    case MOE_ERR_CAPTURE_VIOLATION: return "MOE_ERR_CAPTURE_VIOLATION";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_config_check(const moe_config* cfg) { return check_cfg(cfg); }
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  return layout(*cfg).total;
+}
+
+moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, int32_t* topk_ids,
+                     float* topk_w, float* logits, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  MOE_TRY(check_ptr(w->w_router, "w_router"));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(topk_ids, "topk_ids", 4));
+  MOE_TRY(check_ptr(topk_w, "topk_w", 4));
+  if (logits && !aligned(logits, 4)) return fail(MOE_ERR_INVALID_ARG, "logits is not 4-byte aligned");
+  moe::RouteArgs ra{};
+  ra.x = static_cast<const uint16_t*>(x);
+  ra.wr = static_cast<const uint16_t*>(w->w_router);
+  ra.bias = w->router_bias;
+  ra.T = T;
+  ra.H = cfg->hidden;
+  ra.E = cfg->n_experts;
+  ra.k = cfg->top_k;
+  ra.ids = topk_ids;
+  ra.wts = topk_w;
+  ra.logits = logits;
+  const hipError_t e = moe::launch_route(ra, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "route launch");
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_T(*cfg, T));
+  MOE_TRY(check_ptr(topk_ids, "topk_ids", 4));
+  MOE_TRY(check_ptr(counts, "counts", 4));
+  MOE_TRY(check_ptr(offsets, "offsets", 4));
+  MOE_TRY(check_ptr(perm, "perm", 4));
+  if (pos && !aligned(pos, 4)) return fail(MOE_ERR_INVALID_ARG, "pos is not 4-byte aligned");
+  moe::PermuteArgs pa{};
+  pa.ids = topk_ids;
+  pa.N = T * cfg->top_k;
+  pa.E = cfg->n_experts;
+  pa.tile = 0;
+  pa.counts = counts;
+  pa.offsets = offsets;
+  pa.perm = perm;
+  pa.pos = pos;
+  pa.items = nullptr;
+  pa.n_items = nullptr;
+  const hipError_t e = moe::launch_permute(pa, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "permute launch");
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, float* out,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_forward_args(cfg, w, x, T, out, workspace, ws_bytes));
+  return enqueue_forward(*cfg, *w, x, T, out, workspace, stream, nullptr);
+}
+
+moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, float* out,
+                             void* workspace, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
+  MOE_TRY(check_forward_args(cfg, w, x, T, out, workspace, ws_bytes));
+  if (!events) return fail(MOE_ERR_INVALID_ARG, "events is NULL");
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[i] is NULL");
+  return enqueue_forward(*cfg, *w, x, T, out, workspace, stream, events);
+}
+
+moe_status moe_workspace_views(const moe_config* cfg, void* workspace, size_t ws_bytes, moe_views* v) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_ws(*cfg, workspace, ws_bytes));
+  if (!v) return fail(MOE_ERR_INVALID_ARG, "views is NULL");
+  const Layout L = layout(*cfg);
+  v->topk_ids = at<int32_t>(workspace, L.ids);
+  v->topk_w = at<float>(workspace, L.wts);
+  v->counts = at<int32_t>(workspace, L.counts);
+  v->offsets = at<int32_t>(workspace, L.offsets);
+  v->perm = at<int32_t>(workspace, L.perm);
+  v->pos = at<int32_t>(workspace, L.pos);
+  return MOE_OK;
+}
+
+moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t ws_bytes, int32_t* host_counts,
+                           hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  MOE_TRY(check_ws(*cfg, workspace, ws_bytes));
+  if (!host_counts) return fail(MOE_ERR_INVALID_ARG, "host_counts is NULL");
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (st != hipStreamCaptureStatusNone)
+    return fail(MOE_ERR_CAPTURE_VIOLATION, "moe_read_counts synchronises and cannot run on a capturing stream");
+  const Layout L = layout(*cfg);
+  e = hipMemcpyAsync(host_counts, static_cast<const char*>(workspace) + L.counts, (size_t)cfg->n_experts * 4,
+                     hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipStreamSynchronize(stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "hipStreamSynchronize");
+}
+
+moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const int32_t* buckets, int32_t n_buckets,
+                             const void* x_static, float* out_static, void* workspace, size_t ws_bytes,
+                             hipStream_t stream, moe_graph** graph) {
+  if (!graph) return fail(MOE_ERR_INVALID_ARG, "graph out-pointer is NULL");
+  *graph = nullptr;
+  MOE_TRY(check_forward_args(cfg, w, x_static, 1, out_static, workspace, ws_bytes));
+  if (!buckets || n_buckets < 1) return fail(MOE_ERR_INVALID_ARG, "empty bucket list");
+  for (int i = 0; i < n_buckets; ++i) {
+    if (buckets[i] < 1 || buckets[i] > cfg->t_max || (i && buckets[i] <= buckets[i - 1]))
+      return fail(MOE_ERR_INVALID_ARG, "buckets must be strictly ascending within [1, t_max]");
+  }
+  if (!stream) return fail(MOE_ERR_NOT_CAPTURABLE, "capture needs a created stream, not the NULL stream");
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (st != hipStreamCaptureStatusNone) return fail(MOE_ERR_NOT_CAPTURABLE, "stream is already capturing");
+
+  moe_graph* g = new moe_graph();
+  g->cfg = *cfg;
+  for (int i = 0; i < n_buckets; ++i) {
+    const int32_t b = buckets[i];
+    e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+      graph_release(g);
+      return fail(MOE_ERR_NOT_CAPTURABLE, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+    }
+    const moe_status rs = enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr);
+    const std::string launch_msg = rs == MOE_OK ? std::string() : g_last_error;
+    hipGraph_t gr = nullptr;
+    e = hipStreamEndCapture(stream, &gr);
+    if (rs != MOE_OK || e != hipSuccess || !gr) {
+      if (gr) (void)hipGraphDestroy(gr);
+      graph_release(g);
+      return fail(MOE_ERR_NOT_CAPTURABLE,
+                  "capture of bucket " + std::to_string(b) + " failed: " +
+                      (rs != MOE_OK ? launch_msg : std::string(hipGetErrorString(e))));
+    }
+    hipGraphExec_t ge = nullptr;
+    e = hipGraphInstantiate(&ge, gr, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      (void)hipGraphDestroy(gr);
+      graph_release(g);
+      return fail(MOE_ERR_NOT_CAPTURABLE, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    }
+    g->buckets.push_back(b);
+    g->graphs.push_back(gr);
+    g->execs.push_back(ge);
+  }
+  *graph = g;
+  return MOE_OK;
+}
+
+int32_t moe_graph_bucket_for(const moe_graph* g, int32_t T) {
+  if (!g || T < 1) return -1;
+  for (int32_t b : g->buckets)
+    if (b >= T) return b;
+  return -1;
+}
+
+moe_status moe_graph_replay(moe_graph* g, int32_t T, hipStream_t stream) {
+  if (!g) return fail(MOE_ERR_INVALID_ARG, "graph is NULL");
+  for (size_t i = 0; i < g->buckets.size(); ++i) {
+    if (g->buckets[i] >= T && T >= 1) {
+      const hipError_t e = hipGraphLaunch(g->execs[i], stream);
+      return e == hipSuccess ? MOE_OK : hip_fail(e, "hipGraphLaunch");
+    }
+  }
+  return fail(MOE_ERR_INVALID_ARG, "T=" + std::to_string(T) + " exceeds the largest captured bucket");
+}
+
+void moe_graph_destroy(moe_graph* g) {
+  if (g) graph_release(g);
+}
+
+}  // extern "C"

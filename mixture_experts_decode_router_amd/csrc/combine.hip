@@ -1,0 +1,38 @@
+// Deterministic per-token combine: out[t][c] = sum_{j=0..k-1} w[t][j] * y[t*k+j][c],
+// j ascending, fp32 fused multiply-adds in a fixed order and no atomics.  It
+// takes the place of the index_add_ of the grouped MoE path (unsloth commit
+// 80aaf1121b page, third paragraph), whose float atomics make the sum order,
+// and so the result, vary from run to run.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int c = (blockIdx.y * kThreads + threadIdx.x) * 4;
+  if (c >= a.H) return;
+  const float* w = a.wts + (size_t)t * a.k;
+  const float* y = a.y + (size_t)t * a.k * a.H + c;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < a.k; ++j) {
+    const float wj = w[j];
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(y + (size_t)j * a.H);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+  }
+  *reinterpret_cast<f32x4_t*>(a.out + (size_t)t * a.H + c) = acc;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  const dim3 grid(a.T, (a.H / 4 + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// Shared device helpers for the gfx950 MoE kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA 16x16x32 operand
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;     // MFMA 16x16 accumulator
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // 16-byte load
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
+// Lane l supplies A row (l % 16) and B column (l % 16), 8 consecutive k
+// values each; the k assignment only has to agree between A and B.  Lane l
+// receives D[4*(l/16) + q][l % 16] for q = 0..3.
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Streaming (read-once) 16-byte load: non-temporal hint for weights.
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace moe

@@ -1,0 +1,69 @@
+// Host-side launchers of the gfx950 MoE kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Decode/prefill token-tile height of the skinny expert kernels: one MFMA
+// column block of 16 tokens.
+constexpr int kSkinnyTile = 16;
+
+struct RouteArgs {
+  const uint16_t* x;      // bf16 [T][H]
+  const uint16_t* wr;     // bf16 [E][H]
+  const float* bias;      // [E] or null
+  int T, H, E, k;
+  int32_t* ids;           // [T][k]
+  float* wts;             // [T][k]
+  float* logits;          // [T][E] or null
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const int32_t* ids;     // [N]
+  int N, E;
+  int tile;               // token-tile height for the work list (0: no list)
+  int32_t* counts;        // [E]
+  int32_t* offsets;       // [E+1]
+  int32_t* perm;          // [N]
+  int32_t* pos;           // [N] or null
+  int32_t* items;         // [max_items][2] = (expert, first row in its group) or null
+  int32_t* n_items;       // [1] or null
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+struct ExpertArgs {
+  // routing (device)
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* items;
+  const int32_t* n_items;
+  int max_items;          // grid bound on the work list
+  int H, I, E, k;
+  // activations
+  const uint16_t* x;      // bf16 [T][H]
+  uint16_t* h;            // bf16 [N][I]  (sorted-slot order)
+  float* y;               // fp32 [N][H]  (flat-slot order)
+  // weights
+  const uint16_t* w_gate_up;  // bf16 [E][2I][H]
+  const uint16_t* w_down;     // bf16 [E][H][I]
+  const uint8_t* q_gate_up;   // [E][2I][H/2]
+  const float* s_gate_up;     // [E][2I][H/64]
+  const uint8_t* q_down;      // [E][H][I/2]
+  const float* s_down;        // [E][H][I/64]
+  const float* codebook;      // [16]
+};
+hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, hipStream_t s);
+hipError_t launch_down(const ExpertArgs& a, bool nf4, hipStream_t s);
+
+struct CombineArgs {
+  const float* y;         // [T*k][H]
+  const float* wts;       // [T][k]
+  float* out;             // [T][H]
+  int T, H, k;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,132 @@
+"""Device-side holder of one MoE layer: weights, workspace and config, with
+methods that call the C entry points.  torch provides device memory and
+streams; every step of the block runs in the HIP library."""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    """Host array -> device tensor with the same bytes (uint16 -> int16 view)."""
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class MoELayer:
+    """One sparse-MoE layer on the GPU.
+
+    `inp` is any object with the fields H, E, k, I, wfmt, w_router, bias and
+    either (w_gate_up, w_down) bf16 bit arrays or (q_gate_up, s_gate_up,
+    q_down, s_down, codebook) 4-bit arrays (see synthetic.MoEInputs).
+    """
+
+    def __init__(self, inp, t_max: int, device: str = "cuda"):
+        self.device = torch.device(device)
+        self.H, self.E, self.k, self.I = inp.H, inp.E, inp.k, inp.I
+        self.wfmt = L.MOE_W_BF16 if inp.wfmt == "bf16" else L.MOE_W_NF4_B64
+        self.cfg = L.moe_config(inp.H, inp.I, inp.E, inp.k, t_max, self.wfmt)
+        st = L.moe_config_check(self.cfg)
+        if st != L.MOE_OK:
+            raise L.MoEError(st, L.moe_last_error())
+        self.t_max = t_max
+        self.tensors = {}
+        t = self.tensors
+        t["w_router"] = _dev(inp.w_router, self.device)
+        if inp.bias is not None:
+            t["router_bias"] = _dev(np.asarray(inp.bias, np.float32), self.device)
+        if inp.wfmt == "bf16":
+            t["w_gate_up"] = _dev(inp.w_gate_up, self.device)
+            t["w_down"] = _dev(inp.w_down, self.device)
+        else:
+            for name in ("q_gate_up", "s_gate_up", "q_down", "s_down", "codebook"):
+                t[name] = _dev(getattr(inp, name), self.device)
+        self.w = L.moe_weights(*[t[f].data_ptr() if f in t else None
+                                 for f, _ in L.moe_weights._fields_])
+        self.ws_bytes = L.moe_workspace_size(self.cfg)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.graph = None
+
+    # ------------------------------------------------------------ helpers
+    def upload_x(self, x_bits: np.ndarray) -> torch.Tensor:
+        return _dev(x_bits, self.device)
+
+    def _view(self, addr: int, n: int, dtype) -> torch.Tensor:
+        off = addr - self.workspace.data_ptr()
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return self.workspace[off:off + nbytes].view(dtype)
+
+    # ------------------------------------------------------------ entry points
+    def route(self, x: torch.Tensor, T: Optional[int] = None, with_logits: bool = False, stream=None):
+        T = T or x.shape[0]
+        ids = torch.empty(T, self.k, dtype=torch.int32, device=self.device)
+        wts = torch.empty(T, self.k, dtype=torch.float32, device=self.device)
+        logits = torch.empty(T, self.E, dtype=torch.float32, device=self.device) if with_logits else None
+        L.moe_route(self.cfg, self.w, x, T, ids, wts, logits, stream)
+        return ids, wts, logits
+
+    def permute(self, ids: torch.Tensor, T: Optional[int] = None, with_pos: bool = True, stream=None):
+        T = T or ids.shape[0]
+        n = T * self.k
+        counts = torch.empty(self.E, dtype=torch.int32, device=self.device)
+        offsets = torch.empty(self.E + 1, dtype=torch.int32, device=self.device)
+        perm = torch.empty(n, dtype=torch.int32, device=self.device)
+        pos = torch.empty(n, dtype=torch.int32, device=self.device) if with_pos else None
+        L.moe_permute(self.cfg, ids, T, counts, offsets, perm, pos, stream)
+        return counts, offsets, perm, pos
+
+    def forward(self, x: torch.Tensor, T: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+        T = T or x.shape[0]
+        if out is None:
+            out = torch.empty(T, self.H, dtype=torch.float32, device=self.device)
+        L.moe_forward(self.cfg, self.w, x, T, out, self.workspace, self.ws_bytes, stream)
+        return out
+
+    def forward_timed(self, x: torch.Tensor, out: torch.Tensor, events, T: Optional[int] = None,
+                      stream=None) -> None:
+        L.moe_forward_timed(self.cfg, self.w, x, T or x.shape[0], out, self.workspace, self.ws_bytes,
+                            stream, events)
+
+    def views(self, T: int) -> dict:
+        """Routing arrays a forward / replay wrote into the workspace (device tensors)."""
+        v = L.moe_workspace_views(self.cfg, self.workspace, self.ws_bytes)
+        n = T * self.k
+        return dict(
+            ids=self._view(v.topk_ids, n, torch.int32).view(T, self.k),
+            w=self._view(v.topk_w, n, torch.float32).view(T, self.k),
+            counts=self._view(v.counts, self.E, torch.int32),
+            offsets=self._view(v.offsets, self.E + 1, torch.int32),
+            perm=self._view(v.perm, n, torch.int32),
+            pos=self._view(v.pos, n, torch.int32),
+        )
+
+    def read_counts(self, stream=None) -> np.ndarray:
+        return L.moe_read_counts(self.cfg, self.workspace, self.ws_bytes, stream)
+
+    # ------------------------------------------------------------ graphs
+    def capture(self, buckets: Sequence[int], x_static: torch.Tensor, out_static: torch.Tensor,
+                stream) -> int:
+        self.release_graph()
+        self.graph = L.moe_graph_capture(self.cfg, self.w, list(buckets), x_static, out_static,
+                                         self.workspace, self.ws_bytes, stream)
+        return self.graph
+
+    def replay(self, T: int, stream=None) -> None:
+        L.moe_graph_replay(self.graph, T, stream)
+
+    def release_graph(self) -> None:
+        if self.graph is not None:
+            L.moe_graph_destroy(self.graph)
+            self.graph = None
+
+    def __del__(self):
+        try:
+            self.release_graph()
+        except Exception:
+            pass

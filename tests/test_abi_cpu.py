@@ -1,0 +1,163 @@
+"""The C-ABI library loads on a CPU-only machine, exports every entry point
+include/moe.h declares, and rejects bad arguments on the host before any
+launch (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_decode_router_amd as pkg
+from mixture_experts_decode_router_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert len(declared) >= 14
+    assert sorted(L.EXPORTS) == declared
+    lib = pkg.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)", out))
+    assert set(declared) <= exported
+
+
+def test_status_strings():
+    names = {L.MOE_OK: "MOE_OK", L.MOE_ERR_INVALID_ARG: "MOE_ERR_INVALID_ARG",
+             L.MOE_ERR_UNSUPPORTED: "MOE_ERR_UNSUPPORTED", L.MOE_ERR_WORKSPACE: "MOE_ERR_WORKSPACE",
+             L.MOE_ERR_NOT_CAPTURABLE: "MOE_ERR_NOT_CAPTURABLE",
+             L.MOE_ERR_CAPTURE_VIOLATION: "MOE_ERR_CAPTURE_VIOLATION", L.MOE_ERR_HIP: "MOE_ERR_HIP"}
+    for code, name in names.items():
+        assert L.moe_status_str(code) == name
+    assert L.moe_status_str(99) == "MOE_ERR_UNKNOWN"
+
+
+QWEN = dict(hidden=2048, inter=768, n_experts=128, top_k=8)
+
+
+def cfg(**kw):
+    d = dict(QWEN, t_max=64, wfmt=L.MOE_W_BF16)
+    d.update(kw)
+    return L.moe_config(d["hidden"], d["inter"], d["n_experts"], d["top_k"], d["t_max"], d["wfmt"])
+
+
+def test_workspace_size_layout():
+    c = cfg()
+    n = 64 * 8
+    items = 128 + n // 16
+    al = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    expect = (al(n * 4) * 4 + al(128 * 4) + al(129 * 4) + al(items * 8) + al(4)
+              + al(n * 768 * 2) + al(n * 2048 * 4))
+    assert L.moe_workspace_size(c) == expect
+    assert L.moe_workspace_size(cfg(hidden=2000)) == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=2000), dict(hidden=64), dict(hidden=8192), dict(inter=100), dict(n_experts=24),
+    dict(n_experts=512), dict(top_k=0), dict(top_k=17), dict(n_experts=16, top_k=17),
+    dict(t_max=0), dict(t_max=8193, top_k=8), dict(wfmt=7),
+])
+def test_unsupported_configs(bad):
+    assert L.moe_config_check(cfg(**bad)) == L.MOE_ERR_UNSUPPORTED
+    assert L.moe_last_error()
+
+
+def test_supported_configs():
+    for c in (cfg(), cfg(hidden=256, inter=128, n_experts=16, top_k=2), cfg(hidden=4096, inter=1536),
+              cfg(n_experts=256, top_k=16, t_max=4096), cfg(wfmt=L.MOE_W_NF4_B64)):
+        assert L.moe_config_check(c) == L.MOE_OK, L.moe_last_error()
+
+
+FAKE = 1 << 32  # aligned, never dereferenced: validation fails before any launch
+
+
+def weights(**kw):
+    d = dict(w_router=FAKE, router_bias=None, w_gate_up=FAKE, w_down=FAKE)
+    d.update(kw)
+    return L.moe_weights(d["w_router"], d["router_bias"], d["w_gate_up"], d["w_down"],
+                         None, None, None, None, None)
+
+
+def forward_status(c=None, w=None, x=FAKE, T=8, out=FAKE, ws=FAKE, ws_bytes=None):
+    c = c or cfg()
+    w = w or weights()
+    if ws_bytes is None:
+        ws_bytes = L.moe_workspace_size(c)
+    return L.lib().moe_forward(ctypes.byref(c), ctypes.byref(w), x, T, out, ws, ws_bytes, None)
+
+
+def test_forward_argument_validation():
+    assert forward_status(T=0) == L.MOE_ERR_INVALID_ARG
+    assert forward_status(T=65) == L.MOE_ERR_INVALID_ARG
+    assert "T=65" in L.moe_last_error()
+    assert forward_status(x=None) == L.MOE_ERR_INVALID_ARG
+    assert forward_status(x=FAKE + 2) == L.MOE_ERR_INVALID_ARG
+    assert forward_status(out=None) == L.MOE_ERR_INVALID_ARG
+    assert forward_status(w=weights(w_down=None)) == L.MOE_ERR_INVALID_ARG
+    assert forward_status(w=weights(w_router=FAKE + 8)) == L.MOE_ERR_INVALID_ARG
+    assert forward_status(w=weights(router_bias=FAKE + 2)) == L.MOE_ERR_INVALID_ARG
+    assert forward_status(ws=FAKE + 16) == L.MOE_ERR_INVALID_ARG
+    assert forward_status(ws_bytes=1024) == L.MOE_ERR_WORKSPACE
+    assert forward_status(c=cfg(hidden=100)) == L.MOE_ERR_UNSUPPORTED
+    nf4 = cfg(wfmt=L.MOE_W_NF4_B64)
+    assert forward_status(c=nf4) == L.MOE_ERR_INVALID_ARG  # 4-bit pointers missing
+    assert "q_gate_up" in L.moe_last_error()
+
+
+def test_route_permute_validation():
+    c = cfg()
+    w = weights()
+    lib = L.lib()
+    assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 0, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 8, None, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(c), None, FAKE, 8, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(c), FAKE, 8, FAKE, None, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(c), FAKE, 100, FAKE, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_graph_capture_validation_on_host():
+    c = cfg()
+    w = weights()
+    lib = L.lib()
+    g = ctypes.c_void_p()
+    ws_bytes = L.moe_workspace_size(c)
+
+    def cap(buckets, stream=FAKE):
+        b = (ctypes.c_int32 * len(buckets))(*buckets)
+        return lib.moe_graph_capture(ctypes.byref(c), ctypes.byref(w), b, len(buckets), FAKE, FAKE, FAKE,
+                                     ws_bytes, stream, ctypes.byref(g))
+
+    assert cap([1, 2, 2]) == L.MOE_ERR_INVALID_ARG
+    assert cap([4, 2]) == L.MOE_ERR_INVALID_ARG
+    assert cap([1, 128]) == L.MOE_ERR_INVALID_ARG
+    assert cap([]) == L.MOE_ERR_INVALID_ARG
+    # the NULL stream cannot be captured: refused, caller runs eagerly
+    assert cap([1, 2, 4, 8], stream=None) == L.MOE_ERR_NOT_CAPTURABLE
+    assert g.value is None
+    assert lib.moe_graph_replay(None, 1, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_graph_bucket_for(None, 1) == -1
+    lib.moe_graph_destroy(None)
+
+
+def test_workspace_views_are_host_arithmetic():
+    c = cfg()
+    ws = 1 << 33
+    v = L.moe_workspace_views(c, ws, L.moe_workspace_size(c))
+    n = 64 * 8
+    assert v.topk_ids == ws
+    assert v.topk_w == ws + n * 4
+    assert v.counts == ws + 2 * n * 4
+    assert v.offsets == v.counts + 512
+    assert v.perm == v.offsets + 768
+    assert v.pos == v.perm + n * 4

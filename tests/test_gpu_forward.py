@@ -1,0 +1,112 @@
+"""Whole-block parity (HIP vs fp64 oracle): routing arrays in the workspace
+bit-exact, outputs within max|err| <= 2e-2 * rms (bf16 weights) or
+5e-2 * rms (4-bit weights, oracle on the same dequantised weights)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+from mixture_experts_decode_router_amd.layer import MoELayer
+from tests.gpu_util import TOL_BF16, TOL_NF4, layer, oracle_forward, rel_err, say, workload
+
+pytestmark = pytest.mark.gpu
+
+LAYER_OF = {"tiny": ("tiny", 64), "q8": ("q64", 64), "q64": ("q64", 64), "q48q": ("q48q", 64),
+            "q4096": ("q4096", 4096)}
+
+
+def run_forward(lay, x_bits):
+    x = lay.upload_x(x_bits)
+    out = lay.forward(x)
+    torch.cuda.synchronize()
+    return out, lay.views(x_bits.shape[0])
+
+
+def check_views(views, ref):
+    assert np.array_equal(views["ids"].cpu().numpy(), ref["ids"])
+    assert np.array_equal(views["counts"].cpu().numpy(), ref["counts"])
+    assert np.array_equal(views["offsets"].cpu().numpy(), ref["offsets"])
+    assert np.array_equal(views["perm"].cpu().numpy(), ref["perm"])
+    assert np.array_equal(views["pos"].cpu().numpy(), ref["pos"])
+    np.testing.assert_allclose(views["w"].cpu().numpy(), ref["w"], rtol=3e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("name", ["tiny", "q8", "q64", "q48q", "q4096"])
+def test_forward_matches_oracle(name):
+    inp = workload(name)
+    lay = layer(*LAYER_OF[name])
+    say(f"[gpu] forward {name} T={inp.T} wfmt={inp.wfmt}")
+    out, views = run_forward(lay, inp.x)
+    ref_out, ref = oracle_forward(name)
+    check_views(views, ref)
+    err = rel_err(out.cpu().numpy(), ref_out)
+    tol = TOL_NF4 if inp.wfmt == "nf4" else TOL_BF16
+    say(f"[gpu]   max|err|/rms = {err:.3e} (tolerance {tol})")
+    assert err <= tol
+
+
+@pytest.mark.parametrize("T", list(S.SWEEP_T))
+def test_forward_decode_sweep(T):
+    inp = workload("q64", T)
+    say(f"[gpu] forward sweep T={T}")
+    out, views = run_forward(layer("q64", 64), inp.x)
+    ref_out, ref = oracle_forward("q64", T)
+    check_views(views, ref)
+    assert rel_err(out.cpu().numpy(), ref_out) <= TOL_BF16
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=1, H=256, E=16, k=2, I=128, wfmt="bf16"),
+    dict(T=17, H=256, E=16, k=16, I=128, wfmt="bf16"),     # k = E: every expert
+    dict(T=33, H=512, E=32, k=1, I=256, wfmt="bf16"),      # k = 1
+    dict(T=40, H=4096, E=16, k=4, I=384, wfmt="bf16"),     # two LDS chunks along H
+    dict(T=50, H=1024, E=32, k=4, I=2560, wfmt="bf16"),    # two LDS chunks along I
+    dict(T=37, H=512, E=32, k=4, I=256, wfmt="nf4"),
+    dict(T=21, H=4096, E=16, k=3, I=2560, wfmt="nf4"),     # 4-bit, two chunks each way
+    dict(T=300, H=256, E=16, k=2, I=128, wfmt="bf16"),     # many rows per expert (several items)
+])
+def test_forward_edge_shapes(case):
+    inp = S.make_small(case["T"], case["H"], case["E"], case["k"], case["I"], seed=case["T"],
+                       wfmt=case["wfmt"], bias=case["k"] == 4)
+    say(f"[gpu] forward edge {case}")
+    lay = MoELayer(inp, t_max=case["T"])
+    out, views = run_forward(lay, inp.x)
+    ref_out, ref = O.forward_batched(inp)
+    check_views(views, ref)
+    tol = TOL_NF4 if case["wfmt"] == "nf4" else TOL_BF16
+    err = rel_err(out.cpu().numpy(), ref_out)
+    say(f"[gpu]   max|err|/rms = {err:.3e}")
+    assert err <= tol
+
+
+def test_forward_zero_input_gives_zero():
+    inp = workload("q64")
+    lay = layer("q64", 64)
+    say("[gpu] forward zero input")
+    out, views = run_forward(lay, np.zeros((7, inp.H), dtype=np.uint16))
+    assert torch.count_nonzero(out) == 0
+    assert (views["ids"].cpu().numpy() == np.arange(inp.k)).all()
+
+
+def test_forward_deterministic_and_row_independent():
+    inp = workload("q64")
+    lay = layer("q64", 64)
+    say("[gpu] forward determinism / row permutation")
+    x = lay.upload_x(inp.x)
+    a = lay.forward(x).clone()
+    for _ in range(5):
+        assert torch.equal(lay.forward(x), a)
+    rng = np.random.default_rng(4)
+    p = rng.permutation(inp.T)
+    b = lay.forward(lay.upload_x(inp.x[p]))
+    assert torch.equal(b, a[torch.from_numpy(p).cuda()])
+
+
+def test_forward_row_subset_is_bit_identical():
+    """A token's output does not depend on which other tokens share the batch."""
+    inp = workload("q64")
+    lay = layer("q64", 64)
+    a = lay.forward(lay.upload_x(inp.x))
+    b = lay.forward(lay.upload_x(inp.x[:13]))
+    assert torch.equal(a[:13], b)

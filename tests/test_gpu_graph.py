@@ -1,0 +1,132 @@
+"""hipGraph capture per batch-size bucket: replay is bit-identical to eager
+(the captured-equals-eager invariant of the bucketed decode capture), across
+all buckets, partial buckets, re-capture, and the refusal paths."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from mixture_experts_decode_router_amd import _lib as L
+from tests.gpu_util import TOL_BF16, layer, oracle_forward, rel_err, say, workload
+
+pytestmark = pytest.mark.gpu
+
+BUCKETS = list(S.SWEEP_T)  # [1, 2, 4, 8] + 16-steps up to 64
+
+
+@pytest.fixture(scope="module")
+def captured():
+    lay = layer("q64", 64)
+    stream = torch.cuda.Stream()
+    x_static = torch.zeros(64, lay.H, dtype=torch.int16, device="cuda")
+    out_static = torch.zeros(64, lay.H, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    say("[gpu] capture 8 buckets")
+    lay.capture(BUCKETS, x_static, out_static, stream)
+    yield lay, stream, x_static, out_static
+    lay.release_graph()
+
+
+def test_bucket_choice(captured):
+    lay = captured[0]
+    assert [L.moe_graph_bucket_for(lay.graph, t) for t in (1, 2, 3, 5, 8, 9, 17, 33, 49, 64, 65)] == \
+        [1, 2, 4, 8, 8, 16, 32, 48, 64, 64, -1]
+
+
+@pytest.mark.parametrize("T", BUCKETS)
+def test_replay_equals_eager_and_oracle(captured, T):
+    lay, stream, x_static, out_static = captured
+    inp = workload("q64", T)
+    say(f"[gpu] replay bucket T={T}")
+    x = lay.upload_x(inp.x)
+    with torch.cuda.stream(stream):
+        x_static[:T].copy_(x)
+        lay.replay(T, stream)
+        eager = lay.forward(x.clone(), stream=stream)
+    stream.synchronize()
+    assert torch.equal(out_static[:T], eager)
+    ref_out, _ = oracle_forward("q64", T)
+    assert rel_err(out_static[:T].cpu().numpy(), ref_out) <= TOL_BF16
+
+
+def test_partial_bucket_rows_match_eager(captured):
+    lay, stream, x_static, out_static = captured
+    inp = workload("q64", 64)
+    T = 5
+    with torch.cuda.stream(stream):
+        x_static.copy_(lay.upload_x(inp.x))
+        lay.replay(T, stream)          # runs bucket 8 on rows 0..7
+        eager = lay.forward(lay.upload_x(inp.x[:T]), stream=stream)
+    stream.synchronize()
+    assert torch.equal(out_static[:T], eager)
+
+
+def test_replays_are_repeatable(captured):
+    lay, stream, x_static, out_static = captured
+    inp = workload("q64", 64)
+    with torch.cuda.stream(stream):
+        x_static.copy_(lay.upload_x(inp.x))
+        lay.replay(64, stream)
+        first = out_static.clone()
+        for _ in range(10):
+            lay.replay(64, stream)
+            torch.cuda.current_stream().synchronize()
+            assert torch.equal(out_static, first)
+    stream.synchronize()
+
+
+def test_replay_beyond_largest_bucket_is_rejected(captured):
+    lay, stream, _, _ = captured
+    with pytest.raises(L.MoEError) as e:
+        lay.replay(65, stream)
+    assert e.value.status == L.MOE_ERR_INVALID_ARG
+
+
+def test_recapture_after_destroy():
+    lay = layer("q64", 64)
+    inp = workload("q64", 8)
+    stream = torch.cuda.Stream()
+    xs = torch.zeros(64, lay.H, dtype=torch.int16, device="cuda")
+    os_ = torch.zeros(64, lay.H, dtype=torch.float32, device="cuda")
+    for rnd in range(2):
+        g = L.moe_graph_capture(lay.cfg, lay.w, [8, 64], xs, os_, lay.workspace, lay.ws_bytes, stream)
+        with torch.cuda.stream(stream):
+            xs[:8].copy_(lay.upload_x(inp.x))
+            L.moe_graph_replay(g, 8, stream)
+            eager = lay.forward(lay.upload_x(inp.x), stream=stream)
+        stream.synchronize()
+        assert torch.equal(os_[:8], eager), rnd
+        L.moe_graph_destroy(g)
+
+
+def test_capture_refused_on_null_stream():
+    lay = layer("q64", 64)
+    xs = torch.zeros(64, lay.H, dtype=torch.int16, device="cuda")
+    os_ = torch.zeros(64, lay.H, dtype=torch.float32, device="cuda")
+    with pytest.raises(L.MoEError) as e:
+        L.moe_graph_capture(lay.cfg, lay.w, [1, 2], xs, os_, lay.workspace, lay.ws_bytes, 0)
+    assert e.value.status == L.MOE_ERR_NOT_CAPTURABLE
+
+
+def test_synchronising_call_refused_while_capturing():
+    lay = layer("q64", 64)
+    hip = ctypes.CDLL("libamdhip64.so")
+    stream = torch.cuda.Stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    torch.cuda.synchronize()
+    assert hip.hipStreamBeginCapture(sh, 0) == 0  # hipStreamCaptureModeGlobal
+    try:
+        with pytest.raises(L.MoEError) as e:
+            lay.read_counts(stream=stream.cuda_stream)
+        assert e.value.status == L.MOE_ERR_CAPTURE_VIOLATION
+    finally:
+        g = ctypes.c_void_p()
+        assert hip.hipStreamEndCapture(sh, ctypes.byref(g)) == 0
+        if g.value:
+            hip.hipGraphDestroy(g)
+    # and the same call works once the stream is not capturing
+    lay.forward(lay.upload_x(workload("q64", 8).x), stream=stream)
+    counts = lay.read_counts(stream=stream.cuda_stream)
+    assert counts.sum() == 8 * lay.k
