@@ -24,10 +24,9 @@
  *     surfaces at the caller's next synchronising HIP call.
  *   - Results are deterministic: the same inputs give bit-identical outputs
  *     on every run, eager or graph-replayed (no floating-point atomics).
- *   - Supported shapes: hidden % 64 == 0 and 64 <= hidden <= 4096;
- *     inter % 64 == 0 and 64 <= inter <= 4096; n_experts % 16 == 0 and
- *     16 <= n_experts <= 256; 1 <= top_k <= min(n_experts, 16);
- *     1 <= t_max and t_max * top_k <= 65536.  Other shapes return
+ *   - Supported shapes: hidden and inter multiples of 128 in [128, 4096];
+ *     n_experts a multiple of 16 in [16, 256]; 1 <= top_k <= min(n_experts,
+ *     16); 1 <= t_max and t_max * top_k <= 65536.  Other shapes return
  *     MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_MI355X_H
@@ -120,18 +119,24 @@ size_t moe_workspace_size(const moe_config* cfg);
  * the top-k experts per token (largest logit first, equal logits -> lower
  * expert index) and their renormalised softmax weights
  * w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0).
- * The k chosen experts and their order are decided on the correctly rounded
- * fp32 logits (each candidate's dot product is re-formed in fp64).
+ * The k chosen experts and their order are those of the correctly rounded
+ * fp32 logits: an MFMA pass gives each logit with a proven error bound, and
+ * whenever the bound leaves the set or the order open, the candidates' dot
+ * products are re-formed in fp64 and rounded.  The weights use the logits
+ * the decision was taken on (exact, or within the bound when no
+ * re-formation was needed).
  *   x         bf16 [T][H]
  *   topk_ids  int32 [T][k]   (out)
  *   topk_w    fp32  [T][k]   (out)
- *   logits    fp32  [T][E]   (out, nullable): exact for the candidates of
- *             each token, within a stated error bound for the others.
+ *   logits    fp32  [T][E]   (out, nullable): the values described above,
+ *             within the error bound of the exact fp32 logits.
+ *   workspace >= moe_workspace_size(cfg) bytes (partial-logit scratch).
  * Defined by the router step of the grouped_mm path (unsloth commit
  * 80aaf1121b page, third paragraph; router fusion on the unsloth commit
  * a1bc5cbd page, first paragraph). */
 moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
-                     int32_t* topk_ids, float* topk_w, float* logits, hipStream_t stream);
+                     int32_t* topk_ids, float* topk_w, float* logits, void* workspace,
+                     size_t ws_bytes, hipStream_t stream);
 
 /* Bucketing of the T*k token-expert slots s = t*k + j by expert, with no
  * host synchronisation (the capture-safe replacement for bincount described
@@ -142,8 +147,8 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x,
  *                 ascending expert order, ascending s inside a group
  *                 (a stable argsort of the flat ids)           int32 [T*k]
  *   pos[s]      = p with perm[p] = s (nullable)                int32 [T*k]
- * topk_ids values must lie in [0, E); out-of-range ids are not counted and
- * leave perm/pos entries unspecified (memory-safe). */
+ * topk_ids values must lie in [0, E); an out-of-range id is clamped into
+ * that range (the call stays memory-safe, its results are then unspecified). */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T,
                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
                        hipStream_t stream);

@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         "moe_config_check": (S, [POINTER(moe_config)]),
         "moe_workspace_size": (c_size_t, [POINTER(moe_config)]),
         "moe_route": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
-                          c_void_p, c_void_p, c_void_p, c_void_p]),
+                          c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_permute": (S, [POINTER(moe_config), c_void_p, c_int32, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_void_p]),
         "moe_forward": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
@@ -145,9 +145,11 @@ def moe_workspace_size(cfg: moe_config) -> int:
     return lib().moe_workspace_size(ctypes.byref(cfg))
 
 
-def moe_route(cfg, w, x, T, topk_ids, topk_w, logits=None, stream=None):
+def moe_route(cfg, w, x, T, topk_ids, topk_w, logits, workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_route(ctypes.byref(cfg), ctypes.byref(w), ptr(x), T, ptr(topk_ids),
-                           ptr(topk_w), ptr(logits), stream_handle(stream)))
+                           ptr(topk_w), ptr(logits), ptr(workspace), ws_bytes, stream_handle(stream)))
 
 
 def moe_permute(cfg, topk_ids, T, counts, offsets, perm, pos=None, stream=None):

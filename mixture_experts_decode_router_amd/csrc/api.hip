@@ -26,15 +26,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// K dimension staged through LDS in at most 2048-wide chunks; each chunk must
-// be a whole number of 128-wide 4-bit blocks.
-bool k_chunks_ok(int K) {
-  const int n = (K + 2047) / 2048;
-  return K % n == 0 && (K / n) % 128 == 0;
-}
-
 struct Layout {
-  size_t ids, wts, counts, offsets, perm, pos, items, n_items, h, y, total;
+  size_t ids, wts, counts, offsets, perm, pos, items, n_items, route, h, y, total;
   int max_items;
 };
 
@@ -58,6 +51,7 @@ Layout layout(const moe_config& c) {
   L.pos = take(N * 4);
   L.items = take((size_t)L.max_items * 8);
   L.n_items = take(4);
+  L.route = take(moe::route_scratch_floats(c.t_max, c.n_experts, c.hidden) * 4);
   L.h = take(N * c.inter * 2);
   L.y = take(N * c.hidden * 4);
   L.total = off;
@@ -67,8 +61,8 @@ Layout layout(const moe_config& c) {
 moe_status check_cfg(const moe_config* c) {
   if (!c) return fail(MOE_ERR_INVALID_ARG, "cfg is NULL");
   char buf[256];
-  if (c->hidden < 128 || c->hidden > 4096 || c->hidden % 128 || !k_chunks_ok(c->hidden) ||
-      c->inter < 128 || c->inter > 4096 || c->inter % 128 || !k_chunks_ok(c->inter) ||
+  if (c->hidden < 128 || c->hidden > 4096 || c->hidden % 128 ||
+      c->inter < 128 || c->inter > 4096 || c->inter % 128 ||
       c->n_experts < 16 || c->n_experts > 256 || c->n_experts % 16 || c->top_k < 1 ||
       c->top_k > 16 || c->top_k > c->n_experts || (c->wfmt != MOE_W_BF16 && c->wfmt != MOE_W_NF4_B64)) {
     snprintf(buf, sizeof buf, "unsupported shape: hidden=%d inter=%d n_experts=%d top_k=%d wfmt=%d",
@@ -158,7 +152,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ra.ids = at<int32_t>(ws, L.ids);
   ra.wts = at<float>(ws, L.wts);
   ra.logits = nullptr;
-  if ((e = moe::launch_route(ra, s)) != hipSuccess) return hip_fail(e, "route launch");
+  if ((e = moe::launch_route(ra, at<float>(ws, L.route), s)) != hipSuccess) return hip_fail(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   moe::PermuteArgs pa{};
@@ -267,15 +261,18 @@ size_t moe_workspace_size(const moe_config* cfg) {
 }
 
 moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, int32_t* topk_ids,
-                     float* topk_w, float* logits, hipStream_t stream) {
+                     float* topk_w, float* logits, void* workspace, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   MOE_TRY(check_ptr(w->w_router, "w_router"));
+  if (w->router_bias && !aligned(w->router_bias, 4))
+    return fail(MOE_ERR_INVALID_ARG, "router_bias is not 4-byte aligned");
   MOE_TRY(check_T(*cfg, T));
   MOE_TRY(check_ptr(x, "x"));
   MOE_TRY(check_ptr(topk_ids, "topk_ids", 4));
   MOE_TRY(check_ptr(topk_w, "topk_w", 4));
   if (logits && !aligned(logits, 4)) return fail(MOE_ERR_INVALID_ARG, "logits is not 4-byte aligned");
+  MOE_TRY(check_ws(*cfg, workspace, ws_bytes));
   moe::RouteArgs ra{};
   ra.x = static_cast<const uint16_t*>(x);
   ra.wr = static_cast<const uint16_t*>(w->w_router);
@@ -287,7 +284,7 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x,
   ra.ids = topk_ids;
   ra.wts = topk_w;
   ra.logits = logits;
-  const hipError_t e = moe::launch_route(ra, stream);
+  const hipError_t e = moe::launch_route(ra, at<float>(workspace, layout(*cfg).route), stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "route launch");
 }
 

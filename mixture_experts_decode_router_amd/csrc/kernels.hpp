@@ -18,7 +18,9 @@ struct RouteArgs {
   float* wts;             // [T][k]
   float* logits;          // [T][E] or null
 };
-hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// scratch: route_scratch_floats(t_max, E, H) floats of device memory
+hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s);
+size_t route_scratch_floats(int t_max, int E, int H);
 
 struct PermuteArgs {
   const int32_t* ids;     // [N]

@@ -1,26 +1,32 @@
 // Router for gfx950: logits -> top-k (ties to the lower expert index) ->
-// renormalised softmax weights, one fused kernel per 16-token tile.
+// renormalised softmax weights.
 //
 // The block's router is a linear map to fp32 logits followed by softmax,
 // top-k and renormalisation; its pointwise tail is what the compiled walker
 // fused (unsloth commit a1bc5cbd page, first paragraph).  The decision (which
 // k experts, in which order) is taken on the correctly rounded fp32 logit of
-// each expert, so that it is reproducible bit for bit:
+// each expert, so that it is reproducible bit for bit.  Two kernels:
 //
-//   phase 1  bf16 MFMA (fp32 accumulate) gives an approximate logit a[t][e]
-//            and, from the same operands with the sign bits cleared,
-//            S[t][e] = sum_h |x_h * w_h|.  The fp32 accumulation error of a
-//            chain of d additions is at most d * 2^-24 * S, so
-//            |a - l| <= beta = gamma * S + (rounding of the fp32 result and
-//            of the bias add), gamma covering the longest chain with a
-//            factor-2 margin.
-//   phase 2  one wave per token.  Let L be the k-th largest lower bound
-//            a - beta.  Any expert with a + beta < L is beaten strictly by k
-//            others, so the true top-k lies within C = {e : a + beta >= L}
-//            (usually k or k+1 experts).  Each candidate's dot product is
-//            re-formed in fp64 from the exact bf16 products and rounded to
-//            fp32 (plus the fp32 bias); the top-k of C by (value desc,
-//            index asc) is the top-k of all experts.
+//   route_partial  bf16 MFMA (fp32 accumulate) over a K slice: partial
+//            approximate logits a and, from the same operands with the sign
+//            bits cleared, partial S = sum_h |x_h * w_h|.  The grid is
+//            (16-token tiles) x (K splits), so at decode sizes the router
+//            weights are read by many CUs in parallel instead of by a few.
+//   route_select  one wave per token.  Partials are summed in split order.
+//            An fp32 sum along a chain of d additions errs by at most
+//            d * 2^-24 * S, so |a - l| <= beta = gamma * S + (rounding of the
+//            fp32 result and of the bias add), gamma covering the longest
+//            chain with a factor-2 margin.  L = k-th largest lower bound
+//            a - beta (a ballot radix select over order-preserving keys).
+//            Any expert with a + beta < L is beaten strictly by k others, so
+//            the true top-k lies within C = {e : a + beta >= L}.  If |C| = k
+//            and the k intervals [a - beta, a + beta], sorted by a, are
+//            pairwise disjoint, both the set and its order are certain and
+//            the approximate logits are used as they are.  Otherwise every
+//            candidate's dot product is re-formed in fp64 from the exact
+//            bf16 products, rounded to fp32 (plus the fp32 bias), and the
+//            top-k of C by (value desc, index asc) is taken: the top-k of
+//            all experts.
 //
 // Softmax weights w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), fp32, j in
 // selection order (equal to the full softmax renormalised over the top k).
@@ -33,29 +39,87 @@
 namespace moe {
 namespace {
 
-constexpr int kTok = 16;        // tokens per workgroup (one MFMA column block)
-constexpr int kWaves = 8;       // 512 threads: phase-1 work items, then one wave per token
+constexpr int kTok = 16;        // MFMA column block = tokens per partial tile
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 16;
-constexpr int kPart = 256;      // ks * E <= max(E, 128) partial rows per token in LDS
+constexpr int kMaxCand = 64;    // candidates held one per lane; more -> all-expert path
+constexpr int kMaxSplit = 16;   // K splits of the partial pass
 
-struct KParams {
-  RouteArgs a;
-  int ks;         // K splits of phase 1 (items = E/16 * ks)
-  float gamma;    // relative error bound of the phase-1 accumulation
+// ------------------------------------------------------------------ partials
+struct PartParams {
+  const uint16_t* x;
+  const uint16_t* wr;
+  int T, H, E, ks;
+  float* part;   // [ks][T][E] partial logits
+  float* pabs;   // [ks][T][E] partial sums of |x*w|
 };
 
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+// Wave w owns expert tiles w, w+4, ...; every wave walks the workgroup's
+// whole K slice, so no cross-wave reduction is needed.  U k-steps of loads
+// are in flight before the MFMAs consume them.
+template <int NT, int U>  // NT: expert tiles per wave (>= ceil(E/64)); U: k-steps per batch
+__global__ __launch_bounds__(256) void route_partial(PartParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * kTok;
+  const int ks = blockIdx.y;
+  const int H = p.H, E = p.E, T = p.T;
+  const int n_et = E >> 4;
+  const int klen = H / p.ks;
+  const int kbeg = ks * klen;
+  const int trow = t0 + r;
+  const bool tv = trow < T;
+  const uint16_t* pb = p.x + (size_t)(tv ? trow : 0) * H + kbeg + g * 8;
+  const uint16_t* pa = p.wr + (size_t)(wave * 16 + r) * H + kbeg + g * 8;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const uint32_t absm = 0x7fff7fffu;
+  f32x4_t acc[NT], aab[NT];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float ov = __shfl_xor(v, off);
-    int oi = __shfl_xor(i, off);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
+  for (int i = 0; i < NT; ++i) {
+    acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    aab[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int kk = 0; kk < klen; kk += 32 * U) {
+    u32x4_t b[U], av[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      b[u] = tv ? ld16(pb + kk + 32 * u) : zero;
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        av[u][i] = (wave + 4 * i < n_et) ? ld16(pa + (size_t)i * 64 * H + kk + 32 * u) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4_t babs = b[u] & absm;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        acc[i] = mfma16(av[u][i], b[u], acc[i]);
+        aab[i] = mfma16(av[u][i] & absm, babs, aab[i]);
+      }
     }
   }
+  // lane holds D[4g+q][r]: expert 16*(wave + 4i) + 4g + q, token r
+  if (tv) {
+    float* dl = p.part + ((size_t)ks * T + trow) * E;
+    float* ds = p.pabs + ((size_t)ks * T + trow) * E;
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      if (wave + 4 * i < n_et) {
+        const int e0 = 16 * (wave + 4 * i) + 4 * g;
+        *reinterpret_cast<f32x4_t*>(dl + e0) = acc[i];
+        *reinterpret_cast<f32x4_t*>(ds + e0) = aab[i];
+      }
+  }
 }
+
+// ------------------------------------------------------------------ select
+struct SelParams {
+  RouteArgs a;
+  const float* part;
+  const float* pabs;
+  int ks;
+  float gamma;
+};
 
 // Butterfly sum: partners add the same two values, so every lane ends with
 // the bit-identical total.
@@ -74,238 +138,312 @@ __device__ __forceinline__ double dot8_f64(u32x4_t xa, u32x4_t wa, double s) {
   return s;
 }
 
-template <int CH>  // 16-byte chunks per lane covering one row: ceil(H / 512)
-__global__ __launch_bounds__(512) void route_kernel(KParams P) {
-  __shared__ float s_l[kPart * kTok];
-  __shared__ float s_s[kPart * kTok];
-  __shared__ float s_selv[kTok * kMaxK];
-  __shared__ int s_sele[kTok * kMaxK];
-  const RouteArgs& a = P.a;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kTok;
-  const int H = a.H, E = a.E, T = a.T, k = a.k;
-  const int n_et = E >> 4;
-  const int ks_n = P.ks;
+// key f beats key e: larger value, or equal value and lower index
+__device__ __forceinline__ int beats(float vf, int f, float ve, int e) {
+  return (vf > ve || (vf == ve && f < e)) ? 1 : 0;
+}
+
+// order-preserving map float -> uint32 (larger float -> larger key)
+__device__ __forceinline__ uint32_t okey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float okey_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// exact (fp64-formed, fp32-rounded, + fp32 bias) logit of expert e for x row xr
+template <int CH>
+__device__ __forceinline__ float exact_logit(const u32x4_t (&xc)[CH], const RouteArgs& a, int e, int lane) {
+  const int nch = a.H >> 3;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-  // ---------------- phase 1: approximate logits and |x||w| sums (MFMA)
-  for (int item = wave; item < n_et * ks_n; item += kWaves) {
-    const int et = item % n_et, ks = item / n_et;
-    const int r = lane & 15, g = lane >> 4;
-    const int klen = H / ks_n;
-    const int kbeg = ks * klen;
-    const int trow = t0 + r;
-    const bool tv = trow < T;
-    const uint16_t* pa = a.wr + (size_t)(et * 16 + r) * H + kbeg + g * 8;
-    const uint16_t* pb = a.x + (size_t)(tv ? trow : 0) * H + kbeg + g * 8;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, aab = {0.f, 0.f, 0.f, 0.f};
-    const uint32_t absm = 0x7fff7fffu;
-    int kk = 0;
-    for (; kk + 32 * 16 <= klen; kk += 32 * 16) {
-      u32x4_t av[16], bv[16];
+  u32x4_t wc[CH];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        av[u] = ld16(pa + kk + u * 32);
-        bv[u] = tv ? ld16(pb + kk + u * 32) : zero;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        acc = mfma16(av[u], bv[u], acc);
-        aab = mfma16(av[u] & absm, bv[u] & absm, aab);
-      }
-    }
-    for (; kk < klen; kk += 32) {
-      u32x4_t av = ld16(pa + kk);
-      u32x4_t bv = tv ? ld16(pb + kk) : zero;
-      acc = mfma16(av, bv, acc);
-      aab = mfma16(av & absm, bv & absm, aab);
-    }
-    // lane holds D[4g+q][r]: expert et*16 + 4g + q, token r
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = (ks * kTok + r) * E + et * 16 + 4 * g + q;
-      s_l[idx] = acc[q];
-      s_s[idx] = aab[q];
-    }
+  for (int i = 0; i < CH; ++i) {
+    const int c = lane + 64 * i;
+    wc[i] = c < nch ? ld16(a.wr + (size_t)e * a.H + c * 8) : zero;
   }
-  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) s = dot8_f64(xc[i], wc[i], s);
+  s = wave_sum_f64(s);
+  float le = (float)s;
+  if (a.bias) le = le + a.bias[e];
+  return le;
+}
 
-  // ---------------- phase 2: one wave per token, kTok / kWaves tokens per wave
-  for (int tl = wave; tl < kTok; tl += kWaves) {
-  const int t = t0 + tl;
-  if (t >= T) break;
-  constexpr int M = kMaxE / 64;
+template <int M, int CH>  // M = ceil(E / 64) experts per lane; CH = ceil(H / 512) row chunks per lane
+__global__ __launch_bounds__(256) void route_select(SelParams P) {
+  __shared__ float s_v[4][kMaxCand];
+  __shared__ int s_e[4][kMaxCand];
+  __shared__ float s_lo[4][kMaxK];
+  __shared__ float s_hi[4][kMaxK];
+  __shared__ float s_selv[4][kMaxK];
+  __shared__ int s_sele[4][kMaxK];
+  __shared__ __attribute__((aligned(16))) float s_key[4][kMaxE];
+  const RouteArgs& a = P.a;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  const int T = a.T, E = a.E, k = a.k;
+
   float av[M], bd[M];
-  bool valid[M];
+  uint32_t key[M];
+  // all split partials are loaded before any is added (one round trip)
+  float pl[M][kMaxSplit], ps[M][kMaxSplit];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int e = lane + 64 * m;
-    valid[m] = e < E;
+#pragma unroll
+    for (int ks = 0; ks < kMaxSplit; ++ks) {
+      const bool ok = e < E && ks < P.ks;
+      pl[m][ks] = ok ? P.part[((size_t)ks * T + t) * E + e] : 0.f;
+      ps[m][ks] = ok ? P.pabs[((size_t)ks * T + t) * E + e] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int e = lane + 64 * m;
     av[m] = -INFINITY;
     bd[m] = 0.f;
-    if (valid[m]) {
+    key[m] = 0u;
+    if (e < E) {
       float l = 0.f, s = 0.f;
-      for (int ks = 0; ks < ks_n; ++ks) {
-        l += s_l[(ks * kTok + tl) * E + e];
-        s += s_s[(ks * kTok + tl) * E + e];
+#pragma unroll
+      for (int ks = 0; ks < kMaxSplit; ++ks) {
+        if (ks < P.ks) {
+          l += pl[m][ks];
+          s += ps[m][ks];
+        }
       }
       const float bv = a.bias ? a.bias[e] : 0.f;
       av[m] = a.bias ? l + bv : l;
       bd[m] = P.gamma * s + 2.5e-7f * (fabsf(l) + fabsf(bv)) + 1e-30f;
+      key[m] = okey(av[m] - bd[m]);
     }
   }
-
-  // k-th largest lower bound L
-  float L = -INFINITY;
-  {
-    uint32_t removed = 0;
-    for (int j = 0; j < k; ++j) {
-      float v = -INFINITY;
-      int i = INT_MAX;
+  // L = k-th largest lower bound (radix select, most significant bit first)
+  uint32_t theta = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t trial = theta | (1u << b);
+    int cnt = 0;
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int e = lane + 64 * m;
-        const float lo = av[m] - bd[m];
-        if (valid[m] && !((removed >> m) & 1u) && (lo > v || (lo == v && e < i))) {
-          v = lo;
-          i = e;
-        }
-      }
-      wave_argmax(v, i);
-      L = v;
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        if (i == lane + 64 * m) removed |= 1u << m;
-    }
+    for (int m = 0; m < M; ++m) cnt += __popcll(__ballot(key[m] >= trial));
+    if (cnt >= k) theta = trial;
   }
+  const float L = okey_inv(theta);
 
   bool cand[M];
-  float ex[M];
+  int ncand = 0;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    cand[m] = valid[m] && (av[m] + bd[m] >= L);
-    ex[m] = av[m];
-  }
-
-  // re-form each candidate's logit in fp64 from the exact products
-  const int nch = H >> 3;
-  u32x4_t xc[CH];
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = lane + 64 * i;
-    xc[i] = (c < nch) ? ld16(a.x + (size_t)t * H + c * 8) : zero;
-  }
-  constexpr int NB = CH >= 8 ? 2 : 32 / CH;  // candidates per batch (row loads in flight per lane: NB * CH)
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    uint64_t mask = __ballot(cand[m]);
-    while (mask) {
-      int eb[NB];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (mask) {
-          eb[b] = __builtin_ctzll(mask) + 64 * m;
-          mask &= mask - 1;
-        } else {
-          eb[b] = -1;
-        }
-      }
-      u32x4_t wc[NB][CH];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          const int c = lane + 64 * i;
-          wc[b][i] = (eb[b] >= 0 && c < nch) ? ld16(a.wr + (size_t)eb[b] * H + c * 8) : zero;
-        }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        double s = 0.0;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) s = dot8_f64(xc[i], wc[b][i], s);
-        s = wave_sum_f64(s);
-        if (eb[b] >= 0) {
-          float le = (float)s;
-          if (a.bias) le = le + a.bias[eb[b]];
-          if (lane == (eb[b] & 63)) ex[m] = le;
-        }
+    const int e = lane + 64 * m;
+    cand[m] = e < E && av[m] + bd[m] >= L;
+    const uint64_t mask = __ballot(cand[m]);
+    if (cand[m]) {
+      const int slot = ncand + __popcll(mask & ((1ull << lane) - 1ull));
+      if (slot < kMaxCand) {
+        s_v[wave][slot] = av[m];
+        s_e[wave][slot] = e;
       }
     }
+    ncand += __popcll(mask);
   }
+  wave_sync_lds();
 
-  // top-k of the candidates by (exact fp32 logit desc, index asc); the
-  // choices go through LDS so that lane j can emit choice j
-  float* sel_v = s_selv + tl * kMaxK;
-  int* sel_e = s_sele + tl * kMaxK;
-  {
-    uint32_t taken = 0;
-    for (int j = 0; j < k; ++j) {
-      float v = -INFINITY;
-      int i = INT_MAX;
+  const int nch = a.H >> 3;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  if (ncand <= kMaxCand) {
+    // candidate i lives in lane i
+    const bool mine = lane < ncand;
+    float cv = mine ? s_v[wave][lane] : -INFINITY;
+    const int ce = mine ? s_e[wave][lane] : INT_MAX;
+    float cb = 0.f;
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int e = lane + 64 * m;
-        if (cand[m] && !((taken >> m) & 1u) && (ex[m] > v || (ex[m] == v && e < i))) {
-          v = ex[m];
-          i = e;
+    for (int m = 0; m < M; ++m) {
+      const float bm = __shfl(bd[m], ce & 63);  // bound of expert ce (held by lane ce % 64)
+      if (mine && (ce >> 6) == m) cb = bm;
+    }
+    // approximate order and the certainty check
+    int rank = 0;
+    for (int j = 0; j < ncand; ++j) rank += beats(s_v[wave][j], s_e[wave][j], cv, ce);
+    if (mine && rank < k) {
+      s_lo[wave][rank] = cv - cb;
+      s_hi[wave][rank] = cv + cb;
+    }
+    wave_sync_lds();
+    const bool amb_pair = lane + 1 < k && s_lo[wave][lane] <= s_hi[wave][lane + 1];
+    const bool refine = ncand > k || __ballot(amb_pair) != 0ull;
+    if (refine) {
+      u32x4_t xc[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = lane + 64 * i;
+        xc[i] = c < nch ? ld16(a.x + (size_t)t * a.H + c * 8) : zero;
+      }
+      constexpr int NB = CH >= 8 ? 2 : 32 / CH;  // candidates per batch (row loads in flight: NB * CH)
+      for (int j0 = 0; j0 < ncand; j0 += NB) {
+        u32x4_t wc[NB][CH];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int ej = j0 + b < ncand ? s_e[wave][j0 + b] : -1;
+#pragma unroll
+          for (int i = 0; i < CH; ++i) {
+            const int c = lane + 64 * i;
+            wc[b][i] = (ej >= 0 && c < nch) ? ld16(a.wr + (size_t)ej * a.H + c * 8) : zero;
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (j0 + b < ncand) {
+            double sd = 0.0;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) sd = dot8_f64(xc[i], wc[b][i], sd);
+            sd = wave_sum_f64(sd);
+            float le = (float)sd;
+            if (a.bias) le = le + a.bias[s_e[wave][j0 + b]];
+            if (lane == j0 + b) cv = le;
+          }
         }
       }
-      wave_argmax(v, i);
-      if (lane == 0) {
-        sel_v[j] = v;
-        sel_e[j] = i;
-      }
+      wave_sync_lds();
+      if (mine) s_v[wave][lane] = cv;
+      wave_sync_lds();
+      rank = 0;
+      for (int j = 0; j < ncand; ++j) rank += beats(s_v[wave][j], s_e[wave][j], cv, ce);
+    }
+    if (mine && rank < k) {
+      s_selv[wave][rank] = cv;
+      s_sele[wave][rank] = ce;
+    }
+    if (a.logits) {
+      // approximate for everyone, then the candidates' final values on top
 #pragma unroll
       for (int m = 0; m < M; ++m)
-        if (i == lane + 64 * m) taken |= 1u << m;
+        if (lane + 64 * m < E) a.logits[(size_t)t * E + lane + 64 * m] = av[m];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (mine) a.logits[(size_t)t * E + ce] = cv;
+    }
+  } else {
+    // more candidates than lanes (e.g. all-equal logits): exact values for
+    // every candidate, rank over all experts
+    u32x4_t xc[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      xc[i] = c < nch ? ld16(a.x + (size_t)t * a.H + c * 8) : zero;
+    }
+    float ex[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      ex[m] = -INFINITY;
+      uint64_t mask = __ballot(cand[m]);
+      while (mask) {
+        const int bit = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        const float le = exact_logit<CH>(xc, a, bit + 64 * m, lane);
+        if (lane == bit) ex[m] = le;
+      }
+      if (lane + 64 * m < E) s_key[wave][lane + 64 * m] = ex[m];
+    }
+    wave_sync_lds();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int e = lane + 64 * m;
+      if (cand[m]) {
+        int rank = 0;
+        for (int f = 0; f < E; ++f) rank += beats(s_key[wave][f], f, ex[m], e);
+        if (rank < k) {
+          s_selv[wave][rank] = ex[m];
+          s_sele[wave][rank] = e;
+        }
+      }
+      if (a.logits && e < E) a.logits[(size_t)t * E + e] = cand[m] ? ex[m] : av[m];
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_sync_lds();
   // w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0); the sum is a butterfly over
   // lanes 0..k-1 (others add 0), the same on every run
-  const float pj = lane < k ? expf(sel_v[lane] - sel_v[0]) : 0.f;
+  const float pj = lane < k ? expf(s_selv[wave][lane] - s_selv[wave][0]) : 0.f;
   float sum = pj;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
   if (lane < k) {
-    a.ids[(size_t)t * k + lane] = sel_e[lane];
+    a.ids[(size_t)t * k + lane] = s_sele[wave][lane];
     a.wts[(size_t)t * k + lane] = pj / sum;
   }
-  if (a.logits) {
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      if (valid[m]) a.logits[(size_t)t * E + lane + 64 * m] = cand[m] ? ex[m] : av[m];
-  }
-  }  // token loop
+}
+
+template <int M>
+void launch_select(const SelParams& P, dim3 grid, hipStream_t s) {
+  const int ch = (P.a.H + 511) / 512;
+  if (ch <= 1)
+    hipLaunchKernelGGL((route_select<M, 1>), grid, dim3(256), 0, s, P);
+  else if (ch <= 2)
+    hipLaunchKernelGGL((route_select<M, 2>), grid, dim3(256), 0, s, P);
+  else if (ch <= 4)
+    hipLaunchKernelGGL((route_select<M, 4>), grid, dim3(256), 0, s, P);
+  else
+    hipLaunchKernelGGL((route_select<M, 8>), grid, dim3(256), 0, s, P);
 }
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+int route_splits(int H) {
+  // K splits of the partial-logit pass: a function of H only, so a token's
+  // approximate logits (and with them its routing weights) do not depend on
+  // the batch it is in.  Slices of >= 256 k, at most 16 splits.
   int ks = 1;
-  {
-    int lim = (16 * kWaves) / a.E;  // phase-1 items (E/16 * ks) fill the waves
-    if (a.H / 256 < lim) lim = a.H / 256;
-    while (ks * 2 <= lim) ks *= 2;
-    while (ks > 1 && (a.H % ks != 0 || (a.H / ks) % 32 != 0)) ks >>= 1;
-  }
-  // longest fp32 addition chain: 32 inside one MFMA, one per k-step, the
-  // partial sums over the splits, plus slack; doubled for margin.
-  const int depth = 32 + (a.H / ks) / 32 + ks + 8;
-  KParams P{a, ks, (float)(2.0 * depth * 5.9604644775390625e-08)};
-  const dim3 grid((a.T + kTok - 1) / kTok), block(64 * kWaves);
-  const int ch = (a.H + 511) / 512;
-  if (ch <= 1)
-    hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, P);
-  else if (ch <= 2)
-    hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, P);
-  else if (ch <= 4)
-    hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, P);
+  while (ks * 2 <= 16 && H % (ks * 2 * 256) == 0) ks *= 2;
+  return ks;
+}
+
+size_t route_scratch_floats(int t_max, int E, int H) { return 2 * (size_t)route_splits(H) * t_max * E; }
+
+template <int NT>
+void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
+  const int klen = pp.H / pp.ks;
+  if (klen % (32 * 8) == 0)
+    hipLaunchKernelGGL((route_partial<NT, 8>), grid, dim3(256), 0, s, pp);
+  else if (klen % (32 * 4) == 0)
+    hipLaunchKernelGGL((route_partial<NT, 4>), grid, dim3(256), 0, s, pp);
   else
-    hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, P);
+    hipLaunchKernelGGL((route_partial<NT, 1>), grid, dim3(256), 0, s, pp);
+}
+
+hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s) {
+  const int ks = route_splits(a.H);
+  PartParams pp{a.x, a.wr, a.T, a.H, a.E, ks, scratch, scratch + (size_t)ks * a.T * a.E};
+  const dim3 pgrid((a.T + kTok - 1) / kTok, ks);
+  const int n_et = a.E / 16;
+  if (n_et <= 4)
+    launch_partial<1>(pp, pgrid, s);
+  else if (n_et <= 8)
+    launch_partial<2>(pp, pgrid, s);
+  else if (n_et <= 12)
+    launch_partial<3>(pp, pgrid, s);
+  else
+    launch_partial<4>(pp, pgrid, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // longest fp32 addition chain: 32 inside one MFMA, one per k-step of the
+  // slice, the ks split partials, plus slack; doubled.
+  const int depth = 32 + (a.H / ks) / 32 + ks + 8;
+  SelParams sp{a, pp.part, pp.pabs, ks, (float)(2.0 * depth * 5.9604644775390625e-08)};
+  const dim3 grid((a.T + 3) / 4);
+  if (a.E <= 64)
+    launch_select<1>(sp, grid, s);
+  else if (a.E <= 128)
+    launch_select<2>(sp, grid, s);
+  else
+    launch_select<4>(sp, grid, s);
   return hipGetLastError();
 }
 

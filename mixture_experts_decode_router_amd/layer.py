@@ -67,7 +67,7 @@ class MoELayer:
         ids = torch.empty(T, self.k, dtype=torch.int32, device=self.device)
         wts = torch.empty(T, self.k, dtype=torch.float32, device=self.device)
         logits = torch.empty(T, self.E, dtype=torch.float32, device=self.device) if with_logits else None
-        L.moe_route(self.cfg, self.w, x, T, ids, wts, logits, stream)
+        L.moe_route(self.cfg, self.w, x, T, ids, wts, logits, self.workspace, self.ws_bytes, stream)
         return ids, wts, logits
 
     def permute(self, ids: torch.Tensor, T: Optional[int] = None, with_pos: bool = True, stream=None):

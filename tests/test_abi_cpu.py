@@ -57,7 +57,9 @@ def test_workspace_size_layout():
     n = 64 * 8
     items = 128 + n // 16
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
-    expect = (al(n * 4) * 4 + al(128 * 4) + al(129 * 4) + al(items * 8) + al(4)
+    # router partial logits: 8 K splits (H = 2048) x t_max x E, two arrays
+    route = 2 * 8 * 64 * 128 * 4
+    expect = (al(n * 4) * 4 + al(128 * 4) + al(129 * 4) + al(items * 8) + al(4) + al(route)
               + al(n * 768 * 2) + al(n * 2048 * 4))
     assert L.moe_workspace_size(c) == expect
     assert L.moe_workspace_size(cfg(hidden=2000)) == 0
@@ -119,9 +121,11 @@ def test_route_permute_validation():
     c = cfg()
     w = weights()
     lib = L.lib()
-    assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 0, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 8, None, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(ctypes.byref(c), None, FAKE, 8, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    wsb = L.moe_workspace_size(c)
+    assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 0, FAKE, FAKE, None, FAKE, wsb, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 8, None, FAKE, None, FAKE, wsb, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(c), None, FAKE, 8, FAKE, FAKE, None, FAKE, wsb, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 8, FAKE, FAKE, None, FAKE, 64, None) == L.MOE_ERR_WORKSPACE
     assert lib.moe_permute(ctypes.byref(c), FAKE, 8, FAKE, None, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_permute(ctypes.byref(c), FAKE, 100, FAKE, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
 

@@ -29,7 +29,7 @@ def check_views(views, ref):
     assert np.array_equal(views["offsets"].cpu().numpy(), ref["offsets"])
     assert np.array_equal(views["perm"].cpu().numpy(), ref["perm"])
     assert np.array_equal(views["pos"].cpu().numpy(), ref["pos"])
-    np.testing.assert_allclose(views["w"].cpu().numpy(), ref["w"], rtol=3e-6, atol=1e-7)
+    np.testing.assert_allclose(views["w"].cpu().numpy(), ref["w"], rtol=2e-5, atol=1e-6)
 
 
 @pytest.mark.parametrize("name", ["tiny", "q8", "q64", "q48q", "q4096"])
@@ -110,3 +110,5 @@ def test_forward_row_subset_is_bit_identical():
     a = lay.forward(lay.upload_x(inp.x))
     b = lay.forward(lay.upload_x(inp.x[:13]))
     assert torch.equal(a[:13], b)
+    c = lay.forward(lay.upload_x(inp.x[40:41]))
+    assert torch.equal(a[40:41], c)
