@@ -93,6 +93,8 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row-major", action="store_true",
+                    help="keep expert weights row-major instead of the tiled layout")
     ap.add_argument("--sweep", action="store_true", help="also time every decode bucket (stderr + JSON extra)")
     args = ap.parse_args()
 
@@ -115,7 +117,7 @@ def main():
     inp = S.make(args.workload)
     T, H, E, k, I = inp.T, inp.H, inp.E, inp.k, inp.I
     log(f"[bench] workload {args.workload}: T={T} H={H} E={E} k={k} I={I} wfmt={inp.wfmt}")
-    lay = MoELayer(inp, t_max=T)
+    lay = MoELayer(inp, t_max=T, tiled=not args.row_major)
     stream = torch.cuda.Stream()
     x_static = lay.upload_x(inp.x)
     out_static = torch.empty(T, H, dtype=torch.float32, device="cuda")
@@ -209,7 +211,9 @@ def main():
         "dtype": "bf16" if inp.wfmt == "bf16" else "nf4-b64 weights, bf16 MFMA",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations; no checkpoint)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "T": T, "hidden": H, "experts": E,
-                   "top_k": k, "inter": I, "weights": inp.wfmt, "parallelism": "single GPU"},
+                   "top_k": k, "inter": I, "weights": inp.wfmt,
+                   "weight_layout": "row-major" if args.row_major else "tiled (packed once at load, untimed)",
+                   "parallelism": "single GPU"},
         "roofline": {
             "kernel": "grouped gate/up + SiLU*up (" + ("bf16" if inp.wfmt == "bf16" else "4-bit") + ")",
             "bound": "hbm",

@@ -51,8 +51,10 @@ typedef enum {
 } moe_status;
 
 typedef enum {
-  MOE_W_BF16 = 0,     /* bf16 expert weights */
-  MOE_W_NF4_B64 = 1   /* 4-bit codes + one fp32 absmax per 64 consecutive weights */
+  MOE_W_BF16 = 0,           /* bf16 expert weights, row-major */
+  MOE_W_NF4_B64 = 1,        /* 4-bit codes + one fp32 absmax per 64 consecutive weights, row-major */
+  MOE_W_BF16_TILED = 2,     /* MOE_W_BF16 in the tiled layout written by moe_pack_weights */
+  MOE_W_NF4_B64_TILED = 3   /* MOE_W_NF4_B64 in the tiled layout written by moe_pack_weights */
 } moe_wformat;
 
 /* Shape of one MoE layer.  t_max bounds T for every call made with this
@@ -78,7 +80,8 @@ typedef struct {
  *   q_gate_up  uint8 [E][2I][H/2]    s_gate_up fp32 [E][2I][H/64]
  *   q_down     uint8 [E][H][I/2]     s_down    fp32 [E][H][I/64]
  *   codebook   fp32 [16]
- * Unused fields may be NULL. */
+ * The _TILED formats hold the same values in the layout moe_pack_weights
+ * writes (same buffer sizes).  Unused fields may be NULL. */
 typedef struct {
   const void* w_router;
   const float* router_bias;
@@ -169,6 +172,25 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
 moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x,
                              int32_t T, float* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream, hipEvent_t* events /* host, 6 */);
+
+/* One-time conversion of row-major expert weights (cfg->wfmt = MOE_W_BF16 or
+ * MOE_W_NF4_B64) into the tiled layout of MOE_W_BF16_TILED /
+ * MOE_W_NF4_B64_TILED, in which every 16-row MFMA fragment of a k-step is
+ * one contiguous kilobyte in the order the 64 lanes of a wave load it.  Per
+ * expert, for a matrix of R rows x K columns (gate/up: R = 2I, K = H; down:
+ * R = H, K = I), with rt < R/16, r < 16, g < 4:
+ *   bf16    16-byte chunk (rt*K/32 + ks)*64 + 16g + r
+ *             = W[16rt + r][32ks + 8g .. 32ks + 8g + 7]
+ *   codes   16-byte chunk (rt*K/128 + kb)*64 + 16g + r
+ *             = codes of row 16rt + r for k in [128kb + 32g, 128kb + 32g + 32)
+ *   scales  float (rt*K/128 + kb)*32 + 2r + h = absmax of row 16rt + r,
+ *             64-block 2kb + h
+ * Writes dst's expert tensors (w_gate_up, w_down; or q_gate_up, s_gate_up,
+ * q_down, s_down), caller-allocated with the source sizes and not
+ * overlapping the source; other fields of dst are not touched.  Stream
+ * ordered, no host synchronisation. */
+moe_status moe_pack_weights(const moe_config* cfg, const moe_weights* src, const moe_weights* dst,
+                            hipStream_t stream);
 
 /* Device pointers of the routing arrays inside `workspace` (pure host
  * arithmetic; nothing is read from the device). */

@@ -27,11 +27,14 @@ MOE_ERR_HIP = 6
 
 MOE_W_BF16 = 0
 MOE_W_NF4_B64 = 1
+MOE_W_BF16_TILED = 2
+MOE_W_NF4_B64_TILED = 3
 
 # every entry point include/moe.h declares
 EXPORTS = (
     "moe_status_str", "moe_last_error", "moe_config_check", "moe_workspace_size",
-    "moe_route", "moe_permute", "moe_forward", "moe_forward_timed", "moe_workspace_views",
+    "moe_route", "moe_permute", "moe_forward", "moe_forward_timed", "moe_pack_weights",
+    "moe_workspace_views",
     "moe_read_counts", "moe_graph_capture", "moe_graph_replay", "moe_graph_bucket_for",
     "moe_graph_destroy",
 )
@@ -86,6 +89,7 @@ def lib() -> ctypes.CDLL:
                             c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_forward_timed": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
                                   c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+        "moe_pack_weights": (S, [POINTER(moe_config), POINTER(moe_weights), POINTER(moe_weights), c_void_p]),
         "moe_workspace_views": (S, [POINTER(moe_config), c_void_p, c_size_t, POINTER(moe_views)]),
         "moe_read_counts": (S, [POINTER(moe_config), c_void_p, c_size_t, c_void_p, c_void_p]),
         "moe_graph_capture": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
@@ -169,6 +173,11 @@ def moe_forward_timed(cfg, w, x, T, out, workspace, ws_bytes, stream, events):
     arr = (c_void_p * 6)(*events)
     _check(lib().moe_forward_timed(ctypes.byref(cfg), ctypes.byref(w), ptr(x), T, ptr(out),
                                    ptr(workspace), ws_bytes, stream_handle(stream), arr))
+
+
+def moe_pack_weights(cfg, src, dst, stream=None):
+    _check(lib().moe_pack_weights(ctypes.byref(cfg), ctypes.byref(src), ctypes.byref(dst),
+                                  stream_handle(stream)))
 
 
 def moe_workspace_views(cfg, workspace, ws_bytes=None) -> moe_views:

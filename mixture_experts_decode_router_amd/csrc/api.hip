@@ -64,7 +64,7 @@ moe_status check_cfg(const moe_config* c) {
   if (c->hidden < 128 || c->hidden > 4096 || c->hidden % 128 ||
       c->inter < 128 || c->inter > 4096 || c->inter % 128 ||
       c->n_experts < 16 || c->n_experts > 256 || c->n_experts % 16 || c->top_k < 1 ||
-      c->top_k > 16 || c->top_k > c->n_experts || (c->wfmt != MOE_W_BF16 && c->wfmt != MOE_W_NF4_B64)) {
+      c->top_k > 16 || c->top_k > c->n_experts || c->wfmt < MOE_W_BF16 || c->wfmt > MOE_W_NF4_B64_TILED) {
     snprintf(buf, sizeof buf, "unsupported shape: hidden=%d inter=%d n_experts=%d top_k=%d wfmt=%d",
              c->hidden, c->inter, c->n_experts, c->top_k, c->wfmt);
     return fail(MOE_ERR_UNSUPPORTED, buf);
@@ -88,12 +88,15 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
     if (_s != MOE_OK) return _s;     \
   } while (0)
 
+bool is_nf4(const moe_config& c) { return c.wfmt == MOE_W_NF4_B64 || c.wfmt == MOE_W_NF4_B64_TILED; }
+bool is_tiled(const moe_config& c) { return c.wfmt == MOE_W_BF16_TILED || c.wfmt == MOE_W_NF4_B64_TILED; }
+
 moe_status check_weights(const moe_config& c, const moe_weights* w) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
   MOE_TRY(check_ptr(w->w_router, "w_router"));
   if (w->router_bias && !aligned(w->router_bias, 4))
     return fail(MOE_ERR_INVALID_ARG, "router_bias is not 4-byte aligned");
-  if (c.wfmt == MOE_W_BF16) {
+  if (!is_nf4(c)) {
     MOE_TRY(check_ptr(w->w_gate_up, "w_gate_up"));
     MOE_TRY(check_ptr(w->w_down, "w_down"));
   } else {
@@ -190,10 +193,10 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ea.q_down = w.q_down;
   ea.s_down = w.s_down;
   ea.codebook = w.codebook;
-  const bool nf4 = c.wfmt == MOE_W_NF4_B64;
-  if ((e = moe::launch_gate_up(ea, nf4, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  const bool nf4 = is_nf4(c), tiled = is_tiled(c);
+  if ((e = moe::launch_gate_up(ea, nf4, tiled, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if ((e = moe::launch_down(ea, nf4, s)) != hipSuccess) return hip_fail(e, "down launch");
+  if ((e = moe::launch_down(ea, nf4, tiled, s)) != hipSuccess) return hip_fail(e, "down launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   moe::CombineArgs ca{};
@@ -325,6 +328,53 @@ moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const 
   for (int i = 0; i < 6; ++i)
     if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[i] is NULL");
   return enqueue_forward(*cfg, *w, x, T, out, workspace, stream, events);
+}
+
+moe_status moe_pack_weights(const moe_config* cfg, const moe_weights* src, const moe_weights* dst,
+                            hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  if (cfg->wfmt != MOE_W_BF16 && cfg->wfmt != MOE_W_NF4_B64)
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_weights converts from a row-major format (MOE_W_BF16 or MOE_W_NF4_B64)");
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  moe::PackArgs pa{};
+  pa.nf4 = is_nf4(*cfg);
+  pa.E = cfg->n_experts;
+  pa.H = cfg->hidden;
+  pa.I = cfg->inter;
+  if (!pa.nf4) {
+    MOE_TRY(check_ptr(src->w_gate_up, "src w_gate_up"));
+    MOE_TRY(check_ptr(src->w_down, "src w_down"));
+    MOE_TRY(check_ptr(dst->w_gate_up, "dst w_gate_up"));
+    MOE_TRY(check_ptr(dst->w_down, "dst w_down"));
+    if (src->w_gate_up == dst->w_gate_up || src->w_down == dst->w_down)
+      return fail(MOE_ERR_INVALID_ARG, "packing cannot be done in place");
+    pa.src_gate_up = src->w_gate_up;
+    pa.src_down = src->w_down;
+    pa.dst_gate_up = const_cast<void*>(dst->w_gate_up);
+    pa.dst_down = const_cast<void*>(dst->w_down);
+  } else {
+    MOE_TRY(check_ptr(src->q_gate_up, "src q_gate_up"));
+    MOE_TRY(check_ptr(src->s_gate_up, "src s_gate_up"));
+    MOE_TRY(check_ptr(src->q_down, "src q_down"));
+    MOE_TRY(check_ptr(src->s_down, "src s_down"));
+    MOE_TRY(check_ptr(dst->q_gate_up, "dst q_gate_up"));
+    MOE_TRY(check_ptr(dst->s_gate_up, "dst s_gate_up"));
+    MOE_TRY(check_ptr(dst->q_down, "dst q_down"));
+    MOE_TRY(check_ptr(dst->s_down, "dst s_down"));
+    if (src->q_gate_up == dst->q_gate_up || src->q_down == dst->q_down || src->s_gate_up == dst->s_gate_up ||
+        src->s_down == dst->s_down)
+      return fail(MOE_ERR_INVALID_ARG, "packing cannot be done in place");
+    pa.src_gate_up = src->q_gate_up;
+    pa.src_down = src->q_down;
+    pa.src_s_gate_up = src->s_gate_up;
+    pa.src_s_down = src->s_down;
+    pa.dst_gate_up = const_cast<uint8_t*>(dst->q_gate_up);
+    pa.dst_down = const_cast<uint8_t*>(dst->q_down);
+    pa.dst_s_gate_up = const_cast<float*>(dst->s_gate_up);
+    pa.dst_s_down = const_cast<float*>(dst->s_down);
+  }
+  const hipError_t e = moe::launch_pack(pa, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "pack launch");
 }
 
 moe_status moe_workspace_views(const moe_config* cfg, void* workspace, size_t ws_bytes, moe_views* v) {

@@ -20,6 +20,11 @@
 // Rows of the 16-column block beyond the item's M rows carry zeros; output
 // column j depends only on B column j, so they never touch valid outputs.
 //
+// Weights are row-major ([E][rows][K], each 16-row MFMA fragment read as 16
+// rows x 64 B) or tiled (each fragment one contiguous kilobyte in lane
+// order, written once by the pack kernel): the tiled layout turns every wave
+// load into one contiguous 1 KiB read.
+//
 // 4-bit weights (NF4_B64): each lane loads 16 bytes = 32 codes of one row and
 // feeds four MFMA steps with them (lane group g covers k in
 // [kb + 32g, kb + 32g + 32) of a 128-k block; the activation fragment uses the
@@ -49,7 +54,7 @@ __device__ __forceinline__ bool load_item(const ExpertArgs& a, int item, Item& i
 }
 
 // ------------------------------------------------------------------ bf16
-template <int U>
+template <int U, bool TILED>
 __global__ __launch_bounds__(kThreads) void gate_up_bf16(ExpertArgs a) {
   const int ntile = a.I / 64;
   const int item = blockIdx.x / ntile, nt = blockIdx.x - item * ntile;
@@ -62,16 +67,21 @@ __global__ __launch_bounds__(kThreads) void gate_up_bf16(ExpertArgs a) {
   const bool rv = r < it.M;
   const int tok = rv ? a.perm[it.base + r] / a.k : 0;
   const uint16_t* xr = a.x + (size_t)tok * H + g * 8;
-  const uint16_t* wg = a.w_gate_up + ((size_t)it.e * 2 * I + n0 + r) * H + g * 8;
-  const uint16_t* wu = wg + (size_t)I * H;
+  // row-major: row n0 + r, k offset 8g, step 32 elements; tiled: fragment
+  // (row tile, k-step) is 512 elements, this lane's 8 at offset 8 * lane
+  const uint16_t* wg = TILED ? a.w_gate_up + (((size_t)it.e * (2 * I / 16) + n0 / 16) * (H / 32) * 64 + lane) * 8
+                             : a.w_gate_up + ((size_t)it.e * 2 * I + n0 + r) * H + g * 8;
+  const uint16_t* wu = TILED ? wg + (size_t)(I / 16) * (H / 32) * 512 : wg + (size_t)I * H;
+  const int wstep = TILED ? 512 : 32;  // elements per k-step
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   for (int kk = 0; kk < H; kk += 32 * U) {
     u32x4_t ga[U], ua[U], xb[U];
+    const size_t wo = (size_t)(kk / 32) * wstep;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      ga[u] = ld16_stream(wg + kk + u * 32);
-      ua[u] = ld16_stream(wu + kk + u * 32);
+      ga[u] = ld16_stream(wg + wo + u * wstep);
+      ua[u] = ld16_stream(wu + wo + u * wstep);
       xb[u] = rv ? ld16(xr + kk + u * 32) : zero;
     }
 #pragma unroll
@@ -90,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_bf16(ExpertArgs a) {
   }
 }
 
-template <int U>
+template <int U, bool TILED>
 __global__ __launch_bounds__(kThreads) void down_bf16(ExpertArgs a) {
   const int ctile = a.H / 128;
   const int item = blockIdx.x / ctile, ct = blockIdx.x - item * ctile;
@@ -102,16 +112,19 @@ __global__ __launch_bounds__(kThreads) void down_bf16(ExpertArgs a) {
   const int c0 = ct * 128 + wave * 32;
   const bool rv = r < it.M;
   const uint16_t* hr = a.h + (size_t)(it.base + (rv ? r : 0)) * I + g * 8;
-  const uint16_t* w0 = a.w_down + ((size_t)it.e * H + c0 + r) * I + g * 8;
-  const uint16_t* w1 = w0 + (size_t)16 * I;
+  const uint16_t* w0 = TILED ? a.w_down + (((size_t)it.e * (H / 16) + c0 / 16) * (I / 32) * 64 + lane) * 8
+                             : a.w_down + ((size_t)it.e * H + c0 + r) * I + g * 8;
+  const uint16_t* w1 = TILED ? w0 + (size_t)(I / 32) * 512 : w0 + (size_t)16 * I;
+  const int wstep = TILED ? 512 : 32;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int kk = 0; kk < I; kk += 32 * U) {
     u32x4_t a0[U], a1[U], hb[U];
+    const size_t wo = (size_t)(kk / 32) * wstep;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      a0[u] = ld16_stream(w0 + kk + u * 32);
-      a1[u] = ld16_stream(w1 + kk + u * 32);
+      a0[u] = ld16_stream(w0 + wo + u * wstep);
+      a1[u] = ld16_stream(w1 + wo + u * wstep);
       hb[u] = rv ? ld16(hr + kk + u * 32) : zero;
     }
 #pragma unroll
@@ -141,7 +154,7 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t w, float sc, const float* c
   return o;
 }
 
-template <int NB>  // 128-k blocks per loop iteration (H % (128 * NB) == 0)
+template <int NB, bool TILED>  // NB: 128-k blocks per loop iteration (H % (128 * NB) == 0)
 __global__ __launch_bounds__(kThreads) void gate_up_nf4(ExpertArgs a) {
   __shared__ float s_cb[16];
   const int ntile = a.I / 64;
@@ -157,12 +170,17 @@ __global__ __launch_bounds__(kThreads) void gate_up_nf4(ExpertArgs a) {
   const bool rv = r < it.M;
   const int tok = rv ? a.perm[it.base + r] / a.k : 0;
   const uint16_t* xr = a.x + (size_t)tok * H + 32 * g;
+  // per 128-k block kb: codes at qg + kb * qstep, scale at sg[kb * sstep]
+  const int nkb = H / 128;
   const size_t rowg = (size_t)it.e * 2 * I + n0 + r;
   const size_t rowu = rowg + I;
-  const uint8_t* qg = a.q_gate_up + rowg * (H / 2) + 16 * g;
-  const uint8_t* qu = a.q_gate_up + rowu * (H / 2) + 16 * g;
-  const float* sg = a.s_gate_up + rowg * (H / 64) + g / 2;
-  const float* su = a.s_gate_up + rowu * (H / 64) + g / 2;
+  const size_t tg = (size_t)it.e * (2 * I / 16) + n0 / 16, tu = tg + I / 16;  // row tiles
+  const uint8_t* qg = TILED ? a.q_gate_up + (tg * nkb * 64 + lane) * 16 : a.q_gate_up + rowg * (H / 2) + 16 * g;
+  const uint8_t* qu = TILED ? a.q_gate_up + (tu * nkb * 64 + lane) * 16 : a.q_gate_up + rowu * (H / 2) + 16 * g;
+  const float* sg = TILED ? a.s_gate_up + tg * nkb * 32 + 2 * r + g / 2 : a.s_gate_up + rowg * (H / 64) + g / 2;
+  const float* su = TILED ? a.s_gate_up + tu * nkb * 32 + 2 * r + g / 2 : a.s_gate_up + rowu * (H / 64) + g / 2;
+  const int qstep = TILED ? 1024 : 64;  // bytes per 128-k block
+  const int sstep = TILED ? 32 : 2;     // floats per 128-k block
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   for (int kb = 0; kb < H; kb += 128 * NB) {
@@ -171,10 +189,10 @@ __global__ __launch_bounds__(kThreads) void gate_up_nf4(ExpertArgs a) {
 #pragma unroll
     for (int h = 0; h < NB; ++h) {
       const int k0 = kb + 128 * h;
-      cg[h] = ld16_stream(qg + k0 / 2);
-      cu[h] = ld16_stream(qu + k0 / 2);
-      scg[h] = sg[k0 / 64];
-      scu[h] = su[k0 / 64];
+      cg[h] = ld16_stream(qg + (size_t)(k0 / 128) * qstep);
+      cu[h] = ld16_stream(qu + (size_t)(k0 / 128) * qstep);
+      scg[h] = sg[(k0 / 128) * sstep];
+      scu[h] = su[(k0 / 128) * sstep];
 #pragma unroll
       for (int st = 0; st < 4; ++st) xb[h][st] = rv ? ld16(xr + k0 + 8 * st) : zero;
     }
@@ -195,6 +213,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_nf4(ExpertArgs a) {
   }
 }
 
+template <bool TILED>
 __global__ __launch_bounds__(kThreads) void down_nf4(ExpertArgs a) {
   __shared__ float s_cb[16];
   const int ctile = a.H / 128;
@@ -209,18 +228,22 @@ __global__ __launch_bounds__(kThreads) void down_nf4(ExpertArgs a) {
   const int c0 = ct * 128 + wave * 32;
   const bool rv = r < it.M;
   const uint16_t* hr = a.h + (size_t)(it.base + (rv ? r : 0)) * I + 32 * g;
+  const int nkb = I / 128;
   const size_t row0 = (size_t)it.e * H + c0 + r;
   const size_t row1 = row0 + 16;
-  const uint8_t* q0 = a.q_down + row0 * (I / 2) + 16 * g;
-  const uint8_t* q1 = a.q_down + row1 * (I / 2) + 16 * g;
-  const float* s0 = a.s_down + row0 * (I / 64) + g / 2;
-  const float* s1 = a.s_down + row1 * (I / 64) + g / 2;
+  const size_t t0 = (size_t)it.e * (H / 16) + c0 / 16, t1 = t0 + 1;  // row tiles
+  const uint8_t* q0 = TILED ? a.q_down + (t0 * nkb * 64 + lane) * 16 : a.q_down + row0 * (I / 2) + 16 * g;
+  const uint8_t* q1 = TILED ? a.q_down + (t1 * nkb * 64 + lane) * 16 : a.q_down + row1 * (I / 2) + 16 * g;
+  const float* s0 = TILED ? a.s_down + t0 * nkb * 32 + 2 * r + g / 2 : a.s_down + row0 * (I / 64) + g / 2;
+  const float* s1 = TILED ? a.s_down + t1 * nkb * 32 + 2 * r + g / 2 : a.s_down + row1 * (I / 64) + g / 2;
+  const int qstep = TILED ? 1024 : 64;
+  const int sstep = TILED ? 32 : 2;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int kb = 0; kb < I; kb += 128) {
-    const u32x4_t c0v = ld16_stream(q0 + kb / 2);
-    const u32x4_t c1v = ld16_stream(q1 + kb / 2);
-    const float sc0 = s0[kb / 64], sc1 = s1[kb / 64];
+    const u32x4_t c0v = ld16_stream(q0 + (size_t)(kb / 128) * qstep);
+    const u32x4_t c1v = ld16_stream(q1 + (size_t)(kb / 128) * qstep);
+    const float sc0 = s0[(kb / 128) * sstep], sc1 = s1[(kb / 128) * sstep];
     u32x4_t hb[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) hb[st] = rv ? ld16(hr + kb + 8 * st) : zero;
@@ -249,19 +272,26 @@ hipError_t launch_u(int K, F8 f8, F4 f4, dim3 grid, hipStream_t s, const ExpertA
 
 }  // namespace
 
-hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, hipStream_t s) {
+hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
   const dim3 grid(a.max_items * (a.I / 64));
-  if (nf4) return launch_u(a.H, gate_up_nf4<2>, gate_up_nf4<1>, grid, s, a);
-  return launch_u(a.H, gate_up_bf16<8>, gate_up_bf16<4>, grid, s, a);
+  if (nf4)
+    return tiled ? launch_u(a.H, gate_up_nf4<2, true>, gate_up_nf4<1, true>, grid, s, a)
+                 : launch_u(a.H, gate_up_nf4<2, false>, gate_up_nf4<1, false>, grid, s, a);
+  return tiled ? launch_u(a.H, gate_up_bf16<8, true>, gate_up_bf16<4, true>, grid, s, a)
+               : launch_u(a.H, gate_up_bf16<8, false>, gate_up_bf16<4, false>, grid, s, a);
 }
 
-hipError_t launch_down(const ExpertArgs& a, bool nf4, hipStream_t s) {
+hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
   const dim3 grid(a.max_items * (a.H / 128));
   if (nf4) {
-    hipLaunchKernelGGL(down_nf4, grid, dim3(kThreads), 0, s, a);
+    if (tiled)
+      hipLaunchKernelGGL(down_nf4<true>, grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(down_nf4<false>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
-  return launch_u(a.I, down_bf16<8>, down_bf16<4>, grid, s, a);
+  return tiled ? launch_u(a.I, down_bf16<8, true>, down_bf16<4, true>, grid, s, a)
+               : launch_u(a.I, down_bf16<8, false>, down_bf16<4, false>, grid, s, a);
 }
 
 }  // namespace moe

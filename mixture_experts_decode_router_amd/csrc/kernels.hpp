@@ -57,8 +57,23 @@ struct ExpertArgs {
   const float* s_down;        // [E][H][I/64]
   const float* codebook;      // [16]
 };
-hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, hipStream_t s);
-hipError_t launch_down(const ExpertArgs& a, bool nf4, hipStream_t s);
+// tiled: weights in the fragment-tiled layout written by launch_pack
+hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
+hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
+
+struct PackArgs {
+  bool nf4;
+  int E, H, I;
+  const void* src_gate_up;  // bf16 [E][2I][H] or codes [E][2I][H/2]
+  const void* src_down;     // bf16 [E][H][I]  or codes [E][H][I/2]
+  const float* src_s_gate_up;
+  const float* src_s_down;
+  void* dst_gate_up;
+  void* dst_down;
+  float* dst_s_gate_up;
+  float* dst_s_down;
+};
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 
 struct CombineArgs {
   const float* y;         // [T*k][H]

@@ -26,10 +26,11 @@ class MoELayer:
     q_down, s_down, codebook) 4-bit arrays (see synthetic.MoEInputs).
     """
 
-    def __init__(self, inp, t_max: int, device: str = "cuda"):
+    def __init__(self, inp, t_max: int, device: str = "cuda", tiled: bool = True):
         self.device = torch.device(device)
         self.H, self.E, self.k, self.I = inp.H, inp.E, inp.k, inp.I
-        self.wfmt = L.MOE_W_BF16 if inp.wfmt == "bf16" else L.MOE_W_NF4_B64
+        rowmajor = L.MOE_W_BF16 if inp.wfmt == "bf16" else L.MOE_W_NF4_B64
+        self.wfmt = rowmajor + 2 if tiled else rowmajor
         self.cfg = L.moe_config(inp.H, inp.I, inp.E, inp.k, t_max, self.wfmt)
         st = L.moe_config_check(self.cfg)
         if st != L.MOE_OK:
@@ -48,6 +49,19 @@ class MoELayer:
                 t[name] = _dev(getattr(inp, name), self.device)
         self.w = L.moe_weights(*[t[f].data_ptr() if f in t else None
                                  for f, _ in L.moe_weights._fields_])
+        if tiled:
+            # convert once into the tiled layout on the device; the
+            # row-major copies are released afterwards
+            src_cfg = L.moe_config(inp.H, inp.I, inp.E, inp.k, t_max, rowmajor)
+            names = ("w_gate_up", "w_down") if inp.wfmt == "bf16" else \
+                ("q_gate_up", "s_gate_up", "q_down", "s_down")
+            packed = {n: torch.empty_like(t[n]) for n in names}
+            dst = L.moe_weights(*[(packed[f] if f in packed else t[f]).data_ptr() if (f in packed or f in t)
+                                  else None for f, _ in L.moe_weights._fields_])
+            L.moe_pack_weights(src_cfg, self.w, dst)
+            torch.cuda.synchronize(self.device)
+            t.update(packed)
+            self.w = dst
         self.ws_bytes = L.moe_workspace_size(self.cfg)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.graph = None

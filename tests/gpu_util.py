@@ -24,12 +24,13 @@ def workload(name, T=None):
 
 
 @functools.lru_cache(maxsize=None)
-def layer(name, t_max):
+def layer(name, t_max, tiled=True):
     """Device layer for a named workload (weights are shared between q8,
-    q64 and q4096, but the q4096 layer carries the router bias)."""
+    q64 and q4096, but the q4096 layer carries the router bias).  tiled:
+    expert weights packed into the fragment-tiled layout (else row-major)."""
     from mixture_experts_decode_router_amd.layer import MoELayer
-    say(f"[gpu] uploading layer {name} t_max={t_max}")
-    return MoELayer(workload(name), t_max=t_max)
+    say(f"[gpu] uploading layer {name} t_max={t_max} tiled={tiled}")
+    return MoELayer(workload(name), t_max=t_max, tiled=tiled)
 
 
 @functools.lru_cache(maxsize=None)

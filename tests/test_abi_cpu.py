@@ -165,3 +165,19 @@ def test_workspace_views_are_host_arithmetic():
     assert v.offsets == v.counts + 512
     assert v.perm == v.offsets + 768
     assert v.pos == v.perm + n * 4
+
+
+def test_pack_validation_on_host():
+    lib = L.lib()
+    w = weights()
+    other = weights(w_gate_up=FAKE * 2, w_down=FAKE * 3)
+    # source must be a row-major format
+    c = cfg(wfmt=L.MOE_W_BF16_TILED)
+    assert lib.moe_pack_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(other), None) == L.MOE_ERR_INVALID_ARG
+    # not in place
+    c = cfg()
+    assert lib.moe_pack_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(w), None) == L.MOE_ERR_INVALID_ARG
+    assert "in place" in L.moe_last_error()
+    # 4-bit needs its four tensors
+    c = cfg(wfmt=L.MOE_W_NF4_B64)
+    assert lib.moe_pack_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(other), None) == L.MOE_ERR_INVALID_ARG

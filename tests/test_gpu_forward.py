@@ -46,6 +46,21 @@ def test_forward_matches_oracle(name):
     assert err <= tol
 
 
+@pytest.mark.parametrize("name", ["q64", "q48q"])
+def test_forward_row_major_weights(name):
+    """Same parity with the expert weights left row-major (no packing)."""
+    inp = workload(name)
+    lay = layer(name, 64, tiled=False)
+    say(f"[gpu] forward {name} row-major weights")
+    out, views = run_forward(lay, inp.x)
+    ref_out, ref = oracle_forward(name)
+    check_views(views, ref)
+    tol = TOL_NF4 if inp.wfmt == "nf4" else TOL_BF16
+    assert rel_err(out.cpu().numpy(), ref_out) <= tol
+    tiled = layer(name, 64).forward(layer(name, 64).upload_x(inp.x))
+    assert torch.equal(out, tiled)   # same arithmetic, only the weight layout differs
+
+
 @pytest.mark.parametrize("T", list(S.SWEEP_T))
 def test_forward_decode_sweep(T):
     inp = workload("q64", T)
@@ -56,21 +71,22 @@ def test_forward_decode_sweep(T):
     assert rel_err(out.cpu().numpy(), ref_out) <= TOL_BF16
 
 
+@pytest.mark.parametrize("tiled", [True, False])
 @pytest.mark.parametrize("case", [
     dict(T=1, H=256, E=16, k=2, I=128, wfmt="bf16"),
     dict(T=17, H=256, E=16, k=16, I=128, wfmt="bf16"),     # k = E: every expert
     dict(T=33, H=512, E=32, k=1, I=256, wfmt="bf16"),      # k = 1
-    dict(T=40, H=4096, E=16, k=4, I=384, wfmt="bf16"),     # two LDS chunks along H
-    dict(T=50, H=1024, E=32, k=4, I=2560, wfmt="bf16"),    # two LDS chunks along I
-    dict(T=37, H=512, E=32, k=4, I=256, wfmt="nf4"),
-    dict(T=21, H=4096, E=16, k=3, I=2560, wfmt="nf4"),     # 4-bit, two chunks each way
+    dict(T=40, H=4096, E=16, k=4, I=384, wfmt="bf16"),     # longest rows
+    dict(T=50, H=1024, E=32, k=4, I=2560, wfmt="bf16"),    # long intermediate
+    dict(T=37, H=384, E=32, k=4, I=256, wfmt="nf4"),       # H an odd number of 128-blocks
+    dict(T=21, H=4096, E=16, k=3, I=2560, wfmt="nf4"),
     dict(T=300, H=256, E=16, k=2, I=128, wfmt="bf16"),     # many rows per expert (several items)
 ])
-def test_forward_edge_shapes(case):
+def test_forward_edge_shapes(case, tiled):
     inp = S.make_small(case["T"], case["H"], case["E"], case["k"], case["I"], seed=case["T"],
                        wfmt=case["wfmt"], bias=case["k"] == 4)
-    say(f"[gpu] forward edge {case}")
-    lay = MoELayer(inp, t_max=case["T"])
+    say(f"[gpu] forward edge {case} tiled={tiled}")
+    lay = MoELayer(inp, t_max=case["T"], tiled=tiled)
     out, views = run_forward(lay, inp.x)
     ref_out, ref = O.forward_batched(inp)
     check_views(views, ref)
