@@ -150,11 +150,12 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x,
  *                 ascending expert order, ascending s inside a group
  *                 (a stable argsort of the flat ids)           int32 [T*k]
  *   pos[s]      = p with perm[p] = s (nullable)                int32 [T*k]
+ *   workspace >= moe_workspace_size(cfg) bytes (chunk histograms at large T*k).
  * topk_ids values must lie in [0, E); an out-of-range id is clamped into
  * that range (the call stays memory-safe, its results are then unspecified). */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T,
                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
-                       hipStream_t stream);
+                       void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Whole block: route -> permute -> grouped gate/up with SiLU*up ->
  * grouped down -> per-token weighted combine.

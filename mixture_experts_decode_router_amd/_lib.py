@@ -84,7 +84,7 @@ def lib() -> ctypes.CDLL:
         "moe_route": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
                           c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_permute": (S, [POINTER(moe_config), c_void_p, c_int32, c_void_p, c_void_p,
-                            c_void_p, c_void_p, c_void_p]),
+                            c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_forward": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
                             c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_forward_timed": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
@@ -156,9 +156,11 @@ def moe_route(cfg, w, x, T, topk_ids, topk_w, logits, workspace, ws_bytes=None, 
                            ptr(topk_w), ptr(logits), ptr(workspace), ws_bytes, stream_handle(stream)))
 
 
-def moe_permute(cfg, topk_ids, T, counts, offsets, perm, pos=None, stream=None):
+def moe_permute(cfg, topk_ids, T, counts, offsets, perm, pos, workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_permute(ctypes.byref(cfg), ptr(topk_ids), T, ptr(counts), ptr(offsets),
-                             ptr(perm), ptr(pos), stream_handle(stream)))
+                             ptr(perm), ptr(pos), ptr(workspace), ws_bytes, stream_handle(stream)))
 
 
 def moe_forward(cfg, w, x, T, out, workspace, ws_bytes=None, stream=None):

@@ -22,7 +22,8 @@ LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "experts_skinny.hip", "combine.hip", "pack.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "experts_skinny.hip", "combine.hip", "pack.hip",
+           "experts_mfma.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -27,11 +27,15 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t ids, wts, counts, offsets, perm, pos, items, n_items, route, h, y, total;
+  size_t ids, wts, counts, offsets, perm, pos, items, n_items, route, chunks, h, y, total;
   int max_items;
 };
 
-int max_items_for(int N, int E) { return std::min(E, N) + (N + moe::kSkinnyTile - 1) / moe::kSkinnyTile; }
+// bound on the work-list length: sum over experts of ceil(c_e / tile)
+// rounded up to a multiple of group
+int max_items_for(int N, int E, int tile = moe::kSkinnyTile, int group = 1) {
+  return std::min(E, N) * group + (N + tile - 1) / tile;
+}
 
 Layout layout(const moe_config& c) {
   Layout L{};
@@ -42,7 +46,8 @@ Layout layout(const moe_config& c) {
     off = al256(off + bytes);
     return o;
   };
-  L.max_items = max_items_for((int)N, c.n_experts);
+  L.max_items = std::max(max_items_for((int)N, c.n_experts),
+                         max_items_for((int)N, c.n_experts, moe::kMfmaTile, moe::kMfmaGroup));
   L.ids = take(N * 4);
   L.wts = take(N * 4);
   L.counts = take((size_t)c.n_experts * 4);
@@ -52,6 +57,7 @@ Layout layout(const moe_config& c) {
   L.items = take((size_t)L.max_items * 8);
   L.n_items = take(4);
   L.route = take(moe::route_scratch_floats(c.t_max, c.n_experts, c.hidden) * 4);
+  L.chunks = take(moe::permute_scratch_ints((int)N, c.n_experts) * 4);
   L.h = take(N * c.inter * 2);
   L.y = take(N * c.hidden * 4);
   L.total = off;
@@ -158,17 +164,23 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   if ((e = moe::launch_route(ra, at<float>(ws, L.route), s)) != hipSuccess) return hip_fail(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
+  // Large groups (on average >= 32 rows per expert) go to the LDS-tiled MFMA
+  // kernels; both paths give bit-identical per-row results.
+  const bool mfma_path = c.wfmt == MOE_W_BF16_TILED && N >= 32 * c.n_experts;
+  const int tile = mfma_path ? moe::kMfmaTile : moe::kSkinnyTile;
   moe::PermuteArgs pa{};
   pa.ids = ra.ids;
   pa.N = N;
   pa.E = c.n_experts;
-  pa.tile = moe::kSkinnyTile;
+  pa.tile = tile;
+  pa.group = mfma_path ? moe::kMfmaGroup : 1;
   pa.counts = at<int32_t>(ws, L.counts);
   pa.offsets = at<int32_t>(ws, L.offsets);
   pa.perm = at<int32_t>(ws, L.perm);
   pa.pos = at<int32_t>(ws, L.pos);
   pa.items = at<int32_t>(ws, L.items);
   pa.n_items = at<int32_t>(ws, L.n_items);
+  pa.chunk_base = at<int32_t>(ws, L.chunks);
   if ((e = moe::launch_permute(pa, s)) != hipSuccess) return hip_fail(e, "permute launch");
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
@@ -178,7 +190,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ea.perm = pa.perm;
   ea.items = pa.items;
   ea.n_items = pa.n_items;
-  ea.max_items = max_items_for(N, c.n_experts);
+  ea.max_items = max_items_for(N, c.n_experts, tile, pa.group);
   ea.H = c.hidden;
   ea.I = c.inter;
   ea.E = c.n_experts;
@@ -194,9 +206,11 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ea.s_down = w.s_down;
   ea.codebook = w.codebook;
   const bool nf4 = is_nf4(c), tiled = is_tiled(c);
-  if ((e = moe::launch_gate_up(ea, nf4, tiled, s)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  e = mfma_path ? moe::launch_gate_up_mfma(ea, s) : moe::launch_gate_up(ea, nf4, tiled, s);
+  if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if ((e = moe::launch_down(ea, nf4, tiled, s)) != hipSuccess) return hip_fail(e, "down launch");
+  e = mfma_path ? moe::launch_down_mfma(ea, s) : moe::launch_down(ea, nf4, tiled, s);
+  if (e != hipSuccess) return hip_fail(e, "down launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   moe::CombineArgs ca{};
@@ -292,7 +306,8 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x,
 }
 
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T, int32_t* counts,
-                       int32_t* offsets, int32_t* perm, int32_t* pos, hipStream_t stream) {
+                       int32_t* offsets, int32_t* perm, int32_t* pos, void* workspace, size_t ws_bytes,
+                       hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_T(*cfg, T));
   MOE_TRY(check_ptr(topk_ids, "topk_ids", 4));
@@ -300,17 +315,20 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T
   MOE_TRY(check_ptr(offsets, "offsets", 4));
   MOE_TRY(check_ptr(perm, "perm", 4));
   if (pos && !aligned(pos, 4)) return fail(MOE_ERR_INVALID_ARG, "pos is not 4-byte aligned");
+  MOE_TRY(check_ws(*cfg, workspace, ws_bytes));
   moe::PermuteArgs pa{};
   pa.ids = topk_ids;
   pa.N = T * cfg->top_k;
   pa.E = cfg->n_experts;
   pa.tile = 0;
+  pa.group = 1;
   pa.counts = counts;
   pa.offsets = offsets;
   pa.perm = perm;
   pa.pos = pos;
   pa.items = nullptr;
   pa.n_items = nullptr;
+  pa.chunk_base = at<int32_t>(workspace, layout(*cfg).chunks);
   const hipError_t e = moe::launch_permute(pa, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "permute launch");
 }

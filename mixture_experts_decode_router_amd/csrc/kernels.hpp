@@ -8,6 +8,16 @@ namespace moe {
 // Decode/prefill token-tile height of the skinny expert kernels: one MFMA
 // column block of 16 tokens.
 constexpr int kSkinnyTile = 16;
+// Token-tile height of the LDS-tiled MFMA expert kernels (large groups).
+constexpr int kMfmaTile = 128;
+// The MFMA kernels run an expert's token tiles in groups of kMfmaGroup: a
+// group's tiles and all its column tiles are consecutive work, so the
+// weight and token stages they share are read from L2 together.  The work
+// list of each expert is padded to whole groups (padding items are empty).
+#ifndef MOE_MFMA_GROUP
+#define MOE_MFMA_GROUP 1
+#endif
+constexpr int kMfmaGroup = MOE_MFMA_GROUP;
 
 struct RouteArgs {
   const uint16_t* x;      // bf16 [T][H]
@@ -26,14 +36,17 @@ struct PermuteArgs {
   const int32_t* ids;     // [N]
   int N, E;
   int tile;               // token-tile height for the work list (0: no list)
+  int group;              // pad each expert's tile count to a multiple of this (>= 1)
   int32_t* counts;        // [E]
   int32_t* offsets;       // [E+1]
   int32_t* perm;          // [N]
   int32_t* pos;           // [N] or null
   int32_t* items;         // [max_items][2] = (expert, first row in its group) or null
   int32_t* n_items;       // [1] or null
+  int32_t* chunk_base;    // permute_scratch_ints(N, E) ints, or null (single workgroup)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+size_t permute_scratch_ints(int n_max, int E);
 
 struct ExpertArgs {
   // routing (device)
@@ -60,6 +73,11 @@ struct ExpertArgs {
 // tiled: weights in the fragment-tiled layout written by launch_pack
 hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
 hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
+
+// LDS-tiled MFMA grouped GEMMs (bf16 weights in the tiled layout only);
+// the work list must use kMfmaTile.
+hipError_t launch_gate_up_mfma(const ExpertArgs& a, hipStream_t s);
+hipError_t launch_down_mfma(const ExpertArgs& a, hipStream_t s);
 
 struct PackArgs {
   bool nf4;

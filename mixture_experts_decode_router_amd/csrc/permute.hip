@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
       c[q] = e < E ? s_hist[e] : 0;
       csum += c[q];
       tc[q] = a.tile > 0 ? (c[q] + a.tile - 1) / a.tile : 0;
+      tc[q] = (tc[q] + a.group - 1) / a.group * a.group;
       tsum += tc[q];
     }
     const int cincl = wave_incl_scan(csum, lane);
@@ -127,10 +128,155 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   }
 }
 
+// ------------------------------------------------------------------
+// Large N: the same three steps spread over workgroups.  Slots are cut into
+// chunks of kChunk; (1) each chunk's expert histogram, (2) one workgroup
+// turns the chunk histograms into counts, offsets, the work list and each
+// chunk's starting cursor per expert (offsets[e] + slots of e in earlier
+// chunks), (3) every chunk scatters its slots in ascending order from its
+// cursors, exactly as the single-workgroup kernel does.
+constexpr int kChunk = 2048;
+constexpr int kChunkThreads = 256;
+
+__global__ __launch_bounds__(kChunkThreads) void permute_chunk_hist(PermuteArgs a) {
+  __shared__ int s_h[kMaxE];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x;
+  for (int e = tid; e < kMaxE; e += kChunkThreads) s_h[e] = 0;
+  __syncthreads();
+  const int s0 = c * kChunk, s1 = min(a.N, s0 + kChunk);
+  for (int s = s0 + tid; s < s1; s += kChunkThreads) atomicAdd(&s_h[clamp_expert(a.ids[s], a.E)], 1);
+  __syncthreads();
+  for (int e = tid; e < a.E; e += kChunkThreads) a.chunk_base[(size_t)c * a.E + e] = s_h[e];
+}
+
+constexpr int kMaxChunks = 65536 / kChunk;  // T*k <= 65536
+
+__global__ __launch_bounds__(kThreads) void permute_chunk_scan(PermuteArgs a) {
+  __shared__ int s_cnt[kMaxE];
+  __shared__ int s_ch[kMaxChunks * kMaxE];  // chunk histograms, loaded in parallel
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E;
+  const int nchunk = (a.N + kChunk - 1) / kChunk;
+  for (int i = tid; i < nchunk * E; i += kThreads) s_ch[i] = a.chunk_base[i];
+  __syncthreads();
+  // per expert: chunk-relative cursors and the total count
+  for (int e = tid; e < E; e += kThreads) {
+    int run = 0;
+    for (int c = 0; c < nchunk; ++c) {
+      const int v = s_ch[c * E + e];
+      s_ch[c * E + e] = run;
+      run += v;
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int c[4], tsum = 0, csum = 0, tc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      c[q] = e < E ? s_cnt[e] : 0;
+      csum += c[q];
+      tc[q] = a.tile > 0 ? (c[q] + a.tile - 1) / a.tile : 0;
+      tc[q] = (tc[q] + a.group - 1) / a.group * a.group;
+      tsum += tc[q];
+    }
+    const int cincl = wave_incl_scan(csum, lane);
+    int run = cincl - csum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      if (e < E) {
+        s_cnt[e] = run;  // now the offset
+        a.offsets[e] = run;
+        a.counts[e] = c[q];
+      }
+      run += c[q];
+    }
+    if (lane == 63) a.offsets[E] = cincl;
+    if (a.items) {
+      const int tincl = wave_incl_scan(tsum, lane);
+      int trun = tincl - tsum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * lane + q;
+        for (int i = 0; i < tc[q]; ++i) {
+          a.items[2 * (trun + i)] = e;
+          a.items[2 * (trun + i) + 1] = i * a.tile;
+        }
+        trun += tc[q];
+      }
+      if (lane == 63) *a.n_items = tincl;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nchunk * E; i += kThreads) a.chunk_base[i] = s_ch[i] + s_cnt[i % E];
+}
+
+__global__ __launch_bounds__(kChunkThreads) void permute_chunk_scatter(PermuteArgs a) {
+  constexpr int kW = kChunkThreads / 64;
+  __shared__ int s_cursor[kMaxE];
+  __shared__ int s_wcnt[kW][kMaxE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E;
+  const int c = blockIdx.x;
+  for (int e = tid; e < kMaxE; e += kChunkThreads) {
+    s_cursor[e] = e < E ? a.chunk_base[(size_t)c * E + e] : 0;
+    for (int w = 0; w < kW; ++w) s_wcnt[w][e] = 0;
+  }
+  __syncthreads();
+  const int s0 = c * kChunk, s1 = min(a.N, s0 + kChunk);
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  for (int base = s0; base < s1; base += kChunkThreads) {
+    const int s = base + tid;
+    const bool v = s < s1;
+    const int e = v ? clamp_expert(a.ids[s], E) : 0;
+    uint64_t m = __ballot(v);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = v && ((e >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const int rank = __popcll(m & lt_mask);
+    if (v && rank == 0) s_wcnt[wave][e] = __popcll(m);
+    __syncthreads();
+    if (v) {
+      int p = s_cursor[e] + rank;
+      for (int w2 = 0; w2 < wave; ++w2) p += s_wcnt[w2][e];
+      a.perm[p] = s;
+      if (a.pos) a.pos[s] = p;
+    }
+    __syncthreads();
+    for (int e2 = tid; e2 < E; e2 += kChunkThreads) {
+      int add = 0;
+      for (int w2 = 0; w2 < kW; ++w2) {
+        add += s_wcnt[w2][e2];
+        s_wcnt[w2][e2] = 0;
+      }
+      s_cursor[e2] += add;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
+size_t permute_scratch_ints(int n_max, int E) { return (size_t)((n_max + kChunk - 1) / kChunk) * E; }
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  if (a.N <= 2 * kChunk || a.chunk_base == nullptr) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  const int nchunk = (a.N + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(permute_chunk_hist, dim3(nchunk), dim3(kChunkThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(permute_chunk_scan, dim3(1), dim3(kThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(permute_chunk_scatter, dim3(nchunk), dim3(kChunkThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ class MoELayer:
         offsets = torch.empty(self.E + 1, dtype=torch.int32, device=self.device)
         perm = torch.empty(n, dtype=torch.int32, device=self.device)
         pos = torch.empty(n, dtype=torch.int32, device=self.device) if with_pos else None
-        L.moe_permute(self.cfg, ids, T, counts, offsets, perm, pos, stream)
+        L.moe_permute(self.cfg, ids, T, counts, offsets, perm, pos, self.workspace, self.ws_bytes, stream)
         return counts, offsets, perm, pos
 
     def forward(self, x: torch.Tensor, T: Optional[int] = None, out: Optional[torch.Tensor] = None,

@@ -55,11 +55,14 @@ def cfg(**kw):
 def test_workspace_size_layout():
     c = cfg()
     n = 64 * 8
-    items = 128 + n // 16
+    # work list: the longer of the skinny list (16-row tiles) and the MFMA
+    # list (128-row tiles, each expert padded to groups of 4)
+    items = max(128 + n // 16, 128 * 4 + n // 128)
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
     # router partial logits: 8 K splits (H = 2048) x t_max x E, two arrays
     route = 2 * 8 * 64 * 128 * 4
-    expect = (al(n * 4) * 4 + al(128 * 4) + al(129 * 4) + al(items * 8) + al(4) + al(route)
+    chunks = 1 * 128 * 4   # per-2048-slot chunk histograms
+    expect = (al(n * 4) * 4 + al(128 * 4) + al(129 * 4) + al(items * 8) + al(4) + al(route) + al(chunks)
               + al(n * 768 * 2) + al(n * 2048 * 4))
     assert L.moe_workspace_size(c) == expect
     assert L.moe_workspace_size(cfg(hidden=2000)) == 0
@@ -126,8 +129,9 @@ def test_route_permute_validation():
     assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 8, None, FAKE, None, FAKE, wsb, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(c), None, FAKE, 8, FAKE, FAKE, None, FAKE, wsb, None) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(c), ctypes.byref(w), FAKE, 8, FAKE, FAKE, None, FAKE, 64, None) == L.MOE_ERR_WORKSPACE
-    assert lib.moe_permute(ctypes.byref(c), FAKE, 8, FAKE, None, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
-    assert lib.moe_permute(ctypes.byref(c), FAKE, 100, FAKE, FAKE, FAKE, None, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(c), FAKE, 8, FAKE, None, FAKE, None, FAKE, wsb, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(c), FAKE, 100, FAKE, FAKE, FAKE, None, FAKE, wsb, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(c), FAKE, 8, FAKE, FAKE, FAKE, None, FAKE, 100, None) == L.MOE_ERR_WORKSPACE
 
 
 def test_graph_capture_validation_on_host():

@@ -119,6 +119,18 @@ def test_forward_deterministic_and_row_independent():
     assert torch.equal(b, a[torch.from_numpy(p).cuda()])
 
 
+def test_prefill_rows_match_decode_rows_bit_for_bit():
+    """T=4096 runs the LDS-tiled MFMA kernels, T=16 the skinny ones: the same
+    token gets the same bits either way."""
+    inp = workload("q4096")
+    lay = layer("q4096", 4096)
+    say("[gpu] prefill vs decode path rows")
+    a = lay.forward(lay.upload_x(inp.x))
+    for lo in (0, 2000, 4080):
+        b = lay.forward(lay.upload_x(inp.x[lo:lo + 16]))
+        assert torch.equal(a[lo:lo + 16], b), lo
+
+
 def test_forward_row_subset_is_bit_identical():
     """A token's output does not depend on which other tokens share the batch."""
     inp = workload("q64")
