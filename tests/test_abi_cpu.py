@@ -56,8 +56,8 @@ def test_workspace_size_layout():
     c = cfg()
     n = 64 * 8
     # work list: the longer of the skinny list (16-row tiles) and the MFMA
-    # list (128-row tiles, each expert padded to groups of 4)
-    items = max(128 + n // 16, 128 * 4 + n // 128)
+    # list (128-row tiles)
+    items = max(128 + n // 16, 128 + n // 128)
     al = lambda b: (b + 255) // 256 * 256  # noqa: E731
     # router partial logits: 8 K splits (H = 2048) x t_max x E, two arrays
     route = 2 * 8 * 64 * 128 * 4
