@@ -13,6 +13,12 @@ stream the kernels run on, the whole-block HBM fraction, and the fp64 CPU
 oracle timed on this host's cores on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload q64|q8|q48q|q4096]
+
+Profiler summaries (under profiles/) are made from rocprofv3 CSV output:
+
+    python bench.py --summarize stats DIR          # --kernel-trace --stats run
+    python bench.py --summarize traffic FETCH_DIR WRITE_DIR --workload W
+                                                   # two --pmc runs with --calib-copy
 """
 import argparse
 import json
@@ -83,6 +89,83 @@ def cpu_baseline(inp, budget_s=10.0):
                        f"expert weights pre-converted to fp64 (not timed)")
 
 
+# ---------------------------------------------------------------- profiles
+
+CALIB_MIB = 256   # size of the plain copy that calibrates the HBM byte counters
+
+
+def _csvs(d, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+
+
+def _short(name):
+    import re
+    n = name.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    n = re.sub(r"\((moe::|unsigned int|at::|long|int,).*", "", n)
+    return n[:90]
+
+
+def summarize_stats(d):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (kernel_stats.csv)."""
+    import csv
+    rows = []
+    for path in _csvs(d, "kernel_stats.csv"):
+        rows += list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    return "\n".join(out)
+
+
+def _counter_rows(d, counter):
+    """(dispatch id, kernel name, value in KiB) of every dispatch, in dispatch order."""
+    import csv
+    rows = []
+    for path in _csvs(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(rows)
+
+
+def summarize_traffic(fetch_dir, write_dir, workload):
+    """HBM bytes per launch of every MoE kernel from two --pmc runs (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for the --calib-copy copy of CALIB_MIB MiB (the largest copy kernel
+    dispatch of the run)."""
+    from mixture_experts_decode_router_amd.build import source_digest
+
+    def calib(rows):
+        # the --calib-copy copies are the first copy dispatches of the run
+        copies = [v for _, k, v in rows if "copy" in k.lower()][:3]
+        if len(copies) < 3:
+            raise SystemExit("no calibration copies in the run: profile with --calib-copy")
+        copies.sort()
+        return CALIB_MIB * 1024.0 / copies[1]
+
+    def means(rows):
+        acc = {}
+        for _, k, v in rows:
+            acc.setdefault(k, []).append(v)
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    fr, wr = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    cf, cw = calib(fr), calib(wr)
+    (f, nf), (w, _) = means(fr), means(wr)
+    kernels = {}
+    for k in sorted(set(f) | set(w)):
+        if "moe::" not in k:
+            continue
+        fk, wk = f.get(k, 0.0), w.get(k, 0.0)
+        kernels[_short(k)] = dict(dispatches=nf.get(k, 0), fetch_kib=round(fk, 1), write_kib=round(wk, 1),
+                                  bytes_per_launch=int(round((fk * cf + wk * cw) * 1024)))
+    return dict(workload=workload, source_digest=source_digest(), copy_mib=CALIB_MIB,
+                fetch_scale=round(cf, 4), write_scale=round(cw, 4), kernels=kernels)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,7 +179,21 @@ def main():
     ap.add_argument("--row-major", action="store_true",
                     help="keep expert weights row-major instead of the tiled layout")
     ap.add_argument("--sweep", action="store_true", help="also time every decode bucket (stderr + JSON extra)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help=f"run a plain {CALIB_MIB} MiB device copy first (calibrates profiler byte counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="'stats DIR' or 'traffic FETCH_DIR WRITE_DIR': print a profile summary, no GPU")
     args = ap.parse_args()
+
+    if args.summarize:
+        kind, dirs = args.summarize[0], args.summarize[1:]
+        if kind == "stats" and len(dirs) == 1:
+            print(summarize_stats(dirs[0]))
+        elif kind == "traffic" and len(dirs) == 2:
+            print(json.dumps(summarize_traffic(dirs[0], dirs[1], args.workload), indent=1))
+        else:
+            ap.error("--summarize stats DIR | --summarize traffic FETCH_DIR WRITE_DIR")
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs (--gpus > 1) are not "
@@ -113,6 +210,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.calib_copy:
+        src = torch.full((CALIB_MIB << 20,), 7, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     inp = S.make(args.workload)
     T, H, E, k, I = inp.T, inp.H, inp.E, inp.k, inp.I
@@ -185,7 +290,17 @@ def main():
 
     dominant = "gate_up"
     dom_us = stage_us[dominant]
-    achieved = model[dominant] / (dom_us * 1e-6) / 1e9
+    # the library runs the LDS-tiled MFMA kernels when the tiled bf16 layout
+    # has at least 32 routed rows per expert on average (prefill sizes): those
+    # are bound by the matrix cores, the skinny decode kernels by HBM
+    mfma_path = inp.wfmt == "bf16" and not args.row_major and T * k >= 32 * E
+    if mfma_path:
+        dom_flops = 2.0 * T * k * H * 2 * I
+        achieved = dom_flops / (dom_us * 1e-6) / 1e12
+        bound, peak, unit = "mfma", PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = model[dominant] / (dom_us * 1e-6) / 1e9
+        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{args.workload}.json")
     if os.path.exists(tpath):
@@ -194,6 +309,9 @@ def main():
             from mixture_experts_decode_router_amd.build import source_digest
             if tj.get("source_digest") == source_digest():
                 traffic = tj.get("bytes_per_launch")
+                if traffic is None:
+                    cand = [v for kname, v in tj.get("kernels", {}).items() if kname.startswith(dominant)]
+                    traffic = cand[0]["bytes_per_launch"] if len(cand) == 1 else None
         except Exception:
             traffic = None
     step_s = ms_per_step * 1e-3
@@ -216,13 +334,14 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {
             "kernel": "grouped gate/up + SiLU*up (" + ("bf16" if inp.wfmt == "bf16" else "4-bit") + ")",
-            "bound": "hbm",
+            "bound": bound,
             "achieved": round(achieved, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": model[dominant],
+            "algorithmic_flops_per_launch": 2 * T * k * H * 2 * I,
             "avg_launch_us": round(dom_us, 2),
         },
         "block": {
