@@ -47,7 +47,7 @@ Layout layout(const moe_config& c) {
     return o;
   };
   L.max_items = std::max(max_items_for((int)N, c.n_experts),
-                         max_items_for((int)N, c.n_experts, moe::kMfmaTile, moe::kMfmaGroup));
+                         max_items_for((int)N, c.n_experts, moe::kMfmaTile));
   L.ids = take(N * 4);
   L.wts = take(N * 4);
   L.counts = take((size_t)c.n_experts * 4);
@@ -173,7 +173,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   pa.N = N;
   pa.E = c.n_experts;
   pa.tile = tile;
-  pa.group = mfma_path ? moe::kMfmaGroup : 1;
+  pa.group = 1;
   pa.counts = at<int32_t>(ws, L.counts);
   pa.offsets = at<int32_t>(ws, L.offsets);
   pa.perm = at<int32_t>(ws, L.perm);

@@ -1,15 +1,27 @@
 // Grouped expert GEMMs for large per-expert row counts (prefill-sized T):
-// LDS double-buffered MFMA tiles.
+// LDS-tiled MFMA with the operands copied global -> LDS by the load unit.
 //
-// Work item = (expert e, up to 128 of its routed rows) x one 128-wide tile of
-// weight rows; a 256-thread workgroup computes the 128 x 128 output tile,
-// each of its 2 x 2 waves a 64 x 64 quarter as 4 x 4 MFMA 16x16x32 tiles.
-// Per 64-k step the workgroup copies its 128 x 64 weight slab (16 fragments
-// of the tiled layout, each one contiguous kilobyte) and its 128 x 64 token
-// slab (gathered rows) into LDS in fragment order, so every ds_read_b128 of a
-// wave reads one kilobyte (token fragments with a row swizzle that keeps the
-// stores free of bank conflicts).  Global loads run two stages ahead of the
-// MFMAs (two register slots, two LDS buffers).
+// Work item = (expert e, up to kBM of its routed rows) x one tile of 256
+// weight rows (gate/up: 128 gate rows + the matching 128 up rows; down: 256
+// rows of W_down).  A 512-thread workgroup computes the kBM x 256 output
+// tile; each of its 8 waves owns 64 tokens x (16 kNT) weight rows as kNT x 4
+// MFMA 16x16x32 tiles.  A wave whose 64 rows all lie past the item's last row
+// skips its MFMAs, so a short item costs its weight stream, not its padding.
+//
+// Per 32-k stage the workgroup needs 16 weight fragments (each one contiguous
+// kilobyte of the tiled layout) and kBM/16 token fragments (16 gathered rows
+// x 32 k); the waves move them with global_load_lds_dwordx4, which writes the
+// 64 lanes' 16-byte pieces to LDS in lane order -- exactly the fragment order
+// the MFMA operands are read in, so neither side has bank conflicts and no
+// register staging is needed.  kRing LDS stages form a ring: loads run
+// kRing - 1 stages ahead of the MFMAs.  Each iteration waits for the wave's
+// own loads of the stage to be multiplied (s_waitcnt vmcnt), then one barrier
+// publishes the whole stage and retires the buffer the next loads overwrite.
+//
+// Block order: the tiles of one expert are consecutive, weight tile major and
+// item minor, so all the items of a heavily routed expert stream each weight
+// tile through L2 together (the gathered tokens are small and stay in the
+// last-level cache); consecutive ranges go to one XCD.
 //
 // The MFMA instruction, the k assignment of lanes (lane group g <-> k offset
 // 8g of each 32-k step) and the order of the k-steps are the same as in the
@@ -17,38 +29,64 @@
 // whichever kernel computes it: a token's output does not depend on the batch
 // size that selected the kernel.
 //
-//   gate/up:  tile = 64 gate rows + the matching 64 up rows; epilogue
-//             h = silu(gate) * up -> bf16 h[p][n]
-//   down:     tile = 128 rows of W_down; epilogue y[perm[p]][c] (fp32)
+//   gate/up:  h[p][n] = silu(gate) * up -> bf16 (sorted-slot order)
+//   down:     y[perm[p]][c] (fp32, flat-slot order)
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kBM = 128;           // rows of an item (tokens)
-constexpr int kBK = 64;            // k per LDS stage (two MFMA k-steps)
-constexpr int kThreads = 256;
-constexpr int kFragBytes = 1024;   // one 16 x 32 bf16 MFMA operand fragment
-constexpr int kStageBytes = 2 * 16 * kFragBytes;  // weights 16 KiB + tokens 16 KiB
+#ifndef MOE_MFMA_RING
+#define MOE_MFMA_RING 3
+#endif
+constexpr int kBM = kMfmaTile;                        // token rows of an item
+constexpr int kBN = 256;                              // weight rows of a tile
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kWM = kBM / 64;                         // waves along the tokens (64 rows each)
+constexpr int kWN = kWaves / kWM;                     // waves along the weight rows
+constexpr int kNT = kBN / 16 / kWN;                   // weight row tiles per wave
+constexpr int kFragBytes = 1024;                      // one 16 x 32 bf16 operand fragment
+constexpr int kWFrags = kBN / 16;                     // weight fragments per stage
+constexpr int kXFrags = kBM / 16;                     // token fragments per stage
+constexpr int kXBase = kWFrags * kFragBytes;          // token fragments follow the weights
+constexpr int kStageBytes = (kWFrags + kXFrags) * kFragBytes;
+constexpr int kRing = MOE_MFMA_RING;                  // LDS stages in the ring
+constexpr int kLdsBytes = kRing * kStageBytes;
+constexpr int kWLoads = kWFrags / kWaves;             // weight fragment loads per wave per stage
+constexpr int kXTiles = kXFrags / kWaves;             // token fragment loads per wave per stage
+constexpr int kLoads = kWLoads + kXTiles;
+constexpr int kBlocksPerCU = 2 * kLdsBytes <= 160 * 1024 ? 2 : 1;
+static_assert((kBM == 128 || kBM == 256) && kWFrags % kWaves == 0 && kXFrags % kWaves == 0, "tile split");
+static_assert(kNT % 2 == 0 && kNT <= 8, "gate/up pairs per wave");
+static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
-struct Item {
-  int e, M, base;
-};
+typedef __attribute__((address_space(3))) char lds_char;
 
-__device__ __forceinline__ bool load_item(const ExpertArgs& a, int item, Item& it) {
-  if (item >= *a.n_items) return false;
-  it.e = a.items[2 * item];
-  const int m0 = a.items[2 * item + 1];
-  const int c = a.counts[it.e] - m0;
-  it.M = c < kBM ? c : kBM;
-  it.base = a.offsets[it.e] + m0;
-  return it.M > 0;  // group padding items are empty
+// s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
+#define MOE_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// wait until at most `later` stages of this wave's loads are still in flight
+__device__ __forceinline__ void wait_own_loads(int later) {
+  if (later <= 0) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
+  else if (later == 1) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(kLoads));
+  else if (later == 2) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(2 * kLoads));
+  else __builtin_amdgcn_s_waitcnt(MOE_VMCNT(3 * kLoads));
 }
+static_assert(kRing <= 5 && 3 * kLoads < 64, "wait_own_loads covers up to three later stages");
+
+// Workgroup barrier without __syncthreads' release fence, which would make
+// every wave wait for all its LDS-DMA loads, including those of later stages.
+// The wave's own LDS reads are complete first (lgkmcnt(0)), so no buffer is
+// overwritten while a read of it is in flight; "memory" keeps the compiler
+// from moving LDS accesses across.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Blocks are dealt round-robin over the 8 XCDs; hand each XCD a contiguous
-// range of logical tiles (expert-major) so tiles sharing weights meet in one
-// L2.
+// range of logical tiles.
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   const int per = (nb + 7) / 8;
   const int x = b & 7, i = b >> 3;
@@ -56,184 +94,179 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return x < full ? x * per + i : full * per + (x - full) * (per - 1) + i;
 }
 
-// One stage: weights (16 fragments) then tokens (16 fragments) in LDS.
-// Weight fragment (rtl, ks) at rtl*2 + ks; token fragment (tt, ks) at 16 + tt*2 + ks.
+// MFMAs of one k-step for the first NJ token tiles of the wave
+template <int NJ>
+__device__ __forceinline__ void mma_step(const unsigned char* sb, const int (&wrt)[kNT], int wm, int lane,
+                                         f32x4_t (&acc)[kNT][4]) {
+  u32x4_t af[kNT], bf[NJ];
+#pragma unroll
+  for (int i = 0; i < kNT; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(sb + wrt[i] * kFragBytes + lane * 16);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    bf[j] = *reinterpret_cast<const u32x4_t*>(sb + kXBase + (wm * 4 + j) * kFragBytes + lane * 16);
+#pragma unroll
+  for (int i = 0; i < kNT; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
+}
+
+// kWaves / 4 waves per SIMD per workgroup; kBlocksPerCU workgroups share a CU
 template <bool GATE_UP>
-__global__ __launch_bounds__(kThreads) void expert_mfma(ExpertArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char s_raw[];
-  const int ntile = GATE_UP ? a.I / 64 : a.H / 128;
+__global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mfma(ExpertArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char s_raw[];
+  const int H = a.H, I = a.I;
+  const int ntile = GATE_UP ? I / 128 : (H + kBN - 1) / kBN;
   // the grid is sized for the longest possible work list; the real tiles are
   // the first n_items * ntile blocks, spread evenly over the XCDs
   const int nblk = *a.n_items * ntile;
   if ((int)blockIdx.x >= nblk) return;
   const int lb = xcd_remap(blockIdx.x, nblk);
-  // logical order: groups of kMfmaGroup items (one expert), inside a group
-  // column tile nt major and the group's items minor
-  const int gsz = kMfmaGroup * ntile;
-  const int grp = lb / gsz, rem = lb - grp * gsz;
-  const int nt = rem / kMfmaGroup;
-  const int item = grp * kMfmaGroup + (rem - nt * kMfmaGroup);
-  Item it;
-  if (!load_item(a, item, it)) return;
-  const int H = a.H, I = a.I;
+  // the expert's items are contiguous in the work list (its item i starts at
+  // row i * kBM); inside the expert: weight tile nt major, item minor
+  const int coarse = lb / ntile;
+  const int e = a.items[2 * coarse];
+  const int first = coarse - a.items[2 * coarse + 1] / kBM;
+  const int cnt = a.counts[e];
+  const int ne = (cnt + kBM - 1) / kBM;
+  const int local = lb - first * ntile;
+  const int nt = local / ne;
+  const int m0 = (local - nt * ne) * kBM;
+  const int M = min(cnt - m0, kBM);
+  const int base = a.offsets[e] + m0;
   const int K = GATE_UP ? H : I;
   const int nks = K / 32;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // ---- global sources of this thread's 4 weight chunks and 4 token chunks per stage
-  // weight chunk j = tid + 256 i: fragment f = j / 64 (rtl = f / 2, ks = f % 2), slot j % 64
-  const uint16_t* wsrc[4];
+  // ---- this wave's loads per stage: weight row tiles kWLoads*wave + i, token tiles kXTiles*wave + t
+  const uint16_t* wsrc[kWLoads];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = tid + 256 * i;
-    const int f = j >> 6, slot = j & 63;
-    const int rtl = f >> 1, ks = f & 1;
+  for (int i = 0; i < kWLoads; ++i) {
+    const int rtl = kWLoads * wave + i;  // local row tile
     size_t rt;
     if (GATE_UP) {
-      const size_t rt_gate = (size_t)it.e * (2 * I / 16) + nt * 4;  // first gate row tile of this item tile
-      rt = rtl < 4 ? rt_gate + rtl : rt_gate + I / 16 + (rtl - 4);
+      const int rloc = rtl < 8 ? nt * 8 + rtl : I / 16 + nt * 8 + (rtl - 8);
+      rt = (size_t)e * (2 * I / 16) + rloc;
     } else {
-      rt = (size_t)it.e * (H / 16) + nt * 8 + rtl;
+      const int rloc = min(nt * 16 + rtl, H / 16 - 1);  // rows past H: any valid tile, never stored
+      rt = (size_t)e * (H / 16) + rloc;
     }
-    wsrc[i] = (GATE_UP ? a.w_gate_up : a.w_down) + ((rt * nks + ks) * 64 + slot) * 8;
+    wsrc[i] = (GATE_UP ? a.w_gate_up : a.w_down) + ((rt * nks) * 64 + lane) * 8;
   }
-  // token chunk q = tid + 256 i: row = q / 8, chunk c = q % 8 (k offset 8c within the stage)
-  const uint16_t* xsrc[4];
-  int xdst[4];
-  bool xok[4];
+  // lane (g, r) brings row 16 tt + r, k offset 8 g of each k-step
+  const uint16_t* xsrc[kXTiles];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + 256 * i;
-    const int row = q >> 3, c = q & 7;
-    xok[i] = row < it.M;
-    const size_t srow = !xok[i] ? 0 : (GATE_UP ? (size_t)(a.perm[it.base + row] / a.k) : (size_t)(it.base + row));
-    xsrc[i] = (GATE_UP ? a.x : a.h) + srow * K + c * 8;
-    const int tt = row >> 4, r = row & 15, ks = c >> 2, g = c & 3;
-    // the 8 lanes storing one row's 8 chunks must hit 8 different bank
-    // groups: row r of lane group g sits at slot r ^ (4 ks + g)
-    xdst[i] = (16 + tt * 2 + ks) * kFragBytes + (g * 16 + (r ^ (4 * ks + g))) * 16;
+  for (int t = 0; t < kXTiles; ++t) {
+    int row = (kXTiles * wave + t) * 16 + (lane & 15);
+    row = row < M ? row : M - 1;  // rows past M repeat a valid row; their outputs are never stored
+    const size_t srow = GATE_UP ? (size_t)(a.perm[base + row] / a.k) : (size_t)(base + row);
+    xsrc[t] = (GATE_UP ? a.x : a.h) + srow * K + (lane >> 4) * 8;
   }
 
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  // two register slots of global loads (stage s lives in slot s & 1), so the
-  // loads of stage kb + 2 are in flight while stage kb is multiplied
-  u32x4_t wreg[2][4], xreg[2][4];
-#define MOE_LOAD_STAGE(SLOT, KB)                                               \
-  do {                                                                         \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                            \
-      wreg[SLOT][i] = ld16_stream(wsrc[i] + (size_t)(KB) * 2 * 512);           \
-      xreg[SLOT][i] = xok[i] ? ld16(xsrc[i] + (KB) * kBK) : zero;              \
-    }                                                                          \
-  } while (0)
-#define MOE_STORE_STAGE(SLOT, BUF)                                             \
-  do {                                                                         \
-    unsigned char* sb = s_raw + (BUF) * kStageBytes;                           \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                            \
-      *reinterpret_cast<u32x4_t*>(sb + (tid + 256 * i) * 16) = wreg[SLOT][i];  \
-      *reinterpret_cast<u32x4_t*>(sb + xdst[i]) = xreg[SLOT][i];               \
-    }                                                                          \
-  } while (0)
-
-  f32x4_t acc[4][4];
+  auto issue = [&](int kb, int buf) {
+    lds_char* sb = (lds_char*)(s_raw) + buf * kStageBytes;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kWLoads; ++i)
+      __builtin_amdgcn_global_load_lds(wsrc[i] + (size_t)kb * 512, sb + (kWLoads * wave + i) * kFragBytes, 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // weight row tiles of this wave (rtl) and token tiles (tt)
-  int wrt[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) wrt[i] = GATE_UP ? (i < 2 ? wn * 2 + i : 4 + wn * 2 + (i - 2)) : wn * 4 + i;
-
-  // token fragments are stored row-swizzled (see xdst); lane (g, r) reads slot r ^ (4 ks + g)
-  const int lg = lane >> 4, lr = lane & 15;
-  const int bslot0 = (lg * 16 + (lr ^ lg)) * 16, bslot1 = (lg * 16 + (lr ^ (4 + lg))) * 16;
-  auto compute = [&](int buf) {
-    const unsigned char* base = s_raw + buf * kStageBytes;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4_t af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const u32x4_t*>(base + (wrt[i] * 2 + ks) * kFragBytes + lane * 16);
-        bf[i] = *reinterpret_cast<const u32x4_t*>(base + (16 + (wm * 4 + i) * 2 + ks) * kFragBytes +
-                                                   (ks ? bslot1 : bslot0));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
-    }
+    for (int t = 0; t < kXTiles; ++t)
+      __builtin_amdgcn_global_load_lds(xsrc[t] + kb * 32, sb + kXBase + (kXTiles * wave + t) * kFragBytes, 16, 0, 0);
   };
 
-  // K / 64 stages (an even number: K is a multiple of 128)
-  const int nstage = K / kBK;
-  MOE_LOAD_STAGE(0, 0);
-  MOE_LOAD_STAGE(1, 1);
-  MOE_STORE_STAGE(0, 0);
-  __syncthreads();
-  for (int kb = 0; kb < nstage; kb += 2) {
-    // even stage kb: LDS buffer 0, register slot 0 is free once stored
-    if (kb + 2 < nstage) MOE_LOAD_STAGE(0, kb + 2);
-    compute(0);
-    MOE_STORE_STAGE(1, 1);  // stage kb + 1 (always exists: nstage is even)
-    __syncthreads();
-    // odd stage kb + 1: LDS buffer 1
-    if (kb + 3 < nstage) MOE_LOAD_STAGE(1, kb + 3);
-    compute(1);
-    if (kb + 2 < nstage) MOE_STORE_STAGE(0, 0);
-    __syncthreads();
-  }
-#undef MOE_LOAD_STAGE
-#undef MOE_STORE_STAGE
+  // ---- compute: wave (wm, wn) = 64 tokens x 16*kNT weight rows
+  const int wm = wave % kWM, wn = wave / kWM;
+  constexpr int kH = kNT / 2;
+  int wrt[kNT];  // local weight row tiles of this wave (gate/up: kH gate tiles, then the matching up tiles)
+#pragma unroll
+  for (int i = 0; i < kNT; ++i) wrt[i] = GATE_UP ? (i < kH ? wn * kH + i : 8 + wn * kH + (i - kH)) : wn * kNT + i;
+  f32x4_t acc[kNT][4];
+#pragma unroll
+  for (int i = 0; i < kNT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // a wave whose 64 token rows all lie past the item's end has no MFMAs to do
+  const bool live = wm * 64 < M;
 
-  // ---- epilogue: lane (r, g) holds rows 4g+q of weight tile i, token column r of token tile j
+  const int nstage = nks;  // one 32-k step per stage
+  constexpr int D = kRing - 1;  // stages in flight ahead of the one multiplied
+#pragma unroll
+  for (int st = 0; st < D; ++st)
+    if (st < nstage) issue(st, st);
+  // the k loop; a wave with no live rows still moves its share of every stage
+  auto k_loop = [&](auto with_mma) {
+    for (int kb = 0; kb < nstage; ++kb) {
+      wait_own_loads(min(D - 1, nstage - 1 - kb));  // stage kb landed (later ones may be in flight)
+      stage_barrier();                              // ... for every wave; buffer (kb+D)%kRing is free
+      if (kb + D < nstage) issue(kb + D, (kb + D) % kRing);
+      if constexpr (decltype(with_mma)::value) mma_step<4>(s_raw + (kb % kRing) * kStageBytes, wrt, wm, lane, acc);
+    }
+  };
+  if (live) k_loop(std::true_type{});
+  else k_loop(std::false_type{});
+
+  // ---- epilogue: lane (r, g) holds weight rows 4g+q of tile i, token row r of token tile j
   const int r = lane & 15, g = lane >> 4;
   if (GATE_UP) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = (wm * 4 + j) * 16 + r;
-      if (row < it.M) {
+      const int trow = (wm * 4 + j) * 16 + r;
+      if (trow < M) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kH; ++i) {
           float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = silu(acc[i][j][q]) * acc[i + 2][j][q];
-          const int n = nt * 64 + (wn * 2 + i) * 16 + 4 * g;
+          for (int q = 0; q < 4; ++q) hv[q] = silu(acc[i][j][q]) * acc[i + kH][j][q];
+          const int n = nt * 128 + (wn * kH + i) * 16 + 4 * g;
           u32x2_t pk = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-          *reinterpret_cast<u32x2_t*>(a.h + (size_t)(it.base + row) * I + n) = pk;
+          *reinterpret_cast<u32x2_t*>(a.h + (size_t)(base + trow) * I + n) = pk;
         }
       }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = (wm * 4 + j) * 16 + r;
-      if (row < it.M) {
-        float* yrow = a.y + (size_t)a.perm[it.base + row] * H;
+      const int trow = (wm * 4 + j) * 16 + r;
+      if (trow < M) {
+        float* yrow = a.y + (size_t)a.perm[base + trow] * H;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = nt * 128 + (wn * 4 + i) * 16 + 4 * g;
-          *reinterpret_cast<f32x4_t*>(yrow + c) = acc[i][j];
+        for (int i = 0; i < kNT; ++i) {
+          const int c = nt * kBN + (wn * kNT + i) * 16 + 4 * g;
+          if (c < H) *reinterpret_cast<f32x4_t*>(yrow + c) = acc[i][j];
         }
       }
     }
   }
 }
 
+// dynamic LDS beyond 64 KiB needs the per-function limit raised, once per device
+template <bool GATE_UP>
+hipError_t allow_lds() {
+  static bool done[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (done[dev]) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_mfma<GATE_UP>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e == hipSuccess) done[dev] = true;
+  return e;
+}
+
 }  // namespace
 
 hipError_t launch_gate_up_mfma(const ExpertArgs& a, hipStream_t s) {
-  const dim3 grid(a.max_items * (a.I / 64));
-  hipLaunchKernelGGL(expert_mfma<true>, grid, dim3(kThreads), 2 * kStageBytes, s, a);
+  hipError_t e = allow_lds<true>();
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.max_items * (a.I / 128));
+  hipLaunchKernelGGL(expert_mfma<true>, grid, dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mfma(const ExpertArgs& a, hipStream_t s) {
-  const dim3 grid(a.max_items * (a.H / 128));
-  hipLaunchKernelGGL(expert_mfma<false>, grid, dim3(kThreads), 2 * kStageBytes, s, a);
+  hipError_t e = allow_lds<false>();
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.max_items * ((a.H + kBN - 1) / kBN));
+  hipLaunchKernelGGL(expert_mfma<false>, grid, dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
 

@@ -9,15 +9,10 @@ namespace moe {
 // column block of 16 tokens.
 constexpr int kSkinnyTile = 16;
 // Token-tile height of the LDS-tiled MFMA expert kernels (large groups).
-constexpr int kMfmaTile = 128;
-// The MFMA kernels run an expert's token tiles in groups of kMfmaGroup: a
-// group's tiles and all its column tiles are consecutive work, so the
-// weight and token stages they share are read from L2 together.  The work
-// list of each expert is padded to whole groups (padding items are empty).
-#ifndef MOE_MFMA_GROUP
-#define MOE_MFMA_GROUP 1
+#ifndef MOE_MFMA_TILE
+#define MOE_MFMA_TILE 128
 #endif
-constexpr int kMfmaGroup = MOE_MFMA_GROUP;
+constexpr int kMfmaTile = MOE_MFMA_TILE;
 
 struct RouteArgs {
   const uint16_t* x;      // bf16 [T][H]

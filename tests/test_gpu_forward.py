@@ -96,6 +96,40 @@ def test_forward_edge_shapes(case, tiled):
     assert err <= tol
 
 
+@pytest.mark.parametrize("case", [
+    dict(T=600, H=384, E=16, k=2, I=256),     # down: last 256-row weight tile half past H
+    dict(T=1100, H=512, E=16, k=1, I=384),    # k = 1, three gate/up tiles
+    dict(T=520, H=256, E=16, k=4, I=128),     # shortest K (down K = 128: two stages)
+])
+def test_forward_prefill_mfma_shapes(case):
+    """Shapes that take the LDS-tiled MFMA kernels (>= 32 routed rows per expert)."""
+    inp = S.make_small(case["T"], case["H"], case["E"], case["k"], case["I"], seed=case["T"],
+                       wfmt="bf16", bias=True)
+    say(f"[gpu] forward prefill-path {case}")
+    lay = MoELayer(inp, t_max=case["T"])
+    out, views = run_forward(lay, inp.x)
+    ref_out, ref = O.forward_batched(inp)
+    check_views(views, ref)
+    err = rel_err(out.cpu().numpy(), ref_out)
+    say(f"[gpu]   max|err|/rms = {err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_forward_prefill_one_hot_expert_set():
+    """Every token identical: k experts get all T rows (many 128-row items each)."""
+    inp = S.make_small(700, 256, 16, 2, 128, seed=7, wfmt="bf16", bias=False)
+    inp.x[:] = inp.x[3]
+    say("[gpu] forward prefill-path, all rows identical")
+    lay = MoELayer(inp, t_max=700)
+    out, views = run_forward(lay, inp.x)
+    ref_out, ref = O.forward_batched(inp)
+    check_views(views, ref)
+    assert (views["counts"].cpu().numpy() > 0).sum() == 2
+    assert rel_err(out.cpu().numpy(), ref_out) <= TOL_BF16
+    o = out.cpu()
+    assert torch.equal(o, o[:1].expand_as(o))   # identical rows give identical bits
+
+
 def test_forward_zero_input_gives_zero():
     inp = workload("q64")
     lay = layer("q64", 64)
