@@ -1,7 +1,7 @@
 // Grouped expert GEMMs, "skinny" form for decode-sized groups.
 //
-// One workgroup = one work-list item (expert e, up to 16 of its routed rows)
-// times one tile of output columns.  Tokens are the 16-wide column block of
+// One work unit = one work-list item (expert e, up to 16 of its routed rows)
+// times one tile of output columns (four waves' 16-row sub-tiles).  Tokens are the 16-wide column block of
 // a 16x16x32 bf16 MFMA, weights the 16-row A operand, so each wave computes
 // a 16 x 16 output tile with no cross-lane reduction.  Every k-step a lane
 // loads one 16-byte weight chunk per row tile (streamed from HBM once, with a
@@ -54,14 +54,19 @@ __device__ __forceinline__ bool load_item(const ExpertArgs& a, int item, Item& i
 }
 
 // ------------------------------------------------------------------ bf16
+// The bf16 kernels run one wave per workgroup (4 per item x column tile):
+// the finer grain keeps HBM busy through the last workgroups of the launch.
+constexpr int kSub = 4;  // waves (16-row sub-tiles) per column tile
+
 template <int U, bool TILED>
-__global__ __launch_bounds__(kThreads) void gate_up_bf16(ExpertArgs a) {
+__global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
   const int ntile = a.I / 64;
-  const int item = blockIdx.x / ntile, nt = blockIdx.x - item * ntile;
+  const int wave = blockIdx.x % kSub, bq = blockIdx.x / kSub;
+  const int item = bq / ntile, nt = bq - item * ntile;
   Item it;
   if (!load_item(a, item, it)) return;
   const int H = a.H, I = a.I;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
   const int n0 = nt * 64 + wave * 16;
   const bool rv = r < it.M;
@@ -101,13 +106,14 @@ __global__ __launch_bounds__(kThreads) void gate_up_bf16(ExpertArgs a) {
 }
 
 template <int U, bool TILED>
-__global__ __launch_bounds__(kThreads) void down_bf16(ExpertArgs a) {
+__global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
   const int ctile = a.H / 128;
-  const int item = blockIdx.x / ctile, ct = blockIdx.x - item * ctile;
+  const int wave = blockIdx.x % kSub, bq = blockIdx.x / kSub;
+  const int item = bq / ctile, ct = bq - item * ctile;
   Item it;
   if (!load_item(a, item, it)) return;
   const int H = a.H, I = a.I;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
   const int c0 = ct * 128 + wave * 32;
   const bool rv = r < it.M;
@@ -262,11 +268,11 @@ __global__ __launch_bounds__(kThreads) void down_nf4(ExpertArgs a) {
 }
 
 template <typename F8, typename F4>
-hipError_t launch_u(int K, F8 f8, F4 f4, dim3 grid, hipStream_t s, const ExpertArgs& a) {
+hipError_t launch_u(int K, F8 f8, F4 f4, dim3 grid, hipStream_t s, const ExpertArgs& a, int threads = kThreads) {
   if (K % 256 == 0)
-    hipLaunchKernelGGL(f8, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(f8, grid, dim3(threads), 0, s, a);
   else
-    hipLaunchKernelGGL(f4, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(f4, grid, dim3(threads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -277,8 +283,9 @@ hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t
   if (nf4)
     return tiled ? launch_u(a.H, gate_up_nf4<2, true>, gate_up_nf4<1, true>, grid, s, a)
                  : launch_u(a.H, gate_up_nf4<2, false>, gate_up_nf4<1, false>, grid, s, a);
-  return tiled ? launch_u(a.H, gate_up_bf16<8, true>, gate_up_bf16<4, true>, grid, s, a)
-               : launch_u(a.H, gate_up_bf16<8, false>, gate_up_bf16<4, false>, grid, s, a);
+  const dim3 gw(grid.x * kSub);
+  return tiled ? launch_u(a.H, gate_up_bf16<8, true>, gate_up_bf16<4, true>, gw, s, a, 64)
+               : launch_u(a.H, gate_up_bf16<8, false>, gate_up_bf16<4, false>, gw, s, a, 64);
 }
 
 hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
@@ -290,8 +297,9 @@ hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s)
       hipLaunchKernelGGL(down_nf4<false>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
-  return tiled ? launch_u(a.I, down_bf16<8, true>, down_bf16<4, true>, grid, s, a)
-               : launch_u(a.I, down_bf16<8, false>, down_bf16<4, false>, grid, s, a);
+  const dim3 gw(grid.x * kSub);
+  return tiled ? launch_u(a.I, down_bf16<8, true>, down_bf16<4, true>, gw, s, a, 64)
+               : launch_u(a.I, down_bf16<8, false>, down_bf16<4, false>, gw, s, a, 64);
 }
 
 }  // namespace moe

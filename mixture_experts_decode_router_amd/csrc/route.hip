@@ -19,14 +19,13 @@
 //            chain with a factor-2 margin.  L = k-th largest lower bound
 //            a - beta (a ballot radix select over order-preserving keys).
 //            Any expert with a + beta < L is beaten strictly by k others, so
-//            the true top-k lies within C = {e : a + beta >= L}.  If |C| = k
-//            and the k intervals [a - beta, a + beta], sorted by a, are
-//            pairwise disjoint, both the set and its order are certain and
-//            the approximate logits are used as they are.  Otherwise every
-//            candidate's dot product is re-formed in fp64 from the exact
-//            bf16 products, rounded to fp32 (plus the fp32 bias), and the
-//            top-k of C by (value desc, index asc) is taken: the top-k of
-//            all experts.
+//            the true top-k lies within C = {e : a + beta >= L}.  A candidate
+//            whose interval [a - beta, a + beta] meets no other candidate's
+//            is ordered against every other one by its approximate value; the
+//            dot products of the candidates whose intervals overlap are
+//            re-formed in fp64 from the exact bf16 products, rounded to fp32
+//            (plus the fp32 bias).  The top-k of C by (value desc, index asc)
+//            over these values is the top-k of all experts.
 //
 // Softmax weights w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), fp32, j in
 // selection order (equal to the full softmax renormalised over the top k).
@@ -138,6 +137,10 @@ __device__ __forceinline__ double dot8_f64(u32x4_t xa, u32x4_t wa, double s) {
   return s;
 }
 
+__device__ __forceinline__ float readlane_f(float v, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
 // key f beats key e: larger value, or equal value and lower index
 __device__ __forceinline__ int beats(float vf, int f, float ve, int e) {
   return (vf > ve || (vf == ve && f < e)) ? 1 : 0;
@@ -182,8 +185,6 @@ template <int M, int CH>  // M = ceil(E / 64) experts per lane; CH = ceil(H / 51
 __global__ __launch_bounds__(256) void route_select(SelParams P) {
   __shared__ float s_v[4][kMaxCand];
   __shared__ int s_e[4][kMaxCand];
-  __shared__ float s_lo[4][kMaxK];
-  __shared__ float s_hi[4][kMaxK];
   __shared__ float s_selv[4][kMaxK];
   __shared__ int s_sele[4][kMaxK];
   __shared__ __attribute__((aligned(16))) float s_key[4][kMaxE];
@@ -270,29 +271,37 @@ __global__ __launch_bounds__(256) void route_select(SelParams P) {
       const float bm = __shfl(bd[m], ce & 63);  // bound of expert ce (held by lane ce % 64)
       if (mine && (ce >> 6) == m) cb = bm;
     }
-    // approximate order and the certainty check
-    int rank = 0;
-    for (int j = 0; j < ncand; ++j) rank += beats(s_v[wave][j], s_e[wave][j], cv, ce);
-    if (mine && rank < k) {
-      s_lo[wave][rank] = cv - cb;
-      s_hi[wave][rank] = cv + cb;
+    // Interval of candidate i: [cv - cb, cv + cb] holds its exact logit.  A
+    // candidate whose interval meets no other candidate's is ordered against
+    // every other one by its approximate value; only candidates whose
+    // intervals overlap get the exact value re-formed (typically two).
+    // (candidate j's values are read from its lane: uniform j, no LDS round trip)
+    const float lo = cv - cb, hi = cv + cb;
+    bool need = false;
+    for (int j = 0; j < ncand; ++j) {
+      const float loj = readlane_f(lo, j), hij = readlane_f(hi, j);
+      need |= mine && j != lane && loj <= hi && lo <= hij;
     }
-    wave_sync_lds();
-    const bool amb_pair = lane + 1 < k && s_lo[wave][lane] <= s_hi[wave][lane + 1];
-    const bool refine = ncand > k || __ballot(amb_pair) != 0ull;
-    if (refine) {
+    uint64_t rmask = __ballot(need);
+    if (rmask) {
       u32x4_t xc[CH];
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int c = lane + 64 * i;
         xc[i] = c < nch ? ld16(a.x + (size_t)t * a.H + c * 8) : zero;
       }
-      constexpr int NB = CH >= 8 ? 2 : 32 / CH;  // candidates per batch (row loads in flight: NB * CH)
-      for (int j0 = 0; j0 < ncand; j0 += NB) {
+      constexpr int NB = CH >= 8 ? 2 : (CH >= 4 ? 4 : 8);  // rows per batch (loads in flight: NB * CH)
+      while (rmask) {
+        int lj[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          lj[b] = rmask ? __builtin_ctzll(rmask) : -1;  // candidate lane
+          if (rmask) rmask &= rmask - 1;
+        }
         u32x4_t wc[NB][CH];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          const int ej = j0 + b < ncand ? s_e[wave][j0 + b] : -1;
+          const int ej = lj[b] >= 0 ? __builtin_amdgcn_readlane(ce, lj[b]) : -1;
 #pragma unroll
           for (int i = 0; i < CH; ++i) {
             const int c = lane + 64 * i;
@@ -301,23 +310,21 @@ __global__ __launch_bounds__(256) void route_select(SelParams P) {
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-          if (j0 + b < ncand) {
+          if (lj[b] >= 0) {
             double sd = 0.0;
 #pragma unroll
             for (int i = 0; i < CH; ++i) sd = dot8_f64(xc[i], wc[b][i], sd);
             sd = wave_sum_f64(sd);
             float le = (float)sd;
-            if (a.bias) le = le + a.bias[s_e[wave][j0 + b]];
-            if (lane == j0 + b) cv = le;
+            if (a.bias) le = le + a.bias[__builtin_amdgcn_readlane(ce, lj[b])];
+            if (lane == lj[b]) cv = le;
           }
         }
       }
-      wave_sync_lds();
-      if (mine) s_v[wave][lane] = cv;
-      wave_sync_lds();
-      rank = 0;
-      for (int j = 0; j < ncand; ++j) rank += beats(s_v[wave][j], s_e[wave][j], cv, ce);
     }
+    // final order over the candidates by (value desc, index asc)
+    int rank = 0;
+    for (int j = 0; j < ncand; ++j) rank += beats(readlane_f(cv, j), __builtin_amdgcn_readlane(ce, j), cv, ce);
     if (mine && rank < k) {
       s_selv[wave][rank] = cv;
       s_sele[wave][rank] = ce;
