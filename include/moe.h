@@ -182,8 +182,9 @@ moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const 
  * R = H, K = I), with rt < R/16, r < 16, g < 4:
  *   bf16    16-byte chunk (rt*K/32 + ks)*64 + 16g + r
  *             = W[16rt + r][32ks + 8g .. 32ks + 8g + 7]
- *   codes   16-byte chunk (rt*K/128 + kb)*64 + 16g + r
- *             = codes of row 16rt + r for k in [128kb + 32g, 128kb + 32g + 32)
+ *   codes   16-byte chunk (rt*K/128 + kb)*64 + 16g + r; its 4-byte word st
+ *             (st < 4) = codes of row 16rt + r for k in [128kb + 32st + 8g,
+ *             128kb + 32st + 8g + 8)
  *   scales  float (rt*K/128 + kb)*32 + 2r + h = absmax of row 16rt + r,
  *             64-block 2kb + h
  * Writes dst's expert tensors (w_gate_up, w_down; or q_gate_up, s_gate_up,

@@ -25,11 +25,9 @@
 // order, written once by the pack kernel): the tiled layout turns every wave
 // load into one contiguous 1 KiB read.
 //
-// 4-bit weights (NF4_B64): each lane loads 16 bytes = 32 codes of one row and
-// feeds four MFMA steps with them (lane group g covers k in
-// [kb + 32g, kb + 32g + 32) of a 128-k block; the activation fragment uses the
-// same k assignment), dequantising codebook[code] * absmax to bf16 in
-// registers.  A lane's 32 k lie in one 64-weight scale block.
+// 4-bit weights (NF4_B64): the codebook value of each code (one LDS table
+// read per two codes) feeds the MFMA unscaled; the per-64 absmax scales the
+// MFMA partial sums of each 64-k half block (see the 4-bit section).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,7 +35,8 @@ namespace moe {
 namespace {
 
 constexpr int kTile = kSkinnyTile;  // rows per item (MFMA column block)
-constexpr int kThreads = 256;       // 4 waves
+constexpr int kThreads = 64;        // bf16 kernels: one wave per workgroup
+constexpr int kNf4Threads = 256;    // 4-bit kernels: four waves share a code table
 
 struct Item {
   int e, M, base;
@@ -148,122 +147,185 @@ __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
 }
 
 // ------------------------------------------------------------------ 4-bit
-// 8 codes (one 32-bit word, element 2i in the low nibble of byte i) ->
-// 8 bf16 weights codebook[code] * scale, packed in k order.
-__device__ __forceinline__ u32x4_t dequant8(uint32_t w, float sc, const float* cb) {
+// A weight is codebook[code] * absmax(row, 64-block).  Here the tokens are
+// the MFMA A operand and the weights the B operand, D[token][weight row], so
+// a lane's four outputs all belong to its own weight row and the absmax is
+// applied to MFMA partial sums: each 32-k MFMA step lies in one 64-block
+// (steps 0,1 of a 128-k block use block 2kb, steps 2,3 block 2kb+1), and
+//   D[t][row] = sum_h absmax(row, h) * sum_{k in h} x[t][k] bf16(codebook[code])
+// The per-weight work is one table read per two codes: s_lut[b] holds the
+// packed bf16 pair (codebook[b & 15], codebook[b >> 4]) of code byte b.
+//
+// Lane (g, r) feeds token row r and weight row r, k = 128kb + 32st + 8g + 0..7
+// for step st = 0..3 (dword st of its 16-byte chunk in the tiled layout; four
+// 4-byte loads from a row-major row), and receives D[token 4g + q][row r].
+
+__device__ __forceinline__ void build_lut(uint32_t* s_lut, const float* cb, int tid) {
+  if (tid < 256) s_lut[tid] = pack_bf16x2(cb[tid & 15], cb[tid >> 4]);
+}
+
+// 8 codes (one dword, element 2i in the low nibble of byte i) -> 8 bf16
+__device__ __forceinline__ u32x4_t lut8(const uint32_t* s_lut, uint32_t w) {
   u32x4_t o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t byte = (w >> (8 * i)) & 0xffu;
-    o[i] = pack_bf16x2(cb[byte & 15u] * sc, cb[byte >> 4] * sc);
-  }
+  for (int i = 0; i < 4; ++i) o[i] = s_lut[(w >> (8 * i)) & 0xffu];
   return o;
 }
 
+// codes of one 128-k block for this lane: tiled = one 16-byte chunk,
+// row-major = dwords 16kb + 4st + g of the row
+template <bool TILED>
+__device__ __forceinline__ u32x4_t load_codes(const uint8_t* q, int kb, int g) {
+  if (TILED) return ld16_stream(q + (size_t)kb * 1024);
+  const uint32_t* d = reinterpret_cast<const uint32_t*>(q) + 16 * kb + g;
+  return u32x4_t{d[0], d[4], d[8], d[12]};
+}
+
+// absmax of this lane's weight row for the two 64-blocks of 128-k block kb
+// (tiled: floats kb*32 + 2r, +1 of the row tile; row-major: 2kb, 2kb+1)
+template <bool TILED>
+__device__ __forceinline__ u32x2_t load_scales(const float* s, int kb) {
+  return *reinterpret_cast<const u32x2_t*>(s + (size_t)kb * (TILED ? 32 : 2));
+}
+
+// one 128-k block of one weight tile: acc[q] += absmax_0 * P0[q] + absmax_1 * P1[q]
+__device__ __forceinline__ f32x4_t block_mma(const uint32_t* s_lut, u32x4_t codes, const u32x4_t (&xb)[4],
+                                             u32x2_t sc, f32x4_t acc) {
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t p0 = mfma16(xb[0], lut8(s_lut, codes[0]), zero);
+  p0 = mfma16(xb[1], lut8(s_lut, codes[1]), p0);
+  f32x4_t p1 = mfma16(xb[2], lut8(s_lut, codes[2]), zero);
+  p1 = mfma16(xb[3], lut8(s_lut, codes[3]), p1);
+  const float s0 = __uint_as_float(sc[0]), s1 = __uint_as_float(sc[1]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = fmaf(s1, p1[q], fmaf(s0, p0[q], acc[q]));
+  return acc;
+}
+
+// gate/up: a wave owns two 16-row tiles of gate rows and the matching up
+// rows (32 n), so one token fragment feeds four weight tiles; the table is
+// built once per 4-wave workgroup
 template <int NB, bool TILED>  // NB: 128-k blocks per loop iteration (H % (128 * NB) == 0)
-__global__ __launch_bounds__(kThreads) void gate_up_nf4(ExpertArgs a) {
-  __shared__ float s_cb[16];
-  const int ntile = a.I / 64;
+__global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
+  __shared__ uint32_t s_lut[256];
+  const int ntile = a.I / 128;
   const int item = blockIdx.x / ntile, nt = blockIdx.x - item * ntile;
   Item it;
   if (!load_item(a, item, it)) return;
-  if (threadIdx.x < 16) s_cb[threadIdx.x] = a.codebook[threadIdx.x];
+  build_lut(s_lut, a.codebook, threadIdx.x);
   __syncthreads();
   const int H = a.H, I = a.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = nt * 64 + wave * 16;
+  const int n0 = nt * 128 + wave * 32;
   const bool rv = r < it.M;
   const int tok = rv ? a.perm[it.base + r] / a.k : 0;
-  const uint16_t* xr = a.x + (size_t)tok * H + 32 * g;
-  // per 128-k block kb: codes at qg + kb * qstep, scale at sg[kb * sstep]
+  const uint16_t* xr = a.x + (size_t)tok * H + 8 * g;
   const int nkb = H / 128;
-  const size_t rowg = (size_t)it.e * 2 * I + n0 + r;
-  const size_t rowu = rowg + I;
-  const size_t tg = (size_t)it.e * (2 * I / 16) + n0 / 16, tu = tg + I / 16;  // row tiles
-  const uint8_t* qg = TILED ? a.q_gate_up + (tg * nkb * 64 + lane) * 16 : a.q_gate_up + rowg * (H / 2) + 16 * g;
-  const uint8_t* qu = TILED ? a.q_gate_up + (tu * nkb * 64 + lane) * 16 : a.q_gate_up + rowu * (H / 2) + 16 * g;
-  const float* sg = TILED ? a.s_gate_up + tg * nkb * 32 + 2 * r + g / 2 : a.s_gate_up + rowg * (H / 64) + g / 2;
-  const float* su = TILED ? a.s_gate_up + tu * nkb * 32 + 2 * r + g / 2 : a.s_gate_up + rowu * (H / 64) + g / 2;
-  const int qstep = TILED ? 1024 : 64;  // bytes per 128-k block
-  const int sstep = TILED ? 32 : 2;     // floats per 128-k block
+  // tiles j = 0, 1: gate rows n0 + 16j; j = 2, 3: the matching up rows
+  const uint8_t* q[4];
+  const float* sp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const size_t row0 = (size_t)it.e * 2 * I + (j >= 2 ? I : 0) + n0 + 16 * (j & 1);  // first row of the tile
+    const size_t rt = row0 / 16;
+    q[j] = TILED ? a.q_gate_up + (rt * nkb * 64 + lane) * 16 : a.q_gate_up + (row0 + r) * (H / 2);
+    sp[j] = TILED ? a.s_gate_up + rt * nkb * 32 + 2 * r : a.s_gate_up + (row0 + r) * (H / 64);
+  }
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < H; kb += 128 * NB) {
-    u32x4_t cg[NB], cu[NB], xb[NB][4];
-    float scg[NB], scu[NB];
+  f32x4_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int kb0 = 0; kb0 < nkb; kb0 += NB) {
+    u32x4_t cd[NB][4], xb[NB][4];
+    u32x2_t sc[NB][4];
 #pragma unroll
     for (int h = 0; h < NB; ++h) {
-      const int k0 = kb + 128 * h;
-      cg[h] = ld16_stream(qg + (size_t)(k0 / 128) * qstep);
-      cu[h] = ld16_stream(qu + (size_t)(k0 / 128) * qstep);
-      scg[h] = sg[(k0 / 128) * sstep];
-      scu[h] = su[(k0 / 128) * sstep];
+      const int kb = kb0 + h;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) xb[h][st] = rv ? ld16(xr + k0 + 8 * st) : zero;
+      for (int j = 0; j < 4; ++j) {
+        cd[h][j] = load_codes<TILED>(q[j], kb, g);
+        sc[h][j] = load_scales<TILED>(sp[j], kb);
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) xb[h][st] = rv ? ld16(xr + 128 * kb + 32 * st) : zero;
     }
 #pragma unroll
     for (int h = 0; h < NB; ++h)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        accg = mfma16(dequant8(cg[h][st], scg[h], s_cb), xb[h][st], accg);
-        accu = mfma16(dequant8(cu[h][st], scu[h], s_cb), xb[h][st], accu);
-      }
+      for (int j = 0; j < 4; ++j) acc[j] = block_mma(s_lut, cd[h][j], xb[h], sc[h][j], acc[j]);
   }
-  if (rv) {
-    float hv[4];
+  // lane holds tokens 4g + q of rows n0 + 16j + r
 #pragma unroll
-    for (int q = 0; q < 4; ++q) hv[q] = silu(accg[q]) * accu[q];
-    u32x2_t pk = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
-    *reinterpret_cast<u32x2_t*>(a.h + (size_t)(it.base + r) * I + n0 + 4 * g) = pk;
+  for (int q = 0; q < 4; ++q) {
+    const int m = 4 * g + q;
+    if (m < it.M) {
+      uint16_t* hrow = a.h + (size_t)(it.base + m) * I + n0 + r;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float hv = silu(acc[j][q]) * acc[j + 2][q];
+        hrow[16 * j] = (uint16_t)(pack_bf16x2(hv, 0.f) & 0xffffu);
+      }
+    }
   }
 }
 
-template <bool TILED>
-__global__ __launch_bounds__(kThreads) void down_nf4(ExpertArgs a) {
-  __shared__ float s_cb[16];
+// down: a wave owns two 16-row tiles of W_down (32 output columns)
+template <int NB, bool TILED>  // NB: 128-k blocks per loop iteration (I % (128 * NB) == 0)
+__global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
+  __shared__ uint32_t s_lut[256];
   const int ctile = a.H / 128;
   const int item = blockIdx.x / ctile, ct = blockIdx.x - item * ctile;
   Item it;
   if (!load_item(a, item, it)) return;
-  if (threadIdx.x < 16) s_cb[threadIdx.x] = a.codebook[threadIdx.x];
+  build_lut(s_lut, a.codebook, threadIdx.x);
   __syncthreads();
   const int H = a.H, I = a.I;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int c0 = ct * 128 + wave * 32;
   const bool rv = r < it.M;
-  const uint16_t* hr = a.h + (size_t)(it.base + (rv ? r : 0)) * I + 32 * g;
+  const uint16_t* hr = a.h + (size_t)(it.base + (rv ? r : 0)) * I + 8 * g;
   const int nkb = I / 128;
-  const size_t row0 = (size_t)it.e * H + c0 + r;
-  const size_t row1 = row0 + 16;
-  const size_t t0 = (size_t)it.e * (H / 16) + c0 / 16, t1 = t0 + 1;  // row tiles
-  const uint8_t* q0 = TILED ? a.q_down + (t0 * nkb * 64 + lane) * 16 : a.q_down + row0 * (I / 2) + 16 * g;
-  const uint8_t* q1 = TILED ? a.q_down + (t1 * nkb * 64 + lane) * 16 : a.q_down + row1 * (I / 2) + 16 * g;
-  const float* s0 = TILED ? a.s_down + t0 * nkb * 32 + 2 * r + g / 2 : a.s_down + row0 * (I / 64) + g / 2;
-  const float* s1 = TILED ? a.s_down + t1 * nkb * 32 + 2 * r + g / 2 : a.s_down + row1 * (I / 64) + g / 2;
-  const int qstep = TILED ? 1024 : 64;
-  const int sstep = TILED ? 32 : 2;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < I; kb += 128) {
-    const u32x4_t c0v = ld16_stream(q0 + (size_t)(kb / 128) * qstep);
-    const u32x4_t c1v = ld16_stream(q1 + (size_t)(kb / 128) * qstep);
-    const float sc0 = s0[(kb / 128) * sstep], sc1 = s1[(kb / 128) * sstep];
-    u32x4_t hb[4];
+  const uint8_t* q[2];
+  const float* sp[2];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) hb[st] = rv ? ld16(hr + kb + 8 * st) : zero;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      acc0 = mfma16(dequant8(c0v[st], sc0, s_cb), hb[st], acc0);
-      acc1 = mfma16(dequant8(c1v[st], sc1, s_cb), hb[st], acc1);
-    }
+  for (int j = 0; j < 2; ++j) {
+    const size_t row0 = (size_t)it.e * H + c0 + 16 * j;
+    const size_t rt = row0 / 16;
+    q[j] = TILED ? a.q_down + (rt * nkb * 64 + lane) * 16 : a.q_down + (row0 + r) * (I / 2);
+    sp[j] = TILED ? a.s_down + rt * nkb * 32 + 2 * r : a.s_down + (row0 + r) * (I / 64);
   }
-  if (rv) {
-    const int slot = a.perm[it.base + r];
-    float* yrow = a.y + (size_t)slot * H;
-    *reinterpret_cast<f32x4_t*>(yrow + c0 + 4 * g) = acc0;
-    *reinterpret_cast<f32x4_t*>(yrow + c0 + 16 + 4 * g) = acc1;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int kb0 = 0; kb0 < nkb; kb0 += NB) {
+    u32x4_t cd[NB][2], hb[NB][4];
+    u32x2_t sc[NB][2];
+#pragma unroll
+    for (int h = 0; h < NB; ++h) {
+      const int kb = kb0 + h;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        cd[h][j] = load_codes<TILED>(q[j], kb, g);
+        sc[h][j] = load_scales<TILED>(sp[j], kb);
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) hb[h][st] = rv ? ld16(hr + 128 * kb + 32 * st) : zero;
+    }
+#pragma unroll
+    for (int h = 0; h < NB; ++h)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[j] = block_mma(s_lut, cd[h][j], hb[h], sc[h][j], acc[j]);
+  }
+  // lane holds tokens 4g + q of output columns c0 + 16j + r
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int m = 4 * g + q;
+    if (m < it.M) {
+      float* yrow = a.y + (size_t)a.perm[it.base + m] * H + c0 + r;
+      yrow[0] = acc[0][q];
+      yrow[16] = acc[1][q];
+    }
   }
 }
 
@@ -279,25 +341,41 @@ hipError_t launch_u(int K, F8 f8, F4 f4, dim3 grid, hipStream_t s, const ExpertA
 }  // namespace
 
 hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
-  const dim3 grid(a.max_items * (a.I / 64));
-  if (nf4)
-    return tiled ? launch_u(a.H, gate_up_nf4<2, true>, gate_up_nf4<1, true>, grid, s, a)
-                 : launch_u(a.H, gate_up_nf4<2, false>, gate_up_nf4<1, false>, grid, s, a);
-  const dim3 gw(grid.x * kSub);
+  if (nf4) {
+    // one 128-k block per iteration (more only cost occupancy)
+    const dim3 grid(a.max_items * (a.I / 128));  // 128 n per workgroup
+    if (tiled)
+      hipLaunchKernelGGL((gate_up_nf4<1, true>), grid, dim3(kNf4Threads), 0, s, a);
+    else
+      hipLaunchKernelGGL((gate_up_nf4<1, false>), grid, dim3(kNf4Threads), 0, s, a);
+    return hipGetLastError();
+  }
+  const dim3 gw(a.max_items * (a.I / 64) * kSub);
   return tiled ? launch_u(a.H, gate_up_bf16<8, true>, gate_up_bf16<4, true>, gw, s, a, 64)
                : launch_u(a.H, gate_up_bf16<8, false>, gate_up_bf16<4, false>, gw, s, a, 64);
 }
 
+template <bool TILED>
+void launch_down_nf4(const ExpertArgs& a, hipStream_t s) {
+  const dim3 grid(a.max_items * (a.H / 128));  // 128 output columns per workgroup
+  const int nkb = a.I / 128;
+  if (nkb % 3 == 0)
+    hipLaunchKernelGGL((down_nf4<3, TILED>), grid, dim3(kNf4Threads), 0, s, a);
+  else if (nkb % 2 == 0)
+    hipLaunchKernelGGL((down_nf4<2, TILED>), grid, dim3(kNf4Threads), 0, s, a);
+  else
+    hipLaunchKernelGGL((down_nf4<1, TILED>), grid, dim3(kNf4Threads), 0, s, a);
+}
+
 hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
-  const dim3 grid(a.max_items * (a.H / 128));
   if (nf4) {
     if (tiled)
-      hipLaunchKernelGGL(down_nf4<true>, grid, dim3(kThreads), 0, s, a);
+      launch_down_nf4<true>(a, s);
     else
-      hipLaunchKernelGGL(down_nf4<false>, grid, dim3(kThreads), 0, s, a);
+      launch_down_nf4<false>(a, s);
     return hipGetLastError();
   }
-  const dim3 gw(grid.x * kSub);
+  const dim3 gw(a.max_items * (a.H / 128) * kSub);
   return tiled ? launch_u(a.I, down_bf16<8, true>, down_bf16<4, true>, gw, s, a, 64)
                : launch_u(a.I, down_bf16<8, false>, down_bf16<4, false>, gw, s, a, 64);
 }

@@ -8,8 +8,8 @@
 // down: R = H, K = I), with rt < R/16, r < 16, g < 4:
 //   bf16   16-byte chunk ((rt * K/32 + ks) * 64 + 16 g + r)
 //              = W[16 rt + r][32 ks + 8 g .. 32 ks + 8 g + 7]
-//   codes  16-byte chunk ((rt * K/128 + kb) * 64 + 16 g + r)
-//              = codes of row 16 rt + r, k in [128 kb + 32 g, 128 kb + 32 g + 32)
+//   codes  16-byte chunk ((rt * K/128 + kb) * 64 + 16 g + r), dword st (0..3)
+//              = codes of row 16 rt + r, k in [128 kb + 32 st + 8 g, +8)
 //   scales float ((rt * K/128 + kb) * 32 + 2 r + h)
 //              = absmax of row 16 rt + r, 64-block 2 kb + h
 #include "common.hpp"
@@ -38,6 +38,24 @@ __global__ void pack_chunks(const u32x4_t* __restrict__ src, u32x4_t* __restrict
   dst[d] = src[s];
 }
 
+// 4-bit codes: one thread per output dword (8 codes)
+__global__ void pack_codes(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, size_t n_dwords, int R,
+                           int K) {
+  const size_t d = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= n_dwords) return;
+  const int row_dw = K / 8;                     // dwords per row
+  const size_t per_expert = (size_t)R * row_dw;
+  const size_t e = d / per_expert;
+  const size_t rem = d - e * per_expert;
+  const int st = (int)(rem & 3);
+  const int lane = (int)((rem >> 2) & 63);
+  const size_t blk = rem >> 8;                  // rt * (K / 128) + kb
+  const int nkb = K / 128;
+  const int rt = (int)(blk / nkb), kb = (int)(blk % nkb);
+  const int r = lane & 15, g = lane >> 4;
+  dst[d] = src[e * per_expert + ((size_t)rt * 16 + r) * row_dw + 16 * kb + 4 * st + g];
+}
+
 __global__ void pack_scales(const float* __restrict__ src, float* __restrict__ dst, size_t n, int R, int K) {
   const size_t d = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (d >= n) return;
@@ -61,6 +79,14 @@ hipError_t run_chunks(const void* src, void* dst, int E, int R, int K, int chunk
   return hipGetLastError();
 }
 
+hipError_t run_codes(const void* src, void* dst, int E, int R, int K, hipStream_t s) {
+  const size_t n = (size_t)E * R * (K / 8);
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(pack_codes, dim3(blocks), dim3(256), 0, s, static_cast<const uint32_t*>(src),
+                     static_cast<uint32_t*>(dst), n, R, K);
+  return hipGetLastError();
+}
+
 hipError_t run_scales(const float* src, float* dst, int E, int R, int K, hipStream_t s) {
   const size_t n = (size_t)E * R * (K / 64);
   const unsigned blocks = (unsigned)((n + 255) / 256);
@@ -76,8 +102,8 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
     if ((e = run_chunks(a.src_gate_up, a.dst_gate_up, a.E, 2 * a.I, a.H, 8, 32, s)) != hipSuccess) return e;
     return run_chunks(a.src_down, a.dst_down, a.E, a.H, a.I, 8, 32, s);
   }
-  if ((e = run_chunks(a.src_gate_up, a.dst_gate_up, a.E, 2 * a.I, a.H, 32, 128, s)) != hipSuccess) return e;
-  if ((e = run_chunks(a.src_down, a.dst_down, a.E, a.H, a.I, 32, 128, s)) != hipSuccess) return e;
+  if ((e = run_codes(a.src_gate_up, a.dst_gate_up, a.E, 2 * a.I, a.H, s)) != hipSuccess) return e;
+  if ((e = run_codes(a.src_down, a.dst_down, a.E, a.H, a.I, s)) != hipSuccess) return e;
   if ((e = run_scales(a.src_s_gate_up, a.dst_s_gate_up, a.E, 2 * a.I, a.H, s)) != hipSuccess) return e;
   return run_scales(a.src_s_down, a.dst_s_down, a.E, a.H, a.I, s);
 }

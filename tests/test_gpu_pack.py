@@ -18,9 +18,11 @@ def tiled_bf16(w):
 
 
 def tiled_codes(q):
-    """[E][R][K/2] bytes -> chunk order (rt, kb, g, r) of 16 bytes each."""
+    """[E][R][K/2] bytes -> chunk order (rt, kb, g, r) of 16 bytes each; inside
+    a chunk, 4-byte word st holds the codes of k in [128kb + 32st + 8g, +8)."""
     E, R, B = q.shape
-    return q.reshape(E, R // 16, 16, B // 64, 4, 16).transpose(0, 1, 3, 4, 2, 5).reshape(E, R, B)
+    # row bytes of one 128-k block: (st, g, 4 bytes)
+    return q.reshape(E, R // 16, 16, B // 64, 4, 4, 4).transpose(0, 1, 3, 5, 2, 4, 6).reshape(E, R, B)
 
 
 def tiled_scales(s):
