@@ -255,7 +255,9 @@ def main():
 
     # ---------------- per-kernel durations: eager forwards with stage events
     S_ = args.stage_steps
-    evs = L.hip_events(6 * S_)
+    # timing-only events: no system-scope fence at each record (the default
+    # fence writes back caches and adds microseconds around every stage)
+    evs = L.hip_events(6 * S_, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
     for i in range(5):  # warm
         lay.forward(x_static, T, out_static, stream=stream)
     for i in range(S_):

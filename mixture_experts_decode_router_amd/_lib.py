@@ -231,6 +231,7 @@ def _hiprt():
     if _hip is None:
         h = ctypes.CDLL("libamdhip64.so")
         h.hipEventCreate.argtypes = [POINTER(c_void_p)]
+        h.hipEventCreateWithFlags.argtypes = [POINTER(c_void_p), ctypes.c_uint]
         h.hipEventDestroy.argtypes = [c_void_p]
         h.hipEventSynchronize.argtypes = [c_void_p]
         h.hipEventElapsedTime.argtypes = [POINTER(ctypes.c_float), c_void_p, c_void_p]
@@ -239,14 +240,20 @@ def _hiprt():
     return _hip
 
 
-def hip_events(n: int) -> list[int]:
-    """n raw hipEvent_t handles (caller destroys them with hip_events_destroy)."""
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+HIP_EVENT_RELEASE_TO_DEVICE = 0x40000000
+
+
+def hip_events(n: int, flags: int = 0) -> list[int]:
+    """n raw hipEvent_t handles (caller destroys them with hip_events_destroy).
+    flags: hipEventCreateWithFlags flags, e.g. HIP_EVENT_RELEASE_TO_DEVICE for
+    timing events whose record should not write back caches to the system."""
     h = _hiprt()
     out = []
     for _ in range(n):
         e = c_void_p()
-        if h.hipEventCreate(ctypes.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if h.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(flags)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         out.append(e.value)
     return out
 
