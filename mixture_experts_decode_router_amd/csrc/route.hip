@@ -49,37 +49,58 @@ struct PartParams {
   const uint16_t* x;
   const uint16_t* wr;
   int T, H, E, ks;
-  float* part;   // [ks][T][E] partial logits
-  float* pabs;   // [ks][T][E] partial sums of |x*w|
+  int per_wg;    // K splits summed inside one workgroup (1, or ks at large T)
+  float* part;   // [ks / per_wg][T][E] partial logits
+  float* pabs;   // [ks / per_wg][T][E] partial sums of |x*w|
 };
 
 // Wave w owns expert tiles w, w+4, ...; every wave walks the workgroup's
 // whole K slice, so no cross-wave reduction is needed.  U k-steps of loads
 // are in flight before the MFMAs consume them.
+// Wave w owns expert tiles w, w+4, ...; every wave walks the workgroup's
+// whole K range, so no cross-wave reduction is needed.  U k-steps of loads
+// are in flight before the MFMAs consume them.  A workgroup covers per_wg
+// consecutive K splits: each split is its own MFMA accumulation chain and
+// the split sums are added in split order, exactly as route_select adds
+// stored split partials, so both forms give the same bits.
 template <int NT, int U>  // NT: expert tiles per wave (>= ceil(E/64)); U: k-steps per batch
 __global__ __launch_bounds__(256) void route_partial(PartParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * kTok;
-  const int ks = blockIdx.y;
   const int H = p.H, E = p.E, T = p.T;
   const int n_et = E >> 4;
   const int klen = H / p.ks;
-  const int kbeg = ks * klen;
   const int trow = t0 + r;
   const bool tv = trow < T;
-  const uint16_t* pb = p.x + (size_t)(tv ? trow : 0) * H + kbeg + g * 8;
-  const uint16_t* pa = p.wr + (size_t)(wave * 16 + r) * H + kbeg + g * 8;
+  const uint16_t* pb0 = p.x + (size_t)(tv ? trow : 0) * H + g * 8;
+  const uint16_t* pa0 = p.wr + (size_t)(wave * 16 + r) * H + g * 8;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   const uint32_t absm = 0x7fff7fffu;
+  f32x4_t lsum[NT], ssum[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    lsum[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    ssum[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // the workgroup's K range is per_wg consecutive splits; batches of U
+  // k-steps are software-pipelined (the next batch's loads are in flight
+  // while this batch is multiplied), and at the end of each split its
+  // accumulators are added to the running sums
+  const int kbase = blockIdx.y * p.per_wg * klen;
+  const int nbatch = p.per_wg * klen / (32 * U);
+  const int bps = klen / (32 * U);  // batches per split
+  const uint16_t* pb = pb0 + kbase;
+  const uint16_t* pa = pa0 + kbase;
   f32x4_t acc[NT], aab[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     aab[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  for (int kk = 0; kk < klen; kk += 32 * U) {
-    u32x4_t b[U], av[U][NT];
+  u32x4_t b[U], av[U][NT];
+  auto load = [&](int j) {
+    const int kk = j * 32 * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       b[u] = tv ? ld16(pb + kk + 32 * u) : zero;
@@ -87,26 +108,46 @@ __global__ __launch_bounds__(256) void route_partial(PartParams p) {
       for (int i = 0; i < NT; ++i)
         av[u][i] = (wave + 4 * i < n_et) ? ld16(pa + (size_t)i * 64 * H + kk + 32 * u) : zero;
     }
+  };
+  load(0);
+  for (int j = 0; j < nbatch; ++j) {
+    u32x4_t bc[U], ac[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const u32x4_t babs = b[u] & absm;
+      bc[u] = b[u];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) ac[u][i] = av[u][i];
+    }
+    if (j + 1 < nbatch) load(j + 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4_t babs = bc[u] & absm;
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
-        acc[i] = mfma16(av[u][i], b[u], acc[i]);
-        aab[i] = mfma16(av[u][i] & absm, babs, aab[i]);
+        acc[i] = mfma16(ac[u][i], bc[u], acc[i]);
+        aab[i] = mfma16(ac[u][i] & absm, babs, aab[i]);
+      }
+    }
+    if ((j + 1) % bps == 0) {  // end of a split
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        lsum[i] += acc[i];
+        ssum[i] += aab[i];
+        acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        aab[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
   }
   // lane holds D[4g+q][r]: expert 16*(wave + 4i) + 4g + q, token r
   if (tv) {
-    float* dl = p.part + ((size_t)ks * T + trow) * E;
-    float* ds = p.pabs + ((size_t)ks * T + trow) * E;
+    float* dl = p.part + ((size_t)blockIdx.y * T + trow) * E;
+    float* ds = p.pabs + ((size_t)blockIdx.y * T + trow) * E;
 #pragma unroll
     for (int i = 0; i < NT; ++i)
       if (wave + 4 * i < n_et) {
         const int e0 = 16 * (wave + 4 * i) + 4 * g;
-        *reinterpret_cast<f32x4_t*>(dl + e0) = acc[i];
-        *reinterpret_cast<f32x4_t*>(ds + e0) = aab[i];
+        *reinterpret_cast<f32x4_t*>(dl + e0) = lsum[i];
+        *reinterpret_cast<f32x4_t*>(ds + e0) = ssum[i];
       }
   }
 }
@@ -417,9 +458,7 @@ size_t route_scratch_floats(int t_max, int E, int H) { return 2 * (size_t)route_
 template <int NT>
 void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
   const int klen = pp.H / pp.ks;
-  if (klen % (32 * 8) == 0)
-    hipLaunchKernelGGL((route_partial<NT, 8>), grid, dim3(256), 0, s, pp);
-  else if (klen % (32 * 4) == 0)
+  if (klen % (32 * 4) == 0)
     hipLaunchKernelGGL((route_partial<NT, 4>), grid, dim3(256), 0, s, pp);
   else
     hipLaunchKernelGGL((route_partial<NT, 1>), grid, dim3(256), 0, s, pp);
@@ -427,8 +466,16 @@ void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
 
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s) {
   const int ks = route_splits(a.H);
-  PartParams pp{a.x, a.wr, a.T, a.H, a.E, ks, scratch, scratch + (size_t)ks * a.T * a.E};
-  const dim3 pgrid((a.T + kTok - 1) / kTok, ks);
+  // Small T: one workgroup per (16 tokens, K split), so the router weights
+  // are read by many CUs at once.  Large T: the token tiles alone fill the
+  // chip, so a workgroup sums all splits itself and stores finished sums.
+  const int ntt = (a.T + kTok - 1) / kTok;
+  // (1 or all ks: any other grouping would add the split sums in another
+  // association and change the bits)
+  const int per_wg = ntt >= 128 ? ks : 1;
+  const int nst = ks / per_wg;  // stored partials per token
+  PartParams pp{a.x, a.wr, a.T, a.H, a.E, ks, per_wg, scratch, scratch + (size_t)nst * a.T * a.E};
+  const dim3 pgrid(ntt, nst);
   const int n_et = a.E / 16;
   if (n_et <= 4)
     launch_partial<1>(pp, pgrid, s);
@@ -443,7 +490,7 @@ hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s) {
   // longest fp32 addition chain: 32 inside one MFMA, one per k-step of the
   // slice, the ks split partials, plus slack; doubled.
   const int depth = 32 + (a.H / ks) / 32 + ks + 8;
-  SelParams sp{a, pp.part, pp.pabs, ks, (float)(2.0 * depth * 5.9604644775390625e-08)};
+  SelParams sp{a, pp.part, pp.pabs, nst, (float)(2.0 * depth * 5.9604644775390625e-08)};
   const dim3 grid((a.T + 3) / 4);
   if (a.E <= 64)
     launch_select<1>(sp, grid, s);
