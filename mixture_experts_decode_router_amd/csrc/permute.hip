@@ -130,13 +130,15 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
 
 // ------------------------------------------------------------------
 // Large N: the same three steps spread over workgroups.  Slots are cut into
-// chunks of kChunk; (1) each chunk's expert histogram, (2) one workgroup
-// turns the chunk histograms into counts, offsets, the work list and each
-// chunk's starting cursor per expert (offsets[e] + slots of e in earlier
-// chunks), (3) every chunk scatters its slots in ascending order from its
-// cursors, exactly as the single-workgroup kernel does.
+// chunks of kChunk; (1) each chunk's expert histogram, (2) every chunk's
+// workgroup loads all chunk histograms, forms the expert offsets (exclusive
+// scan of the totals) and its own starting cursor per expert (offset + slots
+// of that expert in earlier chunks), and scatters its slots in ascending
+// order exactly as the single-workgroup kernel does; chunk 0 also writes
+// counts, offsets and the work list.
 constexpr int kChunk = 2048;
-constexpr int kChunkThreads = 256;
+constexpr int kChunkThreads = 1024;
+constexpr int kMaxChunks = 65536 / kChunk;  // T*k <= 65536
 
 __global__ __launch_bounds__(kChunkThreads) void permute_chunk_hist(PermuteArgs a) {
   __shared__ int s_h[kMaxE];
@@ -150,35 +152,41 @@ __global__ __launch_bounds__(kChunkThreads) void permute_chunk_hist(PermuteArgs 
   for (int e = tid; e < a.E; e += kChunkThreads) a.chunk_base[(size_t)c * a.E + e] = s_h[e];
 }
 
-constexpr int kMaxChunks = 65536 / kChunk;  // T*k <= 65536
-
-__global__ __launch_bounds__(kThreads) void permute_chunk_scan(PermuteArgs a) {
-  __shared__ int s_cnt[kMaxE];
-  __shared__ int s_ch[kMaxChunks * kMaxE];  // chunk histograms, loaded in parallel
+__global__ __launch_bounds__(kChunkThreads) void permute_chunk_scatter(PermuteArgs a) {
+  constexpr int kW = kChunkThreads / 64;
+  __shared__ int s_ch[kMaxChunks * kMaxE];  // all chunk histograms
+  __shared__ int s_tot[kMaxE];
+  __shared__ int s_cursor[kMaxE];
+  __shared__ int s_wcnt[kW][kMaxE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
+  const int c = blockIdx.x;
   const int nchunk = (a.N + kChunk - 1) / kChunk;
-  for (int i = tid; i < nchunk * E; i += kThreads) s_ch[i] = a.chunk_base[i];
+  for (int i = tid; i < nchunk * E; i += kChunkThreads) s_ch[i] = a.chunk_base[i];
+  for (int e = tid; e < kMaxE; e += kChunkThreads)
+    for (int w = 0; w < kW; ++w) s_wcnt[w][e] = 0;
   __syncthreads();
-  // per expert: chunk-relative cursors and the total count
-  for (int e = tid; e < E; e += kThreads) {
-    int run = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      const int v = s_ch[c * E + e];
-      s_ch[c * E + e] = run;
-      run += v;
+  // per expert: total count and slots in chunks before this one
+  for (int e = tid; e < E; e += kChunkThreads) {
+    int tot = 0, before = 0;
+    for (int cc = 0; cc < nchunk; ++cc) {
+      const int v = s_ch[cc * E + e];
+      before += cc < c ? v : 0;
+      tot += v;
     }
-    s_cnt[e] = run;
+    s_tot[e] = tot;
+    s_cursor[e] = before;
   }
   __syncthreads();
+  // exclusive scan of the totals (wave 0, 4 experts per lane) -> offsets
   if (wave == 0) {
-    int c[4], tsum = 0, csum = 0, tc[4];
+    int cnt[4], tc[4], csum = 0, tsum = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * lane + q;
-      c[q] = e < E ? s_cnt[e] : 0;
-      csum += c[q];
-      tc[q] = a.tile > 0 ? (c[q] + a.tile - 1) / a.tile : 0;
+      cnt[q] = e < E ? s_tot[e] : 0;
+      csum += cnt[q];
+      tc[q] = a.tile > 0 ? (cnt[q] + a.tile - 1) / a.tile : 0;
       tc[q] = (tc[q] + a.group - 1) / a.group * a.group;
       tsum += tc[q];
     }
@@ -188,42 +196,31 @@ __global__ __launch_bounds__(kThreads) void permute_chunk_scan(PermuteArgs a) {
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * lane + q;
       if (e < E) {
-        s_cnt[e] = run;  // now the offset
-        a.offsets[e] = run;
-        a.counts[e] = c[q];
-      }
-      run += c[q];
-    }
-    if (lane == 63) a.offsets[E] = cincl;
-    if (a.items) {
-      const int tincl = wave_incl_scan(tsum, lane);
-      int trun = tincl - tsum;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * lane + q;
-        for (int i = 0; i < tc[q]; ++i) {
-          a.items[2 * (trun + i)] = e;
-          a.items[2 * (trun + i) + 1] = i * a.tile;
+        s_cursor[e] += run;
+        if (c == 0) {
+          a.offsets[e] = run;
+          a.counts[e] = cnt[q];
         }
-        trun += tc[q];
       }
-      if (lane == 63) *a.n_items = tincl;
+      run += cnt[q];
     }
-  }
-  __syncthreads();
-  for (int i = tid; i < nchunk * E; i += kThreads) a.chunk_base[i] = s_ch[i] + s_cnt[i % E];
-}
-
-__global__ __launch_bounds__(kChunkThreads) void permute_chunk_scatter(PermuteArgs a) {
-  constexpr int kW = kChunkThreads / 64;
-  __shared__ int s_cursor[kMaxE];
-  __shared__ int s_wcnt[kW][kMaxE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E;
-  const int c = blockIdx.x;
-  for (int e = tid; e < kMaxE; e += kChunkThreads) {
-    s_cursor[e] = e < E ? a.chunk_base[(size_t)c * E + e] : 0;
-    for (int w = 0; w < kW; ++w) s_wcnt[w][e] = 0;
+    if (c == 0) {
+      if (lane == 63) a.offsets[E] = cincl;
+      if (a.items) {
+        const int tincl = wave_incl_scan(tsum, lane);
+        int trun = tincl - tsum;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = 4 * lane + q;
+          for (int i = 0; i < tc[q]; ++i) {
+            a.items[2 * (trun + i)] = e;
+            a.items[2 * (trun + i) + 1] = i * a.tile;
+          }
+          trun += tc[q];
+        }
+        if (lane == 63) *a.n_items = tincl;
+      }
+    }
   }
   __syncthreads();
   const int s0 = c * kChunk, s1 = min(a.N, s0 + kChunk);
@@ -274,8 +271,6 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(permute_chunk_hist, dim3(nchunk), dim3(kChunkThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(permute_chunk_scan, dim3(1), dim3(kThreads), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(permute_chunk_scatter, dim3(nchunk), dim3(kChunkThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -97,3 +97,18 @@ def test_route_is_deterministic():
         b = lay.route(x, with_logits=True)
         for u, v in zip(a, b):
             assert torch.equal(u, v)
+
+
+def test_route_large_batch_equals_small_batches_bit_for_bit():
+    """At T=4096 one workgroup sums all K splits itself; at T=64 the splits are
+    stored and summed by the selection kernel.  Same split-order sums, so the
+    same ids, weights and logits, bit for bit."""
+    inp = workload("q4096")
+    lay = layer("q4096", 4096)
+    say("[gpu] route T=4096 vs 64-token slices")
+    ids, w, lg = lay.route(lay.upload_x(inp.x), with_logits=True)
+    for lo in (0, 1984, 4032):
+        ids_s, w_s, lg_s = lay.route(lay.upload_x(inp.x[lo:lo + 64]), with_logits=True)
+        assert torch.equal(ids[lo:lo + 64], ids_s), lo
+        assert torch.equal(w[lo:lo + 64], w_s), lo
+        assert torch.equal(lg[lo:lo + 64], lg_s), lo
