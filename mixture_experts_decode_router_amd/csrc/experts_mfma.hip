@@ -44,7 +44,10 @@ namespace {
 #endif
 constexpr int kBM = kMfmaTile;                        // token rows of an item
 constexpr int kBN = 256;                              // weight rows of a tile
-constexpr int kWaves = 8;
+#ifndef MOE_MFMA_WAVES
+#define MOE_MFMA_WAVES 8
+#endif
+constexpr int kWaves = MOE_MFMA_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr int kWM = kBM / 64;                         // waves along the tokens (64 rows each)
 constexpr int kWN = kWaves / kWM;                     // waves along the weight rows
@@ -69,12 +72,19 @@ typedef __attribute__((address_space(3))) char lds_char;
 // s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
 #define MOE_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-// wait until at most `later` stages of this wave's loads are still in flight
-__device__ __forceinline__ void wait_own_loads(int later) {
+// wait until at most `later` stages of this wave's loads are still in flight;
+// nl = the wave's loads per stage (kLoads, or kLoads - kXTiles when its token
+// tiles lie past the item's end and are not loaded)
+template <int NL>
+__device__ __forceinline__ void wait_loads_n(int later) {
   if (later <= 0) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(0));
-  else if (later == 1) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(kLoads));
-  else if (later == 2) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(2 * kLoads));
-  else __builtin_amdgcn_s_waitcnt(MOE_VMCNT(3 * kLoads));
+  else if (later == 1) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(NL));
+  else if (later == 2) __builtin_amdgcn_s_waitcnt(MOE_VMCNT(2 * NL));
+  else __builtin_amdgcn_s_waitcnt(MOE_VMCNT(3 * NL));
+}
+__device__ __forceinline__ void wait_own_loads(int later, bool tokens) {
+  if (tokens) wait_loads_n<kLoads>(later);
+  else wait_loads_n<kLoads - kXTiles>(later);
 }
 static_assert(kRing <= 5 && 3 * kLoads < 64, "wait_own_loads covers up to three later stages");
 
@@ -152,7 +162,10 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
     }
     wsrc[i] = (GATE_UP ? a.w_gate_up : a.w_down) + ((rt * nks) * 64 + lane) * 8;
   }
-  // lane (g, r) brings row 16 tt + r, k offset 8 g of each k-step
+  // lane (g, r) brings row 16 tt + r, k offset 8 g of each k-step; a wave
+  // whose token tiles all lie past the item's end loads none (their MFMAs
+  // are skipped too)
+  const bool xload = kXTiles * wave * 16 < M;
   const uint16_t* xsrc[kXTiles];
 #pragma unroll
   for (int t = 0; t < kXTiles; ++t) {
@@ -167,9 +180,12 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
 #pragma unroll
     for (int i = 0; i < kWLoads; ++i)
       __builtin_amdgcn_global_load_lds(wsrc[i] + (size_t)kb * 512, sb + (kWLoads * wave + i) * kFragBytes, 16, 0, 0);
+    if (xload) {
 #pragma unroll
-    for (int t = 0; t < kXTiles; ++t)
-      __builtin_amdgcn_global_load_lds(xsrc[t] + kb * 32, sb + kXBase + (kXTiles * wave + t) * kFragBytes, 16, 0, 0);
+      for (int t = 0; t < kXTiles; ++t)
+        __builtin_amdgcn_global_load_lds(xsrc[t] + kb * 32, sb + kXBase + (kXTiles * wave + t) * kFragBytes, 16, 0,
+                                         0);
+    }
   };
 
   // ---- compute: wave (wm, wn) = 64 tokens x 16*kNT weight rows
@@ -194,7 +210,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
   // the k loop; a wave with no live rows still moves its share of every stage
   auto k_loop = [&](auto with_mma) {
     for (int kb = 0; kb < nstage; ++kb) {
-      wait_own_loads(min(D - 1, nstage - 1 - kb));  // stage kb landed (later ones may be in flight)
+      wait_own_loads(min(D - 1, nstage - 1 - kb), xload);  // stage kb landed (later ones may be in flight)
       stage_barrier();                              // ... for every wave; buffer (kb+D)%kRing is free
       if (kb + D < nstage) issue(kb + D, (kb + D) % kRing);
       if constexpr (decltype(with_mma)::value) mma_step<4>(s_raw + (kb % kRing) * kStageBytes, wrt, wm, lane, acc);
