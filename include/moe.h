@@ -220,10 +220,14 @@ moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const 
                              void* workspace, size_t ws_bytes, hipStream_t stream,
                              moe_graph** graph /* host out */);
 
-/* Launches the graph of the smallest bucket >= T on `stream`.  Rows
- * [T, bucket) of x_static are processed as well (their outputs land in rows
- * [T, bucket) of out_static; rows < T do not depend on them).  T larger than
- * the largest bucket -> MOE_ERR_INVALID_ARG. */
+/* Launches the graph of the smallest bucket >= T on `stream`.  The captured
+ * kernels read a live row count kept in the workspace: rows [T, bucket) of
+ * x_static are routed to no expert and counted nowhere (counts sum to T*k),
+ * and rows [T, bucket) of out_static are left untouched; rows < T are
+ * bit-identical to moe_forward of those T rows.  The count is rewritten (one
+ * one-thread kernel on `stream`) only when T differs from the previous
+ * replay of this graph.  A graph must be replayed from one thread at a time.
+ * T larger than the largest bucket -> MOE_ERR_INVALID_ARG. */
 moe_status moe_graph_replay(moe_graph* graph, int32_t T, hipStream_t stream);
 
 /* Bucket size moe_graph_replay(graph, T) would use, or -1. */

@@ -27,7 +27,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t ids, wts, counts, offsets, perm, pos, items, n_items, route, chunks, h, y, total;
+  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, total;
   int max_items;
 };
 
@@ -56,6 +56,7 @@ Layout layout(const moe_config& c) {
   L.pos = take(N * 4);
   L.items = take((size_t)L.max_items * 8);
   L.n_items = take(4);
+  L.live = take(4);
   L.route = take(moe::route_scratch_floats(c.t_max, c.n_experts, c.hidden) * 4);
   L.chunks = take(moe::permute_scratch_ints((int)N, c.n_experts) * 4);
   L.h = take(N * c.inter * 2);
@@ -142,8 +143,10 @@ T* at(void* base, size_t off) {
 }
 
 // Enqueues the whole block; arguments already validated.
+// live: device row count for graph replays of a larger bucket (rows >= *live
+// are routed nowhere and not written), or null for an eager call of T rows.
 moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void* x, int32_t T, float* out,
-                           void* ws, hipStream_t s, hipEvent_t* ev) {
+                           void* ws, hipStream_t s, hipEvent_t* ev, const int32_t* live = nullptr) {
   const Layout L = layout(c);
   const int N = T * c.top_k;
   hipError_t e;
@@ -161,6 +164,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ra.ids = at<int32_t>(ws, L.ids);
   ra.wts = at<float>(ws, L.wts);
   ra.logits = nullptr;
+  ra.live = live;
   if ((e = moe::launch_route(ra, at<float>(ws, L.route), s)) != hipSuccess) return hip_fail(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
@@ -181,6 +185,8 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   pa.items = at<int32_t>(ws, L.items);
   pa.n_items = at<int32_t>(ws, L.n_items);
   pa.chunk_base = at<int32_t>(ws, L.chunks);
+  pa.live = live;
+  pa.k = c.top_k;
   if ((e = moe::launch_permute(pa, s)) != hipSuccess) return hip_fail(e, "permute launch");
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
@@ -220,6 +226,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ca.T = T;
   ca.H = c.hidden;
   ca.k = c.top_k;
+  ca.live = live;
   if ((e = moe::launch_combine(ca, s)) != hipSuccess) return hip_fail(e, "combine launch");
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MOE_OK;
@@ -243,6 +250,8 @@ struct moe_graph {
   std::vector<int32_t> buckets;
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
+  int32_t* live = nullptr;  // device row count read by the captured kernels (in the workspace)
+  int32_t live_set = -1;    // last value enqueued into *live (-1: not yet)
 };
 
 static void graph_release(moe_graph* g) {
@@ -446,6 +455,7 @@ moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const 
 
   moe_graph* g = new moe_graph();
   g->cfg = *cfg;
+  g->live = at<int32_t>(workspace, layout(*cfg).live);
   for (int i = 0; i < n_buckets; ++i) {
     const int32_t b = buckets[i];
     e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
@@ -453,7 +463,7 @@ moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const 
       graph_release(g);
       return fail(MOE_ERR_NOT_CAPTURABLE, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
     }
-    const moe_status rs = enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr);
+    const moe_status rs = enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr, g->live);
     const std::string launch_msg = rs == MOE_OK ? std::string() : g_last_error;
     hipGraph_t gr = nullptr;
     e = hipStreamEndCapture(stream, &gr);
@@ -490,6 +500,13 @@ moe_status moe_graph_replay(moe_graph* g, int32_t T, hipStream_t stream) {
   if (!g) return fail(MOE_ERR_INVALID_ARG, "graph is NULL");
   for (size_t i = 0; i < g->buckets.size(); ++i) {
     if (g->buckets[i] >= T && T >= 1) {
+      // the captured kernels read the live row count from the workspace; it
+      // is rewritten (one tiny kernel) only when it changes
+      if (T != g->live_set) {
+        const hipError_t e = moe::launch_set_live(g->live, T, stream);
+        if (e != hipSuccess) return hip_fail(e, "live-count launch");
+        g->live_set = T;
+      }
       const hipError_t e = hipGraphLaunch(g->execs[i], stream);
       return e == hipSuccess ? MOE_OK : hip_fail(e, "hipGraphLaunch");
     }

@@ -15,6 +15,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
   const int c = (blockIdx.y * kThreads + threadIdx.x) * 4;
   if (c >= a.H) return;
+  if (a.live && t >= *a.live) return;  // row past the live count of a graph replay
   const float* w = a.wts + (size_t)t * a.k;
   const float* y = a.y + (size_t)t * a.k * a.H + c;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -27,11 +28,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   *reinterpret_cast<f32x4_t*>(a.out + (size_t)t * a.H + c) = acc;
 }
 
+__global__ void set_live_kernel(int32_t* live, int T) { *live = T; }
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.T, (a.H / 4 + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_live(int32_t* live, int T, hipStream_t s) {
+  hipLaunchKernelGGL(set_live_kernel, dim3(1), dim3(1), 0, s, live, T);
   return hipGetLastError();
 }
 

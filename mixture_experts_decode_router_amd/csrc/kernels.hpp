@@ -22,6 +22,7 @@ struct RouteArgs {
   int32_t* ids;           // [T][k]
   float* wts;             // [T][k]
   float* logits;          // [T][E] or null
+  const int32_t* live;    // device row count T_live <= T (graph replays), or null: rows >= T_live get no output
 };
 // scratch: route_scratch_floats(t_max, E, H) floats of device memory
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s);
@@ -39,6 +40,8 @@ struct PermuteArgs {
   int32_t* items;         // [max_items][2] = (expert, first row in its group) or null
   int32_t* n_items;       // [1] or null
   int32_t* chunk_base;    // permute_scratch_ints(N, E) ints, or null (single workgroup)
+  const int32_t* live;    // device row count, or null: only the first min(N, live * k) slots are bucketed
+  int k;                  // slots per row (with live)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 size_t permute_scratch_ints(int n_max, int E);
@@ -93,7 +96,10 @@ struct CombineArgs {
   const float* wts;       // [T][k]
   float* out;             // [T][H]
   int T, H, k;
+  const int32_t* live;    // device row count, or null: rows >= live are not written
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+// *live = T (one thread), for graph replays of a bucket larger than T
+hipError_t launch_set_live(int32_t* live, int T, hipStream_t s);
 
 }  // namespace moe

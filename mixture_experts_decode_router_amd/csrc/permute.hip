@@ -22,6 +22,12 @@ constexpr int kMaxE = 256;
 
 __device__ __forceinline__ int clamp_expert(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
+// slots to bucket: all N, or the first live * k of a graph replay whose
+// bucket is larger than its live row count
+__device__ __forceinline__ int live_slots(const PermuteArgs& a) {
+  return a.live ? min(a.N, *a.live * a.k) : a.N;
+}
+
 // inclusive scan of one int per lane across the wave
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -37,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteArgs a) {
   __shared__ int s_cursor[kMaxE];
   __shared__ int s_wcnt[kWaves][kMaxE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = a.N, E = a.E;
+  const int N = live_slots(a), E = a.E;
 
   for (int e = tid; e < kMaxE; e += kThreads) s_hist[e] = 0;
   for (int i = tid; i < kWaves * kMaxE; i += kThreads) (&s_wcnt[0][0])[i] = 0;
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(kChunkThreads) void permute_chunk_hist(PermuteArgs 
   const int c = blockIdx.x;
   for (int e = tid; e < kMaxE; e += kChunkThreads) s_h[e] = 0;
   __syncthreads();
-  const int s0 = c * kChunk, s1 = min(a.N, s0 + kChunk);
+  const int s0 = c * kChunk, s1 = min(live_slots(a), s0 + kChunk);
   for (int s = s0 + tid; s < s1; s += kChunkThreads) atomicAdd(&s_h[clamp_expert(a.ids[s], a.E)], 1);
   __syncthreads();
   for (int e = tid; e < a.E; e += kChunkThreads) a.chunk_base[(size_t)c * a.E + e] = s_h[e];
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(kChunkThreads) void permute_chunk_scatter(PermuteAr
     }
   }
   __syncthreads();
-  const int s0 = c * kChunk, s1 = min(a.N, s0 + kChunk);
+  const int s0 = c * kChunk, s1 = min(live_slots(a), s0 + kChunk);
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   for (int base = s0; base < s1; base += kChunkThreads) {
     const int s = base + tid;

@@ -249,6 +249,7 @@ __global__ __launch_bounds__(256) void route_select(SelParams P) {
       ps[m][ks] = ok ? P.pabs[((size_t)ks * T + t) * E + e] : 0.f;
     }
   }
+  if (a.live && t >= *a.live) return;  // row past the live count of a graph replay
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int e = lane + 64 * m;

@@ -62,7 +62,9 @@ def test_workspace_size_layout():
     # router partial logits: 8 K splits (H = 2048) x t_max x E, two arrays
     route = 2 * 8 * 64 * 128 * 4
     chunks = 1 * 128 * 4   # per-2048-slot chunk histograms
-    expect = (al(n * 4) * 4 + al(128 * 4) + al(129 * 4) + al(items * 8) + al(4) + al(route) + al(chunks)
+    # ids, weights, perm, pos; counts; offsets; work list; its length; the
+    # live row count of graph replays; router partials; chunk histograms; h; y
+    expect = (al(n * 4) * 4 + al(128 * 4) + al(129 * 4) + al(items * 8) + al(4) + al(4) + al(route) + al(chunks)
               + al(n * 768 * 2) + al(n * 2048 * 4))
     assert L.moe_workspace_size(c) == expect
     assert L.moe_workspace_size(cfg(hidden=2000)) == 0

@@ -51,16 +51,40 @@ def test_replay_equals_eager_and_oracle(captured, T):
     assert rel_err(out_static[:T].cpu().numpy(), ref_out) <= TOL_BF16
 
 
-def test_partial_bucket_rows_match_eager(captured):
+@pytest.mark.parametrize("T", [5, 13, 40])
+def test_partial_bucket_masks_rows_past_T(captured, T):
+    """replay(T) runs the smallest bucket >= T; a device live count keeps rows
+    T.. out of routing, bucketing and the output (they are left untouched)."""
     lay, stream, x_static, out_static = captured
     inp = workload("q64", 64)
-    T = 5
+    b = L.moe_graph_bucket_for(lay.graph, T)
+    say(f"[gpu] partial bucket T={T} (bucket {b})")
     with torch.cuda.stream(stream):
         x_static.copy_(lay.upload_x(inp.x))
-        lay.replay(T, stream)          # runs bucket 8 on rows 0..7
+        out_static.fill_(12345.0)
+        lay.replay(T, stream)
+        v = lay.views(b)
+        counts = v["counts"].clone()
+        got = out_static.clone()
         eager = lay.forward(lay.upload_x(inp.x[:T]), stream=stream)
     stream.synchronize()
-    assert torch.equal(out_static[:T], eager)
+    assert torch.equal(got[:T], eager)
+    assert int(counts.sum()) == T * lay.k
+    assert bool((got[T:b] == 12345.0).all())
+
+
+def test_live_count_follows_each_replay(captured):
+    """Alternating partial and full replays of one bucket: each sees its own T."""
+    lay, stream, x_static, out_static = captured
+    inp = workload("q64", 64)
+    with torch.cuda.stream(stream):
+        x_static.copy_(lay.upload_x(inp.x))
+        full = lay.forward(lay.upload_x(inp.x), stream=stream)
+        for T in (64, 50, 64, 33, 64):
+            lay.replay(T, stream)
+            torch.cuda.current_stream().synchronize()
+            assert torch.equal(out_static[:T], full[:T]), T
+    stream.synchronize()
 
 
 def test_replays_are_repeatable(captured):
