@@ -14,7 +14,8 @@ What it computes (Qwen3-MoE sparse block, decode or prefill, one layer):
   2. top-k           the k experts with the largest fp32 logit; equal logits
                      go to the lower expert index; ids stored best first.
   3. weights         softmax over all E logits (fp64), then renormalised over
-                     the k chosen: w_j = p[id_j] / sum_j' p[id_j'].
+                     the k chosen: w_j = p[id_j] / sum_j' p[id_j'] (or, in
+                     the variant without renormalisation, w_j = p[id_j]).
   4. bucketing       per-expert counts (histogram), exclusive-scan offsets
                      (E+1 entries), and the stable permutation of the flat
                      token-expert slots s = t*k + j grouped by expert: the
@@ -119,22 +120,31 @@ def topk_lowest_index(logits32: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k].astype(np.int32)
 
 
-def renormalised_weights(logits32: np.ndarray, ids: np.ndarray) -> np.ndarray:
-    """Softmax over all E logits (fp64, max-subtracted), then renormalised over
-    the chosen k: w_j = p[id_j] / sum_j' p[id_j'].  fp64 [T][k]."""
+def softmax_weights(logits32: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Softmax over all E logits (fp64, max-subtracted) taken at the chosen
+    ids, not renormalised: w_j = p[id_j], so sum_j w_j <= 1.  fp64 [T][k]."""
     l = np.asarray(logits32, dtype=np.float64)
     m = l.max(axis=1, keepdims=True)
     p = np.exp(l - m)
     p = p / p.sum(axis=1, keepdims=True)
-    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    return np.take_along_axis(p, ids.astype(np.int64), axis=1)
+
+
+def renormalised_weights(logits32: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Softmax over all E logits, then renormalised over the chosen k:
+    w_j = p[id_j] / sum_j' p[id_j'].  fp64 [T][k]."""
+    sel = softmax_weights(logits32, ids)
     return sel / sel.sum(axis=1, keepdims=True)
 
 
-def route(x_bits, wr_bits, k: int, bias=None, exact: bool = False):
-    """(ids int32 [T][k], weights fp64 [T][k], logits fp32 [T][E])."""
+def route(x_bits, wr_bits, k: int, bias=None, exact: bool = False, renorm: bool = True):
+    """(ids int32 [T][k], weights fp64 [T][k], logits fp32 [T][E]).
+
+    renorm=False keeps the full-softmax probabilities of the chosen experts
+    (the router variant without top-k renormalisation)."""
     l32 = router_logits(x_bits, wr_bits, bias, exact=exact)
     ids = topk_lowest_index(l32, k)
-    w = renormalised_weights(l32, ids)
+    w = renormalised_weights(l32, ids) if renorm else softmax_weights(l32, ids)
     return ids, w, l32
 
 
@@ -247,12 +257,12 @@ def expert_mlp(x64: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) 
 # full block
 # --------------------------------------------------------------------------
 def forward_per_token(inp, weights: Optional[ExpertWeights] = None, exact_router: bool = False,
-                      routing=None):
+                      routing=None, renorm: bool = True):
     """The definition: loop over tokens, then over the k chosen experts.
 
     Returns (out fp64 [T][H], routing dict)."""
     if routing is None:
-        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias, exact=exact_router)
+        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias, exact=exact_router, renorm=renorm)
     else:
         ids, w, l32 = routing["ids"], routing["w"], routing["logits"]
     W = weights or ExpertWeights(inp)
@@ -267,13 +277,13 @@ def forward_per_token(inp, weights: Optional[ExpertWeights] = None, exact_router
     return out, dict(ids=ids, w=w, logits=l32)
 
 
-def forward_batched(inp, weights: Optional[ExpertWeights] = None, routing=None):
+def forward_batched(inp, weights: Optional[ExpertWeights] = None, routing=None, renorm: bool = True):
     """Same arithmetic grouped by expert: for each expert, one matmul over the
     tokens routed to it, then the per-token weighted sum in ascending j.
 
     Returns (out fp64 [T][H], routing dict incl. counts/offsets/perm/pos)."""
     if routing is None:
-        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias)
+        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias, renorm=renorm)
     else:
         ids, w, l32 = routing["ids"], routing["w"], routing["logits"]
     counts, offsets, perm, pos = permute(ids, inp.E)

@@ -29,6 +29,13 @@ def no_renormalisation(logits32, ids):
     return np.take_along_axis(p, ids.astype(np.int64), axis=1)
 
 
+def renormalised_anyway(logits32, ids):
+    l = np.asarray(logits32, dtype=np.float64)
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
 def sigmoid_not_silu(z):
     return 1.0 / (1.0 + np.exp(-z))
 
@@ -88,6 +95,9 @@ MUTATIONS = {
                              [P.test_hand_worked_block_closed_form, P.test_identical_router_rows_lower_index_wins]),
     "no_renormalisation": (lambda mp: patch(mp, "renormalised_weights", no_renormalisation),
                            [P.test_hand_worked_block_closed_form, P.test_weights_sum_to_one_and_are_positive]),
+    "unrenormalised_variant_renormalises": (lambda mp: patch(mp, "softmax_weights", renormalised_anyway),
+                                            [P.test_unrenormalised_hand_closed_form,
+                                             P.test_unrenormalised_weights_are_softmax_mass_of_the_chosen]),
     "sigmoid_not_silu": (lambda mp: patch(mp, "silu", sigmoid_not_silu),
                          [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
     "gate_up_swapped": (swap_gate_up,

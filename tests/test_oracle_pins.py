@@ -171,6 +171,46 @@ def test_k_one_weight_is_one():
     np.testing.assert_array_equal(ids[:, 0], np.argmax(l, axis=1))
 
 
+def test_unrenormalised_hand_closed_form():
+    """The variant without top-k renormalisation, by hand on the same inputs:
+    token 0 softmax denominator Z = e^2 + 2e + e^(1/2); w = [e^2, e] / Z.
+    y0 = [h0, -h0] with h0 = e/(e+1); y1 = [h1/2, h1/4] with h1 = -2/(1+e).
+    token 1: four equal logits, w = [1/4, 1/4], out = 0."""
+    inp = hand_inputs()
+    out, r = O.forward_per_token(inp, exact_router=True, renorm=False)
+    e = math.e
+    Z = e * e + 2 * e + math.sqrt(e)
+    w0, w1 = e * e / Z, e / Z
+    np.testing.assert_array_equal(r["ids"], [[0, 1], [0, 1]])
+    np.testing.assert_allclose(r["w"][0], [w0, w1], rtol=0, atol=1e-15)
+    assert r["w"][1].tolist() == [0.25, 0.25]
+    h0, h1 = e / (e + 1), -2 / (1 + e)
+    np.testing.assert_allclose(out[0], [w0 * h0 + w1 * h1 / 2, -w0 * h0 + w1 * h1 / 4], rtol=0, atol=1e-15)
+    assert out[1].tolist() == [0.0, 0.0]
+    out_b, _ = O.forward_batched(inp, renorm=False)
+    np.testing.assert_allclose(out_b, out, rtol=0, atol=1e-15)
+
+
+def test_unrenormalised_weights_are_softmax_mass_of_the_chosen():
+    """w_j = p[id_j] from scipy's softmax; the weights sum to 1 minus the mass
+    of the experts not chosen; dividing by their sum gives the renormalised
+    weights; k = E gives the whole softmax (sum 1)."""
+    for name in ("tiny", "q8"):
+        inp = S.make(name)
+        ids, w, l = O.route(inp.x, inp.w_router, inp.k, inp.bias, renorm=False)
+        ids_r, w_r, _ = O.route(inp.x, inp.w_router, inp.k, inp.bias)
+        np.testing.assert_array_equal(ids, ids_r)
+        p = scipy.special.softmax(l.astype(np.float64), axis=1)
+        np.testing.assert_allclose(w, np.take_along_axis(p, ids.astype(np.int64), 1), rtol=1e-13, atol=0)
+        rest = p.sum(axis=1) - np.take_along_axis(p, ids.astype(np.int64), 1).sum(axis=1)
+        assert np.all(w.sum(axis=1) <= 1.0 + 1e-15)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0 - rest, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(w / w.sum(axis=1, keepdims=True), w_r, rtol=1e-13, atol=0)
+    inp = S.make("tiny")
+    ids, w, l = O.route(inp.x, inp.w_router, inp.E, renorm=False)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- bucketing
 def check_bucketing(ids, E):
     T, k = ids.shape
