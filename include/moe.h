@@ -57,15 +57,28 @@ typedef enum {
   MOE_W_NF4_B64_TILED = 3   /* MOE_W_NF4_B64 in the tiled layout written by moe_pack_weights */
 } moe_wformat;
 
+typedef enum {
+  MOE_OUT_F32 = 0,   /* out fp32 [T][H] */
+  MOE_OUT_BF16 = 1   /* out bf16 [T][H]: the fp32 result rounded to nearest even */
+} moe_outdtype;
+
+typedef enum {
+  MOE_TOPK_RENORM = 0,  /* w_j = softmax over the k chosen logits (= full softmax renormalised) */
+  MOE_TOPK_SOFTMAX = 1  /* w_j = softmax over all E logits, taken at the k chosen (sum < 1) */
+} moe_topk_weights;
+
 /* Shape of one MoE layer.  t_max bounds T for every call made with this
- * config and sizes the workspace. */
+ * config and sizes the workspace.  Zero-initialised trailing fields give the
+ * defaults (fp32 output, renormalised top-k weights). */
 typedef struct {
-  int32_t hidden;     /* H: model width */
-  int32_t inter;      /* I: expert intermediate width */
-  int32_t n_experts;  /* E */
-  int32_t top_k;      /* k */
-  int32_t t_max;      /* largest token count T passed with this config */
-  int32_t wfmt;       /* moe_wformat */
+  int32_t hidden;       /* H: model width */
+  int32_t inter;        /* I: expert intermediate width */
+  int32_t n_experts;    /* E */
+  int32_t top_k;        /* k */
+  int32_t t_max;        /* largest token count T passed with this config */
+  int32_t wfmt;         /* moe_wformat */
+  int32_t out_dtype;    /* moe_outdtype */
+  int32_t topk_weights; /* moe_topk_weights */
 } moe_config;
 
 /* Layer weights (device, read-only).  Expert tensors are stacked on E.
@@ -120,8 +133,10 @@ size_t moe_workspace_size(const moe_config* cfg);
 
 /* Router: fp32 logits l[t][e] = sum_h x[t][h]*w_router[e][h] (+ bias[e]),
  * the top-k experts per token (largest logit first, equal logits -> lower
- * expert index) and their renormalised softmax weights
- * w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0).
+ * expert index) and their softmax weights: renormalised over the chosen,
+ * w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0) (MOE_TOPK_RENORM), or the
+ * full softmax over all E experts at the chosen ones (MOE_TOPK_SOFTMAX; the
+ * experts not chosen enter the sum with their bounded MFMA logits).
  * The k chosen experts and their order are those of the correctly rounded
  * fp32 logits: an MFMA pass gives each logit with a proven error bound, and
  * whenever the bound leaves the set or the order open, the candidates' dot
@@ -160,18 +175,19 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T
 /* Whole block: route -> permute -> grouped gate/up with SiLU*up ->
  * grouped down -> per-token weighted combine.
  *   x     bf16 [T][H]
- *   out   fp32 [T][H]: out[t] = sum_{j ascending} topk_w[t][j] * y[t][j]
+ *   out   [T][H], fp32 or bf16 (cfg->out_dtype): out[t] = sum_{j ascending}
+ *         topk_w[t][j] * y[t][j], formed in fp32 (bf16: then rounded to nearest even)
  *   workspace  >= moe_workspace_size(cfg) bytes, 256-byte aligned; its
  *              contents need no initialisation and are overwritten.
  * Calls sharing one workspace must be ordered on one stream. */
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
-                       float* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+                       void* out, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* moe_forward that also records `events[0..5]` (host array of hipEvent_t
  * created by the caller) on `stream` before route, permute, gate/up, down,
  * combine and after combine, for per-stage timing.  Same results. */
 moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x,
-                             int32_t T, float* out, void* workspace, size_t ws_bytes,
+                             int32_t T, void* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream, hipEvent_t* events /* host, 6 */);
 
 /* One-time conversion of row-major expert weights (cfg->wfmt = MOE_W_BF16 or
@@ -207,7 +223,7 @@ moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t 
 /* Per-batch-size hipGraphs of moe_forward (the bucketed decode-step capture
  * of the unsloth commit 80aaf1121b page, second paragraph): one graph per
  * bucket size, all reading `x_static` (bf16 [t_max][H]) and writing
- * `out_static` (fp32 [t_max][H]) through one shared workspace.  Those
+ * `out_static` ([t_max][H] in cfg->out_dtype) through one shared workspace.  Those
  * buffers and the weights must outlive the graph; their addresses are baked
  * in.  `buckets` (host) must be strictly ascending within [1, t_max].
  * `stream` must be a created stream (not NULL) that is not capturing.  On
@@ -216,7 +232,7 @@ moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t 
  * run moe_forward eagerly instead. */
 typedef struct moe_graph moe_graph;
 moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const int32_t* buckets,
-                             int32_t n_buckets, const void* x_static, float* out_static,
+                             int32_t n_buckets, const void* x_static, void* out_static,
                              void* workspace, size_t ws_bytes, hipStream_t stream,
                              moe_graph** graph /* host out */);
 

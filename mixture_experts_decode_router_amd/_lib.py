@@ -29,6 +29,10 @@ MOE_W_BF16 = 0
 MOE_W_NF4_B64 = 1
 MOE_W_BF16_TILED = 2
 MOE_W_NF4_B64_TILED = 3
+MOE_OUT_F32 = 0
+MOE_OUT_BF16 = 1
+MOE_TOPK_RENORM = 0
+MOE_TOPK_SOFTMAX = 1
 
 # every entry point include/moe.h declares
 EXPORTS = (
@@ -42,7 +46,8 @@ EXPORTS = (
 
 class moe_config(Structure):
     _fields_ = [("hidden", c_int32), ("inter", c_int32), ("n_experts", c_int32),
-                ("top_k", c_int32), ("t_max", c_int32), ("wfmt", c_int32)]
+                ("top_k", c_int32), ("t_max", c_int32), ("wfmt", c_int32),
+                ("out_dtype", c_int32), ("topk_weights", c_int32)]
 
 
 class moe_weights(Structure):

@@ -80,6 +80,11 @@ moe_status check_cfg(const moe_config* c) {
     snprintf(buf, sizeof buf, "t_max=%d out of range (need 1 <= t_max and t_max*top_k <= 65536)", c->t_max);
     return fail(MOE_ERR_UNSUPPORTED, buf);
   }
+  if ((c->out_dtype != MOE_OUT_F32 && c->out_dtype != MOE_OUT_BF16) ||
+      (c->topk_weights != MOE_TOPK_RENORM && c->topk_weights != MOE_TOPK_SOFTMAX)) {
+    snprintf(buf, sizeof buf, "unsupported out_dtype=%d or topk_weights=%d", c->out_dtype, c->topk_weights);
+    return fail(MOE_ERR_UNSUPPORTED, buf);
+  }
   return MOE_OK;
 }
 
@@ -145,7 +150,7 @@ T* at(void* base, size_t off) {
 // Enqueues the whole block; arguments already validated.
 // live: device row count for graph replays of a larger bucket (rows >= *live
 // are routed nowhere and not written), or null for an eager call of T rows.
-moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void* x, int32_t T, float* out,
+moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void* x, int32_t T, void* out,
                            void* ws, hipStream_t s, hipEvent_t* ev, const int32_t* live = nullptr) {
   const Layout L = layout(c);
   const int N = T * c.top_k;
@@ -165,6 +170,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ra.wts = at<float>(ws, L.wts);
   ra.logits = nullptr;
   ra.live = live;
+  ra.softmax_all = c.topk_weights == MOE_TOPK_SOFTMAX;
   if ((e = moe::launch_route(ra, at<float>(ws, L.route), s)) != hipSuccess) return hip_fail(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
@@ -227,13 +233,14 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ca.H = c.hidden;
   ca.k = c.top_k;
   ca.live = live;
+  ca.out_bf16 = c.out_dtype == MOE_OUT_BF16;
   if ((e = moe::launch_combine(ca, s)) != hipSuccess) return hip_fail(e, "combine launch");
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MOE_OK;
 }
 
 moe_status check_forward_args(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
-                              const float* out, const void* ws, size_t ws_bytes) {
+                              const void* out, const void* ws, size_t ws_bytes) {
   MOE_TRY(check_cfg(cfg));
   MOE_TRY(check_weights(*cfg, w));
   MOE_TRY(check_T(*cfg, T));
@@ -309,6 +316,7 @@ moe_status moe_route(const moe_config* cfg, const moe_weights* w, const void* x,
   ra.k = cfg->top_k;
   ra.ids = topk_ids;
   ra.wts = topk_w;
+  ra.softmax_all = cfg->topk_weights == MOE_TOPK_SOFTMAX;
   ra.logits = logits;
   const hipError_t e = moe::launch_route(ra, at<float>(workspace, layout(*cfg).route), stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e, "route launch");
@@ -342,13 +350,13 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T
   return e == hipSuccess ? MOE_OK : hip_fail(e, "permute launch");
 }
 
-moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, float* out,
+moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, void* out,
                        void* workspace, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_forward_args(cfg, w, x, T, out, workspace, ws_bytes));
   return enqueue_forward(*cfg, *w, x, T, out, workspace, stream, nullptr);
 }
 
-moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, float* out,
+moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, void* out,
                              void* workspace, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
   MOE_TRY(check_forward_args(cfg, w, x, T, out, workspace, ws_bytes));
   if (!events) return fail(MOE_ERR_INVALID_ARG, "events is NULL");
@@ -437,7 +445,7 @@ moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t 
 }
 
 moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const int32_t* buckets, int32_t n_buckets,
-                             const void* x_static, float* out_static, void* workspace, size_t ws_bytes,
+                             const void* x_static, void* out_static, void* workspace, size_t ws_bytes,
                              hipStream_t stream, moe_graph** graph) {
   if (!graph) return fail(MOE_ERR_INVALID_ARG, "graph out-pointer is NULL");
   *graph = nullptr;

@@ -11,6 +11,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <bool BF16>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
   const int c = (blockIdx.y * kThreads + threadIdx.x) * 4;
@@ -25,7 +26,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
   }
-  *reinterpret_cast<f32x4_t*>(a.out + (size_t)t * a.H + c) = acc;
+  if (BF16) {
+    const u32x2_t pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + (size_t)t * a.H + c) = pk;
+  } else {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + (size_t)t * a.H + c) = acc;
+  }
 }
 
 __global__ void set_live_kernel(int32_t* live, int T) { *live = T; }
@@ -34,7 +40,10 @@ __global__ void set_live_kernel(int32_t* live, int T) { *live = T; }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const dim3 grid(a.T, (a.H / 4 + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, a);
+  if (a.out_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

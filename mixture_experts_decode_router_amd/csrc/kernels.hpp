@@ -23,6 +23,7 @@ struct RouteArgs {
   float* wts;             // [T][k]
   float* logits;          // [T][E] or null
   const int32_t* live;    // device row count T_live <= T (graph replays), or null: rows >= T_live get no output
+  bool softmax_all;       // weights = full softmax over E at the chosen (else renormalised over the k)
 };
 // scratch: route_scratch_floats(t_max, E, H) floats of device memory
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s);
@@ -94,9 +95,10 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 struct CombineArgs {
   const float* y;         // [T*k][H]
   const float* wts;       // [T][k]
-  float* out;             // [T][H]
+  void* out;              // [T][H], fp32 or bf16
   int T, H, k;
   const int32_t* live;    // device row count, or null: rows >= live are not written
+  bool out_bf16;          // round the fp32 sums to bf16 (nearest even)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // *live = T (one thread), for graph replays of a bucket larger than T

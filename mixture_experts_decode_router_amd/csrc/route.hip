@@ -28,7 +28,9 @@
 //            over these values is the top-k of all experts.
 //
 // Softmax weights w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0), fp32, j in
-// selection order (equal to the full softmax renormalised over the top k).
+// selection order (equal to the full softmax renormalised over the top k);
+// or, for the un-renormalised form, the same numerators over the sum across
+// all E experts.
 #include <float.h>
 #include <limits.h>
 
@@ -420,10 +422,26 @@ __global__ __launch_bounds__(256) void route_select(SelParams P) {
   wave_sync_lds();
   // w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0); the sum is a butterfly over
   // lanes 0..k-1 (others add 0), the same on every run
-  const float pj = lane < k ? expf(s_selv[wave][lane] - s_selv[wave][0]) : 0.f;
+  const float lmax = s_selv[wave][0];
+  const float pj = lane < k ? expf(s_selv[wave][lane] - lmax) : 0.f;
   float sum = pj;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (a.softmax_all) {
+    // the full softmax: add the experts not chosen, with their MFMA logits
+    // (each lane its own experts in order, then a butterfly)
+    float rest = 0.f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int e = lane + 64 * m;
+      bool chosen = false;
+      for (int j = 0; j < k; ++j) chosen |= s_sele[wave][j] == e;
+      if (e < E && !chosen) rest += expf(av[m] - lmax);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) rest += __shfl_xor(rest, off);
+    sum += rest;
+  }
   if (lane < k) {
     a.ids[(size_t)t * k + lane] = s_sele[wave][lane];
     a.wts[(size_t)t * k + lane] = pj / sum;

@@ -3,6 +3,7 @@ methods that call the C entry points.  torch provides device memory and
 streams; every step of the block runs in the HIP library."""
 from __future__ import annotations
 
+import copy
 from typing import Optional, Sequence
 
 import numpy as np
@@ -26,12 +27,18 @@ class MoELayer:
     q_down, s_down, codebook) 4-bit arrays (see synthetic.MoEInputs).
     """
 
-    def __init__(self, inp, t_max: int, device: str = "cuda", tiled: bool = True):
+    def __init__(self, inp, t_max: int, device: str = "cuda", tiled: bool = True,
+                 out_bf16: bool = False, renorm: bool = True):
+        """out_bf16: bf16 output (else fp32); renorm: top-k weights renormalised
+        over the k chosen (else the full softmax at the chosen)."""
         self.device = torch.device(device)
         self.H, self.E, self.k, self.I = inp.H, inp.E, inp.k, inp.I
         rowmajor = L.MOE_W_BF16 if inp.wfmt == "bf16" else L.MOE_W_NF4_B64
         self.wfmt = rowmajor + 2 if tiled else rowmajor
-        self.cfg = L.moe_config(inp.H, inp.I, inp.E, inp.k, t_max, self.wfmt)
+        self.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
+        self.cfg = L.moe_config(inp.H, inp.I, inp.E, inp.k, t_max, self.wfmt,
+                                L.MOE_OUT_BF16 if out_bf16 else L.MOE_OUT_F32,
+                                L.MOE_TOPK_RENORM if renorm else L.MOE_TOPK_SOFTMAX)
         st = L.moe_config_check(self.cfg)
         if st != L.MOE_OK:
             raise L.MoEError(st, L.moe_last_error())
@@ -66,6 +73,19 @@ class MoELayer:
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.graph = None
 
+    def with_options(self, out_bf16: bool = False, renorm: bool = True) -> "MoELayer":
+        """The same device weights under another output dtype / top-k weight
+        mode, with a workspace of its own."""
+        other = copy.copy(self)
+        c = self.cfg
+        other.cfg = L.moe_config(c.hidden, c.inter, c.n_experts, c.top_k, c.t_max, c.wfmt,
+                                 L.MOE_OUT_BF16 if out_bf16 else L.MOE_OUT_F32,
+                                 L.MOE_TOPK_RENORM if renorm else L.MOE_TOPK_SOFTMAX)
+        other.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
+        other.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        other.graph = None
+        return other
+
     # ------------------------------------------------------------ helpers
     def upload_x(self, x_bits: np.ndarray) -> torch.Tensor:
         return _dev(x_bits, self.device)
@@ -98,7 +118,7 @@ class MoELayer:
                 stream=None) -> torch.Tensor:
         T = T or x.shape[0]
         if out is None:
-            out = torch.empty(T, self.H, dtype=torch.float32, device=self.device)
+            out = torch.empty(T, self.H, dtype=self.out_dtype, device=self.device)
         L.moe_forward(self.cfg, self.w, x, T, out, self.workspace, self.ws_bytes, stream)
         return out
 

@@ -47,9 +47,20 @@ QWEN = dict(hidden=2048, inter=768, n_experts=128, top_k=8)
 
 
 def cfg(**kw):
-    d = dict(QWEN, t_max=64, wfmt=L.MOE_W_BF16)
+    d = dict(QWEN, t_max=64, wfmt=L.MOE_W_BF16, out_dtype=L.MOE_OUT_F32, topk_weights=L.MOE_TOPK_RENORM)
     d.update(kw)
-    return L.moe_config(d["hidden"], d["inter"], d["n_experts"], d["top_k"], d["t_max"], d["wfmt"])
+    return L.moe_config(d["hidden"], d["inter"], d["n_experts"], d["top_k"], d["t_max"], d["wfmt"],
+                        d["out_dtype"], d["topk_weights"])
+
+
+def test_config_struct_layout():
+    """moe_config is eight int32 fields; zeroed trailing fields are the defaults."""
+    assert ctypes.sizeof(L.moe_config) == 32
+    assert [f for f, _ in L.moe_config._fields_][-2:] == ["out_dtype", "topk_weights"]
+    assert L.MOE_OUT_F32 == 0 and L.MOE_TOPK_RENORM == 0
+    six = L.moe_config(2048, 768, 128, 8, 64, L.MOE_W_BF16)
+    assert six.out_dtype == 0 and six.topk_weights == 0
+    assert L.moe_config_check(six) == L.MOE_OK
 
 
 def test_workspace_size_layout():
@@ -73,7 +84,8 @@ def test_workspace_size_layout():
 @pytest.mark.parametrize("bad", [
     dict(hidden=2000), dict(hidden=64), dict(hidden=8192), dict(inter=100), dict(n_experts=24),
     dict(n_experts=512), dict(top_k=0), dict(top_k=17), dict(n_experts=16, top_k=17),
-    dict(t_max=0), dict(t_max=8193, top_k=8), dict(wfmt=7),
+    dict(t_max=0), dict(t_max=8193, top_k=8), dict(wfmt=7), dict(out_dtype=2), dict(out_dtype=-1),
+    dict(topk_weights=2), dict(topk_weights=-1),
 ])
 def test_unsupported_configs(bad):
     assert L.moe_config_check(cfg(**bad)) == L.MOE_ERR_UNSUPPORTED
@@ -82,7 +94,9 @@ def test_unsupported_configs(bad):
 
 def test_supported_configs():
     for c in (cfg(), cfg(hidden=256, inter=128, n_experts=16, top_k=2), cfg(hidden=4096, inter=1536),
-              cfg(n_experts=256, top_k=16, t_max=4096), cfg(wfmt=L.MOE_W_NF4_B64)):
+              cfg(n_experts=256, top_k=16, t_max=4096), cfg(wfmt=L.MOE_W_NF4_B64),
+              cfg(out_dtype=L.MOE_OUT_BF16), cfg(topk_weights=L.MOE_TOPK_SOFTMAX),
+              cfg(wfmt=L.MOE_W_NF4_B64, out_dtype=L.MOE_OUT_BF16, topk_weights=L.MOE_TOPK_SOFTMAX)):
         assert L.moe_config_check(c) == L.MOE_OK, L.moe_last_error()
 
 
