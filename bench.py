@@ -166,6 +166,37 @@ def summarize_traffic(fetch_dir, write_dir, workload):
                 fetch_scale=round(cf, 4), write_scale=round(cw, 4), kernels=kernels)
 
 
+def measure_ceilings(torch, L, stream):
+    """Achievable rates on this chip, measured beside the block: a plain
+    1 GiB device copy (bytes read + written per second) and the vendor
+    library's dense bf16 GEMM at 8192^3."""
+    ev = L.hip_events(2, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
+
+    def timed(fn, reps):
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                fn()
+            L.hip_event_record(ev[0], stream)
+            for _ in range(reps):
+                fn()
+            L.hip_event_record(ev[1], stream)
+        torch.cuda.synchronize()
+        return L.hip_event_elapsed_ms(ev[0], ev[1]) * 1e-3 / reps
+
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    t_gemm = timed(lambda: torch.mm(a, b), 10)
+    del a, b
+    L.hip_events_destroy(ev)
+    return {"device_copy_GBps": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "vendor_bf16_gemm_TFLOPs": round(2.0 * n ** 3 / t_gemm / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +207,7 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / vendor GEMM ceiling measurement")
     ap.add_argument("--row-major", action="store_true",
                     help="keep expert weights row-major instead of the tiled layout")
     ap.add_argument("--sweep", action="store_true", help="also time every decode bucket (stderr + JSON extra)")
@@ -272,23 +304,50 @@ def main():
     L.hip_events_destroy(evs)
     log("[bench] stage us: " + ", ".join(f"{n} {v:.1f}" for n, v in stage_us.items()))
 
-    # ---------------- cold replays: a 512 MiB scrub between steps (outside the events)
-    cold_us = None
+    # ---------------- per-replay spread: one event between consecutive replays
+    R_ = args.stage_steps
+    evr = L.hip_events(R_ + 1, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
+    L.hip_event_record(evr[0], stream)
+    for i in range(R_):
+        lay.replay(T, stream)
+        L.hip_event_record(evr[i + 1], stream)
+    torch.cuda.synchronize()
+    per = np.array([L.hip_event_elapsed_ms(evr[i], evr[i + 1]) * 1e3 for i in range(R_)])
+    L.hip_events_destroy(evr)
+    replay_pct = {q: round(float(np.percentile(per, p)), 2) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
+    log(f"[bench] replay us p10/p50/p90: {replay_pct['p10']}/{replay_pct['p50']}/{replay_pct['p90']}")
+
+    # ---------------- cold replays: 512 MiB scrub between steps (outside the
+    # events), read-only (evicts L2 and the 256 MB last-level cache without
+    # leaving dirty lines to write back during the step) and, for comparison,
+    # by writing
+    cold = {}
     if args.cold_steps > 0:
-        scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        evc = L.hip_events(2)
-        tot = 0.0
-        with torch.cuda.stream(stream):
-            for i in range(args.cold_steps):
-                scrub.fill_(i & 0xFF)
-                L.hip_event_record(evc[0], stream)
-                lay.replay(T, stream)
-                L.hip_event_record(evc[1], stream)
-                tot += L.hip_event_elapsed_ms(evc[0], evc[1])
+        scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        evc = L.hip_events(2, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        for mode in ("read", "write"):
+            tot = 0.0
+            with torch.cuda.stream(stream):
+                for i in range(args.cold_steps):
+                    if mode == "read":
+                        scrub.max()
+                    else:
+                        scrub.fill_(i & 0xFF)
+                    L.hip_event_record(evc[0], stream)
+                    lay.replay(T, stream)
+                    L.hip_event_record(evc[1], stream)
+                    tot += L.hip_event_elapsed_ms(evc[0], evc[1])
+            cold[mode] = tot * 1e3 / args.cold_steps
         L.hip_events_destroy(evc)
-        cold_us = tot * 1e3 / args.cold_steps
         del scrub
-        log(f"[bench] cold replay {cold_us:.1f} us/step")
+        log(f"[bench] cold replay {cold['read']:.1f} us/step (read scrub), {cold['write']:.1f} (write scrub)")
+
+    # ---------------- measured ceilings of this chip in the same run
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(torch, L, stream)
+        log(f"[bench] ceilings: device copy {ceilings['device_copy_GBps']:.0f} GB/s, "
+            f"vendor bf16 GEMM {ceilings['vendor_bf16_gemm_TFLOPs']:.0f} TFLOP/s")
 
     dominant = "gate_up"
     dom_us = stage_us[dominant]
@@ -353,8 +412,11 @@ def main():
             "n_active_experts": n_act,
             "stage_us": {n: round(v, 2) for n, v in stage_us.items()},
             "gpu_event_us_per_step": round(gpu_ms * 1e3 / args.steps, 2),
-            "cold_us_per_step": None if cold_us is None else round(cold_us, 2),
+            "replay_us": replay_pct,
+            "cold_us_per_step": round(cold["read"], 2) if cold else None,
+            "cold_write_scrub_us_per_step": round(cold["write"], 2) if cold else None,
         },
+        "ceilings": ceilings,
     }
 
     if args.sweep and T <= 64:
