@@ -26,6 +26,9 @@ What it computes (Qwen3-MoE sparse block, decode or prefill, one layer):
   5. experts         SwiGLU MLP per chosen expert: g = Wg x, u = Wu x,
                      h = silu(g) * u with silu(z) = z / (1 + exp(-z)),
                      y = Wd h  (the grouped GEMMs of the same path).
+  0. (optional)      the pre-block step: r = bf16(residual + delta),
+                     x = bf16(r / sqrt(mean(r^2) + eps) * gamma), the
+                     block's input [a1bc5cbd page, first paragraph].
   6. combine         out[t] = sum_j w[t,j] * y[t,j], j ascending (the
                      index_add_ step of the same path), returned as a plain
                      tensor [unsloth commit 4f2bfe7f69 page (first MoE decode
@@ -58,6 +61,29 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> exact fp64 values."""
     u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_rne(v: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bit pattern, one rounding to nearest, ties to even
+    (zeros and finite values in the bf16 normal range).  Not via fp32: that
+    would round twice."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    u = v.view(np.uint64)
+    sign = (u >> np.uint64(63)).astype(np.uint64)
+    mag = u & np.uint64(0x7FFFFFFFFFFFFFFF)
+    # bf16 keeps 7 of the 52 fraction bits: drop 45, round to nearest even
+    keep = mag >> np.uint64(45)
+    rest = mag & np.uint64((1 << 45) - 1)
+    half = np.uint64(1 << 44)
+    up = (rest > half) | ((rest == half) & ((keep & np.uint64(1)) == np.uint64(1)))
+    keep = keep + up.astype(np.uint64)
+    # rebias the exponent from 1023 to 127 (bits above the 7 fraction bits)
+    exp = (keep >> np.uint64(7)).astype(np.int64) - 1023 + 127
+    frac = (keep & np.uint64(0x7F)).astype(np.int64)
+    zero = mag == np.uint64(0)
+    assert np.all(zero | ((exp > 0) & (exp < 255))), "value outside the bf16 normal range"
+    bits = (sign.astype(np.int64) << 15) | np.where(zero, 0, (exp << 7) | frac)
+    return bits.astype(np.uint16)
 
 
 def nf4_unpack(packed: np.ndarray) -> np.ndarray:
@@ -146,6 +172,25 @@ def route(x_bits, wr_bits, k: int, bias=None, exact: bool = False, renorm: bool 
     ids = topk_lowest_index(l32, k)
     w = renormalised_weights(l32, ids) if renorm else softmax_weights(l32, ids)
     return ids, w, l32
+
+
+# --------------------------------------------------------------------------
+# pre-block step: residual add, RMSNorm (the layernorm + residual + router
+# fusion of the a1bc5cbd page, first paragraph)
+# --------------------------------------------------------------------------
+def residual_rmsnorm(residual_bits, delta_bits, gamma_bits, eps):
+    """r = bf16(residual + delta) (the exact sum rounded once to nearest
+    even; delta None: r = residual); x = r / sqrt(mean_h(r^2) + eps) * gamma
+    in fp64.  Returns (r bits uint16 [T][H], x fp64 [T][H]); the block's
+    input is x rounded once to bf16."""
+    r = bf16_bits_to_f64(residual_bits)
+    if delta_bits is not None:
+        r = r + bf16_bits_to_f64(delta_bits)   # exact: two bf16 values
+    r_bits = f64_to_bf16_rne(r)
+    r = bf16_bits_to_f64(r_bits)
+    ms = np.mean(r * r, axis=1, keepdims=True)
+    x = r / np.sqrt(ms + float(eps)) * bf16_bits_to_f64(gamma_bits)[None, :]
+    return r_bits, x
 
 
 # --------------------------------------------------------------------------

@@ -258,6 +258,24 @@ def make(name: str, T: Optional[int] = None) -> MoEInputs:
     return MoEInputs(name, Tn, H, E, k, I, "bf16", x, wr, bias, wgu, wd)
 
 
+# pre-block inputs of the fused residual + RMSNorm + router step
+PRENORM_EPS = 1e-6     # Qwen3's RMSNorm epsilon
+_PRENORM_SEED = 3001
+
+
+def prenorm_inputs(T: int, H: int, seed=None) -> dict:
+    """Residual stream (std 2), the sublayer output added to it (std 1) and
+    the norm's per-channel weight (mean 1, std 0.25), all bf16, plus eps.
+    Independent streams per part: (seed, 0) residual, (seed, 1) delta,
+    (seed, 2) gamma."""
+    seed = _PRENORM_SEED if seed is None else seed
+    res = _normal_bf16(np.random.Generator(np.random.PCG64([seed, 0])), (T, H), 2.0)
+    delta = _normal_bf16(np.random.Generator(np.random.PCG64([seed, 1])), (T, H), 1.0)
+    g = np.random.Generator(np.random.PCG64([seed, 2])).standard_normal(H, dtype=np.float32)
+    gamma = f32_to_bf16_bits(np.float32(1.0) + np.float32(0.25) * g)
+    return dict(residual=res, delta=delta, gamma=gamma, eps=np.float32(PRENORM_EPS))
+
+
 def make_small(T: int, H: int, E: int, k: int, I: int, seed: int, wfmt: str = "bf16",
                bias: bool = False, x_std: float = 1.0, w_std: float = 0.02) -> MoEInputs:
     """Arbitrary small shape for edge-case tests (own seed, one draw order:

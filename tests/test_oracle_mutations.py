@@ -9,6 +9,7 @@ import oracle as O
 import oracle.moe_oracle as M
 from tests import test_formats_pins as F
 from tests import test_oracle_pins as P
+from tests import test_prenorm_pins as N
 
 
 def patch(monkeypatch, name, fn):
@@ -64,6 +65,28 @@ def swapped_nibbles(packed):
     return out
 
 
+def rne_through_fp32(v):
+    return ORIG_RNE(np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
+def norm_variant(kind):
+    def f(residual_bits, delta_bits, gamma_bits, eps):
+        r = M.bf16_bits_to_f64(residual_bits)
+        if delta_bits is not None and kind != "delta_dropped":
+            r = r + M.bf16_bits_to_f64(delta_bits)
+        r_bits = M.f64_to_bf16_rne(r)
+        r = M.bf16_bits_to_f64(r_bits)
+        if kind == "sum_not_mean":
+            ms = np.sum(r * r, axis=1, keepdims=True)
+        else:
+            ms = np.mean(r * r, axis=1, keepdims=True)
+        e = 0.0 if kind == "eps_ignored" else float(eps)
+        g = 1.0 if kind == "gamma_ignored" else M.bf16_bits_to_f64(gamma_bits)[None, :]
+        return r_bits, r / np.sqrt(ms + e) * g
+    return f
+
+
+ORIG_RNE = M.f64_to_bf16_rne
 ORIG_STABLE = M.stable_permute
 ORIG_LOGITS = M.router_logits
 ORIG_UNPACK = M.nf4_unpack
@@ -98,6 +121,16 @@ MUTATIONS = {
     "unrenormalised_variant_renormalises": (lambda mp: patch(mp, "softmax_weights", renormalised_anyway),
                                             [P.test_unrenormalised_hand_closed_form,
                                              P.test_unrenormalised_weights_are_softmax_mass_of_the_chosen]),
+    "bf16_rounding_through_fp32": (lambda mp: patch(mp, "f64_to_bf16_rne", rne_through_fp32),
+                                   [N.test_rne_is_nearest_with_ties_to_even]),
+    "norm_delta_dropped": (lambda mp: patch(mp, "residual_rmsnorm", norm_variant("delta_dropped")),
+                           [N.test_residual_add_matches_torch_bf16_add]),
+    "norm_sum_not_mean": (lambda mp: patch(mp, "residual_rmsnorm", norm_variant("sum_not_mean")),
+                          [N.test_rmsnorm_matches_torch_rms_norm, N.test_rmsnorm_constant_row_closed_form]),
+    "norm_eps_ignored": (lambda mp: patch(mp, "residual_rmsnorm", norm_variant("eps_ignored")),
+                         [N.test_rmsnorm_constant_row_closed_form]),
+    "norm_gamma_ignored": (lambda mp: patch(mp, "residual_rmsnorm", norm_variant("gamma_ignored")),
+                           [N.test_rmsnorm_matches_torch_rms_norm, N.test_rmsnorm_constant_row_closed_form]),
     "sigmoid_not_silu": (lambda mp: patch(mp, "silu", sigmoid_not_silu),
                          [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
     "gate_up_swapped": (swap_gate_up,
