@@ -190,6 +190,36 @@ moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const 
                              int32_t T, void* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream, hipEvent_t* events /* host, 6 */);
 
+/* The pre-block step fused into the block's router pass (the layernorm +
+ * residual + router fusion of the unsloth commit a1bc5cbd page, first
+ * paragraph), per row t:
+ *   r = bf16(residual + delta)                        (rounded once, nearest even)
+ *   x = bf16(r / sqrt(mean_h(r^2) + eps) * gamma)     (formed in fp32, rounded once)
+ * x is the block's input.  Every workgroup of the router pass that covers a
+ * row forms the row's mean square in one fixed order, so x is the same
+ * whatever the batch; an element of x may differ by one bf16 step from the
+ * correctly rounded value only where that value lies within fp32 rounding
+ * of a midpoint between two bf16 numbers. */
+typedef struct {
+  const void* residual;  /* bf16 [T][H]: the residual stream */
+  const void* delta;     /* bf16 [T][H]: added to it first (the sublayer output), or NULL (r = residual) */
+  const void* gamma;     /* bf16 [H]: the RMSNorm weight */
+  float eps;             /* RMSNorm epsilon, finite and > 0 */
+  void* residual_out;    /* bf16 [T][H]: r, or NULL */
+  void* x_out;           /* bf16 [T][H]: x, which the rest of the block reads */
+} moe_prenorm;
+
+/* moe_forward with the pre-block step: x is formed from pn (see
+ * moe_prenorm), written to pn->x_out (and r to pn->residual_out), then the
+ * block runs on it; out, the routing arrays in the workspace and x_out are
+ * bit-identical to moe_prenorm's x followed by moe_forward(x).  All pointers
+ * 16-byte aligned; x_out and residual_out must not overlap residual, delta,
+ * gamma or each other (the router pass reads whole rows in every workgroup
+ * while others write) -> MOE_ERR_INVALID_ARG. */
+moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, const moe_prenorm* pn,
+                               int32_t T, void* out, void* workspace, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* One-time conversion of row-major expert weights (cfg->wfmt = MOE_W_BF16 or
  * MOE_W_NF4_B64) into the tiled layout of MOE_W_BF16_TILED /
  * MOE_W_NF4_B64_TILED, in which every 16-row MFMA fragment of a k-step is
@@ -236,13 +266,23 @@ moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const 
                              void* workspace, size_t ws_bytes, hipStream_t stream,
                              moe_graph** graph /* host out */);
 
+/* moe_graph_capture of moe_forward_prenorm: the graphs read the buffers of
+ * `pn_static` ([t_max][H] each; gamma [H]) and write its x_out, residual_out
+ * and `out_static`; replay as above (rows [T, bucket) of x_out and
+ * residual_out are left untouched too). */
+moe_status moe_graph_capture_prenorm(const moe_config* cfg, const moe_weights* w, const int32_t* buckets,
+                                     int32_t n_buckets, const moe_prenorm* pn_static, void* out_static,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream,
+                                     moe_graph** graph /* host out */);
+
 /* Launches the graph of the smallest bucket >= T on `stream`.  The captured
  * kernels read a live row count kept in the workspace: rows [T, bucket) of
  * x_static are routed to no expert and counted nowhere (counts sum to T*k),
  * and rows [T, bucket) of out_static are left untouched; rows < T are
  * bit-identical to moe_forward of those T rows.  The count is rewritten (one
- * one-thread kernel on `stream`) only when T differs from the previous
- * replay of this graph.  A graph must be replayed from one thread at a time.
+ * one-thread kernel on `stream`) only when T differs from the count last
+ * enqueued into that workspace by any graph of this process.  A graph must be
+ * replayed from one thread at a time.
  * T larger than the largest bucket -> MOE_ERR_INVALID_ARG. */
 moe_status moe_graph_replay(moe_graph* graph, int32_t T, hipStream_t stream);
 

@@ -40,7 +40,7 @@ EXPORTS = (
     "moe_route", "moe_permute", "moe_forward", "moe_forward_timed", "moe_pack_weights",
     "moe_workspace_views",
     "moe_read_counts", "moe_graph_capture", "moe_graph_replay", "moe_graph_bucket_for",
-    "moe_graph_destroy",
+    "moe_graph_destroy", "moe_forward_prenorm", "moe_graph_capture_prenorm",
 )
 
 
@@ -54,6 +54,11 @@ class moe_weights(Structure):
     _fields_ = [("w_router", c_void_p), ("router_bias", c_void_p), ("w_gate_up", c_void_p),
                 ("w_down", c_void_p), ("q_gate_up", c_void_p), ("s_gate_up", c_void_p),
                 ("q_down", c_void_p), ("s_down", c_void_p), ("codebook", c_void_p)]
+
+
+class moe_prenorm(Structure):
+    _fields_ = [("residual", c_void_p), ("delta", c_void_p), ("gamma", c_void_p), ("eps", ctypes.c_float),
+                ("residual_out", c_void_p), ("x_out", c_void_p)]
 
 
 class moe_views(Structure):
@@ -103,6 +108,11 @@ def lib() -> ctypes.CDLL:
         "moe_graph_replay": (S, [c_void_p, c_int32, c_void_p]),
         "moe_graph_bucket_for": (c_int32, [c_void_p, c_int32]),
         "moe_graph_destroy": (None, [c_void_p]),
+        "moe_forward_prenorm": (S, [POINTER(moe_config), POINTER(moe_weights), POINTER(moe_prenorm), c_int32,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]),
+        "moe_graph_capture_prenorm": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
+                                          POINTER(moe_prenorm), c_void_p, c_void_p, c_size_t, c_void_p,
+                                          POINTER(c_void_p)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -175,6 +185,17 @@ def moe_forward(cfg, w, x, T, out, workspace, ws_bytes=None, stream=None):
                              ptr(workspace), ws_bytes, stream_handle(stream)))
 
 
+def make_prenorm(residual, delta, gamma, eps, residual_out, x_out) -> moe_prenorm:
+    return moe_prenorm(ptr(residual), ptr(delta), ptr(gamma), float(eps), ptr(residual_out), ptr(x_out))
+
+
+def moe_forward_prenorm(cfg, w, pn, T, out, workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().moe_forward_prenorm(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(pn), T, ptr(out),
+                                     ptr(workspace), ws_bytes, stream_handle(stream)))
+
+
 def moe_forward_timed(cfg, w, x, T, out, workspace, ws_bytes, stream, events):
     """`events`: six raw hipEvent_t handles (ints), see hip_events()."""
     arr = (c_void_p * 6)(*events)
@@ -212,6 +233,17 @@ def moe_graph_capture(cfg, w, buckets, x_static, out_static, workspace, ws_bytes
     _check(lib().moe_graph_capture(ctypes.byref(cfg), ctypes.byref(w), b, len(buckets), ptr(x_static),
                                    ptr(out_static), ptr(workspace), ws_bytes, stream_handle(stream),
                                    ctypes.byref(g)))
+    return g.value
+
+
+def moe_graph_capture_prenorm(cfg, w, buckets, pn_static, out_static, workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    b = (c_int32 * len(buckets))(*buckets)
+    g = c_void_p()
+    _check(lib().moe_graph_capture_prenorm(ctypes.byref(cfg), ctypes.byref(w), b, len(buckets),
+                                           ctypes.byref(pn_static), ptr(out_static), ptr(workspace), ws_bytes,
+                                           stream_handle(stream), ctypes.byref(g)))
     return g.value
 
 

@@ -1,7 +1,10 @@
 // Host implementation of the C ABI in include/moe.h: argument validation,
 // workspace carve-up, stream-ordered launches and per-bucket hipGraphs.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
+#include <map>
+#include <mutex>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -150,8 +153,10 @@ T* at(void* base, size_t off) {
 // Enqueues the whole block; arguments already validated.
 // live: device row count for graph replays of a larger bucket (rows >= *live
 // are routed nowhere and not written), or null for an eager call of T rows.
+// pn: fuse the pre-block step into the router pass; x is then its output.
 moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void* x, int32_t T, void* out,
-                           void* ws, hipStream_t s, hipEvent_t* ev, const int32_t* live = nullptr) {
+                           void* ws, hipStream_t s, hipEvent_t* ev, const int32_t* live = nullptr,
+                           const moe::PrenormArgs* pn = nullptr) {
   const Layout L = layout(c);
   const int N = T * c.top_k;
   hipError_t e;
@@ -171,6 +176,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ra.logits = nullptr;
   ra.live = live;
   ra.softmax_all = c.topk_weights == MOE_TOPK_SOFTMAX;
+  ra.pn = pn;
   if ((e = moe::launch_route(ra, at<float>(ws, L.route), s)) != hipSuccess) return hip_fail(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
@@ -250,6 +256,44 @@ moe_status check_forward_args(const moe_config* cfg, const moe_weights* w, const
   return MOE_OK;
 }
 
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b) return false;
+  const char *pa = static_cast<const char*>(a), *pb = static_cast<const char*>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// pn for rows [0, rows): pointers, eps, and no output overlapping an input
+moe_status check_prenorm(const moe_config& c, const moe_prenorm* pn, int32_t rows, moe::PrenormArgs* out) {
+  if (!pn) return fail(MOE_ERR_INVALID_ARG, "prenorm is NULL");
+  MOE_TRY(check_ptr(pn->residual, "residual"));
+  MOE_TRY(check_ptr(pn->gamma, "gamma"));
+  MOE_TRY(check_ptr(pn->x_out, "x_out"));
+  if (pn->delta) MOE_TRY(check_ptr(pn->delta, "delta"));
+  if (pn->residual_out) MOE_TRY(check_ptr(pn->residual_out, "residual_out"));
+  if (!(std::isfinite(pn->eps) && pn->eps > 0.f)) return fail(MOE_ERR_INVALID_ARG, "eps must be finite and > 0");
+  const size_t nb = (size_t)rows * c.hidden * 2, gb = (size_t)c.hidden * 2;
+  const void* ins[3] = {pn->residual, pn->delta, pn->gamma};
+  const size_t in_b[3] = {nb, nb, gb};
+  const void* outs[2] = {pn->x_out, pn->residual_out};
+  for (int o = 0; o < 2; ++o)
+    for (int i = 0; i < 3; ++i)
+      if (overlaps(outs[o], nb, ins[i], in_b[i]))
+        return fail(MOE_ERR_INVALID_ARG, "x_out / residual_out must not overlap residual, delta or gamma");
+  if (overlaps(pn->x_out, nb, pn->residual_out, nb))
+    return fail(MOE_ERR_INVALID_ARG, "x_out and residual_out overlap");
+  out->res = static_cast<const uint16_t*>(pn->residual);
+  out->delta = static_cast<const uint16_t*>(pn->delta);
+  out->gamma = static_cast<const uint16_t*>(pn->gamma);
+  out->eps = pn->eps;
+  out->res_out = static_cast<uint16_t*>(pn->residual_out);
+  return MOE_OK;
+}
+
+// last live row count enqueued into each workspace by a graph replay (shared
+// by every graph of the process that uses the workspace)
+std::mutex g_live_mu;
+std::map<const void*, int32_t> g_live_cache;
+
 }  // namespace
 
 struct moe_graph {
@@ -258,7 +302,6 @@ struct moe_graph {
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
   int32_t* live = nullptr;  // device row count read by the captured kernels (in the workspace)
-  int32_t live_set = -1;    // last value enqueued into *live (-1: not yet)
 };
 
 static void graph_release(moe_graph* g) {
@@ -356,6 +399,15 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
   return enqueue_forward(*cfg, *w, x, T, out, workspace, stream, nullptr);
 }
 
+moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, const moe_prenorm* pn, int32_t T,
+                               void* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!pn) return fail(MOE_ERR_INVALID_ARG, "prenorm is NULL");
+  MOE_TRY(check_forward_args(cfg, w, pn->x_out, T, out, workspace, ws_bytes));
+  moe::PrenormArgs pa{};
+  MOE_TRY(check_prenorm(*cfg, pn, T, &pa));
+  return enqueue_forward(*cfg, *w, pn->x_out, T, out, workspace, stream, nullptr, nullptr, &pa);
+}
+
 moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, void* out,
                              void* workspace, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
   MOE_TRY(check_forward_args(cfg, w, x, T, out, workspace, ws_bytes));
@@ -444,9 +496,12 @@ moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t 
   return e == hipSuccess ? MOE_OK : hip_fail(e, "hipStreamSynchronize");
 }
 
-moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const int32_t* buckets, int32_t n_buckets,
-                             const void* x_static, void* out_static, void* workspace, size_t ws_bytes,
-                             hipStream_t stream, moe_graph** graph) {
+}  // extern "C"
+
+static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, const int32_t* buckets,
+                               int32_t n_buckets, const void* x_static, const moe_prenorm* pn,
+                               void* out_static, void* workspace, size_t ws_bytes, hipStream_t stream,
+                               moe_graph** graph) {
   if (!graph) return fail(MOE_ERR_INVALID_ARG, "graph out-pointer is NULL");
   *graph = nullptr;
   MOE_TRY(check_forward_args(cfg, w, x_static, 1, out_static, workspace, ws_bytes));
@@ -455,6 +510,8 @@ moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const 
     if (buckets[i] < 1 || buckets[i] > cfg->t_max || (i && buckets[i] <= buckets[i - 1]))
       return fail(MOE_ERR_INVALID_ARG, "buckets must be strictly ascending within [1, t_max]");
   }
+  moe::PrenormArgs pa{};
+  if (pn) MOE_TRY(check_prenorm(*cfg, pn, buckets[n_buckets - 1], &pa));
   if (!stream) return fail(MOE_ERR_NOT_CAPTURABLE, "capture needs a created stream, not the NULL stream");
   hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(stream, &st);
@@ -464,6 +521,10 @@ moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const 
   moe_graph* g = new moe_graph();
   g->cfg = *cfg;
   g->live = at<int32_t>(workspace, layout(*cfg).live);
+  {
+    std::lock_guard<std::mutex> lk(g_live_mu);
+    g_live_cache[g->live] = -1;  // unknown until the first replay writes it
+  }
   for (int i = 0; i < n_buckets; ++i) {
     const int32_t b = buckets[i];
     e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
@@ -471,7 +532,8 @@ moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const 
       graph_release(g);
       return fail(MOE_ERR_NOT_CAPTURABLE, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
     }
-    const moe_status rs = enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr, g->live);
+    const moe_status rs =
+        enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr, g->live, pn ? &pa : nullptr);
     const std::string launch_msg = rs == MOE_OK ? std::string() : g_last_error;
     hipGraph_t gr = nullptr;
     e = hipStreamEndCapture(stream, &gr);
@@ -497,6 +559,24 @@ moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const 
   return MOE_OK;
 }
 
+extern "C" {
+
+moe_status moe_graph_capture(const moe_config* cfg, const moe_weights* w, const int32_t* buckets, int32_t n_buckets,
+                             const void* x_static, void* out_static, void* workspace, size_t ws_bytes,
+                             hipStream_t stream, moe_graph** graph) {
+  return capture_impl(cfg, w, buckets, n_buckets, x_static, nullptr, out_static, workspace, ws_bytes, stream,
+                      graph);
+}
+
+moe_status moe_graph_capture_prenorm(const moe_config* cfg, const moe_weights* w, const int32_t* buckets,
+                                     int32_t n_buckets, const moe_prenorm* pn_static, void* out_static,
+                                     void* workspace, size_t ws_bytes, hipStream_t stream, moe_graph** graph) {
+  if (graph) *graph = nullptr;
+  if (!pn_static) return fail(MOE_ERR_INVALID_ARG, "prenorm is NULL");
+  return capture_impl(cfg, w, buckets, n_buckets, pn_static->x_out, pn_static, out_static, workspace, ws_bytes,
+                      stream, graph);
+}
+
 int32_t moe_graph_bucket_for(const moe_graph* g, int32_t T) {
   if (!g || T < 1) return -1;
   for (int32_t b : g->buckets)
@@ -510,10 +590,14 @@ moe_status moe_graph_replay(moe_graph* g, int32_t T, hipStream_t stream) {
     if (g->buckets[i] >= T && T >= 1) {
       // the captured kernels read the live row count from the workspace; it
       // is rewritten (one tiny kernel) only when it changes
-      if (T != g->live_set) {
-        const hipError_t e = moe::launch_set_live(g->live, T, stream);
-        if (e != hipSuccess) return hip_fail(e, "live-count launch");
-        g->live_set = T;
+      {
+        std::lock_guard<std::mutex> lk(g_live_mu);
+        int32_t& cached = g_live_cache[g->live];
+        if (T != cached) {
+          const hipError_t e = moe::launch_set_live(g->live, T, stream);
+          if (e != hipSuccess) return hip_fail(e, "live-count launch");
+          cached = T;
+        }
       }
       const hipError_t e = hipGraphLaunch(g->execs[i], stream);
       return e == hipSuccess ? MOE_OK : hip_fail(e, "hipGraphLaunch");

@@ -14,8 +14,18 @@ constexpr int kSkinnyTile = 16;
 #endif
 constexpr int kMfmaTile = MOE_MFMA_TILE;
 
+// Pre-block step fused into the router pass: x = bf16(r / sqrt(mean(r^2) +
+// eps) * gamma) with r = bf16(res + delta), written to RouteArgs::x.
+struct PrenormArgs {
+  const uint16_t* res;    // bf16 [T][H]
+  const uint16_t* delta;  // bf16 [T][H] or null
+  const uint16_t* gamma;  // bf16 [H]
+  float eps;
+  uint16_t* res_out;      // bf16 [T][H] or null
+};
+
 struct RouteArgs {
-  const uint16_t* x;      // bf16 [T][H]
+  const uint16_t* x;      // bf16 [T][H] (with pn: written by the router pass, then read)
   const uint16_t* wr;     // bf16 [E][H]
   const float* bias;      // [E] or null
   int T, H, E, k;
@@ -24,6 +34,7 @@ struct RouteArgs {
   float* logits;          // [T][E] or null
   const int32_t* live;    // device row count T_live <= T (graph replays), or null: rows >= T_live get no output
   bool softmax_all;       // weights = full softmax over E at the chosen (else renormalised over the k)
+  const PrenormArgs* pn;  // host struct: fuse the pre-block step, or null
 };
 // scratch: route_scratch_floats(t_max, E, H) floats of device memory
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s);

@@ -54,19 +54,93 @@ struct PartParams {
   int per_wg;    // K splits summed inside one workgroup (1, or ks at large T)
   float* part;   // [ks / per_wg][T][E] partial logits
   float* pabs;   // [ks / per_wg][T][E] partial sums of |x*w|
+  // pre-block step (PN kernels only): the token operand is formed on the fly
+  // as x = bf16(r * scale * gamma), r = bf16(res + delta), and written out
+  const uint16_t* res;    // bf16 [T][H]
+  const uint16_t* delta;  // bf16 [T][H], or null (r = res)
+  const uint16_t* gamma;  // bf16 [H]
+  float eps;
+  uint16_t* res_out;      // bf16 [T][H] (r), or null
+  uint16_t* x_out;        // bf16 [T][H] (x)
+  const int32_t* live;    // rows >= *live are not written (graph replays), or null
 };
 
-// Wave w owns expert tiles w, w+4, ...; every wave walks the workgroup's
-// whole K slice, so no cross-wave reduction is needed.  U k-steps of loads
-// are in flight before the MFMAs consume them.
+__device__ __forceinline__ float round_bf16(float v) { return bf16lo(pack_bf16x2(v, 0.f)); }
+
+// r = bf16(res + delta) for the 8 elements of one chunk (the fp32 sum of two
+// bf16 values rounds to bf16 exactly as their exact sum does)
+__device__ __forceinline__ void residual8(u32x4_t rv, u32x4_t dv, float (&r)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r[2 * q] = round_bf16(bf16lo(rv[q]) + bf16lo(dv[q]));
+    r[2 * q + 1] = round_bf16(bf16hi(rv[q]) + bf16hi(dv[q]));
+  }
+}
+
+// Pre-block step, first part: 1 / sqrt(mean_h r^2 + eps) of the workgroup's
+// 16 rows into s_scale.  16 threads per row; thread i of a row sums r^2 over
+// chunks i, i + 16, ... (8 elements each, in order, fp32 fma), then a
+// butterfly over the 16 adds the partial sums.  Every workgroup that covers a
+// row gets the same bits.  Rows past T get 0.
+__device__ __forceinline__ void prenorm_scales(const PartParams& p, int t0, float* s_scale) {
+  constexpr int kPass = 16;  // chunks per thread per pass (one load round trip)
+  const int tid = threadIdx.x, rl = tid >> 4, sub = tid & 15;
+  const int row = t0 + rl;
+  const int nch = p.H >> 3;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  float ss = 0.f;
+  if (row < p.T) {
+    const uint16_t* rr = p.res + (size_t)row * p.H;
+    const uint16_t* dr = p.delta ? p.delta + (size_t)row * p.H : nullptr;
+    for (int c0 = 0; c0 < nch; c0 += 16 * kPass) {
+      u32x4_t rv[kPass], dv[kPass];
+#pragma unroll
+      for (int j = 0; j < kPass; ++j) {
+        const int c = c0 + sub + 16 * j;
+        rv[j] = c < nch ? ld16(rr + 8 * c) : zero;
+        dv[j] = (dr && c < nch) ? ld16(dr + 8 * c) : zero;
+      }
+#pragma unroll
+      for (int j = 0; j < kPass; ++j) {
+        float r[8];
+        residual8(rv[j], dv[j], r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(r[i], r[i], ss);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if (sub == 0) s_scale[rl] = row < p.T ? 1.0f / sqrtf(ss / (float)p.H + p.eps) : 0.f;
+  __syncthreads();
+}
+
+// Pre-block step, second part: one token fragment (8 elements of row r of
+// the tile at k = kk + 8g) -> x fragment, r returned in rout.
+__device__ __forceinline__ u32x4_t prenorm_x8(u32x4_t rv, u32x4_t dv, u32x4_t gv, float sc, u32x4_t& rout) {
+  float r[8];
+  residual8(rv, dv, r);
+  u32x4_t xo;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    xo[q] = pack_bf16x2(r[2 * q] * sc * bf16lo(gv[q]), r[2 * q + 1] * sc * bf16hi(gv[q]));
+    rout[q] = pack_bf16x2(r[2 * q], r[2 * q + 1]);
+  }
+  return xo;
+}
+
 // Wave w owns expert tiles w, w+4, ...; every wave walks the workgroup's
 // whole K range, so no cross-wave reduction is needed.  U k-steps of loads
 // are in flight before the MFMAs consume them.  A workgroup covers per_wg
 // consecutive K splits: each split is its own MFMA accumulation chain and
 // the split sums are added in split order, exactly as route_select adds
-// stored split partials, so both forms give the same bits.
-template <int NT, int U>  // NT: expert tiles per wave (>= ceil(E/64)); U: k-steps per batch
+// stored split partials, so both forms give the same bits.  PN: the token
+// operand comes from the pre-block step (prenorm_scales / prenorm_x8); wave
+// 0 writes the fragments it forms to x_out and res_out, so every element of
+// a live row is written by exactly one workgroup.
+template <int NT, int U, bool PN>  // NT: expert tiles per wave (>= ceil(E/64)); U: k-steps per batch
 __global__ __launch_bounds__(256) void route_partial(PartParams p) {
+  __shared__ float s_scale[PN ? kTok : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * kTok;
@@ -75,7 +149,16 @@ __global__ __launch_bounds__(256) void route_partial(PartParams p) {
   const int klen = H / p.ks;
   const int trow = t0 + r;
   const bool tv = trow < T;
-  const uint16_t* pb0 = p.x + (size_t)(tv ? trow : 0) * H + g * 8;
+  const uint16_t* pb0 = (PN ? p.res : p.x) + (size_t)(tv ? trow : 0) * H + g * 8;
+  const uint16_t* pd0 = PN && p.delta ? p.delta + (size_t)(tv ? trow : 0) * H + g * 8 : nullptr;
+  const uint16_t* pg0 = PN ? p.gamma + g * 8 : nullptr;
+  float sc = 0.f;
+  bool wr_out = false;
+  if constexpr (PN) {
+    prenorm_scales(p, t0, s_scale);
+    sc = s_scale[r];
+    wr_out = wave == 0 && tv && (!p.live || trow < *p.live);
+  }
   const uint16_t* pa0 = p.wr + (size_t)(wave * 16 + r) * H + g * 8;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   const uint32_t absm = 0x7fff7fffu;
@@ -93,6 +176,8 @@ __global__ __launch_bounds__(256) void route_partial(PartParams p) {
   const int nbatch = p.per_wg * klen / (32 * U);
   const int bps = klen / (32 * U);  // batches per split
   const uint16_t* pb = pb0 + kbase;
+  const uint16_t* pd = pd0 ? pd0 + kbase : nullptr;
+  const uint16_t* pg = PN ? pg0 + kbase : nullptr;
   const uint16_t* pa = pa0 + kbase;
   f32x4_t acc[NT], aab[NT];
 #pragma unroll
@@ -101,11 +186,16 @@ __global__ __launch_bounds__(256) void route_partial(PartParams p) {
     aab[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   u32x4_t b[U], av[U][NT];
+  u32x4_t db[PN ? U : 1], gb[PN ? U : 1];
   auto load = [&](int j) {
     const int kk = j * 32 * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       b[u] = tv ? ld16(pb + kk + 32 * u) : zero;
+      if constexpr (PN) {
+        db[u] = (tv && pd) ? ld16(pd + kk + 32 * u) : zero;
+        gb[u] = ld16(pg + kk + 32 * u);
+      }
 #pragma unroll
       for (int i = 0; i < NT; ++i)
         av[u][i] = (wave + 4 * i < n_et) ? ld16(pa + (size_t)i * 64 * H + kk + 32 * u) : zero;
@@ -116,7 +206,17 @@ __global__ __launch_bounds__(256) void route_partial(PartParams p) {
     u32x4_t bc[U], ac[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      bc[u] = b[u];
+      if constexpr (PN) {
+        u32x4_t rr;
+        bc[u] = prenorm_x8(b[u], db[u], gb[u], sc, rr);
+        if (wr_out) {
+          const size_t o = (size_t)trow * H + g * 8 + kbase + j * 32 * U + 32 * u;
+          *reinterpret_cast<u32x4_t*>(p.x_out + o) = bc[u];
+          if (p.res_out) *reinterpret_cast<u32x4_t*>(p.res_out + o) = rr;
+        }
+      } else {
+        bc[u] = b[u];
+      }
 #pragma unroll
       for (int i = 0; i < NT; ++i) ac[u][i] = av[u][i];
     }
@@ -474,13 +574,21 @@ int route_splits(int H) {
 
 size_t route_scratch_floats(int t_max, int E, int H) { return 2 * (size_t)route_splits(H) * t_max * E; }
 
-template <int NT>
+template <int NT, bool PN>
 void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
   const int klen = pp.H / pp.ks;
   if (klen % (32 * 4) == 0)
-    hipLaunchKernelGGL((route_partial<NT, 4>), grid, dim3(256), 0, s, pp);
+    hipLaunchKernelGGL((route_partial<NT, 4, PN>), grid, dim3(256), 0, s, pp);
   else
-    hipLaunchKernelGGL((route_partial<NT, 1>), grid, dim3(256), 0, s, pp);
+    hipLaunchKernelGGL((route_partial<NT, 1, PN>), grid, dim3(256), 0, s, pp);
+}
+
+template <int NT>
+void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
+  if (pp.res)
+    launch_partial<NT, true>(pp, grid, s);
+  else
+    launch_partial<NT, false>(pp, grid, s);
 }
 
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s) {
@@ -494,6 +602,15 @@ hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s) {
   const int per_wg = ntt >= 128 ? ks : 1;
   const int nst = ks / per_wg;  // stored partials per token
   PartParams pp{a.x, a.wr, a.T, a.H, a.E, ks, per_wg, scratch, scratch + (size_t)nst * a.T * a.E};
+  if (a.pn) {
+    pp.res = a.pn->res;
+    pp.delta = a.pn->delta;
+    pp.gamma = a.pn->gamma;
+    pp.eps = a.pn->eps;
+    pp.res_out = a.pn->res_out;
+    pp.x_out = const_cast<uint16_t*>(a.x);  // the block's x is the pre-block output
+    pp.live = a.live;
+  }
   const dim3 pgrid(ntt, nst);
   const int n_et = a.E / 16;
   if (n_et <= 4)

@@ -122,6 +122,23 @@ class MoELayer:
         L.moe_forward(self.cfg, self.w, x, T, out, self.workspace, self.ws_bytes, stream)
         return out
 
+    def forward_prenorm(self, residual: torch.Tensor, delta: Optional[torch.Tensor], gamma: torch.Tensor,
+                        eps: float, T: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                        x_out: Optional[torch.Tensor] = None, residual_out: Optional[torch.Tensor] = None,
+                        write_residual: bool = True, stream=None):
+        """The block with the pre-block step fused into its router pass (bf16
+        tensors as int16 bit patterns).  Returns (out, x_out, residual_out)."""
+        T = T or residual.shape[0]
+        if out is None:
+            out = torch.empty(T, self.H, dtype=self.out_dtype, device=self.device)
+        if x_out is None:
+            x_out = torch.empty(T, self.H, dtype=torch.int16, device=self.device)
+        if residual_out is None and write_residual:
+            residual_out = torch.empty(T, self.H, dtype=torch.int16, device=self.device)
+        pn = L.make_prenorm(residual, delta, gamma, eps, residual_out, x_out)
+        L.moe_forward_prenorm(self.cfg, self.w, pn, T, out, self.workspace, self.ws_bytes, stream)
+        return out, x_out, residual_out
+
     def forward_timed(self, x: torch.Tensor, out: torch.Tensor, events, T: Optional[int] = None,
                       stream=None) -> None:
         L.moe_forward_timed(self.cfg, self.w, x, T or x.shape[0], out, self.workspace, self.ws_bytes,
@@ -149,6 +166,15 @@ class MoELayer:
         self.release_graph()
         self.graph = L.moe_graph_capture(self.cfg, self.w, list(buckets), x_static, out_static,
                                          self.workspace, self.ws_bytes, stream)
+        return self.graph
+
+    def capture_prenorm(self, buckets: Sequence[int], residual: torch.Tensor, delta: Optional[torch.Tensor],
+                        gamma: torch.Tensor, eps: float, residual_out: Optional[torch.Tensor],
+                        x_out: torch.Tensor, out_static: torch.Tensor, stream) -> int:
+        self.release_graph()
+        pn = L.make_prenorm(residual, delta, gamma, eps, residual_out, x_out)
+        self.graph = L.moe_graph_capture_prenorm(self.cfg, self.w, list(buckets), pn, out_static,
+                                                 self.workspace, self.ws_bytes, stream)
         return self.graph
 
     def replay(self, T: int, stream=None) -> None:

@@ -201,3 +201,37 @@ def test_pack_validation_on_host():
     # 4-bit needs its four tensors
     c = cfg(wfmt=L.MOE_W_NF4_B64)
     assert lib.moe_pack_weights(ctypes.byref(c), ctypes.byref(w), ctypes.byref(other), None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_prenorm_validation_on_host():
+    c = cfg()
+    w = weights()
+    lib = L.lib()
+    wsb = L.moe_workspace_size(c)
+    H = c.hidden
+    row = 8 * H * 2  # bytes of 8 rows
+
+    def st(T=8, **kw):
+        d = dict(residual=FAKE, delta=FAKE + 4 * row, gamma=FAKE + 8 * row, eps=1e-6,
+                 residual_out=FAKE + 12 * row, x_out=FAKE + 16 * row)
+        d.update(kw)
+        pn = L.moe_prenorm(d["residual"], d["delta"], d["gamma"], d["eps"], d["residual_out"], d["x_out"])
+        return lib.moe_forward_prenorm(ctypes.byref(c), ctypes.byref(w), ctypes.byref(pn), T, FAKE * 3,
+                                       FAKE * 4, wsb, None)
+
+    assert lib.moe_forward_prenorm(ctypes.byref(c), ctypes.byref(w), None, 8, FAKE, FAKE, wsb, None) == \
+        L.MOE_ERR_INVALID_ARG
+    assert st(x_out=None) == L.MOE_ERR_INVALID_ARG
+    assert st(gamma=None) == L.MOE_ERR_INVALID_ARG
+    assert st(residual=FAKE + 2) == L.MOE_ERR_INVALID_ARG
+    for eps in (0.0, -1e-6, float("nan"), float("inf")):
+        assert st(eps=eps) == L.MOE_ERR_INVALID_ARG
+        assert "eps" in L.moe_last_error()
+    # outputs overlapping inputs (whole rows are read while others are written)
+    assert st(x_out=FAKE + row // 2) == L.MOE_ERR_INVALID_ARG
+    assert "overlap" in L.moe_last_error()
+    assert st(residual_out=FAKE) == L.MOE_ERR_INVALID_ARG
+    assert st(x_out=FAKE + 8 * row) == L.MOE_ERR_INVALID_ARG        # onto gamma
+    assert st(residual_out=FAKE + 16 * row) == L.MOE_ERR_INVALID_ARG  # onto x_out
+    assert st(T=0) == L.MOE_ERR_INVALID_ARG
+
