@@ -208,6 +208,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / vendor GEMM ceiling measurement")
+    ap.add_argument("--no-prenorm", action="store_true",
+                    help="skip the step with the fused pre-block residual add + RMSNorm")
     ap.add_argument("--row-major", action="store_true",
                     help="keep expert weights row-major instead of the tiled layout")
     ap.add_argument("--sweep", action="store_true", help="also time every decode bucket (stderr + JSON extra)")
@@ -342,6 +344,37 @@ def main():
         del scrub
         log(f"[bench] cold replay {cold['read']:.1f} us/step (read scrub), {cold['write']:.1f} (write scrub)")
 
+    # ---------------- the step with the pre-block residual add + RMSNorm fused
+    # into the router pass (graph replays, same weights, own workspace)
+    prenorm = None
+    if not args.no_prenorm and T <= 64:
+        pl = lay.with_options()
+        pin = S.prenorm_inputs(T, H)
+        res_s, del_s, gam_s = (pl.upload_x(pin[k]) for k in ("residual", "delta", "gamma"))
+        x_s = torch.empty(T, H, dtype=torch.int16, device="cuda")
+        r_s = torch.empty(T, H, dtype=torch.int16, device="cuda")
+        o_s = torch.empty(T, H, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        pl.capture_prenorm([T], res_s, del_s, gam_s, float(pin["eps"]), r_s, x_s, o_s, stream)
+        evp = L.hip_events(2, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        times = {}
+        for tag, g in (("fused", pl), ("block_only", lay)):
+            for _ in range(10):
+                g.replay(T, stream)
+            L.hip_event_record(evp[0], stream)
+            for _ in range(args.steps):
+                g.replay(T, stream)
+            L.hip_event_record(evp[1], stream)
+            torch.cuda.synchronize()
+            times[tag] = L.hip_event_elapsed_ms(evp[0], evp[1]) * 1e3 / args.steps
+        L.hip_events_destroy(evp)
+        pl.release_graph()
+        prenorm = {"us_per_step": round(times["fused"], 2), "tokens_per_s": round(T / times["fused"] * 1e6, 1),
+                   "block_only_us_per_step": round(times["block_only"], 2),
+                   "fused_step_extra_us": round(times["fused"] - times["block_only"], 2)}
+        log(f"[bench] pre-block step fused: {times['fused']:.1f} us/step vs block alone "
+            f"{times['block_only']:.1f} us/step")
+
     # ---------------- measured ceilings of this chip in the same run
     ceilings = None
     if not args.no_ceilings:
@@ -417,6 +450,7 @@ def main():
             "cold_write_scrub_us_per_step": round(cold["write"], 2) if cold else None,
         },
         "ceilings": ceilings,
+        "prenorm": prenorm,
     }
 
     if args.sweep and T <= 64:
