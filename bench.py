@@ -18,6 +18,7 @@ Profiler summaries (under profiles/) are made from rocprofv3 CSV output:
 
     python bench.py --summarize stats DIR          # --kernel-trace --stats run
     python bench.py --summarize traffic FETCH_DIR WRITE_DIR --workload W
+    python bench.py --summarize mfma DIR --workload W   # --pmc MfmaUtil MfmaFlopsBF16 GRBM_GUI_ACTIVE run
                                                    # two --pmc runs with --calib-copy
 """
 import argparse
@@ -197,6 +198,26 @@ def measure_ceilings(torch, L, stream):
             "vendor_bf16_gemm_TFLOPs": round(2.0 * n ** 3 / t_gemm / 1e12, 1)}
 
 
+def summarize_mfma(d, workload):
+    """Per-kernel MFMA evidence from one --pmc run (MfmaUtil: % of SIMD cycles
+    with the MFMA unit busy; MfmaFlopsBF16: bf16 MFMA flops per dispatch, the
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 count times 512)."""
+    from mixture_experts_decode_router_amd.build import source_digest
+    per = {}
+    for name in ("MfmaUtil", "MfmaFlopsBF16", "GRBM_GUI_ACTIVE"):
+        for _, k, v in _counter_rows(d, name):
+            per.setdefault(k, {}).setdefault(name, []).append(v)
+    kernels = {}
+    for k, m in sorted(per.items()):
+        if "moe::" not in k or "MfmaUtil" not in m:
+            continue
+        mean = {n: sum(v) / len(v) for n, v in m.items()}
+        kernels[_short(k)] = dict(dispatches=len(m["MfmaUtil"]), mfma_util_pct=round(mean["MfmaUtil"], 2),
+                                  mfma_flops_bf16_per_launch=int(mean.get("MfmaFlopsBF16", 0)),
+                                  gui_active_cycles=int(mean.get("GRBM_GUI_ACTIVE", 0)))
+    return dict(workload=workload, source_digest=source_digest(), kernels=kernels)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,8 +246,10 @@ def main():
             print(summarize_stats(dirs[0]))
         elif kind == "traffic" and len(dirs) == 2:
             print(json.dumps(summarize_traffic(dirs[0], dirs[1], args.workload), indent=1))
+        elif kind == "mfma" and len(dirs) == 1:
+            print(json.dumps(summarize_mfma(dirs[0], args.workload), indent=1))
         else:
-            ap.error("--summarize stats DIR | --summarize traffic FETCH_DIR WRITE_DIR")
+            ap.error("--summarize stats DIR | --summarize traffic FETCH_DIR WRITE_DIR | --summarize mfma DIR")
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -408,6 +431,17 @@ def main():
                     traffic = cand[0]["bytes_per_launch"] if len(cand) == 1 else None
         except Exception:
             traffic = None
+    mfma_counter = None
+    mpath = os.path.join(ROOT, "profiles", f"mfma_util_{args.workload}.json")
+    if mfma_path and os.path.exists(mpath):
+        try:
+            mj = json.load(open(mpath))
+            from mixture_experts_decode_router_amd.build import source_digest
+            if mj.get("source_digest") == source_digest():
+                kd = mj["kernels"].get("expert_mfma<true>")
+                mfma_counter = kd["mfma_util_pct"] if kd else None
+        except Exception:
+            mfma_counter = None
     step_s = ms_per_step * 1e-3
     result = {
         "metric": METRIC,
@@ -437,6 +471,7 @@ def main():
             "algorithmic_bytes_per_launch": model[dominant],
             "algorithmic_flops_per_launch": 2 * T * k * H * 2 * I,
             "avg_launch_us": round(dom_us, 2),
+            "mfma_busy_pct_counter": mfma_counter,
         },
         "block": {
             "algorithmic_bytes_per_step": model["block"],
