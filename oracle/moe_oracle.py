@@ -29,6 +29,9 @@ What it computes (Qwen3-MoE sparse block, decode or prefill, one layer):
   0. (optional)      the pre-block step: r = bf16(residual + delta),
                      x = bf16(r / sqrt(mean(r^2) + eps) * gamma), the
                      block's input [a1bc5cbd page, first paragraph].
+                     (optional LoRA: each of the two stacked matrices W gets
+                     + scale * B (A input), fp32 adapters, rank 16 on the
+                     4f2bfe7f69 page.)
   6. combine         out[t] = sum_j w[t,j] * y[t,j], j ascending (the
                      index_add_ step of the same path), returned as a plain
                      tensor [unsloth commit 4f2bfe7f69 page (first MoE decode
@@ -290,19 +293,52 @@ class ExpertWeights:
         self._pending[e] = (gu[: self.I], gu[self.I:], wd)
 
 
-def expert_mlp(x64: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
-    """SwiGLU expert on one token (vector) or a batch (rows): y = Wd (silu(Wg x) * Wu x)."""
+class LoRA:
+    """Low-rank adapters on every expert's stacked gate/up and down matrices
+    (the rank-16 LoRA of the 4f2bfe7f69 page's workload, fp32 adapters):
+    W_gu <- W_gu + scale * B_gu A_gu and W_d <- W_d + scale * B_d A_d, applied
+    as x W^T + scale * (x A^T) B^T.  Arrays (fp32, exact in fp64):
+    a_gate_up [E][r][H], b_gate_up [E][2I][r] (gate rows, then up rows),
+    a_down [E][r][I], b_down [E][H][r]."""
+
+    def __init__(self, a_gate_up, b_gate_up, a_down, b_down, scale):
+        self.a_gate_up, self.b_gate_up = a_gate_up, b_gate_up
+        self.a_down, self.b_down = a_down, b_down
+        self.scale = float(scale)
+
+    def get(self, e: int, I: int):
+        f = lambda a: np.asarray(a[e], dtype=np.float64)  # noqa: E731
+        bgu = f(self.b_gate_up)
+        return f(self.a_gate_up), bgu[:I], bgu[I:], f(self.a_down), f(self.b_down)
+
+
+def expert_mlp(x64: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, lora=None) -> np.ndarray:
+    """SwiGLU expert on one token (vector) or a batch (rows): y = Wd (silu(Wg x) * Wu x).
+    lora = (A_gu, B_g, B_u, A_d, B_d, scale): each projection gets
+    + scale * B (A input) before the nonlinearity / output."""
     g = x64 @ wg.T
     u = x64 @ wu.T
+    if lora is not None:
+        a_gu, b_g, b_u, a_d, b_d, s = lora
+        z = x64 @ a_gu.T
+        g = g + s * (z @ b_g.T)
+        u = u + s * (z @ b_u.T)
     h = silu(g) * u
-    return h @ wd.T
+    y = h @ wd.T
+    if lora is not None:
+        y = y + s * ((h @ a_d.T) @ b_d.T)
+    return y
+
+
+def _lora_of(lora, e, I):
+    return None if lora is None else (*lora.get(e, I), lora.scale)
 
 
 # --------------------------------------------------------------------------
 # full block
 # --------------------------------------------------------------------------
 def forward_per_token(inp, weights: Optional[ExpertWeights] = None, exact_router: bool = False,
-                      routing=None, renorm: bool = True):
+                      routing=None, renorm: bool = True, lora: Optional[LoRA] = None):
     """The definition: loop over tokens, then over the k chosen experts.
 
     Returns (out fp64 [T][H], routing dict)."""
@@ -316,13 +352,15 @@ def forward_per_token(inp, weights: Optional[ExpertWeights] = None, exact_router
     for t in range(inp.T):
         acc = np.zeros(inp.H, dtype=np.float64)
         for j in range(inp.k):
-            wg, wu, wd = W.get(int(ids[t, j]))
-            acc = acc + w[t, j] * expert_mlp(x64[t], wg, wu, wd)
+            e = int(ids[t, j])
+            wg, wu, wd = W.get(e)
+            acc = acc + w[t, j] * expert_mlp(x64[t], wg, wu, wd, _lora_of(lora, e, inp.I))
         out[t] = acc
     return out, dict(ids=ids, w=w, logits=l32)
 
 
-def forward_batched(inp, weights: Optional[ExpertWeights] = None, routing=None, renorm: bool = True):
+def forward_batched(inp, weights: Optional[ExpertWeights] = None, routing=None, renorm: bool = True,
+                    lora: Optional[LoRA] = None):
     """Same arithmetic grouped by expert: for each expert, one matmul over the
     tokens routed to it, then the per-token weighted sum in ascending j.
 
@@ -343,7 +381,7 @@ def forward_batched(inp, weights: Optional[ExpertWeights] = None, routing=None, 
             continue
         slots = perm[a:b].astype(np.int64)
         wg, wu, wd = W.get(e)
-        y_slot[slots] = expert_mlp(x64[slots // k], wg, wu, wd)
+        y_slot[slots] = expert_mlp(x64[slots // k], wg, wu, wd, _lora_of(lora, e, inp.I))
     out = np.zeros((T, inp.H), dtype=np.float64)
     for j in range(k):
         out += w[:, j:j + 1] * y_slot[np.arange(T) * k + j]

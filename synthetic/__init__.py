@@ -276,6 +276,21 @@ def prenorm_inputs(T: int, H: int, seed=None) -> dict:
     return dict(residual=res, delta=delta, gamma=gamma, eps=np.float32(PRENORM_EPS))
 
 
+LORA_RANK = 16
+_LORA_SEED = 4001
+
+
+def lora_adapters(E: int, H: int, I: int, rank: int = LORA_RANK, seed=None, alpha: float = 32.0) -> dict:
+    """fp32 adapters ~ N(0, 0.02) for every expert's stacked gate/up (A [E][r][H],
+    B [E][2I][r]) and down (A [E][r][I], B [E][H][r]), scale alpha / r.
+    Streams (seed, 0..3) in that order."""
+    seed = _LORA_SEED if seed is None else seed
+    g = lambda part, shape: (np.random.Generator(np.random.PCG64([seed, part]))  # noqa: E731
+                             .standard_normal(shape, dtype=np.float32) * np.float32(0.02))
+    return dict(a_gate_up=g(0, (E, rank, H)), b_gate_up=g(1, (E, 2 * I, rank)),
+                a_down=g(2, (E, rank, I)), b_down=g(3, (E, H, rank)), scale=np.float32(alpha / rank))
+
+
 def make_small(T: int, H: int, E: int, k: int, I: int, seed: int, wfmt: str = "bf16",
                bias: bool = False, x_std: float = 1.0, w_std: float = 0.02) -> MoEInputs:
     """Arbitrary small shape for edge-case tests (own seed, one draw order:

@@ -10,11 +10,13 @@ import oracle.moe_oracle as M
 from tests import test_formats_pins as F
 from tests import test_oracle_pins as P
 from tests import test_prenorm_pins as N
+from tests import test_lora_pins as LP
 
 
 def patch(monkeypatch, name, fn):
     monkeypatch.setattr(M, name, fn)
-    monkeypatch.setattr(O, name, fn)
+    if hasattr(O, name):          # private helpers are not re-exported
+        monkeypatch.setattr(O, name, fn)
 
 
 def ties_to_higher_index(logits32, k):
@@ -86,6 +88,31 @@ def norm_variant(kind):
     return f
 
 
+def lora_scale_ignored(lora, e, I):
+    t = ORIG_LORA_OF(lora, e, I)
+    return None if t is None else (*t[:5], 1.0)
+
+
+def lora_variant(kind):
+    def mlp(x64, wg, wu, wd, lora=None):
+        if lora is None:
+            return ORIG_MLP(x64, wg, wu, wd)
+        a_gu, b_g, b_u, a_d, b_d, s = lora
+        g, u = x64 @ wg.T, x64 @ wu.T
+        z = x64 @ a_gu.T
+        if kind == "after_silu":
+            h = M.silu(g) * u + s * (z @ b_g.T)
+        else:
+            h = M.silu(g + s * (z @ b_g.T)) * (u + s * (z @ b_u.T))
+        y = h @ wd.T
+        if kind != "down_dropped":
+            y = y + s * ((h @ a_d.T) @ b_d.T)
+        return y
+    return mlp
+
+
+ORIG_LORA_OF = M._lora_of
+ORIG_MLP = M.expert_mlp
 ORIG_RNE = M.f64_to_bf16_rne
 ORIG_STABLE = M.stable_permute
 ORIG_LOGITS = M.router_logits
@@ -131,6 +158,12 @@ MUTATIONS = {
                          [N.test_rmsnorm_constant_row_closed_form]),
     "norm_gamma_ignored": (lambda mp: patch(mp, "residual_rmsnorm", norm_variant("gamma_ignored")),
                            [N.test_rmsnorm_matches_torch_rms_norm, N.test_rmsnorm_constant_row_closed_form]),
+    "lora_scale_ignored": (lambda mp: patch(mp, "_lora_of", lora_scale_ignored),
+                           [LP.test_lora_hand_closed_form, LP.test_lora_equals_merged_weights]),
+    "lora_delta_after_silu": (lambda mp: patch(mp, "expert_mlp", lora_variant("after_silu")),
+                              [LP.test_lora_hand_closed_form, LP.test_lora_equals_merged_weights]),
+    "lora_down_dropped": (lambda mp: patch(mp, "expert_mlp", lora_variant("down_dropped")),
+                          [LP.test_lora_hand_closed_form, LP.test_lora_equals_merged_weights]),
     "sigmoid_not_silu": (lambda mp: patch(mp, "silu", sigmoid_not_silu),
                          [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
     "gate_up_swapped": (swap_gate_up,
