@@ -94,7 +94,32 @@ typedef struct {
  *   q_down     uint8 [E][H][I/2]     s_down    fp32 [E][H][I/64]
  *   codebook   fp32 [16]
  * The _TILED formats hold the same values in the layout moe_pack_weights
- * writes (same buffer sizes).  Unused fields may be NULL. */
+ * writes (same buffer sizes).  Unused fields may be NULL.
+ *   lora       host pointer to rank-16 adapters on every expert (see
+ *              moe_lora), read during the call (or the capture), or NULL. */
+
+/* Low-rank adapters on the expert GEMMs (the rank-16 LoRA with fp32
+ * adapters of the unsloth commit 4f2bfe7f69 page's workload), fused into the
+ * decode expert kernels: every expert's stacked gate/up matrix acts as
+ * W_gu + scale * B_gu A_gu and its down matrix as W_d + scale * B_d A_d:
+ *   [gate; up] = W_gu x + scale * B_gu (A_gu x)   (before SiLU * up)
+ *   y          = W_d h  + scale * B_d (A_d h)      (h: the bf16 h the down GEMM reads)
+ * A x is formed in fp32 per routed row (fixed order, batch-independent),
+ * the B products in fp32 in the GEMM epilogues.  Supported on the decode
+ * kernels only (T * top_k < 32 * n_experts, or any row-major or 4-bit
+ * format); a call that would take the MFMA prefill kernels with adapters
+ * returns MOE_ERR_UNSUPPORTED.  Device arrays, fp32, 16-byte aligned:
+ *   a_gate_up [E][r][H]   b_gate_up [E][2I][r] (gate rows, then up rows)
+ *   a_down    [E][r][I]   b_down    [E][H][r] */
+typedef struct {
+  const float* a_gate_up;
+  const float* b_gate_up;
+  const float* a_down;
+  const float* b_down;
+  float scale;    /* alpha / r, finite */
+  int32_t rank;   /* r; 16 is supported */
+} moe_lora;
+
 typedef struct {
   const void* w_router;
   const float* router_bias;
@@ -105,6 +130,7 @@ typedef struct {
   const uint8_t* q_down;
   const float* s_down;
   const float* codebook;
+  const moe_lora* lora;
 } moe_weights;
 
 /* Routing arrays inside a forward workspace (device pointers), valid after a

@@ -50,10 +50,16 @@ class moe_config(Structure):
                 ("out_dtype", c_int32), ("topk_weights", c_int32)]
 
 
+class moe_lora(Structure):
+    _fields_ = [("a_gate_up", c_void_p), ("b_gate_up", c_void_p), ("a_down", c_void_p), ("b_down", c_void_p),
+                ("scale", ctypes.c_float), ("rank", c_int32)]
+
+
 class moe_weights(Structure):
     _fields_ = [("w_router", c_void_p), ("router_bias", c_void_p), ("w_gate_up", c_void_p),
                 ("w_down", c_void_p), ("q_gate_up", c_void_p), ("s_gate_up", c_void_p),
-                ("q_down", c_void_p), ("s_down", c_void_p), ("codebook", c_void_p)]
+                ("q_down", c_void_p), ("s_down", c_void_p), ("codebook", c_void_p),
+                ("lora", c_void_p)]   # host pointer to a moe_lora, or None
 
 
 class moe_prenorm(Structure):

@@ -30,7 +30,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, total;
+  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, u_gu, u_d, total;
   int max_items;
 };
 
@@ -64,6 +64,8 @@ Layout layout(const moe_config& c) {
   L.chunks = take(moe::permute_scratch_ints((int)N, c.n_experts) * 4);
   L.h = take(N * c.inter * 2);
   L.y = take(N * c.hidden * 4);
+  L.u_gu = take(N * 16 * 4);  // LoRA: A_gu x per routed row
+  L.u_d = take(N * 16 * 4);   // LoRA: A_d h per routed row
   L.total = off;
   return L;
 }
@@ -104,6 +106,12 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
   } while (0)
 
 bool is_nf4(const moe_config& c) { return c.wfmt == MOE_W_NF4_B64 || c.wfmt == MOE_W_NF4_B64_TILED; }
+
+// Large groups (on average >= 32 rows per expert) go to the LDS-tiled MFMA
+// kernels (tiled bf16 weights only)
+bool mfma_path_for(const moe_config& c, int T) {
+  return c.wfmt == MOE_W_BF16_TILED && (long)T * c.top_k >= 32L * c.n_experts;
+}
 bool is_tiled(const moe_config& c) { return c.wfmt == MOE_W_BF16_TILED || c.wfmt == MOE_W_NF4_B64_TILED; }
 
 moe_status check_weights(const moe_config& c, const moe_weights* w) {
@@ -121,6 +129,22 @@ moe_status check_weights(const moe_config& c, const moe_weights* w) {
     MOE_TRY(check_ptr(w->s_down, "s_down"));
     MOE_TRY(check_ptr(w->codebook, "codebook"));
   }
+  if (w->lora) {
+    const moe_lora& l = *w->lora;
+    if (l.rank != 16) return fail(MOE_ERR_UNSUPPORTED, "LoRA rank " + std::to_string(l.rank) + " (16 is supported)");
+    MOE_TRY(check_ptr(l.a_gate_up, "lora a_gate_up"));
+    MOE_TRY(check_ptr(l.b_gate_up, "lora b_gate_up"));
+    MOE_TRY(check_ptr(l.a_down, "lora a_down"));
+    MOE_TRY(check_ptr(l.b_down, "lora b_down"));
+    if (!std::isfinite(l.scale)) return fail(MOE_ERR_INVALID_ARG, "LoRA scale is not finite");
+  }
+  return MOE_OK;
+}
+
+moe_status check_lora_path(const moe_config& c, const moe_weights* w, int32_t T) {
+  if (w && w->lora && mfma_path_for(c, T))
+    return fail(MOE_ERR_UNSUPPORTED, "LoRA adapters run on the decode kernels: T*top_k must be < 32*n_experts "
+                                     "with tiled bf16 weights (T=" + std::to_string(T) + ")");
   return MOE_OK;
 }
 
@@ -180,9 +204,8 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   if ((e = moe::launch_route(ra, at<float>(ws, L.route), s)) != hipSuccess) return hip_fail(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
-  // Large groups (on average >= 32 rows per expert) go to the LDS-tiled MFMA
-  // kernels; both paths give bit-identical per-row results.
-  const bool mfma_path = c.wfmt == MOE_W_BF16_TILED && N >= 32 * c.n_experts;
+  // both paths give bit-identical per-row results
+  const bool mfma_path = mfma_path_for(c, T);
   const int tile = mfma_path ? moe::kMfmaTile : moe::kSkinnyTile;
   moe::PermuteArgs pa{};
   pa.ids = ra.ids;
@@ -224,9 +247,39 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ea.s_down = w.s_down;
   ea.codebook = w.codebook;
   const bool nf4 = is_nf4(c), tiled = is_tiled(c);
+  moe::LoraAArgs la{};
+  if (w.lora) {  // validated: decode kernels only
+    ea.lora = true;
+    ea.lora_scale = w.lora->scale;
+    ea.lb_gate_up = w.lora->b_gate_up;
+    ea.lb_down = w.lora->b_down;
+    ea.u_gate_up = at<float>(ws, L.u_gu);
+    ea.u_down = at<float>(ws, L.u_d);
+    la.counts = pa.counts;
+    la.offsets = pa.offsets;
+    la.perm = pa.perm;
+    la.items = pa.items;
+    la.n_items = pa.n_items;
+    la.max_items = ea.max_items;
+    la.k = c.top_k;
+    la.K = c.hidden;
+    la.src = ea.x;
+    la.by_token = true;
+    la.A = w.lora->a_gate_up;
+    la.U = at<float>(ws, L.u_gu);
+    if ((e = moe::launch_lora_a(la, s)) != hipSuccess) return hip_fail(e, "LoRA A launch");
+  }
   e = mfma_path ? moe::launch_gate_up_mfma(ea, s) : moe::launch_gate_up(ea, nf4, tiled, s);
   if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (w.lora) {
+    la.K = c.inter;
+    la.src = ea.h;
+    la.by_token = false;
+    la.A = w.lora->a_down;
+    la.U = at<float>(ws, L.u_d);
+    if ((e = moe::launch_lora_a(la, s)) != hipSuccess) return hip_fail(e, "LoRA A launch");
+  }
   e = mfma_path ? moe::launch_down_mfma(ea, s) : moe::launch_down(ea, nf4, tiled, s);
   if (e != hipSuccess) return hip_fail(e, "down launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -253,6 +306,7 @@ moe_status check_forward_args(const moe_config* cfg, const moe_weights* w, const
   MOE_TRY(check_ptr(x, "x"));
   MOE_TRY(check_ptr(out, "out"));
   MOE_TRY(check_ws(*cfg, ws, ws_bytes));
+  MOE_TRY(check_lora_path(*cfg, w, T));
   return MOE_OK;
 }
 
@@ -510,6 +564,7 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
     if (buckets[i] < 1 || buckets[i] > cfg->t_max || (i && buckets[i] <= buckets[i - 1]))
       return fail(MOE_ERR_INVALID_ARG, "buckets must be strictly ascending within [1, t_max]");
   }
+  for (int i = 0; i < n_buckets; ++i) MOE_TRY(check_lora_path(*cfg, w, buckets[i]));
   moe::PrenormArgs pa{};
   if (pn) MOE_TRY(check_prenorm(*cfg, pn, buckets[n_buckets - 1], &pa));
   if (!stream) return fail(MOE_ERR_NOT_CAPTURABLE, "capture needs a created stream, not the NULL stream");

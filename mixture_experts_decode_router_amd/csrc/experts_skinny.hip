@@ -52,12 +52,30 @@ __device__ __forceinline__ bool load_item(const ExpertArgs& a, int item, Item& i
   return true;
 }
 
+// LoRA delta of one output row for one routed row: scale * sum_j B[j] U[j]
+// over the rank-16 adapter (fp32, j in order)
+__device__ __forceinline__ void load_u16(const float* up, f32x4_t (&u)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const f32x4_t*>(up + 4 * i);
+}
+
+__device__ __forceinline__ float lora_dot(const float* brow, const f32x4_t (&u)[4], float scale) {
+  float d = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(brow + 4 * i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d = fmaf(b[q], u[i][q], d);
+  }
+  return scale * d;
+}
+
 // ------------------------------------------------------------------ bf16
 // The bf16 kernels run one wave per workgroup (4 per item x column tile):
 // the finer grain keeps HBM busy through the last workgroups of the launch.
 constexpr int kSub = 4;  // waves (16-row sub-tiles) per column tile
 
-template <int U, bool TILED>
+template <int U, bool TILED, bool LORA>
 __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
   const int ntile = a.I / 64;
   const int wave = blockIdx.x % kSub, bq = blockIdx.x / kSub;
@@ -96,6 +114,17 @@ __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
   }
   // lane holds rows n0 + 4g + q (q = 0..3) of token column r
   if (rv) {
+    if constexpr (LORA) {
+      f32x4_t uu[4];
+      load_u16(a.u_gate_up + (size_t)(it.base + r) * 16, uu);
+      const float* bg = a.lb_gate_up + ((size_t)it.e * 2 * I + n0 + 4 * g) * 16;
+      const float* bu = bg + (size_t)I * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        accg[q] += lora_dot(bg + 16 * q, uu, a.lora_scale);
+        accu[q] += lora_dot(bu + 16 * q, uu, a.lora_scale);
+      }
+    }
     float hv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) hv[q] = silu(accg[q]) * accu[q];
@@ -104,7 +133,7 @@ __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
   }
 }
 
-template <int U, bool TILED>
+template <int U, bool TILED, bool LORA>
 __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
   const int ctile = a.H / 128;
   const int wave = blockIdx.x % kSub, bq = blockIdx.x / kSub;
@@ -139,6 +168,16 @@ __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
     }
   }
   if (rv) {
+    if constexpr (LORA) {
+      f32x4_t uu[4];
+      load_u16(a.u_down + (size_t)(it.base + r) * 16, uu);
+      const float* b0 = a.lb_down + ((size_t)it.e * H + c0 + 4 * g) * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc0[q] += lora_dot(b0 + 16 * q, uu, a.lora_scale);
+        acc1[q] += lora_dot(b0 + 16 * (16 + q), uu, a.lora_scale);
+      }
+    }
     const int slot = a.perm[it.base + r];
     float* yrow = a.y + (size_t)slot * H;
     *reinterpret_cast<f32x4_t*>(yrow + c0 + 4 * g) = acc0;
@@ -205,7 +244,7 @@ __device__ __forceinline__ f32x4_t block_mma(const uint32_t* s_lut, u32x4_t code
 // gate/up: a wave owns two 16-row tiles of gate rows and the matching up
 // rows (32 n), so one token fragment feeds four weight tiles; the table is
 // built once per 4-wave workgroup
-template <int NB, bool TILED>  // NB: 128-k blocks per loop iteration (H % (128 * NB) == 0)
+template <int NB, bool TILED, bool LORA>  // NB: 128-k blocks per loop iteration (H % (128 * NB) == 0)
 __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
   __shared__ uint32_t s_lut[256];
   const int ntile = a.I / 128;
@@ -261,6 +300,16 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
     const int m = 4 * g + q;
     if (m < it.M) {
       uint16_t* hrow = a.h + (size_t)(it.base + m) * I + n0 + r;
+      if constexpr (LORA) {
+        f32x4_t uu[4];
+        load_u16(a.u_gate_up + (size_t)(it.base + m) * 16, uu);
+        const float* bg = a.lb_gate_up + ((size_t)it.e * 2 * I + n0 + r) * 16;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[j][q] += lora_dot(bg + 16 * 16 * j, uu, a.lora_scale);
+          acc[j + 2][q] += lora_dot(bg + (size_t)I * 16 + 16 * 16 * j, uu, a.lora_scale);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float hv = silu(acc[j][q]) * acc[j + 2][q];
@@ -271,7 +320,7 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
 }
 
 // down: a wave owns two 16-row tiles of W_down (32 output columns)
-template <int NB, bool TILED>  // NB: 128-k blocks per loop iteration (I % (128 * NB) == 0)
+template <int NB, bool TILED, bool LORA>  // NB: 128-k blocks per loop iteration (I % (128 * NB) == 0)
 __global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
   __shared__ uint32_t s_lut[256];
   const int ctile = a.H / 128;
@@ -323,6 +372,13 @@ __global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
     const int m = 4 * g + q;
     if (m < it.M) {
       float* yrow = a.y + (size_t)a.perm[it.base + m] * H + c0 + r;
+      if constexpr (LORA) {
+        f32x4_t uu[4];
+        load_u16(a.u_down + (size_t)(it.base + m) * 16, uu);
+        const float* b0 = a.lb_down + ((size_t)it.e * H + c0 + r) * 16;
+        acc[0][q] += lora_dot(b0, uu, a.lora_scale);
+        acc[1][q] += lora_dot(b0 + 16 * 16, uu, a.lora_scale);
+      }
       yrow[0] = acc[0][q];
       yrow[16] = acc[1][q];
     }
@@ -340,44 +396,54 @@ hipError_t launch_u(int K, F8 f8, F4 f4, dim3 grid, hipStream_t s, const ExpertA
 
 }  // namespace
 
-hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
+template <bool LORA>
+hipError_t launch_gate_up_t(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
   if (nf4) {
     // one 128-k block per iteration (more only cost occupancy)
     const dim3 grid(a.max_items * (a.I / 128));  // 128 n per workgroup
     if (tiled)
-      hipLaunchKernelGGL((gate_up_nf4<1, true>), grid, dim3(kNf4Threads), 0, s, a);
+      hipLaunchKernelGGL((gate_up_nf4<1, true, LORA>), grid, dim3(kNf4Threads), 0, s, a);
     else
-      hipLaunchKernelGGL((gate_up_nf4<1, false>), grid, dim3(kNf4Threads), 0, s, a);
+      hipLaunchKernelGGL((gate_up_nf4<1, false, LORA>), grid, dim3(kNf4Threads), 0, s, a);
     return hipGetLastError();
   }
   const dim3 gw(a.max_items * (a.I / 64) * kSub);
-  return tiled ? launch_u(a.H, gate_up_bf16<8, true>, gate_up_bf16<4, true>, gw, s, a, 64)
-               : launch_u(a.H, gate_up_bf16<8, false>, gate_up_bf16<4, false>, gw, s, a, 64);
+  return tiled ? launch_u(a.H, gate_up_bf16<8, true, LORA>, gate_up_bf16<4, true, LORA>, gw, s, a, 64)
+               : launch_u(a.H, gate_up_bf16<8, false, LORA>, gate_up_bf16<4, false, LORA>, gw, s, a, 64);
 }
 
-template <bool TILED>
+template <bool TILED, bool LORA>
 void launch_down_nf4(const ExpertArgs& a, hipStream_t s) {
   const dim3 grid(a.max_items * (a.H / 128));  // 128 output columns per workgroup
   const int nkb = a.I / 128;
   if (nkb % 3 == 0)
-    hipLaunchKernelGGL((down_nf4<3, TILED>), grid, dim3(kNf4Threads), 0, s, a);
+    hipLaunchKernelGGL((down_nf4<3, TILED, LORA>), grid, dim3(kNf4Threads), 0, s, a);
   else if (nkb % 2 == 0)
-    hipLaunchKernelGGL((down_nf4<2, TILED>), grid, dim3(kNf4Threads), 0, s, a);
+    hipLaunchKernelGGL((down_nf4<2, TILED, LORA>), grid, dim3(kNf4Threads), 0, s, a);
   else
-    hipLaunchKernelGGL((down_nf4<1, TILED>), grid, dim3(kNf4Threads), 0, s, a);
+    hipLaunchKernelGGL((down_nf4<1, TILED, LORA>), grid, dim3(kNf4Threads), 0, s, a);
 }
 
-hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
+template <bool LORA>
+hipError_t launch_down_t(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
   if (nf4) {
     if (tiled)
-      launch_down_nf4<true>(a, s);
+      launch_down_nf4<true, LORA>(a, s);
     else
-      launch_down_nf4<false>(a, s);
+      launch_down_nf4<false, LORA>(a, s);
     return hipGetLastError();
   }
   const dim3 gw(a.max_items * (a.H / 128) * kSub);
-  return tiled ? launch_u(a.I, down_bf16<8, true>, down_bf16<4, true>, gw, s, a, 64)
-               : launch_u(a.I, down_bf16<8, false>, down_bf16<4, false>, gw, s, a, 64);
+  return tiled ? launch_u(a.I, down_bf16<8, true, LORA>, down_bf16<4, true, LORA>, gw, s, a, 64)
+               : launch_u(a.I, down_bf16<8, false, LORA>, down_bf16<4, false, LORA>, gw, s, a, 64);
+}
+
+hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
+  return a.lora ? launch_gate_up_t<true>(a, nf4, tiled, s) : launch_gate_up_t<false>(a, nf4, tiled, s);
+}
+
+hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
+  return a.lora ? launch_down_t<true>(a, nf4, tiled, s) : launch_down_t<false>(a, nf4, tiled, s);
 }
 
 }  // namespace moe

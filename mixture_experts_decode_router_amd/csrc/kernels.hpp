@@ -79,7 +79,29 @@ struct ExpertArgs {
   const uint8_t* q_down;      // [E][H][I/2]
   const float* s_down;        // [E][H][I/64]
   const float* codebook;      // [16]
+  // LoRA (skinny kernels): acc[n][p] += lora_scale * sum_j B[e][n][j] * U[p][j]
+  bool lora;
+  float lora_scale;
+  const float* lb_gate_up;    // fp32 [E][2I][16]
+  const float* lb_down;       // fp32 [E][H][16]
+  const float* u_gate_up;     // fp32 [N][16], sorted-slot order
+  const float* u_down;        // fp32 [N][16], sorted-slot order
 };
+
+// U[p][:] = A[e] src-row(p) for every row of the skinny work list (rank 16)
+struct LoraAArgs {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* items;
+  const int32_t* n_items;
+  int max_items, k, K;
+  const uint16_t* src;    // x [T][K] (by_token) or h [N][K] (sorted-slot order)
+  bool by_token;
+  const float* A;         // fp32 [E][16][K]
+  float* U;               // fp32 [N][16]
+};
+hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s);
 // tiled: weights in the fragment-tiled layout written by launch_pack
 hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
 hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);

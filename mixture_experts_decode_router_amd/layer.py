@@ -4,6 +4,7 @@ streams; every step of the block runs in the HIP library."""
 from __future__ import annotations
 
 import copy
+import ctypes
 from typing import Optional, Sequence
 
 import numpy as np
@@ -28,9 +29,11 @@ class MoELayer:
     """
 
     def __init__(self, inp, t_max: int, device: str = "cuda", tiled: bool = True,
-                 out_bf16: bool = False, renorm: bool = True):
+                 out_bf16: bool = False, renorm: bool = True, lora: Optional[dict] = None):
         """out_bf16: bf16 output (else fp32); renorm: top-k weights renormalised
-        over the k chosen (else the full softmax at the chosen)."""
+        over the k chosen (else the full softmax at the chosen); lora: fp32
+        adapters (a_gate_up, b_gate_up, a_down, b_down arrays and scale, as
+        synthetic.lora_adapters makes them) fused into the expert GEMMs."""
         self.device = torch.device(device)
         self.H, self.E, self.k, self.I = inp.H, inp.E, inp.k, inp.I
         rowmajor = L.MOE_W_BF16 if inp.wfmt == "bf16" else L.MOE_W_NF4_B64
@@ -69,6 +72,14 @@ class MoELayer:
             torch.cuda.synchronize(self.device)
             t.update(packed)
             self.w = dst
+        self.lora = None
+        if lora is not None:
+            for name in ("a_gate_up", "b_gate_up", "a_down", "b_down"):
+                t["lora_" + name] = _dev(np.ascontiguousarray(lora[name], dtype=np.float32), self.device)
+            self.lora = L.moe_lora(*[t["lora_" + n].data_ptr() for n in ("a_gate_up", "b_gate_up", "a_down",
+                                                                            "b_down")],
+                                   float(lora["scale"]), int(lora["a_gate_up"].shape[1]))
+            self.w.lora = ctypes.addressof(self.lora)
         self.ws_bytes = L.moe_workspace_size(self.cfg)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.graph = None
@@ -82,6 +93,22 @@ class MoELayer:
                                  L.MOE_OUT_BF16 if out_bf16 else L.MOE_OUT_F32,
                                  L.MOE_TOPK_RENORM if renorm else L.MOE_TOPK_SOFTMAX)
         other.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
+        other.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        other.graph = None
+        return other
+
+    def with_lora(self, lora: dict) -> "MoELayer":
+        """The same device weights with fp32 LoRA adapters attached (see
+        __init__), with a workspace of its own."""
+        other = copy.copy(self)
+        other.tensors = dict(self.tensors)
+        for name in ("a_gate_up", "b_gate_up", "a_down", "b_down"):
+            other.tensors["lora_" + name] = _dev(np.ascontiguousarray(lora[name], dtype=np.float32), self.device)
+        other.lora = L.moe_lora(*[other.tensors["lora_" + n].data_ptr() for n in ("a_gate_up", "b_gate_up",
+                                                                                  "a_down", "b_down")],
+                                float(lora["scale"]), int(lora["a_gate_up"].shape[1]))
+        other.w = L.moe_weights(*[getattr(self.w, f) for f, _ in L.moe_weights._fields_])
+        other.w.lora = ctypes.addressof(other.lora)
         other.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         other.graph = None
         return other

@@ -75,8 +75,9 @@ def test_workspace_size_layout():
     chunks = 1 * 128 * 4   # per-2048-slot chunk histograms
     # ids, weights, perm, pos; counts; offsets; work list; its length; the
     # live row count of graph replays; router partials; chunk histograms; h; y
+    # ... and the two LoRA row buffers (A x, A h: 16 fp32 per routed row)
     expect = (al(n * 4) * 4 + al(128 * 4) + al(129 * 4) + al(items * 8) + al(4) + al(4) + al(route) + al(chunks)
-              + al(n * 768 * 2) + al(n * 2048 * 4))
+              + al(n * 768 * 2) + al(n * 2048 * 4) + 2 * al(n * 16 * 4))
     assert L.moe_workspace_size(c) == expect
     assert L.moe_workspace_size(cfg(hidden=2000)) == 0
 
@@ -234,4 +235,27 @@ def test_prenorm_validation_on_host():
     assert st(x_out=FAKE + 8 * row) == L.MOE_ERR_INVALID_ARG        # onto gamma
     assert st(residual_out=FAKE + 16 * row) == L.MOE_ERR_INVALID_ARG  # onto x_out
     assert st(T=0) == L.MOE_ERR_INVALID_ARG
+
+
+def test_lora_validation_on_host():
+    lib = L.lib()
+
+    def st(c=None, T=8, **kw):
+        c = c or cfg()
+        d = dict(a_gate_up=FAKE, b_gate_up=FAKE * 2, a_down=FAKE * 3, b_down=FAKE * 5, scale=2.0, rank=16)
+        d.update(kw)
+        lo = L.moe_lora(d["a_gate_up"], d["b_gate_up"], d["a_down"], d["b_down"], d["scale"], d["rank"])
+        w = weights()
+        w.lora = ctypes.addressof(lo)
+        return lib.moe_forward(ctypes.byref(c), ctypes.byref(w), FAKE, T, FAKE, FAKE, L.moe_workspace_size(c), None)
+
+    assert st(rank=8) == L.MOE_ERR_UNSUPPORTED
+    assert "rank" in L.moe_last_error()
+    assert st(a_down=None) == L.MOE_ERR_INVALID_ARG
+    assert st(b_gate_up=FAKE + 4) == L.MOE_ERR_INVALID_ARG
+    assert st(scale=float("nan")) == L.MOE_ERR_INVALID_ARG
+    # T*k >= 32E with tiled bf16 weights takes the MFMA prefill kernels: no adapters there
+    big = cfg(t_max=4096, wfmt=L.MOE_W_BF16_TILED)
+    assert st(c=big, T=512) == L.MOE_ERR_UNSUPPORTED
+    assert "LoRA" in L.moe_last_error()
 

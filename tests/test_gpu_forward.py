@@ -81,6 +81,9 @@ def test_forward_decode_sweep(T):
     dict(T=37, H=384, E=32, k=4, I=256, wfmt="nf4"),       # H an odd number of 128-blocks
     dict(T=21, H=4096, E=16, k=3, I=2560, wfmt="nf4"),
     dict(T=300, H=256, E=16, k=2, I=128, wfmt="bf16"),     # many rows per expert (several items)
+    dict(T=24, H=512, E=256, k=8, I=128, wfmt="bf16"),     # largest expert count
+    dict(T=9, H=256, E=48, k=6, I=128, wfmt="bf16"),       # E not a multiple of 64
+    dict(T=13, H=512, E=256, k=16, I=256, wfmt="nf4"),     # largest E and k, 4-bit
 ])
 def test_forward_edge_shapes(case, tiled):
     inp = S.make_small(case["T"], case["H"], case["E"], case["k"], case["I"], seed=case["T"],
@@ -100,6 +103,7 @@ def test_forward_edge_shapes(case, tiled):
     dict(T=600, H=384, E=16, k=2, I=256),     # down: last 256-row weight tile half past H
     dict(T=1100, H=512, E=16, k=1, I=384),    # k = 1, three gate/up tiles
     dict(T=520, H=256, E=16, k=4, I=128),     # shortest K (down K = 128: two stages)
+    dict(T=640, H=256, E=256, k=16, I=128),   # largest E and k on the MFMA kernels
 ])
 def test_forward_prefill_mfma_shapes(case):
     """Shapes that take the LDS-tiled MFMA kernels (>= 32 routed rows per expert)."""
