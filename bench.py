@@ -229,6 +229,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / vendor GEMM ceiling measurement")
+    ap.add_argument("--no-lora", action="store_true", help="skip the step with rank-16 LoRA adapters")
     ap.add_argument("--no-prenorm", action="store_true",
                     help="skip the step with the fused pre-block residual add + RMSNorm")
     ap.add_argument("--row-major", action="store_true",
@@ -398,6 +399,31 @@ def main():
         log(f"[bench] pre-block step fused: {times['fused']:.1f} us/step vs block alone "
             f"{times['block_only']:.1f} us/step")
 
+    # ---------------- the step with rank-16 fp32 LoRA adapters fused into the
+    # expert GEMMs (graph replays, same weights, own workspace)
+    lora = None
+    if not args.no_lora and T * k < 32 * E:
+        ll = lay.with_lora(S.lora_adapters(E, H, I))
+        xl = ll.upload_x(inp.x)
+        ol = torch.empty(T, H, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        ll.capture([T], xl, ol, stream)
+        evl = L.hip_events(2, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        for _ in range(10):
+            ll.replay(T, stream)
+        L.hip_event_record(evl[0], stream)
+        for _ in range(args.steps):
+            ll.replay(T, stream)
+        L.hip_event_record(evl[1], stream)
+        torch.cuda.synchronize()
+        t_l = L.hip_event_elapsed_ms(evl[0], evl[1]) * 1e3 / args.steps
+        L.hip_events_destroy(evl)
+        ll.release_graph()
+        lora = {"rank": 16, "us_per_step": round(t_l, 2), "tokens_per_s": round(T / t_l * 1e6, 1),
+                "extra_us_vs_block": round(t_l - gpu_ms * 1e3 / args.steps, 2),
+                "adapter_bytes_per_step": int(n_act * 16 * 4 * (H + 2 * I + I + H))}
+        log(f"[bench] with rank-16 LoRA: {t_l:.1f} us/step")
+
     # ---------------- measured ceilings of this chip in the same run
     ceilings = None
     if not args.no_ceilings:
@@ -486,6 +512,7 @@ def main():
         },
         "ceilings": ceilings,
         "prenorm": prenorm,
+        "lora": lora,
     }
 
     if args.sweep and T <= 64:
