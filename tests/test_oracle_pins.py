@@ -348,3 +348,26 @@ def test_oracle_reproduces_golden_tiny():
     np.testing.assert_allclose(r["w"], g["weights"], rtol=1e-15, atol=0)
     np.testing.assert_allclose(out[0, :16], g["out_first_row_first_16"], rtol=1e-13, atol=1e-16)
     np.testing.assert_allclose(out.sum(axis=1), g["out_row_sums"], rtol=1e-12, atol=1e-15)
+
+
+def test_oracle_reproduces_golden_variants():
+    """Regression pin for the variants (written by tests/golden/make_golden.py
+    from the oracle alone): weights without renormalisation, LoRA adapters,
+    the pre-block step."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_variants.json")))
+    inp = S.make("tiny")
+    out_s, rs = O.forward_per_token(inp, exact_router=True, renorm=False)
+    np.testing.assert_allclose(rs["w"], g["softmax_weights"], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(out_s.sum(axis=1), g["softmax_out_row_sums"], rtol=1e-12, atol=1e-15)
+    lora = O.LoRA(**S.lora_adapters(inp.E, inp.H, inp.I))
+    out_l, _ = O.forward_per_token(inp, exact_router=True, lora=lora)
+    np.testing.assert_allclose(out_l[0, :16], g["lora_out_first_row_first_16"], rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(out_l.sum(axis=1), g["lora_out_row_sums"], rtol=1e-12, atol=1e-15)
+    p = S.prenorm_inputs(8, 256)
+    r_bits, x64 = O.residual_rmsnorm(p["residual"], p["delta"], p["gamma"], p["eps"])
+    assert r_bits[0, :16].tolist() == g["prenorm_r_bits_row0_first_16"]
+    assert O.f64_to_bf16_rne(x64)[0, :16].tolist() == g["prenorm_x_bits_row0_first_16"]
+    np.testing.assert_allclose(x64.sum(axis=1), g["prenorm_x_row_sums"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose((x64 * x64).sum(axis=1), g["prenorm_x_row_sumsq"], rtol=1e-13, atol=0)
