@@ -88,3 +88,39 @@ def test_bf16_output_graph_replay_equals_eager():
             assert bool((out_static[T:] == 7.0).all()), T
     finally:
         lay.release_graph()
+
+
+def test_all_options_together_match_oracle_and_replay():
+    """Pre-block step + LoRA adapters + weights without renormalisation + bf16
+    output in one call, against the oracle on the kernel's x; a graph replay
+    gives the same bits."""
+    import synthetic as S
+    inp = workload("q64", 64)
+    d = S.lora_adapters(inp.E, inp.H, inp.I)
+    lay = layer("q64", 64).with_lora(d).with_options(out_bf16=True, renorm=False)
+    p = S.prenorm_inputs(64, inp.H)
+    res, dlt, gam = (lay.upload_x(p[n]) for n in ("residual", "delta", "gamma"))
+    say("[gpu] pre-block + LoRA + softmax weights + bf16 out")
+    out, x_out, r_out = lay.forward_prenorm(res, dlt, gam, float(p["eps"]), 64)
+    torch.cuda.synchronize()
+    xb = x_out.cpu().numpy().view(np.uint16)
+    ref, rr = O.forward_batched(inp.with_x(xb), oracle_weights("q64"), renorm=False, lora=O.LoRA(**d))
+    v = lay.views(64)
+    assert np.array_equal(v["ids"].cpu().numpy(), rr["ids"])
+    np.testing.assert_allclose(v["w"].cpu().numpy(), rr["w"], rtol=1e-4, atol=1e-7)
+    err = rel_err(out.float().cpu().numpy(), ref)
+    say(f"[gpu]   max|err|/rms = {err:.3e}")
+    assert out.dtype == torch.bfloat16 and err <= TOL_BF16
+    stream = torch.cuda.Stream()
+    xs = torch.zeros(64, inp.H, dtype=torch.int16, device="cuda")
+    rs = torch.zeros(64, inp.H, dtype=torch.int16, device="cuda")
+    os_ = torch.zeros(64, inp.H, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    lay.capture_prenorm([64], res, dlt, gam, float(p["eps"]), rs, xs, os_, stream)
+    try:
+        lay.replay(64, stream)
+        stream.synchronize()
+        assert torch.equal(xs, x_out) and torch.equal(rs, r_out)
+        assert torch.equal(os_.view(torch.int16), out.view(torch.int16))
+    finally:
+        lay.release_graph()
