@@ -32,6 +32,8 @@ What it computes (Qwen3-MoE sparse block, decode or prefill, one layer):
                      (optional LoRA: each of the two stacked matrices W gets
                      + scale * B (A input), fp32 adapters, rank 16 on the
                      4f2bfe7f69 page.)
+  (backward)        for fixed routing, the chain rule back to x and to the
+                     routing weights (backward_per_token).
   6. combine         out[t] = sum_j w[t,j] * y[t,j], j ascending (the
                      index_add_ step of the same path), returned as a plain
                      tensor [unsloth commit 4f2bfe7f69 page (first MoE decode
@@ -386,6 +388,54 @@ def forward_batched(inp, weights: Optional[ExpertWeights] = None, routing=None, 
     for j in range(k):
         out += w[:, j:j + 1] * y_slot[np.arange(T) * k + j]
     return out, dict(ids=ids, w=w, logits=l32, counts=counts, offsets=offsets, perm=perm, pos=pos)
+
+
+# --------------------------------------------------------------------------
+# backward of the block (frozen weights): gradients of a loss L with respect
+# to the input x and to the routing weights, given dL/dout
+# --------------------------------------------------------------------------
+def silu_grad(z):
+    """d silu / dz = s(z) (1 + z (1 - s(z))), s the logistic function."""
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, routing=None):
+    """The chain rule through the block, token by token, for fixed routing
+    (the top-k choice is piecewise constant in x):
+      d_w[t,j] = <d_out[t], y[t,j]>
+      d_l[t,j] = w_j (d_w_j - sum_i w_i d_w_i)   (softmax over the k chosen logits)
+      d_y      = w[t,j] d_out[t];  d_h = d_y Wd;  d_g = d_h u silu'(g);  d_u = d_h silu(g)
+      d_x[t]   = sum_j (d_g Wg + d_u Wu) + sum_j d_l[t,j] Wr[id_j]
+    Returns dict(d_x fp64 [T][H], d_w fp64 [T][k], d_logits fp64 [T][k], routing)."""
+    if routing is None:
+        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias)
+        routing = dict(ids=ids, w=w, logits=l32)
+    ids, w = routing["ids"], routing["w"]
+    W = weights or ExpertWeights(inp)
+    x64 = bf16_bits_to_f64(inp.x)
+    wr = bf16_bits_to_f64(inp.w_router)
+    d_out = np.asarray(d_out, dtype=np.float64)
+    T, k = ids.shape
+    d_x = np.zeros((T, inp.H))
+    d_w = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            wg, wu, wd = W.get(int(ids[t, j]))
+            g = wg @ x64[t]
+            u = wu @ x64[t]
+            h = silu(g) * u
+            y = wd @ h
+            d_w[t, j] = d_out[t] @ y
+            d_h = w[t, j] * (d_out[t] @ wd)
+            d_g = d_h * u * silu_grad(g)
+            d_u = d_h * silu(g)
+            d_x[t] += d_g @ wg + d_u @ wu
+    d_l = w * (d_w - np.sum(w * d_w, axis=1, keepdims=True))
+    for t in range(T):
+        for j in range(k):
+            d_x[t] += d_l[t, j] * wr[int(ids[t, j])]
+    return dict(d_x=d_x, d_w=d_w, d_logits=d_l, routing=routing)
 
 
 def rms(a: np.ndarray) -> float:

@@ -1,0 +1,74 @@
+"""Pins of the oracle's backward (frozen weights, fixed routing): torch
+autograd in fp64 on an independent dense formulation, a finite-difference
+check, and the zero-gradient case."""
+import numpy as np
+import torch
+
+import oracle as O
+import synthetic as S
+
+
+def dense_torch_forward(inp, x, ids, round_logits=True):
+    """Every expert on every token, masked to the oracle's choice, weights
+    from torch's softmax over the chosen logits; differentiable in x."""
+    wr = torch.from_numpy(O.bf16_bits_to_f64(inp.w_router))
+    # the routing weights are taken on fp32 logits (fp32 dot, plus the fp32
+    # bias in fp32); the rounding enters as a constant offset, so the
+    # gradient flows through in fp64
+    l64 = x @ wr.T
+    l32 = l64.detach().float()
+    if inp.bias is not None:
+        l32 = l32 + torch.from_numpy(np.asarray(inp.bias, np.float32))
+    l = l64 + (l32.double() - l64.detach()) if round_logits else l64
+    mask = torch.zeros_like(l, dtype=torch.bool).scatter_(1, torch.from_numpy(ids.astype(np.int64)), True)
+    g = torch.softmax(l.masked_fill(~mask, float("-inf")), dim=1)
+    out = torch.zeros(x.shape[0], inp.H, dtype=torch.float64)
+    for e in range(inp.E):
+        gu = torch.from_numpy(O.bf16_bits_to_f64(inp.w_gate_up[e]))
+        wd = torch.from_numpy(O.bf16_bits_to_f64(inp.w_down[e]))
+        h = torch.nn.functional.silu(x @ gu[: inp.I].T) * (x @ gu[inp.I:].T)
+        out = out + g[:, e:e + 1] * (h @ wd.T)
+    return out, g
+
+
+def test_backward_matches_torch_autograd():
+    for inp in (S.make("tiny"), S.make_small(6, 128, 8, 3, 64, seed=41, bias=True)):
+        b = O.backward_per_token(inp, np.random.default_rng(3).standard_normal((inp.T, inp.H)))
+        d_out = np.random.default_rng(3).standard_normal((inp.T, inp.H))
+        x = torch.from_numpy(O.bf16_bits_to_f64(inp.x)).requires_grad_(True)
+        out, g = dense_torch_forward(inp, x, b["routing"]["ids"])
+        g.retain_grad()
+        (out * torch.from_numpy(d_out)).sum().backward()
+        ref = x.grad.numpy()
+        assert np.abs(b["d_x"] - ref).max() <= 1e-12 * np.sqrt(np.mean(ref * ref))
+        # the routing-weight gradient is d(out . d_out)/d g at the chosen experts
+        dg = np.take_along_axis(g.grad.numpy(), b["routing"]["ids"].astype(np.int64), 1)
+        np.testing.assert_allclose(b["d_w"], dg, rtol=1e-12, atol=1e-14)
+
+
+def test_backward_finite_differences():
+    """Central differences of L = sum(out * d_out) along a random direction
+    (small enough that no routing decision changes), on the smooth form of
+    the block (logits not rounded to fp32, which moves the result by ~1e-8
+    relative)."""
+    inp = S.make("tiny")
+    rng = np.random.default_rng(9)
+    d_out = rng.standard_normal((inp.T, inp.H))
+    b = O.backward_per_token(inp, d_out)
+    ids = b["routing"]["ids"]
+    v = rng.standard_normal((inp.T, inp.H))
+    x0 = torch.from_numpy(O.bf16_bits_to_f64(inp.x))
+    eps = 1e-6
+
+    def loss(x):
+        out, _ = dense_torch_forward(inp, x, ids, round_logits=False)
+        return float((out * torch.from_numpy(d_out)).sum())
+
+    fd = (loss(x0 + eps * torch.from_numpy(v)) - loss(x0 - eps * torch.from_numpy(v))) / (2 * eps)
+    assert abs(fd - float(np.sum(b["d_x"] * v))) <= 1e-5 * abs(fd)
+
+
+def test_backward_zero_upstream_gives_zero():
+    inp = S.make("tiny")
+    b = O.backward_per_token(inp, np.zeros((inp.T, inp.H)))
+    assert not b["d_x"].any() and not b["d_w"].any() and not b["d_logits"].any()

@@ -11,6 +11,7 @@ from tests import test_formats_pins as F
 from tests import test_oracle_pins as P
 from tests import test_prenorm_pins as N
 from tests import test_lora_pins as LP
+from tests import test_backward_pins as BP
 
 
 def patch(monkeypatch, name, fn):
@@ -111,6 +112,25 @@ def lora_variant(kind):
     return mlp
 
 
+def silu_grad_is_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def backward_uncentred_softmax(inp, d_out, weights=None, routing=None):
+    """The backward with d_l = w * d_w (the softmax Jacobian's centring term
+    dropped): only the router part of d_x changes."""
+    b = ORIG_BACKWARD(inp, d_out, weights, routing)
+    ids, w = b["routing"]["ids"], b["routing"]["w"]
+    wr = M.bf16_bits_to_f64(inp.w_router)
+    wrong = w * b["d_w"]
+    d_x = b["d_x"].copy()
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            d_x[t] += (wrong[t, j] - b["d_logits"][t, j]) * wr[int(ids[t, j])]
+    return dict(b, d_x=d_x, d_logits=wrong)
+
+
+ORIG_BACKWARD = M.backward_per_token
 ORIG_LORA_OF = M._lora_of
 ORIG_MLP = M.expert_mlp
 ORIG_RNE = M.f64_to_bf16_rne
@@ -164,6 +184,12 @@ MUTATIONS = {
                               [LP.test_lora_hand_closed_form, LP.test_lora_equals_merged_weights]),
     "lora_down_dropped": (lambda mp: patch(mp, "expert_mlp", lora_variant("down_dropped")),
                           [LP.test_lora_hand_closed_form, LP.test_lora_equals_merged_weights]),
+    "backward_silu_grad_is_sigmoid": (lambda mp: patch(mp, "silu_grad", silu_grad_is_sigmoid),
+                                      [BP.test_backward_matches_torch_autograd,
+                                       BP.test_backward_finite_differences]),
+    "backward_softmax_not_centred": (lambda mp: patch(mp, "backward_per_token", backward_uncentred_softmax),
+                                     [BP.test_backward_matches_torch_autograd,
+                                      BP.test_backward_finite_differences]),
     "sigmoid_not_silu": (lambda mp: patch(mp, "silu", sigmoid_not_silu),
                          [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
     "gate_up_swapped": (swap_gate_up,
