@@ -230,6 +230,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the copy / vendor GEMM ceiling measurement")
     ap.add_argument("--no-lora", action="store_true", help="skip the step with rank-16 LoRA adapters")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-prenorm", action="store_true",
                     help="skip the step with the fused pre-block residual add + RMSNorm")
     ap.add_argument("--row-major", action="store_true",
@@ -424,6 +425,31 @@ def main():
                 "adapter_bytes_per_step": int(n_act * 16 * 4 * (H + 2 * I + I + H))}
         log(f"[bench] with rank-16 LoRA: {t_l:.1f} us/step")
 
+    # ---------------- backward (frozen weights, the forward's routing): input
+    # and routing-weight gradients, eager, HIP events around the call
+    backward = None
+    if not args.no_backward and inp.wfmt == "bf16" and not args.row_major and T * k < 32 * E:
+        d_out = torch.randn(T, H, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(3))
+        evb = L.hip_events(2, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        tb = 0.0
+        nb = 20
+        with torch.cuda.stream(stream):
+            for i in range(nb + 3):
+                lay.forward(x_static, T, out_static, stream=stream)
+                L.hip_event_record(evb[0], stream)
+                lay.backward(x_static, d_out, T, stream=stream)
+                L.hip_event_record(evb[1], stream)
+                torch.cuda.synchronize()
+                if i >= 3:
+                    tb += L.hip_event_elapsed_ms(evb[0], evb[1]) * 1e3 / nb
+        L.hip_events_destroy(evb)
+        # bytes the backward must move: both expert matrices of every active
+        # expert again, the forward's y, d_out, d_x
+        bb = n_act * 3 * I * H * 2 + T * k * H * 4 + 2 * T * H * 4
+        backward = {"us_per_step": round(tb, 2), "algorithmic_bytes": int(bb),
+                    "hbm_frac": round(bb / (tb * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] backward (d_x, d_w): {tb:.1f} us, {backward['hbm_frac'] * 100:.1f}% of HBM peak")
+
     # ---------------- measured ceilings of this chip in the same run
     ceilings = None
     if not args.no_ceilings:
@@ -513,6 +539,7 @@ def main():
         "ceilings": ceilings,
         "prenorm": prenorm,
         "lora": lora,
+        "backward": backward,
     }
 
     if args.sweep and T <= 64:

@@ -246,6 +246,33 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
                                int32_t T, void* out, void* workspace, size_t ws_bytes,
                                hipStream_t stream);
 
+/* Backward of the block for frozen weights: given dL/dout, the gradients
+ * with respect to the block input x and to the routing weights, for the
+ * routing the forward took (the top-k choice is piecewise constant in x):
+ *   d_topk_w[t][j] = <d_out[t], y[t][j]>
+ *   d_l[t][j]      = w_j (d_topk_w[t][j] - sum_i w_i d_topk_w[t][i])
+ *   d_x[t]         = sum_j d_l[t][j] w_router[id_j]
+ *                  + sum_j (W_gate^T d_g + W_up^T d_u) of slot t*k+j,
+ *     d_h = W_down^T (w_j d_out[t]), d_g = d_h * u * silu'(g), d_u = d_h * silu(g),
+ *     g, u the slot's gate/up pre-activations (formed again, same bits as the
+ *     forward's).
+ * Must follow moe_forward(cfg, w, x, T, ...) on the same `workspace` and
+ * stream with no other use of the workspace in between: it reads that call's
+ * routing arrays and per-slot y (and overwrites y).  Supported: tiled bf16
+ * weights (MOE_W_BF16_TILED), renormalised top-k weights, no LoRA, and the
+ * decode kernels' sizes (T * top_k < 32 * n_experts); else
+ * MOE_ERR_UNSUPPORTED.  Sums run in a fixed order, no float atomics, so the
+ * result is the same on every run.
+ *   d_out     fp32 [T][H]
+ *   d_x       fp32 [T][H] (written)
+ *   d_topk_w  fp32 [T][k] (written), or NULL
+ *   bwd_workspace  >= moe_backward_workspace_size(cfg) bytes, 256-byte
+ *              aligned (gate/up pre-activations and their gradients). */
+size_t moe_backward_workspace_size(const moe_config* cfg);
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
+                        const float* d_out, float* d_x, float* d_topk_w, void* workspace, size_t ws_bytes,
+                        void* bwd_workspace, size_t bwd_bytes, hipStream_t stream);
+
 /* One-time conversion of row-major expert weights (cfg->wfmt = MOE_W_BF16 or
  * MOE_W_NF4_B64) into the tiled layout of MOE_W_BF16_TILED /
  * MOE_W_NF4_B64_TILED, in which every 16-row MFMA fragment of a k-step is

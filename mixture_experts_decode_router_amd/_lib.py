@@ -41,6 +41,7 @@ EXPORTS = (
     "moe_workspace_views",
     "moe_read_counts", "moe_graph_capture", "moe_graph_replay", "moe_graph_bucket_for",
     "moe_graph_destroy", "moe_forward_prenorm", "moe_graph_capture_prenorm",
+    "moe_backward_workspace_size", "moe_backward",
 )
 
 
@@ -114,6 +115,9 @@ def lib() -> ctypes.CDLL:
         "moe_graph_replay": (S, [c_void_p, c_int32, c_void_p]),
         "moe_graph_bucket_for": (c_int32, [c_void_p, c_int32]),
         "moe_graph_destroy": (None, [c_void_p]),
+        "moe_backward_workspace_size": (c_size_t, [POINTER(moe_config)]),
+        "moe_backward": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32, c_void_p, c_void_p,
+                             c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
         "moe_forward_prenorm": (S, [POINTER(moe_config), POINTER(moe_weights), POINTER(moe_prenorm), c_int32,
                                     c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_graph_capture_prenorm": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
@@ -200,6 +204,18 @@ def moe_forward_prenorm(cfg, w, pn, T, out, workspace, ws_bytes=None, stream=Non
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_forward_prenorm(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(pn), T, ptr(out),
                                      ptr(workspace), ws_bytes, stream_handle(stream)))
+
+
+def moe_backward_workspace_size(cfg) -> int:
+    return lib().moe_backward_workspace_size(ctypes.byref(cfg))
+
+
+def moe_backward(cfg, w, x, T, d_out, d_x, d_topk_w, workspace, bwd_workspace, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    bb = bwd_workspace.numel() * bwd_workspace.element_size()
+    _check(lib().moe_backward(ctypes.byref(cfg), ctypes.byref(w), ptr(x), T, ptr(d_out), ptr(d_x), ptr(d_topk_w),
+                              ptr(workspace), ws_bytes, ptr(bwd_workspace), bb, stream_handle(stream)))
 
 
 def moe_forward_timed(cfg, w, x, T, out, workspace, ws_bytes, stream, events):

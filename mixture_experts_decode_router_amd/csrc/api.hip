@@ -462,6 +462,71 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
   return enqueue_forward(*cfg, *w, pn->x_out, T, out, workspace, stream, nullptr, nullptr, &pa);
 }
 
+size_t moe_backward_workspace_size(const moe_config* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  return al256((size_t)cfg->t_max * cfg->top_k * 2 * cfg->inter * 4);
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, const float* d_out,
+                        float* d_x, float* d_topk_w, void* workspace, size_t ws_bytes, void* bwd_workspace,
+                        size_t bwd_bytes, hipStream_t stream) {
+  MOE_TRY(check_forward_args(cfg, w, x, T, d_x, workspace, ws_bytes));
+  const moe_config& c = *cfg;
+  if (c.wfmt != MOE_W_BF16_TILED || c.topk_weights != MOE_TOPK_RENORM || w->lora || mfma_path_for(c, T))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports tiled bf16 weights, renormalised top-k weights, no "
+                                     "LoRA, and T*top_k < 32*n_experts");
+  MOE_TRY(check_ptr(d_out, "d_out"));
+  if (d_topk_w && !aligned(d_topk_w, 4)) return fail(MOE_ERR_INVALID_ARG, "d_topk_w is not 4-byte aligned");
+  if (!bwd_workspace || !aligned(bwd_workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "bwd_workspace is NULL or not 256-byte aligned");
+  if (bwd_bytes < moe_backward_workspace_size(cfg)) return fail(MOE_ERR_WORKSPACE, "bwd_workspace is too small");
+  const Layout L = layout(c);
+  const int N = T * c.top_k;
+  moe::BwdArgs b{};
+  b.T = T;
+  b.H = c.hidden;
+  b.I = c.inter;
+  b.E = c.n_experts;
+  b.k = c.top_k;
+  b.max_items = max_items_for(N, c.n_experts, moe::kSkinnyTile, 1);
+  b.ids = at<int32_t>(workspace, L.ids);
+  b.counts = at<int32_t>(workspace, L.counts);
+  b.offsets = at<int32_t>(workspace, L.offsets);
+  b.perm = at<int32_t>(workspace, L.perm);
+  b.items = at<int32_t>(workspace, L.items);
+  b.n_items = at<int32_t>(workspace, L.n_items);
+  b.wts = at<float>(workspace, L.wts);
+  b.y = at<float>(workspace, L.y);
+  b.d_out = d_out;
+  b.d_x = d_x;
+  b.d_w = d_topk_w;
+  b.w_router = static_cast<const uint16_t*>(w->w_router);
+  b.w_gate_up = static_cast<const uint16_t*>(w->w_gate_up);
+  b.w_down = static_cast<const uint16_t*>(w->w_down);
+  b.gu = static_cast<float*>(bwd_workspace);
+  b.d_xs = at<float>(workspace, L.y);  // y is read first, then its memory holds the per-slot d_x
+  hipError_t e;
+  if ((e = moe::launch_bwd_weights(b, stream)) != hipSuccess) return hip_fail(e, "backward weights launch");
+  moe::ExpertArgs ea{};
+  ea.counts = b.counts;
+  ea.offsets = b.offsets;
+  ea.perm = b.perm;
+  ea.items = b.items;
+  ea.n_items = b.n_items;
+  ea.max_items = b.max_items;
+  ea.H = c.hidden;
+  ea.I = c.inter;
+  ea.E = c.n_experts;
+  ea.k = c.top_k;
+  ea.x = static_cast<const uint16_t*>(x);
+  ea.w_gate_up = b.w_gate_up;
+  ea.gu = b.gu;
+  if ((e = moe::launch_gate_up_preact(ea, stream)) != hipSuccess) return hip_fail(e, "gate/up launch");
+  if ((e = moe::launch_bwd_t(b, true, stream)) != hipSuccess) return hip_fail(e, "backward down launch");
+  if ((e = moe::launch_bwd_t(b, false, stream)) != hipSuccess) return hip_fail(e, "backward gate/up launch");
+  if ((e = moe::launch_bwd_combine(b, stream)) != hipSuccess) return hip_fail(e, "backward combine launch");
+  return MOE_OK;
+}
+
 moe_status moe_forward_timed(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, void* out,
                              void* workspace, size_t ws_bytes, hipStream_t stream, hipEvent_t* events) {
   MOE_TRY(check_forward_args(cfg, w, x, T, out, workspace, ws_bytes));

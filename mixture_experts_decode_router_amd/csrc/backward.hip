@@ -1,0 +1,230 @@
+// Backward of the block for frozen weights and the forward's routing (the
+// top-k choice is piecewise constant in x): given dL/dout, the gradients with
+// respect to the input x and to the routing weights,
+//   d_w[t][j] = <d_out[t], y[t*k+j]>
+//   d_l[t][j] = w_j (d_w_j - sum_i w_i d_w_i)           (renormalised softmax)
+//   d_h[p]    = W_d^T (w_p d_out[t_p]),  d_g = d_h u silu'(g),  d_u = d_h silu(g)
+//   d_x[t]    = sum_j d_l[t][j] Wr[id_j] + sum_j (W_g^T d_g + W_u^T d_u)[t*k+j]
+// The grouped GEMM path these follow is the grouped_mm MoE of the unsloth
+// commit 80aaf1121b page (third paragraph), whose training branch the GRPO
+// runs of the 4f2bfe7f69 page use.
+//
+// Kernels: bwd_weights (one wave per token: d_w, d_l and the router's share
+// of d_x), the forward's gate/up pass writing g and u instead of h,
+// bwd_t<DOWN> and bwd_t<GATE_UP> (grouped transposed GEMVs over the tiled
+// weight fragments, each 16 x 32 fragment pair turned through LDS into MFMA
+// operands), bwd_combine (per-token sum over the k slots, j in order).  No
+// float atomics: every output element is written once, sums run in a fixed
+// order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kU = 8;  // 32-row steps of loads in flight per wave
+
+// a one-wave workgroup's LDS writes are visible to all its lanes (no wait on
+// global loads still in flight)
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// ---------------------------------------------------------------- weights
+__global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  const int H = a.H, k = a.k, n4 = H / 4;
+  const float* dout = a.d_out + (size_t)t * H;
+  // (loops over j run to the static bound 16 so the arrays stay in registers)
+  float dw[16], dl[16];
+  float swd = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    dw[j] = 0.f;
+    if (j < k) {
+      const float* y = a.y + ((size_t)t * k + j) * H;
+      float s = 0.f;
+      for (int c4 = lane; c4 < n4; c4 += 64) {
+        const f32x4_t dv = *reinterpret_cast<const f32x4_t*>(dout + 4 * c4);
+        const f32x4_t yv = *reinterpret_cast<const f32x4_t*>(y + 4 * c4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s = fmaf(dv[q], yv[q], s);
+      }
+      dw[j] = wave_sum(s);
+      swd = fmaf(a.wts[(size_t)t * k + j], dw[j], swd);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) dl[j] = j < k ? a.wts[(size_t)t * k + j] * (dw[j] - swd) : 0.f;
+  if (a.d_w) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k && lane == j) a.d_w[(size_t)t * k + j] = dw[j];
+  }
+  // the router's share: sum_j d_l_j Wr[id_j], j in order
+  for (int c4 = lane; c4 < n4; c4 += 64) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= k) break;
+      const int e = a.ids[(size_t)t * k + j];
+      const u32x2_t wv = *reinterpret_cast<const u32x2_t*>(a.w_router + (size_t)e * H + 4 * c4);
+      acc[0] = fmaf(dl[j], bf16lo(wv[0]), acc[0]);
+      acc[1] = fmaf(dl[j], bf16hi(wv[0]), acc[1]);
+      acc[2] = fmaf(dl[j], bf16lo(wv[1]), acc[2]);
+      acc[3] = fmaf(dl[j], bf16hi(wv[1]), acc[3]);
+    }
+    *reinterpret_cast<f32x4_t*>(a.d_x + (size_t)t * H + 4 * c4) = acc;
+  }
+}
+
+// ---------------------------------------------------------------- transposed GEMVs
+// out[p][n] = sum_m W[e][m][n] v[p][m] for the routed rows p of a work item
+// (<= 16) and one 32-column tile n0 = 32 ks of W (tiled: fragment (rt, ks) is
+// W[16rt .. +16][32ks .. +32], lane (g, r) holding row r, columns 8g .. 8g+7).
+// The rows are the MFMA A operand (lane (r, g): row r, m = 8g .. 8g+7 of a
+// 32-m step); each fragment pair (rt = 2s, 2s+1) goes to LDS and every lane
+// gathers its B operand (columns r and 16 + r, m = 8g .. 8g+7) from it.
+//   DOWN:    W = W_d [H][I], v = w_p d_out[t_p], epilogue: SiLU backward,
+//            gu[p] (g, u) -> (d_g, d_u) in place.
+//   GATE_UP: W = W_gu [2I][H], v = (d_g, d_u)[p], epilogue: d_xs[slot(p)].
+enum { kDown = 0, kGateUp = 1 };
+
+template <int MODE>
+__global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
+  __shared__ uint16_t s_frag[2][512];
+  const int I = a.I, H = a.H;
+  const int ncols = MODE == kDown ? I : H;      // n
+  const int nrows = MODE == kDown ? H : 2 * I;  // m
+  const int ntile = ncols / 32;
+  const int item = blockIdx.x / ntile, ks = blockIdx.x - item * ntile;
+  if (item >= *a.n_items) return;
+  const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
+  const int c = a.counts[e] - m0;
+  const int M = c < 16 ? c : 16, base = a.offsets[e] + m0;
+  const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+  const bool rv = r < M;
+  const float* vrow;
+  float vs = 1.f;
+  if (MODE == kDown) {
+    const int slot = rv ? a.perm[base + r] : 0;
+    vrow = a.d_out + (size_t)(slot / a.k) * H;
+    vs = rv ? a.wts[slot] : 0.f;
+  } else {
+    vrow = a.gu + (size_t)(rv ? base + r : 0) * 2 * I;
+  }
+  const uint16_t* W = MODE == kDown ? a.w_down : a.w_gate_up;
+  const size_t rt0 = (size_t)e * (nrows / 16);
+  const int nsteps = nrows / 32;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // rows 8g + i < 16 of a 32-row step lie in fragment 0 (g < 2), the rest in
+  // fragment 1; within a fragment, row q and column n sit at lane
+  // 16 (n / 8) + q, element n % 8
+  const uint16_t* fr = s_frag[g >> 1];
+  const int q0 = 8 * (g & 1);
+  for (int s0 = 0; s0 < nsteps; s0 += kU) {
+    // kU steps of loads in flight: two weight fragments and the rows' v
+    u32x4_t f0[kU], f1[kU], va[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int s = s0 + u;
+      f0[u] = f1[u] = va[u] = zero;
+      if (s < nsteps) {
+        f0[u] = ld16_stream(W + (((rt0 + 2 * s) * ntile + ks) * 64 + lane) * 8);
+        f1[u] = ld16_stream(W + (((rt0 + 2 * s + 1) * ntile + ks) * 64 + lane) * 8);
+        if (rv) {
+          const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * s + 8 * g);
+          const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * s + 8 * g + 4);
+          va[u] = u32x4_t{pack_bf16x2(vs * v0[0], vs * v0[1]), pack_bf16x2(vs * v0[2], vs * v0[3]),
+                          pack_bf16x2(vs * v1[0], vs * v1[1]), pack_bf16x2(vs * v1[2], vs * v1[3])};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (s0 + u >= nsteps) break;
+      wave_sync_lds();  // the previous step's gathers are done
+      *reinterpret_cast<u32x4_t*>(&s_frag[0][lane * 8]) = f0[u];
+      *reinterpret_cast<u32x4_t*>(&s_frag[1][lane * 8]) = f1[u];
+      wave_sync_lds();
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh) {
+        const int n = 16 * nh + r;
+        const uint16_t* col = fr + (16 * (n >> 3)) * 8 + (n & 7);
+        uint32_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          b[i] = (uint32_t)col[(q0 + 2 * i) * 8] | ((uint32_t)col[(q0 + 2 * i + 1) * 8] << 16);
+        acc[nh] = mfma16(va[u], u32x4_t{b[0], b[1], b[2], b[3]}, acc[nh]);
+      }
+    }
+  }
+  // lane holds D[row 4g + q][column 32 ks + 16 nh + r]
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int m = 4 * g + q;
+    if (m >= M) continue;
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh) {
+      const int n = 32 * ks + 16 * nh + r;
+      if (MODE == kDown) {
+        float* gp = a.gu + (size_t)(base + m) * 2 * I;
+        const float gv = gp[n], uv = gp[I + n];
+        const float sg = 1.0f / (1.0f + __expf(-gv));
+        const float dh = acc[nh][q];
+        gp[n] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
+        gp[I + n] = dh * (gv * sg);
+      } else {
+        a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[nh][q];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+__global__ __launch_bounds__(256) void bwd_combine_kernel(BwdArgs a) {
+  const int t = blockIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= a.H) return;
+  float* dx = a.d_x + (size_t)t * a.H + c;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(dx);
+  for (int j = 0; j < a.k; ++j) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.d_xs + ((size_t)t * a.k + j) * a.H + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] += v[q];
+  }
+  *reinterpret_cast<f32x4_t*>(dx) = acc;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_weights_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
+  if (down)
+    hipLaunchKernelGGL(bwd_t_kernel<kDown>, dim3(a.max_items * (a.I / 32)), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_t_kernel<kGateUp>, dim3(a.max_items * (a.H / 32)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_combine(const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_combine_kernel, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -86,6 +86,7 @@ struct ExpertArgs {
   const float* lb_down;       // fp32 [E][H][16]
   const float* u_gate_up;     // fp32 [N][16], sorted-slot order
   const float* u_down;        // fp32 [N][16], sorted-slot order
+  float* gu;                  // launch_gate_up_preact: fp32 [N][2I] (g, then u), sorted-slot order
 };
 
 // U[p][:] = A[e] src-row(p) for every row of the skinny work list (rank 16)
@@ -105,6 +106,35 @@ hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s);
 // tiled: weights in the fragment-tiled layout written by launch_pack
 hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
 hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
+
+// The skinny gate/up pass (tiled bf16) writing the pre-activations g and u
+// (fp32) to a.gu instead of h: the same accumulations, so the same bits.
+hipError_t launch_gate_up_preact(const ExpertArgs& a, hipStream_t s);
+
+// Backward of the block (frozen tiled bf16 weights, the forward's routing
+// and per-slot y; skinny work list)
+struct BwdArgs {
+  int T, H, I, E, k, max_items;
+  const int32_t* ids;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* items;
+  const int32_t* n_items;
+  const float* wts;           // [T][k]
+  const float* y;             // forward y [N][H], flat-slot order
+  const float* d_out;         // [T][H]
+  float* d_x;                 // [T][H]
+  float* d_w;                 // [T][k] or null
+  const uint16_t* w_router;   // bf16 [E][H]
+  const uint16_t* w_gate_up;  // tiled bf16
+  const uint16_t* w_down;     // tiled bf16
+  float* gu;                  // [N][2I]: g, u from the forward pass, then d_g, d_u
+  float* d_xs;                // [N][H], flat-slot order (may reuse y's memory)
+};
+hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s);
+hipError_t launch_bwd_combine(const BwdArgs& a, hipStream_t s);
 
 // LDS-tiled MFMA grouped GEMMs (bf16 weights in the tiled layout only);
 // the work list must use kMfmaTile.

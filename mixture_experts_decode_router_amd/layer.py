@@ -166,6 +166,20 @@ class MoELayer:
         L.moe_forward_prenorm(self.cfg, self.w, pn, T, out, self.workspace, self.ws_bytes, stream)
         return out, x_out, residual_out
 
+    def backward(self, x: torch.Tensor, d_out: torch.Tensor, T: Optional[int] = None, stream=None):
+        """Gradients for the routing of the last forward on this layer's
+        workspace (which must have been moe_forward of the same x): returns
+        (d_x fp32 [T][H], d_topk_w fp32 [T][k])."""
+        T = T or x.shape[0]
+        if getattr(self, "bwd_workspace", None) is None:
+            self.bwd_workspace = torch.empty(L.moe_backward_workspace_size(self.cfg), dtype=torch.uint8,
+                                             device=self.device)
+        d_x = torch.empty(T, self.H, dtype=torch.float32, device=self.device)
+        d_w = torch.empty(T, self.k, dtype=torch.float32, device=self.device)
+        L.moe_backward(self.cfg, self.w, x, T, d_out, d_x, d_w, self.workspace, self.bwd_workspace,
+                       self.ws_bytes, stream)
+        return d_x, d_w
+
     def forward_timed(self, x: torch.Tensor, out: torch.Tensor, events, T: Optional[int] = None,
                       stream=None) -> None:
         L.moe_forward_timed(self.cfg, self.w, x, T or x.shape[0], out, self.workspace, self.ws_bytes,
