@@ -79,6 +79,7 @@ typedef struct {
   int32_t wfmt;         /* moe_wformat */
   int32_t out_dtype;    /* moe_outdtype */
   int32_t topk_weights; /* moe_topk_weights */
+  int32_t train;        /* 1: moe_forward also keeps the gate/up pre-activations for moe_backward */
 } moe_config;
 
 /* Layer weights (device, read-only).  Expert tensors are stacked on E.
@@ -254,24 +255,21 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
  *   d_x[t]         = sum_j d_l[t][j] w_router[id_j]
  *                  + sum_j (W_gate^T d_g + W_up^T d_u) of slot t*k+j,
  *     d_h = W_down^T (w_j d_out[t]), d_g = d_h * u * silu'(g), d_u = d_h * silu(g),
- *     g, u the slot's gate/up pre-activations (formed again, same bits as the
- *     forward's).
- * Must follow moe_forward(cfg, w, x, T, ...) on the same `workspace` and
- * stream with no other use of the workspace in between: it reads that call's
- * routing arrays and per-slot y (and overwrites y).  Supported: tiled bf16
- * weights (MOE_W_BF16_TILED), renormalised top-k weights, no LoRA, and the
- * decode kernels' sizes (T * top_k < 32 * n_experts); else
- * MOE_ERR_UNSUPPORTED.  Sums run in a fixed order, no float atomics, so the
+ *     g, u the slot's gate/up pre-activations, which the forward kept.
+ * Must follow moe_forward(cfg, w, x, T, ...) with cfg->train = 1 on the same
+ * `workspace` and stream with no other use of the workspace in between: it
+ * reads that call's routing arrays, per-slot y and pre-activations (and
+ * overwrites y and the pre-activations).  Supported: tiled bf16 weights
+ * (MOE_W_BF16_TILED), renormalised top-k weights, no LoRA, and the decode
+ * kernels' sizes (T * top_k < 32 * n_experts); else MOE_ERR_UNSUPPORTED
+ * (cfg->train = 0 too).  Sums run in a fixed order, no float atomics, so the
  * result is the same on every run.
  *   d_out     fp32 [T][H]
  *   d_x       fp32 [T][H] (written)
- *   d_topk_w  fp32 [T][k] (written), or NULL
- *   bwd_workspace  >= moe_backward_workspace_size(cfg) bytes, 256-byte
- *              aligned (gate/up pre-activations and their gradients). */
-size_t moe_backward_workspace_size(const moe_config* cfg);
+ *   d_topk_w  fp32 [T][k] (written), or NULL */
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
                         const float* d_out, float* d_x, float* d_topk_w, void* workspace, size_t ws_bytes,
-                        void* bwd_workspace, size_t bwd_bytes, hipStream_t stream);
+                        hipStream_t stream);
 
 /* One-time conversion of row-major expert weights (cfg->wfmt = MOE_W_BF16 or
  * MOE_W_NF4_B64) into the tiled layout of MOE_W_BF16_TILED /

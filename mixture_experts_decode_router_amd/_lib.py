@@ -41,14 +41,14 @@ EXPORTS = (
     "moe_workspace_views",
     "moe_read_counts", "moe_graph_capture", "moe_graph_replay", "moe_graph_bucket_for",
     "moe_graph_destroy", "moe_forward_prenorm", "moe_graph_capture_prenorm",
-    "moe_backward_workspace_size", "moe_backward",
+    "moe_backward",
 )
 
 
 class moe_config(Structure):
     _fields_ = [("hidden", c_int32), ("inter", c_int32), ("n_experts", c_int32),
                 ("top_k", c_int32), ("t_max", c_int32), ("wfmt", c_int32),
-                ("out_dtype", c_int32), ("topk_weights", c_int32)]
+                ("out_dtype", c_int32), ("topk_weights", c_int32), ("train", c_int32)]
 
 
 class moe_lora(Structure):
@@ -115,9 +115,8 @@ def lib() -> ctypes.CDLL:
         "moe_graph_replay": (S, [c_void_p, c_int32, c_void_p]),
         "moe_graph_bucket_for": (c_int32, [c_void_p, c_int32]),
         "moe_graph_destroy": (None, [c_void_p]),
-        "moe_backward_workspace_size": (c_size_t, [POINTER(moe_config)]),
         "moe_backward": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32, c_void_p, c_void_p,
-                             c_void_p, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
+                             c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_forward_prenorm": (S, [POINTER(moe_config), POINTER(moe_weights), POINTER(moe_prenorm), c_int32,
                                     c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_graph_capture_prenorm": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
@@ -206,16 +205,11 @@ def moe_forward_prenorm(cfg, w, pn, T, out, workspace, ws_bytes=None, stream=Non
                                      ptr(workspace), ws_bytes, stream_handle(stream)))
 
 
-def moe_backward_workspace_size(cfg) -> int:
-    return lib().moe_backward_workspace_size(ctypes.byref(cfg))
-
-
-def moe_backward(cfg, w, x, T, d_out, d_x, d_topk_w, workspace, bwd_workspace, ws_bytes=None, stream=None):
+def moe_backward(cfg, w, x, T, d_out, d_x, d_topk_w, workspace, ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
-    bb = bwd_workspace.numel() * bwd_workspace.element_size()
     _check(lib().moe_backward(ctypes.byref(cfg), ctypes.byref(w), ptr(x), T, ptr(d_out), ptr(d_x), ptr(d_topk_w),
-                              ptr(workspace), ws_bytes, ptr(bwd_workspace), bb, stream_handle(stream)))
+                              ptr(workspace), ws_bytes, stream_handle(stream)))
 
 
 def moe_forward_timed(cfg, w, x, T, out, workspace, ws_bytes, stream, events):

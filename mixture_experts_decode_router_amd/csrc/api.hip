@@ -30,7 +30,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, u_gu, u_d, total;
+  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, u_gu, u_d, gu, total;
   int max_items;
 };
 
@@ -66,6 +66,7 @@ Layout layout(const moe_config& c) {
   L.y = take(N * c.hidden * 4);
   L.u_gu = take(N * 16 * 4);  // LoRA: A_gu x per routed row
   L.u_d = take(N * 16 * 4);   // LoRA: A_d h per routed row
+  L.gu = take(c.train ? N * 2 * c.inter * 4 : 0);  // training forward: gate/up pre-activations
   L.total = off;
   return L;
 }
@@ -86,8 +87,9 @@ moe_status check_cfg(const moe_config* c) {
     return fail(MOE_ERR_UNSUPPORTED, buf);
   }
   if ((c->out_dtype != MOE_OUT_F32 && c->out_dtype != MOE_OUT_BF16) ||
-      (c->topk_weights != MOE_TOPK_RENORM && c->topk_weights != MOE_TOPK_SOFTMAX)) {
-    snprintf(buf, sizeof buf, "unsupported out_dtype=%d or topk_weights=%d", c->out_dtype, c->topk_weights);
+      (c->topk_weights != MOE_TOPK_RENORM && c->topk_weights != MOE_TOPK_SOFTMAX) || (c->train != 0 && c->train != 1)) {
+    snprintf(buf, sizeof buf, "unsupported out_dtype=%d, topk_weights=%d or train=%d", c->out_dtype, c->topk_weights,
+             c->train);
     return fail(MOE_ERR_UNSUPPORTED, buf);
   }
   return MOE_OK;
@@ -238,6 +240,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ea.k = c.top_k;
   ea.x = ra.x;
   ea.h = at<uint16_t>(ws, L.h);
+  ea.gu = c.train ? at<float>(ws, L.gu) : nullptr;
   ea.y = at<float>(ws, L.y);
   ea.w_gate_up = static_cast<const uint16_t*>(w.w_gate_up);
   ea.w_down = static_cast<const uint16_t*>(w.w_down);
@@ -462,23 +465,16 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
   return enqueue_forward(*cfg, *w, pn->x_out, T, out, workspace, stream, nullptr, nullptr, &pa);
 }
 
-size_t moe_backward_workspace_size(const moe_config* cfg) {
-  if (check_cfg(cfg) != MOE_OK) return 0;
-  return al256((size_t)cfg->t_max * cfg->top_k * 2 * cfg->inter * 4);
-}
-
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, const float* d_out,
-                        float* d_x, float* d_topk_w, void* workspace, size_t ws_bytes, void* bwd_workspace,
-                        size_t bwd_bytes, hipStream_t stream) {
+                        float* d_x, float* d_topk_w, void* workspace, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_forward_args(cfg, w, x, T, d_x, workspace, ws_bytes));
   const moe_config& c = *cfg;
-  if (c.wfmt != MOE_W_BF16_TILED || c.topk_weights != MOE_TOPK_RENORM || w->lora || mfma_path_for(c, T))
-    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports tiled bf16 weights, renormalised top-k weights, no "
-                                     "LoRA, and T*top_k < 32*n_experts");
+  if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED || c.topk_weights != MOE_TOPK_RENORM || w->lora ||
+      mfma_path_for(c, T))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports train=1 configs with tiled bf16 weights, renormalised "
+                                     "top-k weights, no LoRA, and T*top_k < 32*n_experts");
   MOE_TRY(check_ptr(d_out, "d_out"));
   if (d_topk_w && !aligned(d_topk_w, 4)) return fail(MOE_ERR_INVALID_ARG, "d_topk_w is not 4-byte aligned");
-  if (!bwd_workspace || !aligned(bwd_workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "bwd_workspace is NULL or not 256-byte aligned");
-  if (bwd_bytes < moe_backward_workspace_size(cfg)) return fail(MOE_ERR_WORKSPACE, "bwd_workspace is too small");
   const Layout L = layout(c);
   const int N = T * c.top_k;
   moe::BwdArgs b{};
@@ -502,25 +498,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.w_router = static_cast<const uint16_t*>(w->w_router);
   b.w_gate_up = static_cast<const uint16_t*>(w->w_gate_up);
   b.w_down = static_cast<const uint16_t*>(w->w_down);
-  b.gu = static_cast<float*>(bwd_workspace);
+  b.gu = at<float>(workspace, L.gu);
   b.d_xs = at<float>(workspace, L.y);  // y is read first, then its memory holds the per-slot d_x
   hipError_t e;
   if ((e = moe::launch_bwd_weights(b, stream)) != hipSuccess) return hip_fail(e, "backward weights launch");
-  moe::ExpertArgs ea{};
-  ea.counts = b.counts;
-  ea.offsets = b.offsets;
-  ea.perm = b.perm;
-  ea.items = b.items;
-  ea.n_items = b.n_items;
-  ea.max_items = b.max_items;
-  ea.H = c.hidden;
-  ea.I = c.inter;
-  ea.E = c.n_experts;
-  ea.k = c.top_k;
-  ea.x = static_cast<const uint16_t*>(x);
-  ea.w_gate_up = b.w_gate_up;
-  ea.gu = b.gu;
-  if ((e = moe::launch_gate_up_preact(ea, stream)) != hipSuccess) return hip_fail(e, "gate/up launch");
   if ((e = moe::launch_bwd_t(b, true, stream)) != hipSuccess) return hip_fail(e, "backward down launch");
   if ((e = moe::launch_bwd_t(b, false, stream)) != hipSuccess) return hip_fail(e, "backward gate/up launch");
   if ((e = moe::launch_bwd_combine(b, stream)) != hipSuccess) return hip_fail(e, "backward combine launch");

@@ -4,14 +4,14 @@
 //   d_w[t][j] = <d_out[t], y[t*k+j]>
 //   d_l[t][j] = w_j (d_w_j - sum_i w_i d_w_i)           (renormalised softmax)
 //   d_h[p]    = W_d^T (w_p d_out[t_p]),  d_g = d_h u silu'(g),  d_u = d_h silu(g)
+//               (g, u: the pre-activations a training forward kept)
 //   d_x[t]    = sum_j d_l[t][j] Wr[id_j] + sum_j (W_g^T d_g + W_u^T d_u)[t*k+j]
 // The grouped GEMM path these follow is the grouped_mm MoE of the unsloth
 // commit 80aaf1121b page (third paragraph), whose training branch the GRPO
 // runs of the 4f2bfe7f69 page use.
 //
-// Kernels: bwd_weights (one wave per token: d_w, d_l and the router's share
-// of d_x), the forward's gate/up pass writing g and u instead of h,
-// bwd_t<DOWN> and bwd_t<GATE_UP> (grouped transposed GEMVs over the tiled
+// Kernels: bwd_weights (one workgroup per token: d_w, d_l and the router's
+// share of d_x), bwd_t<DOWN> and bwd_t<GATE_UP> (grouped transposed GEMVs over the tiled
 // weight fragments, each 16 x 32 fragment pair turned through LDS into MFMA
 // operands), bwd_combine (per-token sum over the k slots, j in order).  No
 // float atomics: every output element is written once, sums run in a fixed
@@ -39,46 +39,68 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------- weights
+// One 256-thread workgroup per token; thread i holds the float4 column
+// chunks i, i + 256, ... (at most 4: H <= 4096).  For each chunk the y rows
+// of all k slots are loaded together, so a token costs one load round trip
+// per chunk, not one per slot.  Per slot: the thread's partial dot, a
+// butterfly over the wave, the four wave sums added in wave order.
 __global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.T) return;
+  __shared__ float s_part[16][4];
+  __shared__ float s_dw[16];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, k = a.k, n4 = H / 4;
   const float* dout = a.d_out + (size_t)t * H;
-  // (loops over j run to the static bound 16 so the arrays stay in registers)
-  float dw[16], dl[16];
-  float swd = 0.f;
+  const float* ybase = a.y + (size_t)t * k * H;
+  float part[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    dw[j] = 0.f;
-    if (j < k) {
-      const float* y = a.y + ((size_t)t * k + j) * H;
-      float s = 0.f;
-      for (int c4 = lane; c4 < n4; c4 += 64) {
-        const f32x4_t dv = *reinterpret_cast<const f32x4_t*>(dout + 4 * c4);
-        const f32x4_t yv = *reinterpret_cast<const f32x4_t*>(y + 4 * c4);
+  for (int j = 0; j < 16; ++j) part[j] = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s = fmaf(dv[q], yv[q], s);
-      }
-      dw[j] = wave_sum(s);
-      swd = fmaf(a.wts[(size_t)t * k + j], dw[j], swd);
+  for (int i = 0; i < 4; ++i) {
+    const int c4 = tid + 256 * i;
+    if (c4 < n4) {
+      const f32x4_t dv = *reinterpret_cast<const f32x4_t*>(dout + 4 * c4);
+      f32x4_t yv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < k) yv[j] = *reinterpret_cast<const f32x4_t*>(ybase + (size_t)j * H + 4 * c4);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j < k)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) part[j] = fmaf(dv[q], yv[j][q], part[j]);
     }
   }
 #pragma unroll
-  for (int j = 0; j < 16; ++j) dl[j] = j < k ? a.wts[(size_t)t * k + j] * (dw[j] - swd) : 0.f;
-  if (a.d_w) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < k && lane == j) a.d_w[(size_t)t * k + j] = dw[j];
+  for (int j = 0; j < 16; ++j) {
+    if (j < k) {
+      const float v = wave_sum(part[j]);
+      if (lane == 0) s_part[j][wave] = v;
+    }
   }
-  // the router's share: sum_j d_l_j Wr[id_j], j in order
-  for (int c4 = lane; c4 < n4; c4 += 64) {
+  __syncthreads();
+  if (tid < k) s_dw[tid] = ((s_part[tid][0] + s_part[tid][1]) + s_part[tid][2]) + s_part[tid][3];
+  __syncthreads();
+  float swd = 0.f;
+  for (int j = 0; j < k; ++j) swd = fmaf(a.wts[(size_t)t * k + j], s_dw[j], swd);
+  if (a.d_w && tid < k) a.d_w[(size_t)t * k + tid] = s_dw[tid];
+  // the router's share: sum_j d_l_j Wr[id_j], j in order, d_l_j = w_j (d_w_j - swd)
+  float dl[16];
+  int ids[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    dl[j] = j < k ? a.wts[(size_t)t * k + j] * (s_dw[j] - swd) : 0.f;
+    ids[j] = j < k ? a.ids[(size_t)t * k + j] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c4 = tid + 256 * i;
+    if (c4 >= n4) break;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (j >= k) break;
-      const int e = a.ids[(size_t)t * k + j];
-      const u32x2_t wv = *reinterpret_cast<const u32x2_t*>(a.w_router + (size_t)e * H + 4 * c4);
+      const u32x2_t wv = *reinterpret_cast<const u32x2_t*>(a.w_router + (size_t)ids[j] * H + 4 * c4);
       acc[0] = fmaf(dl[j], bf16lo(wv[0]), acc[0]);
       acc[1] = fmaf(dl[j], bf16hi(wv[0]), acc[1]);
       acc[2] = fmaf(dl[j], bf16lo(wv[1]), acc[2]);
@@ -210,7 +232,7 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdArgs a) {
 }  // namespace
 
 hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_weights_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_weights_kernel, dim3(a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

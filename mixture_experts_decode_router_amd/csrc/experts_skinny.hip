@@ -75,7 +75,7 @@ __device__ __forceinline__ float lora_dot(const float* brow, const f32x4_t (&u)[
 // the finer grain keeps HBM busy through the last workgroups of the launch.
 constexpr int kSub = 4;  // waves (16-row sub-tiles) per column tile
 
-template <int U, bool TILED, bool LORA, bool PREACT = false>
+template <int U, bool TILED, bool LORA, bool SAVE = false>  // SAVE: also keep g, u in a.gu
 __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
   const int ntile = a.I / 64;
   const int wave = blockIdx.x % kSub, bq = blockIdx.x / kSub;
@@ -113,13 +113,10 @@ __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
     }
   }
   // lane holds rows n0 + 4g + q (q = 0..3) of token column r
-  if (PREACT) {
-    if (rv) {
-      float* gp = a.gu + (size_t)(it.base + r) * 2 * I + n0 + 4 * g;
-      *reinterpret_cast<f32x4_t*>(gp) = accg;
-      *reinterpret_cast<f32x4_t*>(gp + I) = accu;
-    }
-    return;
+  if (SAVE && rv) {
+    float* gp = a.gu + (size_t)(it.base + r) * 2 * I + n0 + 4 * g;
+    *reinterpret_cast<f32x4_t*>(gp) = accg;
+    *reinterpret_cast<f32x4_t*>(gp + I) = accu;
   }
   if (rv) {
     if constexpr (LORA) {
@@ -416,6 +413,8 @@ hipError_t launch_gate_up_t(const ExpertArgs& a, bool nf4, bool tiled, hipStream
     return hipGetLastError();
   }
   const dim3 gw(a.max_items * (a.I / 64) * kSub);
+  if (a.gu && tiled && !LORA)  // training forward: keep the pre-activations
+    return launch_u(a.H, gate_up_bf16<8, true, false, true>, gate_up_bf16<4, true, false, true>, gw, s, a, 64);
   return tiled ? launch_u(a.H, gate_up_bf16<8, true, LORA>, gate_up_bf16<4, true, LORA>, gw, s, a, 64)
                : launch_u(a.H, gate_up_bf16<8, false, LORA>, gate_up_bf16<4, false, LORA>, gw, s, a, 64);
 }
@@ -444,11 +443,6 @@ hipError_t launch_down_t(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t 
   const dim3 gw(a.max_items * (a.H / 128) * kSub);
   return tiled ? launch_u(a.I, down_bf16<8, true, LORA>, down_bf16<4, true, LORA>, gw, s, a, 64)
                : launch_u(a.I, down_bf16<8, false, LORA>, down_bf16<4, false, LORA>, gw, s, a, 64);
-}
-
-hipError_t launch_gate_up_preact(const ExpertArgs& a, hipStream_t s) {
-  const dim3 gw(a.max_items * (a.I / 64) * kSub);
-  return launch_u(a.H, gate_up_bf16<8, true, false, true>, gate_up_bf16<4, true, false, true>, gw, s, a, 64);
 }
 
 hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {

@@ -86,7 +86,8 @@ struct ExpertArgs {
   const float* lb_down;       // fp32 [E][H][16]
   const float* u_gate_up;     // fp32 [N][16], sorted-slot order
   const float* u_down;        // fp32 [N][16], sorted-slot order
-  float* gu;                  // launch_gate_up_preact: fp32 [N][2I] (g, then u), sorted-slot order
+  float* gu;                  // or null; else the skinny bf16 gate/up also keeps g and u here:
+                              // fp32 [N][2I] (g, then u), sorted-slot order
 };
 
 // U[p][:] = A[e] src-row(p) for every row of the skinny work list (rank 16)
@@ -107,10 +108,6 @@ hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s);
 hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
 hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s);
 
-// The skinny gate/up pass (tiled bf16) writing the pre-activations g and u
-// (fp32) to a.gu instead of h: the same accumulations, so the same bits.
-hipError_t launch_gate_up_preact(const ExpertArgs& a, hipStream_t s);
-
 // Backward of the block (frozen tiled bf16 weights, the forward's routing
 // and per-slot y; skinny work list)
 struct BwdArgs {
@@ -129,7 +126,7 @@ struct BwdArgs {
   const uint16_t* w_router;   // bf16 [E][H]
   const uint16_t* w_gate_up;  // tiled bf16
   const uint16_t* w_down;     // tiled bf16
-  float* gu;                  // [N][2I]: g, u from the forward pass, then d_g, d_u
+  float* gu;                  // [N][2I]: g, u kept by the forward, then d_g, d_u
   float* d_xs;                // [N][H], flat-slot order (may reuse y's memory)
 };
 hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s);

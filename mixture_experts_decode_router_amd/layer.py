@@ -29,11 +29,12 @@ class MoELayer:
     """
 
     def __init__(self, inp, t_max: int, device: str = "cuda", tiled: bool = True,
-                 out_bf16: bool = False, renorm: bool = True, lora: Optional[dict] = None):
+                 out_bf16: bool = False, renorm: bool = True, lora: Optional[dict] = None, train: bool = False):
         """out_bf16: bf16 output (else fp32); renorm: top-k weights renormalised
         over the k chosen (else the full softmax at the chosen); lora: fp32
         adapters (a_gate_up, b_gate_up, a_down, b_down arrays and scale, as
-        synthetic.lora_adapters makes them) fused into the expert GEMMs."""
+        synthetic.lora_adapters makes them) fused into the expert GEMMs;
+        train: the forward keeps what backward() needs."""
         self.device = torch.device(device)
         self.H, self.E, self.k, self.I = inp.H, inp.E, inp.k, inp.I
         rowmajor = L.MOE_W_BF16 if inp.wfmt == "bf16" else L.MOE_W_NF4_B64
@@ -41,7 +42,7 @@ class MoELayer:
         self.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
         self.cfg = L.moe_config(inp.H, inp.I, inp.E, inp.k, t_max, self.wfmt,
                                 L.MOE_OUT_BF16 if out_bf16 else L.MOE_OUT_F32,
-                                L.MOE_TOPK_RENORM if renorm else L.MOE_TOPK_SOFTMAX)
+                                L.MOE_TOPK_RENORM if renorm else L.MOE_TOPK_SOFTMAX, int(train))
         st = L.moe_config_check(self.cfg)
         if st != L.MOE_OK:
             raise L.MoEError(st, L.moe_last_error())
@@ -84,16 +85,17 @@ class MoELayer:
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self.graph = None
 
-    def with_options(self, out_bf16: bool = False, renorm: bool = True) -> "MoELayer":
+    def with_options(self, out_bf16: bool = False, renorm: bool = True, train: bool = False) -> "MoELayer":
         """The same device weights under another output dtype / top-k weight
-        mode, with a workspace of its own."""
+        mode / training flag, with a workspace of its own."""
         other = copy.copy(self)
         c = self.cfg
         other.cfg = L.moe_config(c.hidden, c.inter, c.n_experts, c.top_k, c.t_max, c.wfmt,
                                  L.MOE_OUT_BF16 if out_bf16 else L.MOE_OUT_F32,
-                                 L.MOE_TOPK_RENORM if renorm else L.MOE_TOPK_SOFTMAX)
+                                 L.MOE_TOPK_RENORM if renorm else L.MOE_TOPK_SOFTMAX, int(train))
         other.out_dtype = torch.bfloat16 if out_bf16 else torch.float32
-        other.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        other.ws_bytes = L.moe_workspace_size(other.cfg)
+        other.workspace = torch.empty(other.ws_bytes, dtype=torch.uint8, device=self.device)
         other.graph = None
         return other
 
@@ -168,16 +170,12 @@ class MoELayer:
 
     def backward(self, x: torch.Tensor, d_out: torch.Tensor, T: Optional[int] = None, stream=None):
         """Gradients for the routing of the last forward on this layer's
-        workspace (which must have been moe_forward of the same x): returns
-        (d_x fp32 [T][H], d_topk_w fp32 [T][k])."""
+        workspace (a train layer; that forward must have been of the same x):
+        returns (d_x fp32 [T][H], d_topk_w fp32 [T][k])."""
         T = T or x.shape[0]
-        if getattr(self, "bwd_workspace", None) is None:
-            self.bwd_workspace = torch.empty(L.moe_backward_workspace_size(self.cfg), dtype=torch.uint8,
-                                             device=self.device)
         d_x = torch.empty(T, self.H, dtype=torch.float32, device=self.device)
         d_w = torch.empty(T, self.k, dtype=torch.float32, device=self.device)
-        L.moe_backward(self.cfg, self.w, x, T, d_out, d_x, d_w, self.workspace, self.bwd_workspace,
-                       self.ws_bytes, stream)
+        L.moe_backward(self.cfg, self.w, x, T, d_out, d_x, d_w, self.workspace, self.ws_bytes, stream)
         return d_x, d_w
 
     def forward_timed(self, x: torch.Tensor, out: torch.Tensor, events, T: Optional[int] = None,

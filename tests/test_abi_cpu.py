@@ -47,16 +47,17 @@ QWEN = dict(hidden=2048, inter=768, n_experts=128, top_k=8)
 
 
 def cfg(**kw):
-    d = dict(QWEN, t_max=64, wfmt=L.MOE_W_BF16, out_dtype=L.MOE_OUT_F32, topk_weights=L.MOE_TOPK_RENORM)
+    d = dict(QWEN, t_max=64, wfmt=L.MOE_W_BF16, out_dtype=L.MOE_OUT_F32, topk_weights=L.MOE_TOPK_RENORM,
+             train=0)
     d.update(kw)
     return L.moe_config(d["hidden"], d["inter"], d["n_experts"], d["top_k"], d["t_max"], d["wfmt"],
-                        d["out_dtype"], d["topk_weights"])
+                        d["out_dtype"], d["topk_weights"], d["train"])
 
 
 def test_config_struct_layout():
-    """moe_config is eight int32 fields; zeroed trailing fields are the defaults."""
-    assert ctypes.sizeof(L.moe_config) == 32
-    assert [f for f, _ in L.moe_config._fields_][-2:] == ["out_dtype", "topk_weights"]
+    """moe_config is nine int32 fields; zeroed trailing fields are the defaults."""
+    assert ctypes.sizeof(L.moe_config) == 36
+    assert [f for f, _ in L.moe_config._fields_][-3:] == ["out_dtype", "topk_weights", "train"]
     assert L.MOE_OUT_F32 == 0 and L.MOE_TOPK_RENORM == 0
     six = L.moe_config(2048, 768, 128, 8, 64, L.MOE_W_BF16)
     assert six.out_dtype == 0 and six.topk_weights == 0
@@ -86,7 +87,7 @@ def test_workspace_size_layout():
     dict(hidden=2000), dict(hidden=64), dict(hidden=8192), dict(inter=100), dict(n_experts=24),
     dict(n_experts=512), dict(top_k=0), dict(top_k=17), dict(n_experts=16, top_k=17),
     dict(t_max=0), dict(t_max=8193, top_k=8), dict(wfmt=7), dict(out_dtype=2), dict(out_dtype=-1),
-    dict(topk_weights=2), dict(topk_weights=-1),
+    dict(topk_weights=2), dict(topk_weights=-1), dict(train=2), dict(train=-1),
 ])
 def test_unsupported_configs(bad):
     assert L.moe_config_check(cfg(**bad)) == L.MOE_ERR_UNSUPPORTED
@@ -258,4 +259,22 @@ def test_lora_validation_on_host():
     big = cfg(t_max=4096, wfmt=L.MOE_W_BF16_TILED)
     assert st(c=big, T=512) == L.MOE_ERR_UNSUPPORTED
     assert "LoRA" in L.moe_last_error()
+
+
+def test_backward_validation_on_host():
+    lib = L.lib()
+    w = weights()
+
+    def st(c, T=8):
+        return lib.moe_backward(ctypes.byref(c), ctypes.byref(w), FAKE, T, FAKE * 2, FAKE * 3, None, FAKE * 4,
+                                L.moe_workspace_size(c), None)
+
+    tiled = dict(wfmt=L.MOE_W_BF16_TILED)
+    assert st(cfg(**tiled)) == L.MOE_ERR_UNSUPPORTED                     # not a training config
+    assert "train" in L.moe_last_error()
+    assert st(cfg(train=1)) == L.MOE_ERR_UNSUPPORTED                     # row-major weights
+    assert st(cfg(train=1, topk_weights=L.MOE_TOPK_SOFTMAX, **tiled)) == L.MOE_ERR_UNSUPPORTED
+    assert st(cfg(train=1, t_max=4096, **tiled), T=512) == L.MOE_ERR_UNSUPPORTED   # MFMA sizes
+    # a training config has room for the pre-activations
+    assert L.moe_workspace_size(cfg(train=1, **tiled)) == L.moe_workspace_size(cfg(**tiled)) + 64 * 8 * 2 * 768 * 4
 

@@ -1,7 +1,8 @@
 """Backward of the block (frozen weights, the forward's routing) against the
 fp64 oracle's chain rule: input and routing-weight gradients within the bf16
 tolerance; the same bits on every run and whatever the batch; the
-unsupported configurations refused."""
+unsupported configurations refused.  A training forward (train=1) keeps the
+gate/up pre-activations; its outputs are the same bits as a plain forward's."""
 import numpy as np
 import pytest
 import torch
@@ -36,7 +37,7 @@ def rel(a, ref):
 @pytest.mark.parametrize("name,T", [("tiny", 8), ("tiny", 33), ("q8", None), ("q64", 24)])
 def test_backward_matches_oracle(name, T):
     inp = workload(name, T)
-    lay = layer(*LAYER_OF[name])
+    lay = layer(*LAYER_OF[name]).with_options(train=True)
     d_out = d_out_for(inp.T, inp.H)
     say(f"[gpu] backward {name} T={inp.T}")
     d_x, d_w = gpu_backward(lay, inp.x, d_out)
@@ -50,7 +51,7 @@ def test_backward_matches_oracle(name, T):
 
 def test_backward_deterministic_and_batch_independent():
     inp = workload("q64", 64)
-    lay = layer("q64", 64)
+    lay = layer("q64", 64).with_options(train=True)
     d_out = d_out_for(64, inp.H, seed=5)
     a = gpu_backward(lay, inp.x, d_out)
     b = gpu_backward(lay, inp.x, d_out)
@@ -63,9 +64,22 @@ def test_backward_refuses_unsupported_configurations():
     inp = workload("q64", 64)
     x = torch.zeros(8, inp.H, dtype=torch.int16, device="cuda")
     g = torch.zeros(8, inp.H, dtype=torch.float32, device="cuda")
-    for lay in (layer("q64", 64, tiled=False), layer("q64", 64).with_options(renorm=False),
-                layer("q48q", 64), layer("q64", 64).with_lora(S.lora_adapters(inp.E, inp.H, inp.I))):
+    for lay in (layer("q64", 64), layer("q64", 64, tiled=False).with_options(train=True),
+                layer("q64", 64).with_options(renorm=False, train=True), layer("q48q", 64).with_options(train=True),
+                layer("q64", 64).with_options(train=True).with_lora(S.lora_adapters(inp.E, inp.H, inp.I))):
         lay.forward(x)
         with pytest.raises(L.MoEError) as ei:
             lay.backward(x, g)
         assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+
+
+def test_training_forward_gives_the_same_output():
+    inp = workload("q64", 64)
+    base = layer("q64", 64)
+    tr = base.with_options(train=True)
+    x = base.upload_x(inp.x)
+    a = base.forward(x)
+    b = tr.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
