@@ -115,16 +115,22 @@ __global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
 // (<= 16) and one 32-column tile n0 = 32 ks of W (tiled: fragment (rt, ks) is
 // W[16rt .. +16][32ks .. +32], lane (g, r) holding row r, columns 8g .. 8g+7).
 // The rows are the MFMA A operand (lane (r, g): row r, m = 8g .. 8g+7 of a
-// 32-m step); each fragment pair (rt = 2s, 2s+1) goes to LDS and every lane
-// gathers its B operand (columns r and 16 + r, m = 8g .. 8g+7) from it.
+// 32-m step).  Each fragment pair (rt = 2s, 2s+1) is staged in LDS column by
+// column (a column's 16 rows contiguous, columns 48 bytes apart plus 16 per
+// 8 columns, so neither the 2-byte writes nor the reads pile onto few banks);
+// a lane's B operand (column r or 16 + r, m = 8g .. 8g+7) is then one
+// 16-byte read.
 //   DOWN:    W = W_d [H][I], v = w_p d_out[t_p], epilogue: SiLU backward,
 //            gu[p] (g, u) -> (d_g, d_u) in place.
 //   GATE_UP: W = W_gu [2I][H], v = (d_g, d_u)[p], epilogue: d_xs[slot(p)].
 enum { kDown = 0, kGateUp = 1 };
 
+constexpr int kColStride = 48;  // bytes per staged column: 16 rows x 2 B + padding
+__device__ __forceinline__ int stage_off(int col) { return col * kColStride + (col >> 3) * 16; }
+
 template <int MODE>
 __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
-  __shared__ uint16_t s_frag[2][512];
+  __shared__ __attribute__((aligned(16))) uint8_t s_frag[2][32 * kColStride + 4 * 16];
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
   const int nrows = MODE == kDown ? H : 2 * I;  // m
@@ -151,10 +157,8 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   // rows 8g + i < 16 of a 32-row step lie in fragment 0 (g < 2), the rest in
-  // fragment 1; within a fragment, row q and column n sit at lane
-  // 16 (n / 8) + q, element n % 8
-  const uint16_t* fr = s_frag[g >> 1];
-  const int q0 = 8 * (g & 1);
+  // fragment 1: this lane reads rows 8 (g & 1) .. + 7 of columns r, 16 + r
+  const uint8_t* fr = s_frag[g >> 1] + 16 * (g & 1);
   for (int s0 = 0; s0 < nsteps; s0 += kU) {
     // kU steps of loads in flight: two weight fragments and the rows' v
     u32x4_t f0[kU], f1[kU], va[kU];
@@ -176,19 +180,20 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (s0 + u >= nsteps) break;
-      wave_sync_lds();  // the previous step's gathers are done
-      *reinterpret_cast<u32x4_t*>(&s_frag[0][lane * 8]) = f0[u];
-      *reinterpret_cast<u32x4_t*>(&s_frag[1][lane * 8]) = f1[u];
+      wave_sync_lds();  // the previous step's reads are done
+      // this lane's fragment chunk is row r of columns 8g .. 8g + 7
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const int off = stage_off(8 * g + e8) + 2 * r;
+        const uint32_t w0 = f0[u][e8 >> 1], w1 = f1[u][e8 >> 1];
+        *reinterpret_cast<uint16_t*>(&s_frag[0][off]) = (uint16_t)((e8 & 1) ? (w0 >> 16) : w0);
+        *reinterpret_cast<uint16_t*>(&s_frag[1][off]) = (uint16_t)((e8 & 1) ? (w1 >> 16) : w1);
+      }
       wave_sync_lds();
 #pragma unroll
       for (int nh = 0; nh < 2; ++nh) {
-        const int n = 16 * nh + r;
-        const uint16_t* col = fr + (16 * (n >> 3)) * 8 + (n & 7);
-        uint32_t b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          b[i] = (uint32_t)col[(q0 + 2 * i) * 8] | ((uint32_t)col[(q0 + 2 * i + 1) * 8] << 16);
-        acc[nh] = mfma16(va[u], u32x4_t{b[0], b[1], b[2], b[3]}, acc[nh]);
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(fr + stage_off(16 * nh + r));
+        acc[nh] = mfma16(va[u], b, acc[nh]);
       }
     }
   }
