@@ -400,14 +400,21 @@ def silu_grad(z):
     return s * (1.0 + z * (1.0 - s))
 
 
-def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, routing=None):
+def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, routing=None,
+                       lora: Optional["LoRA"] = None):
     """The chain rule through the block, token by token, for fixed routing
     (the top-k choice is piecewise constant in x):
       d_w[t,j] = <d_out[t], y[t,j]>
       d_l[t,j] = w_j (d_w_j - sum_i w_i d_w_i)   (softmax over the k chosen logits)
       d_y      = w[t,j] d_out[t];  d_h = d_y Wd;  d_g = d_h u silu'(g);  d_u = d_h silu(g)
       d_x[t]   = sum_j (d_g Wg + d_u Wu) + sum_j d_l[t,j] Wr[id_j]
-    Returns dict(d_x fp64 [T][H], d_w fp64 [T][k], d_logits fp64 [T][k], routing)."""
+    With LoRA adapters (W -> W + s B A on the stacked gate/up and the down
+    matrix), the same chain rule through W + s B A, plus the adapter
+    gradients summed over every routed (token, expert) pair:
+      d_B_d += s d_y (A_d h)^T,   d_A_d += s (B_d^T d_y) h^T
+      d_B_gu += s [d_g; d_u] (A_gu x)^T,   d_A_gu += s (B_gu^T [d_g; d_u]) x^T
+    Returns dict(d_x fp64 [T][H], d_w fp64 [T][k], d_logits fp64 [T][k],
+    routing, and with lora: d_a_gate_up, d_b_gate_up, d_a_down, d_b_down)."""
     if routing is None:
         ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias)
         routing = dict(ids=ids, w=w, logits=l32)
@@ -419,23 +426,45 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
     T, k = ids.shape
     d_x = np.zeros((T, inp.H))
     d_w = np.zeros((T, k))
+    grads = None
+    if lora is not None:
+        grads = {n: np.zeros(np.shape(getattr(lora, n)), dtype=np.float64)
+                 for n in ("a_gate_up", "b_gate_up", "a_down", "b_down")}
     for t in range(T):
         for j in range(k):
-            wg, wu, wd = W.get(int(ids[t, j]))
+            e = int(ids[t, j])
+            wg, wu, wd = W.get(e)
+            if lora is not None:
+                a_gu, b_g, b_u, a_d, b_d = lora.get(e, inp.I)
+                s = lora.scale
+                wg = wg + s * (b_g @ a_gu)
+                wu = wu + s * (b_u @ a_gu)
+                wd = wd + s * (b_d @ a_d)
             g = wg @ x64[t]
             u = wu @ x64[t]
             h = silu(g) * u
             y = wd @ h
             d_w[t, j] = d_out[t] @ y
-            d_h = w[t, j] * (d_out[t] @ wd)
+            d_y = w[t, j] * d_out[t]
+            d_h = d_y @ wd
             d_g = d_h * u * silu_grad(g)
             d_u = d_h * silu(g)
             d_x[t] += d_g @ wg + d_u @ wu
+            if lora is not None:
+                d_gu = np.concatenate([d_g, d_u])
+                b_gu = np.concatenate([b_g, b_u])
+                grads["b_down"][e] += s * np.outer(d_y, a_d @ h)
+                grads["a_down"][e] += s * np.outer(b_d.T @ d_y, h)
+                grads["b_gate_up"][e] += s * np.outer(d_gu, a_gu @ x64[t])
+                grads["a_gate_up"][e] += s * np.outer(b_gu.T @ d_gu, x64[t])
     d_l = w * (d_w - np.sum(w * d_w, axis=1, keepdims=True))
     for t in range(T):
         for j in range(k):
             d_x[t] += d_l[t, j] * wr[int(ids[t, j])]
-    return dict(d_x=d_x, d_w=d_w, d_logits=d_l, routing=routing)
+    out = dict(d_x=d_x, d_w=d_w, d_logits=d_l, routing=routing)
+    if grads is not None:
+        out.update({"d_" + n: v for n, v in grads.items()})
+    return out
 
 
 def rms(a: np.ndarray) -> float:

@@ -72,3 +72,36 @@ def test_backward_zero_upstream_gives_zero():
     inp = S.make("tiny")
     b = O.backward_per_token(inp, np.zeros((inp.T, inp.H)))
     assert not b["d_x"].any() and not b["d_w"].any() and not b["d_logits"].any()
+
+
+def test_backward_with_lora_matches_torch_autograd():
+    """Adapter gradients and d_x through W + s B A against torch autograd on
+    the dense formulation with the adapters as leaf tensors."""
+    inp = S.make_small(5, 128, 8, 2, 64, seed=43)
+    d = S.lora_adapters(inp.E, inp.H, inp.I, seed=2)
+    lora = O.LoRA(**d)
+    d_out = np.random.default_rng(8).standard_normal((inp.T, inp.H))
+    b = O.backward_per_token(inp, d_out, lora=lora)
+    ids = b["routing"]["ids"]
+    x = torch.from_numpy(O.bf16_bits_to_f64(inp.x)).requires_grad_(True)
+    P = {n: torch.from_numpy(np.asarray(d[n], np.float64)).requires_grad_(True)
+         for n in ("a_gate_up", "b_gate_up", "a_down", "b_down")}
+    s = float(d["scale"])
+    wr = torch.from_numpy(O.bf16_bits_to_f64(inp.w_router))
+    l64 = x @ wr.T
+    l = l64 + (l64.detach().float().double() - l64.detach())
+    mask = torch.zeros_like(l, dtype=torch.bool).scatter_(1, torch.from_numpy(ids.astype(np.int64)), True)
+    gw = torch.softmax(l.masked_fill(~mask, float("-inf")), dim=1)
+    out = torch.zeros(inp.T, inp.H, dtype=torch.float64)
+    for e in range(inp.E):
+        gu = torch.from_numpy(O.bf16_bits_to_f64(inp.w_gate_up[e])) + s * P["b_gate_up"][e] @ P["a_gate_up"][e]
+        wd = torch.from_numpy(O.bf16_bits_to_f64(inp.w_down[e])) + s * P["b_down"][e] @ P["a_down"][e]
+        h = torch.nn.functional.silu(x @ gu[: inp.I].T) * (x @ gu[inp.I:].T)
+        out = out + gw[:, e:e + 1] * (h @ wd.T)
+    (out * torch.from_numpy(d_out)).sum().backward()
+    rms = lambda a: float(np.sqrt(np.mean(a * a)))  # noqa: E731
+    assert np.abs(b["d_x"] - x.grad.numpy()).max() <= 1e-12 * rms(x.grad.numpy())
+    for n in P:
+        ref = P[n].grad.numpy()
+        assert np.abs(b["d_" + n] - ref).max() <= 1e-12 * rms(ref), n
+
