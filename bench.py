@@ -443,13 +443,33 @@ def main():
                 torch.cuda.synchronize()
                 if i >= 3:
                     tb += L.hip_event_elapsed_ms(evb[0], evb[1]) * 1e3 / nb
-        L.hip_events_destroy(evb)
         # bytes the backward must move: both expert matrices of every active
         # expert again, the forward's y, d_out, d_x
         bb = n_act * 3 * I * H * 2 + T * k * H * 4 + 2 * T * H * 4
         backward = {"us_per_step": round(tb, 2), "algorithmic_bytes": int(bb),
                     "hbm_frac": round(bb / (tb * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] backward (d_x, d_w): {tb:.1f} us, {backward['hbm_frac'] * 100:.1f}% of HBM peak")
+        # with rank-16 LoRA adapters: the same plus the adapter gradients
+        tll = tl.with_lora(S.lora_adapters(E, H, I))
+        tbl = 0.0
+        with torch.cuda.stream(stream):
+            for i in range(nb + 3):
+                tll.forward(x_static, T, out_static, stream=stream)
+                L.hip_event_record(evb[0], stream)
+                tll.backward(x_static, d_out, T, stream=stream)
+                L.hip_event_record(evb[1], stream)
+                torch.cuda.synchronize()
+                if i >= 3:
+                    tbl += L.hip_event_elapsed_ms(evb[0], evb[1]) * 1e3 / nb
+        # plus the active experts' adapters read and every expert's adapter
+        # gradient written (zeros where no row went)
+        per_e = 16 * 4 * (2 * H + 3 * I)
+        bbl = bb + n_act * per_e + E * per_e
+        backward["lora"] = {"us_per_step": round(tbl, 2), "algorithmic_bytes": int(bbl),
+                            "hbm_frac": round(bbl / (tbl * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] backward with LoRA gradients: {tbl:.1f} us, "
+            f"{backward['lora']['hbm_frac'] * 100:.1f}% of HBM peak")
+        L.hip_events_destroy(evb)
 
     # ---------------- measured ceilings of this chip in the same run
     ceilings = None

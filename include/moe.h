@@ -260,16 +260,33 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
  * `workspace` and stream with no other use of the workspace in between: it
  * reads that call's routing arrays, per-slot y and pre-activations (and
  * overwrites y and the pre-activations).  Supported: tiled bf16 weights
- * (MOE_W_BF16_TILED), renormalised top-k weights, no LoRA, and the decode
- * kernels' sizes (T * top_k < 32 * n_experts); else MOE_ERR_UNSUPPORTED
- * (cfg->train = 0 too).  Sums run in a fixed order, no float atomics, so the
- * result is the same on every run.
+ * (MOE_W_BF16_TILED), renormalised top-k weights, and the decode kernels'
+ * sizes (T * top_k < 32 * n_experts); else MOE_ERR_UNSUPPORTED (cfg->train
+ * = 0 too).  Sums run in a fixed order, no float atomics, so the result is
+ * the same on every run.
+ * With LoRA adapters (w->lora, the same ones the forward used) the chain
+ * rule runs through W + scale * B A, and the adapters' gradients, summed
+ * over every routed (token, expert) pair, are written to d_lora:
+ *   d_B_d  = scale * sum d_y (A_d h)^T,       d_A_d  = scale * sum (B_d^T d_y) h^T
+ *   d_B_gu = scale * sum [d_g; d_u] (A_gu x)^T,  d_A_gu = scale * sum (B_gu^T [d_g; d_u]) x^T
+ * (d_y = w_j d_out[t]; h = silu(g) * u in fp32 from the kept g, u, which
+ * also replaces the forward's A_d h rows in the workspace); an expert no
+ * row reached gets zeros.  Needs 2 * I <= 4096.
  *   d_out     fp32 [T][H]
  *   d_x       fp32 [T][H] (written)
- *   d_topk_w  fp32 [T][k] (written), or NULL */
+ *   d_topk_w  fp32 [T][k] (written), or NULL
+ *   d_lora    host pointer to the gradient arrays (device, written, shapes of
+ *             moe_lora's arrays), non-NULL exactly when w->lora is */
+typedef struct {
+  float* d_a_gate_up;  /* [E][r][H] */
+  float* d_b_gate_up;  /* [E][2I][r] */
+  float* d_a_down;     /* [E][r][I] */
+  float* d_b_down;     /* [E][H][r] */
+} moe_lora_grads;
+
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
-                        const float* d_out, float* d_x, float* d_topk_w, void* workspace, size_t ws_bytes,
-                        hipStream_t stream);
+                        const float* d_out, float* d_x, float* d_topk_w, const moe_lora_grads* d_lora,
+                        void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* One-time conversion of row-major expert weights (cfg->wfmt = MOE_W_BF16 or
  * MOE_W_NF4_B64) into the tiled layout of MOE_W_BF16_TILED /

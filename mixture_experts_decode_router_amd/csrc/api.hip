@@ -30,7 +30,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, u_gu, u_d, gu, total;
+  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, u_gu, u_d, gu, z_gu, z_d,
+      total;
   int max_items;
 };
 
@@ -67,6 +68,8 @@ Layout layout(const moe_config& c) {
   L.u_gu = take(N * 16 * 4);  // LoRA: A_gu x per routed row
   L.u_d = take(N * 16 * 4);   // LoRA: A_d h per routed row
   L.gu = take(c.train ? N * 2 * c.inter * 4 : 0);  // training forward: gate/up pre-activations
+  L.z_gu = take(c.train ? N * 16 * 4 : 0);         // LoRA backward: B_gu^T [d_g; d_u] per routed row
+  L.z_d = take(c.train ? N * 16 * 4 : 0);          // LoRA backward: B_d^T d_y per routed row
   L.total = off;
   return L;
 }
@@ -466,15 +469,24 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
 }
 
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, const float* d_out,
-                        float* d_x, float* d_topk_w, void* workspace, size_t ws_bytes, hipStream_t stream) {
+                        float* d_x, float* d_topk_w, const moe_lora_grads* d_lora, void* workspace, size_t ws_bytes,
+                        hipStream_t stream) {
   MOE_TRY(check_forward_args(cfg, w, x, T, d_x, workspace, ws_bytes));
   const moe_config& c = *cfg;
-  if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED || c.topk_weights != MOE_TOPK_RENORM || w->lora ||
-      mfma_path_for(c, T))
+  if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED || c.topk_weights != MOE_TOPK_RENORM || mfma_path_for(c, T))
     return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports train=1 configs with tiled bf16 weights, renormalised "
-                                     "top-k weights, no LoRA, and T*top_k < 32*n_experts");
+                                     "top-k weights, and T*top_k < 32*n_experts");
   MOE_TRY(check_ptr(d_out, "d_out"));
   if (d_topk_w && !aligned(d_topk_w, 4)) return fail(MOE_ERR_INVALID_ARG, "d_topk_w is not 4-byte aligned");
+  if (!w->lora != !d_lora)
+    return fail(MOE_ERR_INVALID_ARG, w->lora ? "adapters given but d_lora is NULL" : "d_lora given without adapters");
+  if (w->lora) {
+    if (2 * c.inter > 4096) return fail(MOE_ERR_UNSUPPORTED, "the LoRA backward needs 2*inter <= 4096");
+    MOE_TRY(check_ptr(d_lora->d_a_gate_up, "d_a_gate_up"));
+    MOE_TRY(check_ptr(d_lora->d_b_gate_up, "d_b_gate_up"));
+    MOE_TRY(check_ptr(d_lora->d_a_down, "d_a_down"));
+    MOE_TRY(check_ptr(d_lora->d_b_down, "d_b_down"));
+  }
   const Layout L = layout(c);
   const int N = T * c.top_k;
   moe::BwdArgs b{};
@@ -500,9 +512,39 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.w_down = static_cast<const uint16_t*>(w->w_down);
   b.gu = at<float>(workspace, L.gu);
   b.d_xs = at<float>(workspace, L.y);  // y is read first, then its memory holds the per-slot d_x
+  if (w->lora) {
+    const moe_lora& l = *w->lora;
+    b.lora = true;
+    b.lora_scale = l.scale;
+    b.x = static_cast<const uint16_t*>(x);
+    b.h = at<uint16_t>(workspace, L.h);
+    b.la_gate_up = l.a_gate_up;
+    b.lb_gate_up = l.b_gate_up;
+    b.la_down = l.a_down;
+    b.lb_down = l.b_down;
+    b.u_gate_up = at<float>(workspace, L.u_gu);
+    b.u_down = at<float>(workspace, L.u_d);
+    b.z_gate_up = at<float>(workspace, L.z_gu);
+    b.z_down = at<float>(workspace, L.z_d);
+    b.g_a_gate_up = d_lora->d_a_gate_up;
+    b.g_b_gate_up = d_lora->d_b_gate_up;
+    b.g_a_down = d_lora->d_a_down;
+    b.g_b_down = d_lora->d_b_down;
+  }
   hipError_t e;
+  // with adapters the down-adapter gradients read g, u, so they come before
+  // the down pass turns those into d_g, d_u; the gate/up ones after it
   if ((e = moe::launch_bwd_weights(b, stream)) != hipSuccess) return hip_fail(e, "backward weights launch");
+  if (b.lora) {
+    if ((e = moe::launch_lora_bt(b, true, stream)) != hipSuccess) return hip_fail(e, "LoRA down B^T launch");
+    if ((e = moe::launch_lora_grad(b, true, stream)) != hipSuccess) return hip_fail(e, "LoRA down gradient launch");
+  }
   if ((e = moe::launch_bwd_t(b, true, stream)) != hipSuccess) return hip_fail(e, "backward down launch");
+  if (b.lora) {
+    if ((e = moe::launch_lora_bt(b, false, stream)) != hipSuccess) return hip_fail(e, "LoRA gate/up B^T launch");
+    if ((e = moe::launch_lora_grad(b, false, stream)) != hipSuccess)
+      return hip_fail(e, "LoRA gate/up gradient launch");
+  }
   if ((e = moe::launch_bwd_t(b, false, stream)) != hipSuccess) return hip_fail(e, "backward gate/up launch");
   if ((e = moe::launch_bwd_combine(b, stream)) != hipSuccess) return hip_fail(e, "backward combine launch");
   return MOE_OK;

@@ -119,7 +119,13 @@ __global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
 // column (a column's 16 rows contiguous, columns 48 bytes apart plus 16 per
 // 8 columns, so neither the 2-byte writes nor the reads pile onto few banks);
 // a lane's B operand (column r or 16 + r, m = 8g .. 8g+7) is then one
-// 16-byte read.
+// 16-byte read.  v enters the MFMA rounded to bf16, except in the DOWN pass
+// with adapters (LORA), where it enters as two bf16 parts, hi = RNE(v) and
+// lo = RNE(v - hi), in two MFMAs into the same accumulator, so that d_h
+// carries about 16 bits of v (the weights are exact in bf16): the gate/up
+// adapter gradients are outer products of d_g, d_u with U and of B^T (d_g,
+// d_u) with x, which pass each element's rounding error through unsmoothed.
+// (d_x, a sum over many terms, meets the bf16 tolerance either way.)
 //   DOWN:    W = W_d [H][I], v = w_p d_out[t_p], epilogue: SiLU backward,
 //            gu[p] (g, u) -> (d_g, d_u) in place.
 //   GATE_UP: W = W_gu [2I][H], v = (d_g, d_u)[p], epilogue: d_xs[slot(p)].
@@ -128,8 +134,12 @@ enum { kDown = 0, kGateUp = 1 };
 constexpr int kColStride = 48;  // bytes per staged column: 16 rows x 2 B + padding
 __device__ __forceinline__ int stage_off(int col) { return col * kColStride + (col >> 3) * 16; }
 
-template <int MODE>
+// LoRA (LORA true): s * sum_j A[e][j][n] z[p][j] joins each output first
+// (z = B^T v from lora_bt; A = A_d for DOWN, A_gu for GATE_UP), the chain
+// rule through W + s B A.
+template <int MODE, bool LORA>
 __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
+  constexpr bool kHiLo = LORA && MODE == kDown;
   __shared__ __attribute__((aligned(16))) uint8_t s_frag[2][32 * kColStride + 4 * 16];
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
@@ -161,19 +171,25 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   const uint8_t* fr = s_frag[g >> 1] + 16 * (g & 1);
   for (int s0 = 0; s0 < nsteps; s0 += kU) {
     // kU steps of loads in flight: two weight fragments and the rows' v
-    u32x4_t f0[kU], f1[kU], va[kU];
+    u32x4_t f0[kU], f1[kU], va[kU], vl[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int s = s0 + u;
-      f0[u] = f1[u] = va[u] = zero;
+      f0[u] = f1[u] = va[u] = vl[u] = zero;
       if (s < nsteps) {
         f0[u] = ld16_stream(W + (((rt0 + 2 * s) * ntile + ks) * 64 + lane) * 8);
         f1[u] = ld16_stream(W + (((rt0 + 2 * s + 1) * ntile + ks) * 64 + lane) * 8);
         if (rv) {
           const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * s + 8 * g);
           const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * s + 8 * g + 4);
-          va[u] = u32x4_t{pack_bf16x2(vs * v0[0], vs * v0[1]), pack_bf16x2(vs * v0[2], vs * v0[3]),
-                          pack_bf16x2(vs * v1[0], vs * v1[1]), pack_bf16x2(vs * v1[2], vs * v1[3])};
+          const float t[8] = {vs * v0[0], vs * v0[1], vs * v0[2], vs * v0[3],
+                              vs * v1[0], vs * v1[1], vs * v1[2], vs * v1[3]};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t hi = pack_bf16x2(t[2 * i], t[2 * i + 1]);
+            va[u][i] = hi;
+            if constexpr (kHiLo) vl[u][i] = pack_bf16x2(t[2 * i] - bf16lo(hi), t[2 * i + 1] - bf16hi(hi));
+          }
         }
       }
     }
@@ -194,10 +210,36 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
       for (int nh = 0; nh < 2; ++nh) {
         const u32x4_t b = *reinterpret_cast<const u32x4_t*>(fr + stage_off(16 * nh + r));
         acc[nh] = mfma16(va[u], b, acc[nh]);
+        if constexpr (kHiLo) acc[nh] = mfma16(vl[u], b, acc[nh]);
       }
     }
   }
   // lane holds D[row 4g + q][column 32 ks + 16 nh + r]
+  if constexpr (LORA) {
+    const float* la = (MODE == kDown ? a.la_down + (size_t)e * 16 * I : a.la_gate_up + (size_t)e * 16 * H) +
+                      32 * ks + r;
+    const float* zb = MODE == kDown ? a.z_down : a.z_gate_up;
+    float av[2][16];
+#pragma unroll
+    for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) av[nh][j] = la[(size_t)j * ncols + 16 * nh];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = 4 * g + q;
+      if (m >= M) continue;
+      f32x4_t z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = *reinterpret_cast<const f32x4_t*>(zb + (size_t)(base + m) * 16 + 4 * i);
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) d = fmaf(av[nh][j], z[j >> 2][j & 3], d);
+        acc[nh][q] += a.lora_scale * d;
+      }
+    }
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int m = 4 * g + q;
@@ -242,10 +284,18 @@ hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
-  if (down)
-    hipLaunchKernelGGL(bwd_t_kernel<kDown>, dim3(a.max_items * (a.I / 32)), dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(bwd_t_kernel<kGateUp>, dim3(a.max_items * (a.H / 32)), dim3(64), 0, s, a);
+  const dim3 grid(a.max_items * ((down ? a.I : a.H) / 32));
+  if (down) {
+    if (a.lora)
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, true>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, false>), grid, dim3(64), 0, s, a);
+  } else {
+    if (a.lora)
+      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, true>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false>), grid, dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -113,11 +113,6 @@ __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
     }
   }
   // lane holds rows n0 + 4g + q (q = 0..3) of token column r
-  if (SAVE && rv) {
-    float* gp = a.gu + (size_t)(it.base + r) * 2 * I + n0 + 4 * g;
-    *reinterpret_cast<f32x4_t*>(gp) = accg;
-    *reinterpret_cast<f32x4_t*>(gp + I) = accu;
-  }
   if (rv) {
     if constexpr (LORA) {
       f32x4_t uu[4];
@@ -129,6 +124,11 @@ __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
         accg[q] += lora_dot(bg + 16 * q, uu, a.lora_scale);
         accu[q] += lora_dot(bu + 16 * q, uu, a.lora_scale);
       }
+    }
+    if constexpr (SAVE) {  // the pre-activations the nonlinearity sees
+      float* gp = a.gu + (size_t)(it.base + r) * 2 * I + n0 + 4 * g;
+      *reinterpret_cast<f32x4_t*>(gp) = accg;
+      *reinterpret_cast<f32x4_t*>(gp + I) = accu;
     }
     float hv[4];
 #pragma unroll
@@ -413,8 +413,8 @@ hipError_t launch_gate_up_t(const ExpertArgs& a, bool nf4, bool tiled, hipStream
     return hipGetLastError();
   }
   const dim3 gw(a.max_items * (a.I / 64) * kSub);
-  if (a.gu && tiled && !LORA)  // training forward: keep the pre-activations
-    return launch_u(a.H, gate_up_bf16<8, true, false, true>, gate_up_bf16<4, true, false, true>, gw, s, a, 64);
+  if (a.gu && tiled)  // training forward: keep the pre-activations
+    return launch_u(a.H, gate_up_bf16<8, true, LORA, true>, gate_up_bf16<4, true, LORA, true>, gw, s, a, 64);
   return tiled ? launch_u(a.H, gate_up_bf16<8, true, LORA>, gate_up_bf16<4, true, LORA>, gw, s, a, 64)
                : launch_u(a.H, gate_up_bf16<8, false, LORA>, gate_up_bf16<4, false, LORA>, gw, s, a, 64);
 }

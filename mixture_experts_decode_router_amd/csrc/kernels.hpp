@@ -128,10 +128,33 @@ struct BwdArgs {
   const uint16_t* w_down;     // tiled bf16
   float* gu;                  // [N][2I]: g, u kept by the forward, then d_g, d_u
   float* d_xs;                // [N][H], flat-slot order (may reuse y's memory)
+  // LoRA (lora true): the adapters, the forward's U = A x / A h, the backward's
+  // z = B^T v, and the adapter gradients (same shapes as the adapters)
+  bool lora;
+  float lora_scale;
+  const uint16_t* x;          // bf16 [T][H] (the forward's input)
+  const uint16_t* h;          // bf16 [N][I] sorted-slot order (the forward's h)
+  const float* la_gate_up;    // [E][16][H]
+  const float* lb_gate_up;    // [E][2I][16]
+  const float* la_down;       // [E][16][I]
+  const float* lb_down;       // [E][H][16]
+  const float* u_gate_up;     // [N][16]
+  float* u_down;              // [N][16] (the backward rewrites it from the fp32 h)
+  float* z_gate_up;           // [N][16]
+  float* z_down;              // [N][16]
+  float* g_a_gate_up;
+  float* g_b_gate_up;
+  float* g_a_down;
+  float* g_b_down;
 };
 hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s);
 hipError_t launch_bwd_combine(const BwdArgs& a, hipStream_t s);
+// LoRA backward: z = B^T v per routed row (down: v = w d_out, and U_d = A_d h
+// from the fp32 g, u; gate/up: v = (d_g, d_u))
+hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s);
+// LoRA adapter gradients: down ones before bwd_t(down), gate/up ones after it
+hipError_t launch_lora_grad(const BwdArgs& a, bool down, hipStream_t s);
 
 // LDS-tiled MFMA grouped GEMMs (bf16 weights in the tiled layout only);
 // the work list must use kMfmaTile.

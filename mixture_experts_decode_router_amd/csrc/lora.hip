@@ -83,7 +83,220 @@ __global__ __launch_bounds__(64 * kWaves) void lora_a_kernel(LoraAArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- backward
+// Sixteen adapter rows j times the (up to 16) routed rows of a work item,
+// reduced over K in 64-k blocks spread over the waves as in lora_a_kernel:
+//   out[tok][j] = sum_k P(j, k) Q(tok, k)
+// fetch(r, k0, p, q) gives lane row r's 16 consecutive k from k0 of both
+// operands (P row j = r as the MFMA A operand, Q row tok = r as B).  The
+// waves' tiles are added in wave order.  Ends with a barrier, so s_part can
+// be used again.
+template <typename Fetch>
+__device__ __forceinline__ void rank16_reduce(int nb, int M, float* out, f32x4_t (&s_part)[kWaves][64],
+                                              Fetch fetch) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int nw = nb < kWaves ? nb : kWaves;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (wave < nw) {
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks; ++i) {
+      const int b = wave + kWaves * i;
+      if (b < nb) {
+        float p[16], q[16];
+        fetch(r, 64 * b + 16 * g, p, q);
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc = mfma_f32(p[m], q[m], acc);
+      }
+    }
+  }
+  s_part[wave][lane] = acc;
+  __syncthreads();
+  if (tid < 256) {
+    const int l = tid & 63, qq = tid >> 6;
+    const int tok = l & 15, j = 4 * (l >> 4) + qq;
+    if (tok < M) {
+      float sum = 0.f;
+      for (int w = 0; w < nw; ++w) sum += s_part[w][l][qq];
+      out[(size_t)tok * kRank + j] = sum;
+    }
+  }
+  __syncthreads();
+}
+
+// Per routed row p of a work item (expert e):
+//   z[p][j] = sum_n B[e][n][j] v[p][n]    (v: DOWN w_p d_out[t_p], n < H;
+//                                          GATE_UP (d_g, d_u)[p], n < 2I)
+// and for DOWN also the fp32 adapter input of the down projection,
+//   U_d[p][j] = sum_i A_d[e][j][i] h[p][i],  h = silu(g) u in fp32 from the
+// g, u the training forward kept (the forward's U_d, formed from the bf16 h,
+// is overwritten), so the adapter gradients carry no bf16 rounding of h.
+__global__ __launch_bounds__(64 * kWaves) void lora_bt_kernel(BwdArgs a, int mode) {
+  __shared__ f32x4_t s_part[kWaves][64];
+  const int item = blockIdx.x;
+  if (item >= *a.n_items) return;  // uniform over the workgroup
+  const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
+  const int c = a.counts[e] - m0;
+  const int M = c < 16 ? c : 16, base = a.offsets[e] + m0;
+  const bool down = mode == 0;
+  const int H = a.H, I = a.I;
+  const int Nn = down ? H : 2 * I;
+  const float* B = (down ? a.lb_down : a.lb_gate_up) + (size_t)e * Nn * kRank;
+  float* Z = (down ? a.z_down : a.z_gate_up) + (size_t)base * kRank;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  rank16_reduce(Nn / 64, M, Z, s_part, [&](int r, int k0, float (&p)[16], float (&q)[16]) {
+    const bool tv = r < M;
+    const float* vrow;
+    float vs = 1.f;
+    if (down) {
+      const int slot = tv ? a.perm[base + r] : 0;
+      vrow = a.d_out + (size_t)(slot / a.k) * H;
+      vs = tv ? a.wts[slot] : 0.f;
+    } else {
+      vrow = a.gu + (size_t)(tv ? base + r : 0) * 2 * I;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const f32x4_t vv = tv ? *reinterpret_cast<const f32x4_t*>(vrow + k0 + 4 * v) : zero;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[4 * v + i] = vs * vv[i];
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) p[m] = B[(size_t)(k0 + m) * kRank + r];
+  });
+  if (!down) return;
+  const float* A = a.la_down + (size_t)e * kRank * I;
+  float* Ud = a.u_down + (size_t)base * kRank;
+  rank16_reduce(I / 64, M, Ud, s_part, [&](int r, int k0, float (&p)[16], float (&q)[16]) {
+    const bool tv = r < M;
+    const float* gp = a.gu + (size_t)(tv ? base + r : 0) * 2 * I + k0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const f32x4_t gv = tv ? *reinterpret_cast<const f32x4_t*>(gp + 4 * v) : zero;
+      const f32x4_t uv = tv ? *reinterpret_cast<const f32x4_t*>(gp + I + 4 * v) : zero;
+      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(A + (size_t)r * I + k0 + 4 * v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        q[4 * v + i] = silu(gv[i]) * uv[i];
+        p[4 * v + i] = av[i];
+      }
+    }
+  });
+}
+
+// Adapter gradients of every expert, summed over its routed rows in slot
+// order (no atomics; zero for an expert no row reached), times the scale.
+//   part 0 (down; before the down transposed GEMV turns g, u into d_g, d_u):
+//     d_b_down[e][c][j] = s sum_p (w_p d_out[t_p][c]) U_d[p][j]
+//     d_a_down[e][j][i] = s sum_p z_d[p][j] h[p][i],  h = silu(g) u (fp32)
+//   part 1 (gate/up; after it):
+//     d_b_gate_up[e][n][j] = s sum_p (d_g, d_u)[p][n] U_gu[p][j]
+//     d_a_gate_up[e][j][h] = s sum_p z_gu[p][j] x[t_p][h]
+// Each is a column c of the streamed operand (d_y, h, (d_g, d_u) or x) times
+// the row's rank-16 vector (U or z), so a thread owns one column and its 16
+// sums.  A 256-thread workgroup covers 256 columns of one expert's B or A
+// gradient; the routed rows' vectors (and tokens, weights) are staged in LDS
+// 64 rows at a time, and each thread's column loads are issued 8 rows at a
+// time.  B-gradient rows are 16 contiguous floats per thread; A-gradient
+// rows are written column-coalesced.
+constexpr int kGradRows = 64;
+
+__global__ __launch_bounds__(256) void lora_grad_kernel(BwdArgs a, int part) {
+  __shared__ f32x4_t s_vec[kGradRows][4];
+  __shared__ int s_tok[kGradRows];
+  __shared__ float s_w[kGradRows];
+  const int H = a.H, I = a.I;
+  const int nB = part == 0 ? H : 2 * I;  // columns (rows of the [n][16] array) of the B gradient
+  const int nA = part == 0 ? I : H;      // columns of the [16][n] A gradient
+  const int wgB = (nB + 255) / 256;
+  const int e = blockIdx.y;
+  const bool isB = (int)blockIdx.x < wgB;
+  const int col = (isB ? blockIdx.x : blockIdx.x - wgB) * 256 + threadIdx.x;
+  const bool cv = col < (isB ? nB : nA);
+  const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
+  const float* vec = part == 0 ? (isB ? a.u_down : a.z_down) : (isB ? a.u_gate_up : a.z_gate_up);
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int c0 = p0; c0 < p1; c0 += kGradRows) {
+    const int nr = p1 - c0 < kGradRows ? p1 - c0 : kGradRows;
+    __syncthreads();  // the previous chunk's LDS reads are done
+    {
+      const int r = threadIdx.x >> 2, qq = threadIdx.x & 3;
+      if (r < nr) s_vec[r][qq] = *reinterpret_cast<const f32x4_t*>(vec + (size_t)(c0 + r) * kRank + 4 * qq);
+      if (threadIdx.x < nr) {
+        const int slot = a.perm[c0 + threadIdx.x];
+        s_tok[threadIdx.x] = slot / a.k;
+        s_w[threadIdx.x] = a.wts[slot];
+      }
+    }
+    __syncthreads();
+    for (int r0 = 0; r0 < nr; r0 += 8) {
+      float sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = r0 + u;
+        float v = 0.f;
+        if (cv && r < nr) {
+          const size_t p = (size_t)(c0 + r);
+          if (part == 0) {
+            if (isB) {
+              v = s_w[r] * a.d_out[(size_t)s_tok[r] * H + col];
+            } else {
+              const float* gp = a.gu + p * 2 * I + col;
+              v = silu(gp[0]) * gp[I];
+            }
+          } else {
+            v = isB ? a.gu[p * 2 * I + col]
+                    : __uint_as_float((uint32_t)a.x[(size_t)s_tok[r] * H + col] << 16);
+          }
+        }
+        sv[u] = v;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (r0 + u < nr) {
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const f32x4_t z = s_vec[r0 + u][qq];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[4 * qq + i] = fmaf(sv[u], z[i], acc[4 * qq + i]);
+          }
+        }
+      }
+    }
+  }
+  if (!cv) return;
+  const float sc = a.lora_scale;
+  if (isB) {
+    float* o = (part == 0 ? a.g_b_down : a.g_b_gate_up) + ((size_t)e * nB + col) * kRank;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      *reinterpret_cast<f32x4_t*>(o + 4 * qq) =
+          f32x4_t{sc * acc[4 * qq], sc * acc[4 * qq + 1], sc * acc[4 * qq + 2], sc * acc[4 * qq + 3]};
+  } else {
+    float* o = (part == 0 ? a.g_a_down : a.g_a_gate_up) + (size_t)e * kRank * nA + col;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[(size_t)j * nA] = sc * acc[j];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s) {
+  const int Nn = down ? a.H : 2 * a.I;
+  if (Nn % 64 || Nn > 64 * kMaxBlocks * kWaves || a.I % 64 || a.I > 64 * kMaxBlocks * kWaves)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lora_bt_kernel, dim3(a.max_items), dim3(64 * kWaves), 0, s, a, down ? 0 : 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_grad(const BwdArgs& a, bool down, hipStream_t s) {
+  const int nB = down ? a.H : 2 * a.I, nA = down ? a.I : a.H;
+  hipLaunchKernelGGL(lora_grad_kernel, dim3((nB + 255) / 256 + (nA + 255) / 256, a.E), dim3(256), 0, s, a,
+                     down ? 0 : 1);
+  return hipGetLastError();
+}
 
 hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s) {
   if (a.K % 64 || a.K > 64 * kMaxBlocks * kWaves) return hipErrorInvalidValue;

@@ -171,12 +171,19 @@ class MoELayer:
     def backward(self, x: torch.Tensor, d_out: torch.Tensor, T: Optional[int] = None, stream=None):
         """Gradients for the routing of the last forward on this layer's
         workspace (a train layer; that forward must have been of the same x):
-        returns (d_x fp32 [T][H], d_topk_w fp32 [T][k])."""
+        returns (d_x fp32 [T][H], d_topk_w fp32 [T][k]), and with adapters
+        attached a third item, the adapter gradients {a_gate_up, b_gate_up,
+        a_down, b_down} (fp32, the adapters' shapes)."""
         T = T or x.shape[0]
         d_x = torch.empty(T, self.H, dtype=torch.float32, device=self.device)
         d_w = torch.empty(T, self.k, dtype=torch.float32, device=self.device)
-        L.moe_backward(self.cfg, self.w, x, T, d_out, d_x, d_w, self.workspace, self.ws_bytes, stream)
-        return d_x, d_w
+        grads, d_lora = None, None
+        if self.lora is not None:
+            grads = {n: torch.empty_like(self.tensors["lora_" + n])
+                     for n in ("a_gate_up", "b_gate_up", "a_down", "b_down")}
+            d_lora = L.make_lora_grads(grads["a_gate_up"], grads["b_gate_up"], grads["a_down"], grads["b_down"])
+        L.moe_backward(self.cfg, self.w, x, T, d_out, d_x, d_w, self.workspace, self.ws_bytes, stream, d_lora)
+        return (d_x, d_w) if grads is None else (d_x, d_w, grads)
 
     def forward_timed(self, x: torch.Tensor, out: torch.Tensor, events, T: Optional[int] = None,
                       stream=None) -> None:

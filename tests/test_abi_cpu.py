@@ -265,8 +265,9 @@ def test_backward_validation_on_host():
     lib = L.lib()
     w = weights()
 
-    def st(c, T=8):
-        return lib.moe_backward(ctypes.byref(c), ctypes.byref(w), FAKE, T, FAKE * 2, FAKE * 3, None, FAKE * 4,
+    def st(c, T=8, ww=None, d_lora=None):
+        return lib.moe_backward(ctypes.byref(c), ctypes.byref(ww or w), FAKE, T, FAKE * 2, FAKE * 3, None,
+                                None if d_lora is None else ctypes.byref(d_lora), FAKE * 4,
                                 L.moe_workspace_size(c), None)
 
     tiled = dict(wfmt=L.MOE_W_BF16_TILED)
@@ -275,6 +276,20 @@ def test_backward_validation_on_host():
     assert st(cfg(train=1)) == L.MOE_ERR_UNSUPPORTED                     # row-major weights
     assert st(cfg(train=1, topk_weights=L.MOE_TOPK_SOFTMAX, **tiled)) == L.MOE_ERR_UNSUPPORTED
     assert st(cfg(train=1, t_max=4096, **tiled), T=512) == L.MOE_ERR_UNSUPPORTED   # MFMA sizes
-    # a training config has room for the pre-activations
-    assert L.moe_workspace_size(cfg(train=1, **tiled)) == L.moe_workspace_size(cfg(**tiled)) + 64 * 8 * 2 * 768 * 4
+    # a training config has room for the pre-activations and the two rank-16 z rows per slot
+    assert (L.moe_workspace_size(cfg(train=1, **tiled))
+            == L.moe_workspace_size(cfg(**tiled)) + 64 * 8 * 2 * 768 * 4 + 2 * 64 * 8 * 16 * 4)
+    # LoRA: gradient arrays exactly when adapters are given (every case fails before any launch)
+    lo = L.moe_lora(FAKE, FAKE * 2, FAKE * 3, FAKE * 5, 2.0, 16)
+    wl = weights()
+    wl.lora = ctypes.addressof(lo)
+    good = L.moe_lora_grads(FAKE * 6, FAKE * 7, FAKE * 9, FAKE * 11)
+    tr = cfg(train=1, **tiled)
+    assert st(tr, ww=wl) == L.MOE_ERR_INVALID_ARG
+    assert "d_lora" in L.moe_last_error()
+    assert st(tr, d_lora=good) == L.MOE_ERR_INVALID_ARG
+    assert st(tr, ww=wl, d_lora=L.moe_lora_grads(FAKE * 6, FAKE * 7, None, FAKE * 11)) == L.MOE_ERR_INVALID_ARG
+    assert st(tr, ww=wl, d_lora=L.moe_lora_grads(FAKE * 6, FAKE + 4, FAKE * 9, FAKE * 11)) == L.MOE_ERR_INVALID_ARG
+    assert st(cfg(train=1, inter=2560, **tiled), ww=wl, d_lora=good) == L.MOE_ERR_UNSUPPORTED   # 2I > 4096
+    assert "2*inter" in L.moe_last_error()
 

@@ -2,7 +2,10 @@
 fp64 oracle's chain rule: input and routing-weight gradients within the bf16
 tolerance; the same bits on every run and whatever the batch; the
 unsupported configurations refused.  A training forward (train=1) keeps the
-gate/up pre-activations; its outputs are the same bits as a plain forward's."""
+gate/up pre-activations; its outputs are the same bits as a plain forward's.
+With rank-16 LoRA adapters: the chain rule through W + scale*B A and the
+four adapter gradients, against the oracle's, zero for experts no row
+reached; zero B gives the frozen-weight d_x bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -65,8 +68,7 @@ def test_backward_refuses_unsupported_configurations():
     x = torch.zeros(8, inp.H, dtype=torch.int16, device="cuda")
     g = torch.zeros(8, inp.H, dtype=torch.float32, device="cuda")
     for lay in (layer("q64", 64), layer("q64", 64, tiled=False).with_options(train=True),
-                layer("q64", 64).with_options(renorm=False, train=True), layer("q48q", 64).with_options(train=True),
-                layer("q64", 64).with_options(train=True).with_lora(S.lora_adapters(inp.E, inp.H, inp.I))):
+                layer("q64", 64).with_options(renorm=False, train=True), layer("q48q", 64).with_options(train=True)):
         lay.forward(x)
         with pytest.raises(L.MoEError) as ei:
             lay.backward(x, g)
@@ -83,3 +85,83 @@ def test_training_forward_gives_the_same_output():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
+
+
+LORA_NAMES = ("a_gate_up", "b_gate_up", "a_down", "b_down")
+# Adapter gradients: every factor is fp32 (U = A x, z = B^T v, h = silu(g) u
+# from the kept g, u) except d_h, whose GEMV takes v as two bf16 parts (about
+# 16 bits); the weights are exact bf16 with fp32 accumulation.  Elementwise
+# relative error is then ~1e-5; these rank-1 (per row) outer products have
+# max/rms ratios up to ~20, so max|err|/rms ~2e-4; 2e-3 leaves a factor 10.
+TOL_LORA_GRAD = 2e-3
+
+
+def gpu_backward_lora(lay, x_bits, d_out):
+    x = lay.upload_x(x_bits)
+    lay.forward(x)
+    d_x, d_w, g = lay.backward(x, torch.from_numpy(d_out).cuda())
+    torch.cuda.synchronize()
+    return d_x.cpu().numpy(), d_w.cpu().numpy(), {n: v.cpu().numpy() for n, v in g.items()}
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 8), ("tiny", 33), ("q8", None), ("q64", 24)])
+def test_backward_lora_matches_oracle(name, T):
+    inp = workload(name, T)
+    d = S.lora_adapters(inp.E, inp.H, inp.I)
+    lay = layer(*LAYER_OF[name]).with_options(train=True).with_lora(d)
+    d_out = d_out_for(inp.T, inp.H, seed=23)
+    say(f"[gpu] backward with LoRA {name} T={inp.T}")
+    d_x, d_w, g = gpu_backward_lora(lay, inp.x, d_out)
+    base = "q64" if name in ("q8", "q64") else name
+    b = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights(base), lora=O.LoRA(**d))
+    assert np.array_equal(lay.views(inp.T)["ids"].cpu().numpy(), b["routing"]["ids"])
+    errs = {"d_x": rel(d_x, b["d_x"]), "d_w": rel(d_w, b["d_w"])}
+    for n in LORA_NAMES:
+        assert g[n].shape == d[n].shape
+        errs[n] = rel(g[n], b["d_" + n])
+    say("[gpu]   max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_BF16 and errs["d_w"] <= TOL_BF16
+    assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
+    # experts no row reached: exactly zero gradients
+    hit = np.zeros(inp.E, bool)
+    hit[b["routing"]["ids"].ravel()] = True
+    for n in LORA_NAMES:
+        assert not g[n][~hit].any()
+        assert np.abs(g[n][hit]).max() > 0
+
+
+def test_backward_lora_deterministic():
+    inp = workload("q64", 64)
+    lay = layer("q64", 64).with_options(train=True).with_lora(S.lora_adapters(inp.E, inp.H, inp.I))
+    d_out = d_out_for(64, inp.H, seed=29)
+    a = gpu_backward_lora(lay, inp.x, d_out)
+    b = gpu_backward_lora(lay, inp.x, d_out)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert all(np.array_equal(a[2][n], b[2][n]) for n in LORA_NAMES)
+    # a row's d_x depends on its token only; the adapter gradients sum over the batch
+    c = gpu_backward_lora(lay, inp.x[:13], d_out[:13])
+    assert np.array_equal(c[0], a[0][:13]) and np.array_equal(c[1], a[1][:13])
+
+
+def test_backward_lora_zero_b_is_the_frozen_backward():
+    """B = 0: the adapters add exactly nothing to g, u or y (so d_w is the
+    frozen backward's, bit for bit), z = B^T v = 0 makes d_A exactly zero,
+    d_B and d_x are still the oracle's (d_x within the tolerance: with
+    adapters the down GEMV carries v in two bf16 parts)."""
+    inp = workload("q64", 16)
+    d = S.lora_adapters(inp.E, inp.H, inp.I)
+    d["b_gate_up"][:] = 0
+    d["b_down"][:] = 0
+    base = layer("q64", 64).with_options(train=True)
+    lay = base.with_lora(d)
+    d_out = d_out_for(16, inp.H, seed=31)
+    ref = gpu_backward(base, inp.x, d_out)
+    d_x, d_w, g = gpu_backward_lora(lay, inp.x, d_out)
+    assert np.array_equal(d_w, ref[1])
+    assert not g["a_gate_up"].any() and not g["a_down"].any()
+    b = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights("q64"), lora=O.LoRA(**d))
+    errs = {"d_x": rel(d_x, b["d_x"]), "d_x frozen": rel(ref[0], b["d_x"]),
+            "b_down": rel(g["b_down"], b["d_b_down"]), "b_gate_up": rel(g["b_gate_up"], b["d_b_gate_up"])}
+    say("[gpu]   zero B: max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_BF16 and errs["d_x frozen"] <= TOL_BF16
+    assert errs["b_down"] <= TOL_LORA_GRAD and errs["b_gate_up"] <= TOL_LORA_GRAD

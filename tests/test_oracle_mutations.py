@@ -130,6 +130,19 @@ def backward_uncentred_softmax(inp, d_out, weights=None, routing=None):
     return dict(b, d_x=d_x, d_logits=wrong)
 
 
+def backward_lora_variant(kind):
+    """LoRA backward mistakes: the adapter gradients without the scale, or
+    d_x taken through the frozen weights alone (adapter path dropped)."""
+    def f(inp, d_out, weights=None, routing=None, lora=None):
+        b = ORIG_BACKWARD(inp, d_out, weights, routing, lora)
+        if lora is None:
+            return b
+        if kind == "scale_dropped":
+            return dict(b, **{n: b[n] / lora.scale for n in ("d_a_gate_up", "d_b_gate_up", "d_a_down", "d_b_down")})
+        return dict(b, d_x=ORIG_BACKWARD(inp, d_out, weights, routing)["d_x"])
+    return f
+
+
 ORIG_BACKWARD = M.backward_per_token
 ORIG_LORA_OF = M._lora_of
 ORIG_MLP = M.expert_mlp
@@ -190,6 +203,12 @@ MUTATIONS = {
     "backward_softmax_not_centred": (lambda mp: patch(mp, "backward_per_token", backward_uncentred_softmax),
                                      [BP.test_backward_matches_torch_autograd,
                                       BP.test_backward_finite_differences]),
+    "backward_lora_grad_scale_dropped": (lambda mp: patch(mp, "backward_per_token",
+                                                          backward_lora_variant("scale_dropped")),
+                                         [BP.test_backward_with_lora_matches_torch_autograd]),
+    "backward_lora_d_x_through_frozen_weights": (lambda mp: patch(mp, "backward_per_token",
+                                                                  backward_lora_variant("dx_frozen")),
+                                                 [BP.test_backward_with_lora_matches_torch_autograd]),
     "sigmoid_not_silu": (lambda mp: patch(mp, "silu", sigmoid_not_silu),
                          [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
     "gate_up_swapped": (swap_gate_up,
