@@ -401,7 +401,7 @@ def silu_grad(z):
 
 
 def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, routing=None,
-                       lora: Optional["LoRA"] = None):
+                       lora: Optional["LoRA"] = None, weight_grads: bool = False):
     """The chain rule through the block, token by token, for fixed routing
     (the top-k choice is piecewise constant in x):
       d_w[t,j] = <d_out[t], y[t,j]>
@@ -413,8 +413,12 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
     gradients summed over every routed (token, expert) pair:
       d_B_d += s d_y (A_d h)^T,   d_A_d += s (B_d^T d_y) h^T
       d_B_gu += s [d_g; d_u] (A_gu x)^T,   d_A_gu += s (B_gu^T [d_g; d_u]) x^T
+    With weight_grads, the gradients of the expert weights themselves (the
+    same for W alone or W + s B A, whose derivative in W is the identity):
+      d_W_gu[e] += [d_g; d_u] x^T,   d_W_d[e] += d_y h^T
     Returns dict(d_x fp64 [T][H], d_w fp64 [T][k], d_logits fp64 [T][k],
-    routing, and with lora: d_a_gate_up, d_b_gate_up, d_a_down, d_b_down)."""
+    routing, with lora: d_a_gate_up, d_b_gate_up, d_a_down, d_b_down, with
+    weight_grads: d_w_gate_up [E][2I][H], d_w_down [E][H][I])."""
     if routing is None:
         ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias)
         routing = dict(ids=ids, w=w, logits=l32)
@@ -430,6 +434,9 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
     if lora is not None:
         grads = {n: np.zeros(np.shape(getattr(lora, n)), dtype=np.float64)
                  for n in ("a_gate_up", "b_gate_up", "a_down", "b_down")}
+    wgrads = None
+    if weight_grads:
+        wgrads = {"w_gate_up": np.zeros((inp.E, 2 * inp.I, inp.H)), "w_down": np.zeros((inp.E, inp.H, inp.I))}
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
@@ -450,6 +457,10 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
             d_g = d_h * u * silu_grad(g)
             d_u = d_h * silu(g)
             d_x[t] += d_g @ wg + d_u @ wu
+            if wgrads is not None:
+                wgrads["w_gate_up"][e, :inp.I] += np.outer(d_g, x64[t])
+                wgrads["w_gate_up"][e, inp.I:] += np.outer(d_u, x64[t])
+                wgrads["w_down"][e] += np.outer(d_y, h)
             if lora is not None:
                 d_gu = np.concatenate([d_g, d_u])
                 b_gu = np.concatenate([b_g, b_u])
@@ -464,6 +475,8 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
     out = dict(d_x=d_x, d_w=d_w, d_logits=d_l, routing=routing)
     if grads is not None:
         out.update({"d_" + n: v for n, v in grads.items()})
+    if wgrads is not None:
+        out.update({"d_" + n: v for n, v in wgrads.items()})
     return out
 
 

@@ -105,3 +105,43 @@ def test_backward_with_lora_matches_torch_autograd():
         ref = P[n].grad.numpy()
         assert np.abs(b["d_" + n] - ref).max() <= 1e-12 * rms(ref), n
 
+
+
+def test_backward_weight_grads_match_torch_autograd():
+    """The expert-weight gradients against torch autograd on the dense
+    formulation with every expert's stacked gate/up and down matrices as
+    leaf tensors, without and with LoRA adapters (W + s B A: the gradient in
+    W is the same expression)."""
+    inp = S.make_small(5, 128, 8, 2, 64, seed=47, bias=True)
+    d_out = np.random.default_rng(13).standard_normal((inp.T, inp.H))
+    for d in (None, S.lora_adapters(inp.E, inp.H, inp.I, seed=5)):
+        lora = None if d is None else O.LoRA(**d)
+        b = O.backward_per_token(inp, d_out, lora=lora, weight_grads=True)
+        ids = b["routing"]["ids"]
+        x = torch.from_numpy(O.bf16_bits_to_f64(inp.x))
+        wr = torch.from_numpy(O.bf16_bits_to_f64(inp.w_router))
+        l64 = x @ wr.T
+        l32 = l64.float() + torch.from_numpy(np.asarray(inp.bias, np.float32))
+        mask = torch.zeros_like(l64, dtype=torch.bool).scatter_(1, torch.from_numpy(ids.astype(np.int64)), True)
+        gw = torch.softmax(l32.double().masked_fill(~mask, float("-inf")), dim=1)
+        WG = torch.from_numpy(O.bf16_bits_to_f64(inp.w_gate_up)).requires_grad_(True)
+        WD = torch.from_numpy(O.bf16_bits_to_f64(inp.w_down)).requires_grad_(True)
+        out = torch.zeros(inp.T, inp.H, dtype=torch.float64)
+        for e in range(inp.E):
+            gu, wd = WG[e], WD[e]
+            if d is not None:
+                s = float(d["scale"])
+                gu = gu + s * torch.from_numpy(np.asarray(d["b_gate_up"][e], np.float64)) @ \
+                    torch.from_numpy(np.asarray(d["a_gate_up"][e], np.float64))
+                wd = wd + s * torch.from_numpy(np.asarray(d["b_down"][e], np.float64)) @ \
+                    torch.from_numpy(np.asarray(d["a_down"][e], np.float64))
+            h = torch.nn.functional.silu(x @ gu[: inp.I].T) * (x @ gu[inp.I:].T)
+            out = out + gw[:, e:e + 1] * (h @ wd.T)
+        (out * torch.from_numpy(d_out)).sum().backward()
+        for name, leaf in (("d_w_gate_up", WG), ("d_w_down", WD)):
+            ref = leaf.grad.numpy()
+            assert b[name].shape == ref.shape
+            assert np.abs(b[name] - ref).max() <= 1e-12 * np.sqrt(np.mean(ref * ref)), name
+        # experts no token chose get exactly zero
+        miss = np.setdiff1d(np.arange(inp.E), ids.ravel())
+        assert not b["d_w_gate_up"][miss].any() and not b["d_w_down"][miss].any()

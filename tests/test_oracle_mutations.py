@@ -143,6 +143,21 @@ def backward_lora_variant(kind):
     return f
 
 
+def backward_wgrad_variant(kind):
+    """Expert-weight gradient mistakes: gate and up halves swapped, or the
+    down gradient taken with d_out instead of w * d_out."""
+    def f(inp, d_out, weights=None, routing=None, lora=None, weight_grads=False):
+        b = ORIG_BACKWARD(inp, d_out, weights, routing, lora, weight_grads)
+        if not weight_grads:
+            return b
+        if kind == "halves_swapped":
+            g = b["d_w_gate_up"]
+            return dict(b, d_w_gate_up=np.concatenate([g[:, inp.I:], g[:, :inp.I]], axis=1))
+        r = dict(b["routing"], w=np.ones_like(b["routing"]["w"]))
+        return dict(b, d_w_down=ORIG_BACKWARD(inp, d_out, weights, r, lora, True)["d_w_down"])
+    return f
+
+
 ORIG_BACKWARD = M.backward_per_token
 ORIG_LORA_OF = M._lora_of
 ORIG_MLP = M.expert_mlp
@@ -209,6 +224,12 @@ MUTATIONS = {
     "backward_lora_d_x_through_frozen_weights": (lambda mp: patch(mp, "backward_per_token",
                                                                   backward_lora_variant("dx_frozen")),
                                                  [BP.test_backward_with_lora_matches_torch_autograd]),
+    "backward_wgrad_gate_up_halves_swapped": (lambda mp: patch(mp, "backward_per_token",
+                                                               backward_wgrad_variant("halves_swapped")),
+                                              [BP.test_backward_weight_grads_match_torch_autograd]),
+    "backward_wgrad_down_without_routing_weight": (lambda mp: patch(mp, "backward_per_token",
+                                                                    backward_wgrad_variant("unweighted")),
+                                                   [BP.test_backward_weight_grads_match_torch_autograd]),
     "sigmoid_not_silu": (lambda mp: patch(mp, "silu", sigmoid_not_silu),
                          [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
     "gate_up_swapped": (swap_gate_up,
