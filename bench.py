@@ -469,6 +469,25 @@ def main():
                             "hbm_frac": round(bbl / (tbl * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] backward with LoRA gradients: {tbl:.1f} us, "
             f"{backward['lora']['hbm_frac'] * 100:.1f}% of HBM peak")
+        # with the expert-weight gradients (fp32, every expert's full shape)
+        wg = (torch.empty(E, 2 * I, H, dtype=torch.float32, device="cuda"),
+              torch.empty(E, H, I, dtype=torch.float32, device="cuda"))
+        tbw = 0.0
+        with torch.cuda.stream(stream):
+            for i in range(nb + 3):
+                tl.forward(x_static, T, out_static, stream=stream)
+                L.hip_event_record(evb[0], stream)
+                tl.backward(x_static, d_out, T, stream=stream, weight_grads=wg)
+                L.hip_event_record(evb[1], stream)
+                torch.cuda.synchronize()
+                if i >= 3:
+                    tbw += L.hip_event_elapsed_ms(evb[0], evb[1]) * 1e3 / nb
+        bbw = bb + E * 3 * I * H * 4
+        backward["weight_grads"] = {"us_per_step": round(tbw, 2), "algorithmic_bytes": int(bbw),
+                                    "hbm_frac": round(bbw / (tbw * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] backward with expert-weight gradients: {tbw:.1f} us, "
+            f"{backward['weight_grads']['hbm_frac'] * 100:.1f}% of HBM peak")
+        del wg
         L.hip_events_destroy(evb)
 
     # ---------------- measured ceilings of this chip in the same run

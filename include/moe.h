@@ -272,11 +272,18 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
  * (d_y = w_j d_out[t]; h = silu(g) * u in fp32 from the kept g, u, which
  * also replaces the forward's A_d h rows in the workspace); an expert no
  * row reached gets zeros.  Needs 2 * I <= 4096.
+ * With d_weights, also the gradients of the expert weights themselves,
+ * summed over the routed pairs (the same expression with or without
+ * adapters, since W + scale * B A has derivative 1 in W):
+ *   d_W_gate_up[e] = sum [d_g; d_u] x^T,   d_W_down[e] = sum d_y h^T
+ * (h = silu(g) * u in fp32 as above), zeros for an expert no row reached.
  *   d_out     fp32 [T][H]
  *   d_x       fp32 [T][H] (written)
  *   d_topk_w  fp32 [T][k] (written), or NULL
  *   d_lora    host pointer to the gradient arrays (device, written, shapes of
- *             moe_lora's arrays), non-NULL exactly when w->lora is */
+ *             moe_lora's arrays), non-NULL exactly when w->lora is
+ *   d_weights host pointer to the expert-weight gradient arrays (device,
+ *             written, 16-byte aligned), or NULL */
 typedef struct {
   float* d_a_gate_up;  /* [E][r][H] */
   float* d_b_gate_up;  /* [E][2I][r] */
@@ -284,9 +291,15 @@ typedef struct {
   float* d_b_down;     /* [E][H][r] */
 } moe_lora_grads;
 
+typedef struct {
+  float* d_w_gate_up;  /* [E][2I][H] fp32, row-major (gate rows, then up rows) */
+  float* d_w_down;     /* [E][H][I] fp32, row-major */
+} moe_weight_grads;
+
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
                         const float* d_out, float* d_x, float* d_topk_w, const moe_lora_grads* d_lora,
-                        void* workspace, size_t ws_bytes, hipStream_t stream);
+                        const moe_weight_grads* d_weights, void* workspace, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* One-time conversion of row-major expert weights (cfg->wfmt = MOE_W_BF16 or
  * MOE_W_NF4_B64) into the tiled layout of MOE_W_BF16_TILED /

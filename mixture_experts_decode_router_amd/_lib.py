@@ -68,6 +68,10 @@ class moe_lora_grads(Structure):
                 ("d_b_down", c_void_p)]
 
 
+class moe_weight_grads(Structure):
+    _fields_ = [("d_w_gate_up", c_void_p), ("d_w_down", c_void_p)]
+
+
 class moe_prenorm(Structure):
     _fields_ = [("residual", c_void_p), ("delta", c_void_p), ("gamma", c_void_p), ("eps", ctypes.c_float),
                 ("residual_out", c_void_p), ("x_out", c_void_p)]
@@ -121,7 +125,7 @@ def lib() -> ctypes.CDLL:
         "moe_graph_bucket_for": (c_int32, [c_void_p, c_int32]),
         "moe_graph_destroy": (None, [c_void_p]),
         "moe_backward": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32, c_void_p, c_void_p,
-                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                             c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_forward_prenorm": (S, [POINTER(moe_config), POINTER(moe_weights), POINTER(moe_prenorm), c_int32,
                                     c_void_p, c_void_p, c_size_t, c_void_p]),
         "moe_graph_capture_prenorm": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
@@ -214,12 +218,15 @@ def make_lora_grads(d_a_gate_up, d_b_gate_up, d_a_down, d_b_down) -> moe_lora_gr
     return moe_lora_grads(ptr(d_a_gate_up), ptr(d_b_gate_up), ptr(d_a_down), ptr(d_b_down))
 
 
-def moe_backward(cfg, w, x, T, d_out, d_x, d_topk_w, workspace, ws_bytes=None, stream=None, d_lora=None):
-    """d_lora: a moe_lora_grads (make_lora_grads) when w carries adapters, else None."""
+def moe_backward(cfg, w, x, T, d_out, d_x, d_topk_w, workspace, ws_bytes=None, stream=None, d_lora=None,
+                 d_weights=None):
+    """d_lora: a moe_lora_grads (make_lora_grads) when w carries adapters, else
+    None; d_weights: a moe_weight_grads for the expert-weight gradients, or None."""
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().moe_backward(ctypes.byref(cfg), ctypes.byref(w), ptr(x), T, ptr(d_out), ptr(d_x), ptr(d_topk_w),
                               None if d_lora is None else ctypes.byref(d_lora),
+                              None if d_weights is None else ctypes.byref(d_weights),
                               ptr(workspace), ws_bytes, stream_handle(stream)))
 
 

@@ -469,8 +469,8 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
 }
 
 moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, const float* d_out,
-                        float* d_x, float* d_topk_w, const moe_lora_grads* d_lora, void* workspace, size_t ws_bytes,
-                        hipStream_t stream) {
+                        float* d_x, float* d_topk_w, const moe_lora_grads* d_lora, const moe_weight_grads* d_weights,
+                        void* workspace, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_forward_args(cfg, w, x, T, d_x, workspace, ws_bytes));
   const moe_config& c = *cfg;
   if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED || c.topk_weights != MOE_TOPK_RENORM || mfma_path_for(c, T))
@@ -486,6 +486,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     MOE_TRY(check_ptr(d_lora->d_b_gate_up, "d_b_gate_up"));
     MOE_TRY(check_ptr(d_lora->d_a_down, "d_a_down"));
     MOE_TRY(check_ptr(d_lora->d_b_down, "d_b_down"));
+  }
+  if (d_weights) {
+    MOE_TRY(check_ptr(d_weights->d_w_gate_up, "d_w_gate_up"));
+    MOE_TRY(check_ptr(d_weights->d_w_down, "d_w_down"));
   }
   const Layout L = layout(c);
   const int N = T * c.top_k;
@@ -512,11 +516,16 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.w_down = static_cast<const uint16_t*>(w->w_down);
   b.gu = at<float>(workspace, L.gu);
   b.d_xs = at<float>(workspace, L.y);  // y is read first, then its memory holds the per-slot d_x
+  b.x = static_cast<const uint16_t*>(x);
+  if (d_weights) {
+    b.wgrad = true;
+    b.g_w_gate_up = d_weights->d_w_gate_up;
+    b.g_w_down = d_weights->d_w_down;
+  }
   if (w->lora) {
     const moe_lora& l = *w->lora;
     b.lora = true;
     b.lora_scale = l.scale;
-    b.x = static_cast<const uint16_t*>(x);
     b.h = at<uint16_t>(workspace, L.h);
     b.la_gate_up = l.a_gate_up;
     b.lb_gate_up = l.b_gate_up;
@@ -532,19 +541,23 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     b.g_b_down = d_lora->d_b_down;
   }
   hipError_t e;
-  // with adapters the down-adapter gradients read g, u, so they come before
-  // the down pass turns those into d_g, d_u; the gate/up ones after it
+  // the down-adapter and down-weight gradients read g, u, so they come
+  // before the down pass turns those into d_g, d_u; the gate/up ones after it
   if ((e = moe::launch_bwd_weights(b, stream)) != hipSuccess) return hip_fail(e, "backward weights launch");
   if (b.lora) {
     if ((e = moe::launch_lora_bt(b, true, stream)) != hipSuccess) return hip_fail(e, "LoRA down B^T launch");
     if ((e = moe::launch_lora_grad(b, true, stream)) != hipSuccess) return hip_fail(e, "LoRA down gradient launch");
   }
+  if (b.wgrad && (e = moe::launch_wgrad(b, true, stream)) != hipSuccess)
+    return hip_fail(e, "down weight gradient launch");
   if ((e = moe::launch_bwd_t(b, true, stream)) != hipSuccess) return hip_fail(e, "backward down launch");
   if (b.lora) {
     if ((e = moe::launch_lora_bt(b, false, stream)) != hipSuccess) return hip_fail(e, "LoRA gate/up B^T launch");
     if ((e = moe::launch_lora_grad(b, false, stream)) != hipSuccess)
       return hip_fail(e, "LoRA gate/up gradient launch");
   }
+  if (b.wgrad && (e = moe::launch_wgrad(b, false, stream)) != hipSuccess)
+    return hip_fail(e, "gate/up weight gradient launch");
   if ((e = moe::launch_bwd_t(b, false, stream)) != hipSuccess) return hip_fail(e, "backward gate/up launch");
   if ((e = moe::launch_bwd_combine(b, stream)) != hipSuccess) return hip_fail(e, "backward combine launch");
   return MOE_OK;

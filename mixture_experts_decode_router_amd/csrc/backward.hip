@@ -120,12 +120,13 @@ __global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
 // 8 columns, so neither the 2-byte writes nor the reads pile onto few banks);
 // a lane's B operand (column r or 16 + r, m = 8g .. 8g+7) is then one
 // 16-byte read.  v enters the MFMA rounded to bf16, except in the DOWN pass
-// with adapters (LORA), where it enters as two bf16 parts, hi = RNE(v) and
-// lo = RNE(v - hi), in two MFMAs into the same accumulator, so that d_h
-// carries about 16 bits of v (the weights are exact in bf16): the gate/up
-// adapter gradients are outer products of d_g, d_u with U and of B^T (d_g,
-// d_u) with x, which pass each element's rounding error through unsmoothed.
-// (d_x, a sum over many terms, meets the bf16 tolerance either way.)
+// when adapter or weight gradients are formed (HILO), where it enters as two
+// bf16 parts, hi = RNE(v) and lo = RNE(v - hi), in two MFMAs into the same
+// accumulator, so that d_h carries about 16 bits of v (the weights are exact
+// in bf16): those gradients are outer products of d_g, d_u with U, x or of
+// B^T (d_g, d_u) with x, which pass each element's rounding error through
+// unsmoothed.  (d_x, a sum over many terms, meets the bf16 tolerance either
+// way.)
 //   DOWN:    W = W_d [H][I], v = w_p d_out[t_p], epilogue: SiLU backward,
 //            gu[p] (g, u) -> (d_g, d_u) in place.
 //   GATE_UP: W = W_gu [2I][H], v = (d_g, d_u)[p], epilogue: d_xs[slot(p)].
@@ -137,9 +138,9 @@ __device__ __forceinline__ int stage_off(int col) { return col * kColStride + (c
 // LoRA (LORA true): s * sum_j A[e][j][n] z[p][j] joins each output first
 // (z = B^T v from lora_bt; A = A_d for DOWN, A_gu for GATE_UP), the chain
 // rule through W + s B A.
-template <int MODE, bool LORA>
+template <int MODE, bool LORA, bool HILO>
 __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
-  constexpr bool kHiLo = LORA && MODE == kDown;
+  constexpr bool kHiLo = HILO && MODE == kDown;
   __shared__ __attribute__((aligned(16))) uint8_t s_frag[2][32 * kColStride + 4 * 16];
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
@@ -261,6 +262,102 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- weight gradients
+// d_W[e][r][c] = sum_p A[p][r] B[p][c] over expert e's routed rows p in slot
+// order (no atomics; zero for an expert no row reached):
+//   down (before the down pass turns g, u into d_g, d_u):
+//     A = d_y = w_p d_out[t_p] (r < H),  B = h = silu(g) u in fp32 (c < I)
+//   gate/up (after it): A = (d_g, d_u)[p] (r < 2I),  B = x[t_p] (c < H)
+// A workgroup covers 64 rows of one expert and a few 128-column tiles in
+// turn; thread (4 rows 16 apart, 8 consecutive columns) keeps 32 sums, so
+// each B value loaded serves 4 rows.  The routed rows' tokens and weights are
+// staged in LDS 64 at a time (once per workgroup when the expert has no more
+// rows); each thread's loads are issued 4 rows at a time.  The output is
+// write-bound: fp32 gradients the size of all experts' weights.
+constexpr int kWgRows = 64, kWgCols = 128, kWgChunk = 64, kWgU = 4, kWgTiles = 4;
+
+__global__ __launch_bounds__(256) void wgrad_kernel(BwdArgs a, int part) {
+  __shared__ int s_tok[kWgChunk];
+  __shared__ float s_w[kWgChunk];
+  const int H = a.H, I = a.I;
+  const int R = part == 0 ? H : 2 * I, C = part == 0 ? I : H;
+  const int e = blockIdx.z;
+  const int r0 = blockIdx.y * kWgRows + (threadIdx.x >> 4);  // rows r0 + 16 q
+  const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
+  const bool once = p1 - p0 <= kWgChunk;  // every row staged by the first pass
+  for (int ct = blockIdx.x; ct < C / kWgCols; ct += gridDim.x) {
+    const int c = ct * kWgCols + (threadIdx.x & 15) * 8;
+    float acc[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
+    for (int c0 = p0; c0 < p1; c0 += kWgChunk) {
+      const int nr = p1 - c0 < kWgChunk ? p1 - c0 : kWgChunk;
+      if (!once || ct == (int)blockIdx.x) {
+        __syncthreads();  // the previous chunk's LDS reads are done
+        if ((int)threadIdx.x < nr) {
+          const int slot = a.perm[c0 + threadIdx.x];
+          s_tok[threadIdx.x] = slot / a.k;
+          s_w[threadIdx.x] = a.wts[slot];
+        }
+        __syncthreads();
+      }
+      for (int j0 = 0; j0 < nr; j0 += kWgU) {
+        float av[kWgU][4], bv[kWgU][8];
+#pragma unroll
+        for (int u = 0; u < kWgU; ++u) {
+          const int j = j0 + u;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) av[u][q] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bv[u][i] = 0.f;
+          if (j < nr) {
+            const size_t p = (size_t)(c0 + j);
+            if (part == 0) {
+              const float* dr = a.d_out + (size_t)s_tok[j] * H + r0;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) av[u][q] = s_w[j] * dr[16 * q];
+              const float* gp = a.gu + p * 2 * I + c;
+              const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
+              const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gp + 4);
+              const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(gp + I);
+              const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gp + I + 4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                bv[u][i] = silu(g0[i]) * u0[i];
+                bv[u][4 + i] = silu(g1[i]) * u1[i];
+              }
+            } else {
+              const float* gr = a.gu + p * 2 * I + r0;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) av[u][q] = gr[16 * q];
+              const u32x4_t xv = ld16(a.x + (size_t)s_tok[j] * H + c);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                bv[u][2 * i] = bf16lo(xv[i]);
+                bv[u][2 * i + 1] = bf16hi(xv[i]);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kWgU; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[q][i] = fmaf(av[u][q], bv[u][i], acc[q][i]);
+      }
+    }
+    float* o = (part == 0 ? a.g_w_down : a.g_w_gate_up) + ((size_t)e * R + r0) * C + c;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<f32x4_t*>(o + (size_t)16 * q * C) = f32x4_t{acc[q][0], acc[q][1], acc[q][2], acc[q][3]};
+      *reinterpret_cast<f32x4_t*>(o + (size_t)16 * q * C + 4) = f32x4_t{acc[q][4], acc[q][5], acc[q][6], acc[q][7]};
+    }
+  }  // column tiles
+}
+
 // ---------------------------------------------------------------- combine
 __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdArgs a) {
   const int t = blockIdx.x;
@@ -287,15 +384,26 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
   const dim3 grid(a.max_items * ((down ? a.I : a.H) / 32));
   if (down) {
     if (a.lora)
-      hipLaunchKernelGGL((bwd_t_kernel<kDown, true>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, true, true>), grid, dim3(64), 0, s, a);
+    else if (a.wgrad)
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, true>), grid, dim3(64), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_t_kernel<kDown, false>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, false>), grid, dim3(64), 0, s, a);
   } else {
     if (a.lora)
-      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, true>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, true, false>), grid, dim3(64), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false, false>), grid, dim3(64), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const BwdArgs& a, bool down, hipStream_t s) {
+  const int R = down ? a.H : 2 * a.I, C = down ? a.I : a.H;
+  if (R % kWgRows || C % kWgCols) return hipErrorInvalidValue;
+  const int nct = C / kWgCols;
+  hipLaunchKernelGGL(wgrad_kernel, dim3((nct + kWgTiles - 1) / kWgTiles, R / kWgRows, a.E), dim3(256), 0, s, a,
+                     down ? 0 : 1);
   return hipGetLastError();
 }
 

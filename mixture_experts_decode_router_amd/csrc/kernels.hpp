@@ -132,7 +132,7 @@ struct BwdArgs {
   // z = B^T v, and the adapter gradients (same shapes as the adapters)
   bool lora;
   float lora_scale;
-  const uint16_t* x;          // bf16 [T][H] (the forward's input)
+  const uint16_t* x;          // bf16 [T][H] (the forward's input; LoRA or wgrad)
   const uint16_t* h;          // bf16 [N][I] sorted-slot order (the forward's h)
   const float* la_gate_up;    // [E][16][H]
   const float* lb_gate_up;    // [E][2I][16]
@@ -146,10 +146,16 @@ struct BwdArgs {
   float* g_b_gate_up;
   float* g_a_down;
   float* g_b_down;
+  // expert-weight gradients (wgrad true): fp32, the weights' row-major shapes
+  bool wgrad;
+  float* g_w_gate_up;         // [E][2I][H]
+  float* g_w_down;            // [E][H][I]
 };
 hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s);
 hipError_t launch_bwd_combine(const BwdArgs& a, hipStream_t s);
+// expert-weight gradients: down ones before bwd_t(down), gate/up ones after it
+hipError_t launch_wgrad(const BwdArgs& a, bool down, hipStream_t s);
 // LoRA backward: z = B^T v per routed row (down: v = w d_out, and U_d = A_d h
 // from the fp32 g, u; gate/up: v = (d_g, d_u))
 hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s);

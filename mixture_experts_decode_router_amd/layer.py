@@ -168,12 +168,15 @@ class MoELayer:
         L.moe_forward_prenorm(self.cfg, self.w, pn, T, out, self.workspace, self.ws_bytes, stream)
         return out, x_out, residual_out
 
-    def backward(self, x: torch.Tensor, d_out: torch.Tensor, T: Optional[int] = None, stream=None):
+    def backward(self, x: torch.Tensor, d_out: torch.Tensor, T: Optional[int] = None, stream=None,
+                 weight_grads=None):
         """Gradients for the routing of the last forward on this layer's
         workspace (a train layer; that forward must have been of the same x):
         returns (d_x fp32 [T][H], d_topk_w fp32 [T][k]), and with adapters
         attached a third item, the adapter gradients {a_gate_up, b_gate_up,
-        a_down, b_down} (fp32, the adapters' shapes)."""
+        a_down, b_down} (fp32, the adapters' shapes).  weight_grads: a pair of
+        fp32 device tensors ([E][2I][H], [E][H][I]) that receive the expert-
+        weight gradients, or None."""
         T = T or x.shape[0]
         d_x = torch.empty(T, self.H, dtype=torch.float32, device=self.device)
         d_w = torch.empty(T, self.k, dtype=torch.float32, device=self.device)
@@ -182,7 +185,15 @@ class MoELayer:
             grads = {n: torch.empty_like(self.tensors["lora_" + n])
                      for n in ("a_gate_up", "b_gate_up", "a_down", "b_down")}
             d_lora = L.make_lora_grads(grads["a_gate_up"], grads["b_gate_up"], grads["a_down"], grads["b_down"])
-        L.moe_backward(self.cfg, self.w, x, T, d_out, d_x, d_w, self.workspace, self.ws_bytes, stream, d_lora)
+        d_weights = None
+        if weight_grads is not None:
+            gu, dn = weight_grads
+            if tuple(gu.shape) != (self.E, 2 * self.I, self.H) or tuple(dn.shape) != (self.E, self.H, self.I) \
+                    or gu.dtype != torch.float32 or dn.dtype != torch.float32:
+                raise ValueError("weight_grads must be fp32 [E][2I][H] and [E][H][I]")
+            d_weights = L.moe_weight_grads(gu.data_ptr(), dn.data_ptr())
+        L.moe_backward(self.cfg, self.w, x, T, d_out, d_x, d_w, self.workspace, self.ws_bytes, stream, d_lora,
+                       d_weights)
         return (d_x, d_w) if grads is None else (d_x, d_w, grads)
 
     def forward_timed(self, x: torch.Tensor, out: torch.Tensor, events, T: Optional[int] = None,

@@ -401,7 +401,7 @@ def silu_grad(z):
 
 
 def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, routing=None,
-                       lora: Optional["LoRA"] = None, weight_grads: bool = False):
+                       lora: Optional["LoRA"] = None, weight_grads: bool = False, wgrad_experts=None):
     """The chain rule through the block, token by token, for fixed routing
     (the top-k choice is piecewise constant in x):
       d_w[t,j] = <d_out[t], y[t,j]>
@@ -418,7 +418,9 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
       d_W_gu[e] += [d_g; d_u] x^T,   d_W_d[e] += d_y h^T
     Returns dict(d_x fp64 [T][H], d_w fp64 [T][k], d_logits fp64 [T][k],
     routing, with lora: d_a_gate_up, d_b_gate_up, d_a_down, d_b_down, with
-    weight_grads: d_w_gate_up [E][2I][H], d_w_down [E][H][I])."""
+    weight_grads: d_w_gate_up [E][2I][H], d_w_down [E][H][I]; with
+    wgrad_experts, a list of experts, only those experts' slices, as dicts
+    expert -> array, so that large shapes can be checked expert by expert)."""
     if routing is None:
         ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias)
         routing = dict(ids=ids, w=w, logits=l32)
@@ -436,7 +438,11 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
                  for n in ("a_gate_up", "b_gate_up", "a_down", "b_down")}
     wgrads = None
     if weight_grads:
-        wgrads = {"w_gate_up": np.zeros((inp.E, 2 * inp.I, inp.H)), "w_down": np.zeros((inp.E, inp.H, inp.I))}
+        if wgrad_experts is None:
+            wgrads = {"w_gate_up": np.zeros((inp.E, 2 * inp.I, inp.H)), "w_down": np.zeros((inp.E, inp.H, inp.I))}
+        else:
+            wgrads = {"w_gate_up": {int(e): np.zeros((2 * inp.I, inp.H)) for e in wgrad_experts},
+                      "w_down": {int(e): np.zeros((inp.H, inp.I)) for e in wgrad_experts}}
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
@@ -457,9 +463,9 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
             d_g = d_h * u * silu_grad(g)
             d_u = d_h * silu(g)
             d_x[t] += d_g @ wg + d_u @ wu
-            if wgrads is not None:
-                wgrads["w_gate_up"][e, :inp.I] += np.outer(d_g, x64[t])
-                wgrads["w_gate_up"][e, inp.I:] += np.outer(d_u, x64[t])
+            if wgrads is not None and (wgrad_experts is None or e in wgrads["w_down"]):
+                wgrads["w_gate_up"][e][:inp.I] += np.outer(d_g, x64[t])
+                wgrads["w_gate_up"][e][inp.I:] += np.outer(d_u, x64[t])
                 wgrads["w_down"][e] += np.outer(d_y, h)
             if lora is not None:
                 d_gu = np.concatenate([d_g, d_u])

@@ -265,9 +265,10 @@ def test_backward_validation_on_host():
     lib = L.lib()
     w = weights()
 
-    def st(c, T=8, ww=None, d_lora=None):
+    def st(c, T=8, ww=None, d_lora=None, d_weights=None):
         return lib.moe_backward(ctypes.byref(c), ctypes.byref(ww or w), FAKE, T, FAKE * 2, FAKE * 3, None,
-                                None if d_lora is None else ctypes.byref(d_lora), FAKE * 4,
+                                None if d_lora is None else ctypes.byref(d_lora),
+                                None if d_weights is None else ctypes.byref(d_weights), FAKE * 4,
                                 L.moe_workspace_size(c), None)
 
     tiled = dict(wfmt=L.MOE_W_BF16_TILED)
@@ -292,4 +293,8 @@ def test_backward_validation_on_host():
     assert st(tr, ww=wl, d_lora=L.moe_lora_grads(FAKE * 6, FAKE + 4, FAKE * 9, FAKE * 11)) == L.MOE_ERR_INVALID_ARG
     assert st(cfg(train=1, inter=2560, **tiled), ww=wl, d_lora=good) == L.MOE_ERR_UNSUPPORTED   # 2I > 4096
     assert "2*inter" in L.moe_last_error()
+    # expert-weight gradient arrays: both present and 16-byte aligned
+    assert st(tr, d_weights=L.moe_weight_grads(None, FAKE * 6)) == L.MOE_ERR_INVALID_ARG
+    assert st(tr, d_weights=L.moe_weight_grads(FAKE * 6, FAKE + 8)) == L.MOE_ERR_INVALID_ARG
+    assert "d_w_down" in L.moe_last_error()
 

@@ -145,3 +145,14 @@ def test_backward_weight_grads_match_torch_autograd():
         # experts no token chose get exactly zero
         miss = np.setdiff1d(np.arange(inp.E), ids.ravel())
         assert not b["d_w_gate_up"][miss].any() and not b["d_w_down"][miss].any()
+
+
+def test_weight_grads_expert_subset_equals_full():
+    """The per-expert form (for large shapes) gives the full arrays' slices."""
+    inp = S.make("tiny")
+    d = np.random.default_rng(1).standard_normal((inp.T, inp.H))
+    a = O.backward_per_token(inp, d, weight_grads=True)
+    b = O.backward_per_token(inp, d, weight_grads=True, wgrad_experts=[0, 3, 5])
+    for e in (0, 3, 5):
+        assert np.array_equal(a["d_w_gate_up"][e], b["d_w_gate_up"][e])
+        assert np.array_equal(a["d_w_down"][e], b["d_w_down"][e])

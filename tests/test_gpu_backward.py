@@ -165,3 +165,72 @@ def test_backward_lora_zero_b_is_the_frozen_backward():
     say("[gpu]   zero B: max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
     assert errs["d_x"] <= TOL_BF16 and errs["d_x frozen"] <= TOL_BF16
     assert errs["b_down"] <= TOL_LORA_GRAD and errs["b_gate_up"] <= TOL_LORA_GRAD
+
+
+def weight_grad_buffers(lay):
+    return (torch.full((lay.E, 2 * lay.I, lay.H), float("nan"), dtype=torch.float32, device="cuda"),
+            torch.full((lay.E, lay.H, lay.I), float("nan"), dtype=torch.float32, device="cuda"))
+
+
+@pytest.mark.parametrize("name,T,with_lora", [("tiny", 8, False), ("tiny", 33, True), ("q8", None, False),
+                                              ("q64", 24, True)])
+def test_backward_weight_grads_match_oracle(name, T, with_lora):
+    """Expert-weight gradients (fp32, every expert: zeros where no row went)
+    against the oracle's; at the Qwen shape on a sample of experts (the most
+    and the least loaded active ones and one more) plus every inactive one."""
+    inp = workload(name, T)
+    d = S.lora_adapters(inp.E, inp.H, inp.I) if with_lora else None
+    lay = layer(*LAYER_OF[name]).with_options(train=True)
+    if d is not None:
+        lay = lay.with_lora(d)
+    d_out = d_out_for(inp.T, inp.H, seed=37)
+    say(f"[gpu] backward with weight gradients {name} T={inp.T} lora={with_lora}")
+    x = lay.upload_x(inp.x)
+    lay.forward(x)
+    wg = weight_grad_buffers(lay)
+    res = lay.backward(x, torch.from_numpy(d_out).cuda(), weight_grads=wg)
+    torch.cuda.synchronize()
+    counts = lay.views(inp.T)["counts"].cpu().numpy()
+    active = np.flatnonzero(counts)
+    small = inp.E <= 16
+    experts = list(range(inp.E)) if small else sorted({int(active[np.argmax(counts[active])]),
+                                                       int(active[np.argmin(counts[active])]), int(active[0])})
+    b = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights("q64" if name != "tiny" else name),
+                             lora=None if d is None else O.LoRA(**d), weight_grads=True, wgrad_experts=experts)
+    errs = {"d_x": rel(res[0].cpu().numpy(), b["d_x"])}
+    for key, dev in (("d_w_gate_up", wg[0]), ("d_w_down", wg[1])):
+        for e in experts:
+            got = dev[e].cpu().numpy()
+            ref = b[key][e]
+            if counts[e] == 0:
+                assert not got.any(), (key, e)
+            else:
+                errs[f"{key}[{e}]"] = rel(got, ref)
+    inactive = np.flatnonzero(counts == 0)
+    for dev in wg:
+        assert not bool(torch.isnan(dev).any())
+        if len(inactive):
+            assert not bool(dev[torch.from_numpy(inactive).cuda()].any())
+    say("[gpu]   max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_BF16
+    assert all(v <= TOL_LORA_GRAD for k, v in errs.items() if k != "d_x")
+    if d is not None:   # the adapter gradients are unchanged by also forming the weight gradients
+        ref_l = gpu_backward_lora(lay, inp.x, d_out)
+        for n in LORA_NAMES:
+            assert np.array_equal(res[2][n].cpu().numpy(), ref_l[2][n])
+
+
+def test_backward_weight_grads_deterministic():
+    inp = workload("q64", 64)
+    lay = layer("q64", 64).with_options(train=True)
+    d_out = torch.from_numpy(d_out_for(64, inp.H, seed=41)).cuda()
+    x = lay.upload_x(inp.x)
+    outs = []
+    for _ in range(2):
+        lay.forward(x)
+        wg = weight_grad_buffers(lay)
+        d_x, d_w = lay.backward(x, d_out, weight_grads=wg)
+        outs.append((d_x, d_w, wg))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][2][0], outs[1][2][0]) and torch.equal(outs[0][2][1], outs[1][2][1])
