@@ -401,7 +401,8 @@ def silu_grad(z):
 
 
 def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, routing=None,
-                       lora: Optional["LoRA"] = None, weight_grads: bool = False, wgrad_experts=None):
+                       lora: Optional["LoRA"] = None, weight_grads: bool = False, wgrad_experts=None,
+                       renorm: bool = True):
     """The chain rule through the block, token by token, for fixed routing
     (the top-k choice is piecewise constant in x):
       d_w[t,j] = <d_out[t], y[t,j]>
@@ -413,6 +414,10 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
     gradients summed over every routed (token, expert) pair:
       d_B_d += s d_y (A_d h)^T,   d_A_d += s (B_d^T d_y) h^T
       d_B_gu += s [d_g; d_u] (A_gu x)^T,   d_A_gu += s (B_gu^T [d_g; d_u]) x^T
+    renorm=False (the full softmax taken at the chosen experts, not
+    renormalised): w_j = p[id_j] with p the softmax over all E logits, so
+      d_l[t,e] = [e chosen] w_e d_w_e - p_e sum_j w_j d_w_j   for every e,
+    and the router share of d_x runs over all E experts (d_logits [T][E]).
     With weight_grads, the gradients of the expert weights themselves (the
     same for W alone or W + s B A, whose derivative in W is the identity):
       d_W_gu[e] += [d_g; d_u] x^T,   d_W_d[e] += d_y h^T
@@ -422,7 +427,7 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
     wgrad_experts, a list of experts, only those experts' slices, as dicts
     expert -> array, so that large shapes can be checked expert by expert)."""
     if routing is None:
-        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias)
+        ids, w, l32 = route(inp.x, inp.w_router, inp.k, inp.bias, renorm=renorm)
         routing = dict(ids=ids, w=w, logits=l32)
     ids, w = routing["ids"], routing["w"]
     W = weights or ExpertWeights(inp)
@@ -474,10 +479,20 @@ def backward_per_token(inp, d_out, weights: Optional[ExpertWeights] = None, rout
                 grads["a_down"][e] += s * np.outer(b_d.T @ d_y, h)
                 grads["b_gate_up"][e] += s * np.outer(d_gu, a_gu @ x64[t])
                 grads["a_gate_up"][e] += s * np.outer(b_gu.T @ d_gu, x64[t])
-    d_l = w * (d_w - np.sum(w * d_w, axis=1, keepdims=True))
-    for t in range(T):
-        for j in range(k):
-            d_x[t] += d_l[t, j] * wr[int(ids[t, j])]
+    if renorm:
+        d_l = w * (d_w - np.sum(w * d_w, axis=1, keepdims=True))
+        for t in range(T):
+            for j in range(k):
+                d_x[t] += d_l[t, j] * wr[int(ids[t, j])]
+    else:
+        l = np.asarray(routing["logits"], dtype=np.float64)
+        p = np.exp(l - l.max(axis=1, keepdims=True))
+        p = p / p.sum(axis=1, keepdims=True)
+        d_l = -p * np.sum(w * d_w, axis=1, keepdims=True)
+        for t in range(T):
+            for j in range(k):
+                d_l[t, int(ids[t, j])] += w[t, j] * d_w[t, j]
+        d_x += d_l @ wr
     out = dict(d_x=d_x, d_w=d_w, d_logits=d_l, routing=routing)
     if grads is not None:
         out.update({"d_" + n: v for n, v in grads.items()})

@@ -156,3 +156,38 @@ def test_weight_grads_expert_subset_equals_full():
     for e in (0, 3, 5):
         assert np.array_equal(a["d_w_gate_up"][e], b["d_w_gate_up"][e])
         assert np.array_equal(a["d_w_down"][e], b["d_w_down"][e])
+
+
+def test_backward_unrenormalised_matches_torch_autograd():
+    """Top-k weights without renormalisation (the full softmax at the chosen
+    experts): d_x and the logit gradient over all E experts against torch
+    autograd on the dense formulation with the unmasked softmax."""
+    for inp in (S.make("tiny"), S.make_small(6, 128, 8, 3, 64, seed=53, bias=True)):
+        d_out = np.random.default_rng(17).standard_normal((inp.T, inp.H))
+        b = O.backward_per_token(inp, d_out, renorm=False)
+        ids = b["routing"]["ids"]
+        x = torch.from_numpy(O.bf16_bits_to_f64(inp.x)).requires_grad_(True)
+        wr = torch.from_numpy(O.bf16_bits_to_f64(inp.w_router))
+        l64 = x @ wr.T
+        l32 = l64.detach().float()
+        if inp.bias is not None:
+            l32 = l32 + torch.from_numpy(np.asarray(inp.bias, np.float32))
+        l = l64 + (l32.double() - l64.detach())
+        l.retain_grad()
+        mask = torch.zeros_like(l, dtype=torch.bool).scatter_(1, torch.from_numpy(ids.astype(np.int64)), True)
+        g = torch.softmax(l, dim=1) * mask
+        out = torch.zeros(inp.T, inp.H, dtype=torch.float64)
+        for e in range(inp.E):
+            gu = torch.from_numpy(O.bf16_bits_to_f64(inp.w_gate_up[e]))
+            wd = torch.from_numpy(O.bf16_bits_to_f64(inp.w_down[e]))
+            h = torch.nn.functional.silu(x @ gu[: inp.I].T) * (x @ gu[inp.I:].T)
+            out = out + g[:, e:e + 1] * (h @ wd.T)
+        (out * torch.from_numpy(d_out)).sum().backward()
+        ref = x.grad.numpy()
+        assert np.abs(b["d_x"] - ref).max() <= 1e-12 * np.sqrt(np.mean(ref * ref))
+        assert b["d_logits"].shape == (inp.T, inp.E)
+        np.testing.assert_allclose(b["d_logits"], l.grad.numpy(), rtol=0,
+                                   atol=1e-12 * np.abs(l.grad.numpy()).max())
+        # the renormalised backward differs (its logit gradient lives on the k chosen only)
+        r = O.backward_per_token(inp, d_out)
+        assert np.abs(r["d_x"] - b["d_x"]).max() > 1e-6 * np.sqrt(np.mean(ref * ref))

@@ -158,6 +158,21 @@ def backward_wgrad_variant(kind):
     return f
 
 
+def backward_unrenorm_chosen_only(inp, d_out, weights=None, routing=None, lora=None, weight_grads=False,
+                                  wgrad_experts=None, renorm=True):
+    """The un-renormalised backward with the softmax gradient kept on the k
+    chosen logits only (the experts not chosen dropped from the router share)."""
+    b = ORIG_BACKWARD(inp, d_out, weights, routing, lora, weight_grads, wgrad_experts, renorm)
+    if renorm:
+        return b
+    ids = b["routing"]["ids"].astype(np.int64)
+    wr = M.bf16_bits_to_f64(inp.w_router)
+    keep = np.zeros_like(b["d_logits"], dtype=bool)
+    np.put_along_axis(keep, ids, True, axis=1)
+    dropped = np.where(keep, 0.0, b["d_logits"])
+    return dict(b, d_x=b["d_x"] - dropped @ wr, d_logits=np.where(keep, b["d_logits"], 0.0))
+
+
 ORIG_BACKWARD = M.backward_per_token
 ORIG_LORA_OF = M._lora_of
 ORIG_MLP = M.expert_mlp
@@ -230,6 +245,9 @@ MUTATIONS = {
     "backward_wgrad_down_without_routing_weight": (lambda mp: patch(mp, "backward_per_token",
                                                                     backward_wgrad_variant("unweighted")),
                                                    [BP.test_backward_weight_grads_match_torch_autograd]),
+    "backward_unrenormalised_chosen_only": (lambda mp: patch(mp, "backward_per_token",
+                                                             backward_unrenorm_chosen_only),
+                                            [BP.test_backward_unrenormalised_matches_torch_autograd]),
     "sigmoid_not_silu": (lambda mp: patch(mp, "silu", sigmoid_not_silu),
                          [P.test_hand_worked_block_closed_form, P.test_single_expert_reduces_to_swiglu_mlp]),
     "gate_up_swapped": (swap_gate_up,
