@@ -260,9 +260,13 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
  * `workspace` and stream with no other use of the workspace in between: it
  * reads that call's routing arrays, per-slot y and pre-activations (and
  * overwrites y and the pre-activations).  Supported: tiled bf16 weights
- * (MOE_W_BF16_TILED), renormalised top-k weights, and the decode kernels'
- * sizes (T * top_k < 32 * n_experts); else MOE_ERR_UNSUPPORTED (cfg->train
- * = 0 too).  Sums run in a fixed order, no float atomics, so the result is
+ * (MOE_W_BF16_TILED) and the decode kernels' sizes (T * top_k < 32 *
+ * n_experts); else MOE_ERR_UNSUPPORTED (cfg->train = 0 too).  With top-k
+ * weights without renormalisation (MOE_TOPK_SOFTMAX) the logit gradient
+ * reaches every expert, d_l[e] = [e chosen] w_e d_topk_w_e - p_e sum_j w_j
+ * d_topk_w_j with p the softmax over all E (from the router's approximate
+ * logits, within ~1e-6 of the fp32 ones), and d_x's router share runs over
+ * all E rows of w_router.  Sums run in a fixed order, no float atomics, so the result is
  * the same on every run.
  * With LoRA adapters (w->lora, the same ones the forward used) the chain
  * rule runs through W + scale * B A, and the adapters' gradients, summed

@@ -473,9 +473,9 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
                         void* workspace, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_forward_args(cfg, w, x, T, d_x, workspace, ws_bytes));
   const moe_config& c = *cfg;
-  if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED || c.topk_weights != MOE_TOPK_RENORM || mfma_path_for(c, T))
-    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports train=1 configs with tiled bf16 weights, renormalised "
-                                     "top-k weights, and T*top_k < 32*n_experts");
+  if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED || mfma_path_for(c, T))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports train=1 configs with tiled bf16 weights and "
+                                     "T*top_k < 32*n_experts");
   MOE_TRY(check_ptr(d_out, "d_out"));
   if (d_topk_w && !aligned(d_topk_w, 4)) return fail(MOE_ERR_INVALID_ARG, "d_topk_w is not 4-byte aligned");
   if (!w->lora != !d_lora)
@@ -517,6 +517,12 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.gu = at<float>(workspace, L.gu);
   b.d_xs = at<float>(workspace, L.y);  // y is read first, then its memory holds the per-slot d_x
   b.x = static_cast<const uint16_t*>(x);
+  if (c.topk_weights == MOE_TOPK_SOFTMAX) {
+    b.unrenorm = true;
+    b.r_part = at<float>(workspace, L.route);
+    b.r_nst = moe::route_stored_splits(T, c.hidden);
+    b.r_bias = w->router_bias;
+  }
   if (d_weights) {
     b.wgrad = true;
     b.g_w_gate_up = d_weights->d_w_gate_up;

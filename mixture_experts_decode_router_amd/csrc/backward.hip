@@ -38,6 +38,59 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Top-k weights without renormalisation: w_j = p[id_j], p the softmax over
+// all E logits, so the logit gradient reaches every expert,
+//   d_l[e] = [e chosen] w_e d_w_e - p_e sum_j w_j d_w_j,
+// and the router's share of d_x is sum_e d_l[e] Wr[e] over all E.  p comes
+// from the router's approximate logits (stored split partials summed in
+// split order, plus the bias), which lie within ~1e-6 of the fp32 logits.
+// Thread e < E handles expert e; sums over the workgroup run in wave order.
+__device__ void router_share_all(const BwdArgs& a, int t, float swd, const float* s_dw) {
+  __shared__ float s_dl[256];
+  __shared__ float s_r[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, H = a.H, T = a.T, k = a.k;
+  float lg = -INFINITY;
+  if (tid < E) {
+    float sum = 0.f;
+    for (int sp = 0; sp < a.r_nst; ++sp) sum += a.r_part[((size_t)sp * T + t) * E + tid];
+    lg = a.r_bias ? sum + a.r_bias[tid] : sum;
+  }
+  float m = lg;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) s_r[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_r[0], s_r[1]), fmaxf(s_r[2], s_r[3]));
+  __syncthreads();  // s_r is reused
+  const float ex = tid < E ? __expf(lg - m) : 0.f;
+  const float ws = wave_sum(ex);
+  if (lane == 0) s_r[wave] = ws;
+  __syncthreads();
+  const float z = ((s_r[0] + s_r[1]) + s_r[2]) + s_r[3];
+  if (tid < E) {
+    float dl = -(ex / z) * swd;
+    for (int j = 0; j < k; ++j)
+      if (a.ids[(size_t)t * k + j] == tid) dl = fmaf(a.wts[(size_t)t * k + j], s_dw[j], dl);
+    s_dl[tid] = dl;
+  }
+  __syncthreads();
+  // sum_e d_l[e] Wr[e] per column chunk of 4, e in order
+  for (int c4 = tid; c4 < H / 4; c4 += 256) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int e = 0; e < E; ++e) {
+      const u32x2_t wv = *reinterpret_cast<const u32x2_t*>(a.w_router + (size_t)e * H + 4 * c4);
+      const float dl = s_dl[e];
+      acc[0] = fmaf(dl, bf16lo(wv[0]), acc[0]);
+      acc[1] = fmaf(dl, bf16hi(wv[0]), acc[1]);
+      acc[2] = fmaf(dl, bf16lo(wv[1]), acc[2]);
+      acc[3] = fmaf(dl, bf16hi(wv[1]), acc[3]);
+    }
+    *reinterpret_cast<f32x4_t*>(a.d_x + (size_t)t * H + 4 * c4) = acc;
+  }
+}
+
 // ---------------------------------------------------------------- weights
 // One 256-thread workgroup per token; thread i holds the float4 column
 // chunks i, i + 256, ... (at most 4: H <= 4096).  For each chunk the y rows
@@ -84,6 +137,10 @@ __global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
   float swd = 0.f;
   for (int j = 0; j < k; ++j) swd = fmaf(a.wts[(size_t)t * k + j], s_dw[j], swd);
   if (a.d_w && tid < k) a.d_w[(size_t)t * k + tid] = s_dw[tid];
+  if (a.unrenorm) {
+    router_share_all(a, t, swd, s_dw);
+    return;
+  }
   // the router's share: sum_j d_l_j Wr[id_j], j in order, d_l_j = w_j (d_w_j - swd)
   float dl[16];
   int ids[16];

@@ -39,6 +39,10 @@ struct RouteArgs {
 // scratch: route_scratch_floats(t_max, E, H) floats of device memory
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s);
 size_t route_scratch_floats(int t_max, int E, int H);
+// number of K-split partial logits stored per token at batch size T (the
+// scratch holds them [nst][T][E] from its start: the router's approximate
+// logits, bias not added, are their sum in split order)
+int route_stored_splits(int T, int H);
 
 struct PermuteArgs {
   const int32_t* ids;     // [N]
@@ -146,6 +150,13 @@ struct BwdArgs {
   float* g_b_gate_up;
   float* g_a_down;
   float* g_b_down;
+  // top-k weights without renormalisation (unrenorm true): the router's
+  // stored split partial logits [r_nst][T][E] and bias (or null), for the
+  // softmax over all E experts
+  bool unrenorm;
+  const float* r_part;
+  int r_nst;
+  const float* r_bias;
   // expert-weight gradients (wgrad true): fp32, the weights' row-major shapes
   bool wgrad;
   float* g_w_gate_up;         // [E][2I][H]

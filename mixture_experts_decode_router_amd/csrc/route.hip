@@ -574,6 +574,17 @@ int route_splits(int H) {
 
 size_t route_scratch_floats(int t_max, int E, int H) { return 2 * (size_t)route_splits(H) * t_max * E; }
 
+// Small T: one workgroup per (16 tokens, K split), so the router weights
+// are read by many CUs at once, and every split's partial is stored.  Large
+// T: the token tiles alone fill the chip, so a workgroup sums all splits
+// itself and stores finished sums (1 or all ks per workgroup: any other
+// grouping would add the split sums in another association and change the
+// bits).
+int route_stored_splits(int T, int H) {
+  const int ntt = (T + kTok - 1) / kTok;
+  return ntt >= 128 ? 1 : route_splits(H);
+}
+
 template <int NT, bool PN>
 void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
   const int klen = pp.H / pp.ks;
@@ -593,14 +604,9 @@ void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
 
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s) {
   const int ks = route_splits(a.H);
-  // Small T: one workgroup per (16 tokens, K split), so the router weights
-  // are read by many CUs at once.  Large T: the token tiles alone fill the
-  // chip, so a workgroup sums all splits itself and stores finished sums.
   const int ntt = (a.T + kTok - 1) / kTok;
-  // (1 or all ks: any other grouping would add the split sums in another
-  // association and change the bits)
-  const int per_wg = ntt >= 128 ? ks : 1;
-  const int nst = ks / per_wg;  // stored partials per token
+  const int nst = route_stored_splits(a.T, a.H);  // stored partials per token
+  const int per_wg = ks / nst;
   PartParams pp{a.x, a.wr, a.T, a.H, a.E, ks, per_wg, scratch, scratch + (size_t)nst * a.T * a.E};
   if (a.pn) {
     pp.res = a.pn->res;

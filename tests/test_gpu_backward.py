@@ -68,7 +68,7 @@ def test_backward_refuses_unsupported_configurations():
     x = torch.zeros(8, inp.H, dtype=torch.int16, device="cuda")
     g = torch.zeros(8, inp.H, dtype=torch.float32, device="cuda")
     for lay in (layer("q64", 64), layer("q64", 64, tiled=False).with_options(train=True),
-                layer("q64", 64).with_options(renorm=False, train=True), layer("q48q", 64).with_options(train=True)):
+                layer("q48q", 64).with_options(train=True)):
         lay.forward(x)
         with pytest.raises(L.MoEError) as ei:
             lay.backward(x, g)
@@ -234,3 +234,23 @@ def test_backward_weight_grads_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     assert torch.equal(outs[0][2][0], outs[1][2][0]) and torch.equal(outs[0][2][1], outs[1][2][1])
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 8), ("tiny", 33), ("q8", None), ("q64", 24)])
+def test_backward_unrenormalised_matches_oracle(name, T):
+    """Top-k weights without renormalisation: the logit gradient reaches all
+    E experts, so d_x carries the router rows of every expert."""
+    inp = workload(name, T)
+    lay = layer(*LAYER_OF[name]).with_options(renorm=False, train=True)
+    d_out = d_out_for(inp.T, inp.H, seed=43)
+    say(f"[gpu] backward without renormalisation {name} T={inp.T}")
+    d_x, d_w = gpu_backward(lay, inp.x, d_out)
+    base = "q64" if name in ("q8", "q64") else name
+    b = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights(base), renorm=False)
+    assert np.array_equal(lay.views(inp.T)["ids"].cpu().numpy(), b["routing"]["ids"])
+    r = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights(base))
+    ex, ew = rel(d_x, b["d_x"]), rel(d_w, b["d_w"])
+    gap = rel(r["d_x"], b["d_x"])
+    say(f"[gpu]   d_x max|err|/rms {ex:.3e}, d_w {ew:.3e}; renormalised d_x differs by {gap:.3e}")
+    assert ex <= TOL_BF16 and ew <= TOL_BF16
+    assert gap > 10 * ex   # the test separates the two forms
