@@ -10,6 +10,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxK = 16;  // largest top-k the configuration check accepts
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
@@ -19,12 +20,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   if (a.live && t >= *a.live) return;  // row past the live count of a graph replay
   const float* w = a.wts + (size_t)t * a.k;
   const float* y = a.y + (size_t)t * a.k * a.H + c;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < a.k; ++j) {
-    const float wj = w[j];
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(y + (size_t)j * a.H);
+  // all k rows are loaded before the first multiply-add (one memory round
+  // trip instead of k), with the streaming hint since each is read once; the
+  // sum still runs over j ascending
+  f32x4_t v[kMaxK];
+  float wv[kMaxK];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < a.k) {
+      wv[j] = w[j];
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + (size_t)j * a.H));
+    }
+  }
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < a.k) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(wv[j], v[j][q], acc[q]);
+    }
   }
   if (BF16) {
     const u32x2_t pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};

@@ -6,7 +6,8 @@
 // rows of W_down).  A 512-thread workgroup computes the kBM x 256 output
 // tile; each of its 8 waves owns 64 tokens x (16 kNT) weight rows as kNT x 4
 // MFMA 16x16x32 tiles.  A wave whose 64 rows all lie past the item's last row
-// skips its MFMAs, so a short item costs its weight stream, not its padding.
+// skips its MFMAs, and so does a wave's 16-row token tile that lies wholly
+// past it, so a short item costs its weight stream, not its padding.
 //
 // Per 32-k stage the workgroup needs 16 weight fragments (each one contiguous
 // kilobyte of the tiled layout) and kBM/16 token fragments (16 gathered rows
@@ -43,7 +44,10 @@ namespace {
 #define MOE_MFMA_RING 3
 #endif
 constexpr int kBM = kMfmaTile;                        // token rows of an item
-constexpr int kBN = 256;                              // weight rows of a tile
+#ifndef MOE_MFMA_BN
+#define MOE_MFMA_BN 256
+#endif
+constexpr int kBN = MOE_MFMA_BN;                      // weight rows of a tile
 #ifndef MOE_MFMA_WAVES
 #define MOE_MFMA_WAVES 8
 #endif
@@ -62,7 +66,8 @@ constexpr int kLdsBytes = kRing * kStageBytes;
 constexpr int kWLoads = kWFrags / kWaves;             // weight fragment loads per wave per stage
 constexpr int kXTiles = kXFrags / kWaves;             // token fragment loads per wave per stage
 constexpr int kLoads = kWLoads + kXTiles;
-constexpr int kBlocksPerCU = 2 * kLdsBytes <= 160 * 1024 ? 2 : 1;
+constexpr int kHalfT = kWFrags / 2;                   // gate/up: gate row tiles of a weight tile
+constexpr int kBlocksPerCU = 3 * kLdsBytes <= 160 * 1024 ? 3 : (2 * kLdsBytes <= 160 * 1024 ? 2 : 1);
 static_assert((kBM == 128 || kBM == 256) && kWFrags % kWaves == 0 && kXFrags % kWaves == 0, "tile split");
 static_assert(kNT % 2 == 0 && kNT <= 8, "gate/up pairs per wave");
 static_assert(kLdsBytes <= 160 * 1024, "LDS");
@@ -125,7 +130,7 @@ template <bool GATE_UP>
 __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mfma(ExpertArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char s_raw[];
   const int H = a.H, I = a.I;
-  const int ntile = GATE_UP ? I / 128 : (H + kBN - 1) / kBN;
+  const int ntile = GATE_UP ? I / (kBN / 2) : (H + kBN - 1) / kBN;
   // the grid is sized for the longest possible work list; the real tiles are
   // the first n_items * ntile blocks, spread evenly over the XCDs
   const int nblk = *a.n_items * ntile;
@@ -154,10 +159,10 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
     const int rtl = kWLoads * wave + i;  // local row tile
     size_t rt;
     if (GATE_UP) {
-      const int rloc = rtl < 8 ? nt * 8 + rtl : I / 16 + nt * 8 + (rtl - 8);
+      const int rloc = rtl < kHalfT ? nt * kHalfT + rtl : I / 16 + nt * kHalfT + (rtl - kHalfT);
       rt = (size_t)e * (2 * I / 16) + rloc;
     } else {
-      const int rloc = min(nt * 16 + rtl, H / 16 - 1);  // rows past H: any valid tile, never stored
+      const int rloc = min(nt * kWFrags + rtl, H / 16 - 1);  // rows past H: any valid tile, never stored
       rt = (size_t)e * (H / 16) + rloc;
     }
     wsrc[i] = (GATE_UP ? a.w_gate_up : a.w_down) + ((rt * nks) * 64 + lane) * 8;
@@ -193,14 +198,15 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
   constexpr int kH = kNT / 2;
   int wrt[kNT];  // local weight row tiles of this wave (gate/up: kH gate tiles, then the matching up tiles)
 #pragma unroll
-  for (int i = 0; i < kNT; ++i) wrt[i] = GATE_UP ? (i < kH ? wn * kH + i : 8 + wn * kH + (i - kH)) : wn * kNT + i;
+  for (int i = 0; i < kNT; ++i) wrt[i] = GATE_UP ? (i < kH ? wn * kH + i : kHalfT + wn * kH + (i - kH)) : wn * kNT + i;
   f32x4_t acc[kNT][4];
 #pragma unroll
   for (int i = 0; i < kNT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // a wave whose 64 token rows all lie past the item's end has no MFMAs to do
-  const bool live = wm * 64 < M;
+  // the wave's 16-row token tiles that hold rows of the item (0..4); the
+  // MFMAs of tiles wholly past the item's end are skipped
+  const int nj = min(max((M - wm * 64 + 15) / 16, 0), 4);
 
   const int nstage = nks;  // one 32-k step per stage
   constexpr int D = kRing - 1;  // stages in flight ahead of the one multiplied
@@ -208,16 +214,22 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
   for (int st = 0; st < D; ++st)
     if (st < nstage) issue(st, st);
   // the k loop; a wave with no live rows still moves its share of every stage
-  auto k_loop = [&](auto with_mma) {
+  auto k_loop = [&](auto njc) {
+    constexpr int NJ = decltype(njc)::value;
     for (int kb = 0; kb < nstage; ++kb) {
       wait_own_loads(min(D - 1, nstage - 1 - kb), xload);  // stage kb landed (later ones may be in flight)
       stage_barrier();                              // ... for every wave; buffer (kb+D)%kRing is free
       if (kb + D < nstage) issue(kb + D, (kb + D) % kRing);
-      if constexpr (decltype(with_mma)::value) mma_step<4>(s_raw + (kb % kRing) * kStageBytes, wrt, wm, lane, acc);
+      if constexpr (NJ > 0) mma_step<NJ>(s_raw + (kb % kRing) * kStageBytes, wrt, wm, lane, acc);
     }
   };
-  if (live) k_loop(std::true_type{});
-  else k_loop(std::false_type{});
+  switch (nj) {
+    case 4: k_loop(std::integral_constant<int, 4>{}); break;
+    case 3: k_loop(std::integral_constant<int, 3>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    default: k_loop(std::integral_constant<int, 0>{}); break;
+  }
 
   // ---- epilogue: lane (r, g) holds weight rows 4g+q of tile i, token row r of token tile j
   const int r = lane & 15, g = lane >> 4;
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
           float hv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) hv[q] = silu(acc[i][j][q]) * acc[i + kH][j][q];
-          const int n = nt * 128 + (wn * kH + i) * 16 + 4 * g;
+          const int n = nt * (kBN / 2) + (wn * kH + i) * 16 + 4 * g;
           u32x2_t pk = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
           *reinterpret_cast<u32x2_t*>(a.h + (size_t)(base + trow) * I + n) = pk;
         }
@@ -273,7 +285,7 @@ hipError_t allow_lds() {
 hipError_t launch_gate_up_mfma(const ExpertArgs& a, hipStream_t s) {
   hipError_t e = allow_lds<true>();
   if (e != hipSuccess) return e;
-  const dim3 grid(a.max_items * (a.I / 128));
+  const dim3 grid(a.max_items * (a.I / (kBN / 2)));
   hipLaunchKernelGGL(expert_mfma<true>, grid, dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
