@@ -106,10 +106,10 @@ typedef struct {
  *   [gate; up] = W_gu x + scale * B_gu (A_gu x)   (before SiLU * up)
  *   y          = W_d h  + scale * B_d (A_d h)      (h: the bf16 h the down GEMM reads)
  * A x is formed in fp32 per routed row (fixed order, batch-independent),
- * the B products in fp32 in the GEMM epilogues.  Supported on the decode
- * kernels only (T * top_k < 32 * n_experts, or any row-major or 4-bit
- * format); a call that would take the MFMA prefill kernels with adapters
- * returns MOE_ERR_UNSUPPORTED.  Device arrays, fp32, 16-byte aligned:
+ * the B products in fp32 in the GEMM epilogues.  A call with adapters runs
+ * the 16-row expert kernels at every T (also where T * top_k >= 32 *
+ * n_experts would otherwise take the MFMA prefill kernels: slower there,
+ * the same per-row bits).  Device arrays, fp32, 16-byte aligned:
  *   a_gate_up [E][r][H]   b_gate_up [E][2I][r] (gate rows, then up rows)
  *   a_down    [E][r][I]   b_down    [E][H][r] */
 typedef struct {
@@ -260,9 +260,10 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
  * `workspace` and stream with no other use of the workspace in between: it
  * reads that call's routing arrays, per-slot y and pre-activations (and
  * overwrites y and the pre-activations).  Supported: tiled bf16 weights
- * (MOE_W_BF16_TILED) and the decode kernels' sizes (T * top_k < 32 *
- * n_experts); else MOE_ERR_UNSUPPORTED (cfg->train = 0 too).  With top-k
- * weights without renormalisation (MOE_TOPK_SOFTMAX) the logit gradient
+ * (MOE_W_BF16_TILED), any T (where the forward ran the MFMA prefill
+ * kernels, the backward buckets the same ids again into the 16-row work
+ * items its kernels take); else MOE_ERR_UNSUPPORTED (cfg->train = 0 too).
+ * With top-k weights without renormalisation (MOE_TOPK_SOFTMAX) the logit gradient
  * reaches every expert, d_l[e] = [e chosen] w_e d_topk_w_e - p_e sum_j w_j
  * d_topk_w_j with p the softmax over all E (from the router's approximate
  * logits, within ~1e-6 of the fp32 ones), and d_x's router share runs over

@@ -113,9 +113,11 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
 bool is_nf4(const moe_config& c) { return c.wfmt == MOE_W_NF4_B64 || c.wfmt == MOE_W_NF4_B64_TILED; }
 
 // Large groups (on average >= 32 rows per expert) go to the LDS-tiled MFMA
-// kernels (tiled bf16 weights only)
-bool mfma_path_for(const moe_config& c, int T) {
-  return c.wfmt == MOE_W_BF16_TILED && (long)T * c.top_k >= 32L * c.n_experts;
+// kernels (tiled bf16 weights only).  A call with LoRA adapters runs on the
+// 16-row kernels at every size: those carry the adapter epilogues, and give
+// the same per-row bits.
+bool mfma_path_for(const moe_config& c, int T, bool lora) {
+  return c.wfmt == MOE_W_BF16_TILED && (long)T * c.top_k >= 32L * c.n_experts && !lora;
 }
 bool is_tiled(const moe_config& c) { return c.wfmt == MOE_W_BF16_TILED || c.wfmt == MOE_W_NF4_B64_TILED; }
 
@@ -143,13 +145,6 @@ moe_status check_weights(const moe_config& c, const moe_weights* w) {
     MOE_TRY(check_ptr(l.b_down, "lora b_down"));
     if (!std::isfinite(l.scale)) return fail(MOE_ERR_INVALID_ARG, "LoRA scale is not finite");
   }
-  return MOE_OK;
-}
-
-moe_status check_lora_path(const moe_config& c, const moe_weights* w, int32_t T) {
-  if (w && w->lora && mfma_path_for(c, T))
-    return fail(MOE_ERR_UNSUPPORTED, "LoRA adapters run on the decode kernels: T*top_k must be < 32*n_experts "
-                                     "with tiled bf16 weights (T=" + std::to_string(T) + ")");
   return MOE_OK;
 }
 
@@ -210,7 +205,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   // both paths give bit-identical per-row results
-  const bool mfma_path = mfma_path_for(c, T);
+  const bool mfma_path = mfma_path_for(c, T, w.lora != nullptr);
   const int tile = mfma_path ? moe::kMfmaTile : moe::kSkinnyTile;
   moe::PermuteArgs pa{};
   pa.ids = ra.ids;
@@ -254,7 +249,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ea.codebook = w.codebook;
   const bool nf4 = is_nf4(c), tiled = is_tiled(c);
   moe::LoraAArgs la{};
-  if (w.lora) {  // validated: decode kernels only
+  if (w.lora) {  // adapters run on the 16-row kernels at every size
     ea.lora = true;
     ea.lora_scale = w.lora->scale;
     ea.lb_gate_up = w.lora->b_gate_up;
@@ -312,7 +307,6 @@ moe_status check_forward_args(const moe_config* cfg, const moe_weights* w, const
   MOE_TRY(check_ptr(x, "x"));
   MOE_TRY(check_ptr(out, "out"));
   MOE_TRY(check_ws(*cfg, ws, ws_bytes));
-  MOE_TRY(check_lora_path(*cfg, w, T));
   return MOE_OK;
 }
 
@@ -473,9 +467,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
                         void* workspace, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_forward_args(cfg, w, x, T, d_x, workspace, ws_bytes));
   const moe_config& c = *cfg;
-  if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED || mfma_path_for(c, T))
-    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports train=1 configs with tiled bf16 weights and "
-                                     "T*top_k < 32*n_experts");
+  if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports train=1 configs with tiled bf16 weights");
   MOE_TRY(check_ptr(d_out, "d_out"));
   if (d_topk_w && !aligned(d_topk_w, 4)) return fail(MOE_ERR_INVALID_ARG, "d_topk_w is not 4-byte aligned");
   if (!w->lora != !d_lora)
@@ -547,6 +540,26 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     b.g_b_down = d_lora->d_b_down;
   }
   hipError_t e;
+  if (mfma_path_for(c, T, w->lora != nullptr)) {
+    // the forward ran the MFMA kernels on a work list of 128-row items; the
+    // backward's kernels take 16-row items: bucket the same ids again (the
+    // routing arrays are rewritten with the same values)
+    moe::PermuteArgs pa{};
+    pa.ids = b.ids;
+    pa.N = N;
+    pa.E = c.n_experts;
+    pa.tile = moe::kSkinnyTile;
+    pa.group = 1;
+    pa.counts = at<int32_t>(workspace, L.counts);
+    pa.offsets = at<int32_t>(workspace, L.offsets);
+    pa.perm = at<int32_t>(workspace, L.perm);
+    pa.pos = at<int32_t>(workspace, L.pos);
+    pa.items = at<int32_t>(workspace, L.items);
+    pa.n_items = at<int32_t>(workspace, L.n_items);
+    pa.chunk_base = at<int32_t>(workspace, L.chunks);
+    pa.k = c.top_k;
+    if ((e = moe::launch_permute(pa, stream)) != hipSuccess) return hip_fail(e, "permute launch");
+  }
   // the down-adapter and down-weight gradients read g, u, so they come
   // before the down pass turns those into d_g, d_u; the gate/up ones after it
   if ((e = moe::launch_bwd_weights(b, stream)) != hipSuccess) return hip_fail(e, "backward weights launch");
@@ -671,7 +684,6 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
     if (buckets[i] < 1 || buckets[i] > cfg->t_max || (i && buckets[i] <= buckets[i - 1]))
       return fail(MOE_ERR_INVALID_ARG, "buckets must be strictly ascending within [1, t_max]");
   }
-  for (int i = 0; i < n_buckets; ++i) MOE_TRY(check_lora_path(*cfg, w, buckets[i]));
   moe::PrenormArgs pa{};
   if (pn) MOE_TRY(check_prenorm(*cfg, pn, buckets[n_buckets - 1], &pa));
   if (!stream) return fail(MOE_ERR_NOT_CAPTURABLE, "capture needs a created stream, not the NULL stream");

@@ -30,7 +30,8 @@
 // whichever kernel computes it: a token's output does not depend on the batch
 // size that selected the kernel.
 //
-//   gate/up:  h[p][n] = silu(gate) * up -> bf16 (sorted-slot order)
+//   gate/up:  h[p][n] = silu(gate) * up -> bf16 (sorted-slot order); a
+//             training forward also keeps gate and up (fp32) for the backward
 //   down:     y[perm[p]][c] (fp32, flat-slot order)
 #include <type_traits>
 
@@ -244,6 +245,11 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
 #pragma unroll
           for (int q = 0; q < 4; ++q) hv[q] = silu(acc[i][j][q]) * acc[i + kH][j][q];
           const int n = nt * (kBN / 2) + (wn * kH + i) * 16 + 4 * g;
+          if (a.gu) {  // training forward: keep the pre-activations the nonlinearity sees
+            float* gp = a.gu + (size_t)(base + trow) * 2 * I + n;
+            *reinterpret_cast<f32x4_t*>(gp) = acc[i][j];
+            *reinterpret_cast<f32x4_t*>(gp + I) = acc[i + kH][j];
+          }
           u32x2_t pk = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
           *reinterpret_cast<u32x2_t*>(a.h + (size_t)(base + trow) * I + n) = pk;
         }

@@ -90,7 +90,7 @@ struct ExpertArgs {
   const float* lb_down;       // fp32 [E][H][16]
   const float* u_gate_up;     // fp32 [N][16], sorted-slot order
   const float* u_down;        // fp32 [N][16], sorted-slot order
-  float* gu;                  // or null; else the skinny bf16 gate/up also keeps g and u here:
+  float* gu;                  // or null; else the bf16 gate/up kernels also keep g and u here:
                               // fp32 [N][2I] (g, then u), sorted-slot order
 };
 

@@ -255,10 +255,6 @@ def test_lora_validation_on_host():
     assert st(a_down=None) == L.MOE_ERR_INVALID_ARG
     assert st(b_gate_up=FAKE + 4) == L.MOE_ERR_INVALID_ARG
     assert st(scale=float("nan")) == L.MOE_ERR_INVALID_ARG
-    # T*k >= 32E with tiled bf16 weights takes the MFMA prefill kernels: no adapters there
-    big = cfg(t_max=4096, wfmt=L.MOE_W_BF16_TILED)
-    assert st(c=big, T=512) == L.MOE_ERR_UNSUPPORTED
-    assert "LoRA" in L.moe_last_error()
 
 
 def test_backward_validation_on_host():
@@ -275,7 +271,6 @@ def test_backward_validation_on_host():
     assert st(cfg(**tiled)) == L.MOE_ERR_UNSUPPORTED                     # not a training config
     assert "train" in L.moe_last_error()
     assert st(cfg(train=1)) == L.MOE_ERR_UNSUPPORTED                     # row-major weights
-    assert st(cfg(train=1, t_max=4096, **tiled), T=512) == L.MOE_ERR_UNSUPPORTED   # MFMA sizes
     # a training config has room for the pre-activations and the two rank-16 z rows per slot
     assert (L.moe_workspace_size(cfg(train=1, **tiled))
             == L.moe_workspace_size(cfg(**tiled)) + 64 * 8 * 2 * 768 * 4 + 2 * 64 * 8 * 16 * 4)

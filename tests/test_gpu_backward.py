@@ -75,6 +75,42 @@ def test_backward_refuses_unsupported_configurations():
         assert ei.value.status == L.MOE_ERR_UNSUPPORTED
 
 
+def test_backward_at_prefill_sizes():
+    # T*k = 32*E: the training forward runs the MFMA prefill kernels, which
+    # also keep g, u (outputs the same bits as an inference forward); the
+    # backward re-buckets into 16-row items and matches the oracle's chain
+    # rule, its rows the same bits as a decode-sized call's; with LoRA
+    # adapters the 16-row kernels run throughout
+    inp = workload("tiny", 256)
+    d_out = d_out_for(inp.T, inp.H, seed=29)
+    inf = layer("tiny", 256)
+    lay = inf.with_options(train=True)
+    x = inf.upload_x(inp.x)
+    a = inf.forward(x)
+    b = lay.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    say(f"[gpu] backward tiny at prefill size T={inp.T}")
+    d_x, d_w = gpu_backward(lay, inp.x, d_out)
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights("tiny"))
+    assert np.array_equal(lay.views(inp.T)["ids"].cpu().numpy(), ref["routing"]["ids"])
+    ex, ew = rel(d_x, ref["d_x"]), rel(d_w, ref["d_w"])
+    say(f"[gpu]   d_x max|err|/rms {ex:.3e}, d_w max|err|/rms {ew:.3e}")
+    assert ex <= TOL_BF16 and ew <= TOL_BF16
+    s_x, s_w = gpu_backward(lay, inp.x[:24], d_out[:24])
+    assert np.array_equal(s_x, d_x[:24]) and np.array_equal(s_w, d_w[:24])
+    d = S.lora_adapters(inp.E, inp.H, inp.I)
+    ll = lay.with_lora(d)
+    d_x, d_w, g = gpu_backward_lora(ll, inp.x, d_out)
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights("tiny"), lora=O.LoRA(**d))
+    errs = {"d_x": rel(d_x, ref["d_x"]), "d_w": rel(d_w, ref["d_w"])}
+    for n in LORA_NAMES:
+        errs[n] = rel(g[n], ref["d_" + n])
+    say("[gpu]   with LoRA max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_BF16 and errs["d_w"] <= TOL_BF16
+    assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
+
+
 def test_training_forward_gives_the_same_output():
     inp = workload("q64", 64)
     base = layer("q64", 64)

@@ -1,7 +1,7 @@
 """LoRA adapters fused into the decode expert GEMMs, against the fp64 oracle
 with the same adapters: routing bit-exact, outputs within the bf16 / 4-bit
 tolerances; zero B gives the base block's bits; graph replays equal eager;
-the MFMA prefill sizes are refused."""
+at prefill sizes the adapters run on the 16-row kernels."""
 import numpy as np
 import pytest
 import torch
@@ -93,13 +93,27 @@ def test_lora_graph_replay_equals_eager():
         lay.release_graph()
 
 
-def test_lora_refused_on_prefill_kernels():
-    inp = workload("q4096")
-    lay = layer("q4096", 4096).with_lora(adapters(inp))
-    with pytest.raises(L.MoEError) as ei:
-        lay.forward(lay.upload_x(inp.x))
-    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
-    # decode sizes on the same layer are fine
-    out = lay.forward(lay.upload_x(inp.x[:64]))
+def test_lora_at_prefill_sizes():
+    # T*k = 32*E: without adapters the MFMA prefill kernels run; with them
+    # the 16-row kernels at this size, against the oracle, and zero B gives
+    # the MFMA kernels' bits
+    inp = workload("tiny", 256)
+    d = adapters(inp)
+    base = layer("tiny", 256)
+    say(f"[gpu] LoRA forward tiny at prefill size T={inp.T}")
+    lay = base.with_lora(d)
+    out = lay.forward(lay.upload_x(inp.x))
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
+    ref_out, ref = O.forward_batched(inp, oracle_weights("tiny"), lora=O.LoRA(**d))
+    check_views(lay.views(inp.T), ref)
+    err = rel_err(out.cpu().numpy(), ref_out)
+    say(f"[gpu]   max|err|/rms = {err:.3e}")
+    assert err <= TOL_BF16
+    d0 = adapters(inp)
+    d0["b_gate_up"][:] = 0
+    d0["b_down"][:] = 0
+    x = base.upload_x(inp.x)
+    a = base.forward(x)
+    b = base.with_lora(d0).forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
