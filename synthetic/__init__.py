@@ -67,7 +67,11 @@ def nf4_codebook() -> np.ndarray:
     Eight positive levels are N(0,1) quantiles at evenly spaced probabilities
     from 1/2 (excluded) up to delta = 1 - 1/32, scaled so the largest is +1;
     seven negative levels are built the same way and scaled so the smallest is
-    -1; plus an exact zero.  Returned ascending as fp32, so code 7 is 0.0.
+    -1; plus an exact zero.  Each level is rounded to the nearest bf16 value
+    (ties to even), the operand type the kernels multiply codebook entries
+    in, so that a dequantised weight codebook[code] * absmax is one and the
+    same fp32 product wherever it is formed.  Returned ascending as fp32, so
+    code 7 is 0.0.
     """
     nd = statistics.NormalDist()
     delta = 1.0 - 1.0 / 32.0
@@ -76,7 +80,7 @@ def nf4_codebook() -> np.ndarray:
     pos = np.asarray(pos) / max(pos)
     neg = -np.asarray(neg) / max(neg)
     cb = np.sort(np.concatenate([neg, [0.0], pos])).astype(np.float32)
-    return cb
+    return (f32_to_bf16_bits(cb).astype(np.uint32) << 16).view(np.float32)
 
 
 def quantize_nf4(w: np.ndarray, codebook: np.ndarray):
