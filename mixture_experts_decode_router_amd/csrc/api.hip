@@ -467,8 +467,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
                         void* workspace, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_forward_args(cfg, w, x, T, d_x, workspace, ws_bytes));
   const moe_config& c = *cfg;
-  if (c.train != 1 || c.wfmt != MOE_W_BF16_TILED)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports train=1 configs with tiled bf16 weights");
+  if (c.train != 1 || (c.wfmt != MOE_W_BF16_TILED && c.wfmt != MOE_W_NF4_B64_TILED))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward supports train=1 configs with tiled bf16 or 4-bit weights");
+  if (d_weights && c.wfmt != MOE_W_BF16_TILED)
+    return fail(MOE_ERR_UNSUPPORTED, "expert-weight gradients need bf16 weights (a 4-bit base is frozen)");
   MOE_TRY(check_ptr(d_out, "d_out"));
   if (d_topk_w && !aligned(d_topk_w, 4)) return fail(MOE_ERR_INVALID_ARG, "d_topk_w is not 4-byte aligned");
   if (!w->lora != !d_lora)
@@ -507,6 +509,14 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   b.w_router = static_cast<const uint16_t*>(w->w_router);
   b.w_gate_up = static_cast<const uint16_t*>(w->w_gate_up);
   b.w_down = static_cast<const uint16_t*>(w->w_down);
+  if (is_nf4(c)) {
+    b.nf4 = true;
+    b.q_gate_up = w->q_gate_up;
+    b.s_gate_up = w->s_gate_up;
+    b.q_down = w->q_down;
+    b.s_down = w->s_down;
+    b.codebook = w->codebook;
+  }
   b.gu = at<float>(workspace, L.gu);
   b.d_xs = at<float>(workspace, L.y);  // y is read first, then its memory holds the per-slot d_x
   b.x = static_cast<const uint16_t*>(x);

@@ -195,10 +195,18 @@ __device__ __forceinline__ int stage_off(int col) { return col * kColStride + (c
 // LoRA (LORA true): s * sum_j A[e][j][n] z[p][j] joins each output first
 // (z = B^T v from lora_bt; A = A_d for DOWN, A_gu for GATE_UP), the chain
 // rule through W + s B A.
-template <int MODE, bool LORA, bool HILO>
+// NF4: tiled 4-bit weights, W[m][n] = codebook[code] * absmax[m][n / 64].
+// The lane's 8 codes of row r, columns 8g .. 8g+7 of the strip are dword
+// (ks & 3) of its 16-byte code chunk in 128-column block ks >> 2.  The strip
+// lies in one 64-column scale block, so the absmax depends on the row m
+// only and is folded into v: the MFMA multiplies (v[p][m] * absmax[m]) by
+// the codebook entries, which are bf16 values, so the weights enter exactly
+// (as in the forward, which applies absmax to partial sums).
+template <int MODE, bool LORA, bool HILO, bool NF4 = false>
 __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   constexpr bool kHiLo = HILO && MODE == kDown;
   __shared__ __attribute__((aligned(16))) uint8_t s_frag[2][32 * kColStride + 4 * 16];
+  __shared__ float s_cb[NF4 ? 16 : 1];
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
   const int nrows = MODE == kDown ? H : 2 * I;  // m
@@ -223,6 +231,28 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   const size_t rt0 = (size_t)e * (nrows / 16);
   const int nsteps = nrows / 32;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  // NF4: byte offset of this lane's code dword in row tile rt's chunk, and
+  // the index of its row's absmax, as functions of rt
+  const int nkb = ncols / 128;
+  const uint8_t* Q = MODE == kDown ? a.q_down : a.q_gate_up;
+  const float* SC = MODE == kDown ? a.s_down : a.s_gate_up;
+  auto code_off = [&](size_t rt) { return ((rt * nkb + (ks >> 2)) * 64 + lane) * 16 + 4 * (ks & 3); };
+  // the absmax of rows m = 8g .. 8g+7 of a 32-row step (row tile 2s + (g >> 1),
+  // rows 8 (g & 1) + i) lie at floats 2i + h of the 16 from this base
+  const int sh = (ks >> 1) & 1;
+  auto scale_base = [&](size_t rt) { return (rt * nkb + (ks >> 2)) * 32 + 16 * (g & 1); };
+  if constexpr (NF4) {
+    if (lane < 16) s_cb[lane] = a.codebook[lane];
+    wave_sync_lds();
+  }
+  // 8 codes (element 2i in the low nibble of byte i) -> their 8 codebook
+  // entries as bf16 (exact)
+  auto decode8 = [&](uint32_t w) {
+    u32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(s_cb[(w >> (8 * i)) & 15u], s_cb[(w >> (8 * i + 4)) & 15u]);
+    return o;
+  };
   f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   // rows 8g + i < 16 of a 32-row step lie in fragment 0 (g < 2), the rest in
   // fragment 1: this lane reads rows 8 (g & 1) .. + 7 of columns r, 16 + r
@@ -230,18 +260,32 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   for (int s0 = 0; s0 < nsteps; s0 += kU) {
     // kU steps of loads in flight: two weight fragments and the rows' v
     u32x4_t f0[kU], f1[kU], va[kU], vl[kU];
+    uint32_t c0[NF4 ? kU : 1], c1[NF4 ? kU : 1];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int s = s0 + u;
       f0[u] = f1[u] = va[u] = vl[u] = zero;
+      if constexpr (NF4) c0[u] = c1[u] = 0u;
       if (s < nsteps) {
-        f0[u] = ld16_stream(W + (((rt0 + 2 * s) * ntile + ks) * 64 + lane) * 8);
-        f1[u] = ld16_stream(W + (((rt0 + 2 * s + 1) * ntile + ks) * 64 + lane) * 8);
+        float sm[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};  // absmax of the lane's rows m (NF4)
+        if constexpr (NF4) {
+          c0[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(Q + code_off(rt0 + 2 * s)));
+          c1[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(Q + code_off(rt0 + 2 * s + 1)));
+          const float* sp = SC + scale_base(rt0 + 2 * s + (g >> 1));
+          f32x4_t s4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s4[j] = *reinterpret_cast<const f32x4_t*>(sp + 4 * j);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sm[i] = sh ? s4[i >> 1][2 * (i & 1) + 1] : s4[i >> 1][2 * (i & 1)];
+        } else {
+          f0[u] = ld16_stream(W + (((rt0 + 2 * s) * ntile + ks) * 64 + lane) * 8);
+          f1[u] = ld16_stream(W + (((rt0 + 2 * s + 1) * ntile + ks) * 64 + lane) * 8);
+        }
         if (rv) {
           const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * s + 8 * g);
           const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * s + 8 * g + 4);
-          const float t[8] = {vs * v0[0], vs * v0[1], vs * v0[2], vs * v0[3],
-                              vs * v1[0], vs * v1[1], vs * v1[2], vs * v1[3]};
+          const float t[8] = {vs * v0[0] * sm[0], vs * v0[1] * sm[1], vs * v0[2] * sm[2], vs * v0[3] * sm[3],
+                              vs * v1[0] * sm[4], vs * v1[1] * sm[5], vs * v1[2] * sm[6], vs * v1[3] * sm[7]};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t hi = pack_bf16x2(t[2 * i], t[2 * i + 1]);
@@ -254,6 +298,10 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (s0 + u >= nsteps) break;
+      if constexpr (NF4) {
+        f0[u] = decode8(c0[u]);
+        f1[u] = decode8(c1[u]);
+      }
       wave_sync_lds();  // the previous step's reads are done
       // this lane's fragment chunk is row r of columns 8g .. 8g + 7
 #pragma unroll
@@ -439,6 +487,21 @@ hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
   const dim3 grid(a.max_items * ((down ? a.I : a.H) / 32));
+  if (a.nf4) {  // frozen 4-bit base: no weight gradients
+    if (a.wgrad) return hipErrorInvalidValue;
+    if (down) {
+      if (a.lora)
+        hipLaunchKernelGGL((bwd_t_kernel<kDown, true, true, true>), grid, dim3(64), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_t_kernel<kDown, false, false, true>), grid, dim3(64), 0, s, a);
+    } else {
+      if (a.lora)
+        hipLaunchKernelGGL((bwd_t_kernel<kGateUp, true, false, true>), grid, dim3(64), 0, s, a);
+      else
+        hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false, false, true>), grid, dim3(64), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (down) {
     if (a.lora)
       hipLaunchKernelGGL((bwd_t_kernel<kDown, true, true>), grid, dim3(64), 0, s, a);

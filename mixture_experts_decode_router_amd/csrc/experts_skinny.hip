@@ -315,6 +315,14 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
           acc[j + 2][q] += lora_dot(bg + (size_t)I * 16 + 16 * 16 * j, uu, a.lora_scale);
         }
       }
+      if (a.gu) {  // training forward: keep the pre-activations the nonlinearity sees
+        float* gp = a.gu + (size_t)(it.base + m) * 2 * I + n0 + r;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          gp[16 * j] = acc[j][q];
+          gp[I + 16 * j] = acc[j + 2][q];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float hv = silu(acc[j][q]) * acc[j + 2][q];

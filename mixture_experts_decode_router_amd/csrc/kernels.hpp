@@ -130,6 +130,13 @@ struct BwdArgs {
   const uint16_t* w_router;   // bf16 [E][H]
   const uint16_t* w_gate_up;  // tiled bf16
   const uint16_t* w_down;     // tiled bf16
+  // tiled 4-bit weights (nf4 true): codes, fp32 absmax per 64, fp32 codebook [16]
+  bool nf4;
+  const uint8_t* q_gate_up;
+  const float* s_gate_up;
+  const uint8_t* q_down;
+  const float* s_down;
+  const float* codebook;
   float* gu;                  // [N][2I]: g, u kept by the forward, then d_g, d_u
   float* d_xs;                // [N][H], flat-slot order (may reuse y's memory)
   // LoRA (lora true): the adapters, the forward's U = A x / A h, the backward's

@@ -5,7 +5,8 @@ unsupported configurations refused.  A training forward (train=1) keeps the
 gate/up pre-activations; its outputs are the same bits as a plain forward's.
 With rank-16 LoRA adapters: the chain rule through W + scale*B A and the
 four adapter gradients, against the oracle's, zero for experts no row
-reached; zero B gives the frozen-weight d_x bit for bit."""
+reached; zero B gives the frozen-weight d_x bit for bit.  With a 4-bit
+base (the GRPO setting), against the oracle on the dequantised weights."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +15,7 @@ import oracle as O
 import synthetic as S
 from mixture_experts_decode_router_amd import _lib as L
 from mixture_experts_decode_router_amd.layer import MoELayer
-from tests.gpu_util import TOL_BF16, layer, oracle_weights, say, workload
+from tests.gpu_util import TOL_BF16, TOL_NF4, layer, oracle_weights, say, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -68,11 +69,47 @@ def test_backward_refuses_unsupported_configurations():
     x = torch.zeros(8, inp.H, dtype=torch.int16, device="cuda")
     g = torch.zeros(8, inp.H, dtype=torch.float32, device="cuda")
     for lay in (layer("q64", 64), layer("q64", 64, tiled=False).with_options(train=True),
-                layer("q48q", 64).with_options(train=True)):
+                layer("q48q", 64, tiled=False).with_options(train=True)):
         lay.forward(x)
         with pytest.raises(L.MoEError) as ei:
             lay.backward(x, g)
         assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+    # a 4-bit base is frozen: no expert-weight gradients
+    lay = layer("q48q", 64).with_options(train=True)
+    lay.forward(x)
+    with pytest.raises(L.MoEError) as ei:
+        lay.backward(x, g, weight_grads=weight_grad_buffers(lay))
+    assert ei.value.status == L.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("T,with_lora", [(48, False), (48, True), (7, True)])
+def test_backward_nf4_matches_oracle(T, with_lora):
+    # the 4-bit base of the GRPO setting (rank-16 LoRA on 4-bit weights):
+    # the oracle runs on the identically dequantised weights (codebook
+    # entries are bf16 values, so the kernels multiply by them exactly and
+    # the adapter gradients meet the bf16 base's bound)
+    inp = workload("q48q", T)
+    lay = layer("q48q", 64).with_options(train=True)
+    d = S.lora_adapters(inp.E, inp.H, inp.I) if with_lora else None
+    if d is not None:
+        lay = lay.with_lora(d)
+    d_out = d_out_for(inp.T, inp.H, seed=41)
+    say(f"[gpu] backward 4-bit T={inp.T} lora={with_lora}")
+    x = lay.upload_x(inp.x)
+    out = lay.forward(x)
+    res = lay.backward(x, torch.from_numpy(d_out).cuda())
+    torch.cuda.synchronize()
+    b = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights("q48q"),
+                             lora=None if d is None else O.LoRA(**d))
+    assert np.array_equal(lay.views(inp.T)["ids"].cpu().numpy(), b["routing"]["ids"])
+    errs = {"d_x": rel(res[0].cpu().numpy(), b["d_x"]), "d_w": rel(res[1].cpu().numpy(), b["d_w"])}
+    if d is not None:
+        for n in LORA_NAMES:
+            errs[n] = rel(res[2][n].cpu().numpy(), b["d_" + n])
+    say("[gpu]   max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_NF4 and errs["d_w"] <= TOL_NF4
+    if d is not None:
+        assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
 
 
 def test_backward_at_prefill_sizes():
