@@ -428,7 +428,7 @@ def main():
     # ---------------- backward (frozen weights, the forward's routing): input
     # and routing-weight gradients, eager, HIP events around the call
     backward = None
-    if not args.no_backward and inp.wfmt == "bf16" and not args.row_major and T * k < 32 * E:
+    if not args.no_backward and not args.row_major:
         d_out = torch.randn(T, H, dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(3))
         evb = L.hip_events(2, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
         tl = lay.with_options(train=True)   # a training forward keeps the pre-activations
@@ -444,8 +444,10 @@ def main():
                 if i >= 3:
                     tb += L.hip_event_elapsed_ms(evb[0], evb[1]) * 1e3 / nb
         # bytes the backward must move: both expert matrices of every active
-        # expert again, the forward's y, d_out, d_x
-        bb = n_act * 3 * I * H * 2 + T * k * H * 4 + 2 * T * H * 4
+        # expert again (bf16, or 4-bit codes + fp32 absmax per 64), the
+        # forward's y, d_out, d_x
+        w_e = 3 * I * H * 2 if inp.wfmt == "bf16" else 3 * I * H // 2 + 3 * I * H // 64 * 4
+        bb = n_act * w_e + T * k * H * 4 + 2 * T * H * 4
         backward = {"us_per_step": round(tb, 2), "algorithmic_bytes": int(bb),
                     "hbm_frac": round(bb / (tb * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] backward (d_x, d_w): {tb:.1f} us, {backward['hbm_frac'] * 100:.1f}% of HBM peak")
@@ -469,25 +471,27 @@ def main():
                             "hbm_frac": round(bbl / (tbl * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"[bench] backward with LoRA gradients: {tbl:.1f} us, "
             f"{backward['lora']['hbm_frac'] * 100:.1f}% of HBM peak")
-        # with the expert-weight gradients (fp32, every expert's full shape)
-        wg = (torch.empty(E, 2 * I, H, dtype=torch.float32, device="cuda"),
-              torch.empty(E, H, I, dtype=torch.float32, device="cuda"))
-        tbw = 0.0
-        with torch.cuda.stream(stream):
-            for i in range(nb + 3):
-                tl.forward(x_static, T, out_static, stream=stream)
-                L.hip_event_record(evb[0], stream)
-                tl.backward(x_static, d_out, T, stream=stream, weight_grads=wg)
-                L.hip_event_record(evb[1], stream)
-                torch.cuda.synchronize()
-                if i >= 3:
-                    tbw += L.hip_event_elapsed_ms(evb[0], evb[1]) * 1e3 / nb
-        bbw = bb + E * 3 * I * H * 4
-        backward["weight_grads"] = {"us_per_step": round(tbw, 2), "algorithmic_bytes": int(bbw),
-                                    "hbm_frac": round(bbw / (tbw * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-        log(f"[bench] backward with expert-weight gradients: {tbw:.1f} us, "
-            f"{backward['weight_grads']['hbm_frac'] * 100:.1f}% of HBM peak")
-        del wg
+        # with the expert-weight gradients (fp32, every expert's full shape;
+        # bf16 weights only: a 4-bit base is frozen)
+        if inp.wfmt == "bf16":
+            wg = (torch.empty(E, 2 * I, H, dtype=torch.float32, device="cuda"),
+                  torch.empty(E, H, I, dtype=torch.float32, device="cuda"))
+            tbw = 0.0
+            with torch.cuda.stream(stream):
+                for i in range(nb + 3):
+                    tl.forward(x_static, T, out_static, stream=stream)
+                    L.hip_event_record(evb[0], stream)
+                    tl.backward(x_static, d_out, T, stream=stream, weight_grads=wg)
+                    L.hip_event_record(evb[1], stream)
+                    torch.cuda.synchronize()
+                    if i >= 3:
+                        tbw += L.hip_event_elapsed_ms(evb[0], evb[1]) * 1e3 / nb
+            bbw = bb + E * 3 * I * H * 4
+            backward["weight_grads"] = {"us_per_step": round(tbw, 2), "algorithmic_bytes": int(bbw),
+                                        "hbm_frac": round(bbw / (tbw * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            log(f"[bench] backward with expert-weight gradients: {tbw:.1f} us, "
+                f"{backward['weight_grads']['hbm_frac'] * 100:.1f}% of HBM peak")
+            del wg
         L.hip_events_destroy(evb)
 
     # ---------------- measured ceilings of this chip in the same run
