@@ -287,6 +287,13 @@ def test_backward_validation_on_host():
     assert st(tr, ww=wl, d_lora=L.moe_lora_grads(FAKE * 6, FAKE + 4, FAKE * 9, FAKE * 11)) == L.MOE_ERR_INVALID_ARG
     assert st(cfg(train=1, inter=2560, **tiled), ww=wl, d_lora=good) == L.MOE_ERR_UNSUPPORTED   # 2I > 4096
     assert "2*inter" in L.moe_last_error()
+    # a 4-bit base: tiled codes train (d_x, d_w, adapters); row-major codes
+    # and expert-weight gradients are refused before any launch
+    q = L.moe_weights(FAKE, None, None, None, FAKE * 2, FAKE * 3, FAKE * 5, FAKE * 6, FAKE * 7)
+    assert st(cfg(train=1, wfmt=L.MOE_W_NF4_B64), ww=q) == L.MOE_ERR_UNSUPPORTED
+    assert st(cfg(train=1, wfmt=L.MOE_W_NF4_B64_TILED), ww=q,
+              d_weights=L.moe_weight_grads(FAKE * 6, FAKE * 7)) == L.MOE_ERR_UNSUPPORTED
+    assert "4-bit" in L.moe_last_error()
     # expert-weight gradient arrays: both present and 16-byte aligned
     assert st(tr, d_weights=L.moe_weight_grads(None, FAKE * 6)) == L.MOE_ERR_INVALID_ARG
     assert st(tr, d_weights=L.moe_weight_grads(FAKE * 6, FAKE + 8)) == L.MOE_ERR_INVALID_ARG
