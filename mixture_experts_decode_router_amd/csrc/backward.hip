@@ -206,7 +206,7 @@ template <int MODE, bool LORA, bool HILO, bool NF4 = false>
 __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   constexpr bool kHiLo = HILO && MODE == kDown;
   __shared__ __attribute__((aligned(16))) uint8_t s_frag[2][32 * kColStride + 4 * 16];
-  __shared__ float s_cb[NF4 ? 16 : 1];
+  __shared__ uint32_t s_lut[NF4 ? 256 : 1];  // code byte -> (cb[low nibble], cb[high nibble]) as bf16
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
   const int nrows = MODE == kDown ? H : 2 * I;  // m
@@ -242,15 +242,19 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   const int sh = (ks >> 1) & 1;
   auto scale_base = [&](size_t rt) { return (rt * nkb + (ks >> 2)) * 32 + 16 * (g & 1); };
   if constexpr (NF4) {
-    if (lane < 16) s_cb[lane] = a.codebook[lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = lane + 64 * i;
+      s_lut[b] = pack_bf16x2(a.codebook[b & 15], a.codebook[b >> 4]);
+    }
     wave_sync_lds();
   }
   // 8 codes (element 2i in the low nibble of byte i) -> their 8 codebook
-  // entries as bf16 (exact)
+  // entries as bf16 pairs (exact: the entries are bf16 values)
   auto decode8 = [&](uint32_t w) {
     u32x4_t o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(s_cb[(w >> (8 * i)) & 15u], s_cb[(w >> (8 * i + 4)) & 15u]);
+    for (int i = 0; i < 4; ++i) o[i] = s_lut[(w >> (8 * i)) & 0xffu];
     return o;
   };
   f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
