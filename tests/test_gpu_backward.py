@@ -64,6 +64,31 @@ def test_backward_deterministic_and_batch_independent():
     assert np.array_equal(c[0], a[0][:13]) and np.array_equal(c[1], a[1][:13])
 
 
+def test_backward_nf4_deterministic_and_batch_independent():
+    inp = workload("q48q", 48)
+    lay = layer("q48q", 64).with_options(train=True).with_lora(S.lora_adapters(inp.E, inp.H, inp.I))
+    d_out = d_out_for(48, inp.H, seed=7)
+    a = gpu_backward_lora(lay, inp.x, d_out)
+    b = gpu_backward_lora(lay, inp.x, d_out)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert all(np.array_equal(a[2][n], b[2][n]) for n in LORA_NAMES)
+    c = gpu_backward_lora(lay, inp.x[:11], d_out[:11])
+    assert np.array_equal(c[0], a[0][:11]) and np.array_equal(c[1], a[1][:11])
+
+
+def test_backward_unrenormalised_at_prefill_sizes():
+    # top-k weights without renormalisation: the logit gradient reaches all E
+    # experts through the router's stored partials, also after an MFMA forward
+    inp = workload("tiny", 256)
+    lay = layer("tiny", 256).with_options(train=True, renorm=False)
+    d_out = d_out_for(inp.T, inp.H, seed=31)
+    d_x, d_w = gpu_backward(lay, inp.x, d_out)
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights("tiny"), renorm=False)
+    ex, ew = rel(d_x, ref["d_x"]), rel(d_w, ref["d_w"])
+    say(f"[gpu] unrenormalised backward tiny T={inp.T}: d_x {ex:.3e}, d_w {ew:.3e}")
+    assert ex <= TOL_BF16 and ew <= TOL_BF16
+
+
 def test_backward_refuses_unsupported_configurations():
     inp = workload("q64", 64)
     x = torch.zeros(8, inp.H, dtype=torch.int16, device="cuda")

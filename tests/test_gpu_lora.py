@@ -93,6 +93,30 @@ def test_lora_graph_replay_equals_eager():
         lay.release_graph()
 
 
+def test_lora_graph_replay_at_prefill_size_equals_eager():
+    inp = workload("tiny", 256)
+    lay = layer("tiny", 256).with_lora(adapters(inp))
+    stream = torch.cuda.Stream()
+    x_s = torch.zeros(256, inp.H, dtype=torch.int16, device="cuda")
+    out_s = torch.zeros(256, inp.H, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    lay.capture([16, 256], x_s, out_s, stream)
+    try:
+        for T in (256, 200, 9):
+            x = lay.upload_x(inp.x[:T])
+            for _ in range(2):
+                with torch.cuda.stream(stream):
+                    out_s.fill_(3.0)
+                    x_s[:T].copy_(x)
+                    lay.replay(T, stream)
+                    eager = lay.forward(x.clone(), stream=stream)
+                stream.synchronize()
+                assert torch.equal(out_s[:T], eager), T
+                assert bool((out_s[T:] == 3.0).all()), T
+    finally:
+        lay.release_graph()
+
+
 def test_lora_at_prefill_sizes():
     # T*k = 32*E: without adapters the MFMA prefill kernels run; with them
     # the 16-row kernels at this size, against the oracle, and zero B gives
