@@ -282,6 +282,9 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
  * adapters, since W + scale * B A has derivative 1 in W):
  *   d_W_gate_up[e] = sum [d_g; d_u] x^T,   d_W_down[e] = sum d_y h^T
  * (h = silu(g) * u in fp32 as above), zeros for an expert no row reached.
+ * Bf16 weights only: with a 4-bit base (frozen) d_weights must be NULL, else
+ * MOE_ERR_UNSUPPORTED.  With tiled 4-bit weights the transposed products run
+ * over the codes, W[m][n] = codebook[code] * absmax[m][n / 64].
  *   d_out     fp32 [T][H]
  *   d_x       fp32 [T][H] (written)
  *   d_topk_w  fp32 [T][k] (written), or NULL
