@@ -550,15 +550,18 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     b.g_b_down = d_lora->d_b_down;
   }
   hipError_t e;
+  b.row_tiles = 1;
   if (mfma_path_for(c, T, w->lora != nullptr)) {
     // the forward ran the MFMA kernels on a work list of 128-row items; the
-    // backward's kernels take 16-row items: bucket the same ids again (the
-    // routing arrays are rewritten with the same values)
+    // backward's transposed GEMVs take items of kBwdRowTiles 16-row tiles:
+    // bucket the same ids again (the routing arrays are rewritten with the
+    // same values)
+    b.row_tiles = moe::kBwdRowTiles;
     moe::PermuteArgs pa{};
     pa.ids = b.ids;
     pa.N = N;
     pa.E = c.n_experts;
-    pa.tile = moe::kSkinnyTile;
+    pa.tile = moe::kSkinnyTile * moe::kBwdRowTiles;
     pa.group = 1;
     pa.counts = at<int32_t>(workspace, L.counts);
     pa.offsets = at<int32_t>(workspace, L.offsets);

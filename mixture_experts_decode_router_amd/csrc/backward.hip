@@ -202,9 +202,14 @@ __device__ __forceinline__ int stage_off(int col) { return col * kColStride + (c
 // only and is folded into v: the MFMA multiplies (v[p][m] * absmax[m]) by
 // the codebook entries, which are bf16 values, so the weights enter exactly
 // (as in the forward, which applies absmax to partial sums).
-template <int MODE, bool LORA, bool HILO, bool NF4 = false>
+// RT: 16-row tiles per work item (RT > 1 after an MFMA forward, whose rows
+// are re-bucketed into items of 16 RT rows): each staged weight fragment
+// then serves RT MFMAs, so the weights are streamed once per 16 RT rows.
+template <int MODE, bool LORA, bool HILO, bool NF4 = false, int RT = 1>
 __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
+  static_assert(RT == 1 || (!LORA && !NF4), "adapters and 4-bit bases take 16-row items");
   constexpr bool kHiLo = HILO && MODE == kDown;
+  constexpr int kUr = RT == 1 ? kU : (kU / RT > 1 ? kU / RT : 1);  // steps of loads in flight
   __shared__ __attribute__((aligned(16))) uint8_t s_frag[2][32 * kColStride + 4 * 16];
   __shared__ uint32_t s_lut[NF4 ? 256 : 1];  // code byte -> (cb[low nibble], cb[high nibble]) as bf16
   const int I = a.I, H = a.H;
@@ -215,17 +220,23 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   if (item >= *a.n_items) return;
   const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
   const int c = a.counts[e] - m0;
-  const int M = c < 16 ? c : 16, base = a.offsets[e] + m0;
+  const int M = c < 16 * RT ? c : 16 * RT, base = a.offsets[e] + m0;
   const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
-  const bool rv = r < M;
-  const float* vrow;
-  float vs = 1.f;
-  if (MODE == kDown) {
-    const int slot = rv ? a.perm[base + r] : 0;
-    vrow = a.d_out + (size_t)(slot / a.k) * H;
-    vs = rv ? a.wts[slot] : 0.f;
-  } else {
-    vrow = a.gu + (size_t)(rv ? base + r : 0) * 2 * I;
+  bool rv[RT];
+  const float* vrow[RT];
+  float vs[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = 16 * rt + r;
+    rv[rt] = row < M;
+    vs[rt] = 1.f;
+    if (MODE == kDown) {
+      const int slot = rv[rt] ? a.perm[base + row] : 0;
+      vrow[rt] = a.d_out + (size_t)(slot / a.k) * H;
+      vs[rt] = rv[rt] ? a.wts[slot] : 0.f;
+    } else {
+      vrow[rt] = a.gu + (size_t)(rv[rt] ? base + row : 0) * 2 * I;
+    }
   }
   const uint16_t* W = MODE == kDown ? a.w_down : a.w_gate_up;
   const size_t rt0 = (size_t)e * (nrows / 16);
@@ -257,18 +268,22 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
     for (int i = 0; i < 4; ++i) o[i] = s_lut[(w >> (8 * i)) & 0xffu];
     return o;
   };
-  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4_t acc[RT][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) acc[rt][0] = acc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // rows 8g + i < 16 of a 32-row step lie in fragment 0 (g < 2), the rest in
   // fragment 1: this lane reads rows 8 (g & 1) .. + 7 of columns r, 16 + r
   const uint8_t* fr = s_frag[g >> 1] + 16 * (g & 1);
-  for (int s0 = 0; s0 < nsteps; s0 += kU) {
-    // kU steps of loads in flight: two weight fragments and the rows' v
-    u32x4_t f0[kU], f1[kU], va[kU], vl[kU];
-    uint32_t c0[NF4 ? kU : 1], c1[NF4 ? kU : 1];
+  for (int s0 = 0; s0 < nsteps; s0 += kUr) {
+    // kUr steps of loads in flight: two weight fragments and the rows' v
+    u32x4_t f0[kUr], f1[kUr], va[kUr][RT], vl[kUr][RT];
+    uint32_t c0[NF4 ? kUr : 1], c1[NF4 ? kUr : 1];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
+    for (int u = 0; u < kUr; ++u) {
       const int s = s0 + u;
-      f0[u] = f1[u] = va[u] = vl[u] = zero;
+      f0[u] = f1[u] = zero;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) va[u][rt] = vl[u][rt] = zero;
       if constexpr (NF4) c0[u] = c1[u] = 0u;
       if (s < nsteps) {
         float sm[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};  // absmax of the lane's rows m (NF4)
@@ -285,22 +300,27 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
           f0[u] = ld16_stream(W + (((rt0 + 2 * s) * ntile + ks) * 64 + lane) * 8);
           f1[u] = ld16_stream(W + (((rt0 + 2 * s + 1) * ntile + ks) * 64 + lane) * 8);
         }
-        if (rv) {
-          const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * s + 8 * g);
-          const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * s + 8 * g + 4);
-          const float t[8] = {vs * v0[0] * sm[0], vs * v0[1] * sm[1], vs * v0[2] * sm[2], vs * v0[3] * sm[3],
-                              vs * v1[0] * sm[4], vs * v1[1] * sm[5], vs * v1[2] * sm[6], vs * v1[3] * sm[7]};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t hi = pack_bf16x2(t[2 * i], t[2 * i + 1]);
-            va[u][i] = hi;
-            if constexpr (kHiLo) vl[u][i] = pack_bf16x2(t[2 * i] - bf16lo(hi), t[2 * i + 1] - bf16hi(hi));
+        for (int rt = 0; rt < RT; ++rt) {
+          if (rv[rt]) {
+            const float* vr = vrow[rt];
+            const float w = vs[rt];
+            const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vr + 32 * s + 8 * g);
+            const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vr + 32 * s + 8 * g + 4);
+            const float t[8] = {w * v0[0] * sm[0], w * v0[1] * sm[1], w * v0[2] * sm[2], w * v0[3] * sm[3],
+                                w * v1[0] * sm[4], w * v1[1] * sm[5], w * v1[2] * sm[6], w * v1[3] * sm[7]};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t hi = pack_bf16x2(t[2 * i], t[2 * i + 1]);
+              va[u][rt][i] = hi;
+              if constexpr (kHiLo) vl[u][rt][i] = pack_bf16x2(t[2 * i] - bf16lo(hi), t[2 * i + 1] - bf16hi(hi));
+            }
           }
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
+    for (int u = 0; u < kUr; ++u) {
       if (s0 + u >= nsteps) break;
       if constexpr (NF4) {
         f0[u] = decode8(c0[u]);
@@ -319,8 +339,11 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 #pragma unroll
       for (int nh = 0; nh < 2; ++nh) {
         const u32x4_t b = *reinterpret_cast<const u32x4_t*>(fr + stage_off(16 * nh + r));
-        acc[nh] = mfma16(va[u], b, acc[nh]);
-        if constexpr (kHiLo) acc[nh] = mfma16(vl[u], b, acc[nh]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          acc[rt][nh] = mfma16(va[u][rt], b, acc[rt][nh]);
+          if constexpr (kHiLo) acc[rt][nh] = mfma16(vl[u][rt], b, acc[rt][nh]);
+        }
       }
     }
   }
@@ -346,26 +369,29 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
         float d = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) d = fmaf(av[nh][j], z[j >> 2][j & 3], d);
-        acc[nh][q] += a.lora_scale * d;
+        acc[0][nh][q] += a.lora_scale * d;
       }
     }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int m = 4 * g + q;
-    if (m >= M) continue;
+  for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-    for (int nh = 0; nh < 2; ++nh) {
-      const int n = 32 * ks + 16 * nh + r;
-      if (MODE == kDown) {
-        float* gp = a.gu + (size_t)(base + m) * 2 * I;
-        const float gv = gp[n], uv = gp[I + n];
-        const float sg = 1.0f / (1.0f + __expf(-gv));
-        const float dh = acc[nh][q];
-        gp[n] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
-        gp[I + n] = dh * (gv * sg);
-      } else {
-        a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[nh][q];
+    for (int q = 0; q < 4; ++q) {
+      const int m = 16 * rt + 4 * g + q;
+      if (m >= M) continue;
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh) {
+        const int n = 32 * ks + 16 * nh + r;
+        if (MODE == kDown) {
+          float* gp = a.gu + (size_t)(base + m) * 2 * I;
+          const float gv = gp[n], uv = gp[I + n];
+          const float sg = 1.0f / (1.0f + __expf(-gv));
+          const float dh = acc[rt][nh][q];
+          gp[n] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
+          gp[I + n] = dh * (gv * sg);
+        } else {
+          a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[rt][nh][q];
+        }
       }
     }
   }
@@ -506,6 +532,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
     }
     return hipGetLastError();
   }
+  if (a.row_tiles == kBwdRowTiles && !a.lora) {
+    constexpr int R = kBwdRowTiles;
+    if (down && a.wgrad)
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, true, false, R>), grid, dim3(64), 0, s, a);
+    else if (down)
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, false, false, R>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false, false, false, R>), grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.row_tiles != 1) return hipErrorInvalidValue;
   if (down) {
     if (a.lora)
       hipLaunchKernelGGL((bwd_t_kernel<kDown, true, true>), grid, dim3(64), 0, s, a);

@@ -8,6 +8,12 @@ namespace moe {
 // Decode/prefill token-tile height of the skinny expert kernels: one MFMA
 // column block of 16 tokens.
 constexpr int kSkinnyTile = 16;
+// 16-row tiles per work item of the backward's transposed GEMVs after an
+// MFMA forward (its rows re-bucketed into items of 16 * kBwdRowTiles rows).
+#ifndef MOE_BWD_ROW_TILES
+#define MOE_BWD_ROW_TILES 4
+#endif
+constexpr int kBwdRowTiles = MOE_BWD_ROW_TILES;
 // Token-tile height of the LDS-tiled MFMA expert kernels (large groups).
 #ifndef MOE_MFMA_TILE
 #define MOE_MFMA_TILE 128
@@ -139,6 +145,7 @@ struct BwdArgs {
   const float* codebook;
   float* gu;                  // [N][2I]: g, u kept by the forward, then d_g, d_u
   float* d_xs;                // [N][H], flat-slot order (may reuse y's memory)
+  int row_tiles;              // 16-row tiles per work item: 1, or kBwdRowTiles (bf16, no adapters)
   // LoRA (lora true): the adapters, the forward's U = A x / A h, the backward's
   // z = B^T v, and the adapter gradients (same shapes as the adapters)
   bool lora;

@@ -161,6 +161,22 @@ def test_backward_at_prefill_sizes():
     assert ex <= TOL_BF16 and ew <= TOL_BF16
     s_x, s_w = gpu_backward(lay, inp.x[:24], d_out[:24])
     assert np.array_equal(s_x, d_x[:24]) and np.array_equal(s_w, d_w[:24])
+    # with the expert-weight gradients (the down pass with v in two parts)
+    x = lay.upload_x(inp.x)
+    lay.forward(x)
+    wg = weight_grad_buffers(lay)
+    res = lay.backward(x, torch.from_numpy(d_out).cuda(), weight_grads=wg)
+    torch.cuda.synchronize()
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights("tiny"), weight_grads=True,
+                               wgrad_experts=list(range(inp.E)))
+    errs = {"d_x": rel(res[0].cpu().numpy(), ref["d_x"])}
+    counts = lay.views(inp.T)["counts"].cpu().numpy()
+    for key, dev in (("d_w_gate_up", wg[0]), ("d_w_down", wg[1])):
+        assert all(not dev[e].any() for e in range(inp.E) if counts[e] == 0)
+        errs[key] = max(rel(dev[e].cpu().numpy(), ref[key][e]) for e in range(inp.E) if counts[e] > 0)
+    say("[gpu]   with weight gradients max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_BF16
+    assert errs["d_w_gate_up"] <= TOL_LORA_GRAD and errs["d_w_down"] <= TOL_LORA_GRAD
     d = S.lora_adapters(inp.E, inp.H, inp.I)
     ll = lay.with_lora(d)
     d_x, d_w, g = gpu_backward_lora(ll, inp.x, d_out)
