@@ -324,7 +324,9 @@ __device__ __forceinline__ float exact_logit(const u32x4_t (&xc)[CH], const Rout
   return le;
 }
 
-template <int M, int CH>  // M = ceil(E / 64) experts per lane; CH = ceil(H / 512) row chunks per lane
+// NS: the number of stored split partials when it is known at compile time
+// (their loads are then issued back to back, unpredicated), or 0 (P.ks).
+template <int M, int CH, int NS>  // M = ceil(E / 64) experts per lane; CH = ceil(H / 512) row chunks per lane
 __global__ __launch_bounds__(256) void route_select(SelParams P) {
   __shared__ float s_v[4][kMaxCand];
   __shared__ int s_e[4][kMaxCand];
@@ -340,15 +342,23 @@ __global__ __launch_bounds__(256) void route_select(SelParams P) {
   float av[M], bd[M];
   uint32_t key[M];
   // all split partials are loaded before any is added (one round trip)
-  float pl[M][kMaxSplit], ps[M][kMaxSplit];
+  constexpr int kS = NS > 0 ? NS : kMaxSplit;
+  const int nsp = NS > 0 ? NS : P.ks;
+  float pl[M][kS], ps[M][kS];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const int e = lane + 64 * m;
+    const int ec = e < E ? e : E - 1;  // lanes past E read a valid element, never used
 #pragma unroll
-    for (int ks = 0; ks < kMaxSplit; ++ks) {
-      const bool ok = e < E && ks < P.ks;
-      pl[m][ks] = ok ? P.part[((size_t)ks * T + t) * E + e] : 0.f;
-      ps[m][ks] = ok ? P.pabs[((size_t)ks * T + t) * E + e] : 0.f;
+    for (int ks = 0; ks < kS; ++ks) {
+      if (NS > 0) {
+        pl[m][ks] = P.part[((size_t)ks * T + t) * E + ec];
+        ps[m][ks] = P.pabs[((size_t)ks * T + t) * E + ec];
+      } else {
+        const bool ok = e < E && ks < nsp;
+        pl[m][ks] = ok ? P.part[((size_t)ks * T + t) * E + e] : 0.f;
+        ps[m][ks] = ok ? P.pabs[((size_t)ks * T + t) * E + e] : 0.f;
+      }
     }
   }
   if (a.live && t >= *a.live) return;  // row past the live count of a graph replay
@@ -361,8 +371,8 @@ __global__ __launch_bounds__(256) void route_select(SelParams P) {
     if (e < E) {
       float l = 0.f, s = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < kMaxSplit; ++ks) {
-        if (ks < P.ks) {
+      for (int ks = 0; ks < kS; ++ks) {
+        if (ks < nsp) {
           l += pl[m][ks];
           s += ps[m][ks];
         }
@@ -548,17 +558,29 @@ __global__ __launch_bounds__(256) void route_select(SelParams P) {
   }
 }
 
-template <int M>
-void launch_select(const SelParams& P, dim3 grid, hipStream_t s) {
+template <int M, int NS>
+void launch_select_ns(const SelParams& P, dim3 grid, hipStream_t s) {
   const int ch = (P.a.H + 511) / 512;
   if (ch <= 1)
-    hipLaunchKernelGGL((route_select<M, 1>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 1, NS>), grid, dim3(256), 0, s, P);
   else if (ch <= 2)
-    hipLaunchKernelGGL((route_select<M, 2>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 2, NS>), grid, dim3(256), 0, s, P);
   else if (ch <= 4)
-    hipLaunchKernelGGL((route_select<M, 4>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 4, NS>), grid, dim3(256), 0, s, P);
   else
-    hipLaunchKernelGGL((route_select<M, 8>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 8, NS>), grid, dim3(256), 0, s, P);
+}
+
+// the split counts of H = 2048 (8 stored at decode sizes, 1 at large T) get
+// their own kernels; any other count takes the predicated loads
+template <int M>
+void launch_select(const SelParams& P, dim3 grid, hipStream_t s) {
+  if (P.ks == 1)
+    launch_select_ns<M, 1>(P, grid, s);
+  else if (P.ks == 8)
+    launch_select_ns<M, 8>(P, grid, s);
+  else
+    launch_select_ns<M, 0>(P, grid, s);
 }
 
 }  // namespace
