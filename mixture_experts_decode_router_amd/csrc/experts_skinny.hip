@@ -80,24 +80,49 @@ __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
   const int ntile = a.I / 64;
   const int wave = blockIdx.x % kSub, bq = blockIdx.x / kSub;
   const int item = bq / ntile, nt = bq - item * ntile;
-  Item it;
-  if (!load_item(a, item, it)) return;
+  if (item >= *a.n_items) return;
   const int H = a.H, I = a.I;
   const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
   const int n0 = nt * 64 + wave * 16;
-  const bool rv = r < it.M;
-  const int tok = rv ? a.perm[it.base + r] / a.k : 0;
-  const uint16_t* xr = a.x + (size_t)tok * H + g * 8;
+  Item it;
+  it.e = a.items[2 * item];
   // row-major: row n0 + r, k offset 8g, step 32 elements; tiled: fragment
   // (row tile, k-step) is 512 elements, this lane's 8 at offset 8 * lane
   const uint16_t* wg = TILED ? a.w_gate_up + (((size_t)it.e * (2 * I / 16) + n0 / 16) * (H / 32) * 64 + lane) * 8
                              : a.w_gate_up + ((size_t)it.e * 2 * I + n0 + r) * H + g * 8;
   const uint16_t* wu = TILED ? wg + (size_t)(I / 16) * (H / 32) * 512 : wg + (size_t)I * H;
   const int wstep = TILED ? 512 : 32;  // elements per k-step
+  // the first U k-steps of weights depend on the expert only: they are in
+  // flight while the item's rows and tokens are looked up
+  u32x4_t ga0[U], ua0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    ga0[u] = ld16_stream(wg + u * wstep);
+    ua0[u] = ld16_stream(wu + u * wstep);
+  }
+  {
+    const int m0 = a.items[2 * item + 1];
+    const int c = a.counts[it.e] - m0;
+    it.M = c < kTile ? c : kTile;
+    it.base = a.offsets[it.e] + m0;
+  }
+  const bool rv = r < it.M;
+  const int tok = rv ? a.perm[it.base + r] / a.k : 0;
+  const uint16_t* xr = a.x + (size_t)tok * H + g * 8;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  for (int kk = 0; kk < H; kk += 32 * U) {
+  {
+    u32x4_t xb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) xb[u] = rv ? ld16(xr + u * 32) : zero;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      accg = mfma16(ga0[u], xb[u], accg);
+      accu = mfma16(ua0[u], xb[u], accu);
+    }
+  }
+  for (int kk = 32 * U; kk < H; kk += 32 * U) {
     u32x4_t ga[U], ua[U], xb[U];
     const size_t wo = (size_t)(kk / 32) * wstep;
 #pragma unroll
@@ -143,21 +168,45 @@ __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
   const int ctile = a.H / 128;
   const int wave = blockIdx.x % kSub, bq = blockIdx.x / kSub;
   const int item = bq / ctile, ct = bq - item * ctile;
-  Item it;
-  if (!load_item(a, item, it)) return;
+  if (item >= *a.n_items) return;
   const int H = a.H, I = a.I;
   const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
   const int c0 = ct * 128 + wave * 32;
-  const bool rv = r < it.M;
-  const uint16_t* hr = a.h + (size_t)(it.base + (rv ? r : 0)) * I + g * 8;
+  Item it;
+  it.e = a.items[2 * item];
   const uint16_t* w0 = TILED ? a.w_down + (((size_t)it.e * (H / 16) + c0 / 16) * (I / 32) * 64 + lane) * 8
                              : a.w_down + ((size_t)it.e * H + c0 + r) * I + g * 8;
   const uint16_t* w1 = TILED ? w0 + (size_t)(I / 32) * 512 : w0 + (size_t)16 * I;
   const int wstep = TILED ? 512 : 32;
+  // the first U k-steps of weights go out before the item's rows are known
+  u32x4_t a00[U], a10[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    a00[u] = ld16_stream(w0 + u * wstep);
+    a10[u] = ld16_stream(w1 + u * wstep);
+  }
+  {
+    const int m0 = a.items[2 * item + 1];
+    const int c = a.counts[it.e] - m0;
+    it.M = c < kTile ? c : kTile;
+    it.base = a.offsets[it.e] + m0;
+  }
+  const bool rv = r < it.M;
+  const uint16_t* hr = a.h + (size_t)(it.base + (rv ? r : 0)) * I + g * 8;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int kk = 0; kk < I; kk += 32 * U) {
+  {
+    u32x4_t hb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) hb[u] = rv ? ld16(hr + u * 32) : zero;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc0 = mfma16(a00[u], hb[u], acc0);
+      acc1 = mfma16(a10[u], hb[u], acc1);
+    }
+  }
+  for (int kk = 32 * U; kk < I; kk += 32 * U) {
     u32x4_t a0[U], a1[U], hb[U];
     const size_t wo = (size_t)(kk / 32) * wstep;
 #pragma unroll
