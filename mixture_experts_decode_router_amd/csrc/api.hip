@@ -201,8 +201,6 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ra.live = live;
   ra.softmax_all = c.topk_weights == MOE_TOPK_SOFTMAX;
   ra.pn = pn;
-  if ((e = moe::launch_route(ra, at<float>(ws, L.route), s)) != hipSuccess) return hip_fail(e, "route launch");
-  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   // both paths give bit-identical per-row results
   const bool mfma_path = mfma_path_for(c, T, w.lora != nullptr);
@@ -222,7 +220,12 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   pa.chunk_base = at<int32_t>(ws, L.chunks);
   pa.live = live;
   pa.k = c.top_k;
-  if ((e = moe::launch_permute(pa, s)) != hipSuccess) return hip_fail(e, "permute launch");
+  // a small batch is bucketed by the router's select workgroup
+  bool fused = false;
+  if ((e = moe::launch_route(ra, at<float>(ws, L.route), s, &pa, &fused)) != hipSuccess)
+    return hip_fail(e, "route launch");
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (!fused && (e = moe::launch_permute(pa, s)) != hipSuccess) return hip_fail(e, "permute launch");
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   moe::ExpertArgs ea{};

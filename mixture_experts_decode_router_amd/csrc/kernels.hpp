@@ -42,8 +42,12 @@ struct RouteArgs {
   bool softmax_all;       // weights = full softmax over E at the chosen (else renormalised over the k)
   const PrenormArgs* pn;  // host struct: fuse the pre-block step, or null
 };
-// scratch: route_scratch_floats(t_max, E, H) floats of device memory
-hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s);
+struct PermuteArgs;
+// scratch: route_scratch_floats(t_max, E, H) floats of device memory.
+// fuse: the bucketing to run as well when the batch is small enough for the
+// select workgroup to do it (*fused says whether it did), or null
+hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const PermuteArgs* fuse = nullptr,
+                        bool* fused = nullptr);
 size_t route_scratch_floats(int t_max, int E, int H);
 // number of K-split partial logits stored per token at batch size T (the
 // scratch holds them [nst][T][E] from its start: the router's approximate

@@ -261,6 +261,7 @@ struct SelParams {
   const float* pabs;
   int ks;
   float gamma;
+  PermuteArgs pa;  // the fused bucketing of small batches (route_select<..., true>)
 };
 
 // Butterfly sum: partners add the same two values, so every lane ends with
@@ -326,17 +327,23 @@ __device__ __forceinline__ float exact_logit(const u32x4_t (&xc)[CH], const Rout
 
 // NS: the number of stored split partials when it is known at compile time
 // (their loads are then issued back to back, unpredicated), or 0 (P.ks).
+struct SelShared {
+  float v[4][kMaxCand];
+  int e[4][kMaxCand];
+  float selv[4][kMaxK];
+  int sele[4][kMaxK];
+  __attribute__((aligned(16))) float key[4][kMaxE];
+};
+
+// one wave selects token t (t < T)
 template <int M, int CH, int NS>  // M = ceil(E / 64) experts per lane; CH = ceil(H / 512) row chunks per lane
-__global__ __launch_bounds__(256) void route_select(SelParams P) {
-  __shared__ float s_v[4][kMaxCand];
-  __shared__ int s_e[4][kMaxCand];
-  __shared__ float s_selv[4][kMaxK];
-  __shared__ int s_sele[4][kMaxK];
-  __shared__ __attribute__((aligned(16))) float s_key[4][kMaxE];
+__device__ __forceinline__ void select_token(const SelParams& P, int t, int wave, int lane, SelShared& sh) {
+  float (&s_v)[4][kMaxCand] = sh.v;
+  int (&s_e)[4][kMaxCand] = sh.e;
+  float (&s_selv)[4][kMaxK] = sh.selv;
+  int (&s_sele)[4][kMaxK] = sh.sele;
+  float (&s_key)[4][kMaxE] = sh.key;
   const RouteArgs& a = P.a;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.T) return;
   const int T = a.T, E = a.E, k = a.k;
 
   float av[M], bd[M];
@@ -558,29 +565,130 @@ __global__ __launch_bounds__(256) void route_select(SelParams P) {
   }
 }
 
-template <int M, int NS>
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Bucketing of at most 64 slots by one wave, after the selection of a batch
+// of at most four tokens in the same workgroup: the histogram, exclusive
+// scan, work list and stable permutation the bucketing kernel forms (a
+// slot's position is its expert's offset plus the number of same-expert
+// slots before it, found with eight ballots over the id bits), without a
+// launch of its own.
+__device__ void bucket_small(const PermuteArgs& pa, int lane, int* s_cnt, int* s_off) {
+  const int E = pa.E;
+  const int N = pa.live ? min(pa.N, *pa.live * pa.k) : pa.N;
+  for (int e = lane; e < kMaxE; e += 64) s_cnt[e] = 0;
+  wave_sync_lds();
+  const bool v = lane < N;
+  int e = v ? pa.ids[lane] : 0;
+  e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+  if (v) atomicAdd(&s_cnt[e], 1);
+  wave_sync_lds();
+  int c[4], tc[4], csum = 0, tsum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ee = 4 * lane + q;
+    c[q] = ee < E ? s_cnt[ee] : 0;
+    csum += c[q];
+    tc[q] = pa.tile > 0 ? (c[q] + pa.tile - 1) / pa.tile : 0;
+    tc[q] = (tc[q] + pa.group - 1) / pa.group * pa.group;
+    tsum += tc[q];
+  }
+  const int cincl = wave_incl_scan(csum, lane);
+  int run = cincl - csum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ee = 4 * lane + q;
+    if (ee < E) {
+      s_off[ee] = run;
+      pa.offsets[ee] = run;
+      pa.counts[ee] = c[q];
+    }
+    run += c[q];
+  }
+  if (lane == 63) pa.offsets[E] = cincl;
+  if (pa.items) {
+    const int tincl = wave_incl_scan(tsum, lane);
+    int trun = tincl - tsum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ee = 4 * lane + q;
+      for (int i = 0; i < tc[q]; ++i) {
+        pa.items[2 * (trun + i)] = ee;
+        pa.items[2 * (trun + i) + 1] = i * pa.tile;
+      }
+      trun += tc[q];
+    }
+    if (lane == 63) *pa.n_items = tincl;
+  }
+  wave_sync_lds();
+  uint64_t m = __ballot(v);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = v && ((e >> b) & 1);
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  const int rank = __popcll(m & ((1ull << lane) - 1ull));
+  if (v) {
+    const int p = s_off[e] + rank;
+    pa.perm[p] = lane;
+    if (pa.pos) pa.pos[lane] = p;
+  }
+}
+
+// FUSE: one workgroup holds the whole batch (T <= 4, T * k <= 64) and wave 0
+// buckets its slots once every wave has written its token's ids
+template <int M, int CH, int NS, bool FUSE>
+__global__ __launch_bounds__(256) void route_select(SelParams P) {
+  __shared__ SelShared sh;
+  __shared__ int s_cnt[FUSE ? kMaxE : 1], s_off[FUSE ? kMaxE : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t < P.a.T) select_token<M, CH, NS>(P, t, wave, lane, sh);
+  if constexpr (FUSE) {
+    __syncthreads();  // the ids of every token are written (workgroup scope)
+    if (wave == 0) bucket_small(P.pa, lane, s_cnt, s_off);
+  }
+}
+
+template <int M, int NS, bool FUSE>
 void launch_select_ns(const SelParams& P, dim3 grid, hipStream_t s) {
   const int ch = (P.a.H + 511) / 512;
   if (ch <= 1)
-    hipLaunchKernelGGL((route_select<M, 1, NS>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 1, NS, FUSE>), grid, dim3(256), 0, s, P);
   else if (ch <= 2)
-    hipLaunchKernelGGL((route_select<M, 2, NS>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 2, NS, FUSE>), grid, dim3(256), 0, s, P);
   else if (ch <= 4)
-    hipLaunchKernelGGL((route_select<M, 4, NS>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 4, NS, FUSE>), grid, dim3(256), 0, s, P);
   else
-    hipLaunchKernelGGL((route_select<M, 8, NS>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 8, NS, FUSE>), grid, dim3(256), 0, s, P);
+}
+
+template <int M, bool FUSE>
+void launch_select_f(const SelParams& P, dim3 grid, hipStream_t s) {
+  if (P.ks == 1)
+    launch_select_ns<M, 1, FUSE>(P, grid, s);
+  else if (P.ks == 8)
+    launch_select_ns<M, 8, FUSE>(P, grid, s);
+  else
+    launch_select_ns<M, 0, FUSE>(P, grid, s);
 }
 
 // the split counts of H = 2048 (8 stored at decode sizes, 1 at large T) get
 // their own kernels; any other count takes the predicated loads
 template <int M>
-void launch_select(const SelParams& P, dim3 grid, hipStream_t s) {
-  if (P.ks == 1)
-    launch_select_ns<M, 1>(P, grid, s);
-  else if (P.ks == 8)
-    launch_select_ns<M, 8>(P, grid, s);
+void launch_select(const SelParams& P, dim3 grid, bool fuse, hipStream_t s) {
+  if (fuse)
+    launch_select_f<M, true>(P, grid, s);
   else
-    launch_select_ns<M, 0>(P, grid, s);
+    launch_select_f<M, false>(P, grid, s);
 }
 
 }  // namespace
@@ -624,7 +732,7 @@ void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
     launch_partial<NT, false>(pp, grid, s);
 }
 
-hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s) {
+hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const PermuteArgs* fuse, bool* fused) {
   const int ks = route_splits(a.H);
   const int ntt = (a.T + kTok - 1) / kTok;
   const int nst = route_stored_splits(a.T, a.H);  // stored partials per token
@@ -654,14 +762,19 @@ hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s) {
   // longest fp32 addition chain: 32 inside one MFMA, one per k-step of the
   // slice, the ks split partials, plus slack; doubled.
   const int depth = 32 + (a.H / ks) / 32 + ks + 8;
-  SelParams sp{a, pp.part, pp.pabs, nst, (float)(2.0 * depth * 5.9604644775390625e-08)};
+  SelParams sp{a, pp.part, pp.pabs, nst, (float)(2.0 * depth * 5.9604644775390625e-08), PermuteArgs{}};
   const dim3 grid((a.T + 3) / 4);
+  // a batch of at most four tokens is selected by one workgroup, which then
+  // also buckets its slots (one launch fewer)
+  const bool fuse_now = fuse && a.T <= 4 && a.T * a.k <= 64;
+  if (fuse_now) sp.pa = *fuse;
+  if (fused) *fused = fuse_now;
   if (a.E <= 64)
-    launch_select<1>(sp, grid, s);
+    launch_select<1>(sp, grid, fuse_now, s);
   else if (a.E <= 128)
-    launch_select<2>(sp, grid, s);
+    launch_select<2>(sp, grid, fuse_now, s);
   else
-    launch_select<4>(sp, grid, s);
+    launch_select<4>(sp, grid, fuse_now, s);
   return hipGetLastError();
 }
 
