@@ -327,22 +327,23 @@ __device__ __forceinline__ float exact_logit(const u32x4_t (&xc)[CH], const Rout
 
 // NS: the number of stored split partials when it is known at compile time
 // (their loads are then issued back to back, unpredicated), or 0 (P.ks).
+template <int NW>  // waves (tokens) per workgroup
 struct SelShared {
-  float v[4][kMaxCand];
-  int e[4][kMaxCand];
-  float selv[4][kMaxK];
-  int sele[4][kMaxK];
-  __attribute__((aligned(16))) float key[4][kMaxE];
+  float v[NW][kMaxCand];
+  int e[NW][kMaxCand];
+  float selv[NW][kMaxK];
+  int sele[NW][kMaxK];
+  __attribute__((aligned(16))) float key[NW][kMaxE];
 };
 
 // one wave selects token t (t < T)
-template <int M, int CH, int NS>  // M = ceil(E / 64) experts per lane; CH = ceil(H / 512) row chunks per lane
-__device__ __forceinline__ void select_token(const SelParams& P, int t, int wave, int lane, SelShared& sh) {
-  float (&s_v)[4][kMaxCand] = sh.v;
-  int (&s_e)[4][kMaxCand] = sh.e;
-  float (&s_selv)[4][kMaxK] = sh.selv;
-  int (&s_sele)[4][kMaxK] = sh.sele;
-  float (&s_key)[4][kMaxE] = sh.key;
+template <int M, int CH, int NS, int NW>  // M = ceil(E / 64) experts per lane; CH = ceil(H / 512) row chunks per lane
+__device__ __forceinline__ void select_token(const SelParams& P, int t, int wave, int lane, SelShared<NW>& sh) {
+  float (&s_v)[NW][kMaxCand] = sh.v;
+  int (&s_e)[NW][kMaxCand] = sh.e;
+  float (&s_selv)[NW][kMaxK] = sh.selv;
+  int (&s_sele)[NW][kMaxK] = sh.sele;
+  float (&s_key)[NW][kMaxE] = sh.key;
   const RouteArgs& a = P.a;
   const int T = a.T, E = a.E, k = a.k;
 
@@ -574,8 +575,8 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
-// Bucketing of at most 64 slots by one wave, after the selection of a batch
-// of at most four tokens in the same workgroup: the histogram, exclusive
+// Bucketing of at most 64 slots by one wave, after the selection of a small
+// batch in the same workgroup: the histogram, exclusive
 // scan, work list and stable permutation the bucketing kernel forms (a
 // slot's position is its expert's offset plus the number of same-expert
 // slots before it, found with eight ballots over the id bits), without a
@@ -643,52 +644,57 @@ __device__ void bucket_small(const PermuteArgs& pa, int lane, int* s_cnt, int* s
   }
 }
 
-// FUSE: one workgroup holds the whole batch (T <= 4, T * k <= 64) and wave 0
-// buckets its slots once every wave has written its token's ids
-template <int M, int CH, int NS, bool FUSE>
-__global__ __launch_bounds__(256) void route_select(SelParams P) {
-  __shared__ SelShared sh;
+// NW waves (tokens) per workgroup.  FUSE: one workgroup holds the whole
+// batch (T <= NW, T * k <= 64) and wave 0 buckets its slots once every wave
+// has written its token's ids
+constexpr int kSelWaves = 4, kFuseMaxT = 8;
+template <int M, int CH, int NS, bool FUSE, int NW>
+__global__ __launch_bounds__(64 * NW) void route_select(SelParams P) {
+  __shared__ SelShared<NW> sh;
   __shared__ int s_cnt[FUSE ? kMaxE : 1], s_off[FUSE ? kMaxE : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t < P.a.T) select_token<M, CH, NS>(P, t, wave, lane, sh);
+  const int t = blockIdx.x * NW + wave;
+  if (t < P.a.T) select_token<M, CH, NS, NW>(P, t, wave, lane, sh);
   if constexpr (FUSE) {
     __syncthreads();  // the ids of every token are written (workgroup scope)
     if (wave == 0) bucket_small(P.pa, lane, s_cnt, s_off);
   }
 }
 
-template <int M, int NS, bool FUSE>
-void launch_select_ns(const SelParams& P, dim3 grid, hipStream_t s) {
+template <int M, int NS, bool FUSE, int NW>
+void launch_select_ns(const SelParams& P, hipStream_t s) {
   const int ch = (P.a.H + 511) / 512;
+  const dim3 grid((P.a.T + NW - 1) / NW), block(64 * NW);
   if (ch <= 1)
-    hipLaunchKernelGGL((route_select<M, 1, NS, FUSE>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 1, NS, FUSE, NW>), grid, block, 0, s, P);
   else if (ch <= 2)
-    hipLaunchKernelGGL((route_select<M, 2, NS, FUSE>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 2, NS, FUSE, NW>), grid, block, 0, s, P);
   else if (ch <= 4)
-    hipLaunchKernelGGL((route_select<M, 4, NS, FUSE>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 4, NS, FUSE, NW>), grid, block, 0, s, P);
   else
-    hipLaunchKernelGGL((route_select<M, 8, NS, FUSE>), grid, dim3(256), 0, s, P);
+    hipLaunchKernelGGL((route_select<M, 8, NS, FUSE, NW>), grid, block, 0, s, P);
 }
 
-template <int M, bool FUSE>
-void launch_select_f(const SelParams& P, dim3 grid, hipStream_t s) {
+template <int M, bool FUSE, int NW>
+void launch_select_f(const SelParams& P, hipStream_t s) {
   if (P.ks == 1)
-    launch_select_ns<M, 1, FUSE>(P, grid, s);
+    launch_select_ns<M, 1, FUSE, NW>(P, s);
   else if (P.ks == 8)
-    launch_select_ns<M, 8, FUSE>(P, grid, s);
+    launch_select_ns<M, 8, FUSE, NW>(P, s);
   else
-    launch_select_ns<M, 0, FUSE>(P, grid, s);
+    launch_select_ns<M, 0, FUSE, NW>(P, s);
 }
 
 // the split counts of H = 2048 (8 stored at decode sizes, 1 at large T) get
 // their own kernels; any other count takes the predicated loads
 template <int M>
-void launch_select(const SelParams& P, dim3 grid, bool fuse, hipStream_t s) {
-  if (fuse)
-    launch_select_f<M, true>(P, grid, s);
+void launch_select(const SelParams& P, bool fuse, hipStream_t s) {
+  if (fuse && P.a.T <= kSelWaves)
+    launch_select_f<M, true, kSelWaves>(P, s);
+  else if (fuse)
+    launch_select_f<M, true, kFuseMaxT>(P, s);
   else
-    launch_select_f<M, false>(P, grid, s);
+    launch_select_f<M, false, kSelWaves>(P, s);
 }
 
 }  // namespace
@@ -763,18 +769,17 @@ hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const
   // slice, the ks split partials, plus slack; doubled.
   const int depth = 32 + (a.H / ks) / 32 + ks + 8;
   SelParams sp{a, pp.part, pp.pabs, nst, (float)(2.0 * depth * 5.9604644775390625e-08), PermuteArgs{}};
-  const dim3 grid((a.T + 3) / 4);
-  // a batch of at most four tokens is selected by one workgroup, which then
-  // also buckets its slots (one launch fewer)
-  const bool fuse_now = fuse && a.T <= 4 && a.T * a.k <= 64;
+  // a batch of at most kFuseMaxT tokens is selected by one workgroup, which
+  // then also buckets its slots (one launch fewer)
+  const bool fuse_now = fuse && a.T <= kFuseMaxT && a.T * a.k <= 64;
   if (fuse_now) sp.pa = *fuse;
   if (fused) *fused = fuse_now;
   if (a.E <= 64)
-    launch_select<1>(sp, grid, fuse_now, s);
+    launch_select<1>(sp, fuse_now, s);
   else if (a.E <= 128)
-    launch_select<2>(sp, grid, fuse_now, s);
+    launch_select<2>(sp, fuse_now, s);
   else
-    launch_select<4>(sp, grid, fuse_now, s);
+    launch_select<4>(sp, fuse_now, s);
   return hipGetLastError();
 }
 

@@ -86,6 +86,7 @@ def test_forward_decode_sweep(T):
     dict(T=13, H=512, E=256, k=16, I=256, wfmt="nf4"),     # largest E and k, 4-bit
     dict(T=4, H=256, E=16, k=16, I=128, wfmt="bf16"),      # small batch bucketed by the router: 64 slots
     dict(T=3, H=512, E=256, k=8, I=128, wfmt="bf16"),      # ... with the largest expert count
+    dict(T=7, H=256, E=48, k=6, I=128, wfmt="bf16"),       # ... eight-wave select, E not a multiple of 64
 ])
 def test_forward_edge_shapes(case, tiled):
     inp = S.make_small(case["T"], case["H"], case["E"], case["k"], case["I"], seed=case["T"],
