@@ -172,11 +172,14 @@ __global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
 // (<= 16) and one 32-column tile n0 = 32 ks of W (tiled: fragment (rt, ks) is
 // W[16rt .. +16][32ks .. +32], lane (g, r) holding row r, columns 8g .. 8g+7).
 // The rows are the MFMA A operand (lane (r, g): row r, m = 8g .. 8g+7 of a
-// 32-m step).  Each fragment pair (rt = 2s, 2s+1) is staged in LDS column by
-// column (a column's 16 rows contiguous, columns 48 bytes apart plus 16 per
-// 8 columns, so neither the 2-byte writes nor the reads pile onto few banks);
-// a lane's B operand (column r or 16 + r, m = 8g .. 8g+7) is then one
-// 16-byte read.  v enters the MFMA rounded to bf16, except in the DOWN pass
+// 32-m step).  Each fragment pair (rt = 2s, 2s+1) is written to LDS row-major
+// (one 16-byte write per lane and fragment: rows m = 0..31, 32 columns, rows
+// kRowStride elements apart) and a lane's B operand (column r or 16 + r, m =
+// 8g .. 8g+7) is read back with two transposing reads (ds_read_b64_tr_b16:
+// within each 16-lane group, lane j's value q comes from the address lane
+// 4q + (j >> 2) supplies, plus j & 3 elements; so lane (r, g) supplies row
+// 8g + (r >> 2) (+ 4 for the second read), column 16 nh + 4 (r & 3)).  v
+// enters the MFMA rounded to bf16, except in the DOWN pass
 // when adapter or weight gradients are formed (HILO), where it enters as two
 // bf16 parts, hi = RNE(v) and lo = RNE(v - hi), in two MFMAs into the same
 // accumulator, so that d_h carries about 16 bits of v (the weights are exact
@@ -189,8 +192,16 @@ __global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
 //   GATE_UP: W = W_gu [2I][H], v = (d_g, d_u)[p], epilogue: d_xs[slot(p)].
 enum { kDown = 0, kGateUp = 1 };
 
-constexpr int kColStride = 48;  // bytes per staged column: 16 rows x 2 B + padding
-__device__ __forceinline__ int stage_off(int col) { return col * kColStride + (col >> 3) * 16; }
+constexpr int kRowStride = 40;  // elements per staged row: 32 columns + padding (rows stay 16-byte aligned)
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+
+// 4 bf16 of the transposing read at element offset off of the LDS array
+__device__ __forceinline__ uint2 read_tr4(const uint16_t* base, int off) {
+  const v4s_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off));
+  return uint2{(uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16),
+               (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16)};
+}
 
 // LoRA (LORA true): s * sum_j A[e][j][n] z[p][j] joins each output first
 // (z = B^T v from lora_bt; A = A_d for DOWN, A_gu for GATE_UP), the chain
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   static_assert(RT == 1 || (!LORA && !NF4), "adapters and 4-bit bases take 16-row items");
   constexpr bool kHiLo = HILO && MODE == kDown;
   constexpr int kUr = RT == 1 ? kU : (kU / RT > 1 ? kU / RT : 1);  // steps of loads in flight
-  __shared__ __attribute__((aligned(16))) uint8_t s_frag[2][32 * kColStride + 4 * 16];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[32 * kRowStride];
   __shared__ uint32_t s_lut[NF4 ? 256 : 1];  // code byte -> (cb[low nibble], cb[high nibble]) as bf16
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
@@ -271,9 +282,10 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   f32x4_t acc[RT][2];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) acc[rt][0] = acc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // rows 8g + i < 16 of a 32-row step lie in fragment 0 (g < 2), the rest in
-  // fragment 1: this lane reads rows 8 (g & 1) .. + 7 of columns r, 16 + r
-  const uint8_t* fr = s_frag[g >> 1] + 16 * (g & 1);
+  // this lane's fragment rows go to rows r and 16 + r, columns 8g .. 8g+7;
+  // its transposing reads start at row 8g + (r >> 2), column 4 (r & 3)
+  const int w_off0 = r * kRowStride + 8 * g, w_off1 = (16 + r) * kRowStride + 8 * g;
+  const int tr_off = (8 * g + (r >> 2)) * kRowStride + 4 * (r & 3);
   for (int s0 = 0; s0 < nsteps; s0 += kUr) {
     // kUr steps of loads in flight: two weight fragments and the rows' v
     u32x4_t f0[kUr], f1[kUr], va[kUr][RT], vl[kUr][RT];
@@ -327,18 +339,14 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
         f1[u] = decode8(c1[u]);
       }
       wave_sync_lds();  // the previous step's reads are done
-      // this lane's fragment chunk is row r of columns 8g .. 8g + 7
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const int off = stage_off(8 * g + e8) + 2 * r;
-        const uint32_t w0 = f0[u][e8 >> 1], w1 = f1[u][e8 >> 1];
-        *reinterpret_cast<uint16_t*>(&s_frag[0][off]) = (uint16_t)((e8 & 1) ? (w0 >> 16) : w0);
-        *reinterpret_cast<uint16_t*>(&s_frag[1][off]) = (uint16_t)((e8 & 1) ? (w1 >> 16) : w1);
-      }
+      *reinterpret_cast<u32x4_t*>(s_w + w_off0) = f0[u];
+      *reinterpret_cast<u32x4_t*>(s_w + w_off1) = f1[u];
       wave_sync_lds();
 #pragma unroll
       for (int nh = 0; nh < 2; ++nh) {
-        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(fr + stage_off(16 * nh + r));
+        const uint2 lo = read_tr4(s_w, tr_off + 16 * nh);                   // m = 8g .. 8g+3
+        const uint2 hi = read_tr4(s_w, tr_off + 4 * kRowStride + 16 * nh);  // m = 8g+4 .. 8g+7
+        const u32x4_t b = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           acc[rt][nh] = mfma16(va[u][rt], b, acc[rt][nh]);
