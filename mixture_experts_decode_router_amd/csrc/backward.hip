@@ -216,18 +216,22 @@ __device__ __forceinline__ uint2 read_tr4(const uint16_t* base, int off) {
 // RT: 16-row tiles per work item (RT > 1 after an MFMA forward, whose rows
 // are re-bucketed into items of 16 RT rows): each staged weight fragment
 // then serves RT MFMAs, so the weights are streamed once per 16 RT rows.
-template <int MODE, bool LORA, bool HILO, bool NF4 = false, int RT = 1>
+// NS: 32-column strips per work unit (NS > 1 with RT > 1): the rows' v,
+// read once per step for all NS strips, is read once per 32 NS columns.
+template <int MODE, bool LORA, bool HILO, bool NF4 = false, int RT = 1, int NS = 1>
 __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   static_assert(RT == 1 || (!LORA && !NF4), "adapters and 4-bit bases take 16-row items");
+  static_assert(NS == 1 || RT > 1, "several strips per unit go with several row tiles");
   constexpr bool kHiLo = HILO && MODE == kDown;
   constexpr int kUr = RT == 1 ? kU : (kU / RT > 1 ? kU / RT : 1);  // steps of loads in flight
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[32 * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[NS][32 * kRowStride];
   __shared__ uint32_t s_lut[NF4 ? 256 : 1];  // code byte -> (cb[low nibble], cb[high nibble]) as bf16
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
   const int nrows = MODE == kDown ? H : 2 * I;  // m
-  const int ntile = ncols / 32;
-  const int item = blockIdx.x / ntile, ks = blockIdx.x - item * ntile;
+  const int nfr = ncols / 32;                   // 32-column fragments per row tile
+  const int ntile = nfr / NS;
+  const int item = blockIdx.x / ntile, ks = (blockIdx.x - item * ntile) * NS;  // first strip
   if (item >= *a.n_items) return;
   const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
   const int c = a.counts[e] - m0;
@@ -279,21 +283,24 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
     for (int i = 0; i < 4; ++i) o[i] = s_lut[(w >> (8 * i)) & 0xffu];
     return o;
   };
-  f32x4_t acc[RT][2];
+  f32x4_t acc[RT][NS][2];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) acc[rt][0] = acc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[rt][j][0] = acc[rt][j][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // this lane's fragment rows go to rows r and 16 + r, columns 8g .. 8g+7;
   // its transposing reads start at row 8g + (r >> 2), column 4 (r & 3)
   const int w_off0 = r * kRowStride + 8 * g, w_off1 = (16 + r) * kRowStride + 8 * g;
   const int tr_off = (8 * g + (r >> 2)) * kRowStride + 4 * (r & 3);
   for (int s0 = 0; s0 < nsteps; s0 += kUr) {
     // kUr steps of loads in flight: two weight fragments and the rows' v
-    u32x4_t f0[kUr], f1[kUr], va[kUr][RT], vl[kUr][RT];
+    u32x4_t f0[kUr][NS], f1[kUr][NS], va[kUr][RT], vl[kUr][RT];
     uint32_t c0[NF4 ? kUr : 1], c1[NF4 ? kUr : 1];
 #pragma unroll
     for (int u = 0; u < kUr; ++u) {
       const int s = s0 + u;
-      f0[u] = f1[u] = zero;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) f0[u][j] = f1[u][j] = zero;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) va[u][rt] = vl[u][rt] = zero;
       if constexpr (NF4) c0[u] = c1[u] = 0u;
@@ -309,8 +316,11 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) sm[i] = sh ? s4[i >> 1][2 * (i & 1) + 1] : s4[i >> 1][2 * (i & 1)];
         } else {
-          f0[u] = ld16_stream(W + (((rt0 + 2 * s) * ntile + ks) * 64 + lane) * 8);
-          f1[u] = ld16_stream(W + (((rt0 + 2 * s + 1) * ntile + ks) * 64 + lane) * 8);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            f0[u][j] = ld16_stream(W + (((rt0 + 2 * s) * nfr + ks + j) * 64 + lane) * 8);
+            f1[u][j] = ld16_stream(W + (((rt0 + 2 * s + 1) * nfr + ks + j) * 64 + lane) * 8);
+          }
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -335,22 +345,28 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
     for (int u = 0; u < kUr; ++u) {
       if (s0 + u >= nsteps) break;
       if constexpr (NF4) {
-        f0[u] = decode8(c0[u]);
-        f1[u] = decode8(c1[u]);
+        f0[u][0] = decode8(c0[u]);
+        f1[u][0] = decode8(c1[u]);
       }
       wave_sync_lds();  // the previous step's reads are done
-      *reinterpret_cast<u32x4_t*>(s_w + w_off0) = f0[u];
-      *reinterpret_cast<u32x4_t*>(s_w + w_off1) = f1[u];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        *reinterpret_cast<u32x4_t*>(s_w[j] + w_off0) = f0[u][j];
+        *reinterpret_cast<u32x4_t*>(s_w[j] + w_off1) = f1[u][j];
+      }
       wave_sync_lds();
 #pragma unroll
-      for (int nh = 0; nh < 2; ++nh) {
-        const uint2 lo = read_tr4(s_w, tr_off + 16 * nh);                   // m = 8g .. 8g+3
-        const uint2 hi = read_tr4(s_w, tr_off + 4 * kRowStride + 16 * nh);  // m = 8g+4 .. 8g+7
-        const u32x4_t b = {lo.x, lo.y, hi.x, hi.y};
+      for (int j = 0; j < NS; ++j) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          acc[rt][nh] = mfma16(va[u][rt], b, acc[rt][nh]);
-          if constexpr (kHiLo) acc[rt][nh] = mfma16(vl[u][rt], b, acc[rt][nh]);
+        for (int nh = 0; nh < 2; ++nh) {
+          const uint2 lo = read_tr4(s_w[j], tr_off + 16 * nh);                   // m = 8g .. 8g+3
+          const uint2 hi = read_tr4(s_w[j], tr_off + 4 * kRowStride + 16 * nh);  // m = 8g+4 .. 8g+7
+          const u32x4_t b = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            acc[rt][j][nh] = mfma16(va[u][rt], b, acc[rt][j][nh]);
+            if constexpr (kHiLo) acc[rt][j][nh] = mfma16(vl[u][rt], b, acc[rt][j][nh]);
+          }
         }
       }
     }
@@ -377,7 +393,7 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
         float d = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) d = fmaf(av[nh][j], z[j >> 2][j & 3], d);
-        acc[0][nh][q] += a.lora_scale * d;
+        acc[0][0][nh][q] += a.lora_scale * d;
       }
     }
   }
@@ -388,17 +404,20 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
       const int m = 16 * rt + 4 * g + q;
       if (m >= M) continue;
 #pragma unroll
-      for (int nh = 0; nh < 2; ++nh) {
-        const int n = 32 * ks + 16 * nh + r;
-        if (MODE == kDown) {
-          float* gp = a.gu + (size_t)(base + m) * 2 * I;
-          const float gv = gp[n], uv = gp[I + n];
-          const float sg = 1.0f / (1.0f + __expf(-gv));
-          const float dh = acc[rt][nh][q];
-          gp[n] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
-          gp[I + n] = dh * (gv * sg);
-        } else {
-          a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[rt][nh][q];
+      for (int j = 0; j < NS; ++j) {
+#pragma unroll
+        for (int nh = 0; nh < 2; ++nh) {
+          const int n = 32 * (ks + j) + 16 * nh + r;
+          if (MODE == kDown) {
+            float* gp = a.gu + (size_t)(base + m) * 2 * I;
+            const float gv = gp[n], uv = gp[I + n];
+            const float sg = 1.0f / (1.0f + __expf(-gv));
+            const float dh = acc[rt][j][nh][q];
+            gp[n] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
+            gp[I + n] = dh * (gv * sg);
+          } else {
+            a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[rt][j][nh][q];
+          }
         }
       }
     }
@@ -525,6 +544,7 @@ hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
   const dim3 grid(a.max_items * ((down ? a.I : a.H) / 32));
+  const dim3 grid_ns(a.max_items * ((down ? a.I : a.H) / (32 * kBwdStrips)));
   if (a.nf4) {  // frozen 4-bit base: no weight gradients
     if (a.wgrad) return hipErrorInvalidValue;
     if (down) {
@@ -541,13 +561,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.row_tiles == kBwdRowTiles && !a.lora) {
-    constexpr int R = kBwdRowTiles;
+    constexpr int R = kBwdRowTiles, NS = kBwdStrips;
+    if ((down ? a.I : a.H) % (32 * NS)) return hipErrorInvalidValue;
     if (down && a.wgrad)
-      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, true, false, R>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, true, false, R, NS>), grid_ns, dim3(64), 0, s, a);
     else if (down)
-      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, false, false, R>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, false, false, R, NS>), grid_ns, dim3(64), 0, s, a);
     else
-      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false, false, false, R>), grid, dim3(64), 0, s, a);
+      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false, false, false, R, NS>), grid_ns, dim3(64), 0, s, a);
     return hipGetLastError();
   }
   if (a.row_tiles != 1) return hipErrorInvalidValue;

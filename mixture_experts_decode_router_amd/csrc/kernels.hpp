@@ -14,6 +14,11 @@ constexpr int kSkinnyTile = 16;
 #define MOE_BWD_ROW_TILES 4
 #endif
 constexpr int kBwdRowTiles = MOE_BWD_ROW_TILES;
+// ... and 32-column strips per work unit there (H and I are multiples of 128)
+#ifndef MOE_BWD_STRIPS
+#define MOE_BWD_STRIPS 2
+#endif
+constexpr int kBwdStrips = MOE_BWD_STRIPS;
 // Token-tile height of the LDS-tiled MFMA expert kernels (large groups).
 #ifndef MOE_MFMA_TILE
 #define MOE_MFMA_TILE 128
