@@ -583,8 +583,16 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     if ((e = moe::launch_lora_bt(b, true, stream)) != hipSuccess) return hip_fail(e, "LoRA down B^T launch");
     if ((e = moe::launch_lora_grad(b, true, stream)) != hipSuccess) return hip_fail(e, "LoRA down gradient launch");
   }
+  if (b.wgrad && c.inter <= c.hidden) {
+    // y has been read: its memory holds the fp32 h of every routed row until
+    // the gate/up pass writes the per-slot d_x there
+    float* hf = at<float>(workspace, L.y);
+    if ((e = moe::launch_h(b, hf, stream)) != hipSuccess) return hip_fail(e, "h launch");
+    b.hf = hf;
+  }
   if (b.wgrad && (e = moe::launch_wgrad(b, true, stream)) != hipSuccess)
     return hip_fail(e, "down weight gradient launch");
+  b.hf = nullptr;
   if ((e = moe::launch_bwd_t(b, true, stream)) != hipSuccess) return hip_fail(e, "backward down launch");
   if (b.lora) {
     if ((e = moe::launch_lora_bt(b, false, stream)) != hipSuccess) return hip_fail(e, "LoRA gate/up B^T launch");

@@ -438,6 +438,22 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 // write-bound: fp32 gradients the size of all experts' weights.
 constexpr int kWgRows = 64, kWgCols = 128, kWgChunk = 64, kWgU = 4, kWgTiles = 4;
 
+// h = silu(g) u in fp32 for every routed row (sorted-slot order), formed
+// once for the down weight gradient instead of once per output row block
+__global__ __launch_bounds__(256) void h_kernel(BwdArgs a, float* hf) {
+  const int I = a.I;
+  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
+  if (i4 >= (size_t)a.T * a.k * (I / 4)) return;
+  const size_t p = i4 / (I / 4);
+  const int n = (int)(i4 - p * (I / 4)) * 4;
+  const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(a.gu + p * 2 * I + n);
+  const f32x4_t uv = *reinterpret_cast<const f32x4_t*>(a.gu + p * 2 * I + I + n);
+  f32x4_t h;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) h[q] = silu(gv[q]) * uv[q];
+  *reinterpret_cast<f32x4_t*>(hf + p * I + n) = h;
+}
+
 __global__ __launch_bounds__(256) void wgrad_kernel(BwdArgs a, int part) {
   __shared__ int s_tok[kWgChunk];
   __shared__ float s_w[kWgChunk];
@@ -480,15 +496,25 @@ __global__ __launch_bounds__(256) void wgrad_kernel(BwdArgs a, int part) {
               const float* dr = a.d_out + (size_t)s_tok[j] * H + r0;
 #pragma unroll
               for (int q = 0; q < 4; ++q) av[u][q] = s_w[j] * dr[16 * q];
-              const float* gp = a.gu + p * 2 * I + c;
-              const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
-              const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gp + 4);
-              const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(gp + I);
-              const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gp + I + 4);
+              if (a.hf) {  // h formed once per routed row
+                const f32x4_t h0 = *reinterpret_cast<const f32x4_t*>(a.hf + p * I + c);
+                const f32x4_t h1 = *reinterpret_cast<const f32x4_t*>(a.hf + p * I + c + 4);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                bv[u][i] = silu(g0[i]) * u0[i];
-                bv[u][4 + i] = silu(g1[i]) * u1[i];
+                for (int i = 0; i < 4; ++i) {
+                  bv[u][i] = h0[i];
+                  bv[u][4 + i] = h1[i];
+                }
+              } else {
+                const float* gp = a.gu + p * 2 * I + c;
+                const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
+                const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gp + 4);
+                const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(gp + I);
+                const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gp + I + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  bv[u][i] = silu(g0[i]) * u0[i];
+                  bv[u][4 + i] = silu(g1[i]) * u1[i];
+                }
               }
             } else {
               const float* gr = a.gu + p * 2 * I + r0;
@@ -585,6 +611,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
     else
       hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false, false>), grid, dim3(64), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_h(const BwdArgs& a, float* hf, hipStream_t s) {
+  const size_t n4 = (size_t)a.T * a.k * (a.I / 4);
+  hipLaunchKernelGGL(h_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a, hf);
   return hipGetLastError();
 }
 

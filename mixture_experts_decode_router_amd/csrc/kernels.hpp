@@ -182,6 +182,7 @@ struct BwdArgs {
   const float* r_bias;
   // expert-weight gradients (wgrad true): fp32, the weights' row-major shapes
   bool wgrad;
+  const float* hf;            // fp32 h [N][I] (sorted-slot order) formed by launch_h, or null
   float* g_w_gate_up;         // [E][2I][H]
   float* g_w_down;            // [E][H][I]
 };
@@ -190,6 +191,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s);
 hipError_t launch_bwd_combine(const BwdArgs& a, hipStream_t s);
 // expert-weight gradients: down ones before bwd_t(down), gate/up ones after it
 hipError_t launch_wgrad(const BwdArgs& a, bool down, hipStream_t s);
+// h = silu(g) u in fp32 for every routed row, into hf (fp32 [T*k][I])
+hipError_t launch_h(const BwdArgs& a, float* hf, hipStream_t s);
 // LoRA backward: z = B^T v per routed row (down: v = w d_out, and U_d = A_d h
 // from the fp32 g, u; gate/up: v = (d_g, d_u))
 hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s);
