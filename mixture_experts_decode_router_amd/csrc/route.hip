@@ -325,8 +325,6 @@ __device__ __forceinline__ float exact_logit(const u32x4_t (&xc)[CH], const Rout
   return le;
 }
 
-// NS: the number of stored split partials when it is known at compile time
-// (their loads are then issued back to back, unpredicated), or 0 (P.ks).
 template <int NW>  // waves (tokens) per workgroup
 struct SelShared {
   float v[NW][kMaxCand];
@@ -336,7 +334,9 @@ struct SelShared {
   __attribute__((aligned(16))) float key[NW][kMaxE];
 };
 
-// one wave selects token t (t < T)
+// One wave selects token t (t < T).  NS: the number of stored split
+// partials when it is known at compile time (their loads are then issued
+// back to back, unpredicated), or 0 (P.ks).
 template <int M, int CH, int NS, int NW>  // M = ceil(E / 64) experts per lane; CH = ceil(H / 512) row chunks per lane
 __device__ __forceinline__ void select_token(const SelParams& P, int t, int wave, int lane, SelShared<NW>& sh) {
   float (&s_v)[NW][kMaxCand] = sh.v;
