@@ -246,22 +246,45 @@ __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
 // applied to MFMA partial sums: each 32-k MFMA step lies in one 64-block
 // (steps 0,1 of a 128-k block use block 2kb, steps 2,3 block 2kb+1), and
 //   D[t][row] = sum_h absmax(row, h) * sum_{k in h} x[t][k] bf16(codebook[code])
-// The per-weight work is one table read per two codes: s_lut[b] holds the
-// packed bf16 pair (codebook[b & 15], codebook[b >> 4]) of code byte b.
+// The per-weight work is one table read per two codes: entry b of the table
+// is the packed bf16 pair (codebook[b & 15], codebook[b >> 4]) of code byte
+// b.  The table is held kLutRep times over (copy c of entry b at word
+// b * kLutRep + c) and lane l reads copy l % kLutRep, so the lanes of one
+// read land in distinct LDS banks whatever bytes they look up (one shared
+// copy puts several lanes of each read in one bank: random code bytes over 64
+// lanes).
 //
 // Lane (g, r) feeds token row r and weight row r, k = 128kb + 32st + 8g + 0..7
 // for step st = 0..3 (dword st of its 16-byte chunk in the tiled layout; four
 // 4-byte loads from a row-major row), and receives D[token 4g + q][row r].
 
+#ifndef MOE_LUT_REP
+#define MOE_LUT_REP 16
+#endif
+constexpr int kLutRep = MOE_LUT_REP;  // copies of the code-pair table
+static_assert((kLutRep & (kLutRep - 1)) == 0 && kLutRep <= 64, "table copies");
+
+// thread tid < 256 writes every copy of entry tid, starting at copy
+// tid % kLutRep so that the lanes of each store fall in distinct banks
 __device__ __forceinline__ void build_lut(uint32_t* s_lut, const float* cb, int tid) {
-  if (tid < 256) s_lut[tid] = pack_bf16x2(cb[tid & 15], cb[tid >> 4]);
+  if (tid < 256) {
+    const uint32_t v = pack_bf16x2(cb[tid & 15], cb[tid >> 4]);
+#pragma unroll 8
+    for (int c = 0; c < kLutRep; ++c) s_lut[tid * kLutRep + ((c + tid) & (kLutRep - 1))] = v;
+  }
 }
 
-// 8 codes (one dword, element 2i in the low nibble of byte i) -> 8 bf16
-__device__ __forceinline__ u32x4_t lut8(const uint32_t* s_lut, uint32_t w) {
+// this lane's copy of the table
+__device__ __forceinline__ const uint32_t* lut_copy(const uint32_t* s_lut, int lane) {
+  return s_lut + (lane & (kLutRep - 1));
+}
+
+// 8 codes (one dword, element 2i in the low nibble of byte i) -> 8 bf16,
+// read from the lane's copy of the table
+__device__ __forceinline__ u32x4_t lut8(const uint32_t* s_lutl, uint32_t w) {
   u32x4_t o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = s_lut[(w >> (8 * i)) & 0xffu];
+  for (int i = 0; i < 4; ++i) o[i] = s_lutl[((w >> (8 * i)) & 0xffu) * kLutRep];
   return o;
 }
 
@@ -282,13 +305,13 @@ __device__ __forceinline__ u32x2_t load_scales(const float* s, int kb) {
 }
 
 // one 128-k block of one weight tile: acc[q] += absmax_0 * P0[q] + absmax_1 * P1[q]
-__device__ __forceinline__ f32x4_t block_mma(const uint32_t* s_lut, u32x4_t codes, const u32x4_t (&xb)[4],
+__device__ __forceinline__ f32x4_t block_mma(const uint32_t* s_lutl, u32x4_t codes, const u32x4_t (&xb)[4],
                                              u32x2_t sc, f32x4_t acc) {
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t p0 = mfma16(xb[0], lut8(s_lut, codes[0]), zero);
-  p0 = mfma16(xb[1], lut8(s_lut, codes[1]), p0);
-  f32x4_t p1 = mfma16(xb[2], lut8(s_lut, codes[2]), zero);
-  p1 = mfma16(xb[3], lut8(s_lut, codes[3]), p1);
+  f32x4_t p0 = mfma16(xb[0], lut8(s_lutl, codes[0]), zero);
+  p0 = mfma16(xb[1], lut8(s_lutl, codes[1]), p0);
+  f32x4_t p1 = mfma16(xb[2], lut8(s_lutl, codes[2]), zero);
+  p1 = mfma16(xb[3], lut8(s_lutl, codes[3]), p1);
   const float s0 = __uint_as_float(sc[0]), s1 = __uint_as_float(sc[1]);
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = fmaf(s1, p1[q], fmaf(s0, p0[q], acc[q]));
@@ -300,7 +323,7 @@ __device__ __forceinline__ f32x4_t block_mma(const uint32_t* s_lut, u32x4_t code
 // built once per 4-wave workgroup
 template <int NB, bool TILED, bool LORA>  // NB: 128-k blocks per loop iteration (H % (128 * NB) == 0)
 __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
-  __shared__ uint32_t s_lut[256];
+  __shared__ uint32_t s_lut[256 * kLutRep];
   const int ntile = a.I / 128;
   const int item = blockIdx.x / ntile, nt = blockIdx.x - item * ntile;
   Item it;
@@ -311,6 +334,7 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int n0 = nt * 128 + wave * 32;
+  const uint32_t* sl = lut_copy(s_lut, lane);
   const bool rv = r < it.M;
   const int tok = rv ? a.perm[it.base + r] / a.k : 0;
   const uint16_t* xr = a.x + (size_t)tok * H + 8 * g;
@@ -346,7 +370,7 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
 #pragma unroll
     for (int h = 0; h < NB; ++h)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = block_mma(s_lut, cd[h][j], xb[h], sc[h][j], acc[j]);
+      for (int j = 0; j < 4; ++j) acc[j] = block_mma(sl, cd[h][j], xb[h], sc[h][j], acc[j]);
   }
   // lane holds tokens 4g + q of rows n0 + 16j + r
 #pragma unroll
@@ -384,7 +408,7 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
 // down: a wave owns two 16-row tiles of W_down (32 output columns)
 template <int NB, bool TILED, bool LORA>  // NB: 128-k blocks per loop iteration (I % (128 * NB) == 0)
 __global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
-  __shared__ uint32_t s_lut[256];
+  __shared__ uint32_t s_lut[256 * kLutRep];
   const int ctile = a.H / 128;
   const int item = blockIdx.x / ctile, ct = blockIdx.x - item * ctile;
   Item it;
@@ -395,6 +419,7 @@ __global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int c0 = ct * 128 + wave * 32;
+  const uint32_t* sl = lut_copy(s_lut, lane);
   const bool rv = r < it.M;
   const uint16_t* hr = a.h + (size_t)(it.base + (rv ? r : 0)) * I + 8 * g;
   const int nkb = I / 128;
@@ -426,7 +451,7 @@ __global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
 #pragma unroll
     for (int h = 0; h < NB; ++h)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[j] = block_mma(s_lut, cd[h][j], hb[h], sc[h][j], acc[j]);
+      for (int j = 0; j < 2; ++j) acc[j] = block_mma(sl, cd[h][j], hb[h], sc[h][j], acc[j]);
   }
   // lane holds tokens 4g + q of output columns c0 + 16j + r
 #pragma unroll
@@ -458,6 +483,12 @@ hipError_t launch_u(int K, F8 f8, F4 f4, dim3 grid, hipStream_t s, const ExpertA
 
 }  // namespace
 
+// 4-bit down: a grid of at most kNf4DnSmallGrid workgroups (a few tokens)
+// takes the largest count up to 3 of 128-k blocks per loop iteration that
+// divides I / 128, which shortens each wave's chain of dependent loads; a
+// larger grid takes one block per iteration, which keeps more waves resident
+constexpr int kNf4DnSmallGrid = 1024;
+
 template <bool LORA>
 hipError_t launch_gate_up_t(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
   if (nf4) {
@@ -480,9 +511,10 @@ template <bool TILED, bool LORA>
 void launch_down_nf4(const ExpertArgs& a, hipStream_t s) {
   const dim3 grid(a.max_items * (a.H / 128));  // 128 output columns per workgroup
   const int nkb = a.I / 128;
-  if (nkb % 3 == 0)
+  const bool small = (long)grid.x <= kNf4DnSmallGrid;
+  if (small && nkb % 3 == 0)
     hipLaunchKernelGGL((down_nf4<3, TILED, LORA>), grid, dim3(kNf4Threads), 0, s, a);
-  else if (nkb % 2 == 0)
+  else if (small && nkb % 2 == 0)
     hipLaunchKernelGGL((down_nf4<2, TILED, LORA>), grid, dim3(kNf4Threads), 0, s, a);
   else
     hipLaunchKernelGGL((down_nf4<1, TILED, LORA>), grid, dim3(kNf4Threads), 0, s, a);

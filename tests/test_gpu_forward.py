@@ -71,6 +71,19 @@ def test_forward_decode_sweep(T):
     assert rel_err(out.cpu().numpy(), ref_out) <= TOL_BF16
 
 
+@pytest.mark.parametrize("T", [1, 4, 8, 16])
+def test_forward_decode_sweep_4bit(T):
+    """4-bit Qwen layer at decode sizes: the small grids of T <= 8 take the
+    down kernel's three-block iterations, T = 16 (and q48q) the one-block
+    form."""
+    inp = workload("q48q", T)
+    say(f"[gpu] forward 4-bit sweep T={T}")
+    out, views = run_forward(layer("q48q", 64), inp.x)
+    ref_out, ref = oracle_forward("q48q", T)
+    check_views(views, ref)
+    assert rel_err(out.cpu().numpy(), ref_out) <= TOL_NF4
+
+
 @pytest.mark.parametrize("tiled", [True, False])
 @pytest.mark.parametrize("case", [
     dict(T=1, H=256, E=16, k=2, I=128, wfmt="bf16"),
