@@ -93,7 +93,12 @@ typedef struct {
  * along the last axis; element 2i in the low nibble of byte i):
  *   q_gate_up  uint8 [E][2I][H/2]    s_gate_up fp32 [E][2I][H/64]
  *   q_down     uint8 [E][H][I/2]     s_down    fp32 [E][H][I/64]
- *   codebook   fp32 [16]
+ *   codebook   fp32 [16], finite normal values (or zero) of magnitude <= 1.
+ *              The kernels take each entry as two bf16 parts, hi = the
+ *              nearest bf16 and lo = the bf16 nearest to (entry - hi), which
+ *              carry it to within 2^-18 of its magnitude; an entry that is
+ *              a bf16 value enters exactly.  The absmax scales are applied
+ *              to fp32 partial sums over each 64-block.
  * The _TILED formats hold the same values in the layout moe_pack_weights
  * writes (same buffer sizes).  Unused fields may be NULL.
  *   lora       host pointer to rank-16 adapters on every expert (see
@@ -200,7 +205,10 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T
                        void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Whole block: route -> permute -> grouped gate/up with SiLU*up ->
- * grouped down -> per-token weighted combine.
+ * grouped down -> per-token weighted combine (the router, bincount, cumsum,
+ * argsort, grouped_mm and index_add_ steps of the grouped_mm MoE path on the
+ * unsloth commit 80aaf1121b page, third paragraph; the result a plain tensor
+ * as on the unsloth commit 4f2bfe7f69 page, second paragraph).
  *   x     bf16 [T][H]
  *   out   [T][H], fp32 or bf16 (cfg->out_dtype): out[t] = sum_{j ascending}
  *         topk_w[t][j] * y[t][j], formed in fp32 (bf16: then rounded to nearest even)
@@ -364,14 +372,19 @@ moe_status moe_graph_capture_prenorm(const moe_config* cfg, const moe_weights* w
                                      void* workspace, size_t ws_bytes, hipStream_t stream,
                                      moe_graph** graph /* host out */);
 
-/* Launches the graph of the smallest bucket >= T on `stream`.  The captured
- * kernels read a live row count kept in the workspace: rows [T, bucket) of
- * x_static are routed to no expert and counted nowhere (counts sum to T*k),
- * and rows [T, bucket) of out_static are left untouched; rows < T are
- * bit-identical to moe_forward of those T rows.  The count is rewritten (one
- * one-thread kernel on `stream`) only when T differs from the count last
- * enqueued into that workspace by any graph of this process.  A graph must be
- * replayed from one thread at a time.
+/* Launches the graph of the smallest bucket >= T on `stream` (the replay of
+ * the bucket captured for a batch size, with the batch's rows copied into
+ * the static input first and the output rows read back from the static
+ * output, on the unsloth commit 80aaf1121b page, second paragraph).  Each
+ * graph's first node writes the live row count T into the workspace, and
+ * the captured kernels read it there: rows [T, bucket) of x_static are
+ * routed to no expert and counted nowhere (counts sum to T*k), and rows
+ * [T, bucket) of out_static are left untouched; rows < T are bit-identical
+ * to moe_forward of those T rows.  When T differs from the previous replay
+ * of the same graph, that node's argument is updated on the host first (no
+ * extra launch).  So whatever was written to the workspace between replays
+ * (eager calls, other graphs on it, any fill) does not change a replay's
+ * result.  A graph must be replayed from one thread at a time.
  * T larger than the largest bucket -> MOE_ERR_INVALID_ARG. */
 moe_status moe_graph_replay(moe_graph* graph, int32_t T, hipStream_t stream);
 

@@ -3,8 +3,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
-#include <map>
-#include <mutex>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -346,11 +344,6 @@ moe_status check_prenorm(const moe_config& c, const moe_prenorm* pn, int32_t row
   return MOE_OK;
 }
 
-// last live row count enqueued into each workspace by a graph replay (shared
-// by every graph of the process that uses the workspace)
-std::mutex g_live_mu;
-std::map<const void*, int32_t> g_live_cache;
-
 }  // namespace
 
 struct moe_graph {
@@ -358,6 +351,10 @@ struct moe_graph {
   std::vector<int32_t> buckets;
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
+  // each graph's first node writes the live row count its kernels read; its
+  // argument is the row count of that graph's last replay
+  std::vector<hipGraphNode_t> live_nodes;
+  std::vector<int32_t> live_vals;
   int32_t* live = nullptr;  // device row count read by the captured kernels (in the workspace)
 };
 
@@ -719,10 +716,6 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
   moe_graph* g = new moe_graph();
   g->cfg = *cfg;
   g->live = at<int32_t>(workspace, layout(*cfg).live);
-  {
-    std::lock_guard<std::mutex> lk(g_live_mu);
-    g_live_cache[g->live] = -1;  // unknown until the first replay writes it
-  }
   for (int i = 0; i < n_buckets; ++i) {
     const int32_t b = buckets[i];
     e = hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal);
@@ -730,8 +723,13 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
       graph_release(g);
       return fail(MOE_ERR_NOT_CAPTURABLE, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
     }
-    const moe_status rs =
-        enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr, g->live, pn ? &pa : nullptr);
+    // the graph writes its own live row count first (the bucket size until
+    // a replay with fewer rows sets the node's argument)
+    moe_status rs = MOE_OK;
+    if ((e = moe::launch_set_live(g->live, b, stream)) != hipSuccess) rs = hip_fail(e, "live-count launch");
+    if (rs == MOE_OK)
+      rs = enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr, g->live,
+                           pn ? &pa : nullptr);
     const std::string launch_msg = rs == MOE_OK ? std::string() : g_last_error;
     hipGraph_t gr = nullptr;
     e = hipStreamEndCapture(stream, &gr);
@@ -741,6 +739,19 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
       return fail(MOE_ERR_NOT_CAPTURABLE,
                   "capture of bucket " + std::to_string(b) + " failed: " +
                       (rs != MOE_OK ? launch_msg : std::string(hipGetErrorString(e))));
+    }
+    // the live-count node: the graph's only root (capture on one stream
+    // makes a chain)
+    size_t nroot = 0;
+    hipGraphNode_t root = nullptr;
+    hipGraphNodeType rtype = hipGraphNodeTypeEmpty;
+    e = hipGraphGetRootNodes(gr, nullptr, &nroot);
+    if (e == hipSuccess && nroot == 1) e = hipGraphGetRootNodes(gr, &root, &nroot);
+    if (e == hipSuccess && root) e = hipGraphNodeGetType(root, &rtype);
+    if (e != hipSuccess || nroot != 1 || !root || rtype != hipGraphNodeTypeKernel) {
+      (void)hipGraphDestroy(gr);
+      graph_release(g);
+      return fail(MOE_ERR_NOT_CAPTURABLE, "captured graph does not start with its live-count node");
     }
     hipGraphExec_t ge = nullptr;
     e = hipGraphInstantiate(&ge, gr, nullptr, nullptr, 0);
@@ -752,6 +763,8 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
     g->buckets.push_back(b);
     g->graphs.push_back(gr);
     g->execs.push_back(ge);
+    g->live_nodes.push_back(root);
+    g->live_vals.push_back(b);
   }
   *graph = g;
   return MOE_OK;
@@ -786,16 +799,22 @@ moe_status moe_graph_replay(moe_graph* g, int32_t T, hipStream_t stream) {
   if (!g) return fail(MOE_ERR_INVALID_ARG, "graph is NULL");
   for (size_t i = 0; i < g->buckets.size(); ++i) {
     if (g->buckets[i] >= T && T >= 1) {
-      // the captured kernels read the live row count from the workspace; it
-      // is rewritten (one tiny kernel) only when it changes
-      {
-        std::lock_guard<std::mutex> lk(g_live_mu);
-        int32_t& cached = g_live_cache[g->live];
-        if (T != cached) {
-          const hipError_t e = moe::launch_set_live(g->live, T, stream);
-          if (e != hipSuccess) return hip_fail(e, "live-count launch");
-          cached = T;
-        }
+      // the captured kernels read the live row count the graph's first node
+      // writes; its argument changes only when T does
+      if (T != g->live_vals[i]) {
+        int32_t* lp = g->live;
+        int32_t tv = T;
+        void* args[2] = {&lp, &tv};
+        hipKernelNodeParams p{};
+        p.func = moe::set_live_kernel_fn();
+        p.gridDim = dim3(1);
+        p.blockDim = dim3(1);
+        p.sharedMemBytes = 0;
+        p.kernelParams = args;
+        p.extra = nullptr;
+        const hipError_t e = hipGraphExecKernelNodeSetParams(g->execs[i], g->live_nodes[i], &p);
+        if (e != hipSuccess) return hip_fail(e, "hipGraphExecKernelNodeSetParams");
+        g->live_vals[i] = T;
       }
       const hipError_t e = hipGraphLaunch(g->execs[i], stream);
       return e == hipSuccess ? MOE_OK : hip_fail(e, "hipGraphLaunch");

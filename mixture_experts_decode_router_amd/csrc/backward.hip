@@ -211,8 +211,10 @@ __device__ __forceinline__ uint2 read_tr4(const uint16_t* base, int off) {
 // (ks & 3) of its 16-byte code chunk in 128-column block ks >> 2.  The strip
 // lies in one 64-column scale block, so the absmax depends on the row m
 // only and is folded into v: the MFMA multiplies (v[p][m] * absmax[m]) by
-// the codebook entries, which are bf16 values, so the weights enter exactly
-// (as in the forward, which applies absmax to partial sums).
+// the codebook entries.  Each fp32 entry enters as two bf16 parts, hi =
+// RNE(cb) and lo = RNE(cb - hi), staged as two fragments and multiplied in
+// two MFMAs into the same accumulator (lo first), so the weights carry the
+// entry to within 2^-18 of its magnitude, as in the forward.
 // RT: 16-row tiles per work item (RT > 1 after an MFMA forward, whose rows
 // are re-bucketed into items of 16 RT rows): each staged weight fragment
 // then serves RT MFMAs, so the weights are streamed once per 16 RT rows.
@@ -224,8 +226,10 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
   static_assert(NS == 1 || RT > 1, "several strips per unit go with several row tiles");
   constexpr bool kHiLo = HILO && MODE == kDown;
   constexpr int kUr = RT == 1 ? kU : (kU / RT > 1 ? kU / RT : 1);  // steps of loads in flight
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[NS][32 * kRowStride];
-  __shared__ uint32_t s_lut[NF4 ? 256 : 1];  // code byte -> (cb[low nibble], cb[high nibble]) as bf16
+  constexpr int kStage = NF4 ? 2 : NS;  // staged fragments per step: the strips, or the hi and lo parts
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[kStage][32 * kRowStride];
+  // code byte -> the hi and the lo bf16 parts of (cb[low nibble], cb[high nibble])
+  __shared__ u32x2_t s_lut[NF4 ? 256 : 1];
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
   const int nrows = MODE == kDown ? H : 2 * I;  // m
@@ -271,17 +275,21 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = lane + 64 * i;
-      s_lut[b] = pack_bf16x2(a.codebook[b & 15], a.codebook[b >> 4]);
+      const float cl = a.codebook[b & 15], ch = a.codebook[b >> 4];
+      const uint32_t hi = pack_bf16x2(cl, ch);
+      s_lut[b] = u32x2_t{hi, pack_bf16x2(cl - bf16lo(hi), ch - bf16hi(hi))};
     }
     wave_sync_lds();
   }
-  // 8 codes (element 2i in the low nibble of byte i) -> their 8 codebook
-  // entries as bf16 pairs (exact: the entries are bf16 values)
-  auto decode8 = [&](uint32_t w) {
-    u32x4_t o;
+  // 8 codes (element 2i in the low nibble of byte i) -> the hi and lo parts
+  // of their 8 codebook entries as bf16 pairs
+  auto decode8 = [&](uint32_t w, u32x4_t& hi, u32x4_t& lo) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = s_lut[(w >> (8 * i)) & 0xffu];
-    return o;
+    for (int i = 0; i < 4; ++i) {
+      const u32x2_t v = s_lut[(w >> (8 * i)) & 0xffu];
+      hi[i] = v[0];
+      lo[i] = v[1];
+    }
   };
   f32x4_t acc[RT][NS][2];
 #pragma unroll
@@ -344,15 +352,20 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < kUr; ++u) {
       if (s0 + u >= nsteps) break;
+      u32x4_t f0l = zero, f1l = zero;  // NF4: the lo parts
       if constexpr (NF4) {
-        f0[u][0] = decode8(c0[u]);
-        f1[u][0] = decode8(c1[u]);
+        decode8(c0[u], f0[u][0], f0l);
+        decode8(c1[u], f1[u][0], f1l);
       }
       wave_sync_lds();  // the previous step's reads are done
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         *reinterpret_cast<u32x4_t*>(s_w[j] + w_off0) = f0[u][j];
         *reinterpret_cast<u32x4_t*>(s_w[j] + w_off1) = f1[u][j];
+      }
+      if constexpr (NF4) {
+        *reinterpret_cast<u32x4_t*>(s_w[1] + w_off0) = f0l;
+        *reinterpret_cast<u32x4_t*>(s_w[1] + w_off1) = f1l;
       }
       wave_sync_lds();
 #pragma unroll
@@ -362,6 +375,12 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
           const uint2 lo = read_tr4(s_w[j], tr_off + 16 * nh);                   // m = 8g .. 8g+3
           const uint2 hi = read_tr4(s_w[j], tr_off + 4 * kRowStride + 16 * nh);  // m = 8g+4 .. 8g+7
           const u32x4_t b = {lo.x, lo.y, hi.x, hi.y};
+          if constexpr (NF4) {  // the codebook entries' lo parts
+            const uint2 llo = read_tr4(s_w[1], tr_off + 16 * nh);
+            const uint2 lhi = read_tr4(s_w[1], tr_off + 4 * kRowStride + 16 * nh);
+            const u32x4_t bl = {llo.x, llo.y, lhi.x, lhi.y};
+            acc[0][j][nh] = mfma16(va[u][0], bl, acc[0][j][nh]);
+          }
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
             acc[rt][j][nh] = mfma16(va[u][rt], b, acc[rt][j][nh]);

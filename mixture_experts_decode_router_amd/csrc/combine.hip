@@ -66,4 +66,6 @@ hipError_t launch_set_live(int32_t* live, int T, hipStream_t s) {
   return hipGetLastError();
 }
 
+void* set_live_kernel_fn() { return reinterpret_cast<void*>(&set_live_kernel); }
+
 }  // namespace moe

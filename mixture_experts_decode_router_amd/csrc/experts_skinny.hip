@@ -26,8 +26,9 @@
 // load into one contiguous 1 KiB read.
 //
 // 4-bit weights (NF4_B64): the codebook value of each code (one LDS table
-// read per two codes) feeds the MFMA unscaled; the per-64 absmax scales the
-// MFMA partial sums of each 64-k half block (see the 4-bit section).
+// read per two codes, as a hi and a lo bf16 part) feeds the MFMA unscaled;
+// the per-64 absmax scales the MFMA partial sums of each 64-k half block
+// (see the 4-bit section).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -240,19 +241,26 @@ __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
 }
 
 // ------------------------------------------------------------------ 4-bit
-// A weight is codebook[code] * absmax(row, 64-block).  Here the tokens are
-// the MFMA A operand and the weights the B operand, D[token][weight row], so
-// a lane's four outputs all belong to its own weight row and the absmax is
-// applied to MFMA partial sums: each 32-k MFMA step lies in one 64-block
-// (steps 0,1 of a 128-k block use block 2kb, steps 2,3 block 2kb+1), and
-//   D[t][row] = sum_h absmax(row, h) * sum_{k in h} x[t][k] bf16(codebook[code])
-// The per-weight work is one table read per two codes: entry b of the table
-// is the packed bf16 pair (codebook[b & 15], codebook[b >> 4]) of code byte
-// b.  The table is held kLutRep times over (copy c of entry b at word
-// b * kLutRep + c) and lane l reads copy l % kLutRep, so the lanes of one
-// read land in distinct LDS banks whatever bytes they look up (one shared
-// copy puts several lanes of each read in one bank: random code bytes over 64
-// lanes).
+// A weight is codebook[code] * absmax(row, 64-block), the codebook holding
+// 16 fp32 values.  Each entry enters the MFMA as two bf16 parts, hi =
+// RNE(cb) and lo = RNE(cb - hi) (cb - hi is exact in fp32), so the operand
+// hi + lo carries cb to within 2^-18 of its magnitude (17 significant bits
+// where a single bf16 holds 8): a bf16-valued entry has lo = 0 and enters
+// exactly.  Here the tokens are the MFMA A operand and the weights the B
+// operand, D[token][weight row], so a lane's four outputs all belong to its
+// own weight row and the absmax is applied to MFMA partial sums: each 32-k
+// MFMA step lies in one 64-block (steps 0,1 of a 128-k block use block 2kb,
+// steps 2,3 block 2kb+1), and
+//   D[t][row] = sum_h absmax(row, h) * sum_{k in h} x[t][k] (lo[code] + hi[code])
+// (the lo products are accumulated first, then the hi ones, into one fp32
+// accumulator).  The per-weight work is one 8-byte table read per two codes:
+// entry b of the table holds the packed bf16 pairs (hi[b & 15], hi[b >> 4])
+// and (lo[b & 15], lo[b >> 4]) of code byte b.  The table is held kLutRep
+// times over (copy c of entry b at entry b * kLutRep + c) and lane l reads
+// copy l % kLutRep, so within each group of kLutRep consecutive lanes the
+// reads land in distinct LDS banks whatever bytes they look up (one shared
+// copy puts several lanes of each read in one bank: random code bytes over
+// 64 lanes); lanes kLutRep apart share a copy and can still collide.
 //
 // Lane (g, r) feeds token row r and weight row r, k = 128kb + 32st + 8g + 0..7
 // for step st = 0..3 (dword st of its 16-byte chunk in the tiled layout; four
@@ -262,30 +270,34 @@ __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
 #define MOE_LUT_REP 16
 #endif
 constexpr int kLutRep = MOE_LUT_REP;  // copies of the code-pair table
-static_assert((kLutRep & (kLutRep - 1)) == 0 && kLutRep <= 64, "table copies");
+static_assert((kLutRep & (kLutRep - 1)) == 0 && kLutRep <= 32, "table copies");
 
 // thread tid < 256 writes every copy of entry tid, starting at copy
 // tid % kLutRep so that the lanes of each store fall in distinct banks
-__device__ __forceinline__ void build_lut(uint32_t* s_lut, const float* cb, int tid) {
+__device__ __forceinline__ void build_lut(u32x2_t* s_lut, const float* cb, int tid) {
   if (tid < 256) {
-    const uint32_t v = pack_bf16x2(cb[tid & 15], cb[tid >> 4]);
+    const float c0 = cb[tid & 15], c1 = cb[tid >> 4];
+    const uint32_t hi = pack_bf16x2(c0, c1);
+    const u32x2_t v = {hi, pack_bf16x2(c0 - bf16lo(hi), c1 - bf16hi(hi))};
 #pragma unroll 8
     for (int c = 0; c < kLutRep; ++c) s_lut[tid * kLutRep + ((c + tid) & (kLutRep - 1))] = v;
   }
 }
 
 // this lane's copy of the table
-__device__ __forceinline__ const uint32_t* lut_copy(const uint32_t* s_lut, int lane) {
+__device__ __forceinline__ const u32x2_t* lut_copy(const u32x2_t* s_lut, int lane) {
   return s_lut + (lane & (kLutRep - 1));
 }
 
-// 8 codes (one dword, element 2i in the low nibble of byte i) -> 8 bf16,
-// read from the lane's copy of the table
-__device__ __forceinline__ u32x4_t lut8(const uint32_t* s_lutl, uint32_t w) {
-  u32x4_t o;
+// 8 codes (one dword, element 2i in the low nibble of byte i) -> the hi and
+// lo parts of their 8 entries, read from the lane's copy of the table
+__device__ __forceinline__ void lut8(const u32x2_t* s_lutl, uint32_t w, u32x4_t& hi, u32x4_t& lo) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = s_lutl[((w >> (8 * i)) & 0xffu) * kLutRep];
-  return o;
+  for (int i = 0; i < 4; ++i) {
+    const u32x2_t v = s_lutl[((w >> (8 * i)) & 0xffu) * kLutRep];
+    hi[i] = v[0];
+    lo[i] = v[1];
+  }
 }
 
 // codes of one 128-k block for this lane: tiled = one 16-byte chunk,
@@ -305,13 +317,20 @@ __device__ __forceinline__ u32x2_t load_scales(const float* s, int kb) {
 }
 
 // one 128-k block of one weight tile: acc[q] += absmax_0 * P0[q] + absmax_1 * P1[q]
-__device__ __forceinline__ f32x4_t block_mma(const uint32_t* s_lutl, u32x4_t codes, const u32x4_t (&xb)[4],
+__device__ __forceinline__ f32x4_t block_mma(const u32x2_t* s_lutl, u32x4_t codes, const u32x4_t (&xb)[4],
                                              u32x2_t sc, f32x4_t acc) {
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t p0 = mfma16(xb[0], lut8(s_lutl, codes[0]), zero);
-  p0 = mfma16(xb[1], lut8(s_lutl, codes[1]), p0);
-  f32x4_t p1 = mfma16(xb[2], lut8(s_lutl, codes[2]), zero);
-  p1 = mfma16(xb[3], lut8(s_lutl, codes[3]), p1);
+  u32x4_t hi[4], lo[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) lut8(s_lutl, codes[st], hi[st], lo[st]);
+  f32x4_t p0 = mfma16(xb[0], lo[0], zero);
+  p0 = mfma16(xb[1], lo[1], p0);
+  p0 = mfma16(xb[0], hi[0], p0);
+  p0 = mfma16(xb[1], hi[1], p0);
+  f32x4_t p1 = mfma16(xb[2], lo[2], zero);
+  p1 = mfma16(xb[3], lo[3], p1);
+  p1 = mfma16(xb[2], hi[2], p1);
+  p1 = mfma16(xb[3], hi[3], p1);
   const float s0 = __uint_as_float(sc[0]), s1 = __uint_as_float(sc[1]);
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = fmaf(s1, p1[q], fmaf(s0, p0[q], acc[q]));
@@ -323,7 +342,7 @@ __device__ __forceinline__ f32x4_t block_mma(const uint32_t* s_lutl, u32x4_t cod
 // built once per 4-wave workgroup
 template <int NB, bool TILED, bool LORA>  // NB: 128-k blocks per loop iteration (H % (128 * NB) == 0)
 __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
-  __shared__ uint32_t s_lut[256 * kLutRep];
+  __shared__ u32x2_t s_lut[256 * kLutRep];
   const int ntile = a.I / 128;
   const int item = blockIdx.x / ntile, nt = blockIdx.x - item * ntile;
   Item it;
@@ -334,7 +353,7 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int n0 = nt * 128 + wave * 32;
-  const uint32_t* sl = lut_copy(s_lut, lane);
+  const u32x2_t* sl = lut_copy(s_lut, lane);
   const bool rv = r < it.M;
   const int tok = rv ? a.perm[it.base + r] / a.k : 0;
   const uint16_t* xr = a.x + (size_t)tok * H + 8 * g;
@@ -408,7 +427,7 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
 // down: a wave owns two 16-row tiles of W_down (32 output columns)
 template <int NB, bool TILED, bool LORA>  // NB: 128-k blocks per loop iteration (I % (128 * NB) == 0)
 __global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
-  __shared__ uint32_t s_lut[256 * kLutRep];
+  __shared__ u32x2_t s_lut[256 * kLutRep];
   const int ctile = a.H / 128;
   const int item = blockIdx.x / ctile, ct = blockIdx.x - item * ctile;
   Item it;
@@ -419,7 +438,7 @@ __global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int c0 = ct * 128 + wave * 32;
-  const uint32_t* sl = lut_copy(s_lut, lane);
+  const u32x2_t* sl = lut_copy(s_lut, lane);
   const bool rv = r < it.M;
   const uint16_t* hr = a.h + (size_t)(it.base + (rv ? r : 0)) * I + 8 * g;
   const int nkb = I / 128;

@@ -227,7 +227,10 @@ struct CombineArgs {
   bool out_bf16;          // round the fp32 sums to bf16 (nearest even)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
-// *live = T (one thread), for graph replays of a bucket larger than T
+// *live = T (one thread): the first node of every captured graph, whose
+// argument a replay with fewer rows than the bucket sets
 hipError_t launch_set_live(int32_t* live, int T, hipStream_t s);
+// the kernel launch_set_live launches, (int32_t* live, int T)
+void* set_live_kernel_fn();
 
 }  // namespace moe

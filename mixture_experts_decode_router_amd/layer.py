@@ -5,6 +5,7 @@ from __future__ import annotations
 
 import copy
 import ctypes
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -29,12 +30,18 @@ class MoELayer:
     """
 
     def __init__(self, inp, t_max: int, device: str = "cuda", tiled: bool = True,
-                 out_bf16: bool = False, renorm: bool = True, lora: Optional[dict] = None, train: bool = False):
+                 out_bf16: bool = False, renorm: bool = True, lora: Optional[dict] = None, train: bool = False,
+                 poison: Optional[bool] = None):
         """out_bf16: bf16 output (else fp32); renorm: top-k weights renormalised
         over the k chosen (else the full softmax at the chosen); lora: fp32
         adapters (a_gate_up, b_gate_up, a_down, b_down arrays and scale, as
         synthetic.lora_adapters makes them) fused into the expert GEMMs;
-        train: the forward keeps what backward() needs."""
+        train: the forward keeps what backward() needs; poison: fill the
+        workspace with 0xFF bytes on the call's stream before every eager
+        route, permute and forward, so that a kernel reading workspace it did
+        not write first gives wrong results (default: the environment
+        variable MOE_POISON_WORKSPACE=1)."""
+        self.poison = os.environ.get("MOE_POISON_WORKSPACE") == "1" if poison is None else bool(poison)
         self.device = torch.device(device)
         self.H, self.E, self.k, self.I = inp.H, inp.E, inp.k, inp.I
         rowmajor = L.MOE_W_BF16 if inp.wfmt == "bf16" else L.MOE_W_NF4_B64
@@ -119,6 +126,14 @@ class MoELayer:
     def upload_x(self, x_bits: np.ndarray) -> torch.Tensor:
         return _dev(x_bits, self.device)
 
+    def _poison(self, stream) -> None:
+        if not self.poison:
+            return
+        if isinstance(stream, int):
+            raise ValueError("workspace poisoning needs a torch stream (or None)")
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+            self.workspace.fill_(0xFF)
+
     def _view(self, addr: int, n: int, dtype) -> torch.Tensor:
         off = addr - self.workspace.data_ptr()
         nbytes = n * torch.tensor([], dtype=dtype).element_size()
@@ -130,6 +145,7 @@ class MoELayer:
         ids = torch.empty(T, self.k, dtype=torch.int32, device=self.device)
         wts = torch.empty(T, self.k, dtype=torch.float32, device=self.device)
         logits = torch.empty(T, self.E, dtype=torch.float32, device=self.device) if with_logits else None
+        self._poison(stream)
         L.moe_route(self.cfg, self.w, x, T, ids, wts, logits, self.workspace, self.ws_bytes, stream)
         return ids, wts, logits
 
@@ -140,6 +156,7 @@ class MoELayer:
         offsets = torch.empty(self.E + 1, dtype=torch.int32, device=self.device)
         perm = torch.empty(n, dtype=torch.int32, device=self.device)
         pos = torch.empty(n, dtype=torch.int32, device=self.device) if with_pos else None
+        self._poison(stream)
         L.moe_permute(self.cfg, ids, T, counts, offsets, perm, pos, self.workspace, self.ws_bytes, stream)
         return counts, offsets, perm, pos
 
@@ -148,6 +165,7 @@ class MoELayer:
         T = T or x.shape[0]
         if out is None:
             out = torch.empty(T, self.H, dtype=self.out_dtype, device=self.device)
+        self._poison(stream)
         L.moe_forward(self.cfg, self.w, x, T, out, self.workspace, self.ws_bytes, stream)
         return out
 
@@ -165,6 +183,7 @@ class MoELayer:
         if residual_out is None and write_residual:
             residual_out = torch.empty(T, self.H, dtype=torch.int16, device=self.device)
         pn = L.make_prenorm(residual, delta, gamma, eps, residual_out, x_out)
+        self._poison(stream)
         L.moe_forward_prenorm(self.cfg, self.w, pn, T, out, self.workspace, self.ws_bytes, stream)
         return out, x_out, residual_out
 

@@ -67,11 +67,8 @@ def nf4_codebook() -> np.ndarray:
     Eight positive levels are N(0,1) quantiles at evenly spaced probabilities
     from 1/2 (excluded) up to delta = 1 - 1/32, scaled so the largest is +1;
     seven negative levels are built the same way and scaled so the smallest is
-    -1; plus an exact zero.  Each level is rounded to the nearest bf16 value
-    (ties to even), the operand type the kernels multiply codebook entries
-    in, so that a dequantised weight codebook[code] * absmax is one and the
-    same fp32 product wherever it is formed.  Returned ascending as fp32, so
-    code 7 is 0.0.
+    -1; plus an exact zero.  Returned ascending as fp32 (each level the
+    nearest fp32 value of its quantile), so code 7 is 0.0.
     """
     nd = statistics.NormalDist()
     delta = 1.0 - 1.0 / 32.0
@@ -80,7 +77,7 @@ def nf4_codebook() -> np.ndarray:
     pos = np.asarray(pos) / max(pos)
     neg = -np.asarray(neg) / max(neg)
     cb = np.sort(np.concatenate([neg, [0.0], pos])).astype(np.float32)
-    return (f32_to_bf16_bits(cb).astype(np.uint32) << 16).view(np.float32)
+    return cb
 
 
 def quantize_nf4(w: np.ndarray, codebook: np.ndarray):
@@ -262,6 +259,23 @@ def make(name: str, T: Optional[int] = None) -> MoEInputs:
     return MoEInputs(name, Tn, H, E, k, I, "bf16", x, wr, bias, wgu, wd)
 
 
+def router_inputs(name: str, T: Optional[int] = None):
+    """(x, w_router, bias, k) of a named workload without drawing its expert
+    weights: the same arrays make(name, T) returns for these fields."""
+    if name == "tiny":
+        H, E, k = 256, 16, 2
+        seed = _LAYER_SEED_TINY
+        Tn = 8 if T is None else T
+    else:
+        H, E, k = QWEN["H"], QWEN["E"], QWEN["k"]
+        seed = _LAYER_SEED_Q4 if name == "q48q" else _LAYER_SEED
+        Tn = {"q8": 8, "q64": 64, "q48q": 48, "q4096": 4096}[name] if T is None else T
+    xseed = _X_SEED[name] if T is None else [_X_SEED[name], T]
+    wr = _normal_bf16(_child_rng(seed, 0, 0), (E, H), 0.02)
+    bias = skew_bias(E) if name == "q4096" else None
+    return activations(Tn, H, xseed), wr, bias, k
+
+
 # pre-block inputs of the fused residual + RMSNorm + router step
 PRENORM_EPS = 1e-6     # Qwen3's RMSNorm epsilon
 _PRENORM_SEED = 3001
@@ -295,10 +309,21 @@ def lora_adapters(E: int, H: int, I: int, rank: int = LORA_RANK, seed=None, alph
                 a_down=g(2, (E, rank, I)), b_down=g(3, (E, H, rank)), scale=np.float32(alpha / rank))
 
 
+def random_codebook(seed: int) -> np.ndarray:
+    """16 ascending fp32 values: -1, 14 uniform draws in (-1, 1), +1.  Unlike
+    the normal-quantile table it has no structure (no exact zero, entries
+    with all 24 significant bits)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 77]))
+    mid = np.sort(rng.uniform(-1.0, 1.0, 14)).astype(np.float32)
+    return np.concatenate([[np.float32(-1.0)], mid, [np.float32(1.0)]]).astype(np.float32)
+
+
 def make_small(T: int, H: int, E: int, k: int, I: int, seed: int, wfmt: str = "bf16",
-               bias: bool = False, x_std: float = 1.0, w_std: float = 0.02) -> MoEInputs:
+               bias: bool = False, x_std: float = 1.0, w_std: float = 0.02,
+               codebook: Optional[np.ndarray] = None) -> MoEInputs:
     """Arbitrary small shape for edge-case tests (own seed, one draw order:
-    router, gate/up, down, activations)."""
+    router, gate/up, down, activations).  codebook: the 4-bit table (default
+    the normal-quantile one)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     wr = _normal_bf16(rng, (E, H), w_std)
     if wfmt == "bf16":
@@ -306,7 +331,7 @@ def make_small(T: int, H: int, E: int, k: int, I: int, seed: int, wfmt: str = "b
         wd = _normal_bf16(rng, (E, H, I), w_std)
         extra = dict(w_gate_up=wgu, w_down=wd)
     else:
-        cb = nf4_codebook()
+        cb = nf4_codebook() if codebook is None else np.asarray(codebook, dtype=np.float32)
         qgu, sgu = quantize_nf4(rng.standard_normal((E, 2 * I, H), dtype=np.float32) * np.float32(w_std), cb)
         qd, sd = quantize_nf4(rng.standard_normal((E, H, I), dtype=np.float32) * np.float32(w_std), cb)
         extra = dict(q_gate_up=qgu, s_gate_up=sgu, q_down=qd, s_down=sd, codebook=cb)

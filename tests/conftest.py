@@ -7,6 +7,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# every test layer fills its workspace with 0xFF bytes before each eager
+# route, permute and forward: a kernel that reads workspace memory no
+# earlier kernel of the same call wrote then gives wrong results
+os.environ.setdefault("MOE_POISON_WORKSPACE", "1")
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

@@ -40,13 +40,10 @@ def test_codebook_is_normal_quantiles():
     d = 1 - 1 / 32
     pos = scipy.stats.norm.ppf(np.linspace(0.5, d, 9)[1:])
     neg = scipy.stats.norm.ppf(np.linspace(0.5, d, 8)[1:])
-    # the levels rounded to bf16: every entry is a bf16 value within half a
-    # bf16 ulp of its quantile (relative 2^-8 at most), so the nearest one
-    assert np.all((cb.view(np.uint32) & 0xFFFF) == 0)
-    q = np.concatenate([(-neg / neg.max())[::-1], [0.0], pos / pos.max()])
-    np.testing.assert_allclose(cb, q, rtol=2.0 ** -8, atol=0)
-    ulp = 2.0 ** (np.floor(np.log2(np.abs(np.where(q == 0, 1.0, q)))) - 7)
-    assert np.all(np.abs(cb - q) <= ulp / 2)
+    np.testing.assert_allclose(cb[8:], pos / pos.max(), rtol=1e-6)
+    np.testing.assert_allclose(cb[:7], (-neg / neg.max())[::-1], rtol=1e-6)
+    # fp32 values, not narrowed to a shorter format: most entries are not bf16 values
+    assert (cb.view(np.uint32) & 0xFFFF).astype(bool).sum() >= 12
 
 
 def test_nf4_pack_unpack_round_trip_and_nibble_order():

@@ -110,9 +110,10 @@ def test_backward_refuses_unsupported_configurations():
 @pytest.mark.parametrize("T,with_lora", [(48, False), (48, True), (7, True)])
 def test_backward_nf4_matches_oracle(T, with_lora):
     # the 4-bit base of the GRPO setting (rank-16 LoRA on 4-bit weights):
-    # the oracle runs on the identically dequantised weights (codebook
-    # entries are bf16 values, so the kernels multiply by them exactly and
-    # the adapter gradients meet the bf16 base's bound)
+    # the oracle runs on the identically dequantised weights, whose fp32
+    # codebook entries the kernels take as two bf16 parts (17 significant
+    # bits), so the adapter gradients meet the bf16 base's bound (with one
+    # bf16 part, the codebook's own rounding showed 4-7 % of rms there)
     inp = workload("q48q", T)
     lay = layer("q48q", 64).with_options(train=True)
     d = S.lora_adapters(inp.E, inp.H, inp.I) if with_lora else None
@@ -135,6 +136,32 @@ def test_backward_nf4_matches_oracle(T, with_lora):
     assert errs["d_x"] <= TOL_NF4 and errs["d_w"] <= TOL_NF4
     if d is not None:
         assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
+
+
+@pytest.mark.parametrize("cb", ["normal", "random"])
+def test_backward_nf4_skewed_many_rows_per_expert(cb):
+    # a 4-bit base with skewed routing, so that one expert gets more than
+    # one 16-row work item, and a codebook of arbitrary fp32 values (or the
+    # normal-quantile one); rank-16 adapters, against the oracle on the
+    # dequantised weights
+    book = S.random_codebook(5) if cb == "random" else None
+    inp = S.make_small(96, 256, 16, 2, 128, seed=61, wfmt="nf4", bias=True, codebook=book)
+    d = S.lora_adapters(inp.E, inp.H, inp.I)
+    lay = MoELayer(inp, t_max=96, train=True).with_lora(d)
+    d_out = d_out_for(inp.T, inp.H, seed=43)
+    say(f"[gpu] backward 4-bit skewed T={inp.T} codebook={cb}")
+    d_x, d_w, g = gpu_backward_lora(lay, inp.x, d_out)
+    counts = lay.views(inp.T)["counts"].cpu().numpy()
+    assert counts.max() > 16
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), O.ExpertWeights(inp), lora=O.LoRA(**d))
+    assert np.array_equal(lay.views(inp.T)["ids"].cpu().numpy(), ref["routing"]["ids"])
+    errs = {"d_x": rel(d_x, ref["d_x"]), "d_w": rel(d_w, ref["d_w"])}
+    for n in LORA_NAMES:
+        errs[n] = rel(g[n], ref["d_" + n])
+    say(f"[gpu]   max rows per expert {counts.max()}; max|err|/rms " +
+        ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_NF4 and errs["d_w"] <= TOL_NF4
+    assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
 
 
 def test_backward_at_prefill_sizes():

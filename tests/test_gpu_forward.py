@@ -100,10 +100,13 @@ def test_forward_decode_sweep_4bit(T):
     dict(T=4, H=256, E=16, k=16, I=128, wfmt="bf16"),      # small batch bucketed by the router: 64 slots
     dict(T=3, H=512, E=256, k=8, I=128, wfmt="bf16"),      # ... with the largest expert count
     dict(T=7, H=256, E=48, k=6, I=128, wfmt="bf16"),       # ... eight-wave select, E not a multiple of 64
+    dict(T=29, H=512, E=16, k=2, I=256, wfmt="nf4", cb="random"),  # codebook of arbitrary fp32 values
+    dict(T=6, H=256, E=16, k=4, I=384, wfmt="nf4", cb="random"),   # ... small grid (three-block down)
 ])
 def test_forward_edge_shapes(case, tiled):
+    book = S.random_codebook(case["T"]) if case.get("cb") == "random" else None
     inp = S.make_small(case["T"], case["H"], case["E"], case["k"], case["I"], seed=case["T"],
-                       wfmt=case["wfmt"], bias=case["k"] == 4)
+                       wfmt=case["wfmt"], bias=case["k"] == 4, codebook=book)
     say(f"[gpu] forward edge {case} tiled={tiled}")
     lay = MoELayer(inp, t_max=case["T"], tiled=tiled)
     out, views = run_forward(lay, inp.x)

@@ -87,6 +87,37 @@ def test_live_count_follows_each_replay(captured):
     stream.synchronize()
 
 
+def test_replay_ignores_what_the_workspace_held_before(captured):
+    """Every replay writes its own live row count (the graph's first node),
+    so a workspace overwritten between two replays of the same partial T
+    (here filled with 0xFF bytes) gives the same result; so does a second
+    graph set on the same workspace replayed in between with another T."""
+    lay, stream, x_static, out_static = captured
+    inp = workload("q64", 64)
+    say("[gpu] replays around a workspace fill")
+    other = L.moe_graph_capture(lay.cfg, lay.w, [64], x_static, out_static, lay.workspace, lay.ws_bytes, stream)
+    try:
+        with torch.cuda.stream(stream):
+            x_static.copy_(lay.upload_x(inp.x))
+            eager = lay.forward(lay.upload_x(inp.x[:40]), stream=stream)
+            lay.replay(40, stream)
+            first = out_static[:40].clone()
+            lay.workspace.fill_(255)
+            out_static.fill_(-7.0)
+            lay.replay(40, stream)
+            second = out_static.clone()
+            L.moe_graph_replay(other, 64, stream)
+            lay.replay(40, stream)
+            third = out_static[:40].clone()
+        stream.synchronize()
+    finally:
+        L.moe_graph_destroy(other)
+    assert torch.equal(first, eager)
+    assert torch.equal(second[:40], eager)
+    assert bool((second[40:48] == -7.0).all())
+    assert torch.equal(third, eager)
+
+
 def test_replays_are_repeatable(captured):
     lay, stream, x_static, out_static = captured
     inp = workload("q64", 64)

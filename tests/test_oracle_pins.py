@@ -80,6 +80,72 @@ def test_router_fast_path_equals_exact_sum_tiny():
     assert np.array_equal(a, b)
 
 
+def _exact_f32(q):
+    """The fp32 value nearest to the rational q (ties to even mantissa),
+    decided by exact rational distances (no intermediate rounding)."""
+    from fractions import Fraction
+    f = np.float32(float(q))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Fraction(float(c)) - q), int(np.array(c).view(np.uint32)) & 1))
+
+
+@pytest.mark.parametrize("name", ["tiny", "q8", "q64", "q48q", "q4096"])
+def test_router_logits_that_decide_routing_are_correctly_rounded(name):
+    """Every logit among a token's top k+1 (the ones whose order and
+    membership decide the routing) equals the fp32 value nearest to the exact
+    dot product.  The oracle rounds its fp64 matmul to fp32; that fp64 sum is
+    within (H-1) 2^-53 sum|x w| of the exact one, so the fp32 rounding can
+    differ only where the fp64 value lies that close to a midpoint between
+    two fp32 numbers: those logits are re-formed exactly in rationals
+    (bf16 products are exact) and rounded to nearest, ties to even.  Adjacent
+    top-(k+1) pairs within 2 fp32 ulp of each other are re-formed the same
+    way whatever their distance from a midpoint."""
+    from fractions import Fraction
+    x_bits, wr_bits, _, k = S.router_inputs(name)
+    x, wr = O.bf16_bits_to_f64(x_bits), O.bf16_bits_to_f64(wr_bits)
+    H = x.shape[1]
+    l64 = x @ wr.T
+    l32 = O.router_logits(x_bits, wr_bits)
+    S_abs = np.abs(x) @ np.abs(wr).T
+    err64 = (H - 1) * 2.0 ** -53 * S_abs * 1.01
+    top = np.argsort(-l32.astype(np.float64), axis=1, kind="stable")[:, :k + 1]
+    ulp = lambda v: np.spacing(np.abs(v).astype(np.float32)).astype(np.float64)  # noqa: E731
+    # distance of the fp64 value from the nearest fp32 rounding boundary
+    lo = np.nextafter(l32, np.float32(-np.inf)).astype(np.float64)
+    hi = np.nextafter(l32, np.float32(np.inf)).astype(np.float64)
+    c = l32.astype(np.float64)
+    dist = np.minimum(np.abs(l64 - (c + lo) / 2), np.abs(l64 - (c + hi) / 2))
+    redo = set()
+    for t in range(l32.shape[0]):
+        row = top[t]
+        for e in row:
+            if dist[t, e] <= err64[t, e]:
+                redo.add((t, int(e)))
+        vals = l32[t, row].astype(np.float64)
+        for j in range(k):
+            if vals[j] - vals[j + 1] <= 2 * ulp(vals[j]):
+                redo.add((t, int(row[j])))
+                redo.add((t, int(row[j + 1])))
+    for t, e in sorted(redo):
+        q = sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x[t], wr[e])), Fraction(0))
+        assert _exact_f32(q) == l32[t, e], (name, t, e)
+    print(f"{name}: {len(redo)} logits re-formed exactly")
+
+
+def test_exact_f32_rounding_helper():
+    """The helper's rounding against cases with a known answer: values on
+    an fp32 number, just above and below a midpoint, and exactly on a
+    midpoint (ties to even, both directions)."""
+    from fractions import Fraction
+    one = Fraction(1)
+    u = Fraction(1, 2 ** 23)                                   # ulp of 1.0f
+    assert _exact_f32(one) == np.float32(1.0)
+    assert _exact_f32(one + u / 2) == np.float32(1.0)          # tie -> even (1.0)
+    assert _exact_f32(one + u / 2 + Fraction(1, 2 ** 80)) == np.nextafter(np.float32(1), np.float32(2))
+    assert _exact_f32(one + 3 * u / 2) == np.float32(1.0) + np.float32(2 * 2.0 ** -23)  # tie -> even (1 + 2u)
+    assert _exact_f32(-(one + u / 2 - Fraction(1, 2 ** 80))) == np.float32(-1.0)
+
+
 def test_router_bias_added_in_fp32():
     inp = S.make_small(6, 64, 8, 2, 64, seed=5, bias=True)
     plain = O.router_logits(inp.x, inp.w_router)
