@@ -375,14 +375,14 @@ moe_status moe_graph_capture_prenorm(const moe_config* cfg, const moe_weights* w
 /* Launches the graph of the smallest bucket >= T on `stream` (the replay of
  * the bucket captured for a batch size, with the batch's rows copied into
  * the static input first and the output rows read back from the static
- * output, on the unsloth commit 80aaf1121b page, second paragraph).  Each
- * graph's first node writes the live row count T into the workspace, and
- * the captured kernels read it there: rows [T, bucket) of x_static are
- * routed to no expert and counted nowhere (counts sum to T*k), and rows
- * [T, bucket) of out_static are left untouched; rows < T are bit-identical
- * to moe_forward of those T rows.  When T differs from the previous replay
- * of the same graph, that node's argument is updated on the host first (no
- * extra launch).  So whatever was written to the workspace between replays
+ * output, on the unsloth commit 80aaf1121b page, second paragraph).  The
+ * graph's first node, the router's first kernel, also writes the live row
+ * count T into the workspace, and the later kernels read it there: rows
+ * [T, bucket) of x_static are routed to no expert and counted nowhere
+ * (counts sum to T*k), and rows [T, bucket) of out_static are left
+ * untouched; rows < T are bit-identical to moe_forward of those T rows.
+ * When T differs from the previous replay of the same graph, that node's
+ * argument is updated on the host first (no extra launch).  So whatever was written to the workspace between replays
  * (eager calls, other graphs on it, any fill) does not change a replay's
  * result.  A graph must be replayed from one thread at a time.
  * T larger than the largest bucket -> MOE_ERR_INVALID_ARG. */

@@ -176,9 +176,10 @@ T* at(void* base, size_t off) {
 // live: device row count for graph replays of a larger bucket (rows >= *live
 // are routed nowhere and not written), or null for an eager call of T rows.
 // pn: fuse the pre-block step into the router pass; x is then its output.
+// rnode: receives the router's first kernel launch (graph captures), or null.
 moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void* x, int32_t T, void* out,
                            void* ws, hipStream_t s, hipEvent_t* ev, const int32_t* live = nullptr,
-                           const moe::PrenormArgs* pn = nullptr) {
+                           const moe::PrenormArgs* pn = nullptr, moe::RouteNode* rnode = nullptr) {
   const Layout L = layout(c);
   const int N = T * c.top_k;
   hipError_t e;
@@ -220,7 +221,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   pa.k = c.top_k;
   // a small batch is bucketed by the router's select workgroup
   bool fused = false;
-  if ((e = moe::launch_route(ra, at<float>(ws, L.route), s, &pa, &fused)) != hipSuccess)
+  if ((e = moe::launch_route(ra, at<float>(ws, L.route), s, &pa, &fused, rnode)) != hipSuccess)
     return hip_fail(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (!fused && (e = moe::launch_permute(pa, s)) != hipSuccess) return hip_fail(e, "permute launch");
@@ -351,9 +352,11 @@ struct moe_graph {
   std::vector<int32_t> buckets;
   std::vector<hipGraph_t> graphs;
   std::vector<hipGraphExec_t> execs;
-  // each graph's first node writes the live row count its kernels read; its
-  // argument is the row count of that graph's last replay
+  // each graph's first node (the router's first kernel) also writes the live
+  // row count the later kernels read; its argument is the row count of that
+  // graph's last replay
   std::vector<hipGraphNode_t> live_nodes;
+  std::vector<moe::RouteNode> live_launch;
   std::vector<int32_t> live_vals;
   int32_t* live = nullptr;  // device row count read by the captured kernels (in the workspace)
 };
@@ -723,13 +726,11 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
       graph_release(g);
       return fail(MOE_ERR_NOT_CAPTURABLE, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
     }
-    // the graph writes its own live row count first (the bucket size until
-    // a replay with fewer rows sets the node's argument)
-    moe_status rs = MOE_OK;
-    if ((e = moe::launch_set_live(g->live, b, stream)) != hipSuccess) rs = hip_fail(e, "live-count launch");
-    if (rs == MOE_OK)
-      rs = enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr, g->live,
-                           pn ? &pa : nullptr);
+    // the router's first kernel writes the live row count (the bucket size
+    // until a replay with fewer rows sets the node's argument)
+    moe::RouteNode rn{};
+    const moe_status rs = enqueue_forward(*cfg, *w, x_static, b, out_static, workspace, stream, nullptr,
+                                          g->live, pn ? &pa : nullptr, &rn);
     const std::string launch_msg = rs == MOE_OK ? std::string() : g_last_error;
     hipGraph_t gr = nullptr;
     e = hipStreamEndCapture(stream, &gr);
@@ -740,8 +741,8 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
                   "capture of bucket " + std::to_string(b) + " failed: " +
                       (rs != MOE_OK ? launch_msg : std::string(hipGetErrorString(e))));
     }
-    // the live-count node: the graph's only root (capture on one stream
-    // makes a chain)
+    // the router node: the graph's only root (capture on one stream makes a
+    // chain)
     size_t nroot = 0;
     hipGraphNode_t root = nullptr;
     hipGraphNodeType rtype = hipGraphNodeTypeEmpty;
@@ -751,7 +752,7 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
     if (e != hipSuccess || nroot != 1 || !root || rtype != hipGraphNodeTypeKernel) {
       (void)hipGraphDestroy(gr);
       graph_release(g);
-      return fail(MOE_ERR_NOT_CAPTURABLE, "captured graph does not start with its live-count node");
+      return fail(MOE_ERR_NOT_CAPTURABLE, "captured graph does not start with the router kernel");
     }
     hipGraphExec_t ge = nullptr;
     e = hipGraphInstantiate(&ge, gr, nullptr, nullptr, 0);
@@ -764,6 +765,7 @@ static moe_status capture_impl(const moe_config* cfg, const moe_weights* w, cons
     g->graphs.push_back(gr);
     g->execs.push_back(ge);
     g->live_nodes.push_back(root);
+    g->live_launch.push_back(rn);
     g->live_vals.push_back(b);
   }
   *graph = g;
@@ -802,17 +804,7 @@ moe_status moe_graph_replay(moe_graph* g, int32_t T, hipStream_t stream) {
       // the captured kernels read the live row count the graph's first node
       // writes; its argument changes only when T does
       if (T != g->live_vals[i]) {
-        int32_t* lp = g->live;
-        int32_t tv = T;
-        void* args[2] = {&lp, &tv};
-        hipKernelNodeParams p{};
-        p.func = moe::set_live_kernel_fn();
-        p.gridDim = dim3(1);
-        p.blockDim = dim3(1);
-        p.sharedMemBytes = 0;
-        p.kernelParams = args;
-        p.extra = nullptr;
-        const hipError_t e = hipGraphExecKernelNodeSetParams(g->execs[i], g->live_nodes[i], &p);
+        const hipError_t e = moe::set_route_live(g->execs[i], g->live_nodes[i], g->live_launch[i], T);
         if (e != hipSuccess) return hip_fail(e, "hipGraphExecKernelNodeSetParams");
         g->live_vals[i] = T;
       }

@@ -48,8 +48,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
-__global__ void set_live_kernel(int32_t* live, int T) { *live = T; }
-
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
@@ -61,11 +59,5 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_set_live(int32_t* live, int T, hipStream_t s) {
-  hipLaunchKernelGGL(set_live_kernel, dim3(1), dim3(1), 0, s, live, T);
-  return hipGetLastError();
-}
-
-void* set_live_kernel_fn() { return reinterpret_cast<void*>(&set_live_kernel); }
 
 }  // namespace moe

@@ -43,16 +43,29 @@ struct RouteArgs {
   int32_t* ids;           // [T][k]
   float* wts;             // [T][k]
   float* logits;          // [T][E] or null
-  const int32_t* live;    // device row count T_live <= T (graph replays), or null: rows >= T_live get no output
+  const int32_t* live;    // device row count T_live <= T (graph replays: the router's first kernel writes
+                          // T there, or the count a replay set), or null: rows >= T_live get no output
   bool softmax_all;       // weights = full softmax over E at the chosen (else renormalised over the k)
   const PrenormArgs* pn;  // host struct: fuse the pre-block step, or null
 };
 struct PermuteArgs;
+// The router's first kernel as launched: enough to re-issue its arguments
+// with another live row count into a captured graph (the kernel's first
+// workgroup writes that count to RouteArgs::live for the rest of the step).
+struct RouteNode {
+  void* fn;
+  dim3 grid, block;
+  alignas(16) unsigned char args[192];
+};
 // scratch: route_scratch_floats(t_max, E, H) floats of device memory.
 // fuse: the bucketing to run as well when the batch is small enough for the
-// select workgroup to do it (*fused says whether it did), or null
+// select workgroup to do it (*fused says whether it did), or null.
+// With a.live set, the first kernel stores a.T there (graph captures).
+// node: receives the first kernel's launch, or null.
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const PermuteArgs* fuse = nullptr,
-                        bool* fused = nullptr);
+                        bool* fused = nullptr, RouteNode* node = nullptr);
+// sets the live row count of a captured router node (see RouteNode)
+hipError_t set_route_live(hipGraphExec_t ge, hipGraphNode_t gn, const RouteNode& rn, int live_rows);
 size_t route_scratch_floats(int t_max, int E, int H);
 // number of K-split partial logits stored per token at batch size T (the
 // scratch holds them [nst][T][E] from its start: the router's approximate
@@ -227,10 +240,6 @@ struct CombineArgs {
   bool out_bf16;          // round the fp32 sums to bf16 (nearest even)
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
-// *live = T (one thread): the first node of every captured graph, whose
-// argument a replay with fewer rows than the bucket sets
-hipError_t launch_set_live(int32_t* live, int T, hipStream_t s);
-// the kernel launch_set_live launches, (int32_t* live, int T)
-void* set_live_kernel_fn();
+
 
 }  // namespace moe

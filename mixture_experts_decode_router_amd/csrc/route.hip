@@ -34,6 +34,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <cstring>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -62,7 +64,11 @@ struct PartParams {
   float eps;
   uint16_t* res_out;      // bf16 [T][H] (r), or null
   uint16_t* x_out;        // bf16 [T][H] (x)
-  const int32_t* live;    // rows >= *live are not written (graph replays), or null
+  // graph replays: the live row count.  Rows >= live_rows are not written
+  // (PN); workgroup (0, 0) stores live_rows to *live_out, where the later
+  // kernels of the step read it.  Eager calls: live_out null, live_rows = T.
+  int live_rows;
+  int32_t* live_out;
 };
 
 __device__ __forceinline__ float round_bf16(float v) { return bf16lo(pack_bf16x2(v, 0.f)); }
@@ -157,8 +163,9 @@ __global__ __launch_bounds__(256) void route_partial(PartParams p) {
   if constexpr (PN) {
     prenorm_scales(p, t0, s_scale);
     sc = s_scale[r];
-    wr_out = wave == 0 && tv && (!p.live || trow < *p.live);
+    wr_out = wave == 0 && tv && trow < p.live_rows;
   }
+  if (p.live_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.live_out = p.live_rows;
   const uint16_t* pa0 = p.wr + (size_t)(wave * 16 + r) * H + g * 8;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   const uint32_t absm = 0x7fff7fffu;
@@ -738,7 +745,16 @@ void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
     launch_partial<NT, false>(pp, grid, s);
 }
 
-hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const PermuteArgs* fuse, bool* fused) {
+// the instantiation launch_partial<NT> picks for pp (the same choice)
+template <int NT>
+const void* partial_fn(const PartParams& pp) {
+  const bool u4 = (pp.H / pp.ks) % (32 * 4) == 0;
+  if (pp.res) return u4 ? (const void*)&route_partial<NT, 4, true> : (const void*)&route_partial<NT, 1, true>;
+  return u4 ? (const void*)&route_partial<NT, 4, false> : (const void*)&route_partial<NT, 1, false>;
+}
+
+hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const PermuteArgs* fuse, bool* fused,
+                        RouteNode* node) {
   const int ks = route_splits(a.H);
   const int ntt = (a.T + kTok - 1) / kTok;
   const int nst = route_stored_splits(a.T, a.H);  // stored partials per token
@@ -751,18 +767,32 @@ hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const
     pp.eps = a.pn->eps;
     pp.res_out = a.pn->res_out;
     pp.x_out = const_cast<uint16_t*>(a.x);  // the block's x is the pre-block output
-    pp.live = a.live;
   }
+  pp.live_rows = a.T;
+  pp.live_out = a.live ? const_cast<int32_t*>(a.live) : nullptr;
   const dim3 pgrid(ntt, nst);
   const int n_et = a.E / 16;
-  if (n_et <= 4)
+  const void* fn;
+  if (n_et <= 4) {
     launch_partial<1>(pp, pgrid, s);
-  else if (n_et <= 8)
+    fn = partial_fn<1>(pp);
+  } else if (n_et <= 8) {
     launch_partial<2>(pp, pgrid, s);
-  else if (n_et <= 12)
+    fn = partial_fn<2>(pp);
+  } else if (n_et <= 12) {
     launch_partial<3>(pp, pgrid, s);
-  else
+    fn = partial_fn<3>(pp);
+  } else {
     launch_partial<4>(pp, pgrid, s);
+    fn = partial_fn<4>(pp);
+  }
+  if (node) {
+    static_assert(sizeof(PartParams) <= sizeof(node->args), "router node arguments");
+    node->fn = const_cast<void*>(fn);
+    node->grid = pgrid;
+    node->block = dim3(256);
+    std::memcpy(node->args, &pp, sizeof(pp));
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // longest fp32 addition chain: 32 inside one MFMA, one per k-step of the
@@ -781,6 +811,21 @@ hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const
   else
     launch_select<4>(sp, fuse_now, s);
   return hipGetLastError();
+}
+
+hipError_t set_route_live(hipGraphExec_t ge, hipGraphNode_t gn, const RouteNode& rn, int live_rows) {
+  PartParams pp;
+  std::memcpy(&pp, rn.args, sizeof(pp));
+  pp.live_rows = live_rows;
+  void* args[1] = {&pp};
+  hipKernelNodeParams kp{};
+  kp.func = rn.fn;
+  kp.gridDim = rn.grid;
+  kp.blockDim = rn.block;
+  kp.sharedMemBytes = 0;
+  kp.kernelParams = args;
+  kp.extra = nullptr;
+  return hipGraphExecKernelNodeSetParams(ge, gn, &kp);
 }
 
 }  // namespace moe
