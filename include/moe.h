@@ -218,6 +218,22 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t T
 moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
                        void* out, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument.  The workspace is a static device array inside the
+ * library, 16 MiB on each GPU the library runs on, held until the process
+ * ends; its address is looked up once per device on the first call there.
+ * Same results as moe_forward(cfg, w, x, T, out, <workspace>, ...).  A
+ * config whose moe_workspace_size() exceeds 16 MiB (the Qwen3-30B-A3B layer
+ * in bf16 fits up to t_max = 192) -> MOE_ERR_WORKSPACE.  Every call on one GPU
+ * shares that array and leaves its last contents there (nothing in it needs
+ * to start at any value): calls that may overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller; calls on one stream
+ * are ordered by the stream.  The routing arrays of the last call are not
+ * exposed (moe_workspace_views needs a caller-owned workspace). */
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T,
+                               void* out, hipStream_t stream);
+
 /* moe_forward that also records `events[0..5]` (host array of hipEvent_t
  * created by the caller) on `stream` before route, permute, gate/up, down,
  * combine and after combine, for per-stage timing.  Same results. */

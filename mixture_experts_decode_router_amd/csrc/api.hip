@@ -4,11 +4,19 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "kernels.hpp"
 #include "moe.h"
+
+// Device scratch of moe_forward_noalloc: one array per GPU, in the code
+// object, so the call needs no allocation.  Host code uses only the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in there), fetched on the first call on each device.
+constexpr size_t kNoAllocScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -345,6 +353,26 @@ moe_status check_prenorm(const moe_config& c, const moe_prenorm* pn, int32_t row
   return MOE_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 struct moe_graph {
@@ -454,6 +482,19 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* 
                        void* workspace, size_t ws_bytes, hipStream_t stream) {
   MOE_TRY(check_forward_args(cfg, w, x, T, out, workspace, ws_bytes));
   return enqueue_forward(*cfg, *w, x, T, out, workspace, stream, nullptr);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const moe_weights* w, const void* x, int32_t T, void* out,
+                               hipStream_t stream) {
+  MOE_TRY(check_cfg(cfg));
+  const size_t need = layout(*cfg).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "config needs " + std::to_string(need) + " bytes of workspace; the static scratch "
+                                   "holds " + std::to_string(kNoAllocScratchBytes) + " (use moe_forward with a workspace)");
+  void* ws = nullptr;
+  MOE_TRY(noalloc_scratch(&ws));
+  MOE_TRY(check_forward_args(cfg, w, x, T, out, ws, need));
+  return enqueue_forward(*cfg, *w, x, T, out, ws, stream, nullptr);
 }
 
 moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, const moe_prenorm* pn, int32_t T,
