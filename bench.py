@@ -62,32 +62,58 @@ def bytes_model(H, I, E, k, T, n_act, wfmt):
     return dict(gate_up=gate_up, down=down, block=block, flops=flops)
 
 
-def cpu_baseline(inp, budget_s=10.0):
-    """fp64 per-token oracle on this host: repeat the batch until ~budget_s."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
+
+
+def cpu_baseline(inp, budget_s=10.0, budget_1t_s=5.0):
+    """fp64 per-token oracle on this host: repeat the batch until ~budget_s on
+    the BLAS threads numpy has (all the cores this process may use), then
+    again on one thread for ~budget_1t_s."""
     import numpy as np
 
     import oracle as O
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = len(os.sched_getaffinity(0))
     W = O.ExpertWeights(inp)
     ids, _, _ = O.route(inp.x, inp.w_router, inp.k, inp.bias)
     W.preload(np.unique(ids))                  # bf16 -> fp64 conversion, not timed
-    n_tok, reps = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        O.forward_per_token(inp, W)
-        n_tok += inp.T
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 1000:
-            break
+
+    def timed(budget):
+        n_tok, reps = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            O.forward_per_token(inp, W)
+            n_tok += inp.T
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget or reps >= 1000:
+                return n_tok, reps, el
+
+    n_tok, reps, el = timed(budget_s)
+    one = None
+    if threadpool_limits is not None and budget_1t_s > 0:
+        with threadpool_limits(limits=1):
+            n1, r1, e1 = timed(budget_1t_s)
+        one = dict(value=round(n1 / e1, 1), unit="tokens/s", cores=1,
+                   sample=f"the same batch repeated {r1}x = {n1} tokens in {e1:.1f} s on one BLAS thread")
     return dict(value=n_tok / el, unit="tokens/s", cores=int(threads), kind="oracle",
                 sample=f"fp64 per-token oracle (router, top-k, SwiGLU experts, combine) over the "
                        f"{inp.T}-token batch repeated {reps}x = {n_tok} tokens in {el:.1f} s; "
-                       f"expert weights pre-converted to fp64 (not timed)")
+                       f"expert weights pre-converted to fp64 (not timed)",
+                cpu_model=_cpu_model(), os_cpu_count=os.cpu_count(),
+                affinity_cpus=len(os.sched_getaffinity(0)), one_thread=one)
 
 
 # ---------------------------------------------------------------- profiles
@@ -168,9 +194,12 @@ def summarize_traffic(fetch_dir, write_dir, workload):
 
 
 def measure_ceilings(torch, L, stream):
-    """Achievable rates on this chip, measured beside the block: a plain
-    1 GiB device copy (bytes read + written per second) and the vendor
-    library's dense bf16 GEMM at 8192^3."""
+    """Achievable rates on this chip, measured beside the block: a read-only
+    stream of 2 GiB with the decode GEMMs' load form (the library's read
+    probe; best of three grid sizes), a plain 1 GiB device copy (bytes read +
+    written per second), the bf16 MFMA issue rate on register operands (the
+    library's MFMA probe, 16x16x32 and 32x32x16, 4 waves per SIMD) and the
+    vendor library's dense bf16 GEMM at 8192^3."""
     ev = L.hip_events(2, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
 
     def timed(fn, reps):
@@ -184,17 +213,36 @@ def measure_ceilings(torch, L, stream):
         torch.cuda.synchronize()
         return L.hip_event_elapsed_ms(ev[0], ev[1]) * 1e-3 / reps
 
+    nbytes = 2 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(16384 * 4, dtype=torch.int32, device="cuda")
+    read = {}
+    for n_wg in (512, 1024, 2048, 4096):
+        t = timed(lambda: L.moe_probe_read(src, nbytes, sink, n_wg, stream), 10)
+        read[n_wg] = nbytes / t / 1e9
+    del src, sink
     src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     t_copy = timed(lambda: dst.copy_(src), 10)
     del src, dst
+    fs = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    mfma = {}
+    for shape, tag in ((0, "16x16x32"), (1, "32x32x16")):
+        iters = 4000
+        t = timed(lambda: L.moe_probe_mfma(fs, 1024, iters, shape, stream), 5)
+        mfma[tag] = 1024 * 4 * iters * 131072 / t / 1e12
+    del fs
     n = 8192
     a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
     b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
     t_gemm = timed(lambda: torch.mm(a, b), 10)
     del a, b
     L.hip_events_destroy(ev)
-    return {"device_copy_GBps": round(2 * (1 << 30) / t_copy / 1e9, 1),
+    best = max(read, key=read.get)
+    return {"stream_read_GBps": round(read[best], 1), "stream_read_workgroups": best,
+            "device_copy_GBps": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "mfma_bf16_16x16x32_TFLOPs": round(mfma["16x16x32"], 1),
+            "mfma_bf16_32x32x16_TFLOPs": round(mfma["32x32x16"], 1),
             "vendor_bf16_gemm_TFLOPs": round(2.0 * n ** 3 / t_gemm / 1e12, 1)}
 
 
@@ -498,8 +546,10 @@ def main():
     ceilings = None
     if not args.no_ceilings:
         ceilings = measure_ceilings(torch, L, stream)
-        log(f"[bench] ceilings: device copy {ceilings['device_copy_GBps']:.0f} GB/s, "
-            f"vendor bf16 GEMM {ceilings['vendor_bf16_gemm_TFLOPs']:.0f} TFLOP/s")
+        log(f"[bench] ceilings: read stream {ceilings['stream_read_GBps']:.0f} GB/s, device copy "
+            f"{ceilings['device_copy_GBps']:.0f} GB/s, MFMA 16x16x32 {ceilings['mfma_bf16_16x16x32_TFLOPs']:.0f} / "
+            f"32x32x16 {ceilings['mfma_bf16_32x32x16_TFLOPs']:.0f} TFLOP/s, vendor bf16 GEMM "
+            f"{ceilings['vendor_bf16_gemm_TFLOPs']:.0f} TFLOP/s")
 
     dominant = "gate_up"
     dom_us = stage_us[dominant]
@@ -542,6 +592,12 @@ def main():
     result = {
         "metric": METRIC,
         "value": round(value, 1),
+        "value_cold": round(T / (cold["read"] * 1e-6), 1) if cold else None,
+        "value_basis": "value: K back-to-back graph replays, wall clock between two synchronisations "
+                       "(expert weights cannot stay in cache between steps; router weights, x and the "
+                       "routing arrays can); value_cold: mean of single replays timed with HIP events, "
+                       "a 512 MiB read scrub between them (outside the events) evicting L2 and the "
+                       "last-level cache",
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,

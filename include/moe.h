@@ -363,6 +363,22 @@ moe_status moe_workspace_views(const moe_config* cfg, void* workspace, size_t ws
 moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t ws_bytes,
                            int32_t* host_counts /* host, E */, hipStream_t stream);
 
+/* Measurement aids (not part of the block): the achievable rates its
+ * kernels are held to, timed by the caller around the call.
+ * moe_probe_read streams `bytes` (a multiple of 16) from `src` once with the
+ * load form the decode expert GEMMs stream weights with (16-byte
+ * non-temporal loads, each wave instruction one contiguous KiB, each wave
+ * walking its own contiguous range) and writes one XOR of the words each
+ * wave read to `sink` (uint32 [n_wg * 4]), so no load can be dropped; n_wg
+ * workgroups of 256 threads.
+ * moe_probe_mfma runs n_wg workgroups of 4 waves, each wave issuing `iters`
+ * rounds of independent bf16 MFMAs on register operands (shape 0: eight
+ * 16x16x32, 131072 flops per round; shape 1: four 32x32x16, 131072 flops
+ * per round), no memory traffic but `sink` (fp32 [n_wg * 256], the sums of
+ * the accumulators).  Bad arguments -> MOE_ERR_INVALID_ARG. */
+moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t n_wg, hipStream_t stream);
+moe_status moe_probe_mfma(float* sink, int32_t n_wg, int32_t iters, int32_t shape, hipStream_t stream);
+
 /* Per-batch-size hipGraphs of moe_forward (the bucketed decode-step capture
  * of the unsloth commit 80aaf1121b page, second paragraph): one graph per
  * bucket size, all reading `x_static` (bf16 [t_max][H]) and writing

@@ -717,6 +717,24 @@ moe_status moe_workspace_views(const moe_config* cfg, void* workspace, size_t ws
   return MOE_OK;
 }
 
+moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t n_wg, hipStream_t stream) {
+  MOE_TRY(check_ptr(src, "src"));
+  MOE_TRY(check_ptr(sink, "sink", 4));
+  if (bytes == 0 || bytes % 16) return fail(MOE_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (n_wg < 1 || n_wg > 65536) return fail(MOE_ERR_INVALID_ARG, "n_wg must lie in [1, 65536]");
+  const hipError_t e = moe::launch_probe_read(src, bytes, sink, n_wg, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "probe launch");
+}
+
+moe_status moe_probe_mfma(float* sink, int32_t n_wg, int32_t iters, int32_t shape, hipStream_t stream) {
+  MOE_TRY(check_ptr(sink, "sink", 4));
+  if (n_wg < 1 || n_wg > 65536) return fail(MOE_ERR_INVALID_ARG, "n_wg must lie in [1, 65536]");
+  if (iters < 1) return fail(MOE_ERR_INVALID_ARG, "iters must be >= 1");
+  if (shape != 0 && shape != 1) return fail(MOE_ERR_INVALID_ARG, "shape must be 0 (16x16x32) or 1 (32x32x16)");
+  const hipError_t e = moe::launch_probe_mfma(sink, n_wg, iters, shape, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "probe launch");
+}
+
 moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t ws_bytes, int32_t* host_counts,
                            hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));

@@ -242,4 +242,9 @@ struct CombineArgs {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 
+// measurement probes (probe.hip): sink holds n_wg * 4 words (read) or
+// n_wg * 256 floats (mfma)
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s);
+hipError_t launch_probe_mfma(float* sink, int n_wg, int iters, int shape, hipStream_t s);
+
 }  // namespace moe
