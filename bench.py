@@ -451,7 +451,7 @@ def main():
     # ---------------- the step with rank-16 fp32 LoRA adapters fused into the
     # expert GEMMs (graph replays, same weights, own workspace)
     lora = None
-    if not args.no_lora and T * k < 32 * E:
+    if not args.no_lora:
         ll = lay.with_lora(S.lora_adapters(E, H, I))
         xl = ll.upload_x(inp.x)
         ol = torch.empty(T, H, dtype=torch.float32, device="cuda")

@@ -111,10 +111,10 @@ typedef struct {
  *   [gate; up] = W_gu x + scale * B_gu (A_gu x)   (before SiLU * up)
  *   y          = W_d h  + scale * B_d (A_d h)      (h: the bf16 h the down GEMM reads)
  * A x is formed in fp32 per routed row (fixed order, batch-independent),
- * the B products in fp32 in the GEMM epilogues.  A call with adapters runs
- * the 16-row expert kernels at every T (also where T * top_k >= 32 *
- * n_experts would otherwise take the MFMA prefill kernels: slower there,
- * the same per-row bits).  Device arrays, fp32, 16-byte aligned:
+ * the B products in fp32 in the GEMM epilogues: the 16-row decode kernels
+ * and the MFMA prefill kernels (T * top_k >= 32 * n_experts, tiled bf16
+ * weights) add them with the same arithmetic, so a row's result does not
+ * depend on the batch.  Device arrays, fp32, 16-byte aligned:
  *   a_gate_up [E][r][H]   b_gate_up [E][2I][r] (gate rows, then up rows)
  *   a_down    [E][r][I]   b_down    [E][H][r] */
 typedef struct {

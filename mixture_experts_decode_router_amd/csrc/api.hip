@@ -122,8 +122,8 @@ bool is_nf4(const moe_config& c) { return c.wfmt == MOE_W_NF4_B64 || c.wfmt == M
 // kernels (tiled bf16 weights only).  A call with LoRA adapters runs on the
 // 16-row kernels at every size: those carry the adapter epilogues, and give
 // the same per-row bits.
-bool mfma_path_for(const moe_config& c, int T, bool lora) {
-  return c.wfmt == MOE_W_BF16_TILED && (long)T * c.top_k >= 32L * c.n_experts && !lora;
+bool mfma_path_for(const moe_config& c, int T) {
+  return c.wfmt == MOE_W_BF16_TILED && (long)T * c.top_k >= 32L * c.n_experts;
 }
 bool is_tiled(const moe_config& c) { return c.wfmt == MOE_W_BF16_TILED || c.wfmt == MOE_W_NF4_B64_TILED; }
 
@@ -210,7 +210,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ra.pn = pn;
 
   // both paths give bit-identical per-row results
-  const bool mfma_path = mfma_path_for(c, T, w.lora != nullptr);
+  const bool mfma_path = mfma_path_for(c, T);
   const int tile = mfma_path ? moe::kMfmaTile : moe::kSkinnyTile;
   moe::PermuteArgs pa{};
   pa.ids = ra.ids;
@@ -259,7 +259,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ea.codebook = w.codebook;
   const bool nf4 = is_nf4(c), tiled = is_tiled(c);
   moe::LoraAArgs la{};
-  if (w.lora) {  // adapters run on the 16-row kernels at every size
+  if (w.lora) {  // adapter terms in the expert kernels' epilogues, at every size
     ea.lora = true;
     ea.lora_scale = w.lora->scale;
     ea.lb_gate_up = w.lora->b_gate_up;
@@ -272,6 +272,7 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
     la.items = pa.items;
     la.n_items = pa.n_items;
     la.max_items = ea.max_items;
+    la.subs = tile / moe::kSkinnyTile;
     la.k = c.top_k;
     la.K = c.hidden;
     la.src = ea.x;
@@ -595,17 +596,18 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
   }
   hipError_t e;
   b.row_tiles = 1;
-  if (mfma_path_for(c, T, w->lora != nullptr)) {
+  if (mfma_path_for(c, T)) {
     // the forward ran the MFMA kernels on a work list of 128-row items; the
-    // backward's transposed GEMVs take items of kBwdRowTiles 16-row tiles:
-    // bucket the same ids again (the routing arrays are rewritten with the
-    // same values)
-    b.row_tiles = moe::kBwdRowTiles;
+    // backward's transposed GEMVs take items of kBwdRowTiles 16-row tiles
+    // (with adapters, of one 16-row tile): bucket the same ids again (the
+    // routing arrays are rewritten with the same values, and the adapters'
+    // per-row U stay in place)
+    b.row_tiles = w->lora ? 1 : moe::kBwdRowTiles;
     moe::PermuteArgs pa{};
     pa.ids = b.ids;
     pa.N = N;
     pa.E = c.n_experts;
-    pa.tile = moe::kSkinnyTile * moe::kBwdRowTiles;
+    pa.tile = moe::kSkinnyTile * b.row_tiles;
     pa.group = 1;
     pa.counts = at<int32_t>(workspace, L.counts);
     pa.offsets = at<int32_t>(workspace, L.offsets);

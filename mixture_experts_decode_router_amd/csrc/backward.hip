@@ -449,16 +449,21 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 //   down (before the down pass turns g, u into d_g, d_u):
 //     A = d_y = w_p d_out[t_p] (r < H),  B = h = silu(g) u in fp32 (c < I)
 //   gate/up (after it): A = (d_g, d_u)[p] (r < 2I),  B = x[t_p] (c < H)
-// A workgroup covers 64 rows of one expert and a few 128-column tiles in
-// turn; thread (4 rows 16 apart, 8 consecutive columns) keeps 32 sums, so
-// each B value loaded serves 4 rows.  The routed rows' tokens and weights are
-// staged in LDS 64 at a time (once per workgroup when the expert has no more
-// rows); each thread's loads are issued 4 rows at a time.  The output is
-// write-bound: fp32 gradients the size of all experts' weights.
-constexpr int kWgRows = 64, kWgCols = 128, kWgChunk = 64, kWgU = 4, kWgTiles = 4;
+// On the matrix cores: a 256-thread workgroup owns a 64 x 64 tile of one
+// expert's d_W and walks the expert's rows 32 at a time (one MFMA k-step).
+// Each chunk of A and B is written to LDS as [p][column] bf16 tiles and read
+// back transposed (ds_read_b64_tr_b16, as in the transposed GEMVs above), so
+// a lane gets 8 consecutive p of one column.  fp32 operands enter as two
+// bf16 parts, hi = RNE(v) and lo = RNE(v - hi) (about 16 bits of v); x is
+// bf16 and enters whole.  Products: A_lo B_hi (+ A_hi B_lo for the down
+// part), then A_hi B_hi, into one fp32 accumulator per output element.  The
+// next chunk's global loads are issued before this chunk's MFMAs.  The
+// output is write-bound: fp32 gradients the size of all experts' weights.
+constexpr int kWmR = 64, kWmC = 64, kWmP = 32;
+constexpr int kWmS = 72;  // LDS row stride in elements (64 columns + padding; rows stay 16-byte aligned)
 
 // h = silu(g) u in fp32 for every routed row (sorted-slot order), formed
-// once for the down weight gradient instead of once per output row block
+// once for the down weight gradient instead of once per output tile
 __global__ __launch_bounds__(256) void h_kernel(BwdArgs a, float* hf) {
   const int I = a.I;
   const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
@@ -473,96 +478,137 @@ __global__ __launch_bounds__(256) void h_kernel(BwdArgs a, float* hf) {
   *reinterpret_cast<f32x4_t*>(hf + p * I + n) = h;
 }
 
-__global__ __launch_bounds__(256) void wgrad_kernel(BwdArgs a, int part) {
-  __shared__ int s_tok[kWgChunk];
-  __shared__ float s_w[kWgChunk];
+// 8 fp32 -> their hi and lo bf16 parts, packed in pairs
+__device__ __forceinline__ void split8(const float (&v)[8], u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    lo[i] = pack_bf16x2(v[2 * i] - bf16lo(hi[i]), v[2 * i + 1] - bf16hi(hi[i]));
+  }
+}
+
+// the MFMA operand of 16 columns starting at col0: lane (r, g) gets column
+// col0 + r, rows p = 8g .. 8g+7 of a [32 p][kWmS] tile
+__device__ __forceinline__ u32x4_t wm_operand(const uint16_t* tile, int tr_off, int col0) {
+  const uint2 lo = read_tr4(tile, tr_off + col0);
+  const uint2 hi = read_tr4(tile, tr_off + 4 * kWmS + col0);
+  return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+
+template <int PART>  // 0: down, 1: gate/up
+__global__ __launch_bounds__(256) void wgrad_mfma_kernel(BwdArgs a) {
+  constexpr bool kBLo = PART == 0;  // B in two parts (h fp32); x is bf16
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kWmP * kWmS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[kBLo ? 2 : 1][kWmP * kWmS];
   const int H = a.H, I = a.I;
-  const int R = part == 0 ? H : 2 * I, C = part == 0 ? I : H;
+  const int R = PART == 0 ? H : 2 * I, C = PART == 0 ? I : H;
   const int e = blockIdx.z;
-  const int r0 = blockIdx.y * kWgRows + (threadIdx.x >> 4);  // rows r0 + 16 q
+  const int r0 = blockIdx.y * kWmR, c0 = blockIdx.x * kWmC;
   const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
-  const bool once = p1 - p0 <= kWgChunk;  // every row staged by the first pass
-  for (int ct = blockIdx.x; ct < C / kWgCols; ct += gridDim.x) {
-    const int c = ct * kWgCols + (threadIdx.x & 15) * 8;
-    float acc[4][8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;  // the wave's 32 x 32 sub-tile
+  const int rr = lane & 15, g = lane >> 4;
+  const int tr_off = (8 * g + (rr >> 2)) * kWmS + 4 * (rr & 3);
+  // chunk fill: thread t brings row p = chunk start + (t >> 3), columns 8 (t & 7) .. +7
+  const int pl = tid >> 3, col = (tid & 7) * 8;
+  f32x4_t acc[2][2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
-    for (int c0 = p0; c0 < p1; c0 += kWgChunk) {
-      const int nr = p1 - c0 < kWgChunk ? p1 - c0 : kWgChunk;
-      if (!once || ct == (int)blockIdx.x) {
-        __syncthreads();  // the previous chunk's LDS reads are done
-        if ((int)threadIdx.x < nr) {
-          const int slot = a.perm[c0 + threadIdx.x];
-          s_tok[threadIdx.x] = slot / a.k;
-          s_w[threadIdx.x] = a.wts[slot];
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // the chunk's raw values for this thread: A (8 fp32), B (8 fp32, or 8 bf16)
+  f32x4_t ra0, ra1, rb0, rb1, rg0, rg1;
+  u32x4_t rx;
+  float rw = 0.f;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  auto fetch = [&](int pc) {
+    const int p = pc + pl;
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    ra0 = ra1 = rb0 = rb1 = rg0 = rg1 = z;
+    rx = zero;
+    rw = 0.f;
+    if (p < p1) {
+      if (PART == 0) {
+        const int slot = a.perm[p];
+        rw = a.wts[slot];
+        const float* dr = a.d_out + (size_t)(slot / a.k) * H + r0 + col;
+        ra0 = *reinterpret_cast<const f32x4_t*>(dr);
+        ra1 = *reinterpret_cast<const f32x4_t*>(dr + 4);
+        if (a.hf) {
+          const float* hr = a.hf + (size_t)p * I + c0 + col;
+          rb0 = *reinterpret_cast<const f32x4_t*>(hr);
+          rb1 = *reinterpret_cast<const f32x4_t*>(hr + 4);
+        } else {
+          const float* gp = a.gu + (size_t)p * 2 * I + c0 + col;
+          rb0 = *reinterpret_cast<const f32x4_t*>(gp);
+          rb1 = *reinterpret_cast<const f32x4_t*>(gp + 4);
+          rg0 = *reinterpret_cast<const f32x4_t*>(gp + I);
+          rg1 = *reinterpret_cast<const f32x4_t*>(gp + I + 4);
         }
-        __syncthreads();
-      }
-      for (int j0 = 0; j0 < nr; j0 += kWgU) {
-        float av[kWgU][4], bv[kWgU][8];
-#pragma unroll
-        for (int u = 0; u < kWgU; ++u) {
-          const int j = j0 + u;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) av[u][q] = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) bv[u][i] = 0.f;
-          if (j < nr) {
-            const size_t p = (size_t)(c0 + j);
-            if (part == 0) {
-              const float* dr = a.d_out + (size_t)s_tok[j] * H + r0;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) av[u][q] = s_w[j] * dr[16 * q];
-              if (a.hf) {  // h formed once per routed row
-                const f32x4_t h0 = *reinterpret_cast<const f32x4_t*>(a.hf + p * I + c);
-                const f32x4_t h1 = *reinterpret_cast<const f32x4_t*>(a.hf + p * I + c + 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  bv[u][i] = h0[i];
-                  bv[u][4 + i] = h1[i];
-                }
-              } else {
-                const float* gp = a.gu + p * 2 * I + c;
-                const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gp);
-                const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gp + 4);
-                const f32x4_t u0 = *reinterpret_cast<const f32x4_t*>(gp + I);
-                const f32x4_t u1 = *reinterpret_cast<const f32x4_t*>(gp + I + 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  bv[u][i] = silu(g0[i]) * u0[i];
-                  bv[u][4 + i] = silu(g1[i]) * u1[i];
-                }
-              }
-            } else {
-              const float* gr = a.gu + p * 2 * I + r0;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) av[u][q] = gr[16 * q];
-              const u32x4_t xv = ld16(a.x + (size_t)s_tok[j] * H + c);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                bv[u][2 * i] = bf16lo(xv[i]);
-                bv[u][2 * i + 1] = bf16hi(xv[i]);
-              }
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kWgU; ++u)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[q][i] = fmaf(av[u][q], bv[u][i], acc[q][i]);
+      } else {
+        const float* gr = a.gu + (size_t)p * 2 * I + r0 + col;
+        ra0 = *reinterpret_cast<const f32x4_t*>(gr);
+        ra1 = *reinterpret_cast<const f32x4_t*>(gr + 4);
+        rx = ld16(a.x + (size_t)(a.perm[p] / a.k) * H + c0 + col);
       }
     }
-    float* o = (part == 0 ? a.g_w_down : a.g_w_gate_up) + ((size_t)e * R + r0) * C + c;
+  };
+  if (p0 < p1) fetch(p0);
+  for (int pc = p0; pc < p1; pc += kWmP) {
+    float av[8], bv[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<f32x4_t*>(o + (size_t)16 * q * C) = f32x4_t{acc[q][0], acc[q][1], acc[q][2], acc[q][3]};
-      *reinterpret_cast<f32x4_t*>(o + (size_t)16 * q * C + 4) = f32x4_t{acc[q][4], acc[q][5], acc[q][6], acc[q][7]};
+      av[q] = PART == 0 ? rw * ra0[q] : ra0[q];
+      av[4 + q] = PART == 0 ? rw * ra1[q] : ra1[q];
     }
-  }  // column tiles
+    u32x4_t ahi, alo, bhi, blo;
+    split8(av, ahi, alo);
+    if constexpr (PART == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bv[q] = a.hf ? rb0[q] : silu(rb0[q]) * rg0[q];
+        bv[4 + q] = a.hf ? rb1[q] : silu(rb1[q]) * rg1[q];
+      }
+      split8(bv, bhi, blo);
+    } else {
+      bhi = rx;
+      blo = zero;
+    }
+    __syncthreads();  // the previous chunk's LDS reads are done
+    *reinterpret_cast<u32x4_t*>(s_a[0] + pl * kWmS + col) = ahi;
+    *reinterpret_cast<u32x4_t*>(s_a[1] + pl * kWmS + col) = alo;
+    *reinterpret_cast<u32x4_t*>(s_b[0] + pl * kWmS + col) = bhi;
+    if constexpr (kBLo) *reinterpret_cast<u32x4_t*>(s_b[kBLo ? 1 : 0] + pl * kWmS + col) = blo;
+    __syncthreads();
+    if (pc + kWmP < p1) fetch(pc + kWmP);  // in flight during the MFMAs
+    u32x4_t oa[2][2], ob[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      oa[i][0] = wm_operand(s_a[0], tr_off, 32 * wr + 16 * i);
+      oa[i][1] = wm_operand(s_a[1], tr_off, 32 * wr + 16 * i);
+      ob[i][0] = wm_operand(s_b[0], tr_off, 32 * wc + 16 * i);
+      if constexpr (kBLo) ob[i][1] = wm_operand(s_b[kBLo ? 1 : 0], tr_off, 32 * wc + 16 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acc[i][j] = mfma16(oa[i][1], ob[j][0], acc[i][j]);
+        if constexpr (kBLo) acc[i][j] = mfma16(oa[i][0], ob[j][1], acc[i][j]);
+        acc[i][j] = mfma16(oa[i][0], ob[j][0], acc[i][j]);
+      }
+  }
+  // lane holds D[4g + q][r] of sub-tile (i, j): row r0 + 32 wr + 16 i + 4g + q, column c0 + 32 wc + 16 j + r
+  float* o = (PART == 0 ? a.g_w_down : a.g_w_gate_up) + (size_t)e * R * C;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const size_t row = (size_t)(r0 + 32 * wr + 16 * i + 4 * g + q);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) o[row * C + c0 + 32 * wc + 16 * j + rr] = acc[i][j][q];
+    }
 }
 
 // ---------------------------------------------------------------- combine
@@ -641,10 +687,12 @@ hipError_t launch_h(const BwdArgs& a, float* hf, hipStream_t s) {
 
 hipError_t launch_wgrad(const BwdArgs& a, bool down, hipStream_t s) {
   const int R = down ? a.H : 2 * a.I, C = down ? a.I : a.H;
-  if (R % kWgRows || C % kWgCols) return hipErrorInvalidValue;
-  const int nct = C / kWgCols;
-  hipLaunchKernelGGL(wgrad_kernel, dim3((nct + kWgTiles - 1) / kWgTiles, R / kWgRows, a.E), dim3(256), 0, s, a,
-                     down ? 0 : 1);
+  if (R % kWmR || C % kWmC) return hipErrorInvalidValue;
+  const dim3 grid(C / kWmC, R / kWmR, a.E);
+  if (down)
+    hipLaunchKernelGGL(wgrad_mfma_kernel<0>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(wgrad_mfma_kernel<1>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

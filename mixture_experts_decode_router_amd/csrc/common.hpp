@@ -44,4 +44,26 @@ __device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Rank-16 LoRA term of one 16 x 16 output tile, D[row][col] = sum_j
+// P[row][j] Q[col][j] (fp32 adapters), as four fp32 MFMA 16x16x4 steps:
+// lane (r, g) supplies P[row r][4g .. 4g+3] and Q[col r][4g .. 4g+3] (step c
+// multiplies j = 4g + c) and receives D[4g + q][r], the accumulator layout of
+// the bf16 16x16 tiles.  Every expert kernel (16-row and MFMA, bf16 and
+// 4-bit) adds scale * D with this same sequence, so a row gets the same bits
+// whichever kernel its batch size selects.
+__device__ __forceinline__ f32x4_t lora_tile(f32x4_t prow, f32x4_t qrow) {
+  f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) d = __builtin_amdgcn_mfma_f32_16x16x4f32(prow[c], qrow[c], d, 0, 0, 0);
+  return d;
+}
+
+__device__ __forceinline__ f32x4_t ld4f(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
+
+// acc += scale * d, elementwise
+__device__ __forceinline__ void add_scaled(f32x4_t& acc, f32x4_t d, float scale) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] += scale * d[q];
+}
+
 }  // namespace moe

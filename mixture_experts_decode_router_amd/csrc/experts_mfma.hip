@@ -126,8 +126,10 @@ __device__ __forceinline__ void mma_step(const unsigned char* sb, const int (&wr
     for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
 }
 
-// kWaves / 4 waves per SIMD per workgroup; kBlocksPerCU workgroups share a CU
-template <bool GATE_UP>
+// kWaves / 4 waves per SIMD per workgroup; kBlocksPerCU workgroups share a CU.
+// LORA: the epilogue adds scale * sum_j B[e][row][j] U[p][j] to each fp32
+// accumulator before anything else uses it (lora_tile, as the 16-row kernels).
+template <bool GATE_UP, bool LORA>
 __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mfma(ExpertArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char s_raw[];
   const int H = a.H, I = a.I;
@@ -234,6 +236,28 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
 
   // ---- epilogue: lane (r, g) holds weight rows 4g+q of tile i, token row r of token tile j
   const int r = lane & 15, g = lane >> 4;
+  if constexpr (LORA) {  // before any accumulator is used; every lane takes part in the MFMAs
+    const float* ub = GATE_UP ? a.u_gate_up : a.u_down;
+    f32x4_t uq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int trow = (wm * 4 + j) * 16 + r;
+      uq[j] = trow < M ? ld4f(ub + (size_t)(base + trow) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < kNT; ++i) {
+      size_t brow;  // the adapter row of this lane's weight row in tile i
+      if (GATE_UP) {
+        const int n = nt * (kBN / 2) + (wn * kH + (i % kH)) * 16 + r;
+        brow = (size_t)e * 2 * I + (i < kH ? n : I + n);
+      } else {
+        brow = (size_t)e * H + min(nt * kBN + (wn * kNT + i) * 16 + r, H - 1);  // rows past H are never stored
+      }
+      const f32x4_t bq = ld4f((GATE_UP ? a.lb_gate_up : a.lb_down) + brow * 16 + 4 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) add_scaled(acc[i][j], lora_tile(bq, uq[j]), a.lora_scale);
+    }
+  }
   if (GATE_UP) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
 }
 
 // dynamic LDS beyond 64 KiB needs the per-function limit raised, once per device
-template <bool GATE_UP>
+template <bool GATE_UP, bool LORA>
 hipError_t allow_lds() {
   static bool done[64] = {};
   int dev = 0;
@@ -280,28 +304,29 @@ hipError_t allow_lds() {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (done[dev]) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_mfma<GATE_UP>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&expert_mfma<GATE_UP, LORA>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e == hipSuccess) done[dev] = true;
   return e;
 }
 
-}  // namespace
-
-hipError_t launch_gate_up_mfma(const ExpertArgs& a, hipStream_t s) {
-  hipError_t e = allow_lds<true>();
+template <bool GATE_UP, bool LORA>
+hipError_t launch_mfma_t(const ExpertArgs& a, hipStream_t s) {
+  hipError_t e = allow_lds<GATE_UP, LORA>();
   if (e != hipSuccess) return e;
-  const dim3 grid(a.max_items * (a.I / (kBN / 2)));
-  hipLaunchKernelGGL(expert_mfma<true>, grid, dim3(kThreads), kLdsBytes, s, a);
+  const dim3 grid(a.max_items * (GATE_UP ? a.I / (kBN / 2) : (a.H + kBN - 1) / kBN));
+  hipLaunchKernelGGL((expert_mfma<GATE_UP, LORA>), grid, dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_gate_up_mfma(const ExpertArgs& a, hipStream_t s) {
+  return a.lora ? launch_mfma_t<true, true>(a, s) : launch_mfma_t<true, false>(a, s);
+}
+
 hipError_t launch_down_mfma(const ExpertArgs& a, hipStream_t s) {
-  hipError_t e = allow_lds<false>();
-  if (e != hipSuccess) return e;
-  const dim3 grid(a.max_items * ((a.H + kBN - 1) / kBN));
-  hipLaunchKernelGGL(expert_mfma<false>, grid, dim3(kThreads), kLdsBytes, s, a);
-  return hipGetLastError();
+  return a.lora ? launch_mfma_t<false, true>(a, s) : launch_mfma_t<false, false>(a, s);
 }
 
 }  // namespace moe

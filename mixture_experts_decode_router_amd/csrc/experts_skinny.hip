@@ -53,24 +53,6 @@ __device__ __forceinline__ bool load_item(const ExpertArgs& a, int item, Item& i
   return true;
 }
 
-// LoRA delta of one output row for one routed row: scale * sum_j B[j] U[j]
-// over the rank-16 adapter (fp32, j in order)
-__device__ __forceinline__ void load_u16(const float* up, f32x4_t (&u)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) u[i] = *reinterpret_cast<const f32x4_t*>(up + 4 * i);
-}
-
-__device__ __forceinline__ float lora_dot(const float* brow, const f32x4_t (&u)[4], float scale) {
-  float d = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(brow + 4 * i);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) d = fmaf(b[q], u[i][q], d);
-  }
-  return scale * d;
-}
-
 // ------------------------------------------------------------------ bf16
 // The bf16 kernels run one wave per workgroup (4 per item x column tile):
 // the finer grain keeps HBM busy through the last workgroups of the launch.
@@ -139,18 +121,13 @@ __global__ __launch_bounds__(64) void gate_up_bf16(ExpertArgs a) {
     }
   }
   // lane holds rows n0 + 4g + q (q = 0..3) of token column r
+  if constexpr (LORA) {  // every lane takes part in the MFMAs
+    const f32x4_t uq = rv ? ld4f(a.u_gate_up + (size_t)(it.base + r) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float* bg = a.lb_gate_up + ((size_t)it.e * 2 * I + n0 + r) * 16 + 4 * g;
+    add_scaled(accg, lora_tile(ld4f(bg), uq), a.lora_scale);
+    add_scaled(accu, lora_tile(ld4f(bg + (size_t)I * 16), uq), a.lora_scale);
+  }
   if (rv) {
-    if constexpr (LORA) {
-      f32x4_t uu[4];
-      load_u16(a.u_gate_up + (size_t)(it.base + r) * 16, uu);
-      const float* bg = a.lb_gate_up + ((size_t)it.e * 2 * I + n0 + 4 * g) * 16;
-      const float* bu = bg + (size_t)I * 16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        accg[q] += lora_dot(bg + 16 * q, uu, a.lora_scale);
-        accu[q] += lora_dot(bu + 16 * q, uu, a.lora_scale);
-      }
-    }
     if constexpr (SAVE) {  // the pre-activations the nonlinearity sees
       float* gp = a.gu + (size_t)(it.base + r) * 2 * I + n0 + 4 * g;
       *reinterpret_cast<f32x4_t*>(gp) = accg;
@@ -222,17 +199,13 @@ __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
       acc1 = mfma16(a1[u], hb[u], acc1);
     }
   }
+  if constexpr (LORA) {  // every lane takes part in the MFMAs
+    const f32x4_t uq = rv ? ld4f(a.u_down + (size_t)(it.base + r) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float* b0 = a.lb_down + ((size_t)it.e * H + c0 + r) * 16 + 4 * g;
+    add_scaled(acc0, lora_tile(ld4f(b0), uq), a.lora_scale);
+    add_scaled(acc1, lora_tile(ld4f(b0 + 16 * 16), uq), a.lora_scale);
+  }
   if (rv) {
-    if constexpr (LORA) {
-      f32x4_t uu[4];
-      load_u16(a.u_down + (size_t)(it.base + r) * 16, uu);
-      const float* b0 = a.lb_down + ((size_t)it.e * H + c0 + 4 * g) * 16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc0[q] += lora_dot(b0 + 16 * q, uu, a.lora_scale);
-        acc1[q] += lora_dot(b0 + 16 * (16 + q), uu, a.lora_scale);
-      }
-    }
     const int slot = a.perm[it.base + r];
     float* yrow = a.y + (size_t)slot * H;
     *reinterpret_cast<f32x4_t*>(yrow + c0 + 4 * g) = acc0;
@@ -392,21 +365,20 @@ __global__ __launch_bounds__(kNf4Threads) void gate_up_nf4(ExpertArgs a) {
       for (int j = 0; j < 4; ++j) acc[j] = block_mma(sl, cd[h][j], xb[h], sc[h][j], acc[j]);
   }
   // lane holds tokens 4g + q of rows n0 + 16j + r
+  if constexpr (LORA) {  // tokens are the rows of these tiles: P = U, Q = the adapter's B rows
+    const f32x4_t up = rv ? ld4f(a.u_gate_up + (size_t)(it.base + r) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float* bg = a.lb_gate_up + ((size_t)it.e * 2 * I + n0 + r) * 16 + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      add_scaled(acc[j], lora_tile(up, ld4f(bg + 16 * 16 * j)), a.lora_scale);
+      add_scaled(acc[j + 2], lora_tile(up, ld4f(bg + (size_t)I * 16 + 16 * 16 * j)), a.lora_scale);
+    }
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int m = 4 * g + q;
     if (m < it.M) {
       uint16_t* hrow = a.h + (size_t)(it.base + m) * I + n0 + r;
-      if constexpr (LORA) {
-        f32x4_t uu[4];
-        load_u16(a.u_gate_up + (size_t)(it.base + m) * 16, uu);
-        const float* bg = a.lb_gate_up + ((size_t)it.e * 2 * I + n0 + r) * 16;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[j][q] += lora_dot(bg + 16 * 16 * j, uu, a.lora_scale);
-          acc[j + 2][q] += lora_dot(bg + (size_t)I * 16 + 16 * 16 * j, uu, a.lora_scale);
-        }
-      }
       if (a.gu) {  // training forward: keep the pre-activations the nonlinearity sees
         float* gp = a.gu + (size_t)(it.base + m) * 2 * I + n0 + r;
 #pragma unroll
@@ -473,18 +445,17 @@ __global__ __launch_bounds__(kNf4Threads) void down_nf4(ExpertArgs a) {
       for (int j = 0; j < 2; ++j) acc[j] = block_mma(sl, cd[h][j], hb[h], sc[h][j], acc[j]);
   }
   // lane holds tokens 4g + q of output columns c0 + 16j + r
+  if constexpr (LORA) {
+    const f32x4_t up = rv ? ld4f(a.u_down + (size_t)(it.base + r) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float* b0 = a.lb_down + ((size_t)it.e * H + c0 + r) * 16 + 4 * g;
+    add_scaled(acc[0], lora_tile(up, ld4f(b0)), a.lora_scale);
+    add_scaled(acc[1], lora_tile(up, ld4f(b0 + 16 * 16)), a.lora_scale);
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int m = 4 * g + q;
     if (m < it.M) {
       float* yrow = a.y + (size_t)a.perm[it.base + m] * H + c0 + r;
-      if constexpr (LORA) {
-        f32x4_t uu[4];
-        load_u16(a.u_down + (size_t)(it.base + m) * 16, uu);
-        const float* b0 = a.lb_down + ((size_t)it.e * H + c0 + r) * 16;
-        acc[0][q] += lora_dot(b0, uu, a.lora_scale);
-        acc[1][q] += lora_dot(b0 + 16 * 16, uu, a.lora_scale);
-      }
       yrow[0] = acc[0][q];
       yrow[16] = acc[1][q];
     }

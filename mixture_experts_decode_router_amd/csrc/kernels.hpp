@@ -130,6 +130,7 @@ struct LoraAArgs {
   const int32_t* items;
   const int32_t* n_items;
   int max_items, k, K;
+  int subs;               // 16-row sub-tiles per work item (1, or kMfmaTile / 16 on the MFMA path's work list)
   const uint16_t* src;    // x [T][K] (by_token) or h [N][K] (sorted-slot order)
   bool by_token;
   const float* A;         // fp32 [E][16][K]
@@ -213,7 +214,8 @@ hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s);
 hipError_t launch_lora_grad(const BwdArgs& a, bool down, hipStream_t s);
 
 // LDS-tiled MFMA grouped GEMMs (bf16 weights in the tiled layout only);
-// the work list must use kMfmaTile.
+// the work list must use kMfmaTile.  With a.lora the epilogues add the
+// adapters' B U terms exactly as the 16-row kernels do.
 hipError_t launch_gate_up_mfma(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_down_mfma(const ExpertArgs& a, hipStream_t s);
 

@@ -7,7 +7,7 @@
 // accumulators (the rank-16, fp32-adapter LoRA of the unsloth commit
 // 4f2bfe7f69 page's workload, injected into the grouped GEMMs).
 //
-// One workgroup per item; K is cut into 64-k blocks, block b going to wave
+// One workgroup per item (per 16-row sub-tile of a longer item); K is cut into 64-k blocks, block b going to wave
 // b % 16 (at most four per wave).  The 16 x 16 tile U^T = A[e] (16 x K) *
 // src^T (K x 16 rows) is one fp32 MFMA accumulation per wave over its blocks
 // in order (16x16x4: lane (r, g) feeds A row r and the column of row r,
@@ -30,10 +30,11 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
 
 __global__ __launch_bounds__(64 * kWaves) void lora_a_kernel(LoraAArgs a) {
   __shared__ f32x4_t s_part[kWaves][64];
-  const int item = blockIdx.x;
+  const int item = blockIdx.x / a.subs, sub = blockIdx.x - item * a.subs;
   if (item >= *a.n_items) return;  // uniform over the workgroup
-  const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
+  const int e = a.items[2 * item], m0 = a.items[2 * item + 1] + 16 * sub;
   const int c = a.counts[e] - m0;
+  if (c <= 0) return;  // a sub-tile past the item's rows
   const int M = c < 16 ? c : 16, base = a.offsets[e] + m0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -300,7 +301,8 @@ hipError_t launch_lora_grad(const BwdArgs& a, bool down, hipStream_t s) {
 
 hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s) {
   if (a.K % 64 || a.K > 64 * kMaxBlocks * kWaves) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lora_a_kernel, dim3(a.max_items), dim3(64 * kWaves), 0, s, a);
+  if (a.subs < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lora_a_kernel, dim3(a.max_items * a.subs), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -361,6 +361,36 @@ def test_backward_weight_grads_match_oracle(name, T, with_lora):
             assert np.array_equal(res[2][n].cpu().numpy(), ref_l[2][n])
 
 
+def test_backward_weight_grads_wide_intermediate():
+    """I > H: the down weight gradient forms h = silu(g) u from the kept
+    g, u itself (no room for an fp32 h in y's memory); every expert
+    against the oracle, several 32-row chunks per expert."""
+    inp = S.make_small(80, 256, 16, 4, 384, seed=71, bias=True)
+    lay = MoELayer(inp, t_max=80, train=True)
+    d_out = d_out_for(inp.T, inp.H, seed=47)
+    say(f"[gpu] backward with weight gradients, I > H, T={inp.T}")
+    x = lay.upload_x(inp.x)
+    lay.forward(x)
+    wg = weight_grad_buffers(lay)
+    res = lay.backward(x, torch.from_numpy(d_out).cuda(), weight_grads=wg)
+    torch.cuda.synchronize()
+    counts = lay.views(inp.T)["counts"].cpu().numpy()
+    assert counts.max() > 32
+    b = O.backward_per_token(inp, d_out.astype(np.float64), O.ExpertWeights(inp), weight_grads=True,
+                             wgrad_experts=list(range(inp.E)))
+    errs = {"d_x": rel(res[0].cpu().numpy(), b["d_x"])}
+    for key, dev in (("d_w_gate_up", wg[0]), ("d_w_down", wg[1])):
+        for e in range(inp.E):
+            got = dev[e].cpu().numpy()
+            if counts[e] == 0:
+                assert not got.any(), (key, e)
+            else:
+                errs[f"{key}[{e}]"] = rel(got, b[key][e])
+    worst = max((v, k) for k, v in errs.items() if k != "d_x")
+    say(f"[gpu]   d_x {errs['d_x']:.3e}; worst weight gradient {worst[1]} {worst[0]:.3e}")
+    assert errs["d_x"] <= TOL_BF16 and worst[0] <= TOL_LORA_GRAD
+
+
 def test_backward_weight_grads_deterministic():
     inp = workload("q64", 64)
     lay = layer("q64", 64).with_options(train=True)

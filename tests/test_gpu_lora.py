@@ -1,7 +1,8 @@
 """LoRA adapters fused into the decode expert GEMMs, against the fp64 oracle
 with the same adapters: routing bit-exact, outputs within the bf16 / 4-bit
 tolerances; zero B gives the base block's bits; graph replays equal eager;
-at prefill sizes the adapters run on the 16-row kernels."""
+at prefill sizes the MFMA kernels add the adapter terms with the same
+arithmetic as the 16-row kernels, so rows do not depend on the batch."""
 import numpy as np
 import pytest
 import torch
@@ -117,27 +118,33 @@ def test_lora_graph_replay_at_prefill_size_equals_eager():
         lay.release_graph()
 
 
-def test_lora_at_prefill_sizes():
-    # T*k = 32*E: without adapters the MFMA prefill kernels run; with them
-    # the 16-row kernels at this size, against the oracle, and zero B gives
-    # the MFMA kernels' bits
-    inp = workload("tiny", 256)
+@pytest.mark.parametrize("T", [256, 1024])
+def test_lora_at_prefill_sizes(T):
+    # T*k >= 32*E: the MFMA prefill kernels run, adding the adapter terms in
+    # their epilogues (several 128-row items per expert at T = 1024), against
+    # the oracle; each row is the same bits as a decode-sized call's (16-row
+    # kernels); zero B gives the base MFMA kernels' bits
+    inp = workload("tiny", T)
     d = adapters(inp)
-    base = layer("tiny", 256)
+    base = layer("tiny", 1024)
     say(f"[gpu] LoRA forward tiny at prefill size T={inp.T}")
     lay = base.with_lora(d)
-    out = lay.forward(lay.upload_x(inp.x))
+    x = lay.upload_x(inp.x)
+    out = lay.forward(x)
     torch.cuda.synchronize()
     ref_out, ref = O.forward_batched(inp, oracle_weights("tiny"), lora=O.LoRA(**d))
     check_views(lay.views(inp.T), ref)
     err = rel_err(out.cpu().numpy(), ref_out)
     say(f"[gpu]   max|err|/rms = {err:.3e}")
     assert err <= TOL_BF16
+    small = lay.forward(lay.upload_x(inp.x[:16]))
+    torch.cuda.synchronize()
+    assert torch.equal(small, out[:16])
     d0 = adapters(inp)
     d0["b_gate_up"][:] = 0
     d0["b_down"][:] = 0
-    x = base.upload_x(inp.x)
-    a = base.forward(x)
-    b = base.with_lora(d0).forward(x)
+    xb = base.upload_x(inp.x)
+    a = base.forward(xb)
+    b = base.with_lora(d0).forward(xb)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
