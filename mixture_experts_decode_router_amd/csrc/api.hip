@@ -595,30 +595,11 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     b.g_b_down = d_lora->d_b_down;
   }
   hipError_t e;
-  b.row_tiles = 1;
-  if (mfma_path_for(c, T)) {
-    // the forward ran the MFMA kernels on a work list of 128-row items; the
-    // backward's transposed GEMVs take items of kBwdRowTiles 16-row tiles
-    // (with adapters, of one 16-row tile): bucket the same ids again (the
-    // routing arrays are rewritten with the same values, and the adapters'
-    // per-row U stay in place)
-    b.row_tiles = w->lora ? 1 : moe::kBwdRowTiles;
-    moe::PermuteArgs pa{};
-    pa.ids = b.ids;
-    pa.N = N;
-    pa.E = c.n_experts;
-    pa.tile = moe::kSkinnyTile * b.row_tiles;
-    pa.group = 1;
-    pa.counts = at<int32_t>(workspace, L.counts);
-    pa.offsets = at<int32_t>(workspace, L.offsets);
-    pa.perm = at<int32_t>(workspace, L.perm);
-    pa.pos = at<int32_t>(workspace, L.pos);
-    pa.items = at<int32_t>(workspace, L.items);
-    pa.n_items = at<int32_t>(workspace, L.n_items);
-    pa.chunk_base = at<int32_t>(workspace, L.chunks);
-    pa.k = c.top_k;
-    if ((e = moe::launch_permute(pa, stream)) != hipSuccess) return hip_fail(e, "permute launch");
-  }
+  // the transposed products run over the forward's work list: 16-row items
+  // (the 16-row GEMVs) or, after the MFMA forward, 128-row items (the tiled
+  // transposed GEMMs); the adapter kernels take 16-row sub-tiles of either
+  b.row_tiles = mfma_path_for(c, T) ? moe::kMfmaTile / moe::kSkinnyTile : 1;
+  b.max_items = max_items_for(N, c.n_experts, moe::kSkinnyTile * b.row_tiles, 1);
   // the down-adapter and down-weight gradients read g, u, so they come
   // before the down pass turns those into d_g, d_u; the gate/up ones after it
   if ((e = moe::launch_bwd_weights(b, stream)) != hipSuccess) return hip_fail(e, "backward weights launch");

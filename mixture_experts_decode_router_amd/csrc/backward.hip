@@ -391,29 +391,17 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
     }
   }
   // lane holds D[row 4g + q][column 32 ks + 16 nh + r]
-  if constexpr (LORA) {
+  if constexpr (LORA) {  // s A^T z: rows p (P = z), columns n (Q[n][j] = A[e][j][n])
     const float* la = (MODE == kDown ? a.la_down + (size_t)e * 16 * I : a.la_gate_up + (size_t)e * 16 * H) +
                       32 * ks + r;
     const float* zb = MODE == kDown ? a.z_down : a.z_gate_up;
-    float av[2][16];
+    const f32x4_t zp = r < M ? ld4f(zb + (size_t)(base + r) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nh = 0; nh < 2; ++nh)
+    for (int nh = 0; nh < 2; ++nh) {
+      f32x4_t aq;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) av[nh][j] = la[(size_t)j * ncols + 16 * nh];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int m = 4 * g + q;
-      if (m >= M) continue;
-      f32x4_t z[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = *reinterpret_cast<const f32x4_t*>(zb + (size_t)(base + m) * 16 + 4 * i);
-#pragma unroll
-      for (int nh = 0; nh < 2; ++nh) {
-        float d = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) d = fmaf(av[nh][j], z[j >> 2][j & 3], d);
-        acc[0][0][nh][q] += a.lora_scale * d;
-      }
+      for (int c = 0; c < 4; ++c) aq[c] = la[(size_t)(4 * g + c) * ncols + 16 * nh];
+      add_scaled(acc[0][0][nh], lora_tile(zp, aq), a.lora_scale);
     }
   }
 #pragma unroll
@@ -437,6 +425,203 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
           } else {
             a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[rt][j][nh][q];
           }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- transposed GEMMs
+// The same products as bwd_t_kernel, out[p][n] = sum_m W[e][m][n] v[p][m],
+// over the 128-row items of the MFMA forward's work list, as LDS-tiled MFMA
+// GEMMs: a 512-thread workgroup owns an item's 128 rows x 256 columns n; 8
+// waves, each 64 rows x 64 columns as 4 x 4 MFMA 16x16x32 tiles.  Per 32-m
+// stage every wave loads its share of the weight fragments (2 row tiles x 8
+// column blocks, each one contiguous kilobyte of the tiled layout) and of
+// the rows' v (fp32, rounded to bf16: hi, and lo = v - hi where HILO) one
+// stage ahead into registers and writes them to one of two LDS buffers in
+// MFMA operand order; a lane's B operand (column n, m = 8g .. 8g+7) is read
+// straight out of the weight fragments with transposing LDS reads.  The
+// operands, the lanes' m assignment and the m order are those of
+// bwd_t_kernel, so every output is the same bits as there: a row's gradient
+// does not depend on the batch.  Epilogues as in bwd_t_kernel.
+constexpr int kBgBN = 256;                       // output columns per workgroup
+constexpr int kBgWaves = 8;
+constexpr int kBgThreads = 64 * kBgWaves;
+constexpr int kBgWFrags = 2 * (kBgBN / 32);      // weight fragments per stage
+constexpr int kBgVFrags = kMfmaTile / 16;        // v fragments per stage (hi or lo)
+constexpr int kBgWLoads = kBgWFrags / kBgWaves;  // weight fragments per wave per stage
+static_assert(kMfmaTile == 128 && kBgWFrags % kBgWaves == 0, "transposed GEMM tiles");
+
+template <bool HL>
+constexpr int bg_stage_bytes() { return (kBgWFrags + kBgVFrags * (HL ? 2 : 1)) * 1024; }
+
+template <int MODE, bool LORA, bool HILO>
+__global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
+  constexpr bool kHiLo = HILO && MODE == kDown;
+  constexpr int kStageBytes = bg_stage_bytes<kHiLo>();
+  constexpr int kVBase = kBgWFrags * 1024;  // v fragments follow the weights in a stage
+  __shared__ __attribute__((aligned(1024))) unsigned char s_buf[2 * kStageBytes];
+  const int I = a.I, H = a.H;
+  const int ncols = MODE == kDown ? I : H;      // n
+  const int nrows = MODE == kDown ? H : 2 * I;  // m
+  const int nkb = ncols / 32;                   // 32-column blocks of a row tile
+  const int ntile = (ncols + kBgBN - 1) / kBgBN;
+  const int item = blockIdx.x / ntile, nt = blockIdx.x - item * ntile;
+  if (item >= *a.n_items) return;
+  const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
+  const int cnt = a.counts[e] - m0;
+  const int M = cnt < kMfmaTile ? cnt : kMfmaTile, base = a.offsets[e] + m0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // the wave's 64 rows x 64 columns
+  const int nsteps = nrows / 32;
+  const int n0 = nt * kBgBN;
+  const uint16_t* W = MODE == kDown ? a.w_down : a.w_gate_up;
+  const size_t rt0 = (size_t)e * (nrows / 16);
+
+  // weights: this wave's fragments f = kBgWLoads * wave + i of a stage (row
+  // tile f / 8 of the stage, column block f % 8 of the window; blocks past
+  // ncols load the last valid block, whose columns are never stored)
+  const uint16_t* wsrc[kBgWLoads];
+#pragma unroll
+  for (int i = 0; i < kBgWLoads; ++i) {
+    const int f = kBgWLoads * wave + i;
+    const int kb = min(n0 / 32 + (f & 7), nkb - 1);
+    wsrc[i] = W + ((rt0 + (f >> 3)) * nkb + kb) * 512 + lane * 8;
+  }
+  const size_t wstep = (size_t)2 * nkb * 512;  // elements per 32-m stage (two row tiles)
+  // v rows: thread t brings row p = t / 4 (a valid row when p >= M, times 0),
+  // m = 8 (t % 4) .. +7 of each stage
+  const int vp = tid >> 2, vg = tid & 3;
+  const int vpc = vp < M ? vp : 0;
+  const float* vrow;
+  float vw;
+  if (MODE == kDown) {
+    const int slot = a.perm[base + vpc];
+    vrow = a.d_out + (size_t)(slot / a.k) * H + 8 * vg;
+    vw = vp < M ? a.wts[slot] : 0.f;
+  } else {
+    vrow = a.gu + (size_t)(base + vpc) * 2 * I + 8 * vg;
+    vw = vp < M ? 1.f : 0.f;
+  }
+  const int v_off = kVBase + (vp >> 4) * 1024 + (16 * vg + (vp & 15)) * 16;  // MFMA operand order
+  u32x4_t wr[kBgWLoads];
+  f32x4_t v0, v1;
+  auto load = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < kBgWLoads; ++i) wr[i] = ld16_stream(wsrc[i] + st * wstep);
+    v0 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * st);
+    v1 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * st + 4);
+  };
+  auto store = [&](int buf) {
+    unsigned char* sb = s_buf + buf * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kBgWLoads; ++i)
+      *reinterpret_cast<u32x4_t*>(sb + (kBgWLoads * wave + i) * 1024 + lane * 16) = wr[i];
+    const float t[8] = {vw * v0[0], vw * v0[1], vw * v0[2], vw * v0[3],
+                        vw * v1[0], vw * v1[1], vw * v1[2], vw * v1[3]};
+    u32x4_t hi, lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = pack_bf16x2(t[2 * i], t[2 * i + 1]);
+      lo[i] = pack_bf16x2(t[2 * i] - bf16lo(hi[i]), t[2 * i + 1] - bf16hi(hi[i]));
+    }
+    *reinterpret_cast<u32x4_t*>(sb + v_off) = hi;
+    if constexpr (kHiLo) *reinterpret_cast<u32x4_t*>(sb + v_off + kBgVFrags * 1024) = lo;
+  };
+  // transposing reads of the weight fragments: lane (s, G) supplies row
+  // 8G + (s >> 2) (row tile G >> 1 of the stage, row (8G + (s >> 2)) & 15 in
+  // it) and 4 columns from 16 (t & 1) + 4 (s & 3) of column block t >> 1 of
+  // the wave's window (element (16 g' + r') * 8 + 4 h of the fragment)
+  const int s_ = lane & 15, G = lane >> 4;
+  const int rloc = (8 * G + (s_ >> 2)) & 15, rtl = G >> 1;
+  int tr_byte[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int kbw = 2 * wn + (t >> 1);  // column block within the window
+    const int gq = 2 * (t & 1) + ((s_ & 3) >> 1), h = s_ & 1;
+    tr_byte[t] = (rtl * 8 + kbw) * 1024 + (16 * gq + rloc) * 16 + 8 * h;
+  }
+  const int nj = min(max((M - wm * 64 + 15) / 16, 0), 4);  // the wave's row tiles holding rows of the item
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    store(buf);
+    __syncthreads();  // stage st in LDS; every wave is done with stage st - 1's buffer
+    if (st + 1 < nsteps) load(st + 1);  // in flight during this stage's MFMAs
+    if (nj > 0) {
+      const unsigned char* sb = s_buf + buf * kStageBytes;
+      u32x4_t bop[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + tr_byte[t]));
+        const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + tr_byte[t] + 64));
+        bop[t] = u32x4_t{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                         (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                         (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                         (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nj) break;
+        const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(sb + kVBase + (wm * 4 + i) * 1024 + lane * 16);
+        u32x4_t al;
+        if constexpr (kHiLo)
+          al = *reinterpret_cast<const u32x4_t*>(sb + kVBase + (kBgVFrags + wm * 4 + i) * 1024 + lane * 16);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[i][t] = mfma16(ah, bop[t], acc[i][t]);
+          if constexpr (kHiLo) acc[i][t] = mfma16(al, bop[t], acc[i][t]);
+        }
+      }
+    }
+  }
+  // lane (r, g) holds D[row 4g + q][column r] of tile (i, t): row
+  // wm * 64 + 16 i + 4g + q of the item, column n0 + wn * 64 + 16 t + r
+  const int r = lane & 15, g = lane >> 4;
+  if constexpr (LORA) {  // s A^T z, as in bwd_t_kernel
+    const float* la = (MODE == kDown ? a.la_down + (size_t)e * 16 * I : a.la_gate_up + (size_t)e * 16 * H);
+    const float* zb = MODE == kDown ? a.z_down : a.z_gate_up;
+    f32x4_t aq[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = min(n0 + wn * 64 + 16 * t + r, ncols - 1);  // columns past ncols are never stored
+#pragma unroll
+      for (int c = 0; c < 4; ++c) aq[t][c] = la[(size_t)(4 * g + c) * ncols + n];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int prow = wm * 64 + 16 * i + r;
+      const f32x4_t zp = prow < M ? ld4f(zb + (size_t)(base + prow) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) add_scaled(acc[i][t], lora_tile(zp, aq[t]), a.lora_scale);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = wm * 64 + 16 * i + 4 * g + q;
+      if (m >= M) continue;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int n = n0 + wn * 64 + 16 * t + r;
+        if (n >= ncols) continue;
+        if (MODE == kDown) {
+          float* gp = a.gu + (size_t)(base + m) * 2 * I;
+          const float gv = gp[n], uv = gp[I + n];
+          const float sg = 1.0f / (1.0f + __expf(-gv));
+          const float dh = acc[i][t][q];
+          gp[n] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
+          gp[I + n] = dh * (gv * sg);
+        } else {
+          a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[i][t][q];
         }
       }
     }
@@ -626,6 +811,12 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdArgs a) {
   *reinterpret_cast<f32x4_t*>(dx) = acc;
 }
 
+template <int MODE, bool LORA, bool HILO>
+hipError_t launch_bg(const BwdArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, LORA, HILO>), grid, dim3(kBgThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
@@ -635,7 +826,6 @@ hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
   const dim3 grid(a.max_items * ((down ? a.I : a.H) / 32));
-  const dim3 grid_ns(a.max_items * ((down ? a.I : a.H) / (32 * kBwdStrips)));
   if (a.nf4) {  // frozen 4-bit base: no weight gradients
     if (a.wgrad) return hipErrorInvalidValue;
     if (down) {
@@ -651,16 +841,16 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  if (a.row_tiles == kBwdRowTiles && !a.lora) {
-    constexpr int R = kBwdRowTiles, NS = kBwdStrips;
-    if ((down ? a.I : a.H) % (32 * NS)) return hipErrorInvalidValue;
-    if (down && a.wgrad)
-      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, true, false, R, NS>), grid_ns, dim3(64), 0, s, a);
-    else if (down)
-      hipLaunchKernelGGL((bwd_t_kernel<kDown, false, false, false, R, NS>), grid_ns, dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL((bwd_t_kernel<kGateUp, false, false, false, R, NS>), grid_ns, dim3(64), 0, s, a);
-    return hipGetLastError();
+  if (a.row_tiles == kMfmaTile / 16) {  // the MFMA forward's 128-row items
+    const dim3 gg(a.max_items * (((down ? a.I : a.H) + kBgBN - 1) / kBgBN));
+    const bool hl = down && (a.lora || a.wgrad);
+    hipError_t e;
+    if (down && a.lora) e = launch_bg<kDown, true, true>(a, gg, s);
+    else if (down && hl) e = launch_bg<kDown, false, true>(a, gg, s);
+    else if (down) e = launch_bg<kDown, false, false>(a, gg, s);
+    else if (a.lora) e = launch_bg<kGateUp, true, false>(a, gg, s);
+    else e = launch_bg<kGateUp, false, false>(a, gg, s);
+    return e;
   }
   if (a.row_tiles != 1) return hipErrorInvalidValue;
   if (down) {

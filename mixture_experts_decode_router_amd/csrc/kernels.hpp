@@ -8,17 +8,6 @@ namespace moe {
 // Decode/prefill token-tile height of the skinny expert kernels: one MFMA
 // column block of 16 tokens.
 constexpr int kSkinnyTile = 16;
-// 16-row tiles per work item of the backward's transposed GEMVs after an
-// MFMA forward (its rows re-bucketed into items of 16 * kBwdRowTiles rows).
-#ifndef MOE_BWD_ROW_TILES
-#define MOE_BWD_ROW_TILES 4
-#endif
-constexpr int kBwdRowTiles = MOE_BWD_ROW_TILES;
-// ... and 32-column strips per work unit there (H and I are multiples of 128)
-#ifndef MOE_BWD_STRIPS
-#define MOE_BWD_STRIPS 2
-#endif
-constexpr int kBwdStrips = MOE_BWD_STRIPS;
 // Token-tile height of the LDS-tiled MFMA expert kernels (large groups).
 #ifndef MOE_MFMA_TILE
 #define MOE_MFMA_TILE 128
@@ -168,7 +157,8 @@ struct BwdArgs {
   const float* codebook;
   float* gu;                  // [N][2I]: g, u kept by the forward, then d_g, d_u
   float* d_xs;                // [N][H], flat-slot order (may reuse y's memory)
-  int row_tiles;              // 16-row tiles per work item: 1, or kBwdRowTiles (bf16, no adapters)
+  int row_tiles;              // 16-row tiles per work item: 1 (16-row GEMVs), or kMfmaTile / 16 after an
+                              // MFMA forward (the tiled transposed GEMMs; bf16 weights)
   // LoRA (lora true): the adapters, the forward's U = A x / A h, the backward's
   // z = B^T v, and the adapter gradients (same shapes as the adapters)
   bool lora;

@@ -134,10 +134,12 @@ __device__ __forceinline__ void rank16_reduce(int nb, int M, float* out, f32x4_t
 // is overwritten), so the adapter gradients carry no bf16 rounding of h.
 __global__ __launch_bounds__(64 * kWaves) void lora_bt_kernel(BwdArgs a, int mode) {
   __shared__ f32x4_t s_part[kWaves][64];
-  const int item = blockIdx.x;
+  // one workgroup per 16-row sub-tile of a work item (row_tiles per item)
+  const int item = blockIdx.x / a.row_tiles, sub = blockIdx.x - item * a.row_tiles;
   if (item >= *a.n_items) return;  // uniform over the workgroup
-  const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
+  const int e = a.items[2 * item], m0 = a.items[2 * item + 1] + 16 * sub;
   const int c = a.counts[e] - m0;
+  if (c <= 0) return;  // a sub-tile past the item's rows
   const int M = c < 16 ? c : 16, base = a.offsets[e] + m0;
   const bool down = mode == 0;
   const int H = a.H, I = a.I;
@@ -288,7 +290,8 @@ hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s) {
   const int Nn = down ? a.H : 2 * a.I;
   if (Nn % 64 || Nn > 64 * kMaxBlocks * kWaves || a.I % 64 || a.I > 64 * kMaxBlocks * kWaves)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lora_bt_kernel, dim3(a.max_items), dim3(64 * kWaves), 0, s, a, down ? 0 : 1);
+  if (a.row_tiles < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lora_bt_kernel, dim3(a.max_items * a.row_tiles), dim3(64 * kWaves), 0, s, a, down ? 0 : 1);
   return hipGetLastError();
 }
 

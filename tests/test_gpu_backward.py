@@ -164,15 +164,17 @@ def test_backward_nf4_skewed_many_rows_per_expert(cb):
     assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
 
 
-def test_backward_at_prefill_sizes():
-    # T*k = 32*E: the training forward runs the MFMA prefill kernels, which
+@pytest.mark.parametrize("T", [256, 1024])
+def test_backward_at_prefill_sizes(T):
+    # T*k >= 32*E: the training forward runs the MFMA prefill kernels, which
     # also keep g, u (outputs the same bits as an inference forward); the
-    # backward re-buckets into 16-row items and matches the oracle's chain
-    # rule, its rows the same bits as a decode-sized call's; with LoRA
-    # adapters the 16-row kernels run throughout
-    inp = workload("tiny", 256)
+    # backward's tiled transposed GEMMs run over the same 128-row items
+    # (several per expert at T = 1024) and match the oracle's chain rule,
+    # its rows the same bits as a decode-sized call's (16-row GEMVs); also
+    # with the expert-weight gradients and with LoRA adapters
+    inp = workload("tiny", T)
     d_out = d_out_for(inp.T, inp.H, seed=29)
-    inf = layer("tiny", 256)
+    inf = layer("tiny", 1024)
     lay = inf.with_options(train=True)
     x = inf.upload_x(inp.x)
     a = inf.forward(x)
@@ -214,6 +216,8 @@ def test_backward_at_prefill_sizes():
     say("[gpu]   with LoRA max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
     assert errs["d_x"] <= TOL_BF16 and errs["d_w"] <= TOL_BF16
     assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
+    s_x, s_w, _ = gpu_backward_lora(ll, inp.x[:24], d_out[:24])
+    assert np.array_equal(s_x, d_x[:24]) and np.array_equal(s_w, d_w[:24])
 
 
 def test_training_forward_gives_the_same_output():
