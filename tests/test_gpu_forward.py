@@ -73,9 +73,10 @@ def test_forward_decode_sweep(T):
 
 @pytest.mark.parametrize("T", [1, 4, 8, 16])
 def test_forward_decode_sweep_4bit(T):
-    """4-bit Qwen layer at decode sizes: the small grids of T <= 8 take the
-    down kernel's three-block iterations, T = 16 (and q48q) the one-block
-    form."""
+    """4-bit Qwen layer at decode sizes: the down kernel's grid of (E + T k /
+    16) x 16 workgroups stays within the small-grid bound (1024) up to T = 7,
+    so T = 1 and 4 take its three-block iterations; T = 8, 16 (and q48q) the
+    one-block form."""
     inp = workload("q48q", T)
     say(f"[gpu] forward 4-bit sweep T={T}")
     out, views = run_forward(layer("q48q", 64), inp.x)
