@@ -119,9 +119,8 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
 bool is_nf4(const moe_config& c) { return c.wfmt == MOE_W_NF4_B64 || c.wfmt == MOE_W_NF4_B64_TILED; }
 
 // Large groups (on average >= 32 rows per expert) go to the LDS-tiled MFMA
-// kernels (tiled bf16 weights only).  A call with LoRA adapters runs on the
-// 16-row kernels at every size: those carry the adapter epilogues, and give
-// the same per-row bits.
+// kernels (tiled bf16 weights only, with or without LoRA adapters); they
+// give the same per-row bits as the 16-row kernels.
 bool mfma_path_for(const moe_config& c, int T) {
   return c.wfmt == MOE_W_BF16_TILED && (long)T * c.top_k >= 32L * c.n_experts;
 }
@@ -227,12 +226,16 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   pa.chunk_base = at<int32_t>(ws, L.chunks);
   pa.live = live;
   pa.k = c.top_k;
-  // a small batch is bucketed by the router's select workgroup
+  // most experts hold rows: the 16-row kernels find their slots themselves
+  // (no bucketing launch); else a small batch is bucketed by the router's
+  // select workgroup, a larger one by the bucketing kernel
+  const bool direct = !mfma_path && !is_nf4(c) && !w.lora && !c.train && N >= 2 * c.n_experts &&
+                      N <= moe::kDirectMaxN;
   bool fused = false;
-  if ((e = moe::launch_route(ra, at<float>(ws, L.route), s, &pa, &fused, rnode)) != hipSuccess)
+  if ((e = moe::launch_route(ra, at<float>(ws, L.route), s, direct ? nullptr : &pa, &fused, rnode)) != hipSuccess)
     return hip_fail(e, "route launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  if (!fused && (e = moe::launch_permute(pa, s)) != hipSuccess) return hip_fail(e, "permute launch");
+  if (!direct && !fused && (e = moe::launch_permute(pa, s)) != hipSuccess) return hip_fail(e, "permute launch");
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 
   moe::ExpertArgs ea{};
@@ -257,6 +260,15 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
   ea.q_down = w.q_down;
   ea.s_down = w.s_down;
   ea.codebook = w.codebook;
+  if (direct) {
+    ea.ids = ra.ids;
+    ea.N = N;
+    ea.live = live;
+    ea.r_counts = pa.counts;
+    ea.r_offsets = pa.offsets;
+    ea.r_perm = pa.perm;
+    ea.r_pos = pa.pos;
+  }
   const bool nf4 = is_nf4(c), tiled = is_tiled(c);
   moe::LoraAArgs la{};
   if (w.lora) {  // adapter terms in the expert kernels' epilogues, at every size

@@ -213,6 +213,292 @@ __global__ __launch_bounds__(64) void down_bf16(ExpertArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ direct form
+// When most experts hold rows (at decode sizes, 2E <= N <= kDirectMaxN
+// slots), the grid covers every expert and no work list is formed: the wave
+// for (expert e, column tile) finds e's slots itself by scanning the N
+// routed ids, so no bucketing kernel runs before it.  Its first batch of
+// weights depends on e only and is in flight from the wave's start, and its
+// chain of dependent loads before the first MFMA is ids -> token rows
+// instead of work list -> counts/offsets -> perm -> token rows.  Lane l holds
+// P consecutive slots (P a multiple of 4, at most 16); e's slots in ascending
+// order are ranked by a wave prefix sum of the per-lane match counts, and
+// e's offset in sorted-slot order is the number of slots routed to lower
+// experts: the values the bucketing kernel forms, so h keeps its sorted-slot
+// layout, and one wave per expert records counts, offsets, perm and pos.  An
+// expert takes its rows 32 at a time (two 16-row MFMA column blocks per
+// weight load, half as many k-steps per batch of loads, which keeps the
+// register count of the one-block pass), the last pass 16 if no more
+// remain; each 16-row block gets the same MFMA chain as in the work-list
+// kernels, so rows keep their bits.
+struct SlotList {
+  int count, off;
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// e's live slots, ascending, into s_slot[0 .. count); every lane gets count
+// and the offset.  ids is read in whole 16-byte chunks (the workspace pads
+// the array to a multiple of 16 bytes); entries at or past N are ignored.
+__device__ __forceinline__ SlotList scan_slots(const ExpertArgs& a, int e, int lane, int* s_slot) {
+  const int N = a.live ? min(a.N, *a.live * a.k) : a.N;
+  const int P = (((N + 63) >> 6) + 3) & ~3;  // <= 16 for N <= kDirectMaxN
+  const int s0 = lane * P;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  u32x4_t v[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = (4 * c < P && s0 + 4 * c < N) ? ld16(a.ids + s0 + 4 * c) : zero;
+  uint32_t m = 0u;
+  int lt = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int id = (int)v[q >> 2][q & 3];
+    const int ce = id < 0 ? 0 : (id >= a.E ? a.E - 1 : id);  // as the bucketing clamps
+    const bool ok = q < P && s0 + q < N;
+    m |= (ok && ce == e ? 1u : 0u) << q;
+    lt += ok && ce < e ? 1 : 0;
+  }
+  const int cnt = __popc(m);
+  const int incl = wave_incl_scan(cnt, lane);
+  const int lti = wave_incl_scan(lt, lane);
+  SlotList sl;
+  sl.count = __builtin_amdgcn_readlane(incl, 63);
+  sl.off = __builtin_amdgcn_readlane(lti, 63);
+  int rk = incl - cnt;
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if ((m >> q) & 1u) s_slot[rk++] = s0 + q;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return sl;
+}
+
+// the bucketing of expert e as the bucketing kernel writes it (work list aside)
+__device__ __forceinline__ void publish_slots(const ExpertArgs& a, int e, const SlotList& sl, int lane,
+                                              const int* s_slot) {
+  if (lane == 0) {
+    a.r_counts[e] = sl.count;
+    a.r_offsets[e] = sl.off;
+    if (e == a.E - 1) a.r_offsets[a.E] = sl.off + sl.count;
+  }
+  for (int i = lane; i < sl.count; i += 64) {
+    const int s = s_slot[i];
+    a.r_perm[sl.off + i] = s;
+    if (a.r_pos) a.r_pos[s] = sl.off + i;
+  }
+}
+
+// rows m0 .. m0 + 16 RT - 1 of expert e's list through one pass over its
+// gate/up weights (wg: this lane's first gate chunk; its up chunk is wuo
+// elements further).  PRE: the first U k-steps of weights are already in
+// pg / pu (issued before the slot scan).
+template <int U, int RT, bool PRE = false>
+__device__ __forceinline__ void gate_up_pass(const ExpertArgs& a, const uint16_t* wg, size_t wuo, int wstep,
+                                             const SlotList& sl, int m0, const int* s_slot, int n0, int lane,
+                                             const u32x4_t* pg = nullptr, const u32x4_t* pu = nullptr) {
+  const int H = a.H, I = a.I, r = lane & 15, g = lane >> 4;
+  bool rv[RT];
+  const uint16_t* xr[RT];
+#pragma unroll
+  for (int j = 0; j < RT; ++j) {
+    const int i = m0 + 16 * j + r;
+    rv[j] = i < sl.count;
+    const int tok = rv[j] ? s_slot[i] / a.k : 0;
+    xr[j] = a.x + (size_t)tok * H + g * 8;
+  }
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  f32x4_t accg[RT], accu[RT];
+#pragma unroll
+  for (int j = 0; j < RT; ++j) accg[j] = accu[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto batch = [&](const u32x4_t* ga, const u32x4_t* ua, int kk) {
+    u32x4_t xb[RT][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < RT; ++j) xb[j][u] = rv[j] ? ld16(xr[j] + kk + u * 32) : zero;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int j = 0; j < RT; ++j) {
+        accg[j] = mfma16(ga[u], xb[j][u], accg[j]);
+        accu[j] = mfma16(ua[u], xb[j][u], accu[j]);
+      }
+    }
+  };
+  int kk0 = 0;
+  if constexpr (PRE) {
+    batch(pg, pu, 0);
+    __builtin_amdgcn_sched_barrier(0);  // the loop's loads stay below: pg, pu and them are not live together
+    kk0 = 32 * U;
+  }
+  for (int kk = kk0; kk < H; kk += 32 * U) {
+    u32x4_t ga[U], ua[U];
+    const size_t wo = (size_t)(kk / 32) * wstep;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ga[u] = ld16_stream(wg + wo + u * wstep);
+      ua[u] = ld16_stream(wg + wuo + wo + u * wstep);
+    }
+    batch(ga, ua, kk);
+  }
+#pragma unroll
+  for (int j = 0; j < RT; ++j) {
+    if (rv[j]) {
+      float hv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hv[q] = silu(accg[j][q]) * accu[j][q];
+      u32x2_t pk = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+      *reinterpret_cast<u32x2_t*>(a.h + (size_t)(sl.off + m0 + 16 * j + r) * I + n0 + 4 * g) = pk;
+    }
+  }
+}
+
+// k-steps per batch of weight loads in the direct kernels' one-block pass
+// (the first batch is issued before the slot scan; eight would not fit the
+// register budget of four waves per SIMD with it)
+constexpr int kDU = 4;
+
+template <int U, bool TILED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void gate_up_direct(ExpertArgs a) {
+  __shared__ int s_slot[kDirectMaxN];
+  const int ntile = a.I / 64;
+  const int wave = blockIdx.x % kSub, bq = blockIdx.x / kSub;
+  const int e = bq / ntile, nt = bq - e * ntile;
+  const int H = a.H, I = a.I;
+  const int lane = threadIdx.x;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = nt * 64 + wave * 16;
+  const uint16_t* wg = TILED ? a.w_gate_up + (((size_t)e * (2 * I / 16) + n0 / 16) * (H / 32) * 64 + lane) * 8
+                             : a.w_gate_up + ((size_t)e * 2 * I + n0 + r) * H + g * 8;
+  const size_t wuo = TILED ? (size_t)(I / 16) * (H / 32) * 512 : (size_t)I * H;  // up rows after the gate rows
+  const int wstep = TILED ? 512 : 32;
+  // the first batch of weights depends on the expert only: it is in flight
+  // during the slot scan (and dropped if the expert has no rows)
+  u32x4_t pg[U], pu[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    pg[u] = ld16_stream(wg + u * wstep);
+    pu[u] = ld16_stream(wg + wuo + u * wstep);
+  }
+  const SlotList sl = scan_slots(a, e, lane, s_slot);
+  if (nt == 0 && wave == 0) publish_slots(a, e, sl, lane, s_slot);
+  if (sl.count <= kTile) {
+    if (sl.count > 0) gate_up_pass<U, 1, true>(a, wg, wuo, wstep, sl, 0, s_slot, n0, lane, pg, pu);
+    return;
+  }
+  for (int m0 = 0; m0 < sl.count; m0 += 2 * kTile) {
+    if (sl.count - m0 > kTile)
+      gate_up_pass<U / 2, 2>(a, wg, wuo, wstep, sl, m0, s_slot, n0, lane);
+    else
+      gate_up_pass<U, 1>(a, wg, wuo, wstep, sl, m0, s_slot, n0, lane);
+  }
+}
+
+// rows m0 .. m0 + 16 RT - 1 of expert e's list through one pass over its
+// down weights (w0: this lane's first chunk of the wave's first 16-column
+// block; block b's chunks are wb elements further).  PRE: the first U
+// k-steps of weights are already in pre.
+template <int U, int RT, int CB, bool PRE = false>
+__device__ __forceinline__ void down_pass(const ExpertArgs& a, const uint16_t* w0, size_t wb, int wstep,
+                                          const SlotList& sl, int m0, const int* s_slot, int c0, int lane,
+                                          const u32x4_t* pre = nullptr) {
+  const int H = a.H, I = a.I, r = lane & 15, g = lane >> 4;
+  bool rv[RT];
+  const uint16_t* hr[RT];
+#pragma unroll
+  for (int j = 0; j < RT; ++j) {
+    const int i = m0 + 16 * j + r;
+    rv[j] = i < sl.count;
+    hr[j] = a.h + (size_t)(sl.off + (rv[j] ? i : 0)) * I + g * 8;
+  }
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  f32x4_t acc[RT][CB];
+#pragma unroll
+  for (int j = 0; j < RT; ++j)
+#pragma unroll
+    for (int b = 0; b < CB; ++b) acc[j][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // wv[b * U + u]: block b, k-step u of the batch
+  auto batch = [&](const u32x4_t* wv, int kk) {
+    u32x4_t hb[RT][U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < RT; ++j) hb[j][u] = rv[j] ? ld16(hr[j] + kk + u * 32) : zero;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < RT; ++j)
+#pragma unroll
+        for (int b = 0; b < CB; ++b) acc[j][b] = mfma16(wv[b * U + u], hb[j][u], acc[j][b]);
+  };
+  int kk0 = 0;
+  if constexpr (PRE) {
+    batch(pre, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    kk0 = 32 * U;
+  }
+  for (int kk = kk0; kk < I; kk += 32 * U) {
+    u32x4_t wv[CB * U];
+    const size_t wo = (size_t)(kk / 32) * wstep;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < CB; ++b) wv[b * U + u] = ld16_stream(w0 + b * wb + wo + u * wstep);
+    batch(wv, kk);
+  }
+#pragma unroll
+  for (int j = 0; j < RT; ++j) {
+    if (rv[j]) {
+      float* yrow = a.y + (size_t)s_slot[m0 + 16 * j + r] * H + c0 + 4 * g;
+#pragma unroll
+      for (int b = 0; b < CB; ++b) *reinterpret_cast<f32x4_t*>(yrow + 16 * b) = acc[j][b];
+    }
+  }
+}
+
+constexpr int kDnCB = 2;  // 16-column blocks of the output per wave (direct down)
+
+// wave (e, cw) computes output columns cw * 16 CB .. + 16 CB - 1 of expert
+// e's rows; U2: k-steps per batch of loads in the two-block pass
+template <int U, int U2, int CB, bool TILED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void down_direct(ExpertArgs a) {
+  __shared__ int s_slot[kDirectMaxN];
+  const int ncw = a.H / (16 * CB);
+  const int e = blockIdx.x / ncw, cw = blockIdx.x - e * ncw;
+  const int H = a.H, I = a.I;
+  const int lane = threadIdx.x;
+  const int r = lane & 15, g = lane >> 4;
+  const int c0 = cw * 16 * CB;
+  const uint16_t* w0 = TILED ? a.w_down + (((size_t)e * (H / 16) + c0 / 16) * (I / 32) * 64 + lane) * 8
+                             : a.w_down + ((size_t)e * H + c0 + r) * I + g * 8;
+  const size_t wb = TILED ? (size_t)(I / 32) * 512 : (size_t)16 * I;
+  const int wstep = TILED ? 512 : 32;
+  u32x4_t pre[CB * U];  // first batch, in flight during the slot scan
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int b = 0; b < CB; ++b) pre[b * U + u] = ld16_stream(w0 + b * wb + u * wstep);
+  const SlotList sl = scan_slots(a, e, lane, s_slot);
+  if (sl.count <= kTile) {
+    if (sl.count > 0) down_pass<U, 1, CB, true>(a, w0, wb, wstep, sl, 0, s_slot, c0, lane, pre);
+    return;
+  }
+  for (int m0 = 0; m0 < sl.count; m0 += 2 * kTile) {
+    if (sl.count - m0 > kTile)
+      down_pass<U2, 2, CB>(a, w0, wb, wstep, sl, m0, s_slot, c0, lane);
+    else
+      down_pass<U, 1, CB>(a, w0, wb, wstep, sl, m0, s_slot, c0, lane);
+  }
+}
+
 // ------------------------------------------------------------------ 4-bit
 // A weight is codebook[code] * absmax(row, 64-block), the codebook holding
 // 16 fp32 values.  Each entry enters the MFMA as two bf16 parts, hi =
@@ -524,11 +810,35 @@ hipError_t launch_down_t(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t 
                : launch_u(a.I, down_bf16<8, false, LORA>, down_bf16<4, false, LORA>, gw, s, a, 64);
 }
 
+// the direct form covers bf16 weights without adapters or kept pre-activations
+bool direct_ok(const ExpertArgs& a, bool nf4) {
+  return !nf4 && !a.lora && !a.gu && a.N >= 1 && a.N <= kDirectMaxN && a.H % (32 * kDU) == 0 &&
+         a.I % (32 * kDU) == 0;
+}
+
 hipError_t launch_gate_up(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
+  if (a.ids) {
+    if (!direct_ok(a, nf4)) return hipErrorInvalidValue;
+    const dim3 gw(a.E * (a.I / 64) * kSub);
+    if (tiled)
+      hipLaunchKernelGGL((gate_up_direct<kDU, true>), gw, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((gate_up_direct<kDU, false>), gw, dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   return a.lora ? launch_gate_up_t<true>(a, nf4, tiled, s) : launch_gate_up_t<false>(a, nf4, tiled, s);
 }
 
 hipError_t launch_down(const ExpertArgs& a, bool nf4, bool tiled, hipStream_t s) {
+  if (a.ids) {
+    if (!direct_ok(a, nf4)) return hipErrorInvalidValue;
+    const dim3 gw(a.E * (a.H / (16 * kDnCB)));
+    if (tiled)
+      hipLaunchKernelGGL((down_direct<kDU, kDU / 2, kDnCB, true>), gw, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((down_direct<kDU, kDU / 2, kDnCB, false>), gw, dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   return a.lora ? launch_down_t<true>(a, nf4, tiled, s) : launch_down_t<false>(a, nf4, tiled, s);
 }
 

@@ -79,6 +79,9 @@ struct PermuteArgs {
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 size_t permute_scratch_ints(int n_max, int E);
 
+// Largest slot count (T * k) of the direct form of the 16-row expert kernels.
+constexpr int kDirectMaxN = 1024;
+
 struct ExpertArgs {
   // routing (device)
   const int32_t* counts;
@@ -109,6 +112,18 @@ struct ExpertArgs {
   const float* u_down;        // fp32 [N][16], sorted-slot order
   float* gu;                  // or null; else the bf16 gate/up kernels also keep g and u here:
                               // fp32 [N][2I] (g, then u), sorted-slot order
+  // direct form of the 16-row bf16 kernels (ids set; no LoRA, gu null): no
+  // work list, each wave finds its expert's slots among the first
+  // min(N, *live * k) routed ids (N <= kDirectMaxN), and the gate/up kernel
+  // records the bucketing in r_* (counts [E], offsets [E+1], perm [N], pos
+  // [N] or null) as the bucketing kernel would, work list aside
+  const int32_t* ids;         // [N] or null (work-list form)
+  int N;
+  const int32_t* live;        // device row count, or null
+  int32_t* r_counts;
+  int32_t* r_offsets;
+  int32_t* r_perm;
+  int32_t* r_pos;
 };
 
 // U[p][:] = A[e] src-row(p) for every row of the skinny work list (rank 16)

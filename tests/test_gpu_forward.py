@@ -101,6 +101,8 @@ def test_forward_decode_sweep_4bit(T):
     dict(T=4, H=256, E=16, k=16, I=128, wfmt="bf16"),      # small batch bucketed by the router: 64 slots
     dict(T=3, H=512, E=256, k=8, I=128, wfmt="bf16"),      # ... with the largest expert count
     dict(T=7, H=256, E=48, k=6, I=128, wfmt="bf16"),       # ... eight-wave select, E not a multiple of 64
+    dict(T=11, H=256, E=16, k=3, I=128, wfmt="bf16"),     # direct form, 33 slots (ragged scan tail)
+    dict(T=64, H=256, E=16, k=16, I=128, wfmt="bf16"),    # 1024 slots: the direct form's largest (row-major)
     dict(T=29, H=512, E=16, k=2, I=256, wfmt="nf4", cb="random"),  # codebook of arbitrary fp32 values
     dict(T=6, H=256, E=16, k=4, I=384, wfmt="nf4", cb="random"),   # ... small grid (three-block down)
 ])
@@ -198,3 +200,23 @@ def test_forward_row_subset_is_bit_identical():
     assert torch.equal(a[:13], b)
     c = lay.forward(lay.upload_x(inp.x[40:41]))
     assert torch.equal(a[40:41], c)
+
+
+@pytest.mark.parametrize("tiled", [True, False])
+def test_direct_form_many_rows_per_expert(tiled):
+    """Direct form (2E <= T k <= 1024 slots, no work list): every token
+    identical, so k experts get all 40 rows (a two-block pass, then a
+    one-block pass).  Parity with the oracle, routing arrays as the bucketing
+    kernel writes them, and each row bit-identical to the same token alone
+    (T = 1 runs the work-list kernels)."""
+    inp = S.make_small(40, 256, 32, 8, 256, seed=11, wfmt="bf16", bias=True)
+    inp.x[:] = inp.x[5]
+    say(f"[gpu] direct form, 40 identical rows tiled={tiled}")
+    lay = MoELayer(inp, t_max=40, tiled=tiled)
+    out, views = run_forward(lay, inp.x)
+    ref_out, ref = O.forward_batched(inp)
+    check_views(views, ref)
+    assert (views["counts"].cpu().numpy() == 40).sum() == 8
+    assert rel_err(out.cpu().numpy(), ref_out) <= TOL_BF16
+    one = lay.forward(lay.upload_x(inp.x[:1]))
+    assert torch.equal(out, one.expand_as(out))
