@@ -45,6 +45,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def bucketing_form(wfmt, T, E, k, row_major=False, lora=False, train=False):
+    """Where the library buckets the routed slots for a forward of T rows (the
+    rule of its forward): "direct" -- the 16-row expert kernels scan the ids
+    themselves and no bucketing kernel runs (bf16 weights, no adapters, no kept
+    pre-activations, 2E <= T k <= 1024 slots below the MFMA path); "router" --
+    the router's select workgroup (T <= 8, T k <= 64); else "kernel"."""
+    n = T * k
+    mfma = wfmt == "bf16" and not row_major and n >= 32 * E
+    if not mfma and wfmt == "bf16" and not lora and not train and 2 * E <= n <= 1024:
+        return "direct"
+    if T <= 8 and n <= 64:
+        return "router"
+    return "kernel"
+
+
 def bytes_model(H, I, E, k, T, n_act, wfmt):
     """Algorithmic HBM bytes of each kernel and of the block (each weight of an
     active expert read once, activations read once, outputs written once)."""
@@ -377,7 +392,10 @@ def main():
         for j, n in enumerate(names):
             stage_us[n] += L.hip_event_elapsed_ms(e[j], e[j + 1]) * 1e3 / S_
     L.hip_events_destroy(evs)
-    log("[bench] stage us: " + ", ".join(f"{n} {v:.1f}" for n, v in stage_us.items()))
+    bucketing = bucketing_form(inp.wfmt, T, E, k, row_major=args.row_major)
+    log("[bench] stage us: " + ", ".join(f"{n} {v:.1f}" for n, v in stage_us.items())
+        + ("" if bucketing == "kernel" else
+           f" (bucketing: {bucketing}; no bucketing kernel, the permute figure is the cost of an event pair)"))
 
     # ---------------- per-replay spread: one event between consecutive replays
     R_ = args.stage_steps
@@ -631,6 +649,7 @@ def main():
             "mfma_frac": round(model["flops"] / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
             "n_active_experts": n_act,
             "stage_us": {n: round(v, 2) for n, v in stage_us.items()},
+            "bucketing": bucketing,
             "gpu_event_us_per_step": round(gpu_ms * 1e3 / args.steps, 2),
             "replay_us": replay_pct,
             "cold_us_per_step": round(cold["read"], 2) if cold else None,
