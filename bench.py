@@ -602,7 +602,7 @@ def main():
             mj = json.load(open(mpath))
             from mixture_experts_decode_router_amd.build import source_digest
             if mj.get("source_digest") == source_digest():
-                kd = mj["kernels"].get("expert_mfma<true>")
+                kd = mj["kernels"].get("expert_mfma<true, false>")
                 mfma_counter = kd["mfma_util_pct"] if kd else None
         except Exception:
             mfma_counter = None
