@@ -38,7 +38,16 @@ WORKLOAD_TEXT = {
     "q8": "Qwen3-30B-A3B MoE layer (H=2048, E=128, top-8, I=768), decode T=8, bf16 weights, hipGraph replay",
     "q48q": "Qwen3-30B-A3B MoE layer, decode T=48, 4-bit blockwise weights (64 per fp32 absmax), hipGraph replay",
     "q4096": "Qwen3-30B-A3B MoE layer, prefill T=4096, bf16, Zipf-skewed router bias, hipGraph replay",
+    "q4096q": "Qwen3-30B-A3B MoE layer, prefill T=4096, 4-bit blockwise weights (the q48q layer), hipGraph replay",
 }
+# workload -> (synthetic workload, token count or None for its own)
+WORKLOAD_INPUT = {"q4096q": ("q48q", 4096)}
+
+
+def make_workload(name, T=None):
+    import synthetic as S
+    base, t0 = WORKLOAD_INPUT.get(name, (name, None))
+    return S.make(base, T=T if T is not None else t0)
 
 
 def log(*a):
@@ -341,7 +350,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    inp = S.make(args.workload)
+    inp = make_workload(args.workload)
     T, H, E, k, I = inp.T, inp.H, inp.E, inp.k, inp.I
     log(f"[bench] workload {args.workload}: T={T} H={H} E={E} k={k} I={I} wfmt={inp.wfmt}")
     lay = MoELayer(inp, t_max=T, tiled=not args.row_major)
@@ -571,10 +580,11 @@ def main():
 
     dominant = "gate_up"
     dom_us = stage_us[dominant]
-    # the library runs the LDS-tiled MFMA kernels when the tiled bf16 layout
-    # has at least 32 routed rows per expert on average (prefill sizes): those
-    # are bound by the matrix cores, the skinny decode kernels by HBM
-    mfma_path = inp.wfmt == "bf16" and not args.row_major and T * k >= 32 * E
+    # the library runs the LDS-tiled MFMA kernels when the tiled layout (bf16
+    # or 4-bit) has at least 32 routed rows per expert on average (prefill
+    # sizes): those are bound by the matrix cores, the skinny decode kernels
+    # by HBM
+    mfma_path = not args.row_major and T * k >= 32 * E
     if mfma_path:
         dom_flops = 2.0 * T * k * H * 2 * I
         achieved = dom_flops / (dom_us * 1e-6) / 1e12
@@ -664,7 +674,7 @@ def main():
     if args.sweep and T <= 64:
         sweep = {}
         for b in buckets:
-            xb = lay.upload_x(S.make(args.workload, T=b).x)
+            xb = lay.upload_x(make_workload(args.workload, T=b).x)
             with torch.cuda.stream(stream):
                 x_static[:b].copy_(xb)
             for _ in range(5):

@@ -112,9 +112,9 @@ typedef struct {
  *   y          = W_d h  + scale * B_d (A_d h)      (h: the bf16 h the down GEMM reads)
  * A x is formed in fp32 per routed row (fixed order, batch-independent),
  * the B products in fp32 in the GEMM epilogues: the 16-row decode kernels
- * and the MFMA prefill kernels (T * top_k >= 32 * n_experts, tiled bf16
- * weights) add them with the same arithmetic, so a row's result does not
- * depend on the batch.  Device arrays, fp32, 16-byte aligned:
+ * and the MFMA prefill kernels (T * top_k >= 32 * n_experts, tiled bf16 or
+ * 4-bit weights) add them with the same arithmetic, so a row's result does
+ * not depend on the batch.  Device arrays, fp32, 16-byte aligned:
  *   a_gate_up [E][r][H]   b_gate_up [E][2I][r] (gate rows, then up rows)
  *   a_down    [E][r][I]   b_down    [E][H][r] */
 typedef struct {
@@ -283,10 +283,12 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
  * Must follow moe_forward(cfg, w, x, T, ...) with cfg->train = 1 on the same
  * `workspace` and stream with no other use of the workspace in between: it
  * reads that call's routing arrays, per-slot y and pre-activations (and
- * overwrites y and the pre-activations).  Supported: tiled bf16 weights
- * (MOE_W_BF16_TILED), any T (where the forward ran the MFMA prefill
- * kernels, the backward buckets the same ids again into the 16-row work
- * items its kernels take); else MOE_ERR_UNSUPPORTED (cfg->train = 0 too).
+ * overwrites y and the pre-activations).  Supported: tiled weights
+ * (MOE_W_BF16_TILED, or MOE_W_NF4_B64_TILED as below), any T (where the
+ * forward ran the bf16 MFMA prefill kernels, the backward's transposed
+ * products run as tiled GEMMs over the same 128-row work items; a 4-bit
+ * training forward runs the 16-row kernels at every T); else
+ * MOE_ERR_UNSUPPORTED (cfg->train = 0 too).
  * With top-k weights without renormalisation (MOE_TOPK_SOFTMAX) the logit gradient
  * reaches every expert, d_l[e] = [e chosen] w_e d_topk_w_e - p_e sum_j w_j
  * d_topk_w_j with p the softmax over all E (from the router's approximate

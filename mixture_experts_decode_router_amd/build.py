@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "experts_skinny.hip", "combine.hip", "pack.hip",
-           "experts_mfma.hip", "lora.hip", "backward.hip", "probe.hip"]
+           "experts_mfma.hip", "experts_mfma_nf4.hip", "lora.hip", "backward.hip", "probe.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

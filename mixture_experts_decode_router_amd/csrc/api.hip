@@ -119,10 +119,12 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
 bool is_nf4(const moe_config& c) { return c.wfmt == MOE_W_NF4_B64 || c.wfmt == MOE_W_NF4_B64_TILED; }
 
 // Large groups (on average >= 32 rows per expert) go to the LDS-tiled MFMA
-// kernels (tiled bf16 weights only, with or without LoRA adapters); they
-// give the same per-row bits as the 16-row kernels.
+// kernels (tiled weights, with or without LoRA adapters); they give the
+// same per-row bits as the 16-row kernels.  A 4-bit training forward stays
+// on the 16-row kernels: the 4-bit backward runs over 16-row work items.
 bool mfma_path_for(const moe_config& c, int T) {
-  return c.wfmt == MOE_W_BF16_TILED && (long)T * c.top_k >= 32L * c.n_experts;
+  const bool tiled_ok = c.wfmt == MOE_W_BF16_TILED || (c.wfmt == MOE_W_NF4_B64_TILED && !c.train);
+  return tiled_ok && (long)T * c.top_k >= 32L * c.n_experts;
 }
 bool is_tiled(const moe_config& c) { return c.wfmt == MOE_W_BF16_TILED || c.wfmt == MOE_W_NF4_B64_TILED; }
 
@@ -293,7 +295,8 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
     la.U = at<float>(ws, L.u_gu);
     if ((e = moe::launch_lora_a(la, s)) != hipSuccess) return hip_fail(e, "LoRA A launch");
   }
-  e = mfma_path ? moe::launch_gate_up_mfma(ea, s) : moe::launch_gate_up(ea, nf4, tiled, s);
+  e = mfma_path ? (nf4 ? moe::launch_gate_up_mfma_nf4(ea, s) : moe::launch_gate_up_mfma(ea, s))
+                : moe::launch_gate_up(ea, nf4, tiled, s);
   if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (w.lora) {
@@ -304,7 +307,8 @@ moe_status enqueue_forward(const moe_config& c, const moe_weights& w, const void
     la.U = at<float>(ws, L.u_d);
     if ((e = moe::launch_lora_a(la, s)) != hipSuccess) return hip_fail(e, "LoRA A launch");
   }
-  e = mfma_path ? moe::launch_down_mfma(ea, s) : moe::launch_down(ea, nf4, tiled, s);
+  e = mfma_path ? (nf4 ? moe::launch_down_mfma_nf4(ea, s) : moe::launch_down_mfma(ea, s))
+                : moe::launch_down(ea, nf4, tiled, s);
   if (e != hipSuccess) return hip_fail(e, "down launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
 

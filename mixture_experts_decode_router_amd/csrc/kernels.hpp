@@ -223,6 +223,10 @@ hipError_t launch_lora_grad(const BwdArgs& a, bool down, hipStream_t s);
 // adapters' B U terms exactly as the 16-row kernels do.
 hipError_t launch_gate_up_mfma(const ExpertArgs& a, hipStream_t s);
 hipError_t launch_down_mfma(const ExpertArgs& a, hipStream_t s);
+// the same work list and outputs for tiled 4-bit weights (adapters allowed,
+// kept pre-activations allowed)
+hipError_t launch_gate_up_mfma_nf4(const ExpertArgs& a, hipStream_t s);
+hipError_t launch_down_mfma_nf4(const ExpertArgs& a, hipStream_t s);
 
 struct PackArgs {
   bool nf4;

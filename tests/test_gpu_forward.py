@@ -1,6 +1,8 @@
 """Whole-block parity (HIP vs fp64 oracle): routing arrays in the workspace
 bit-exact, outputs within max|err| <= 2e-2 * rms (bf16 weights) or
 5e-2 * rms (4-bit weights, oracle on the same dequantised weights)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -8,7 +10,7 @@ import torch
 import oracle as O
 import synthetic as S
 from mixture_experts_decode_router_amd.layer import MoELayer
-from tests.gpu_util import TOL_BF16, TOL_NF4, layer, oracle_forward, rel_err, say, workload
+from tests.gpu_util import TOL_BF16, TOL_NF4, layer, oracle_forward, oracle_weights, rel_err, say, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -126,11 +128,17 @@ def test_forward_edge_shapes(case, tiled):
     dict(T=1100, H=512, E=16, k=1, I=384),    # k = 1, three gate/up tiles
     dict(T=520, H=256, E=16, k=4, I=128),     # shortest K (down K = 128: two stages)
     dict(T=640, H=256, E=256, k=16, I=128),   # largest E and k on the MFMA kernels
+    dict(T=600, H=384, E=16, k=2, I=256, wfmt="nf4"),    # 4-bit: H an odd number of 128-blocks
+    dict(T=520, H=256, E=16, k=4, I=128, wfmt="nf4"),    # 4-bit: shortest K
+    dict(T=640, H=256, E=256, k=16, I=128, wfmt="nf4"),  # 4-bit: largest E and k
+    dict(T=700, H=512, E=32, k=2, I=384, wfmt="nf4", cb="random"),  # 4-bit: arbitrary fp32 codebook
 ])
 def test_forward_prefill_mfma_shapes(case):
     """Shapes that take the LDS-tiled MFMA kernels (>= 32 routed rows per expert)."""
+    wfmt = case.get("wfmt", "bf16")
+    book = S.random_codebook(case["T"]) if case.get("cb") == "random" else None
     inp = S.make_small(case["T"], case["H"], case["E"], case["k"], case["I"], seed=case["T"],
-                       wfmt="bf16", bias=True)
+                       wfmt=wfmt, bias=True, codebook=book)
     say(f"[gpu] forward prefill-path {case}")
     lay = MoELayer(inp, t_max=case["T"])
     out, views = run_forward(lay, inp.x)
@@ -138,7 +146,7 @@ def test_forward_prefill_mfma_shapes(case):
     check_views(views, ref)
     err = rel_err(out.cpu().numpy(), ref_out)
     say(f"[gpu]   max|err|/rms = {err:.3e}")
-    assert err <= TOL_BF16
+    assert err <= (TOL_NF4 if wfmt == "nf4" else TOL_BF16)
 
 
 def test_forward_prefill_one_hot_expert_set():
@@ -189,6 +197,25 @@ def test_prefill_rows_match_decode_rows_bit_for_bit():
     for lo in (0, 2000, 4080):
         b = lay.forward(lay.upload_x(inp.x[lo:lo + 16]))
         assert torch.equal(a[lo:lo + 16], b), lo
+
+
+def test_prefill_rows_match_decode_rows_4bit():
+    """4-bit Qwen layer at T=1024 (the LDS-tiled 4-bit MFMA kernels) against
+    the same tokens in batches of 16 (the 16-row 4-bit kernels): the same
+    bits, and parity with the oracle on sampled rows."""
+    inp = S.make("q48q", 1024)
+    lay = MoELayer(inp, t_max=1024)
+    say("[gpu] 4-bit prefill vs decode path rows")
+    a = lay.forward(lay.upload_x(inp.x))
+    for lo in (0, 500, 1008):
+        b = lay.forward(lay.upload_x(inp.x[lo:lo + 16]))
+        assert torch.equal(a[lo:lo + 16], b), lo
+    rows = np.array([0, 1, 333, 777, 1023])
+    sub = dataclasses.replace(inp, x=inp.x[rows], T=len(rows))
+    ref_out, _ = O.forward_batched(sub, oracle_weights("q48q"))
+    err = rel_err(a.cpu().numpy()[rows], ref_out)
+    say(f"[gpu]   sampled rows max|err|/rms = {err:.3e}")
+    assert err <= TOL_NF4
 
 
 def test_forward_row_subset_is_bit_identical():

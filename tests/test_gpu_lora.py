@@ -148,3 +148,35 @@ def test_lora_at_prefill_sizes(T):
     b = base.with_lora(d0).forward(xb)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("T", [600, 1100])
+def test_lora_at_prefill_sizes_4bit(T):
+    # 4-bit base at T*k >= 32*E: the 4-bit LDS-tiled MFMA kernels add the
+    # adapter terms in their epilogues, against the oracle on the dequantised
+    # weights; rows equal a decode-sized call's (the 16-row 4-bit kernels);
+    # zero B gives the base kernels' bits
+    from mixture_experts_decode_router_amd.layer import MoELayer
+    inp = S.make_small(T, 384, 16, 2, 256, seed=T + 1, wfmt="nf4", bias=True)
+    d = S.lora_adapters(inp.E, inp.H, inp.I, seed=T)
+    base = MoELayer(inp, t_max=T)
+    say(f"[gpu] LoRA forward 4-bit at prefill size T={T}")
+    lay = base.with_lora(d)
+    out = lay.forward(lay.upload_x(inp.x))
+    torch.cuda.synchronize()
+    ref_out, ref = O.forward_batched(inp, lora=O.LoRA(**d))
+    check_views(lay.views(T), ref)
+    err = rel_err(out.cpu().numpy(), ref_out)
+    say(f"[gpu]   max|err|/rms = {err:.3e}")
+    assert err <= TOL_NF4
+    small = lay.forward(lay.upload_x(inp.x[:16]))
+    torch.cuda.synchronize()
+    assert torch.equal(small, out[:16])
+    d0 = S.lora_adapters(inp.E, inp.H, inp.I, seed=T)
+    d0["b_gate_up"][:] = 0
+    d0["b_down"][:] = 0
+    xb = base.upload_x(inp.x)
+    a = base.forward(xb)
+    b = base.with_lora(d0).forward(xb)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
