@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * kWaves) void lora_bt_kernel(BwdArgs a, int mod
   });
 }
 
-// Adapter gradients of every expert, summed over its routed rows in slot
+// Adapter gradients of every expert, summed over its routed rows in a fixed
 // order (no atomics; zero for an expert no row reached), times the scale.
 //   part 0 (down; before the down transposed GEMV turns g, u into d_g, d_u):
 //     d_b_down[e][c][j] = s sum_p (w_p d_out[t_p][c]) U_d[p][j]
@@ -196,49 +196,61 @@ __global__ __launch_bounds__(64 * kWaves) void lora_bt_kernel(BwdArgs a, int mod
 //     d_b_gate_up[e][n][j] = s sum_p (d_g, d_u)[p][n] U_gu[p][j]
 //     d_a_gate_up[e][j][h] = s sum_p z_gu[p][j] x[t_p][h]
 // Each is a column c of the streamed operand (d_y, h, (d_g, d_u) or x) times
-// the row's rank-16 vector (U or z), so a thread owns one column and its 16
-// sums.  A 256-thread workgroup covers 256 columns of one expert's B or A
-// gradient; the routed rows' vectors (and tokens, weights) are staged in LDS
-// 64 rows at a time, and each thread's column loads are issued 8 rows at a
-// time.  B-gradient rows are 16 contiguous floats per thread; A-gradient
-// rows are written column-coalesced.
-constexpr int kGradRows = 64;
+// the row's rank-16 vector (U or z).  A 256-thread workgroup covers 256 / G
+// columns of one expert's B or A gradient with G row groups (G = GROUPS):
+// thread (group q, column c) sums rows q, q + G, ... of the expert's sorted
+// rows (its 16 sums, row by row in ascending order),
+// the routed rows' vectors (and tokens, weights) staged in LDS kGradRows
+// rows at a time, each thread's column loads issued 8 rows at a time; then
+// the groups' partial sums are added in group order through LDS.  With 8
+// groups (prefill sizes) a heavily routed expert's rows are walked by 8
+// threads per column; at decode sizes (a few rows per expert) one group and
+// 256 columns per workgroup keep the launch small.  Either way the result
+// is the same on every run.  B-gradient rows are 16 contiguous floats;
+// A-gradient rows are written column-coalesced.
+constexpr int kGradRows = 128;
 
+template <int GROUPS>
 __global__ __launch_bounds__(256) void lora_grad_kernel(BwdArgs a, int part) {
+  constexpr int kCols = 256 / GROUPS;       // columns per workgroup
+  constexpr int kPer = kGradRows / GROUPS;  // rows per thread per staged chunk
   __shared__ f32x4_t s_vec[kGradRows][4];
   __shared__ int s_tok[kGradRows];
   __shared__ float s_w[kGradRows];
+  __shared__ float s_red[GROUPS][GROUPS > 1 ? kCols : 1][kRank + 1];  // +1: no bank conflicts on the column reads
   const int H = a.H, I = a.I;
   const int nB = part == 0 ? H : 2 * I;  // columns (rows of the [n][16] array) of the B gradient
   const int nA = part == 0 ? I : H;      // columns of the [16][n] A gradient
-  const int wgB = (nB + 255) / 256;
+  const int wgB = (nB + kCols - 1) / kCols;
   const int e = blockIdx.y;
   const bool isB = (int)blockIdx.x < wgB;
-  const int col = (isB ? blockIdx.x : blockIdx.x - wgB) * 256 + threadIdx.x;
+  const int grp = threadIdx.x / kCols, cl = threadIdx.x % kCols;
+  const int col = (isB ? blockIdx.x : blockIdx.x - wgB) * kCols + cl;
   const bool cv = col < (isB ? nB : nA);
   const int p0 = a.offsets[e], p1 = a.offsets[e + 1];
   const float* vec = part == 0 ? (isB ? a.u_down : a.z_down) : (isB ? a.u_gate_up : a.z_gate_up);
-  float acc[16];
+  float acc[kRank];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int j = 0; j < kRank; ++j) acc[j] = 0.f;
   for (int c0 = p0; c0 < p1; c0 += kGradRows) {
     const int nr = p1 - c0 < kGradRows ? p1 - c0 : kGradRows;
     __syncthreads();  // the previous chunk's LDS reads are done
-    {
-      const int r = threadIdx.x >> 2, qq = threadIdx.x & 3;
-      if (r < nr) s_vec[r][qq] = *reinterpret_cast<const f32x4_t*>(vec + (size_t)(c0 + r) * kRank + 4 * qq);
-      if (threadIdx.x < nr) {
-        const int slot = a.perm[c0 + threadIdx.x];
-        s_tok[threadIdx.x] = slot / a.k;
-        s_w[threadIdx.x] = a.wts[slot];
-      }
+    for (int i = threadIdx.x; i < 4 * nr; i += 256) {
+      const int r = i >> 2, qq = i & 3;
+      s_vec[r][qq] = *reinterpret_cast<const f32x4_t*>(vec + (size_t)(c0 + r) * kRank + 4 * qq);
+    }
+    if (threadIdx.x < nr) {
+      const int slot = a.perm[c0 + threadIdx.x];
+      s_tok[threadIdx.x] = slot / a.k;
+      s_w[threadIdx.x] = a.wts[slot];
     }
     __syncthreads();
-    for (int r0 = 0; r0 < nr; r0 += 8) {
+    // this thread's rows grp, grp + GROUPS, ... of the chunk, 8 at a time
+    for (int u0 = 0; u0 < kPer; u0 += 8) {
       float sv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int r = r0 + u;
+        const int r = grp + GROUPS * (u0 + u);
         float v = 0.f;
         if (cv && r < nr) {
           const size_t p = (size_t)(c0 + r);
@@ -250,18 +262,18 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(BwdArgs a, int part) {
               v = silu(gp[0]) * gp[I];
             }
           } else {
-            v = isB ? a.gu[p * 2 * I + col]
-                    : __uint_as_float((uint32_t)a.x[(size_t)s_tok[r] * H + col] << 16);
+            v = isB ? a.gu[p * 2 * I + col] : __uint_as_float((uint32_t)a.x[(size_t)s_tok[r] * H + col] << 16);
           }
         }
         sv[u] = v;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (r0 + u < nr) {
+        const int r = grp + GROUPS * (u0 + u);
+        if (r < nr) {
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
-            const f32x4_t z = s_vec[r0 + u][qq];
+            const f32x4_t z = s_vec[r][qq];
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[4 * qq + i] = fmaf(sv[u], z[i], acc[4 * qq + i]);
           }
@@ -269,18 +281,45 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(BwdArgs a, int part) {
       }
     }
   }
-  if (!cv) return;
   const float sc = a.lora_scale;
-  if (isB) {
-    float* o = (part == 0 ? a.g_b_down : a.g_b_gate_up) + ((size_t)e * nB + col) * kRank;
+  if constexpr (GROUPS == 1) {
+    if (!cv) return;
+    if (isB) {
+      float* o = (part == 0 ? a.g_b_down : a.g_b_gate_up) + ((size_t)e * nB + col) * kRank;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
-      *reinterpret_cast<f32x4_t*>(o + 4 * qq) =
-          f32x4_t{sc * acc[4 * qq], sc * acc[4 * qq + 1], sc * acc[4 * qq + 2], sc * acc[4 * qq + 3]};
+      for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<f32x4_t*>(o + 4 * qq) =
+            f32x4_t{sc * acc[4 * qq], sc * acc[4 * qq + 1], sc * acc[4 * qq + 2], sc * acc[4 * qq + 3]};
+    } else {
+      float* o = (part == 0 ? a.g_a_down : a.g_a_gate_up) + (size_t)e * kRank * nA + col;
+#pragma unroll
+      for (int j = 0; j < kRank; ++j) o[(size_t)j * nA] = sc * acc[j];
+    }
   } else {
-    float* o = (part == 0 ? a.g_a_down : a.g_a_gate_up) + (size_t)e * kRank * nA + col;
+    // the groups' partial sums, added in group order: thread (q, c)
+    // finishes rank values 2q, 2q + 1 of column c
+    static_assert(GROUPS == 1 || kRank == 2 * GROUPS, "two rank values per thread in the final sum");
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[(size_t)j * nA] = sc * acc[j];
+    for (int j = 0; j < kRank; ++j) s_red[grp][cl][j] = acc[j];
+    __syncthreads();
+    if (!cv) return;
+    float fin[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < GROUPS; ++q) sum += s_red[q][cl][2 * grp + t];
+      fin[t] = sc * sum;
+    }
+    if (isB) {
+      float* o = (part == 0 ? a.g_b_down : a.g_b_gate_up) + ((size_t)e * nB + col) * kRank + 2 * grp;
+      o[0] = fin[0];
+      o[1] = fin[1];
+    } else {
+      float* o = (part == 0 ? a.g_a_down : a.g_a_gate_up) + (size_t)e * kRank * nA + col;
+      o[(size_t)(2 * grp) * nA] = fin[0];
+      o[(size_t)(2 * grp + 1) * nA] = fin[1];
+    }
   }
 }
 
@@ -297,8 +336,15 @@ hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s) {
 
 hipError_t launch_lora_grad(const BwdArgs& a, bool down, hipStream_t s) {
   const int nB = down ? a.H : 2 * a.I, nA = down ? a.I : a.H;
-  hipLaunchKernelGGL(lora_grad_kernel, dim3((nB + 255) / 256 + (nA + 255) / 256, a.E), dim3(256), 0, s, a,
-                     down ? 0 : 1);
+  // prefill sizes (on average >= 32 routed rows per expert): 8 row groups
+  if ((long)a.T * a.k >= 32L * a.E) {
+    constexpr int cols = 256 / 8;
+    hipLaunchKernelGGL(lora_grad_kernel<8>, dim3((nB + cols - 1) / cols + (nA + cols - 1) / cols, a.E), dim3(256), 0,
+                       s, a, down ? 0 : 1);
+  } else {
+    hipLaunchKernelGGL(lora_grad_kernel<1>, dim3((nB + 255) / 256 + (nA + 255) / 256, a.E), dim3(256), 0, s, a,
+                       down ? 0 : 1);
+  }
   return hipGetLastError();
 }
 
