@@ -285,9 +285,9 @@ moe_status moe_forward_prenorm(const moe_config* cfg, const moe_weights* w, cons
  * reads that call's routing arrays, per-slot y and pre-activations (and
  * overwrites y and the pre-activations).  Supported: tiled weights
  * (MOE_W_BF16_TILED, or MOE_W_NF4_B64_TILED as below), any T (where the
- * forward ran the bf16 MFMA prefill kernels, the backward's transposed
- * products run as tiled GEMMs over the same 128-row work items; a 4-bit
- * training forward runs the 16-row kernels at every T); else
+ * forward ran the MFMA prefill kernels, bf16 or 4-bit, the backward's
+ * transposed products run as tiled GEMMs over the same 128-row work items);
+ * else
  * MOE_ERR_UNSUPPORTED (cfg->train = 0 too).
  * With top-k weights without renormalisation (MOE_TOPK_SOFTMAX) the logit gradient
  * reaches every expert, d_l[e] = [e chosen] w_e d_topk_w_e - p_e sum_j w_j

@@ -118,15 +118,14 @@ moe_status check_ptr(const void* p, const char* name, size_t align = 16) {
 
 bool is_nf4(const moe_config& c) { return c.wfmt == MOE_W_NF4_B64 || c.wfmt == MOE_W_NF4_B64_TILED; }
 
-// Large groups (on average >= 32 rows per expert) go to the LDS-tiled MFMA
-// kernels (tiled weights, with or without LoRA adapters); they give the
-// same per-row bits as the 16-row kernels.  A 4-bit training forward stays
-// on the 16-row kernels: the 4-bit backward runs over 16-row work items.
-bool mfma_path_for(const moe_config& c, int T) {
-  const bool tiled_ok = c.wfmt == MOE_W_BF16_TILED || (c.wfmt == MOE_W_NF4_B64_TILED && !c.train);
-  return tiled_ok && (long)T * c.top_k >= 32L * c.n_experts;
-}
 bool is_tiled(const moe_config& c) { return c.wfmt == MOE_W_BF16_TILED || c.wfmt == MOE_W_NF4_B64_TILED; }
+// Large groups (on average >= 32 rows per expert) go to the LDS-tiled MFMA
+// kernels (tiled weights, bf16 or 4-bit, with or without LoRA adapters, in
+// inference and in training, whose backward then runs over the same 128-row
+// work items); they give the same per-row bits as the 16-row kernels.
+bool mfma_path_for(const moe_config& c, int T) {
+  return is_tiled(c) && (long)T * c.top_k >= 32L * c.n_experts;
+}
 
 moe_status check_weights(const moe_config& c, const moe_weights* w) {
   if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");

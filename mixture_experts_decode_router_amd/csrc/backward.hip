@@ -18,6 +18,7 @@
 // order.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "nf4.hpp"
 
 namespace moe {
 namespace {
@@ -628,6 +629,218 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- 4-bit transposed GEMMs
+// bwd_gemm_kernel for tiled 4-bit weights, over the 128-row items of the
+// 4-bit MFMA forward: the same workgroup tile (an item's 128 rows x 256
+// columns n, 8 waves of 64 x 64) and the same arithmetic as bwd_t_kernel's
+// 4-bit form.  Per 32-m stage the workgroup's four 16-byte code chunks (two
+// row tiles x two 128-column blocks of the window) are turned into the hi
+// and lo bf16 parts of their codebook entries and written to LDS as the
+// weight fragments the bf16 kernel stages (the code chunk's lane order is
+// the fragments' lane order), so the transposing reads are the same; the
+// rows' v (w d_out or (d_g, d_u), fp32) is staged as fp32.  Each wave's 64
+// columns lie in one 64-column absmax block, so its A operand is v[p][m]
+// times absmax[m] of that block, rounded to bf16 (hi, and lo with HILO) by
+// the wave itself, and per step the MFMAs run lo-part weights, then hi-part
+// weights, then (HILO) v's lo part with the hi-part weights, into one
+// accumulator: bwd_t_kernel's sequence, so a row's gradient is the same
+// bits from either kernel.  Two 50 KiB stages and the code-pair table's
+// copies: one workgroup per CU.
+constexpr int kBqVStride = 36;                        // floats per staged v row (32 m + padding)
+constexpr int kBqWBytes = kBgWFrags * 1024;           // one part (hi or lo) of a stage's weight fragments
+constexpr int kBqVBytes = kMfmaTile * kBqVStride * 4;
+constexpr int kBqStage = 2 * kBqWBytes + kBqVBytes;
+constexpr int kBqLds = 2 * kBqStage + 256 * kLutRep * 8;
+
+template <int MODE, bool LORA, bool HILO>
+__global__ __launch_bounds__(kBgThreads) void bwd_gemm_nf4_kernel(BwdArgs a) {
+  constexpr bool kHiLo = HILO && MODE == kDown;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char s_dyn[];
+  u32x2_t* s_lut = reinterpret_cast<u32x2_t*>(s_dyn + 2 * kBqStage);
+  const int I = a.I, H = a.H;
+  const int ncols = MODE == kDown ? I : H;      // n
+  const int nrows = MODE == kDown ? H : 2 * I;  // m
+  const int nkb = ncols / 128;                  // 128-column code blocks of a row tile
+  const int ntile = (ncols + kBgBN - 1) / kBgBN;
+  const int item = blockIdx.x / ntile, nt = blockIdx.x - item * ntile;
+  if (item >= *a.n_items) return;
+  const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
+  const int cnt = a.counts[e] - m0;
+  const int M = cnt < kMfmaTile ? cnt : kMfmaTile, base = a.offsets[e] + m0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // the wave's 64 rows x 64 columns
+  const int r = lane & 15, g = lane >> 4;
+  const int nsteps = nrows / 32;
+  const int n0 = nt * kBgBN;
+  const size_t rt0 = (size_t)e * (nrows / 16);
+  const uint8_t* Q = MODE == kDown ? a.q_down : a.q_gate_up;
+  const float* SC = MODE == kDown ? a.s_down : a.s_gate_up;
+  build_lut(s_lut, a.codebook, tid);
+  const u32x2_t* s_lutl = lut_copy(s_lut, lane);
+
+  // codes: wave w decodes dwords 2 (w & 1), +1 of chunk w >> 1 = (row tile
+  // (w >> 1) >> 1 of the stage, 128-column block (w >> 1) & 1 of the window;
+  // blocks past ncols decode the last valid block, whose columns are never
+  // stored); dword st of a chunk is the fragment of 32-column block 4 kb + st
+  const int cw = wave >> 1, dh = wave & 1;
+  const int c_rtl = cw >> 1, c_kbw = cw & 1;
+  const int c_kb = min(n0 / 128 + c_kbw, nkb - 1);
+  const uint8_t* csrc = Q + ((rt0 + c_rtl) * nkb + c_kb) * 1024 + lane * 16 + 8 * dh;
+  const size_t cstep = (size_t)2 * nkb * 1024;  // bytes per 32-m stage (two row tiles)
+  // v rows: thread t brings row p = t / 4, m = 8 (t % 4) .. +7 of each stage
+  const int vp = tid >> 2, vg = tid & 3;
+  const int vpc = vp < M ? vp : 0;
+  const float* vrow;
+  float vw;
+  if (MODE == kDown) {
+    const int slot = a.perm[base + vpc];
+    vrow = a.d_out + (size_t)(slot / a.k) * H + 8 * vg;
+    vw = vp < M ? a.wts[slot] : 0.f;
+  } else {
+    vrow = a.gu + (size_t)(base + vpc) * 2 * I + 8 * vg;
+    vw = vp < M ? 1.f : 0.f;
+  }
+  // absmax of this lane's rows m = 8g .. 8g+7 of a stage for the wave's
+  // column block: row tile 2s + (g >> 1), rows 8 (g & 1) + i, floats 2i + h
+  const int wblk = min((n0 + wn * 64) / 64, 2 * nkb - 1);  // blocks past ncols: never stored
+  const int w_kb = wblk >> 1, w_h = wblk & 1;
+  const float* ssrc = SC + ((rt0 + (g >> 1)) * nkb + w_kb) * 32 + 16 * (g & 1);
+  const size_t sstep = (size_t)2 * nkb * 32;
+
+  u32x2_t cd;
+  f32x4_t v0, v1, s4[4];
+  auto load = [&](int st) {
+    cd = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(csrc + st * cstep));
+    v0 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * st);
+    v1 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * st + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s4[j] = *reinterpret_cast<const f32x4_t*>(ssrc + st * sstep + 4 * j);
+  };
+  auto store = [&](int buf) {
+    unsigned char* sb = s_dyn + buf * kBqStage;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      u32x4_t hi, lo;
+      lut8(s_lutl, cd[d], hi, lo);
+      const int f = c_rtl * 8 + 4 * c_kbw + 2 * dh + d;  // fragment (row tile, column block) of the stage
+      *reinterpret_cast<u32x4_t*>(sb + f * 1024 + lane * 16) = hi;
+      *reinterpret_cast<u32x4_t*>(sb + kBqWBytes + f * 1024 + lane * 16) = lo;
+    }
+    float* vs = reinterpret_cast<float*>(sb + 2 * kBqWBytes) + vp * kBqVStride + 8 * vg;
+    *reinterpret_cast<f32x4_t*>(vs) = f32x4_t{vw * v0[0], vw * v0[1], vw * v0[2], vw * v0[3]};
+    *reinterpret_cast<f32x4_t*>(vs + 4) = f32x4_t{vw * v1[0], vw * v1[1], vw * v1[2], vw * v1[3]};
+  };
+  // transposing reads of the weight fragments, as in bwd_gemm_kernel
+  const int s_ = lane & 15, G = lane >> 4;
+  const int rloc = (8 * G + (s_ >> 2)) & 15, rtl = G >> 1;
+  int tr_byte[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int kbw = 2 * wn + (t >> 1);
+    const int gq = 2 * (t & 1) + ((s_ & 3) >> 1), h = s_ & 1;
+    tr_byte[t] = (rtl * 8 + kbw) * 1024 + (16 * gq + rloc) * 16 + 8 * h;
+  }
+  const int nj = min(max((M - wm * 64 + 15) / 16, 0), 4);
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto bop = [&](const unsigned char* p) {
+    const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+    const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 64));
+    return u32x4_t{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                   (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                   (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                   (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+  };
+
+  __syncthreads();  // the table is built
+  load(0);
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    float smc[8];  // absmax of the lane's rows m for the wave's column block
+#pragma unroll
+    for (int i = 0; i < 8; ++i) smc[i] = w_h ? s4[i >> 1][2 * (i & 1) + 1] : s4[i >> 1][2 * (i & 1)];
+    store(buf);
+    __syncthreads();  // stage st in LDS; every wave is done with stage st - 1's buffer
+    if (st + 1 < nsteps) load(st + 1);  // in flight during this stage's MFMAs
+    if (nj > 0) {
+      const unsigned char* sb = s_dyn + buf * kBqStage;
+      u32x4_t bh[4], bl[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bh[t] = bop(sb + tr_byte[t]);
+        bl[t] = bop(sb + kBqWBytes + tr_byte[t]);
+      }
+      const float* vs = reinterpret_cast<const float*>(sb + 2 * kBqWBytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nj) break;
+        // A operand: row p = wm * 64 + 16 i + r, m = 8g .. 8g+7, times the absmax of m
+        const float* vr = vs + (wm * 64 + 16 * i + r) * kBqVStride + 8 * g;
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(vr);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(vr + 4);
+        const float t8[8] = {x0[0] * smc[0], x0[1] * smc[1], x0[2] * smc[2], x0[3] * smc[3],
+                             x1[0] * smc[4], x1[1] * smc[5], x1[2] * smc[6], x1[3] * smc[7]};
+        u32x4_t ah, al;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ah[q] = pack_bf16x2(t8[2 * q], t8[2 * q + 1]);
+          if constexpr (kHiLo) al[q] = pack_bf16x2(t8[2 * q] - bf16lo(ah[q]), t8[2 * q + 1] - bf16hi(ah[q]));
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc[i][t] = mfma16(ah, bl[t], acc[i][t]);
+          acc[i][t] = mfma16(ah, bh[t], acc[i][t]);
+          if constexpr (kHiLo) acc[i][t] = mfma16(al, bh[t], acc[i][t]);
+        }
+      }
+    }
+  }
+  if constexpr (LORA) {  // s A^T z, as in bwd_t_kernel
+    const float* la = (MODE == kDown ? a.la_down + (size_t)e * 16 * I : a.la_gate_up + (size_t)e * 16 * H);
+    const float* zb = MODE == kDown ? a.z_down : a.z_gate_up;
+    f32x4_t aq[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int n = min(n0 + wn * 64 + 16 * t + r, ncols - 1);  // columns past ncols are never stored
+#pragma unroll
+      for (int c = 0; c < 4; ++c) aq[t][c] = la[(size_t)(4 * g + c) * ncols + n];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int prow = wm * 64 + 16 * i + r;
+      const f32x4_t zp = prow < M ? ld4f(zb + (size_t)(base + prow) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) add_scaled(acc[i][t], lora_tile(zp, aq[t]), a.lora_scale);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = wm * 64 + 16 * i + 4 * g + q;
+      if (m >= M) continue;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int n = n0 + wn * 64 + 16 * t + r;
+        if (n >= ncols) continue;
+        if (MODE == kDown) {
+          float* gp = a.gu + (size_t)(base + m) * 2 * I;
+          const float gv = gp[n], uv = gp[I + n];
+          const float sg = 1.0f / (1.0f + __expf(-gv));
+          const float dh = acc[i][t][q];
+          gp[n] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
+          gp[I + n] = dh * (gv * sg);
+        } else {
+          a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[i][t][q];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- weight gradients
 // d_W[e][r][c] = sum_p A[p][r] B[p][c] over expert e's routed rows p in slot
 // order (no atomics; zero for an expert no row reached):
@@ -817,6 +1030,24 @@ hipError_t launch_bg(const BwdArgs& a, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// dynamic LDS beyond 64 KiB needs the per-function limit raised, once per device
+template <int MODE, bool LORA, bool HILO>
+hipError_t launch_bq(const BwdArgs& a, dim3 grid, hipStream_t s) {
+  static bool done[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!done[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_gemm_nf4_kernel<MODE, LORA, HILO>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kBqLds);
+    if (e != hipSuccess) return e;
+    done[dev] = true;
+  }
+  hipLaunchKernelGGL((bwd_gemm_nf4_kernel<MODE, LORA, HILO>), grid, dim3(kBgThreads), kBqLds, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
@@ -828,6 +1059,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool down, hipStream_t s) {
   const dim3 grid(a.max_items * ((down ? a.I : a.H) / 32));
   if (a.nf4) {  // frozen 4-bit base: no weight gradients
     if (a.wgrad) return hipErrorInvalidValue;
+    if (a.row_tiles == kMfmaTile / 16) {  // the 4-bit MFMA forward's 128-row items
+      const dim3 gg(a.max_items * (((down ? a.I : a.H) + kBgBN - 1) / kBgBN));
+      if (down && a.lora) return launch_bq<kDown, true, true>(a, gg, s);
+      if (down) return launch_bq<kDown, false, false>(a, gg, s);
+      if (a.lora) return launch_bq<kGateUp, true, false>(a, gg, s);
+      return launch_bq<kGateUp, false, false>(a, gg, s);
+    }
+    if (a.row_tiles != 1) return hipErrorInvalidValue;
     if (down) {
       if (a.lora)
         hipLaunchKernelGGL((bwd_t_kernel<kDown, true, true, true>), grid, dim3(64), 0, s, a);

@@ -429,3 +429,45 @@ def test_backward_unrenormalised_matches_oracle(name, T):
     say(f"[gpu]   d_x max|err|/rms {ex:.3e}, d_w {ew:.3e}; renormalised d_x differs by {gap:.3e}")
     assert ex <= TOL_BF16 and ew <= TOL_BF16
     assert gap > 10 * ex   # the test separates the two forms
+
+
+@pytest.mark.parametrize("T,cb", [(600, "normal"), (1100, "random")])
+def test_backward_nf4_at_prefill_sizes(T, cb):
+    # a 4-bit base at T*k >= 32*E: the training forward runs the 4-bit MFMA
+    # prefill kernels (outputs the same bits as an inference forward) and the
+    # backward's 4-bit tiled transposed GEMMs run over the same 128-row items
+    # (several per expert at T = 1100; H = 384 leaves a ragged 256-column
+    # tile), against the oracle on the dequantised weights, with and without
+    # adapters; rows are the same bits as a decode-sized call's (16-row GEMVs)
+    book = S.random_codebook(11) if cb == "random" else None
+    inp = S.make_small(T, 384, 16, 2, 256, seed=T + 3, wfmt="nf4", bias=True, codebook=book)
+    d_out = d_out_for(inp.T, inp.H, seed=47)
+    inf = MoELayer(inp, t_max=T)
+    lay = MoELayer(inp, t_max=T, train=True)
+    x = inf.upload_x(inp.x)
+    a = inf.forward(x)
+    b = lay.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    say(f"[gpu] backward 4-bit at prefill size T={T} codebook={cb}")
+    d_x, d_w = gpu_backward(lay, inp.x, d_out)
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), O.ExpertWeights(inp))
+    assert np.array_equal(lay.views(inp.T)["ids"].cpu().numpy(), ref["routing"]["ids"])
+    counts = lay.views(inp.T)["counts"].cpu().numpy()
+    ex, ew = rel(d_x, ref["d_x"]), rel(d_w, ref["d_w"])
+    say(f"[gpu]   max rows per expert {counts.max()}; d_x {ex:.3e}, d_w {ew:.3e}")
+    assert ex <= TOL_NF4 and ew <= TOL_NF4
+    s_x, s_w = gpu_backward(lay, inp.x[:24], d_out[:24])
+    assert np.array_equal(s_x, d_x[:24]) and np.array_equal(s_w, d_w[:24])
+    d = S.lora_adapters(inp.E, inp.H, inp.I, seed=T)
+    ll = lay.with_lora(d)
+    d_x, d_w, g = gpu_backward_lora(ll, inp.x, d_out)
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), O.ExpertWeights(inp), lora=O.LoRA(**d))
+    errs = {"d_x": rel(d_x, ref["d_x"]), "d_w": rel(d_w, ref["d_w"])}
+    for n in LORA_NAMES:
+        errs[n] = rel(g[n], ref["d_" + n])
+    say("[gpu]   with LoRA max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_NF4 and errs["d_w"] <= TOL_NF4
+    assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
+    s_x, s_w, _ = gpu_backward_lora(ll, inp.x[:24], d_out[:24])
+    assert np.array_equal(s_x, d_x[:24]) and np.array_equal(s_w, d_w[:24])
