@@ -58,6 +58,22 @@ __device__ __forceinline__ f32x4_t lora_tile(f32x4_t prow, f32x4_t qrow) {
   return d;
 }
 
+// Gathered token fragments (16 rows x 32 k of bf16) in LDS, as the LDS-tiled
+// MFMA kernels fetch them row by row: slot 4p + c (16 bytes) holds k chunk
+// xchunk(p, c) of row p, so lanes 4p .. 4p+3 of the copy read one 64-byte
+// row segment.  xchunk(p, .) is an involution on 0..3 (c ^ s(p)), so chunk
+// g of row r sits in slot 4r + xchunk(r, g) = xslot(lane) for the MFMA lane
+// (r, g).  The 16-byte reads are served 8 lanes at a time; s(r) = bits 1, 2
+// of r takes 4 distinct values over each 8 consecutive rows, so 8
+// consecutive lanes of an operand read (8 rows, one chunk) cover 8 distinct
+// 16-byte bank groups (no bank conflicts in the counters; a swizzle built
+// for 16-lane groups showed 4 conflict cycles per read).
+__device__ __forceinline__ int xchunk(int p, int c) { return c ^ ((p >> 1) & 3); }
+__device__ __forceinline__ int xslot(int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  return 4 * r + xchunk(r, g);
+}
+
 __device__ __forceinline__ f32x4_t ld4f(const float* p) { return *reinterpret_cast<const f32x4_t*>(p); }
 
 // acc += scale * d, elementwise

@@ -12,9 +12,15 @@
 // Per 32-k stage the workgroup needs 16 weight fragments (each one contiguous
 // kilobyte of the tiled layout) and kBM/16 token fragments (16 gathered rows
 // x 32 k); the waves move them with global_load_lds_dwordx4, which writes the
-// 64 lanes' 16-byte pieces to LDS in lane order -- exactly the fragment order
-// the MFMA operands are read in, so neither side has bank conflicts and no
-// register staging is needed.  kRing LDS stages form a ring: loads run
+// 64 lanes' 16-byte pieces to LDS in lane order, so no register staging is
+// needed.  A weight fragment arrives in MFMA operand order.  A token
+// fragment is fetched row by row (lanes 4p .. 4p+3 bring the 64 bytes of
+// row p, in the order of xchunk): the load unit serves four lanes that read
+// one contiguous row segment about 3.5x faster than sixteen lanes that each
+// read another row, which the operand order would need (measured from L2:
+// 33 against 9.3 TB/s).  The MFMA lanes then read their 16 bytes from slot
+// 4r + xchunk(r, g), an order in which every 8 consecutive lanes of a read
+// hit distinct banks.  kRing LDS stages form a ring: loads run
 // kRing - 1 stages ahead of the MFMAs.  Each iteration waits for the wave's
 // own loads of the stage to be multiplied (s_waitcnt vmcnt), then one barrier
 // publishes the whole stage and retires the buffer the next loads overwrite.
@@ -110,16 +116,17 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return x < full ? x * per + i : full * per + (x - full) * (per - 1) + i;
 }
 
-// MFMAs of one k-step for the first NJ token tiles of the wave
+// MFMAs of one k-step for the first NJ token tiles of the wave; xoff: this
+// lane's byte offset in a token fragment (xslot)
 template <int NJ>
-__device__ __forceinline__ void mma_step(const unsigned char* sb, const int (&wrt)[kNT], int wm, int lane,
+__device__ __forceinline__ void mma_step(const unsigned char* sb, const int (&wrt)[kNT], int wm, int lane, int xoff,
                                          f32x4_t (&acc)[kNT][4]) {
   u32x4_t af[kNT], bf[NJ];
 #pragma unroll
   for (int i = 0; i < kNT; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(sb + wrt[i] * kFragBytes + lane * 16);
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
-    bf[j] = *reinterpret_cast<const u32x4_t*>(sb + kXBase + (wm * 4 + j) * kFragBytes + lane * 16);
+    bf[j] = *reinterpret_cast<const u32x4_t*>(sb + kXBase + (wm * 4 + j) * kFragBytes + xoff);
 #pragma unroll
   for (int i = 0; i < kNT; ++i)
 #pragma unroll
@@ -170,17 +177,17 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
     }
     wsrc[i] = (GATE_UP ? a.w_gate_up : a.w_down) + ((rt * nks) * 64 + lane) * 8;
   }
-  // lane (g, r) brings row 16 tt + r, k offset 8 g of each k-step; a wave
-  // whose token tiles all lie past the item's end loads none (their MFMAs
-  // are skipped too)
+  // lane 4p + c brings row 16 tt + p, k offset 8 xchunk(p, c) of each
+  // k-step; a wave whose token tiles all lie past the item's end loads none
+  // (their MFMAs are skipped too)
   const bool xload = kXTiles * wave * 16 < M;
   const uint16_t* xsrc[kXTiles];
 #pragma unroll
   for (int t = 0; t < kXTiles; ++t) {
-    int row = (kXTiles * wave + t) * 16 + (lane & 15);
+    int row = (kXTiles * wave + t) * 16 + (lane >> 2);
     row = row < M ? row : M - 1;  // rows past M repeat a valid row; their outputs are never stored
     const size_t srow = GATE_UP ? (size_t)(a.perm[base + row] / a.k) : (size_t)(base + row);
-    xsrc[t] = (GATE_UP ? a.x : a.h) + srow * K + (lane >> 4) * 8;
+    xsrc[t] = (GATE_UP ? a.x : a.h) + srow * K + xchunk(lane >> 2, lane & 3) * 8;
   }
 
   auto issue = [&](int kb, int buf) {
@@ -210,6 +217,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
   // the wave's 16-row token tiles that hold rows of the item (0..4); the
   // MFMAs of tiles wholly past the item's end are skipped
   const int nj = min(max((M - wm * 64 + 15) / 16, 0), 4);
+  const int xoff = xslot(lane) * 16;
 
   const int nstage = nks;  // one 32-k step per stage
   constexpr int D = kRing - 1;  // stages in flight ahead of the one multiplied
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
       wait_own_loads(min(D - 1, nstage - 1 - kb), xload);  // stage kb landed (later ones may be in flight)
       stage_barrier();                              // ... for every wave; buffer (kb+D)%kRing is free
       if (kb + D < nstage) issue(kb + D, (kb + D) % kRing);
-      if constexpr (NJ > 0) mma_step<NJ>(s_raw + (kb % kRing) * kStageBytes, wrt, wm, lane, acc);
+      if constexpr (NJ > 0) mma_step<NJ>(s_raw + (kb % kRing) * kStageBytes, wrt, wm, lane, xoff, acc);
     }
   };
   switch (nj) {

@@ -11,8 +11,9 @@
 //
 // Tokens (x rows gathered by perm for gate/up, h rows for down) move global
 // -> LDS with global_load_lds_dwordx4 in 64-k stages (two 32-k fragments per
-// 16-row tile; a kQRing-stage ring keeps kQRing - 1 stages of loads ahead),
-// as in the bf16 LDS-tiled kernels.  Weights stay 4-bit until a lane needs
+// 16-row tile, fetched row by row; a kQRing-stage ring keeps kQRing - 1
+// stages of loads ahead), as in the bf16 LDS-tiled kernels.  Weights stay
+// 4-bit until a lane needs
 // them: each wave loads the 16-byte code chunk and the two absmax values of
 // its row in each of its row tiles at the start of each 128-k block (the two
 // token-half waves of a tile share them through L2; loading them a block
@@ -75,7 +76,7 @@ __device__ __forceinline__ int q_xcd_remap(int b, int nb) {
 // the wave's first NJ token tiles
 template <int NJ, int HB>
 __device__ __forceinline__ void q_stage_mma(const unsigned char* sb, const u32x2_t* sl, const u32x4_t (&cd)[2],
-                                            const u32x2_t (&sc)[2], int wm, int lane, f32x4_t (&acc)[2][4]) {
+                                            const u32x2_t (&sc)[2], int wm, int xoff, f32x4_t (&acc)[2][4]) {
   u32x4_t hi[2][2], lo[2][2];  // [tile][32-k step]
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -88,7 +89,7 @@ __device__ __forceinline__ void q_stage_mma(const unsigned char* sb, const u32x2
     u32x4_t x[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      x[ks] = *reinterpret_cast<const u32x4_t*>(sb + (((wm * 4 + j) * 2 + ks) * kQFrag) + lane * 16);
+      x[ks] = *reinterpret_cast<const u32x4_t*>(sb + (((wm * 4 + j) * 2 + ks) * kQFrag) + xoff);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const float s = __uint_as_float(sc[i][HB]);
@@ -132,16 +133,18 @@ __global__ __launch_bounds__(kQThreads, 4) void expert_mfma_nf4(ExpertArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
 
-  // ---- token loads: wave w brings row tile w, both 32-k halves of a stage;
-  // a wave whose rows all lie past the item's end loads none
+  // ---- token loads: wave w brings row tile w, both 32-k halves of a stage,
+  // row by row (lane 4p + c: row p, k chunk xchunk(p, c) of each half); a
+  // wave whose rows all lie past the item's end loads none
   const bool xload = wave * 16 < M;
   const uint16_t* xsrc;
   {
-    int row = wave * 16 + r;
+    int row = wave * 16 + (lane >> 2);
     row = row < M ? row : M - 1;  // rows past M repeat a valid row; their outputs are never stored
     const size_t srow = GATE_UP ? (size_t)(a.perm[base + row] / a.k) : (size_t)(base + row);
-    xsrc = (GATE_UP ? a.x : a.h) + srow * K + g * 8;
+    xsrc = (GATE_UP ? a.x : a.h) + srow * K + xchunk(lane >> 2, lane & 3) * 8;
   }
+  const int xoff = xslot(lane) * 16;  // this lane's operand in a token fragment
   auto issue = [&](int st, int buf) {
     if (!xload) return;
     lds_char* sb = (lds_char*)(s_raw) + buf * kQStageBytes;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kQThreads, 4) void expert_mfma_nf4(ExpertArgs a) {
       }
     }
     if (st + D < nstage) issue(st + D, (st + D) % kQRing);
-    if constexpr (NJ > 0) q_stage_mma<NJ, HB>(s_raw + (st % kQRing) * kQStageBytes, sl, cd, sc, wm, lane, acc);
+    if constexpr (NJ > 0) q_stage_mma<NJ, HB>(s_raw + (st % kQRing) * kQStageBytes, sl, cd, sc, wm, xoff, acc);
   };
   auto k_loop = [&](auto njc) {
     for (int kb = 0; kb < nkb; ++kb) {
