@@ -261,6 +261,114 @@ __global__ __launch_bounds__(256) void route_partial(PartParams p) {
   }
 }
 
+// The same partials with the operands staged through LDS (plain token
+// rows, no pre-block step): each wave copies, per 32-k step, its token tile
+// and its NT expert tiles (16 rows x 64 bytes each) global -> LDS with
+// global_load_lds_dwordx4, four lanes per 64-byte row segment (xchunk
+// order), into a private ring of RS steps, RS - 1 of them in flight; then
+// reads its MFMA operands from the xslot positions.  Loaded directly, each
+// lane's 16 bytes come from another row, a pattern the load unit serves
+// about 3.5x slower.  The operands each lane receives, the MFMA sequence and
+// the split sums are those of route_partial, so the partials are the same
+// bits.  Tiles past E copy tile 0 and are never stored.
+typedef __attribute__((address_space(3))) char lds_char_t;
+#define MOE_R_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+template <int L, int RS>
+__device__ __forceinline__ void route_wait(int later) {  // at most `later` steps of L loads still in flight
+  static_assert(RS <= 8 && L * (RS - 2) < 64, "wait counts");
+  switch (later) {
+    case 0: __builtin_amdgcn_s_waitcnt(MOE_R_VMCNT(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(MOE_R_VMCNT(L)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(MOE_R_VMCNT(2 * L)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(MOE_R_VMCNT(3 * L)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(MOE_R_VMCNT(4 * L)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(MOE_R_VMCNT(5 * L)); break;
+    default: __builtin_amdgcn_s_waitcnt(MOE_R_VMCNT(6 * L)); break;
+  }
+  asm volatile("" ::: "memory");  // the LDS reads of the step stay below
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void route_partial_lds(PartParams p) {
+  constexpr int L = 1 + NT;  // copies per wave per step: the token tile, then its expert tiles
+  constexpr int RS = NT == 1 ? 6 : (NT == 2 ? 5 : 3);  // ring steps, within 60 KiB of static LDS
+  __shared__ __attribute__((aligned(1024))) unsigned char s_ring[4][RS][L][1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int t0 = blockIdx.x * kTok;
+  const int H = p.H, E = p.E, T = p.T;
+  const int n_et = E >> 4;
+  const int klen = H / p.ks;
+  const int trow = t0 + r;
+  const bool tv = trow < T;
+  if (p.live_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *p.live_out = p.live_rows;
+  // copy lanes: lane 4q + c brings row q of a tile, k chunk xchunk(q, c) of each step
+  const int q = lane >> 2, cc = xchunk(q, lane & 3);
+  const int kbase = blockIdx.y * p.per_wg * klen;
+  const uint16_t* xs = p.x + (size_t)min(t0 + q, T - 1) * H + kbase + cc * 8;  // rows past T: never stored
+  const uint16_t* ws = p.wr + (size_t)q * H + kbase + cc * 8;  // row q of expert tile 0
+  const int nsteps = p.per_wg * klen / 32;
+  const int sps = klen / 32;  // steps per split
+  auto issue = [&](int st) {
+    lds_char_t* sb = (lds_char_t*)&s_ring[wave][st % RS][0][0];
+    __builtin_amdgcn_global_load_lds(xs + st * 32, sb, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int et = wave + 4 * i < n_et ? wave + 4 * i : 0;
+      __builtin_amdgcn_global_load_lds(ws + (size_t)et * 16 * H + st * 32, sb + (1 + i) * 1024, 16, 0, 0);
+    }
+  };
+  const int xo = xslot(lane) * 16;
+  const uint32_t absm = 0x7fff7fffu;
+  f32x4_t lsum[NT], ssum[NT], acc[NT], aab[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) lsum[i] = ssum[i] = acc[i] = aab[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < RS - 1; ++st)
+    if (st < nsteps) issue(st);
+  for (int st = 0; st < nsteps; ++st) {
+    route_wait<L, RS>(min(RS - 2, nsteps - 1 - st));  // step st has landed
+    if (st + RS - 1 < nsteps) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads of the buffer it overwrites are done
+      issue(st + RS - 1);
+    }
+    // tiles past E (copies of tile 0) are multiplied too and never stored
+    const unsigned char* sb = &s_ring[wave][st % RS][0][0];
+    u32x4_t av[NT];
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(sb + xo);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) av[i] = *reinterpret_cast<const u32x4_t*>(sb + (1 + i) * 1024 + xo);
+    const u32x4_t babs = b & absm;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      acc[i] = mfma16(av[i], b, acc[i]);
+      aab[i] = mfma16(av[i] & absm, babs, aab[i]);
+    }
+    if ((st + 1) % sps == 0) {  // end of a split
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        lsum[i] += acc[i];
+        ssum[i] += aab[i];
+        acc[i] = aab[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  // lane holds D[4g+q][r]: expert 16*(wave + 4i) + 4g + q, token r
+  if (tv) {
+    const int g = lane >> 4;
+    float* dl = p.part + ((size_t)blockIdx.y * T + trow) * E;
+    float* ds = p.pabs + ((size_t)blockIdx.y * T + trow) * E;
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      if (wave + 4 * i < n_et) {
+        const int e0 = 16 * (wave + 4 * i) + 4 * g;
+        *reinterpret_cast<f32x4_t*>(dl + e0) = lsum[i];
+        *reinterpret_cast<f32x4_t*>(ds + e0) = ssum[i];
+      }
+  }
+}
+
 // ------------------------------------------------------------------ select
 struct SelParams {
   RouteArgs a;
@@ -737,12 +845,14 @@ void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((route_partial<NT, 1, PN>), grid, dim3(256), 0, s, pp);
 }
 
+// plain token rows: the LDS-staged form; with the pre-block step: the
+// register form, which forms the token operand on the fly
 template <int NT>
 void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
   if (pp.res)
     launch_partial<NT, true>(pp, grid, s);
   else
-    launch_partial<NT, false>(pp, grid, s);
+    hipLaunchKernelGGL((route_partial_lds<NT>), grid, dim3(256), 0, s, pp);
 }
 
 // the instantiation launch_partial<NT> picks for pp (the same choice)
@@ -750,7 +860,8 @@ template <int NT>
 const void* partial_fn(const PartParams& pp) {
   const bool u4 = (pp.H / pp.ks) % (32 * 4) == 0;
   if (pp.res) return u4 ? (const void*)&route_partial<NT, 4, true> : (const void*)&route_partial<NT, 1, true>;
-  return u4 ? (const void*)&route_partial<NT, 4, false> : (const void*)&route_partial<NT, 1, false>;
+  void (*lds_form)(PartParams) = route_partial_lds<NT>;
+  return (const void*)lds_form;
 }
 
 hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const PermuteArgs* fuse, bool* fused,
