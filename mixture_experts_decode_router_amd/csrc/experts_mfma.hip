@@ -288,15 +288,28 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
       }
     }
   } else {
+    // y rows leave row by row: lane L = 4p + c takes over the four columns
+    // 4c .. 4c+3 of token row p from lane 16c + p (a lane permutation), so
+    // four consecutive lanes store one 64-byte segment of a row; stored with
+    // one row per lane, as the accumulators lie, the y writes cost the down
+    // GEMM about a third of its time at T = 4096
+    const int p = lane >> 2, cq = lane & 3;
+    const int src = (16 * cq + p) * 4;  // byte address of the source lane
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int trow = (wm * 4 + j) * 16 + r;
+      const int trow = (wm * 4 + j) * 16 + p;
+      f32x4_t v[kNT];
+#pragma unroll
+      for (int i = 0; i < kNT; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[i][q] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(acc[i][j][q])));
       if (trow < M) {
         float* yrow = a.y + (size_t)a.perm[base + trow] * H;
 #pragma unroll
         for (int i = 0; i < kNT; ++i) {
-          const int c = nt * kBN + (wn * kNT + i) * 16 + 4 * g;
-          if (c < H) *reinterpret_cast<f32x4_t*>(yrow + c) = acc[i][j];
+          const int c = nt * kBN + (wn * kNT + i) * 16 + 4 * cq;
+          if (c < H) *reinterpret_cast<f32x4_t*>(yrow + c) = v[i];
         }
       }
     }
