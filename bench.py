@@ -222,8 +222,11 @@ def measure_ceilings(torch, L, stream):
     stream of 2 GiB with the decode GEMMs' load form (the library's read
     probe; best of three grid sizes), a plain 1 GiB device copy (bytes read +
     written per second), the bf16 MFMA issue rate on register operands (the
-    library's MFMA probe, 16x16x32 and 32x32x16, 4 waves per SIMD) and the
-    vendor library's dense bf16 GEMM at 8192^3."""
+    library's MFMA probe, 16x16x32 and 32x32x16, 4 waves per SIMD), the
+    LDS-DMA copy rate of 16-row x 64-byte tiles of a 16 MiB buffer of 4 KiB
+    rows (the prefill GEMMs' gathered token copies; the library's gather
+    probe, one row per lane and four lanes per row segment, 2 GiB copied) and
+    the vendor library's dense bf16 GEMM at 8192^3."""
     ev = L.hip_events(2, L.HIP_EVENT_DISABLE_SYSTEM_FENCE)
 
     def timed(fn, reps):
@@ -256,6 +259,13 @@ def measure_ceilings(torch, L, stream):
         t = timed(lambda: L.moe_probe_mfma(fs, 1024, iters, shape, stream), 5)
         mfma[tag] = 1024 * 4 * iters * 131072 / t / 1e12
     del fs
+    gsrc = torch.ones(16 << 20, dtype=torch.uint8, device="cuda")
+    gsink = torch.empty(1024 * 4, dtype=torch.int32, device="cuda")
+    gather = {}
+    for order, tag in ((0, "row_per_lane"), (1, "four_lanes_per_row")):
+        t = timed(lambda: L.moe_probe_gather(gsrc, 16 << 20, 4096, order, 512, gsink, 1024, stream), 10)
+        gather[tag] = 1024 * 4 * 512 * 1024 / t / 1e9
+    del gsrc, gsink
     n = 8192
     a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
     b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
@@ -267,6 +277,8 @@ def measure_ceilings(torch, L, stream):
             "device_copy_GBps": round(2 * (1 << 30) / t_copy / 1e9, 1),
             "mfma_bf16_16x16x32_TFLOPs": round(mfma["16x16x32"], 1),
             "mfma_bf16_32x32x16_TFLOPs": round(mfma["32x32x16"], 1),
+            "lds_copy_row_per_lane_GBps": round(gather["row_per_lane"], 1),
+            "lds_copy_four_lanes_per_row_GBps": round(gather["four_lanes_per_row"], 1),
             "vendor_bf16_gemm_TFLOPs": round(2.0 * n ** 3 / t_gemm / 1e12, 1)}
 
 

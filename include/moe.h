@@ -377,9 +377,21 @@ moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t 
  * rounds of independent bf16 MFMAs on register operands (shape 0: eight
  * 16x16x32, 131072 flops per round; shape 1: four 32x32x16, 131072 flops
  * per round), no memory traffic but `sink` (fp32 [n_wg * 256], the sums of
- * the accumulators).  Bad arguments -> MOE_ERR_INVALID_ARG. */
+ * the accumulators).
+ * moe_probe_gather copies 16-row x 64-byte tiles of `src` (rows of
+ * `row_bytes`, a power of two >= 64; bytes / row_bytes a power of two >= 16,
+ * bytes <= 2^31) global -> LDS with the LDS-DMA copy the prefill expert
+ * GEMMs fetch gathered token rows with: each of the n_wg * 4 waves copies
+ * `iters` tiles, tiles w, w + 4 n_wg, ... modulo the tile count, 8 per batch,
+ * with the lanes one row each (order 0: lane l row l % 16, 16-byte chunk
+ * l / 16) or four per 64-byte row segment (order 1: row l / 4, chunk l % 4),
+ * and writes the XOR of the words each wave copied to `sink` (uint32
+ * [n_wg * 4]); with iters * 4 n_wg equal to the tile count every word is
+ * copied once.  Bad arguments -> MOE_ERR_INVALID_ARG. */
 moe_status moe_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t n_wg, hipStream_t stream);
 moe_status moe_probe_mfma(float* sink, int32_t n_wg, int32_t iters, int32_t shape, hipStream_t stream);
+moe_status moe_probe_gather(const void* src, size_t bytes, int32_t row_bytes, int32_t order, int32_t iters,
+                            uint32_t* sink, int32_t n_wg, hipStream_t stream);
 
 /* Per-batch-size hipGraphs of moe_forward (the bucketed decode-step capture
  * of the unsloth commit 80aaf1121b page, second paragraph): one graph per

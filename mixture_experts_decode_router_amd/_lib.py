@@ -41,7 +41,7 @@ EXPORTS = (
     "moe_workspace_views",
     "moe_read_counts", "moe_graph_capture", "moe_graph_replay", "moe_graph_bucket_for",
     "moe_graph_destroy", "moe_forward_prenorm", "moe_graph_capture_prenorm",
-    "moe_backward", "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma",
+    "moe_backward", "moe_forward_noalloc", "moe_probe_read", "moe_probe_mfma", "moe_probe_gather",
 )
 
 
@@ -117,6 +117,7 @@ def lib() -> ctypes.CDLL:
                                     c_void_p, c_void_p]),
         "moe_probe_read": (S, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p]),
         "moe_probe_mfma": (S, [c_void_p, c_int32, c_int32, c_int32, c_void_p]),
+        "moe_probe_gather": (S, [c_void_p, c_size_t, c_int32, c_int32, c_int32, c_void_p, c_int32, c_void_p]),
         "moe_forward_timed": (S, [POINTER(moe_config), POINTER(moe_weights), c_void_p, c_int32,
                                   c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
         "moe_pack_weights": (S, [POINTER(moe_config), POINTER(moe_weights), POINTER(moe_weights), c_void_p]),
@@ -218,6 +219,10 @@ def moe_probe_read(src, nbytes, sink, n_wg, stream=None):
 
 def moe_probe_mfma(sink, n_wg, iters, shape, stream=None):
     _check(lib().moe_probe_mfma(ptr(sink), n_wg, iters, shape, stream_handle(stream)))
+
+
+def moe_probe_gather(src, nbytes, row_bytes, order, iters, sink, n_wg, stream=None):
+    _check(lib().moe_probe_gather(ptr(src), nbytes, row_bytes, order, iters, ptr(sink), n_wg, stream_handle(stream)))
 
 
 def make_prenorm(residual, delta, gamma, eps, residual_out, x_out) -> moe_prenorm:

@@ -733,6 +733,26 @@ moe_status moe_probe_mfma(float* sink, int32_t n_wg, int32_t iters, int32_t shap
   return e == hipSuccess ? MOE_OK : hip_fail(e, "probe launch");
 }
 
+moe_status moe_probe_gather(const void* src, size_t bytes, int32_t row_bytes, int32_t order, int32_t iters,
+                            uint32_t* sink, int32_t n_wg, hipStream_t stream) {
+  MOE_TRY(check_ptr(src, "src"));
+  MOE_TRY(check_ptr(sink, "sink", 4));
+  auto pow2 = [](size_t v) { return v != 0 && (v & (v - 1)) == 0; };
+  if (row_bytes < 64 || !pow2((size_t)row_bytes))
+    return fail(MOE_ERR_INVALID_ARG, "row_bytes must be a power of two >= 64");
+  if (bytes % (size_t)row_bytes || !pow2(bytes / (size_t)row_bytes) || bytes / (size_t)row_bytes < 16 ||
+      bytes > ((size_t)1 << 31))
+    return fail(MOE_ERR_INVALID_ARG, "bytes / row_bytes must be a power of two >= 16, bytes <= 2^31");
+  if (order != 0 && order != 1) return fail(MOE_ERR_INVALID_ARG, "order must be 0 (row per lane) or 1 (row-major)");
+  if (iters < 1 || iters > (1 << 20)) return fail(MOE_ERR_INVALID_ARG, "iters must lie in [1, 2^20]");
+  if (n_wg < 1 || n_wg > 65536) return fail(MOE_ERR_INVALID_ARG, "n_wg must lie in [1, 65536]");
+  uint32_t seg_log = 0;
+  while ((64u << seg_log) < (uint32_t)row_bytes) ++seg_log;
+  const uint32_t tiles = (uint32_t)(bytes / (size_t)row_bytes / 16) << seg_log;
+  const hipError_t e = moe::launch_probe_gather(src, (uint32_t)row_bytes, seg_log, tiles, iters, order, sink, n_wg, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "probe launch");
+}
+
 moe_status moe_read_counts(const moe_config* cfg, const void* workspace, size_t ws_bytes, int32_t* host_counts,
                            hipStream_t stream) {
   MOE_TRY(check_cfg(cfg));

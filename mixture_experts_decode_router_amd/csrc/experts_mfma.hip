@@ -16,9 +16,10 @@
 // needed.  A weight fragment arrives in MFMA operand order.  A token
 // fragment is fetched row by row (lanes 4p .. 4p+3 bring the 64 bytes of
 // row p, in the order of xchunk): the load unit serves four lanes that read
-// one contiguous row segment about 3.5x faster than sixteen lanes that each
-// read another row, which the operand order would need (measured from L2:
-// 33 against 9.3 TB/s).  The MFMA lanes then read their 16 bytes from slot
+// one contiguous row segment about twice as fast as sixteen lanes that each
+// read another row, which the operand order would need (moe_probe_gather
+// over 16 MiB of 4 KiB rows: 20 against 9.7 TB/s).  The MFMA lanes then
+// read their 16 bytes from slot
 // 4r + xchunk(r, g), an order in which every 8 consecutive lanes of a read
 // hit distinct banks.  kRing LDS stages form a ring: loads run
 // kRing - 1 stages ahead of the MFMAs.  Each iteration waits for the wave's

@@ -257,5 +257,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 // n_wg * 256 floats (mfma)
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s);
 hipError_t launch_probe_mfma(float* sink, int n_wg, int iters, int shape, hipStream_t s);
+hipError_t launch_probe_gather(const void* src, uint32_t row_bytes, uint32_t seg_log, uint32_t tiles, int iters,
+                               int order, uint32_t* sink, int n_wg, hipStream_t s);
 
 }  // namespace moe

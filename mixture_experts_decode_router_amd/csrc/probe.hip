@@ -10,6 +10,10 @@
 // mfma:  each wave issues `iters` rounds of independent bf16 MFMAs on
 //        register operands (16x16x32: 8 accumulators; 32x32x16: 4), no
 //        memory traffic, and writes the sum of its accumulators.
+// gather: each wave copies 16-row x 64-byte tiles of a row-major buffer
+//        global -> LDS with global_load_lds_dwordx4, as the prefill expert
+//        GEMMs copy gathered token rows, with the lanes either one row each
+//        (the MFMA operand order) or four per 64-byte row segment.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -94,6 +98,52 @@ __global__ __launch_bounds__(kProbeThreads, 4) void probe_mfma_kernel(float* sin
   sink[(size_t)blockIdx.x * kProbeThreads + l] = s;
 }
 
+typedef __attribute__((address_space(3))) char probe_lds_t;
+#define MOE_P_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Tile u of the buffer: row group u >> seg_log (16 rows), 64-byte segment
+// u & (segs - 1) of each row.  Wave w copies tiles w, w + nwaves, ... (mod
+// the tile count), 8 per batch into its 8 KiB of LDS, then folds the batch
+// into its XOR (one read of each LDS word), so no copy can be dropped.
+__global__ __launch_bounds__(kProbeThreads) void probe_gather_kernel(const uint8_t* src, uint32_t row_bytes,
+                                                                      uint32_t seg_log, uint32_t tiles, int iters,
+                                                                      int order, uint32_t* sink) {
+  __shared__ __attribute__((aligned(1024))) u32x4_t s_buf[kProbeThreads / 64][8][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t nwaves = gridDim.x * (kProbeThreads / 64);
+  uint32_t u = (blockIdx.x * (kProbeThreads / 64) + wave) % tiles;
+  const uint32_t step = nwaves % tiles;
+  const int row = order == 0 ? (lane & 15) : (lane >> 2);
+  const int chunk = order == 0 ? (lane >> 4) : (lane & 3);
+  const size_t lane_off = (size_t)row * row_bytes + chunk * 16;
+  uint32_t acc = 0u;
+  for (int it = 0; it < iters; it += 8) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      if (it + b < iters) {
+        const size_t off = (size_t)(u >> seg_log) * 16 * row_bytes + (size_t)(u & ((1u << seg_log) - 1u)) * 64;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + off + lane_off),
+                                         (probe_lds_t*)&s_buf[wave][b][0], 16, 0, 0);
+        u += step;
+        if (u >= tiles) u -= tiles;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(MOE_P_VMCNT(0));
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      if (it + b < iters) {
+        const u32x4_t v = s_buf[wave][b][lane];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reads are done before the next copies land
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off);
+  if (lane == 0) sink[(size_t)blockIdx.x * (kProbeThreads / 64) + wave] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s) {
@@ -107,6 +157,13 @@ hipError_t launch_probe_mfma(float* sink, int n_wg, int iters, int shape, hipStr
     hipLaunchKernelGGL(probe_mfma_kernel<0>, dim3(n_wg), dim3(kProbeThreads), 0, s, sink, iters);
   else
     hipLaunchKernelGGL(probe_mfma_kernel<1>, dim3(n_wg), dim3(kProbeThreads), 0, s, sink, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_gather(const void* src, uint32_t row_bytes, uint32_t seg_log, uint32_t tiles, int iters,
+                               int order, uint32_t* sink, int n_wg, hipStream_t s) {
+  hipLaunchKernelGGL(probe_gather_kernel, dim3(n_wg), dim3(kProbeThreads), 0, s, static_cast<const uint8_t*>(src),
+                     row_bytes, seg_log, tiles, iters, order, sink);
   return hipGetLastError();
 }
 

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void route_partial(PartParams p) {
 // order), into a private ring of RS steps, RS - 1 of them in flight; then
 // reads its MFMA operands from the xslot positions.  Loaded directly, each
 // lane's 16 bytes come from another row, a pattern the load unit serves
-// about 3.5x slower.  The operands each lane receives, the MFMA sequence and
+// about half as fast.  The operands each lane receives, the MFMA sequence and
 // the split sums are those of route_partial, so the partials are the same
 // bits.  Tiles past E copy tile 0 and are never stored.
 typedef __attribute__((address_space(3))) char lds_char_t;
