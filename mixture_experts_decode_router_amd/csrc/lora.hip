@@ -7,7 +7,8 @@
 // accumulators (the rank-16, fp32-adapter LoRA of the unsloth commit
 // 4f2bfe7f69 page's workload, injected into the grouped GEMMs).
 //
-// One workgroup per item (per 16-row sub-tile of a longer item); K is cut into 64-k blocks, block b going to wave
+// One workgroup per item (per 16-row sub-tile, or per eight of them, of a
+// longer item); K is cut into 64-k blocks, block b going to wave
 // b % 16 (at most four per wave).  The 16 x 16 tile U^T = A[e] (16 x K) *
 // src^T (K x 16 rows) is one fp32 MFMA accumulation per wave over its blocks
 // in order (16x16x4: lane (r, g) feeds A row r and the column of row r,
@@ -28,59 +29,104 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// SUBS: 16-row sub-tiles per workgroup (1 at decode sizes; all eight of a
+// 128-row item on the MFMA path's work list, so each wave loads its A blocks
+// once for 128 rows instead of once per 16).  Per sub-tile the MFMA sequence
+// and the wave-order sum are the same, so a row's U does not depend on SUBS.
+template <int SUBS>
 __global__ __launch_bounds__(64 * kWaves) void lora_a_kernel(LoraAArgs a) {
   __shared__ f32x4_t s_part[kWaves][64];
-  const int item = blockIdx.x / a.subs, sub = blockIdx.x - item * a.subs;
+  const int per = a.subs / SUBS;  // workgroups per work item
+  const int item = blockIdx.x / per, sub0 = (blockIdx.x - item * per) * SUBS;
   if (item >= *a.n_items) return;  // uniform over the workgroup
-  const int e = a.items[2 * item], m0 = a.items[2 * item + 1] + 16 * sub;
+  const int e = a.items[2 * item], m0 = a.items[2 * item + 1] + 16 * sub0;
   const int c = a.counts[e] - m0;
-  if (c <= 0) return;  // a sub-tile past the item's rows
-  const int M = c < 16 ? c : 16, base = a.offsets[e] + m0;
+  if (c <= 0) return;  // sub-tiles past the item's rows
+  const int nt = min((c + 15) / 16, SUBS);  // sub-tiles holding rows
+  const int base = a.offsets[e] + m0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int nb = a.K / 64;                  // 64-k blocks
   const int nw = nb < kWaves ? nb : kWaves;  // waves holding at least one
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[SUBS];
+#pragma unroll
+  for (int t = 0; t < SUBS; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if (wave < nw) {
-    const bool tv = r < M;
-    const int row = tv ? (a.by_token ? a.perm[base + r] / a.k : base + r) : 0;
-    const uint16_t* xr = a.src + (size_t)row * a.K + 16 * g;
+    int row[SUBS];  // this lane's source row in each sub-tile (0 past the rows: its products are never stored)
+#pragma unroll
+    for (int t = 0; t < SUBS; ++t) {
+      const int m = 16 * t + r;
+      row[t] = (t < nt && m < c) ? (a.by_token ? a.perm[base + m] / a.k : base + m) : 0;
+    }
     const float* ar = a.A + ((size_t)e * kRank + r) * a.K + 16 * g;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
-    f32x4_t av[kMaxBlocks][4];
-    u32x4_t xv[kMaxBlocks][2];
+    if constexpr (SUBS == 1) {
+      // all blocks' operands in flight before the first MFMA
+      const bool tv = r < c;
+      const uint16_t* xr = a.src + (size_t)row[0] * a.K + 16 * g;
+      f32x4_t av[kMaxBlocks][4];
+      u32x4_t xv[kMaxBlocks][2];
 #pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i) {
-      const int b = wave + kWaves * i;
-      if (b < nb) {
+      for (int i = 0; i < kMaxBlocks; ++i) {
+        const int b = wave + kWaves * i;
+        if (b < nb) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) av[i][v] = *reinterpret_cast<const f32x4_t*>(ar + 64 * b + 4 * v);
+          for (int v = 0; v < 4; ++v) av[i][v] = *reinterpret_cast<const f32x4_t*>(ar + 64 * b + 4 * v);
 #pragma unroll
-        for (int v = 0; v < 2; ++v) xv[i][v] = tv ? ld16(xr + 64 * b + 8 * v) : zero;
+          for (int v = 0; v < 2; ++v) xv[i][v] = tv ? ld16(xr + 64 * b + 8 * v) : zero;
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i) {
-      if (wave + kWaves * i < nb) {
+      for (int i = 0; i < kMaxBlocks; ++i) {
+        if (wave + kWaves * i < nb) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          const uint32_t w = xv[i][m >> 3][(m & 7) >> 1];
-          acc = mfma_f32(av[i][m >> 2][m & 3], (m & 1) ? bf16hi(w) : bf16lo(w), acc);
+          for (int m = 0; m < 16; ++m) {
+            const uint32_t w = xv[i][m >> 3][(m & 7) >> 1];
+            acc[0] = mfma_f32(av[i][m >> 2][m & 3], (m & 1) ? bf16hi(w) : bf16lo(w), acc[0]);
+          }
+        }
+      }
+    } else {
+      // per block: its A values once, then every sub-tile's rows
+      for (int i = 0; i < kMaxBlocks; ++i) {
+        const int b = wave + kWaves * i;
+        if (b >= nb) break;
+        f32x4_t av[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = *reinterpret_cast<const f32x4_t*>(ar + 64 * b + 4 * v);
+#pragma unroll
+        for (int t = 0; t < SUBS; ++t) {
+          if (t < nt) {
+            const bool tv = 16 * t + r < c;
+            const uint16_t* xr = a.src + (size_t)row[t] * a.K + 16 * g + 64 * b;
+            const u32x4_t xv[2] = {tv ? ld16(xr) : zero, tv ? ld16(xr + 8) : zero};
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+              const uint32_t w = xv[m >> 3][(m & 7) >> 1];
+              acc[t] = mfma_f32(av[m >> 2][m & 3], (m & 1) ? bf16hi(w) : bf16lo(w), acc[t]);
+            }
+          }
         }
       }
     }
   }
-  s_part[wave][lane] = acc;
-  __syncthreads();
   // lane l of each wave holds D[4(l/16) + q][l % 16] = U[row l % 16][j = 4(l/16) + q]
-  if (tid < 256) {
-    const int l = tid & 63, q = tid >> 6;
-    const int tok = l & 15, j = 4 * (l >> 4) + q;
-    if (tok < M) {
-      float sum = 0.f;
-      for (int w = 0; w < nw; ++w) sum += s_part[w][l][q];
-      a.U[(size_t)(base + tok) * kRank + j] = sum;
+  // of each sub-tile; the waves' tiles are added in wave order
+#pragma unroll
+  for (int t = 0; t < SUBS; ++t) {
+    if (t >= nt) break;  // uniform
+    s_part[wave][lane] = acc[t];
+    __syncthreads();
+    if (tid < 256) {
+      const int l = tid & 63, q = tid >> 6;
+      const int tok = l & 15, j = 4 * (l >> 4) + q;
+      if (16 * t + tok < c) {
+        float sum = 0.f;
+        for (int w = 0; w < nw; ++w) sum += s_part[w][l][q];
+        a.U[(size_t)(base + 16 * t + tok) * kRank + j] = sum;
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -351,7 +397,10 @@ hipError_t launch_lora_grad(const BwdArgs& a, bool down, hipStream_t s) {
 hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s) {
   if (a.K % 64 || a.K > 64 * kMaxBlocks * kWaves) return hipErrorInvalidValue;
   if (a.subs < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lora_a_kernel, dim3(a.max_items * a.subs), dim3(64 * kWaves), 0, s, a);
+  if (a.subs % 8 == 0)  // the MFMA path's 128-row items: one workgroup per 8 sub-tiles
+    hipLaunchKernelGGL(lora_a_kernel<8>, dim3(a.max_items * (a.subs / 8)), dim3(64 * kWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL(lora_a_kernel<1>, dim3(a.max_items * a.subs), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 
