@@ -678,10 +678,11 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_nf4_kernel(BwdArgs a) {
   build_lut(s_lut, a.codebook, tid);
   const u32x2_t* s_lutl = lut_copy(s_lut, lane);
 
-  // codes: wave w decodes dwords 2 (w & 1), +1 of chunk w >> 1 = (row tile
-  // (w >> 1) >> 1 of the stage, 128-column block (w >> 1) & 1 of the window;
-  // blocks past ncols decode the last valid block, whose columns are never
-  // stored); dword st of a chunk is the fragment of 32-column block 4 kb + st
+  // codes: wave w decodes dwords 2 (w & 1), +1 of chunk w >> 1, which is
+  // row tile (w >> 1) >> 1 of the stage and 128-column block (w >> 1) & 1 of
+  // the window (blocks past ncols decode the last valid block, whose columns
+  // are never stored); dword st of a chunk is the fragment of 32-column
+  // block 4 kb + st
   const int cw = wave >> 1, dh = wave & 1;
   const int c_rtl = cw >> 1, c_kbw = cw & 1;
   const int c_kb = min(n0 / 128 + c_kbw, nkb - 1);

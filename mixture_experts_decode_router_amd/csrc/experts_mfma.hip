@@ -19,10 +19,9 @@
 // one contiguous row segment about twice as fast as sixteen lanes that each
 // read another row, which the operand order would need (moe_probe_gather
 // over 16 MiB of 4 KiB rows: 20 against 9.7 TB/s).  The MFMA lanes then
-// read their 16 bytes from slot
-// 4r + xchunk(r, g), an order in which every 8 consecutive lanes of a read
-// hit distinct banks.  kRing LDS stages form a ring: loads run
-// kRing - 1 stages ahead of the MFMAs.  Each iteration waits for the wave's
+// read their 16 bytes from slot 4r + xchunk(r, g), an order in which every
+// 8 consecutive lanes of a read hit distinct banks.  kRing LDS stages form a
+// ring: loads run kRing - 1 stages ahead of the MFMAs.  Each iteration waits for the wave's
 // own loads of the stage to be multiplied (s_waitcnt vmcnt), then one barrier
 // publishes the whole stage and retires the buffer the next loads overwrite.
 //
