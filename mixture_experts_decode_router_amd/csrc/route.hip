@@ -289,11 +289,20 @@ __device__ __forceinline__ void route_wait(int later) {  // at most `later` step
   asm volatile("" ::: "memory");  // the LDS reads of the step stay below
 }
 
-template <int NT>
-__global__ __launch_bounds__(256) void route_partial_lds(PartParams p) {
+// W waves per workgroup (4, or 8 where one workgroup sums all K splits of
+// its tokens and the token tiles alone give one workgroup per CU); wave w
+// owns expert tiles w, w + W, ...
+template <int W, int NT>
+constexpr int route_ring() {
+  return W == 4 ? (NT == 1 ? 6 : (NT == 2 ? 5 : 3)) : (NT == 1 ? 3 : 2);  // within 60 KiB of static LDS
+}
+
+template <int NT, int W = 4>
+__global__ __launch_bounds__(64 * W) void route_partial_lds(PartParams p) {
   constexpr int L = 1 + NT;  // copies per wave per step: the token tile, then its expert tiles
-  constexpr int RS = NT == 1 ? 6 : (NT == 2 ? 5 : 3);  // ring steps, within 60 KiB of static LDS
-  __shared__ __attribute__((aligned(1024))) unsigned char s_ring[4][RS][L][1024];
+  constexpr int RS = route_ring<W, NT>();  // ring steps
+  static_assert(W * RS * L <= 60, "static LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char s_ring[W][RS][L][1024];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15;
   const int t0 = blockIdx.x * kTok;
@@ -315,7 +324,7 @@ __global__ __launch_bounds__(256) void route_partial_lds(PartParams p) {
     __builtin_amdgcn_global_load_lds(xs + st * 32, sb, 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const int et = wave + 4 * i < n_et ? wave + 4 * i : 0;
+      const int et = wave + W * i < n_et ? wave + W * i : 0;
       __builtin_amdgcn_global_load_lds(ws + (size_t)et * 16 * H + st * 32, sb + (1 + i) * 1024, 16, 0, 0);
     }
   };
@@ -354,15 +363,15 @@ __global__ __launch_bounds__(256) void route_partial_lds(PartParams p) {
       }
     }
   }
-  // lane holds D[4g+q][r]: expert 16*(wave + 4i) + 4g + q, token r
+  // lane holds D[4g+q][r]: expert 16*(wave + W i) + 4g + q, token r
   if (tv) {
     const int g = lane >> 4;
     float* dl = p.part + ((size_t)blockIdx.y * T + trow) * E;
     float* ds = p.pabs + ((size_t)blockIdx.y * T + trow) * E;
 #pragma unroll
     for (int i = 0; i < NT; ++i)
-      if (wave + 4 * i < n_et) {
-        const int e0 = 16 * (wave + 4 * i) + 4 * g;
+      if (wave + W * i < n_et) {
+        const int e0 = 16 * (wave + W * i) + 4 * g;
         *reinterpret_cast<f32x4_t*>(dl + e0) = lsum[i];
         *reinterpret_cast<f32x4_t*>(ds + e0) = ssum[i];
       }
@@ -847,10 +856,18 @@ void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
 
 // plain token rows: the LDS-staged form; with the pre-block step: the
 // register form, which forms the token operand on the fly
+// plain token rows where one workgroup sums all K splits of its tokens
+// (large T) and there are at least two expert tiles per wave of four: eight
+// waves, half the expert tiles each
+template <int NT>
+bool partial_eight_waves(const PartParams& pp) { return NT >= 2 && pp.per_wg == pp.ks; }
+
 template <int NT>
 void launch_partial(const PartParams& pp, dim3 grid, hipStream_t s) {
   if (pp.res)
     launch_partial<NT, true>(pp, grid, s);
+  else if (partial_eight_waves<NT>(pp))
+    hipLaunchKernelGGL((route_partial_lds<(NT + 1) / 2, 8>), grid, dim3(512), 0, s, pp);
   else
     hipLaunchKernelGGL((route_partial_lds<NT>), grid, dim3(256), 0, s, pp);
 }
@@ -860,7 +877,7 @@ template <int NT>
 const void* partial_fn(const PartParams& pp) {
   const bool u4 = (pp.H / pp.ks) % (32 * 4) == 0;
   if (pp.res) return u4 ? (const void*)&route_partial<NT, 4, true> : (const void*)&route_partial<NT, 1, true>;
-  void (*lds_form)(PartParams) = route_partial_lds<NT>;
+  void (*lds_form)(PartParams) = partial_eight_waves<NT>(pp) ? route_partial_lds<(NT + 1) / 2, 8> : route_partial_lds<NT>;
   return (const void*)lds_form;
 }
 
@@ -884,24 +901,28 @@ hipError_t launch_route(const RouteArgs& a, float* scratch, hipStream_t s, const
   const dim3 pgrid(ntt, nst);
   const int n_et = a.E / 16;
   const void* fn;
+  bool eight = false;  // the eight-wave form (512 threads)
   if (n_et <= 4) {
     launch_partial<1>(pp, pgrid, s);
     fn = partial_fn<1>(pp);
   } else if (n_et <= 8) {
     launch_partial<2>(pp, pgrid, s);
     fn = partial_fn<2>(pp);
+    eight = !pp.res && partial_eight_waves<2>(pp);
   } else if (n_et <= 12) {
     launch_partial<3>(pp, pgrid, s);
     fn = partial_fn<3>(pp);
+    eight = !pp.res && partial_eight_waves<3>(pp);
   } else {
     launch_partial<4>(pp, pgrid, s);
     fn = partial_fn<4>(pp);
+    eight = !pp.res && partial_eight_waves<4>(pp);
   }
   if (node) {
     static_assert(sizeof(PartParams) <= sizeof(node->args), "router node arguments");
     node->fn = const_cast<void*>(fn);
     node->grid = pgrid;
-    node->block = dim3(256);
+    node->block = dim3(eight ? 512 : 256);
     std::memcpy(node->args, &pp, sizeof(pp));
   }
   hipError_t e = hipGetLastError();
