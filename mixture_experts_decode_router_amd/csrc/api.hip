@@ -608,6 +608,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     b.g_b_gate_up = d_lora->d_b_gate_up;
     b.g_a_down = d_lora->d_a_down;
     b.g_b_down = d_lora->d_b_down;
+    // y's memory is free while the adapter gradients are formed (read by the
+    // routing-weight gradients before, rewritten by the gate/up pass after)
+    b.lora_part = at<float>(workspace, L.y);
+    b.lora_part_floats = (size_t)c.t_max * c.top_k * c.hidden;
   }
   hipError_t e;
   // the transposed products run over the forward's work list: 16-row items

@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
   if constexpr (LORA) {  // s A^T z, as in bwd_t_kernel
     const float* la = (MODE == kDown ? a.la_down + (size_t)e * 16 * I : a.la_gate_up + (size_t)e * 16 * H);
     const float* zb = MODE == kDown ? a.z_down : a.z_gate_up;
-    f32x4_t aq[4];
+    f32x4_t aq[4], zq[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int n = min(n0 + wn * 64 + 16 * t + r, ncols - 1);  // columns past ncols are never stored
@@ -599,10 +599,19 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int prow = wm * 64 + 16 * i + r;
-      const f32x4_t zp = prow < M ? ld4f(zb + (size_t)(base + prow) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) add_scaled(acc[i][t], lora_tile(zp, aq[t]), a.lora_scale);
+      zq[i] = prow < M ? ld4f(zb + (size_t)(base + prow) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // each sum is formed here, one tile at a time (the empty asm keeps the
+    // compiler from sinking the adds into the conditional stores below, which
+    // would hold all sixteen rank-16 tiles beside the accumulators)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        add_scaled(acc[i][t], lora_tile(zq[i], aq[t]), a.lora_scale);
+        asm volatile("" : "+v"(acc[i][t]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -802,7 +811,7 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_nf4_kernel(BwdArgs a) {
   if constexpr (LORA) {  // s A^T z, as in bwd_t_kernel
     const float* la = (MODE == kDown ? a.la_down + (size_t)e * 16 * I : a.la_gate_up + (size_t)e * 16 * H);
     const float* zb = MODE == kDown ? a.z_down : a.z_gate_up;
-    f32x4_t aq[4];
+    f32x4_t aq[4], zq[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int n = min(n0 + wn * 64 + 16 * t + r, ncols - 1);  // columns past ncols are never stored
@@ -812,10 +821,19 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_nf4_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int prow = wm * 64 + 16 * i + r;
-      const f32x4_t zp = prow < M ? ld4f(zb + (size_t)(base + prow) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) add_scaled(acc[i][t], lora_tile(zp, aq[t]), a.lora_scale);
+      zq[i] = prow < M ? ld4f(zb + (size_t)(base + prow) * 16 + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // each sum is formed here, one tile at a time (the empty asm keeps the
+    // compiler from sinking the adds into the conditional stores below, which
+    // would hold all sixteen rank-16 tiles beside the accumulators)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        add_scaled(acc[i][t], lora_tile(zq[i], aq[t]), a.lora_scale);
+        asm volatile("" : "+v"(acc[i][t]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

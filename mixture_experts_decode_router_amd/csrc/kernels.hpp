@@ -192,6 +192,8 @@ struct BwdArgs {
   float* g_b_gate_up;
   float* g_a_down;
   float* g_b_down;
+  float* lora_part;           // prefill adapter gradients: per-item partial sums (may reuse y's memory), or null
+  size_t lora_part_floats;    // its capacity
   // top-k weights without renormalisation (unrenorm true): the router's
   // stored split partial logits [r_nst][T][E] and bias (or null), for the
   // softmax over all E experts

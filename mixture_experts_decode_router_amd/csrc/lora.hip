@@ -369,6 +369,145 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(BwdArgs a, int part) {
   }
 }
 
+// The same adapter gradients at prefill sizes, in two passes that spread a
+// heavily routed expert over many workgroups.  Pass 1: one workgroup per
+// (work item, 256 columns of the B or the A gradient); wave w takes 64 of
+// the columns and accumulates, over the item's rows four at a time, the
+// 16 x 16 tiles D_t[i][j] = sum_p data[p][c0 + 4i + t] vec[p][j] (t < 4) with
+// fp32 MFMA 16x16x4 (lane (r, g) feeds row p = 4s + g: columns c0 + 4r .. +3
+// as the A operand of the four tiles, vec[p][r] as the B operand), and stores
+// the item's partial gradient.  Pass 2 adds each expert's item partials in
+// item order, times the scale.  data / vec as in lora_grad_kernel.
+// Partial layout per item: the B part [nB][16], then the A part [16][nA]
+// (the gradients' own layouts, so pass 2 reads and writes contiguously).
+constexpr int kItemCols = 256;
+constexpr int kItemBatch = 8;  // row steps (4 rows each) whose loads are in flight together
+
+template <int PART>
+__global__ __launch_bounds__(256) void lora_grad_item_kernel(BwdArgs a) {
+  __shared__ int s_tok[kMfmaTile];
+  __shared__ float s_w[kMfmaTile];
+  const int item = blockIdx.x;
+  if (item >= *a.n_items) return;  // uniform over the workgroup
+  const int e = a.items[2 * item], m0 = a.items[2 * item + 1];
+  const int cnt = a.counts[e] - m0;
+  const int rows = 16 * a.row_tiles;
+  const int M = cnt < rows ? cnt : rows;
+  if (M <= 0) return;  // an item past the expert's rows (pass 2 skips it)
+  const int base = a.offsets[e] + m0;
+  const int H = a.H, I = a.I, k = a.k;
+  const int nB = PART == 0 ? H : 2 * I, nA = PART == 0 ? I : H;
+  const int gB = (nB + kItemCols - 1) / kItemCols;
+  const bool isB = (int)blockIdx.y < gB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((PART == 0 && isB) || (PART == 1 && !isB)) {
+    // the rows' tokens (and routing weights): token-indexed operands
+    for (int i = tid; i < M; i += 256) {
+      const int slot = a.perm[base + i];
+      s_tok[i] = slot / k;
+      s_w[i] = a.wts[slot];
+    }
+    __syncthreads();
+  }
+  const int n = isB ? nB : nA;
+  const int c0 = (isB ? (int)blockIdx.y : (int)blockIdx.y - gB) * kItemCols + 64 * wave;
+  if (c0 >= n) return;  // no barrier follows
+  const int r = lane & 15, g = lane >> 4;
+  const int c = c0 + 4 * r;  // this lane's four columns
+  const float* vec = PART == 0 ? (isB ? a.u_down : a.z_down) : (isB ? a.u_gate_up : a.z_gate_up);
+  const int nsteps = (M + 3) / 4;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsteps; s0 += kItemBatch) {
+    f32x4_t dv[kItemBatch];
+    float vv[kItemBatch];
+#pragma unroll
+    for (int u = 0; u < kItemBatch; ++u) {
+      const int lr = 4 * (s0 + u) + g;  // the lane's row of this step (item-local)
+      const bool ok = lr < M;
+      const size_t p = (size_t)base + (ok ? lr : 0);
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+      if (ok) {
+        if (PART == 0 && isB) {
+          const f32x4_t o = *reinterpret_cast<const f32x4_t*>(a.d_out + (size_t)s_tok[lr] * H + c);
+          const float w = s_w[lr];
+          d = f32x4_t{w * o[0], w * o[1], w * o[2], w * o[3]};
+        } else if (PART == 0) {
+          const f32x4_t gg = *reinterpret_cast<const f32x4_t*>(a.gu + p * 2 * I + c);
+          const f32x4_t uu = *reinterpret_cast<const f32x4_t*>(a.gu + p * 2 * I + I + c);
+          d = f32x4_t{silu(gg[0]) * uu[0], silu(gg[1]) * uu[1], silu(gg[2]) * uu[2], silu(gg[3]) * uu[3]};
+        } else if (isB) {
+          d = *reinterpret_cast<const f32x4_t*>(a.gu + p * 2 * I + c);
+        } else {
+          const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(a.x + (size_t)s_tok[lr] * H + c);
+          d = f32x4_t{bf16lo(xv[0]), bf16hi(xv[0]), bf16lo(xv[1]), bf16hi(xv[1])};
+        }
+      }
+      dv[u] = d;
+      vv[u] = ok ? vec[p * kRank + r] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kItemBatch; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = mfma_f32(dv[u][t], vv[u], acc[t]);
+  }
+  // lane (r, g) holds D_t[4g + q][r]: column c0 + 16g + 4q + t, rank index r
+  float* P = a.lora_part + (size_t)item * (nB + nA) * kRank;
+  if (isB) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) P[(size_t)(c0 + 16 * g + 4 * q + t) * kRank + r] = acc[t][q];
+  } else {
+    float* PA = P + (size_t)nB * kRank + (size_t)r * nA + c0 + 16 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4_t*>(PA + 4 * q) = f32x4_t{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
+  }
+}
+
+// Pass 2: workgroup (chunk of 1024 floats, expert e) adds the partials of
+// e's items in item order (items of one expert are consecutive in the work
+// list; items past the expert's rows hold nothing and are skipped); zero
+// for an expert no row reached.
+__global__ __launch_bounds__(256) void lora_grad_reduce_kernel(BwdArgs a, int part) {
+  const int e = blockIdx.y;
+  const int H = a.H, I = a.I;
+  const int nB = part == 0 ? H : 2 * I, nA = part == 0 ? I : H;
+  const int nitems = *a.n_items;
+  // e's items: [i0, i1) = (items of experts < e, items of experts <= e)
+  int i0 = 0, i1 = 0;
+  for (int c0 = 0; c0 < nitems; c0 += 256) {
+    const int i = c0 + (int)threadIdx.x;
+    const int ei = i < nitems ? a.items[2 * i] : INT_MAX;
+    i0 += __syncthreads_count(ei < e);
+    i1 += __syncthreads_count(ei <= e);
+  }
+  const int per = (nB + nA) * kRank;  // floats per item
+  const int v = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (v >= per) return;
+  const int cnt = a.counts[e];
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  for (int i = i0; i < i1; i += 4) {  // four items' loads in flight, added in item order
+    f32x4_t pv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = i + u < i1 && a.items[2 * (i + u) + 1] < cnt;
+      pv[u] = ok ? *reinterpret_cast<const f32x4_t*>(a.lora_part + (size_t)(i + u) * per + v) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += pv[u];
+  }
+  const float sc = a.lora_scale;
+  const f32x4_t o = {sc * s[0], sc * s[1], sc * s[2], sc * s[3]};
+  if (v < nB * kRank)
+    *reinterpret_cast<f32x4_t*>((part == 0 ? a.g_b_down : a.g_b_gate_up) + (size_t)e * nB * kRank + v) = o;
+  else
+    *reinterpret_cast<f32x4_t*>((part == 0 ? a.g_a_down : a.g_a_gate_up) + (size_t)e * kRank * nA + v - nB * kRank) =
+        o;
+}
+
 }  // namespace
 
 hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s) {
@@ -382,8 +521,18 @@ hipError_t launch_lora_bt(const BwdArgs& a, bool down, hipStream_t s) {
 
 hipError_t launch_lora_grad(const BwdArgs& a, bool down, hipStream_t s) {
   const int nB = down ? a.H : 2 * a.I, nA = down ? a.I : a.H;
-  // prefill sizes (on average >= 32 routed rows per expert): 8 row groups
-  if ((long)a.T * a.k >= 32L * a.E) {
+  // prefill sizes with room for every item's partial: per-item MFMA pass,
+  // then the ordered sum over each expert's items
+  if (a.lora_part && (long)a.T * a.k >= 32L * a.E && nB % 64 == 0 && nA % 64 == 0 &&
+      16 * a.row_tiles <= kMfmaTile && (size_t)a.max_items * (nB + nA) * kRank <= a.lora_part_floats) {
+    const int groups = (nB + kItemCols - 1) / kItemCols + (nA + kItemCols - 1) / kItemCols;
+    if (down)
+      hipLaunchKernelGGL(lora_grad_item_kernel<0>, dim3(a.max_items, groups), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(lora_grad_item_kernel<1>, dim3(a.max_items, groups), dim3(256), 0, s, a);
+    const int per4 = (nB + nA) * kRank / 4;
+    hipLaunchKernelGGL(lora_grad_reduce_kernel, dim3((per4 + 255) / 256, a.E), dim3(256), 0, s, a, down ? 0 : 1);
+  } else if ((long)a.T * a.k >= 32L * a.E) {  // prefill sizes (on average >= 32 routed rows per expert): 8 row groups
     constexpr int cols = 256 / 8;
     hipLaunchKernelGGL(lora_grad_kernel<8>, dim3((nB + cols - 1) / cols + (nA + cols - 1) / cols, a.E), dim3(256), 0,
                        s, a, down ? 0 : 1);
