@@ -437,12 +437,15 @@ __global__ __launch_bounds__(64) void bwd_t_kernel(BwdArgs a) {
 // over the 128-row items of the MFMA forward's work list, as LDS-tiled MFMA
 // GEMMs: a 512-thread workgroup owns an item's 128 rows x 256 columns n; 8
 // waves, each 64 rows x 64 columns as 4 x 4 MFMA 16x16x32 tiles.  Per 32-m
-// stage every wave loads its share of the weight fragments (2 row tiles x 8
-// column blocks, each one contiguous kilobyte of the tiled layout) and of
-// the rows' v (fp32, rounded to bf16: hi, and lo = v - hi where HILO) one
-// stage ahead into registers and writes them to one of two LDS buffers in
-// MFMA operand order; a lane's B operand (column n, m = 8g .. 8g+7) is read
-// straight out of the weight fragments with transposing LDS reads.  The
+// stage the waves copy global -> LDS (the load unit's LDS path, no
+// registers) the stage's weight fragments (2 row tiles x 8 column blocks,
+// each one contiguous kilobyte of the tiled layout) into a 3-stage ring,
+// two stages ahead, and the rows' fp32 v into a 2-stage ring, one stage
+// ahead; a lane's A operand is its row's v, scaled and rounded to bf16 as it
+// is read (hi, and lo = v - hi where HILO), its B operand (column n, m = 8g
+// .. 8g+7) is read straight out of the weight fragments with transposing LDS
+// reads.  The loop's LDS reads and waits are explicit (asm): the compiler
+// would otherwise wait for every copy in flight before each read.  The
 // operands, the lanes' m assignment and the m order are those of
 // bwd_t_kernel, so every output is the same bits as there: a row's gradient
 // does not depend on the batch.  Epilogues as in bwd_t_kernel.
@@ -454,15 +457,48 @@ constexpr int kBgVFrags = kMfmaTile / 16;        // v fragments per stage (hi or
 constexpr int kBgWLoads = kBgWFrags / kBgWaves;  // weight fragments per wave per stage
 static_assert(kMfmaTile == 128 && kBgWFrags % kBgWaves == 0, "transposed GEMM tiles");
 
-template <bool HL>
-constexpr int bg_stage_bytes() { return (kBgWFrags + kBgVFrags * (HL ? 2 : 1)) * 1024; }
+constexpr int kBgWRing = 3;                      // weight stages in LDS (two in flight)
+constexpr int kBgWStage = kBgWFrags * 1024;      // weight bytes per stage
+constexpr int kBgVStage = kMfmaTile * 32 * 4;    // v bytes per stage: 128 rows x 32 m, fp32
+constexpr int kBgLds = kBgWRing * kBgWStage + 2 * kBgVStage;  // two v stages (one in flight)
+constexpr int kBgVLoads = kBgVStage / 1024 / kBgWaves;        // v copies per wave per stage
+typedef __attribute__((address_space(3))) void bg_lds_t;
+// s_waitcnt vmcnt(n) with the other counters left free (vmcnt[3:0] |
+// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
+#define BG_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// LDS accesses of the transposed GEMM's loop, in asm: the compiler cannot
+// tell which LDS bytes the LDS-DMA copies in flight write, and waits for all
+// of them before any LDS access it emits itself.  Ordering comes from the
+// explicit waits and barriers of the loop.
+__device__ __forceinline__ uint32_t bg_lds_addr(const unsigned char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+// the four transposed B operands of a stage (two 8-byte transposing reads
+// each, 64 bytes apart), waited for in the same asm block
+__device__ __forceinline__ void bg_read_tr(const unsigned char* wb, const int (&tr)[4], u32x4_t (&bop)[4]) {
+  u32x2_t r[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:64\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:64\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(bg_lds_addr(wb + tr[0])), "v"(bg_lds_addr(wb + tr[1])), "v"(bg_lds_addr(wb + tr[2])),
+        "v"(bg_lds_addr(wb + tr[3]))
+      : "memory");
+#pragma unroll
+  for (int t = 0; t < 4; ++t) bop[t] = u32x4_t{r[2 * t][0], r[2 * t][1], r[2 * t + 1][0], r[2 * t + 1][1]};
+}
 
 template <int MODE, bool LORA, bool HILO>
 __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
   constexpr bool kHiLo = HILO && MODE == kDown;
-  constexpr int kStageBytes = bg_stage_bytes<kHiLo>();
-  constexpr int kVBase = kBgWFrags * 1024;  // v fragments follow the weights in a stage
-  __shared__ __attribute__((aligned(1024))) unsigned char s_buf[2 * kStageBytes];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char s_dyn[];
   const int I = a.I, H = a.H;
   const int ncols = MODE == kDown ? I : H;      // n
   const int nrows = MODE == kDown ? H : 2 * I;  // m
@@ -482,7 +518,8 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
 
   // weights: this wave's fragments f = kBgWLoads * wave + i of a stage (row
   // tile f / 8 of the stage, column block f % 8 of the window; blocks past
-  // ncols load the last valid block, whose columns are never stored)
+  // ncols load the last valid block, whose columns are never stored), copied
+  // global -> LDS by the load unit (lane j's 16 bytes to fragment byte 16 j)
   const uint16_t* wsrc[kBgWLoads];
 #pragma unroll
   for (int i = 0; i < kBgWLoads; ++i) {
@@ -491,45 +528,60 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
     wsrc[i] = W + ((rt0 + (f >> 3)) * nkb + kb) * 512 + lane * 8;
   }
   const size_t wstep = (size_t)2 * nkb * 512;  // elements per 32-m stage (two row tiles)
-  // v rows: thread t brings row p = t / 4 (a valid row when p >= M, times 0),
-  // m = 8 (t % 4) .. +7 of each stage
-  const int vp = tid >> 2, vg = tid & 3;
-  const int vpc = vp < M ? vp : 0;
-  const float* vrow;
-  float vw;
-  if (MODE == kDown) {
-    const int slot = a.perm[base + vpc];
-    vrow = a.d_out + (size_t)(slot / a.k) * H + 8 * vg;
-    vw = vp < M ? a.wts[slot] : 0.f;
-  } else {
-    vrow = a.gu + (size_t)(base + vpc) * 2 * I + 8 * vg;
-    vw = vp < M ? 1.f : 0.f;
-  }
-  const int v_off = kVBase + (vp >> 4) * 1024 + (16 * vg + (vp & 15)) * 16;  // MFMA operand order
-  u32x4_t wr[kBgWLoads];
-  f32x4_t v0, v1;
-  auto load = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < kBgWLoads; ++i) wr[i] = ld16_stream(wsrc[i] + st * wstep);
-    v0 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * st);
-    v1 = *reinterpret_cast<const f32x4_t*>(vrow + 32 * st + 4);
-  };
-  auto store = [&](int buf) {
-    unsigned char* sb = s_buf + buf * kStageBytes;
+  auto wring = [&](int st) { return s_dyn + (st % kBgWRing) * kBgWStage; };
+  auto vbuf = [&](int st) { return s_dyn + kBgWRing * kBgWStage + (st & 1) * kBgVStage; };
+  // the copies of stage st into its ring slot; past the last stage, the last
+  // stage's weights again into the slot of stage st, which no later stage reads
+  // (so every stage issues the same number of copies and the counts stay exact)
+  auto issue_w = [&](int st) {
+    const int src = min(st, nsteps - 1);
 #pragma unroll
     for (int i = 0; i < kBgWLoads; ++i)
-      *reinterpret_cast<u32x4_t*>(sb + (kBgWLoads * wave + i) * 1024 + lane * 16) = wr[i];
-    const float t[8] = {vw * v0[0], vw * v0[1], vw * v0[2], vw * v0[3],
-                        vw * v1[0], vw * v1[1], vw * v1[2], vw * v1[3]};
-    u32x4_t hi, lo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hi[i] = pack_bf16x2(t[2 * i], t[2 * i + 1]);
-      lo[i] = pack_bf16x2(t[2 * i] - bf16lo(hi[i]), t[2 * i + 1] - bf16hi(hi[i]));
-    }
-    *reinterpret_cast<u32x4_t*>(sb + v_off) = hi;
-    if constexpr (kHiLo) *reinterpret_cast<u32x4_t*>(sb + v_off + kBgVFrags * 1024) = lo;
+      __builtin_amdgcn_global_load_lds(wsrc[i] + src * wstep, (bg_lds_t*)(wring(st) + (kBgWLoads * wave + i) * 1024),
+                                       16, 0, 0);
   };
+  // v rows (fp32: w d_out[token] or (d_g, d_u)), copied global -> LDS like the
+  // weights: 16-byte slot s of a stage holds chunk (s & 7) ^ sw(row) of row
+  // s >> 3 (m = 4 chunk .. +3), sw(row) = bits 1-2 of the row, so a lane's
+  // two 16-byte reads of one row (row r of a tile, chunks 2g, 2g + 1) meet
+  // no bank conflicts over 8 consecutive rows.  Rows past the item copy row
+  // 0 and are scaled by 0.
+  const float* vsrc[kBgVLoads];
+#pragma unroll
+  for (int j = 0; j < kBgVLoads; ++j) {
+    const int slot = (kBgVLoads * wave + j) * 64 + lane;
+    const int row = slot >> 3, ch = (slot & 7) ^ ((row >> 1) & 3);
+    const int rc = row < M ? row : 0;
+    const float* rp;
+    if (MODE == kDown)
+      rp = a.d_out + (size_t)(a.perm[base + rc] / a.k) * H;
+    else
+      rp = a.gu + (size_t)(base + rc) * 2 * I;
+    vsrc[j] = rp + 4 * ch;
+  }
+  auto issue_v = [&](int st) {
+    const int src = min(st, nsteps - 1);
+#pragma unroll
+    for (int j = 0; j < kBgVLoads; ++j)
+      __builtin_amdgcn_global_load_lds(vsrc[j] + 32 * src, (bg_lds_t*)(vbuf(st) + (kBgVLoads * wave + j) * 1024), 16,
+                                       0, 0);
+  };
+  // the scale of this lane's A-operand row in each of the wave's row tiles
+  const int r_ = lane & 15, g_ = lane >> 4;
+  float vw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 64 + 16 * i + r_;
+    vw[i] = row < M ? (MODE == kDown ? a.wts[a.perm[base + row]] : 1.f) : 0.f;
+  }
+  // byte offsets of the lane's two chunks of row 16 i + r_ (of the wave's 64)
+  int voff[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 64 + 16 * i + r_;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) voff[i][c] = (row * 8 + ((2 * g_ + c) ^ ((row >> 1) & 3))) * 16;
+  }
   // transposing reads of the weight fragments: lane (s, G) supplies row
   // 8G + (s >> 2) (row tile G >> 1 of the stage, row (8G + (s >> 2)) & 15 in
   // it) and 4 columns from 16 (t & 1) + 4 (s & 3) of column block t >> 1 of
@@ -550,39 +602,47 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load(0);
+  // issue order W(0), v(0), W(1), then per stage v(st + 1), W(st + 2): at the
+  // top of stage st only W(st + 1)'s copies may still be in flight
+  issue_w(0);
+  issue_v(0);
+  issue_w(1);
   for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    store(buf);
-    __syncthreads();  // stage st in LDS; every wave is done with stage st - 1's buffer
-    if (st + 1 < nsteps) load(st + 1);  // in flight during this stage's MFMAs
+    __builtin_amdgcn_s_waitcnt(BG_VMCNT(kBgWLoads));
+    // every wave's copies of stage st are in LDS, and every wave is done with
+    // stage st - 1 (whose v buffer v(st + 1) and weight slot W(st + 2) reuse)
+    asm volatile("s_barrier" ::: "memory");
+    issue_v(st + 1);
+    issue_w(st + 2);
     if (nj > 0) {
-      const unsigned char* sb = s_buf + buf * kStageBytes;
+      const unsigned char* wb = wring(st);
+      const unsigned char* vb = vbuf(st);
       u32x4_t bop[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + tr_byte[t]));
-        const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(sb + tr_byte[t] + 64));
-        bop[t] = u32x4_t{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                         (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                         (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                         (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-      }
+      bg_read_tr(wb, tr_byte, bop);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i >= nj) break;
-        const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(sb + kVBase + (wm * 4 + i) * 1024 + lane * 16);
-        u32x4_t al;
-        if constexpr (kHiLo)
-          al = *reinterpret_cast<const u32x4_t*>(sb + kVBase + (kBgVFrags + wm * 4 + i) * 1024 + lane * 16);
+        // the A operand: w v rounded to bf16 (hi, and lo = w v - hi)
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vb + voff[i][0]);
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vb + voff[i][1]);
+        const float t[8] = {vw[i] * v0[0], vw[i] * v0[1], vw[i] * v0[2], vw[i] * v0[3],
+                            vw[i] * v1[0], vw[i] * v1[1], vw[i] * v1[2], vw[i] * v1[3]};
+        u32x4_t ah, al;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc[i][t] = mfma16(ah, bop[t], acc[i][t]);
-          if constexpr (kHiLo) acc[i][t] = mfma16(al, bop[t], acc[i][t]);
+        for (int q = 0; q < 4; ++q) {
+          ah[q] = pack_bf16x2(t[2 * q], t[2 * q + 1]);
+          if constexpr (kHiLo) al[q] = pack_bf16x2(t[2 * q] - bf16lo(ah[q]), t[2 * q + 1] - bf16hi(ah[q]));
+        }
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          acc[i][t4] = mfma16(ah, bop[t4], acc[i][t4]);
+          if constexpr (kHiLo) acc[i][t4] = mfma16(al, bop[t4], acc[i][t4]);
         }
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads are done before the next barrier
   }
+  __builtin_amdgcn_s_waitcnt(BG_VMCNT(0));  // no copy into LDS outlives the workgroup
   // lane (r, g) holds D[row 4g + q][column r] of tile (i, t): row
   // wm * 64 + 16 i + 4g + q of the item, column n0 + wn * 64 + 16 t + r
   const int r = lane & 15, g = lane >> 4;
@@ -1043,9 +1103,22 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdArgs a) {
   *reinterpret_cast<f32x4_t*>(dx) = acc;
 }
 
+// dynamic LDS beyond 64 KiB needs the per-function limit raised, once per device
 template <int MODE, bool LORA, bool HILO>
 hipError_t launch_bg(const BwdArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, LORA, HILO>), grid, dim3(kBgThreads), 0, s, a);
+  constexpr int lds = kBgLds;
+  static bool done[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!done[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_gemm_kernel<MODE, LORA, HILO>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    done[dev] = true;
+  }
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, LORA, HILO>), grid, dim3(kBgThreads), lds, s, a);
   return hipGetLastError();
 }
 
