@@ -220,6 +220,35 @@ def test_backward_at_prefill_sizes(T):
     assert np.array_equal(s_x, d_x[:24]) and np.array_equal(s_w, d_w[:24])
 
 
+def test_backward_lora_adapter_gradients_both_prefill_forms():
+    # T*k >= 32*E: the adapter gradients are formed per 128-row work item
+    # (partial sums in y's memory, then an ordered sum over each expert's
+    # items) where every item's partial fits there, else per expert with 8
+    # row groups.  tiny at T = 256: with t_max = 1024 both passes take the
+    # item form; with t_max = 256 the gate/up pass's partials do not fit and
+    # it takes the row-group form.  Both against the oracle; d_x, d_w and the
+    # down-adapter gradients (the same form in both) the same bits
+    inp = workload("tiny", 256)
+    d_out = d_out_for(inp.T, inp.H, seed=31)
+    d = S.lora_adapters(inp.E, inp.H, inp.I, seed=5)
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), oracle_weights("tiny"), lora=O.LoRA(**d))
+    res = {}
+    for t_max in (1024, 256):
+        lay = MoELayer(inp, t_max=t_max, train=True).with_lora(d)
+        say(f"[gpu] backward tiny T={inp.T} t_max={t_max} with LoRA")
+        res[t_max] = gpu_backward_lora(lay, inp.x, d_out)
+        d_x, d_w, g = res[t_max]
+        errs = {"d_x": rel(d_x, ref["d_x"]), "d_w": rel(d_w, ref["d_w"])}
+        for n in LORA_NAMES:
+            errs[n] = rel(g[n], ref["d_" + n])
+        say("[gpu]   max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+        assert errs["d_x"] <= TOL_BF16 and errs["d_w"] <= TOL_BF16
+        assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
+    a, b = res[1024], res[256]
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[2]["a_down"], b[2]["a_down"]) and np.array_equal(a[2]["b_down"], b[2]["b_down"])
+
+
 def test_training_forward_gives_the_same_output():
     inp = workload("q64", 64)
     base = layer("q64", 64)
