@@ -262,8 +262,15 @@ __global__ __launch_bounds__(kThreads, kWaves / 4 * kBlocksPerCU) void expert_mf
         brow = (size_t)e * H + min(nt * kBN + (wn * kNT + i) * 16 + r, H - 1);  // rows past H are never stored
       }
       const f32x4_t bq = ld4f((GATE_UP ? a.lb_gate_up : a.lb_down) + brow * 16 + 4 * g);
+      // each sum is formed here, one tile at a time (the empty asm keeps the
+      // compiler from sinking the adds into the stores below, which would
+      // hold every rank-16 tile beside the accumulators)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) add_scaled(acc[i][j], lora_tile(bq, uq[j]), a.lora_scale);
+      for (int j = 0; j < 4; ++j) {
+        add_scaled(acc[i][j], lora_tile(bq, uq[j]), a.lora_scale);
+        asm volatile("" : "+v"(acc[i][j]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   if (GATE_UP) {
