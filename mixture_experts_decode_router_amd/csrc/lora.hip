@@ -11,9 +11,10 @@
 // longer item); K is cut into 64-k blocks, block b going to wave
 // b % 16 (at most four per wave).  The 16 x 16 tile U^T = A[e] (16 x K) *
 // src^T (K x 16 rows) is one fp32 MFMA accumulation per wave over its blocks
-// in order (16x16x4: lane (r, g) feeds A row r and the column of row r,
-// k = 16g + i in the i-th MFMA of a block, so every lane reads 16 consecutive
-// k of each operand); the waves' tiles are then added in wave order.  A row's U depends only on its input row and expert, never
+// in order (16x16x4: lane (r, g) feeds A row r and the column of row r, in
+// the i-th MFMA of a block k = 8g + i for i < 8 and 32 + 8g + i - 8 after,
+// so that the four lanes of a row read each of its two 64-byte halves of the
+// block together); the waves' tiles are then added in wave order.  A row's U depends only on its input row and expert, never
 // on the batch.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -24,6 +25,10 @@ namespace {
 constexpr int kRank = 16;
 constexpr int kWaves = 16;
 constexpr int kMaxBlocks = 4;  // 64-k blocks per wave (K <= 64 * 4 * 16 = 4096)
+
+// float offset of the v-th group of four A values of a lane in a 64-k block
+// (k = 8g + 4v for v < 2, 32 + 8g + 4(v - 2) after; the lane base holds 8g)
+__device__ __forceinline__ int a_off(int v) { return v < 2 ? 4 * v : 32 + 4 * (v - 2); }
 
 __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -58,12 +63,12 @@ __global__ __launch_bounds__(64 * kWaves) void lora_a_kernel(LoraAArgs a) {
       const int m = 16 * t + r;
       row[t] = (t < nt && m < c) ? (a.by_token ? a.perm[base + m] / a.k : base + m) : 0;
     }
-    const float* ar = a.A + ((size_t)e * kRank + r) * a.K + 16 * g;
+    const float* ar = a.A + ((size_t)e * kRank + r) * a.K + 8 * g;
     const u32x4_t zero = {0u, 0u, 0u, 0u};
     if constexpr (SUBS == 1) {
       // all blocks' operands in flight before the first MFMA
       const bool tv = r < c;
-      const uint16_t* xr = a.src + (size_t)row[0] * a.K + 16 * g;
+      const uint16_t* xr = a.src + (size_t)row[0] * a.K + 8 * g;
       f32x4_t av[kMaxBlocks][4];
       u32x4_t xv[kMaxBlocks][2];
 #pragma unroll
@@ -71,9 +76,9 @@ __global__ __launch_bounds__(64 * kWaves) void lora_a_kernel(LoraAArgs a) {
         const int b = wave + kWaves * i;
         if (b < nb) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) av[i][v] = *reinterpret_cast<const f32x4_t*>(ar + 64 * b + 4 * v);
+          for (int v = 0; v < 4; ++v) av[i][v] = *reinterpret_cast<const f32x4_t*>(ar + 64 * b + a_off(v));
 #pragma unroll
-          for (int v = 0; v < 2; ++v) xv[i][v] = tv ? ld16(xr + 64 * b + 8 * v) : zero;
+          for (int v = 0; v < 2; ++v) xv[i][v] = tv ? ld16(xr + 64 * b + 32 * v) : zero;
         }
       }
 #pragma unroll
@@ -93,13 +98,13 @@ __global__ __launch_bounds__(64 * kWaves) void lora_a_kernel(LoraAArgs a) {
         if (b >= nb) break;
         f32x4_t av[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) av[v] = *reinterpret_cast<const f32x4_t*>(ar + 64 * b + 4 * v);
+        for (int v = 0; v < 4; ++v) av[v] = *reinterpret_cast<const f32x4_t*>(ar + 64 * b + a_off(v));
 #pragma unroll
         for (int t = 0; t < SUBS; ++t) {
           if (t < nt) {
             const bool tv = 16 * t + r < c;
-            const uint16_t* xr = a.src + (size_t)row[t] * a.K + 16 * g + 64 * b;
-            const u32x4_t xv[2] = {tv ? ld16(xr) : zero, tv ? ld16(xr + 8) : zero};
+            const uint16_t* xr = a.src + (size_t)row[t] * a.K + 8 * g + 64 * b;
+            const u32x4_t xv[2] = {tv ? ld16(xr) : zero, tv ? ld16(xr + 32) : zero};
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
               const uint32_t w = xv[m >> 3][(m & 7) >> 1];
