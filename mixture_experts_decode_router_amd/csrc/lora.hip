@@ -139,8 +139,10 @@ __global__ __launch_bounds__(64 * kWaves) void lora_a_kernel(LoraAArgs a) {
 // Sixteen adapter rows j times the (up to 16) routed rows of a work item,
 // reduced over K in 64-k blocks spread over the waves as in lora_a_kernel:
 //   out[tok][j] = sum_k P(j, k) Q(tok, k)
-// fetch(r, k0, p, q) gives lane row r's 16 consecutive k from k0 of both
-// operands (P row j = r as the MFMA A operand, Q row tok = r as B).  The
+// fetch(r, k0, p, q) gives lane row r's 16 k of both operands (P row j = r
+// as the MFMA A operand, Q row tok = r as B): element 4v + i is k = k0 + 16v
+// + i, with k0 = 64b + 4g, so that the four lanes of a row read 64
+// contiguous bytes of it in each of their four 16-byte loads.  The
 // waves' tiles are added in wave order.  Ends with a barrier, so s_part can
 // be used again.
 template <typename Fetch>
@@ -156,7 +158,7 @@ __device__ __forceinline__ void rank16_reduce(int nb, int M, float* out, f32x4_t
       const int b = wave + kWaves * i;
       if (b < nb) {
         float p[16], q[16];
-        fetch(r, 64 * b + 16 * g, p, q);
+        fetch(r, 64 * b + 4 * g, p, q);
 #pragma unroll
         for (int m = 0; m < 16; ++m) acc = mfma_f32(p[m], q[m], acc);
       }
@@ -211,12 +213,12 @@ __global__ __launch_bounds__(64 * kWaves) void lora_bt_kernel(BwdArgs a, int mod
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const f32x4_t vv = tv ? *reinterpret_cast<const f32x4_t*>(vrow + k0 + 4 * v) : zero;
+      const f32x4_t vv = tv ? *reinterpret_cast<const f32x4_t*>(vrow + k0 + 16 * v) : zero;
 #pragma unroll
       for (int i = 0; i < 4; ++i) q[4 * v + i] = vs * vv[i];
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) p[m] = B[(size_t)(k0 + m) * kRank + r];
+    for (int m = 0; m < 16; ++m) p[m] = B[(size_t)(k0 + 16 * (m >> 2) + (m & 3)) * kRank + r];
   });
   if (!down) return;
   const float* A = a.la_down + (size_t)e * kRank * I;
@@ -226,9 +228,9 @@ __global__ __launch_bounds__(64 * kWaves) void lora_bt_kernel(BwdArgs a, int mod
     const float* gp = a.gu + (size_t)(tv ? base + r : 0) * 2 * I + k0;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const f32x4_t gv = tv ? *reinterpret_cast<const f32x4_t*>(gp + 4 * v) : zero;
-      const f32x4_t uv = tv ? *reinterpret_cast<const f32x4_t*>(gp + I + 4 * v) : zero;
-      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(A + (size_t)r * I + k0 + 4 * v);
+      const f32x4_t gv = tv ? *reinterpret_cast<const f32x4_t*>(gp + 16 * v) : zero;
+      const f32x4_t uv = tv ? *reinterpret_cast<const f32x4_t*>(gp + I + 16 * v) : zero;
+      const f32x4_t av = *reinterpret_cast<const f32x4_t*>(A + (size_t)r * I + k0 + 16 * v);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         q[4 * v + i] = silu(gv[i]) * uv[i];
