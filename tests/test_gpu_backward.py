@@ -249,6 +249,40 @@ def test_backward_lora_adapter_gradients_both_prefill_forms():
     assert np.array_equal(a[2]["a_down"], b[2]["a_down"]) and np.array_equal(a[2]["b_down"], b[2]["b_down"])
 
 
+@pytest.mark.parametrize("T", [300, 700])
+def test_backward_bf16_at_prefill_sizes_ragged_tiles(T):
+    # bf16 weights at T*k >= 32*E with H = 384 and I = 128: the gate/up pass's
+    # second 256-column tile and the down pass's only one are partly past the
+    # columns (their copies clamp to the last column block, those columns are
+    # never stored), and the last item of each expert is partly past its rows;
+    # against the oracle, with and without adapters, and the rows the same
+    # bits as a decode-sized call's (16-row GEMVs)
+    inp = S.make_small(T, 384, 16, 2, 128, seed=T + 11, bias=True)
+    d_out = d_out_for(inp.T, inp.H, seed=53)
+    lay = MoELayer(inp, t_max=T, train=True)
+    say(f"[gpu] backward bf16 H=384 I=128 at prefill size T={T}")
+    d_x, d_w = gpu_backward(lay, inp.x, d_out)
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), O.ExpertWeights(inp))
+    assert np.array_equal(lay.views(inp.T)["ids"].cpu().numpy(), ref["routing"]["ids"])
+    ex, ew = rel(d_x, ref["d_x"]), rel(d_w, ref["d_w"])
+    say(f"[gpu]   d_x {ex:.3e}, d_w {ew:.3e}")
+    assert ex <= TOL_BF16 and ew <= TOL_BF16
+    s_x, s_w = gpu_backward(lay, inp.x[:24], d_out[:24])
+    assert np.array_equal(s_x, d_x[:24]) and np.array_equal(s_w, d_w[:24])
+    d = S.lora_adapters(inp.E, inp.H, inp.I, seed=T)
+    ll = lay.with_lora(d)
+    d_x, d_w, g = gpu_backward_lora(ll, inp.x, d_out)
+    ref = O.backward_per_token(inp, d_out.astype(np.float64), O.ExpertWeights(inp), lora=O.LoRA(**d))
+    errs = {"d_x": rel(d_x, ref["d_x"]), "d_w": rel(d_w, ref["d_w"])}
+    for n in LORA_NAMES:
+        errs[n] = rel(g[n], ref["d_" + n])
+    say("[gpu]   with LoRA max|err|/rms " + ", ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert errs["d_x"] <= TOL_BF16 and errs["d_w"] <= TOL_BF16
+    assert all(errs[n] <= TOL_LORA_GRAD for n in LORA_NAMES)
+    s_x, s_w, _ = gpu_backward_lora(ll, inp.x[:24], d_out[:24])
+    assert np.array_equal(s_x, d_x[:24]) and np.array_equal(s_w, d_w[:24])
+
+
 def test_training_forward_gives_the_same_output():
     inp = workload("q64", 64)
     base = layer("q64", 64)
