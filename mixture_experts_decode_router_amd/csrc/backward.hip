@@ -96,33 +96,46 @@ __device__ void router_share_all(const BwdArgs& a, int t, float swd, const float
 // One 256-thread workgroup per token; thread i holds the float4 column
 // chunks i, i + 256, ... (at most 4: H <= 4096).  For each chunk the y rows
 // of all k slots are loaded together, so a token costs one load round trip
-// per chunk, not one per slot.  Per slot: the thread's partial dot, a
-// butterfly over the wave, the four wave sums added in wave order.
+// per chunk, not one per slot (KS: the slot count where it is known at
+// compile time, whose two chunks' loads are then in flight together).  Per
+// slot: the thread's partial dot, a butterfly over the wave, the four wave
+// sums added in wave order.
+template <int KS>
 __global__ __launch_bounds__(256) void bwd_weights_kernel(BwdArgs a) {
   __shared__ float s_part[16][4];
   __shared__ float s_dw[16];
+  constexpr int kMaxKs = KS > 0 ? KS : 16;
+  constexpr int kPair = KS > 0 && KS <= 8 ? 2 : 1;  // chunks whose loads issue together
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = a.H, k = a.k, n4 = H / 4;
+  const int H = a.H, k = KS > 0 ? KS : a.k, n4 = H / 4;
   const float* dout = a.d_out + (size_t)t * H;
   const float* ybase = a.y + (size_t)t * k * H;
   float part[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) part[j] = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c4 = tid + 256 * i;
-    if (c4 < n4) {
-      const f32x4_t dv = *reinterpret_cast<const f32x4_t*>(dout + 4 * c4);
-      f32x4_t yv[16];
+  for (int i0 = 0; i0 < 4; i0 += kPair) {
+    f32x4_t dv[kPair], yv[kPair][kMaxKs];
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < k) yv[j] = *reinterpret_cast<const f32x4_t*>(ybase + (size_t)j * H + 4 * c4);
+    for (int u = 0; u < kPair; ++u) {
+      const int c4 = tid + 256 * (i0 + u);
+      if (c4 < n4) {
+        dv[u] = *reinterpret_cast<const f32x4_t*>(dout + 4 * c4);
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j < k)
+        for (int j = 0; j < kMaxKs; ++j)
+          if (j < k) yv[u][j] = *reinterpret_cast<const f32x4_t*>(ybase + (size_t)j * H + 4 * c4);
+      }
+    }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) part[j] = fmaf(dv[q], yv[j][q], part[j]);
+    for (int u = 0; u < kPair; ++u) {
+      if (tid + 256 * (i0 + u) < n4) {
+#pragma unroll
+        for (int j = 0; j < kMaxKs; ++j)
+          if (j < k)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) part[j] = fmaf(dv[u][q], yv[u][j][q], part[j]);
+      }
     }
   }
 #pragma unroll
@@ -1143,7 +1156,10 @@ hipError_t launch_bq(const BwdArgs& a, dim3 grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd_weights(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_weights_kernel, dim3(a.T), dim3(256), 0, s, a);
+  if (a.k == 8)
+    hipLaunchKernelGGL(bwd_weights_kernel<8>, dim3(a.T), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_weights_kernel<0>, dim3(a.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
