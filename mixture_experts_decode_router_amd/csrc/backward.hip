@@ -1107,12 +1107,18 @@ __global__ __launch_bounds__(256) void bwd_combine_kernel(BwdArgs a) {
   const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (c >= a.H) return;
   float* dx = a.d_x + (size_t)t * a.H + c;
-  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(dx);
-  for (int j = 0; j < a.k; ++j) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.d_xs + ((size_t)t * a.k + j) * a.H + c);
+  // all k slot rows are loaded before the first add (one round trip), then
+  // added in slot order
+  f32x4_t v[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] += v[q];
-  }
+  for (int j = 0; j < 16; ++j)
+    if (j < a.k) v[j] = *reinterpret_cast<const f32x4_t*>(a.d_xs + ((size_t)t * a.k + j) * a.H + c);
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(dx);
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < a.k)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += v[j][q];
   *reinterpret_cast<f32x4_t*>(dx) = acc;
 }
 
