@@ -339,8 +339,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs (--gpus > 1) are not "
-              "supported (sharding is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py: the library runs on one GPU; multi-GPU runs (--gpus > 1) are not "
+              "supported (the block's expert- and tensor-parallel sharding is not built).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
