@@ -36,8 +36,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, u_gu, u_d, gu, z_gu, z_d,
-      total;
+  size_t ids, wts, counts, offsets, perm, pos, items, n_items, live, route, chunks, h, y, u_gu, u_d, gu, gub, z_gu,
+      z_d, total;
   int max_items;
 };
 
@@ -74,6 +74,7 @@ Layout layout(const moe_config& c) {
   L.u_gu = take(N * 16 * 4);  // LoRA: A_gu x per routed row
   L.u_d = take(N * 16 * 4);   // LoRA: A_d h per routed row
   L.gu = take(c.train ? N * 2 * c.inter * 4 : 0);  // training forward: gate/up pre-activations
+  L.gub = take(c.train ? N * 2 * c.inter * 2 : 0);  // backward: d_g, d_u in bf16 (tiled bf16 weights)
   L.z_gu = take(c.train ? N * 16 * 4 : 0);         // LoRA backward: B_gu^T [d_g; d_u] per routed row
   L.z_d = take(c.train ? N * 16 * 4 : 0);          // LoRA backward: B_d^T d_y per routed row
   L.total = off;
@@ -578,6 +579,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void*
     b.codebook = w->codebook;
   }
   b.gu = at<float>(workspace, L.gu);
+  b.gub = at<uint16_t>(workspace, L.gub);
   b.d_xs = at<float>(workspace, L.y);  // y is read first, then its memory holds the per-slot d_x
   b.x = static_cast<const uint16_t*>(x);
   if (c.topk_weights == MOE_TOPK_SOFTMAX) {

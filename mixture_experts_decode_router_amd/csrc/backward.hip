@@ -559,25 +559,39 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
   // two 16-byte reads of one row (row r of a tile, chunks 2g, 2g + 1) meet
   // no bank conflicts over 8 consecutive rows.  Rows past the item copy row
   // 0 and are scaled by 0.
-  const float* vsrc[kBgVLoads];
+  // The gate/up pass instead copies (d_g, d_u) as the down pass rounded
+  // them to bf16 (the operand it would form, so the same bits): 64 bytes
+  // per row and stage, slot 4 row + c holding chunk xchunk(row, c), the
+  // MFMA operand order of the prefill GEMMs' token tiles, read at xslot.
+  constexpr bool kVb = MODE == kGateUp;
+  constexpr int kVLoads = kVb ? kBgVStage / 2 / 1024 / kBgWaves : kBgVLoads;  // v copies per wave per stage
+  const void* vsrc[kVLoads];
 #pragma unroll
-  for (int j = 0; j < kBgVLoads; ++j) {
-    const int slot = (kBgVLoads * wave + j) * 64 + lane;
-    const int row = slot >> 3, ch = (slot & 7) ^ ((row >> 1) & 3);
-    const int rc = row < M ? row : 0;
-    const float* rp;
-    if (MODE == kDown)
-      rp = a.d_out + (size_t)(a.perm[base + rc] / a.k) * H;
-    else
-      rp = a.gu + (size_t)(base + rc) * 2 * I;
-    vsrc[j] = rp + 4 * ch;
+  for (int j = 0; j < kVLoads; ++j) {
+    const int slot = (kVLoads * wave + j) * 64 + lane;
+    if constexpr (kVb) {
+      const int row = slot >> 2, ch = xchunk(row & 15, slot & 3);
+      const int rc = row < M ? row : 0;
+      vsrc[j] = a.gub + (size_t)(base + rc) * 2 * I + 8 * ch;
+    } else {
+      const int row = slot >> 3, ch = (slot & 7) ^ ((row >> 1) & 3);
+      const int rc = row < M ? row : 0;
+      const float* rp;
+      if (MODE == kDown)
+        rp = a.d_out + (size_t)(a.perm[base + rc] / a.k) * H;
+      else
+        rp = a.gu + (size_t)(base + rc) * 2 * I;
+      vsrc[j] = rp + 4 * ch;
+    }
   }
   auto issue_v = [&](int st) {
     const int src = min(st, nsteps - 1);
 #pragma unroll
-    for (int j = 0; j < kBgVLoads; ++j)
-      __builtin_amdgcn_global_load_lds(vsrc[j] + 32 * src, (bg_lds_t*)(vbuf(st) + (kBgVLoads * wave + j) * 1024), 16,
-                                       0, 0);
+    for (int j = 0; j < kVLoads; ++j) {
+      const void* gsrc = kVb ? (const void*)(static_cast<const uint16_t*>(vsrc[j]) + 32 * src)
+                             : (const void*)(static_cast<const float*>(vsrc[j]) + 32 * src);
+      __builtin_amdgcn_global_load_lds(gsrc, (bg_lds_t*)(vbuf(st) + (kVLoads * wave + j) * 1024), 16, 0, 0);
+    }
   };
   // the scale of this lane's A-operand row in each of the wave's row tiles
   const int r_ = lane & 15, g_ = lane >> 4;
@@ -635,16 +649,20 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i >= nj) break;
-        // the A operand: w v rounded to bf16 (hi, and lo = w v - hi)
-        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vb + voff[i][0]);
-        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vb + voff[i][1]);
-        const float t[8] = {vw[i] * v0[0], vw[i] * v0[1], vw[i] * v0[2], vw[i] * v0[3],
-                            vw[i] * v1[0], vw[i] * v1[1], vw[i] * v1[2], vw[i] * v1[3]};
         u32x4_t ah, al;
+        if constexpr (kVb) {
+          ah = *reinterpret_cast<const u32x4_t*>(vb + (wm * 4 + i) * 1024 + xslot(lane) * 16);
+        } else {
+          // the A operand: w v rounded to bf16 (hi, and lo = w v - hi)
+          const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(vb + voff[i][0]);
+          const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(vb + voff[i][1]);
+          const float t[8] = {vw[i] * v0[0], vw[i] * v0[1], vw[i] * v0[2], vw[i] * v0[3],
+                              vw[i] * v1[0], vw[i] * v1[1], vw[i] * v1[2], vw[i] * v1[3]};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          ah[q] = pack_bf16x2(t[2 * q], t[2 * q + 1]);
-          if constexpr (kHiLo) al[q] = pack_bf16x2(t[2 * q] - bf16lo(ah[q]), t[2 * q + 1] - bf16hi(ah[q]));
+          for (int q = 0; q < 4; ++q) {
+            ah[q] = pack_bf16x2(t[2 * q], t[2 * q + 1]);
+            if constexpr (kHiLo) al[q] = pack_bf16x2(t[2 * q] - bf16lo(ah[q]), t[2 * q + 1] - bf16hi(ah[q]));
+          }
         }
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
@@ -701,8 +719,13 @@ __global__ __launch_bounds__(kBgThreads) void bwd_gemm_kernel(BwdArgs a) {
           const float gv = gp[n], uv = gp[I + n];
           const float sg = 1.0f / (1.0f + __expf(-gv));
           const float dh = acc[i][t][q];
-          gp[n] = dh * uv * (sg * (1.0f + gv * (1.0f - sg)));
-          gp[I + n] = dh * (gv * sg);
+          const float dg = dh * uv * (sg * (1.0f + gv * (1.0f - sg))), du = dh * (gv * sg);
+          gp[n] = dg;
+          gp[I + n] = du;
+          // the gate/up pass's A operand, rounded once here
+          uint16_t* gb = a.gub + (size_t)(base + m) * 2 * I;
+          gb[n] = (uint16_t)pack_bf16x2(dg, 0.f);
+          gb[I + n] = (uint16_t)pack_bf16x2(du, 0.f);
         } else {
           a.d_xs[(size_t)a.perm[base + m] * H + n] = acc[i][t][q];
         }

@@ -171,6 +171,8 @@ struct BwdArgs {
   const float* s_down;
   const float* codebook;
   float* gu;                  // [N][2I]: g, u kept by the forward, then d_g, d_u
+  uint16_t* gub;              // [N][2I]: d_g, d_u rounded to bf16 by the tiled down pass (its gate/up pass's
+                              // A operand); the tiled bf16 backward needs it
   float* d_xs;                // [N][H], flat-slot order (may reuse y's memory)
   int row_tiles;              // 16-row tiles per work item: 1 (16-row GEMVs), or kMfmaTile / 16 after an
                               // MFMA forward (the tiled transposed GEMMs; bf16 weights)
