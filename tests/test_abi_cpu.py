@@ -271,9 +271,10 @@ def test_backward_validation_on_host():
     assert st(cfg(**tiled)) == L.MOE_ERR_UNSUPPORTED                     # not a training config
     assert "train" in L.moe_last_error()
     assert st(cfg(train=1)) == L.MOE_ERR_UNSUPPORTED                     # row-major weights
-    # a training config has room for the pre-activations and the two rank-16 z rows per slot
+    # a training config has room for the pre-activations (fp32, and their
+    # gradients' bf16 copy) and the two rank-16 z rows per slot
     assert (L.moe_workspace_size(cfg(train=1, **tiled))
-            == L.moe_workspace_size(cfg(**tiled)) + 64 * 8 * 2 * 768 * 4 + 2 * 64 * 8 * 16 * 4)
+            == L.moe_workspace_size(cfg(**tiled)) + 64 * 8 * 2 * 768 * (4 + 2) + 2 * 64 * 8 * 16 * 4)
     # LoRA: gradient arrays exactly when adapters are given (every case fails before any launch)
     lo = L.moe_lora(FAKE, FAKE * 2, FAKE * 3, FAKE * 5, 2.0, 16)
     wl = weights()
